@@ -1,0 +1,304 @@
+/*
+ * lam_oracle.c -- plain, slow, token-by-token CPU oracle for the causal
+ * recurrent-memory linear-attention forward scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with
+ * the HIP library; the two meet only through seeded inputs.
+ *
+ * Sources (cited by page title and section; the pages are web articles):
+ *   [LA-arch]  "Mechanisms, trade-offs and cross-layer routing of
+ *              linear-attention architectures" (aitrends.kr), sections
+ *              "Key contributions", "Understanding the core idea",
+ *              "Methodology" and "Technical details": the unified
+ *              recurrent-memory notation (memory W in R^{dv x dk}, read
+ *              y = W phi(q)), the DeltaNet delta rule, Gated DeltaNet's
+ *              scalar decay, Kimi Delta's channel-wise decay on the
+ *              key-feature axis and Gated DeltaNet-2's channel-wise erase
+ *              and write gates.
+ *   [VLA]      "Technical summary: Variational Linear Attention (VLA)"
+ *              (gist.science), section 2.2 (inverse penalty A = M^{-1} kept
+ *              by Sherman-Morrison at O(d^2) per step), section 2.3 (the
+ *              three recursive update rules; unit-length k-hat and alpha-hat;
+ *              ELU+1 feature map).
+ *
+ * Every quantity is computed in `real` (double unless the file is compiled
+ * with -DLAM_ORACLE_REAL=float, which gives the single-precision spread
+ * check).  Inputs and outputs are always double arrays; a float build rounds
+ * each input once on load.
+ *
+ * Readings taken where the pages are silent (each listed in the design notes):
+ *   - the read happens after the update: y_t = W_t q_t (and S_t q-hat_t);
+ *   - Gated DeltaNet's residual is taken against the decayed memory,
+ *     r = v - (alpha W_{t-1}) k;
+ *   - Kimi Delta's decay multiplies the key-channel columns: W diag(alpha_t);
+ *   - Gated DeltaNet-2 reads with the erase direction e = b*k against the
+ *     decayed memory, targets z = w*v and writes along k;
+ *   - VLA's Sherman-Morrison vector u_t is the penalty direction p_t, with
+ *     z_t = A_{t-1} p_t; the output is S_t q-hat_t with no denominator;
+ *   - no 1/sqrt(d) scale and no epsilon in any norm.
+ *
+ * Parity status: every function here is pinned by closed forms, special
+ * cases, invariants and brute force in the CPU test tier; no function is
+ * unpinned.
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef LAM_ORACLE_REAL
+#define LAM_ORACLE_REAL double
+#endif
+typedef LAM_ORACLE_REAL real;
+
+/* Variant codes of the oracle's own interface. */
+enum {
+    ORACLE_DELTANET = 0,      /* alpha = 1                                  */
+    ORACLE_GATED_DELTANET = 1, /* scalar alpha per (b, t, h)                */
+    ORACLE_KIMI_DELTA = 2,    /* alpha per (b, t, h, key channel)          */
+    ORACLE_GATED_DELTANET2 = 3 /* scalar alpha + erase b[dk], write w[dv]   */
+};
+
+/* Row-major index helpers for [B,T,H,n] token streams and [B,H,r,c] states. */
+static size_t tok(long b, long t, long h, long T, long H, long n) {
+    return (((size_t)b * T + t) * H + h) * (size_t)n;
+}
+static size_t st(long b, long h, long H, long r, long c) {
+    return ((size_t)b * H + h) * (size_t)r * (size_t)c;
+}
+
+/*
+ * Delta-rule family, one (b, h) chain.  Per token, in this order
+ * ([LA-arch] Technical details / Methodology):
+ *   decay     W~ = alpha W            (Gated DeltaNet, Gated DeltaNet-2)
+ *             W~ = W diag(alpha)      (Kimi Delta: key-feature channels)
+ *             W~ = W                  (DeltaNet)
+ *   predict   vbar = W~ kk,  kk = k   (kk = b*k for Gated DeltaNet-2)
+ *   residual  r = target - vbar,  target = v  (z = w*v for Gated DeltaNet-2)
+ *   write     W = W~ + beta r k^T
+ *   read      y = W q
+ * With drop_delta set the prediction is skipped (r = target): that is the
+ * plain additive accumulation the VLA page contrasts against (section 2.1),
+ * used only as a test hook.
+ */
+static void delta_chain(int variant, long b, long h, long T, long H, long dk,
+                        long dv, const double *q, const double *k,
+                        const double *v, const double *alpha,
+                        const double *erase_b, const double *write_w,
+                        const double *beta, const double *state_in,
+                        double *out, double *state_out, int drop_delta,
+                        real *W, real *kk, real *target, real *r) {
+    for (long i = 0; i < dv * dk; ++i)
+        W[i] = state_in ? (real)state_in[st(b, h, H, dv, dk) + i] : (real)0;
+
+    for (long t = 0; t < T; ++t) {
+        const double *kt = k + tok(b, t, h, T, H, dk);
+        const double *qt = q + tok(b, t, h, T, H, dk);
+        const double *vt = v + tok(b, t, h, T, H, dv);
+        const real bt = (real)beta[tok(b, t, h, T, H, 1)];
+
+        /* decay */
+        if (variant == ORACLE_GATED_DELTANET || variant == ORACLE_GATED_DELTANET2) {
+            const real a = (real)alpha[tok(b, t, h, T, H, 1)];
+            for (long i = 0; i < dv * dk; ++i) W[i] = a * W[i];
+        } else if (variant == ORACLE_KIMI_DELTA) {
+            const double *at = alpha + tok(b, t, h, T, H, dk);
+            for (long i = 0; i < dv; ++i)
+                for (long j = 0; j < dk; ++j) W[i * dk + j] = W[i * dk + j] * (real)at[j];
+        }
+
+        /* read key and write target */
+        for (long j = 0; j < dk; ++j) kk[j] = (real)kt[j];
+        for (long i = 0; i < dv; ++i) target[i] = (real)vt[i];
+        if (variant == ORACLE_GATED_DELTANET2) {
+            const double *bt_ = erase_b + tok(b, t, h, T, H, dk);
+            const double *wt_ = write_w + tok(b, t, h, T, H, dv);
+            for (long j = 0; j < dk; ++j) kk[j] = (real)bt_[j] * kk[j];
+            for (long i = 0; i < dv; ++i) target[i] = (real)wt_[i] * target[i];
+        }
+
+        /* residual against the (decayed) memory */
+        for (long i = 0; i < dv; ++i) {
+            real pred = 0;
+            if (!drop_delta)
+                for (long j = 0; j < dk; ++j) pred += W[i * dk + j] * kk[j];
+            r[i] = target[i] - pred;
+        }
+
+        /* write along the key */
+        for (long i = 0; i < dv; ++i)
+            for (long j = 0; j < dk; ++j) W[i * dk + j] += bt * r[i] * (real)kt[j];
+
+        /* read with the query */
+        double *yt = out + tok(b, t, h, T, H, dv);
+        for (long i = 0; i < dv; ++i) {
+            real acc = 0;
+            for (long j = 0; j < dk; ++j) acc += W[i * dk + j] * (real)qt[j];
+            yt[i] = (double)acc;
+        }
+    }
+    if (state_out)
+        for (long i = 0; i < dv * dk; ++i) state_out[st(b, h, H, dv, dk) + i] = (double)W[i];
+}
+
+/*
+ * oracle_delta_forward: the four delta-rule variants over a [B,T] block.
+ * Layouts: q, k, erase_b [B,T,H,dk]; v, write_w, out [B,T,H,dv];
+ * alpha [B,T,H] (Gated DeltaNet, Gated DeltaNet-2) or [B,T,H,dk] (Kimi
+ * Delta) or NULL (DeltaNet); beta [B,T,H]; state_in / state_out
+ * [B,H,dv,dk] (NULL in = zero memory, NULL out = not written).
+ * Returns 0, or -1 on a bad argument or allocation failure.
+ */
+int oracle_delta_forward(int variant, long B, long T, long H, long dk, long dv,
+                         const double *q, const double *k, const double *v,
+                         const double *alpha, const double *erase_b,
+                         const double *write_w, const double *beta,
+                         const double *state_in, double *out,
+                         double *state_out, int drop_delta, int nthreads) {
+    if (variant < ORACLE_DELTANET || variant > ORACLE_GATED_DELTANET2) return -1;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return -1;
+    if (!q || !k || !v || !beta || !out) return -1;
+    if (variant != ORACLE_DELTANET && !alpha) return -1;
+    if (variant == ORACLE_GATED_DELTANET2 && (!erase_b || !write_w)) return -1;
+    const long chains = B * H;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads()) \
+    reduction(| : failed)
+    for (long c = 0; c < chains; ++c) {
+        real *buf = (real *)malloc(sizeof(real) * (size_t)(dv * dk + 2 * dk + 2 * dv));
+        if (!buf) { failed = 1; continue; }
+        delta_chain(variant, c / H, c % H, T, H, dk, dv, q, k, v, alpha, erase_b,
+                    write_w, beta, state_in, out, state_out, drop_delta, buf,
+                    buf + dv * dk, buf + dv * dk + dk, buf + dv * dk + dk + dv);
+        free(buf);
+    }
+    return failed ? -1 : 0;
+}
+
+/* ELU(x) + 1 with ELU's scale 1: x + 1 for x > 0, exp(x) otherwise
+ * ([VLA] section 2.3, the feature map of keys and queries). */
+static real elu_plus_one(real x) { return x > 0 ? x + (real)1 : (real)exp((double)x); }
+
+/*
+ * VLA, one (b, h) chain.  Per token, in the order of [VLA] section 2.3:
+ *   features   k-hat = phi(k)/|phi(k)|, q-hat = phi(q)/|phi(q)|, phi = ELU+1
+ *   rule 1     z = A p;  A <- A - z z^T / (1 + p^T z)     (Sherman-Morrison
+ *              for M_t = M_{t-1} + p p^T, section 2.2)
+ *   rule 2     a = A k-hat;  alpha-hat = a / |a|
+ *   rule 3     S <- S + (v - S k-hat) alpha-hat^T
+ *   read       y = S q-hat
+ */
+static void vla_chain(long b, long h, long T, long H, long d, const double *q,
+                      const double *k, const double *v, const double *p,
+                      const double *A_in, const double *S_in, double *out,
+                      double *A_out, double *S_out, double *khat_out,
+                      double *qhat_out, double *ahat_out, double *den_out,
+                      real *A, real *S, real *kh, real *qh, real *pp, real *z,
+                      real *a, real *r) {
+    const size_t s0 = st(b, h, H, d, d);
+    for (long i = 0; i < d; ++i)
+        for (long j = 0; j < d; ++j) {
+            A[i * d + j] = A_in ? (real)A_in[s0 + i * d + j] : (real)(i == j);
+            S[i * d + j] = S_in ? (real)S_in[s0 + i * d + j] : (real)0;
+        }
+
+    for (long t = 0; t < T; ++t) {
+        const size_t o = tok(b, t, h, T, H, d);
+        /* feature maps and unit normalisation */
+        real nk = 0, nq = 0;
+        for (long j = 0; j < d; ++j) {
+            kh[j] = elu_plus_one((real)k[o + j]);
+            qh[j] = elu_plus_one((real)q[o + j]);
+            nk += kh[j] * kh[j];
+            nq += qh[j] * qh[j];
+        }
+        nk = (real)sqrt((double)nk);
+        nq = (real)sqrt((double)nq);
+        for (long j = 0; j < d; ++j) {
+            kh[j] /= nk;
+            qh[j] /= nq;
+            pp[j] = (real)p[o + j];
+        }
+
+        /* rule 1: Sherman-Morrison downdate of the inverse penalty */
+        real den = 1;
+        for (long i = 0; i < d; ++i) {
+            real acc = 0;
+            for (long j = 0; j < d; ++j) acc += A[i * d + j] * pp[j];
+            z[i] = acc;
+        }
+        for (long i = 0; i < d; ++i) den += pp[i] * z[i];
+        for (long i = 0; i < d; ++i)
+            for (long j = 0; j < d; ++j) A[i * d + j] -= z[i] * z[j] / den;
+
+        /* rule 2: gating vector */
+        real na = 0;
+        for (long i = 0; i < d; ++i) {
+            real acc = 0;
+            for (long j = 0; j < d; ++j) acc += A[i * d + j] * kh[j];
+            a[i] = acc;
+            na += acc * acc;
+        }
+        na = (real)sqrt((double)na);
+        for (long i = 0; i < d; ++i) a[i] /= na;
+
+        /* rule 3: residual write along alpha-hat */
+        for (long i = 0; i < d; ++i) {
+            real acc = 0;
+            for (long j = 0; j < d; ++j) acc += S[i * d + j] * kh[j];
+            r[i] = (real)v[o + i] - acc;
+        }
+        for (long i = 0; i < d; ++i)
+            for (long j = 0; j < d; ++j) S[i * d + j] += r[i] * a[j];
+
+        /* read */
+        for (long i = 0; i < d; ++i) {
+            real acc = 0;
+            for (long j = 0; j < d; ++j) acc += S[i * d + j] * qh[j];
+            out[o + i] = (double)acc;
+        }
+        if (khat_out) for (long j = 0; j < d; ++j) khat_out[o + j] = (double)kh[j];
+        if (qhat_out) for (long j = 0; j < d; ++j) qhat_out[o + j] = (double)qh[j];
+        if (ahat_out) for (long j = 0; j < d; ++j) ahat_out[o + j] = (double)a[j];
+        if (den_out) den_out[tok(b, t, h, T, H, 1)] = (double)den;
+    }
+    if (A_out) for (long i = 0; i < d * d; ++i) A_out[s0 + i] = (double)A[i];
+    if (S_out) for (long i = 0; i < d * d; ++i) S_out[s0 + i] = (double)S[i];
+}
+
+/*
+ * oracle_vla_forward: VLA over a [B,T] block, dk = dv = d.
+ * Layouts: q, k, v, p, out [B,T,H,d]; A_in/A_out/S_in/S_out [B,H,d,d]
+ * (NULL A_in = identity, NULL S_in = zero, NULL outs = not written).
+ * Optional per-token diagnostics [B,T,H,d]: k-hat, q-hat, alpha-hat; and the
+ * Sherman-Morrison denominator 1 + p^T z as [B,T,H].
+ * Returns 0, or -1 on a bad argument or allocation failure.
+ */
+int oracle_vla_forward(long B, long T, long H, long d, const double *q,
+                       const double *k, const double *v, const double *p,
+                       const double *A_in, const double *S_in, double *out,
+                       double *A_out, double *S_out, double *khat_out,
+                       double *qhat_out, double *ahat_out, double *den_out,
+                       int nthreads) {
+    if (B < 0 || T < 0 || H < 0 || d <= 0) return -1;
+    if (!q || !k || !v || !p || !out) return -1;
+    const long chains = B * H;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads()) \
+    reduction(| : failed)
+    for (long c = 0; c < chains; ++c) {
+        real *buf = (real *)malloc(sizeof(real) * (size_t)(2 * d * d + 6 * d));
+        if (!buf) { failed = 1; continue; }
+        real *A = buf, *S = buf + d * d, *w = buf + 2 * d * d;
+        vla_chain(c / H, c % H, T, H, d, q, k, v, p, A_in, S_in, out, A_out, S_out,
+                  khat_out, qhat_out, ahat_out, den_out, A, S, w, w + d, w + 2 * d,
+                  w + 3 * d, w + 4 * d, w + 5 * d);
+        free(buf);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Size of `real` in this build (8 for the fp64 oracle, 4 for the spread check). */
+int oracle_real_bytes(void) { return (int)sizeof(real); }

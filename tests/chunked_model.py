@@ -1,0 +1,127 @@
+"""Test-only float64 numpy model of the chunkwise-parallel scan.
+
+This is the algebra the HIP kernels evaluate, written out plainly so that the
+CPU tier can check it against the token-by-token oracle before any kernel is
+trusted.  It is derived from the per-token rules (linear-attention
+architectures page, "Technical details"; VLA page, section 2.3) and shares no
+code with the oracle or with the HIP library.
+
+Per chunk of C tokens (rows = tokens, S = state at the chunk start, dv x dk):
+
+Gated DeltaNet (DeltaNet: every alpha = 1), gamma_t = prod_{j<=t} alpha_j:
+    L     = strict_tril(diag(beta) (K K^T * Gamma)),  Gamma_ts = gamma_t/gamma_s
+    U     = (I + L)^-1 (diag(beta) V - diag(beta gamma) K S^T)
+    Y     = diag(gamma) Q S^T + (tril(Q K^T) * Gamma) U
+    S'    = gamma_C S + U^T diag(gamma_C / gamma) K
+Gated DeltaNet-2: L from E K^T (e_t . k_s), V -> Z and K S^T -> E S^T in U.
+Kimi Delta (g_t = prod_{j<=t} alpha_j per key channel):
+    L_ts  = beta_t sum_c k_tc k_sc g_tc/g_sc  (s < t)
+    U     = (I + L)^-1 diag(beta) (V - (K*G) S^T)
+    Y     = (Q*G) S^T + Aqk U,  Aqk_ts = sum_c q_tc k_sc g_tc/g_sc  (s <= t)
+    S'    = S diag(g_C) + U^T (K * g_C/G)
+VLA state (read key k-hat, write key alpha-hat):
+    U     = (I + strict_tril(Khat Ahat^T))^-1 (V - Khat S^T)
+    Y     = Qhat S^T + tril(Qhat Ahat^T) U
+    S'    = S + U^T Ahat
+VLA inverse penalty (A_c = inverse penalty at the chunk start):
+    I + P A_c P^T = L D L^T,  Z = L^-1 P A_c   (row t: z_t = A_{t-1} p_t)
+    A_t khat_t = A_c khat_t - sum_{s<=t} z_s (z_s . khat_t) / D_s
+    A_next = A_c - Z^T D^-1 Z
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _phi(x):
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def delta_chunked(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None,
+                  state_in=None, C=64):
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    out = np.zeros((B, T, H, dv))
+    state_out = np.zeros((B, H, dv, dk))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dv, dk)) if state_in is None else state_in[b, h].copy()
+            for c0 in range(0, T, C):
+                c1 = min(T, c0 + C)
+                n = c1 - c0
+                Q, K, V = q[b, c0:c1, h], k[b, c0:c1, h], v[b, c0:c1, h]
+                be = beta[b, c0:c1, h]
+                tril = np.tril(np.ones((n, n)))
+                stril = np.tril(np.ones((n, n)), -1)
+                if variant == "kda":
+                    lg = np.cumsum(np.log(alpha[b, c0:c1, h]), axis=0)      # [n, dk]
+                    # Gamma per channel: exp(G_t - G_s), evaluated only for s <= t
+                    D = lg[:, None, :] - lg[None, :, :]                      # [t, s, c]
+                    D = np.where(tril[:, :, None] > 0, D, -np.inf)
+                    Gm = np.exp(D)
+                    Akk = np.einsum("tc,sc,tsc->ts", K, K, Gm)
+                    Aqk = np.einsum("tc,sc,tsc->ts", Q, K, Gm)
+                    G = np.exp(lg)
+                    L = stril * (be[:, None] * Akk)
+                    rhs = be[:, None] * (V - (K * G) @ S.T)
+                    U = np.linalg.solve(np.eye(n) + L, rhs)
+                    Y = (Q * G) @ S.T + (Aqk * tril) @ U
+                    S = S * G[-1][None, :] + U.T @ (K * np.exp(lg[-1][None, :] - lg))
+                else:
+                    if variant == "deltanet":
+                        lg = np.zeros(n)
+                    else:
+                        lg = np.cumsum(np.log(alpha[b, c0:c1, h]))
+                    D = lg[:, None] - lg[None, :]
+                    Gam = np.where(tril > 0, np.exp(np.where(tril > 0, D, 0.0)), 0.0)
+                    g = np.exp(lg)
+                    if variant == "gdn2":
+                        E = erase_b[b, c0:c1, h] * K
+                        Z = write_w[b, c0:c1, h] * V
+                    else:
+                        E, Z = K, V
+                    L = stril * (be[:, None] * (E @ K.T) * Gam)
+                    rhs = be[:, None] * Z - (be * g)[:, None] * (E @ S.T)
+                    U = np.linalg.solve(np.eye(n) + L, rhs)
+                    Y = g[:, None] * (Q @ S.T) + ((Q @ K.T) * Gam) @ U
+                    S = g[-1] * S + U.T @ (np.exp(lg[-1] - lg)[:, None] * K)
+                out[b, c0:c1, h] = Y
+            state_out[b, h] = S
+    return out, state_out
+
+
+def vla_chunked(q, k, v, p, A_in=None, S_in=None, C=64):
+    B, T, H, d = q.shape
+    out = np.zeros((B, T, H, d))
+    A_out = np.zeros((B, H, d, d))
+    S_out = np.zeros((B, H, d, d))
+    for b in range(B):
+        for h in range(H):
+            A = np.eye(d) if A_in is None else A_in[b, h].copy()
+            S = np.zeros((d, d)) if S_in is None else S_in[b, h].copy()
+            for c0 in range(0, T, C):
+                c1 = min(T, c0 + C)
+                n = c1 - c0
+                fk = _phi(k[b, c0:c1, h])
+                fq = _phi(q[b, c0:c1, h])
+                Kh = fk / np.linalg.norm(fk, axis=1, keepdims=True)
+                Qh = fq / np.linalg.norm(fq, axis=1, keepdims=True)
+                P = p[b, c0:c1, h]
+                V = v[b, c0:c1, h]
+                # inverse penalty: LDL^T of I + P A P^T via Cholesky
+                R = np.linalg.cholesky(np.eye(n) + P @ A @ P.T)
+                Dg = np.diag(R) ** 2
+                Lu = R / np.diag(R)[None, :]
+                Z = np.linalg.solve(Lu, P @ A)
+                AK = Kh @ A - np.tril((Kh @ Z.T) / Dg[None, :]) @ Z
+                Ah = AK / np.linalg.norm(AK, axis=1, keepdims=True)
+                A = A - Z.T @ (Z / Dg[:, None])
+                # state
+                stril = np.tril(np.ones((n, n)), -1)
+                U = np.linalg.solve(np.eye(n) + stril * (Kh @ Ah.T), V - Kh @ S.T)
+                Y = Qh @ S.T + (np.tril(np.ones((n, n))) * (Qh @ Ah.T)) @ U
+                S = S + U.T @ Ah
+                out[b, c0:c1, h] = Y
+            A_out[b, h] = A
+            S_out[b, h] = S
+    return out, A_out, S_out
