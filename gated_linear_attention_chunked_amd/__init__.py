@@ -1,1 +1,171 @@
-"""MI355X-native recurrent-memory linear-attention forward scan (placeholder; binding below)."""
+"""MI355X-native (gfx950) recurrent-memory linear-attention forward scan.
+
+Thin Python binding of ``liblam.so`` (C ABI in ``include/lam.h``): it checks
+and marshals torch tensors into plain device pointers and sizes and calls the
+library on torch's current HIP stream.  Every step of the scan runs in the
+library's HIP kernels; there is no Python or CPU fallback -- if the library is
+not built, or the device is not a GPU, the call raises.
+
+Variants (see ``include/lam.h`` for the rules and their sources): DeltaNet
+("deltanet"), Gated DeltaNet ("gdn"), Kimi Delta ("kda"), Gated DeltaNet-2
+("gdn2"), and VLA (``vla_forward``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["forward", "vla_forward", "library", "LamError", "VARIANTS", "ALGOS", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblam.so")
+VARIANTS = {"deltanet": 0, "gdn": 1, "kda": 2, "gdn2": 3}
+ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
+DTYPES = {"f32": 0, "bf16": 1}
+STATUS = {0: "LAM_OK", 1: "LAM_ERR_INVALID_ARG", 2: "LAM_ERR_UNSUPPORTED", 3: "LAM_ERR_HIP"}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class LamError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} "
+                         f"({library().lam_status_string(status).decode()})")
+
+
+def library() -> ctypes.CDLL:
+    """The loaded C library (built in-tree by ``build.py``)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is not built; run "
+                                   "`python -m gated_linear_attention_chunked_amd.build`")
+            lib = ctypes.CDLL(LIB_PATH)
+            i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+            lib.lam_forward.argtypes = [ci, ci, i64, i64, i64, i64, i64] + [vp] * 10 + [ci, vp]
+            lib.lam_forward.restype = ci
+            lib.lam_vla_forward.argtypes = [ci, i64, i64, i64, i64] + [vp] * 9 + [ci, vp]
+            lib.lam_vla_forward.restype = ci
+            lib.lam_status_string.argtypes = [ci]
+            lib.lam_status_string.restype = ctypes.c_char_p
+            lib.lam_abi_version.restype = ci
+            _lib = lib
+        return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.float32:
+        return DTYPES["f32"]
+    if t.dtype == torch.bfloat16:
+        return DTYPES["bf16"]
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name}: must be on {device} (a GPU device)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def forward(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None, state_in=None, *,
+            algo="auto", out=None, state_out=None, with_state=True, stream=None):
+    """Delta-rule family forward scan.
+
+    q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H]; alpha: [B,T,H]
+    ("gdn", "gdn2") or [B,T,H,dk] ("kda"), unused for "deltanet"; erase_b
+    [B,T,H,dk] and write_w [B,T,H,dv] for "gdn2".  All per-token tensors share
+    one dtype (float32 or bfloat16) and device.  state_in: fp32 [B,H,dv,dk]
+    or None (zero memory).  Returns (out [B,T,H,dv], state_out fp32
+    [B,H,dv,dk] or None).
+    """
+    import torch
+
+    var = VARIANTS[variant]
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    dt, dev = q.dtype, q.device
+    _check(q, "q", (B, T, H, dk), dt, dev)
+    _check(k, "k", (B, T, H, dk), dt, dev)
+    _check(v, "v", (B, T, H, dv), dt, dev)
+    _check(beta, "beta", (B, T, H), dt, dev)
+    if var == VARIANTS["kda"]:
+        _check(alpha, "alpha", (B, T, H, dk), dt, dev)
+    elif var != VARIANTS["deltanet"]:
+        _check(alpha, "alpha", (B, T, H), dt, dev)
+    else:
+        alpha = None
+    if var == VARIANTS["gdn2"]:
+        _check(erase_b, "erase_b", (B, T, H, dk), dt, dev)
+        _check(write_w, "write_w", (B, T, H, dv), dt, dev)
+    else:
+        erase_b = write_w = None
+    _check(state_in, "state_in", (B, H, dv, dk), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check(out, "out", (B, T, H, dv), dt, dev)
+    if with_state and state_out is None:
+        state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    _check(state_out, "state_out", (B, H, dv, dk), torch.float32, dev)
+    rc = library().lam_forward(var, _dtype_code(q), B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(alpha), _ptr(erase_b), _ptr(write_w), _ptr(beta),
+                               _ptr(state_in), _ptr(out), _ptr(state_out), ALGOS[algo],
+                               _stream(stream))
+    if rc != 0:
+        raise LamError(rc, "lam_forward")
+    return out, state_out
+
+
+def vla_forward(q, k, v, p, A_in=None, S_in=None, *, algo="auto", out=None, A_out=None,
+                S_out=None, with_state=True, stream=None):
+    """VLA forward scan on raw q, k (ELU+1 features and unit norms inside).
+
+    q, k, v, p: [B,T,H,d] (float32 or bfloat16); A_in, S_in: fp32 [B,H,d,d]
+    or None (identity, zero).  Returns (out, A_out, S_out).
+    """
+    import torch
+
+    B, T, H, d = q.shape
+    dt, dev = q.dtype, q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("p", p)):
+        _check(t, n, (B, T, H, d), dt, dev)
+    for n, t in (("A_in", A_in), ("S_in", S_in)):
+        _check(t, n, (B, H, d, d), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, d), dtype=dt, device=dev)
+    _check(out, "out", (B, T, H, d), dt, dev)
+    if with_state:
+        if A_out is None:
+            A_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+        if S_out is None:
+            S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    for n, t in (("A_out", A_out), ("S_out", S_out)):
+        _check(t, n, (B, H, d, d), torch.float32, dev)
+    rc = library().lam_vla_forward(_dtype_code(q), B, T, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(p),
+                                   _ptr(A_in), _ptr(S_in), _ptr(out), _ptr(A_out), _ptr(S_out),
+                                   ALGOS[algo], _stream(stream))
+    if rc != 0:
+        raise LamError(rc, "lam_vla_forward")
+    return out, A_out, S_out

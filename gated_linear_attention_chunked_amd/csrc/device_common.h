@@ -1,0 +1,70 @@
+// device_common.h -- small device helpers shared by the gfx950 kernels:
+// storage-dtype loads/stores, lane reductions and the XCD-aware block map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lam {
+
+// ---------------------------------------------------------------- storage
+// bf16 is carried as its raw 16-bit pattern; widening is exact.
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+// Round to nearest, ties to even; NaN stays NaN (quiet bit forced).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+struct IoF32 {
+    using T = float;
+    static __device__ __forceinline__ float ld(const void *p, int64_t i) {
+        return static_cast<const float *>(p)[i];
+    }
+    static __device__ __forceinline__ void st(void *p, int64_t i, float x) {
+        static_cast<float *>(p)[i] = x;
+    }
+};
+struct IoBF16 {
+    using T = uint16_t;
+    static __device__ __forceinline__ float ld(const void *p, int64_t i) {
+        return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+    }
+    static __device__ __forceinline__ void st(void *p, int64_t i, float x) {
+        static_cast<uint16_t *>(p)[i] = f32_to_bf16_bits(x);
+    }
+};
+
+// ------------------------------------------------------------- reductions
+// Sum over aligned groups of W lanes (W a power of two <= 64); every lane of
+// the group receives the group's sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int m = W / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+// --------------------------------------------------------------- mapping
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X, so ids
+// congruent mod 8 share an XCD (and its L2).  Given `groups` groups of `per`
+// workgroups that read the same data, return (group, member) such that all
+// members of a group land on one XCD.  Falls back to the plain order when the
+// group count is not a multiple of 8.
+__device__ __forceinline__ void xcd_group_map(int bid, int groups, int per, int &group,
+                                              int &member) {
+    if ((groups & 7) == 0) {
+        const int xcd = bid & 7, local = bid >> 3;
+        group = (local / per) * 8 + xcd;
+        member = local % per;
+    } else {
+        group = bid / per;
+        member = bid % per;
+    }
+}
+
+}  // namespace lam

@@ -1,0 +1,134 @@
+/*
+ * lam.h -- C ABI of the MI355X (gfx950) recurrent-memory linear-attention
+ * forward scan.
+ *
+ * The operation.  Per (batch, head) chain the scan keeps a fixed-size memory
+ * W in R^{dv x dk} and, token by token, predicts the value from the current
+ * key, writes only the residual, and reads with the query
+ * ("Mechanisms, trade-offs and cross-layer routing of linear-attention
+ * architectures", sections "Understanding the core idea" and "Technical
+ * details": the unified recurrent-memory notation, memory W in
+ * R^{dv x dphi}, read y = W phi(q), delta-rule residual r = v - vbar):
+ *
+ *   DeltaNet            r = v - W k;              W = W + beta r k^T
+ *   Gated DeltaNet      r = v - (alpha W) k;      W = alpha W + beta r k^T
+ *   Kimi Delta          r = v - W diag(a) k;      W = W diag(a) + beta r k^T
+ *                       (a in R^dk: decay per key-feature channel)
+ *   Gated DeltaNet-2    e = b*k, z = w*v;  r = z - (alpha W) e;
+ *                       W = alpha W + beta r k^T  (erase b in R^dk, write w in R^dv)
+ *   and every variant reads after its write:  y_t = W_t q_t.
+ *
+ * VLA ("Technical summary: Variational Linear Attention (VLA)", sections 2.2
+ * and 2.3) keeps an inverse penalty A = M^{-1} (d x d) beside its state S
+ * (d x d).  Per token: khat, qhat = unit-normalised ELU+1 features of k, q;
+ * z = A p, A = A - z z^T / (1 + p^T z) (Sherman-Morrison for M + p p^T);
+ * alphahat = A khat / |A khat|; S = S + (v - S khat) alphahat^T; y = S qhat.
+ *
+ * Conventions shared by both entry points.
+ *   Layouts (row-major, contiguous): per-token streams [B,T,H,n] (n = dk for
+ *   q, k, erase_b and Kimi Delta's alpha; n = dv for v, write_w, out; n = d
+ *   for VLA's q, k, v, p, out); per-token scalars (beta, scalar alpha)
+ *   [B,T,H]; states [B,H,dv,dk] (VLA: A and S [B,H,d,d]).
+ *   dtype: every per-token stream and `out` share one storage dtype
+ *   (LAM_F32 or LAM_BF16); states are always fp32; all arithmetic is fp32.
+ *   alpha is the decay itself, in [0, 1]; beta, erase_b, write_w are used as
+ *   given (gate squashing happens upstream).  Delta-rule q and k are used as
+ *   given (normalise upstream); VLA takes raw q and k.
+ *   Pointers: device memory owned by the caller.  The library allocates no
+ *   device memory, keeps no pointer after returning, and uses no workspace.
+ *   A NULL initial state means zero memory (VLA: A = I, S = 0); a NULL
+ *   final-state pointer means the final state is not written.  A final-state
+ *   buffer may be the same buffer as its initial state; `out` must not
+ *   overlap any input (checked).
+ *   Errors: all argument checks happen before any HIP call and return
+ *   LAM_ERR_INVALID_ARG (NULL required pointer, negative size, size overflow,
+ *   bad enum, overlapping out) or LAM_ERR_UNSUPPORTED (head size outside
+ *   {32, 64, 96, 128}, or an algorithm not built for this variant and dtype).
+ *   Work is enqueued on `stream` (NULL = default stream) and the call returns
+ *   at once; a failed launch returns LAM_ERR_HIP, and faults during execution
+ *   surface at the caller's next synchronisation.  No exception crosses the
+ *   ABI and the library prints nothing.  Calls are re-entrant and results are
+ *   bitwise reproducible run to run.
+ */
+#ifndef LAM_H
+#define LAM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LAM_DELTANET = 0,         /* alpha = 1                                      */
+    LAM_GATED_DELTANET = 1,   /* alpha [B,T,H]                                  */
+    LAM_KIMI_DELTA = 2,       /* alpha [B,T,H,dk]                               */
+    LAM_GATED_DELTANET2 = 3   /* alpha [B,T,H], erase_b [B,T,H,dk], write_w [B,T,H,dv] */
+} lam_variant;
+
+typedef enum { LAM_F32 = 0, LAM_BF16 = 1 } lam_dtype;
+
+typedef enum {
+    LAM_OK = 0,
+    LAM_ERR_INVALID_ARG = 1,
+    LAM_ERR_UNSUPPORTED = 2,
+    LAM_ERR_HIP = 3
+} lam_status;
+
+/* Evaluation schedule.  Both compute the same scan; they differ only in
+ * rounding order.  AUTO picks the fastest built one for the shape. */
+typedef enum {
+    LAM_ALGO_AUTO = 0,
+    LAM_ALGO_RECURRENT = 1,   /* token by token, memory in registers           */
+    LAM_ALGO_CHUNKED = 2      /* chunkwise-parallel, matrix-core contractions   */
+} lam_algo;
+
+/*
+ * Delta-rule family forward scan over a [B,T] block (see the rules above).
+ *   variant      lam_variant
+ *   dtype        lam_dtype of q, k, v, alpha, beta, erase_b, write_w, out
+ *   B, T, H      batch, tokens, heads (>= 0; any of them 0 is a no-op except
+ *                that T = 0 still copies the initial state to state_out)
+ *   dk, dv       key and value head sizes, each in {32, 64, 96, 128}
+ *   q, k         [B,T,H,dk]                         required
+ *   v            [B,T,H,dv]                         required
+ *   alpha        [B,T,H] or, for Kimi Delta, [B,T,H,dk]; ignored by DeltaNet
+ *   erase_b      [B,T,H,dk], Gated DeltaNet-2 only (ignored otherwise)
+ *   write_w      [B,T,H,dv], Gated DeltaNet-2 only (ignored otherwise)
+ *   beta         [B,T,H]                            required
+ *   state_in     [B,H,dv,dk] fp32 or NULL (zero memory)
+ *   out          [B,T,H,dv]                         required, written
+ *   state_out    [B,H,dv,dk] fp32 or NULL; may equal state_in
+ *   algo         lam_algo
+ *   stream       HIP stream the work is enqueued on
+ */
+lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                       int64_t dv, const void *q, const void *k, const void *v,
+                       const void *alpha, const void *erase_b, const void *write_w,
+                       const void *beta, const float *state_in, void *out, float *state_out,
+                       int algo, hipStream_t stream);
+
+/*
+ * VLA forward scan over a [B,T] block (dk = dv = d, d in {32, 64, 96, 128}).
+ *   q, k, v, p   [B,T,H,d] raw queries, keys, values and penalty directions
+ *   A_in, S_in   [B,H,d,d] fp32 or NULL (A = I, S = 0)
+ *   out          [B,T,H,d] written
+ *   A_out, S_out [B,H,d,d] fp32 or NULL; each may equal its input buffer
+ */
+lam_status lam_vla_forward(int dtype, int64_t B, int64_t T, int64_t H, int64_t d,
+                           const void *q, const void *k, const void *v, const void *p,
+                           const float *A_in, const float *S_in, void *out, float *A_out,
+                           float *S_out, int algo, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *lam_status_string(lam_status status);
+
+/* ABI version of this header (major * 100 + minor). */
+int lam_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAM_H */

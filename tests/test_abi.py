@@ -1,0 +1,127 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/lam.h declares, and rejects bad arguments before any HIP call.
+
+Pointers passed here are never dereferenced: every call below must fail (or
+return early for an empty batch) during host-side validation.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lam.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+FAKE = 0x7F0000000000  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gated_linear_attention_chunked_amd as lam
+
+    if not os.path.exists(lam.LIB_PATH):
+        from gated_linear_attention_chunked_amd import build
+
+        build.build()
+    return lam.library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lam_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"lam_forward", "lam_vla_forward", "lam_status_string", "lam_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    for s in range(4):
+        assert lib.lam_status_string(s)
+    assert lib.lam_status_string(99) == b"unknown status"
+    assert lib.lam_abi_version() == 100
+
+
+def _fwd(lib, variant=1, dtype=1, B=2, T=8, H=2, dk=64, dv=64, q=FAKE, k=FAKE + 0x10000000,
+         v=FAKE + 0x20000000, alpha=FAKE + 0x30000000, eb=FAKE + 0x40000000,
+         ww=FAKE + 0x50000000, beta=FAKE + 0x60000000, sin=None, out=FAKE + 0x70000000,
+         sout=None, algo=0):
+    return lib.lam_forward(variant, dtype, B, T, H, dk, dv, q, k, v, alpha, eb, ww, beta, sin,
+                           out, sout, algo, None)
+
+
+def test_forward_rejects_bad_enums(lib):
+    assert _fwd(lib, variant=4) == INVALID
+    assert _fwd(lib, variant=-1) == INVALID
+    assert _fwd(lib, dtype=2) == INVALID
+    assert _fwd(lib, algo=3) == INVALID
+
+
+def test_forward_rejects_bad_sizes(lib):
+    assert _fwd(lib, B=-1) == INVALID
+    assert _fwd(lib, T=-1) == INVALID
+    assert _fwd(lib, H=-1) == INVALID
+    assert _fwd(lib, dk=0) == INVALID
+    assert _fwd(lib, dv=-4) == INVALID
+    assert _fwd(lib, dk=48) == UNSUPPORTED
+    assert _fwd(lib, dv=256) == UNSUPPORTED
+    assert _fwd(lib, B=1 << 40, T=1 << 30) == INVALID       # element count overflows
+    assert _fwd(lib, B=1 << 20, H=1 << 10) == INVALID       # too many chains for one grid
+
+
+def test_forward_rejects_missing_pointers(lib):
+    for name in ("q", "k", "v", "beta", "out"):
+        assert _fwd(lib, **{name: None}) == INVALID, name
+    assert _fwd(lib, alpha=None) == INVALID                    # gated variant
+    assert _fwd(lib, variant=2, alpha=None) == INVALID         # Kimi Delta
+    assert _fwd(lib, variant=3, eb=None) == INVALID            # Gated DeltaNet-2
+    assert _fwd(lib, variant=3, ww=None) == INVALID
+
+
+def test_forward_rejects_overlapping_output(lib):
+    assert _fwd(lib, out=FAKE + 64) == INVALID                 # out inside q
+    assert _fwd(lib, sin=FAKE + 0x70000000 + 128) == INVALID   # state_in inside out
+    assert _fwd(lib, sin=FAKE + 0x80000000, sout=FAKE + 0x80000000 + 256) == INVALID
+
+
+def test_forward_empty_batch_is_a_noop(lib):
+    # no work, so no HIP call: returns before touching the device
+    assert _fwd(lib, B=0, q=None, k=None, v=None, beta=None, out=None) == OK
+    assert _fwd(lib, H=0, q=None, k=None, v=None, beta=None, out=None) == OK
+    assert _fwd(lib, T=0, q=None, k=None, v=None, beta=None, out=None, sout=None) == OK
+
+
+def _vla(lib, dtype=0, B=1, T=8, H=2, d=32, q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000,
+         p=FAKE + 0x30000000, Ain=None, Sin=None, out=FAKE + 0x40000000, Aout=None, Sout=None,
+         algo=0):
+    return lib.lam_vla_forward(dtype, B, T, H, d, q, k, v, p, Ain, Sin, out, Aout, Sout, algo,
+                               None)
+
+
+def test_vla_rejects_bad_arguments(lib):
+    assert _vla(lib, dtype=5) == INVALID
+    assert _vla(lib, algo=7) == INVALID
+    assert _vla(lib, B=-1) == INVALID
+    assert _vla(lib, d=40) == UNSUPPORTED
+    assert _vla(lib, d=0) == INVALID
+    for name in ("q", "k", "v", "p", "out"):
+        assert _vla(lib, **{name: None}) == INVALID, name
+    assert _vla(lib, out=FAKE + 4) == INVALID
+    assert _vla(lib, Aout=FAKE + 0x50000000, Sout=FAKE + 0x50000000 + 64) == INVALID
+    assert _vla(lib, B=0, q=None, k=None, v=None, p=None, out=None) == OK
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+
+    import gated_linear_attention_chunked_amd as lam
+
+    q = torch.zeros(1, 4, 1, 32)
+    with pytest.raises(ValueError):
+        lam.forward("deltanet", q, q, q, torch.zeros(1, 4, 1))

@@ -1,0 +1,174 @@
+"""GPU parity: the HIP scan (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Small cases compare every element; the full-size
+workloads run at their real shapes and compare sampled (b, h) chains, which
+the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+from gated_linear_attention_chunked_amd import inputs as I
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+DELTA = ["deltanet", "gdn", "kda", "gdn2"]
+SHAPES = [(32, 32), (64, 64), (96, 96), (128, 128), (128, 64), (64, 128), (32, 96)]
+
+
+def _w(variant, dtype, B, T, H, dk, dv, seed, gate_mu=2.0):
+    return I.Workload(f"{variant}_{dtype}_B{B}_T{T}_H{H}_dk{dk}_dv{dv}", variant, dtype, B, T, H,
+                      dk, dv, seed=seed, gate_mu=gate_mu)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    import gated_linear_attention_chunked_amd as lam
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    lam.library()
+
+
+@pytest.mark.parametrize("algo", ["recurrent", "auto"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", DELTA)
+@pytest.mark.parametrize("dk,dv", SHAPES)
+def test_delta_small(variant, dtype, dk, dv, algo):
+    """Every element, ragged length spanning several tiles, weak and strong
+    decays mixed across heads by the seed, non-zero initial state."""
+    w = _w(variant, dtype, 2, 83, 3, dk, dv, seed=1000 + dk + dv, gate_mu=-1.0)
+    x = I.make_inputs(w)
+    s0 = np.random.default_rng(5).standard_normal((2, 3, dv, dk)) * 0.2
+    s0 = s0.astype(np.float32).astype(np.float64)
+    got = U.run_gpu(w, x, algo=algo, state_in=s0)
+    ref = U.run_oracle(w, x, state_in=s0)
+    U.check(w, got, ref, label=w.name, exact_f32=(algo == "recurrent"))
+
+
+@pytest.mark.parametrize("variant", DELTA)
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 130])
+def test_delta_lengths(variant, T):
+    w = _w(variant, "bf16", 1, T, 2, 128, 128, seed=2000 + T, gate_mu=-4.0)
+    x = I.make_inputs(w)
+    U.check(w, U.run_gpu(w, x), U.run_oracle(w, x), label=w.name)
+
+
+@pytest.mark.parametrize("variant", DELTA)
+def test_weak_decay_long(variant):
+    """alpha ~ 0.98: the memory spans hundreds of tokens, so a dropped or
+    mis-ordered state carry cannot hide behind fast forgetting."""
+    w = _w(variant, "bf16", 2, 700, 2, 128, 128, seed=3000, gate_mu=-4.0)
+    x = I.make_inputs(w)
+    U.check(w, U.run_gpu(w, x), U.run_oracle(w, x), label=w.name)
+
+
+@pytest.mark.parametrize("variant", DELTA)
+def test_empty_sequence_copies_state(variant):
+    import torch
+
+    import gated_linear_attention_chunked_amd as lam
+
+    w = _w(variant, "f32", 2, 0, 2, 64, 64, seed=1)
+    x = I.make_inputs(w)
+    g = I.to_device(x, "f32", "cuda")
+    s0 = torch.randn(2, 2, 64, 64, device="cuda")
+    out, st = lam.forward(variant, g["q"], g["k"], g["v"], g["beta"], alpha=g.get("alpha"),
+                          erase_b=g.get("erase_b"), write_w=g.get("write_w"), state_in=s0)
+    torch.cuda.synchronize()
+    assert out.shape == (2, 0, 2, 64)
+    assert torch.equal(st, s0)
+
+
+@pytest.mark.parametrize("variant", DELTA)
+def test_chained_calls_and_in_place_state(variant):
+    """[0, T) in one call equals two calls chained through the state, with the
+    second call updating its state buffer in place."""
+    import torch
+
+    import gated_linear_attention_chunked_amd as lam
+
+    w = _w(variant, "bf16", 2, 200, 2, 128, 128, seed=4000, gate_mu=-3.0)
+    x = I.make_inputs(w)
+    g = I.to_device(x, w.dtype, "cuda")
+    ks = [k for k in ("q", "k", "v", "beta", "alpha", "erase_b", "write_w") if k in g]
+    full_out, full_st = lam.forward(variant, **{k: g[k] for k in ks})
+    a = {k: g[k][:, :77].contiguous() for k in ks}
+    b = {k: g[k][:, 77:].contiguous() for k in ks}
+    o1, st = lam.forward(variant, **a)
+    o2, st2 = lam.forward(variant, **b, state_in=st, state_out=st)
+    torch.cuda.synchronize()
+    assert st2.data_ptr() == st.data_ptr()
+    got = (torch.cat([o1, o2], 1).float().cpu().numpy().astype(np.float64),
+           st.cpu().numpy().astype(np.float64))
+    ref = U.run_oracle(w, x)
+    U.check(w, got, ref, label="chained " + variant)
+    d = (torch.cat([o1, o2], 1).float() - full_out.float()).abs().max().item()
+    assert d <= 2e-2
+
+
+@pytest.mark.parametrize("variant", DELTA)
+def test_bitwise_reproducible(variant):
+    import torch
+
+    w = _w(variant, "bf16", 2, 300, 4, 128, 128, seed=5000, gate_mu=0.0)
+    x = I.make_inputs(w)
+    r1 = U.run_gpu(w, x)
+    r2 = U.run_gpu(w, x)
+    for a, b in zip(r1, r2):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+def test_vla_small(d, dtype):
+    w = I.Workload(f"vla_{dtype}_B2_T75_H3_d{d}", "vla", dtype, 2, 75, 3, d, d, seed=6000 + d)
+    x = I.make_inputs(w)
+    got = U.run_gpu(w, x)
+    ref = U.run_oracle(w, x)
+    if dtype == "f32":
+        U.check(w, got, ref, label=w.name)
+    else:
+        e_abs, e_rel = U.errs(got[0], ref[0])
+        assert e_abs <= U.BF16_ABS and e_rel <= U.BF16_REL_TRIPWIRE, (e_abs, e_rel)
+        for g, r in zip(got[1:], ref[1:]):
+            assert U.errs(g, r)[1] <= 1e-4
+
+
+def test_vla_initial_state_and_chaining():
+    w = I.Workload("vla_f32_B1_T90_H2_d32", "vla", "f32", 1, 90, 2, 32, 32, seed=6100)
+    x = I.make_inputs(w)
+    ref = U.run_oracle(w, x)
+    first = {k: v[:, :40] for k, v in x.items()}
+    second = {k: v[:, 40:] for k, v in x.items()}
+    w1, w2 = w.replace(T=40), w.replace(T=50)
+    g1 = U.run_gpu(w1, first)
+    g2 = U.run_gpu(w2, second, A_in=g1[1], S_in=g1[2])
+    got = (np.concatenate([g1[0], g2[0]], 1), g2[1], g2[2])
+    U.check(w, got, ref, label="vla chained")
+
+
+# ------------------------------------------------------------ full sizes
+FULL_CHAINS = {
+    "deltanet_f32_B1_T256_H2_d32": None,                        # every chain
+    "gdn_bf16_B8_T4096_H8_d128": [(0, 0), (3, 5), (7, 7), (5, 2)],
+    "kda_bf16_B2_T32768_H8_d128": [(0, 3), (1, 6)],
+    "gdn2_bf16_B8_T4096_H8_d128": [(0, 1), (6, 4), (7, 7)],
+    "vla_f32_B4_T4096_H8_d32": [(0, 0), (2, 5), (3, 7)],
+    "vla_f32_B4_T4096_H8_d96": [(1, 1), (3, 6)],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_CHAINS))
+def test_full_workload(name):
+    """The real shapes, in the launch configuration the benchmark times
+    (algo auto), compared on sampled chains."""
+    w = I.WORKLOADS[name]
+    x = I.make_inputs(w)
+    got = U.run_gpu(w, x)
+    chains = FULL_CHAINS[name]
+    ref = U.run_oracle(w, x, chains=chains)
+    if chains is not None:
+        got = U.pick_chains(got, chains)
+    rep = U.check(w, got, ref, label=name)
+    print(name, rep)
