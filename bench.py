@@ -1,0 +1,238 @@
+"""Throughput benchmark of the recurrent-memory forward scan on one MI355X.
+
+Default workload: Gated DeltaNet, bf16 token streams, fp32 state,
+B=8 T=4096 H=8 dk=dv=128 (one 350M-class layer's heads at sequence 4096).
+A step is one full forward scan of that batch (one lam_forward call) with
+its inputs already resident in HBM.  W untimed warm-up steps are followed by
+exactly K timed steps between two device synchronisations.  Steps rotate
+over three copies of the inputs (3 x 270 MB > the 256 MB last-level cache), so
+no step is served from cache by its predecessor.
+
+Printed: one JSON line with tokens/s (tokens = B*T), the roofline object of
+the scan kernel (algorithmic bytes per launch / mean launch time from HIP
+events on the launch stream, against 8 TB/s HBM) and the fp64 oracle timed
+on host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 matrix-core peak
+FP32_PEAK_TFS = 157.3
+
+
+def algorithmic_bytes(w) -> int:
+    """Every input read once, out and the final state written once (no
+    initial state), in the storage dtype."""
+    es = 2 if w.dtype == "bf16" else 4
+    n_th = w.B * w.T * w.H
+    if w.variant == "vla":
+        per = 5 * w.dk * es                                   # q, k, v, p, out
+        state = 2 * w.B * w.H * w.dk * w.dk * 4               # A_out, S_out
+        return n_th * per + state
+    per = (2 * w.dk + 2 * w.dv + 1) * es                     # q, k, v, out, beta
+    if w.variant in ("gdn", "gdn2"):
+        per += es                                            # scalar alpha
+    if w.variant == "kda":
+        per += w.dk * es                                     # per-channel alpha
+    if w.variant == "gdn2":
+        per += (w.dk + w.dv) * es                            # erase, write
+    return n_th * per + w.B * w.H * w.dv * w.dk * 4          # + state_out
+
+
+def algorithmic_flops(w) -> int:
+    """The recurrence's own work per token-head: predict (2 dk dv), decay +
+    write (3 dk dv), read (2 dk dv); VLA 12 d^2."""
+    n_th = w.B * w.T * w.H
+    if w.variant == "vla":
+        return n_th * 12 * w.dk * w.dk
+    return n_th * 7 * w.dk * w.dv
+
+
+def cpu_threads(chains: int) -> int:
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    cap = int(os.environ.get("OMP_NUM_THREADS", avail) or avail)
+    return max(1, min(avail, cap, chains))
+
+
+def cpu_baseline(w, x, batch_rows: int):
+    """The fp64 oracle on the first `batch_rows` batch rows (all heads, all
+    tokens) of the same inputs; tokens/s scaled to those B*T tokens."""
+    import oracle
+
+    sl = {k: v[:batch_rows] for k, v in x.items()}
+    chains = batch_rows * w.H
+    th = cpu_threads(chains)
+    t0 = time.perf_counter()
+    if w.variant == "vla":
+        oracle.vla_forward(sl["q"], sl["k"], sl["v"], sl["p"], nthreads=th)
+    else:
+        oracle.delta_forward(w.variant, sl["q"], sl["k"], sl["v"], sl["beta"], alpha=sl.get("alpha"),
+                             erase_b=sl.get("erase_b"), write_w=sl.get("write_w"), nthreads=th)
+    dt = time.perf_counter() - t0
+    return {"value": batch_rows * w.T / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
+            "sample": f"fp64 token-by-token oracle on batch rows 0..{batch_rows - 1} of {w.B} "
+                      f"(all {w.H} heads, all {w.T} tokens: {chains} chains, "
+                      f"{batch_rows * w.T} tokens) of the same inputs; {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: Gated DeltaNet B8 T4096 H8 d128)")
+    ap.add_argument("--algo", default="auto", choices=["auto", "recurrent", "chunked"])
+    ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="batch rows timed on the CPU oracle (default: the whole workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=1024,
+                    help="size of the plain device copy timed beside the scan (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the scan shards over (batch, head) chains with no communication; see the "
+              "design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_linear_attention_chunked_amd as lam
+    from gated_linear_attention_chunked_amd import inputs as I
+
+    if not os.path.exists(lam.LIB_PATH):
+        from gated_linear_attention_chunked_amd import build as _b
+
+        _b.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    name = args.workload or I.METRIC_WORKLOAD
+    w = I.WORKLOADS[name]
+    x = I.make_inputs(w)
+    dev = torch.device("cuda:0")
+    copies = [I.to_device(x, w.dtype, dev) for _ in range(max(1, args.copies))]
+    outs = []
+    for g in copies:
+        if w.variant == "vla":
+            outs.append((torch.empty((w.B, w.T, w.H, w.dv), dtype=g["q"].dtype, device=dev),
+                         torch.empty((w.B, w.H, w.dk, w.dk), dtype=torch.float32, device=dev),
+                         torch.empty((w.B, w.H, w.dk, w.dk), dtype=torch.float32, device=dev)))
+        else:
+            outs.append((torch.empty((w.B, w.T, w.H, w.dv), dtype=g["q"].dtype, device=dev),
+                         torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        g, o = copies[i % len(copies)], outs[i % len(outs)]
+        if w.variant == "vla":
+            lam.vla_forward(g["q"], g["k"], g["v"], g["p"], algo=args.algo, out=o[0], A_out=o[1],
+                            S_out=o[2])
+        else:
+            lam.forward(w.variant, g["q"], g["k"], g["v"], g["beta"], alpha=g.get("alpha"),
+                        erase_b=g.get("erase_b"), write_w=g.get("write_w"), algo=args.algo,
+                        out=o[0], state_out=o[1])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+
+    tokens = w.B * w.T
+    value = tokens * args.steps / wall
+    if w.variant == "vla":
+        ran = "recurrent"
+    else:
+        ran = args.algo if args.algo != "auto" else lam.select_algo(w.variant, w.dtype, w.T, w.dk, w.dv)
+    # arithmetic type: the recurrent schedule and fp32 storage compute in fp32;
+    # the chunked schedule on bf16 storage feeds bf16 operands to the matrix
+    # cores (fp32 accumulate, fp32 state)
+    arith_dtype = "bf16" if (ran == "chunked" and w.dtype == "bf16") else "f32"
+    mean_launch_s = float(np.mean(launch_ms)) / 1e3
+    abytes = algorithmic_bytes(w)
+    aflops = algorithmic_flops(w)
+    achieved_gbs = abytes / mean_launch_s / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                "algorithmic_bytes_per_launch": abytes,
+                "mean_launch_us": mean_launch_s * 1e6,
+                "median_launch_us": float(np.median(launch_ms)) * 1e3,
+                "min_launch_us": float(np.min(launch_ms)) * 1e3,
+                "algorithmic_tflops": aflops / mean_launch_s / 1e12}
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(10)]
+        for a, b in ce:
+            a.record(stream)
+            dst.copy_(src)
+            b.record(stream)
+        torch.cuda.synchronize()
+        cms = float(np.median([a.elapsed_time(b) for a, b in ce]))
+        roofline["copy_probe"] = {"bytes": 2 * n * 4, "median_us": cms * 1e3,
+                                  "GB/s": 2 * n * 4 / (cms / 1e3) / 1e9}
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows = min(w.B, args.cpu_rows or w.B)
+        cpu = cpu_baseline(w, x, rows)
+
+    line = {
+        "metric": "gated delta-rule fwd tokens/s, B8 T4096 H8 d128; % of HBM/MFMA roofline"
+        if name == I.METRIC_WORKLOAD else f"{w.variant} fwd tokens/s, {name}",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": arith_dtype,
+        "data": "synthetic (seeded Gaussian activations, no dataset)",
+        "config": {"workload": name, "variant": w.variant, "B": w.B, "T": w.T, "H": w.H,
+                   "dk": w.dk, "dv": w.dv, "state": "fp32", "algo": ran, "storage": w.dtype,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

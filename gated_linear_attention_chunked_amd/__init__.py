@@ -16,7 +16,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["forward", "vla_forward", "library", "LamError", "VARIANTS", "ALGOS", "LIB_PATH"]
+__all__ = ["forward", "vla_forward", "select_algo", "library", "LamError", "VARIANTS", "ALGOS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblam.so")
 VARIANTS = {"deltanet": 0, "gdn": 1, "kda": 2, "gdn2": 3}
@@ -52,8 +52,18 @@ def library() -> ctypes.CDLL:
             lib.lam_status_string.argtypes = [ci]
             lib.lam_status_string.restype = ctypes.c_char_p
             lib.lam_abi_version.restype = ci
+            lib.lam_select_algo.argtypes = [ci, ci, i64, i64, i64]
+            lib.lam_select_algo.restype = ci
             _lib = lib
         return _lib
+
+
+def select_algo(variant, dtype, T, dk, dv) -> str:
+    """Name of the schedule ``algo="auto"`` runs for these arguments."""
+    r = library().lam_select_algo(VARIANTS[variant], DTYPES[dtype], T, dk, dv)
+    if r < 0:
+        raise ValueError("arguments the library would reject")
+    return {v: k for k, v in ALGOS.items()}[r]
 
 
 def _ptr(t):

@@ -48,6 +48,21 @@ const char *lam_status_string(lam_status s) {
 
 int lam_abi_version(void) { return 100; }
 
+int lam_select_algo(int variant, int dtype, int64_t T, int64_t dk, int64_t dv) {
+    if (variant < LAM_DELTANET || variant > LAM_GATED_DELTANET2) return -1;
+    if (dtype != LAM_F32 && dtype != LAM_BF16) return -1;
+    if (T < 0 || !supported_head(dk) || !supported_head(dv)) return -1;
+    lam::DeltaArgs a{};
+    a.variant = variant;
+    a.dtype = dtype;
+    a.B = 1;
+    a.T = T;
+    a.H = 1;
+    a.dk = static_cast<int>(dk);
+    a.dv = static_cast<int>(dv);
+    return (T > 0 && lam::delta_chunked_supported(a)) ? LAM_ALGO_CHUNKED : LAM_ALGO_RECURRENT;
+}
+
 lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
                        int64_t dv, const void *q, const void *k, const void *v,
                        const void *alpha, const void *erase_b, const void *write_w,

@@ -121,6 +121,14 @@ lam_status lam_vla_forward(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
                            const float *A_in, const float *S_in, void *out, float *A_out,
                            float *S_out, int algo, hipStream_t stream);
 
+/*
+ * The schedule LAM_ALGO_AUTO runs for these arguments: LAM_ALGO_RECURRENT or
+ * LAM_ALGO_CHUNKED (the chunked one computes its contractions with bf16
+ * operands and fp32 accumulation when dtype is LAM_BF16, in fp32 otherwise).
+ * Returns -1 for arguments lam_forward would reject.
+ */
+int lam_select_algo(int variant, int dtype, int64_t T, int64_t dk, int64_t dv);
+
 /* Static, NUL-terminated description of a status code. */
 const char *lam_status_string(lam_status status);
 

@@ -41,6 +41,14 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_select_algo(lib):
+    assert lib.lam_select_algo(9, 1, 100, 128, 128) == -1
+    assert lib.lam_select_algo(1, 1, 100, 48, 128) == -1
+    assert lib.lam_select_algo(1, 1, 0, 128, 128) == 1          # empty: recurrent (state copy)
+    for v in range(4):
+        assert lib.lam_select_algo(v, 0, 256, 32, 32) in (1, 2)
+
+
 def test_status_strings_and_version(lib):
     for s in range(4):
         assert lib.lam_status_string(s)
