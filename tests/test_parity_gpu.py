@@ -172,3 +172,52 @@ def test_full_workload(name):
         got = U.pick_chains(got, chains)
     rep = U.check(w, got, ref, label=name)
     print(name, rep)
+
+
+# ---------------------------------------------------- chunked schedule
+CHUNKED = ["deltanet", "gdn", "gdn2"]
+
+
+@pytest.mark.parametrize("variant", CHUNKED)
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 32), (64, 96), (128, 64)])
+@pytest.mark.parametrize("T,gate_mu", [(1, 2.0), (63, -4.0), (64, 2.0), (65, -4.0), (200, 0.0),
+                                       (1000, -4.0)])
+def test_chunked_every_element(variant, dk, dv, T, gate_mu):
+    """The matrix-core chunked schedule, every element, ragged tails, strong
+    and weak decays, non-zero initial state."""
+    w = _w(variant, "bf16", 2, T, 2, dk, dv, seed=7000 + T + dk, gate_mu=gate_mu)
+    x = I.make_inputs(w)
+    s0 = (np.random.default_rng(T).standard_normal((2, 2, dv, dk)) * 0.2).astype(np.float32)
+    s0 = s0.astype(np.float64)
+    got = U.run_gpu(w, x, algo="chunked", state_in=s0)
+    ref = U.run_oracle(w, x, state_in=s0)
+    U.check(w, got, ref, label=w.name)
+
+
+@pytest.mark.parametrize("variant", ["gdn", "gdn2"])
+def test_chunked_zero_and_unit_decays(variant):
+    """alpha = 0 (memory cleared) and alpha = 1 tokens mixed into one chunk."""
+    w = _w(variant, "bf16", 1, 150, 2, 128, 128, seed=7100, gate_mu=-2.0)
+    x = I.make_inputs(w)
+    x["alpha"][:, 10:13] = 0.0
+    x["alpha"][:, 70:90] = 1.0
+    got = U.run_gpu(w, x, algo="chunked")
+    ref = U.run_oracle(w, x)
+    U.check(w, got, ref, label="zero/unit decays " + variant)
+
+
+def test_chunked_rejects_unsupported():
+    import torch
+
+    import gated_linear_attention_chunked_amd as lam
+
+    w = _w("kda", "bf16", 1, 70, 1, 128, 128, seed=1)
+    g = I.to_device(I.make_inputs(w), "bf16", "cuda")
+    with pytest.raises(lam.LamError) as e:
+        lam.forward("kda", g["q"], g["k"], g["v"], g["beta"], alpha=g["alpha"], algo="chunked")
+    assert e.value.status == 2
+    w = _w("gdn", "f32", 1, 70, 1, 128, 128, seed=1)
+    g = I.to_device(I.make_inputs(w), "f32", "cuda")
+    with pytest.raises(lam.LamError):
+        lam.forward("gdn", g["q"], g["k"], g["v"], g["beta"], alpha=g["alpha"], algo="chunked")
+    torch.cuda.synchronize()
