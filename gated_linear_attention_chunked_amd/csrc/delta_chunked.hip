@@ -72,6 +72,22 @@ __device__ __forceinline__ bf16x8 row_frag(const __bf16 *m, int stride, int r0, 
     const __bf16 *p = m + (r0 + (lane & 15)) * stride + c0 + 4 * (lane >> 4);
     return cat8(lds4(p), lds4(p + 16));
 }
+// Column gather with the gfx950 LDS transpose read.  Within each 16-lane
+// group g, lane m supplies the 8-byte piece m[r0 + 4g + m/4][c0 + 4(m%4) ..]
+// and lane i receives m[r0 + 4g + j][c0 + i] in slot j = 0..3: four
+// consecutive rows of one column, i.e. the accumulator-order operand of a
+// reduction over rows, read from a row-major tile.
+__device__ __forceinline__ bf16x4 col_gather4(const __bf16 *m, int stride, int r0, int c0, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const __bf16 *p = m + (r0 + 4 * g + (i >> 2)) * stride + c0 + 4 * (i & 3);
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
+}
+// A operand of a 16x16x32 product contracting over rows r0..r0+31 of a
+// row-major tile, for output rows = columns c0..c0+15 (accumulator order).
+__device__ __forceinline__ bf16x8 col_frag(const __bf16 *m, int stride, int r0, int c0, int lane) {
+    return cat8(col_gather4(m, stride, r0, c0, lane), col_gather4(m, stride, r0 + 16, c0, lane));
+}
 // A operand of a 16x16x16 product: the 16x16 block at (r0, c0).
 __device__ __forceinline__ bf16x4 blk_frag(const __bf16 *m, int stride, int r0, int c0, int lane) {
     return lds4(m + (r0 + (lane & 15)) * stride + c0 + 4 * (lane >> 4));
@@ -422,11 +438,11 @@ constexpr int NLB = 6;  // strictly lower 16x16 blocks of a 64-row chunk
 template <int DK>
 struct PipeLds {
     static constexpr int KS = DK + 8;
+    static constexpr int VS = BV + 8;
     struct Raw {  // staged token streams of one chunk
         alignas(16) __bf16 q[C * KS];
         alignas(16) __bf16 k[C * KS];
-        alignas(16) __bf16 kt[DK * CS];  // keys transposed: [dk][t]
-        alignas(16) __bf16 vt[BV * CS];  // values transposed: [v][t]
+        alignas(16) __bf16 v[C * VS];    // the workgroup's value columns
         alignas(16) float la[C];         // log2 of the decay (0 for padding)
         alignas(16) float beta[C];
     };
@@ -447,6 +463,31 @@ struct PipeLds {
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier that orders LDS only: outstanding global loads (the
+// producers' prefetch) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (fixed order of additions, so it is bitwise reproducible).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_shift(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp_shift<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_shift<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_shift<0x114, 0xf>(x);  // row_shr:4
+    x += dpp_shift<0x118, 0xf>(x);  // row_shr:8
+    x += dpp_shift<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_shift<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
 
 // Bounded wait until `*cnt` reaches `target` (both producers have arrived).
 // Every wave leaves the loop after at most 2^22 polls, so a lost arrival can
@@ -506,31 +547,41 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
                 St[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
-        __syncthreads();  // chunk 0 staged and derived
+        lds_barrier();  // chunk 0 staged and derived
         for (int c = 0; c < nchunks; ++c) {
             const typename Lds::Raw &R = s.raw[c & 1];
             const typename Lds::Der &D = s.der[c & 1];
             bf16x8 bS[KSTEP];
 #pragma unroll
             for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(bf4(St[2 * p]), bf4(St[2 * p + 1]));
-            f32x4 rhs[4], y[4];
+            f32x4 kp[4], qp[4], rhs[4], y[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) kp[ti] = qp[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < KSTEP; ++p) {
+                bf16x8 kf[4], qf[4];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    kf[ti] = row_frag(R.k, KS, 16 * ti, 32 * p, lane);
+                    qf[ti] = row_frag(R.q, KS, 16 * ti, 32 * p, lane);
+                }
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    kp[ti] = mfma32(kf[ti], bS[p], kp[ti]);
+                    qp[ti] = mfma32(qf[ti], bS[p], qp[ti]);
+                }
+            }
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
-                f32x4 kp = {0.f, 0.f, 0.f, 0.f}, qp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < KSTEP; ++p) {
-                    kp = mfma32(row_frag(R.k, KS, 16 * ti, 32 * p, lane), bS[p], kp);
-                    qp = mfma32(row_frag(R.q, KS, 16 * ti, 32 * p, lane), bS[p], qp);
-                }
                 const int t = 16 * ti + 4 * lg;
-                const bf16x4 z = lds4(&R.vt[(16 * vt + lc) * CS + t]);
+                const bf16x4 z = col_gather4(R.v, Lds::VS, 16 * ti, 16 * vt, lane);
                 const float4 be = *reinterpret_cast<const float4 *>(&D.beta[t]);
                 const float4 ga = *reinterpret_cast<const float4 *>(&D.gam[t]);
                 const float bb[4] = {be.x, be.y, be.z, be.w}, gg[4] = {ga.x, ga.y, ga.z, ga.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    rhs[ti][r] = bb[r] * fmaf(-gg[r], kp[r], static_cast<float>(z[r]));
-                    y[ti][r] = gg[r] * qp[r];
+                    rhs[ti][r] = bb[r] * fmaf(-gg[r], kp[ti][r], static_cast<float>(z[r]));
+                    y[ti][r] = gg[r] * qp[ti][r];
                 }
             }
             // blockwise forward solve U_i = D_i (R_i - sum_{j<i} L_ij U_j)
@@ -559,22 +610,34 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
             const f32x4 us3 = u[3] * f32x4{s3.x, s3.y, s3.z, s3.w};
             const bf16x8 bW0 = cat8(bf4(us0), bf4(us1)), bW1 = cat8(bf4(us2), bf4(us3));
             const float gC = D.gam[C - 1];
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                f32x4 acc = St[kt] * gC;
-                acc = mfma32(row_frag(R.kt, CS, 16 * kt, 0, lane), bW0, acc);
-                acc = mfma32(row_frag(R.kt, CS, 16 * kt, 32, lane), bW1, acc);
-                St[kt] = acc;
-            }
             const bf16x8 bU0 = cat8(ub[0], ub[1]), bU1 = cat8(ub[2], ub[3]);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) St[kt] = St[kt] * gC;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const bf16x8 bW = h2 ? bW1 : bW0;
+                bf16x8 af[KT];
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) af[kt] = col_frag(R.k, KS, 32 * h2, 16 * kt, lane);
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) St[kt] = mfma32(af[kt], bW, St[kt]);
+            }
+            {
+                bf16x8 yf[6];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) yf[ti] = row_frag(D.aqk, CS, 16 * ti, 0, lane);
+                yf[4] = row_frag(D.aqk, CS, 32, 32, lane);
+                yf[5] = row_frag(D.aqk, CS, 48, 32, lane);
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) y[ti] = mfma32(yf[ti], bU0, y[ti]);
+                y[2] = mfma32(yf[4], bU1, y[2]);
+                y[3] = mfma32(yf[5], bU1, y[3]);
+            }
             __bf16 *ys = s.ys[vt];
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                y[ti] = mfma32(row_frag(D.aqk, CS, 16 * ti, 0, lane), bU0, y[ti]);
-                if (ti >= 2) y[ti] = mfma32(row_frag(D.aqk, CS, 16 * ti, 32, lane), bU1, y[ti]);
+            for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) ys[(16 * ti + 4 * lg + r) * 24 + lc] = static_cast<__bf16>(y[ti][r]);
-            }
             // each lane stores one 32-byte output row segment
             const int t0 = c * C;
             if (t0 + lane < T) {
@@ -583,7 +646,7 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
                 dst[0] = src[0];
                 dst[1] = src[1];
             }
-            __syncthreads();
+            lds_barrier();
         }
         if (a.state_out) {
 #pragma unroll
@@ -599,81 +662,78 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
         const uint16_t *gv = static_cast<const uint16_t *>(a.v);
         const uint16_t *gsc = static_cast<const uint16_t *>(pw == 0 ? a.alpha : a.beta);
         uint4 rq[QL], rk[QL], rv[2];
-        float rs = 0.f;
+        uint32_t rs = 0u;   // raw bf16 bits of the decay (pw 0) or beta (pw 1)
+        bool rok = false;   // this lane's row lies inside the sequence
+        // Loads read a clamped, always valid row; rows past the end are
+        // replaced by padding at commit, so no loaded value is consumed here
+        // and the loads stay in flight until the next chunk's staging.
         auto fetch = [&](int c) {  // lane = token row of chunk c
             const int t = c * C + lane;
-            const bool ok = t < T;
-            const int64_t o = tok(t);
+            rok = t < T;
+            const int64_t o = tok(min(t, T - 1));
 #pragma unroll
             for (int i = 0; i < QL; ++i) {
-                rq[i] = ok ? *reinterpret_cast<const uint4 *>(gq + o * DK + pw * HALF + 8 * i) : make_uint4(0, 0, 0, 0);
-                rk[i] = ok ? *reinterpret_cast<const uint4 *>(gk + o * DK + pw * HALF + 8 * i) : make_uint4(0, 0, 0, 0);
+                rq[i] = *reinterpret_cast<const uint4 *>(gq + o * DK + pw * HALF + 8 * i);
+                rk[i] = *reinterpret_cast<const uint4 *>(gk + o * DK + pw * HALF + 8 * i);
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                rv[i] = ok ? *reinterpret_cast<const uint4 *>(gv + o * dv + v0 + 16 * pw + 8 * i) : make_uint4(0, 0, 0, 0);
-            if (pw == 0)
-                rs = (kDecay && ok) ? bf16_bits_to_f32(gsc[o]) : 1.f;  // decay (log taken at commit)
-            else
-                rs = ok ? bf16_bits_to_f32(gsc[o]) : 0.f;
+            for (int i = 0; i < 2; ++i) rv[i] = *reinterpret_cast<const uint4 *>(gv + o * dv + v0 + 16 * pw + 8 * i);
+            if (pw == 1 || kDecay) rs = static_cast<uint32_t>(gsc[o]);
         };
         auto commit = [&](int c) {
             typename Lds::Raw &R = s.raw[c & 1];
             const int t = lane;
+            if (!rok) {
+                const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < QL; ++i) rq[i] = rk[i] = z;
+                rv[0] = rv[1] = z;
+            }
 #pragma unroll
             for (int i = 0; i < QL; ++i) {
                 *reinterpret_cast<uint4 *>(&R.q[t * KS + pw * HALF + 8 * i]) = rq[i];
                 *reinterpret_cast<uint4 *>(&R.k[t * KS + pw * HALF + 8 * i]) = rk[i];
-                const uint32_t w4[4] = {rk[i].x, rk[i].y, rk[i].z, rk[i].w};
-                uint16_t *ktp = reinterpret_cast<uint16_t *>(R.kt);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    ktp[(pw * HALF + 8 * i + 2 * j) * CS + t] = static_cast<uint16_t>(w4[j] & 0xffffu);
-                    ktp[(pw * HALF + 8 * i + 2 * j + 1) * CS + t] = static_cast<uint16_t>(w4[j] >> 16);
-                }
             }
-            uint16_t *vtp = reinterpret_cast<uint16_t *>(R.vt);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint32_t w4[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    vtp[(16 * pw + 8 * i + 2 * j) * CS + t] = static_cast<uint16_t>(w4[j] & 0xffffu);
-                    vtp[(16 * pw + 8 * i + 2 * j + 1) * CS + t] = static_cast<uint16_t>(w4[j] >> 16);
-                }
+            for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4 *>(&R.v[t * Lds::VS + 16 * pw + 8 * i]) = rv[i];
+            if (pw == 0) {
+                const float al = bf16_bits_to_f32(static_cast<uint16_t>(rs));
+                R.la[t] = (kDecay && rok) ? fmaxf(__builtin_amdgcn_logf(al), -200.f) : 0.f;
+            } else {
+                R.beta[t] = rok ? bf16_bits_to_f32(static_cast<uint16_t>(rs)) : 0.f;
             }
-            if (pw == 0)
-                R.la[t] = kDecay ? fmaxf(__builtin_amdgcn_logf(rs), -200.f) : 0.f;
-            else
-                R.beta[t] = rs;
         };
         // State-independent matrices of chunk c from its staged streams.
         auto derive = [&](int c) {
             const typename Lds::Raw &R = s.raw[c & 1];
             typename Lds::Der &D = s.der[c & 1];
             // gate prefix sums (each producer keeps its own copy)
-            float g = R.la[lane];
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float y = __shfl_up(g, o, 64);
-                if (lane >= o) g += y;
-            }
+            const float g = wave_prefix_sum(R.la[lane]);
             const float gl = __shfl(g, 63, 64);
             float *gw = s.gw[pw];
             gw[lane] = g;
+            // key fragments of the four row tiles, loaded once
+            bf16x8 kf[4][KSTEP];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int p = 0; p < KSTEP; ++p) kf[ti][p] = row_frag(R.k, KS, 16 * ti, 32 * p, lane);
             if (pw == 0) {
                 D.gam[lane] = exp2_fast(g);
                 D.sc[lane] = exp2_fast(gl - g);
                 D.beta[lane] = R.beta[lane];
                 // diagonal tiles of E K^T -> L_ii (fp32), then their inverses
+                f32x4 accd[4];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) accd[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < KSTEP; ++p)
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) accd[ti] = mfma32(kf[ti][p], kf[ti][p], accd[ti]);
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int p = 0; p < KSTEP; ++p)
-                        acc = mfma32(row_frag(R.k, KS, 16 * ti, 32 * p, lane), row_frag(R.k, KS, 16 * ti, 32 * p, lane), acc);
-                    const int sidx = 16 * ti + lc;
-                    const float gs = gw[sidx];
+                    const f32x4 acc = accd[ti];
+                    const float gs = gw[16 * ti + lc];
                     const float4 gt4 = *reinterpret_cast<const float4 *>(&gw[16 * ti + 4 * lg]);
                     const float4 bt4 = *reinterpret_cast<const float4 *>(&R.beta[16 * ti + 4 * lg]);
                     const float gt[4] = {gt4.x, gt4.y, gt4.z, gt4.w}, bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
@@ -711,44 +771,56 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) D.dinv[(16 * lg + i) * DS + lc] = static_cast<__bf16>(x[i]);
             } else {
-                // strictly lower off-diagonal tiles of E K^T -> -L blocks
+                // strictly lower off-diagonal tiles of E K^T -> -L blocks, and
+                // the lower tiles of Q K^T -> Aqk; all 16 accumulators built
+                // with their chains interleaved, then masked and stored
+                bf16x8 qf[4][KSTEP];
 #pragma unroll
-                for (int blk = 0; blk < NLB; ++blk) {
-                    const int ti = blk < 1 ? 1 : (blk < 3 ? 2 : 3);
-                    const int si = blk - ti * (ti - 1) / 2;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                    for (int p = 0; p < KSTEP; ++p)
-                        acc = mfma32(row_frag(R.k, KS, 16 * ti, 32 * p, lane), row_frag(R.k, KS, 16 * si, 32 * p, lane), acc);
-                    const float gs = gw[16 * si + lc];
-                    const float4 gt4 = *reinterpret_cast<const float4 *>(&gw[16 * ti + 4 * lg]);
-                    const float4 bt4 = *reinterpret_cast<const float4 *>(&R.beta[16 * ti + 4 * lg]);
-                    const float gt[4] = {gt4.x, gt4.y, gt4.z, gt4.w}, bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+                    for (int p = 0; p < KSTEP; ++p) qf[ti][p] = row_frag(R.q, KS, 16 * ti, 32 * p, lane);
+                constexpr int TI[NLB] = {1, 2, 2, 3, 3, 3}, SI[NLB] = {0, 0, 1, 0, 1, 2};
+                f32x4 accl[NLB], accq[10];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        D.lnb[(16 * blk + 4 * lg + r) * DS + lc] =
-                            static_cast<__bf16>(-(bt[r] * exp2_fast(gt[r] - gs) * acc[r]));
+                for (int j = 0; j < NLB; ++j) accl[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 10; ++j) accq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < KSTEP; ++p) {
+#pragma unroll
+                    for (int j = 0; j < NLB; ++j) accl[j] = mfma32(kf[TI[j]][p], kf[SI[j]][p], accl[j]);
+                    int j = 0;
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                        for (int si = 0; si <= ti; ++si, ++j) accq[j] = mfma32(qf[ti][p], kf[si][p], accq[j]);
                 }
-                // lower tiles of Q K^T -> Aqk
+                float gt[4][4], bt[4][4], gs[4];
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) {
-                    const float4 gt4 = *reinterpret_cast<const float4 *>(&gw[16 * ti + 4 * lg]);
-                    const float gt[4] = {gt4.x, gt4.y, gt4.z, gt4.w};
+                    const float4 g4 = *reinterpret_cast<const float4 *>(&gw[16 * ti + 4 * lg]);
+                    const float4 b4 = *reinterpret_cast<const float4 *>(&R.beta[16 * ti + 4 * lg]);
+                    gt[ti][0] = g4.x; gt[ti][1] = g4.y; gt[ti][2] = g4.z; gt[ti][3] = g4.w;
+                    bt[ti][0] = b4.x; bt[ti][1] = b4.y; bt[ti][2] = b4.z; bt[ti][3] = b4.w;
+                    gs[ti] = gw[16 * ti + lc];
+                }
 #pragma unroll
-                    for (int si = 0; si <= ti; ++si) {
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < NLB; ++j)
 #pragma unroll
-                        for (int p = 0; p < KSTEP; ++p)
-                            acc = mfma32(row_frag(R.q, KS, 16 * ti, 32 * p, lane), row_frag(R.k, KS, 16 * si, 32 * p, lane), acc);
-                        const float gs = gw[16 * si + lc];
+                    for (int r = 0; r < 4; ++r)
+                        D.lnb[(16 * j + 4 * lg + r) * DS + lc] = static_cast<__bf16>(
+                            -(bt[TI[j]][r] * exp2_fast(gt[TI[j]][r] - gs[SI[j]]) * accl[j][r]));
+                int j = 0;
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                    for (int si = 0; si <= ti; ++si, ++j)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int tr = 4 * lg + r;
-                            const float val = (si < ti || lc <= tr) ? acc[r] * exp2_fast(gt[r] - gs) : 0.f;
+                            const float val = (si < ti || lc <= tr) ? accq[j][r] * exp2_fast(gt[ti][r] - gs[si]) : 0.f;
                             D.aqk[(16 * ti + tr) * CS + 16 * si + lc] = static_cast<__bf16>(val);
                         }
-                    }
-                }
             }
         };
 
@@ -761,7 +833,7 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
             if (nchunks > 1) fetch(1);
             derive(0);
         }
-        __syncthreads();  // chunk 0 staged and derived
+        lds_barrier();  // chunk 0 staged and derived
         for (int c = 0; c < nchunks; ++c) {
             if (c + 1 < nchunks) {
                 commit(c + 1);
@@ -770,7 +842,7 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
                 if (c + 2 < nchunks) fetch(c + 2);
                 derive(c + 1);
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
 }
