@@ -424,16 +424,25 @@ __global__ __launch_bounds__(NT) void delta_chunked_kernel(DeltaArgs a) {
 }
 
 // ===========================================================================
-// Pipelined schedule (DeltaNet, Gated DeltaNet).  Waves 0-1 ("carry") run the
-// state-dependent part of chunk c while waves 2-3 ("producers") stage chunk
-// c+1 into the other half of a double-buffered LDS set and compute its
-// state-independent matrices.  Carry and producers meet at one workgroup
-// barrier per chunk; the two producers order their staging writes before
-// their tile reads with a bounded LDS counter wait that the carry waves never
-// touch.  Producers alone issue global loads (two chunks ahead), so the carry
-// waves never wait on HBM.
+// Pipelined schedule (DeltaNet, Gated DeltaNet): 8 waves per workgroup, two
+// per SIMD, in three roles.
+//   carry  (waves 0-1, one 16-column tile of the slice each): the critical
+//          path E S^T -> right-hand side -> blockwise solve -> state update;
+//          U is published to LDS as soon as the solve ends.
+//   output (waves 2-3, same tiles): Q S^T while the carry solves, then Y from
+//          the published U, the output store, and a replica of the state
+//          update (the same MFMA sequence on the same operands, so the two
+//          copies of the state stay bit-identical without a state handoff).
+//   producers (waves 4-7): stage chunk c+1 into the other half of a
+//          double-buffered LDS set and compute its state-independent
+//          matrices, a quarter each.
+// All eight waves meet at one LDS barrier per chunk.  Producers order their
+// staging writes before their tile reads, and each output wave waits for its
+// carry wave's U, through bounded LDS counters.  Only producers issue global
+// loads (two chunks ahead), so carry waves never wait on HBM.
 // ===========================================================================
-constexpr int NLB = 6;  // strictly lower 16x16 blocks of a 64-row chunk
+constexpr int NLB = 6;     // strictly lower 16x16 blocks of a 64-row chunk
+constexpr int NT8 = 512;   // threads per workgroup of the pipelined schedule
 
 template <int DK>
 struct PipeLds {
@@ -456,10 +465,12 @@ struct PipeLds {
     };
     Raw raw[2];
     Der der[2];
-    alignas(16) float ld[4 * 272];    // diagonal blocks of L, fp32 (block stride padded)
-    alignas(16) float gw[2][C];       // per-producer copy of the gate prefix sums
-    alignas(16) __bf16 ys[2][C * 24]; // output staging, one 64x16 tile per carry wave
-    unsigned int pcount;
+    alignas(16) float ld[4 * 272];     // diagonal blocks of L, fp32 (block stride padded)
+    alignas(16) float gw[4][C];        // per-producer copy of the gate prefix sums
+    alignas(16) __bf16 ys[2][C * 24];  // output staging, one 64x16 tile per output wave
+    alignas(16) bf16x4 uh[2][4][64];   // U of the current chunk, per tile, fragment order
+    unsigned int pcount;               // producer arrivals
+    unsigned int ucount[2];            // U publications per tile
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -488,13 +499,15 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     return x;
 }
 
-
-// Bounded wait until `*cnt` reaches `target` (both producers have arrived).
-// Every wave leaves the loop after at most 2^22 polls, so a lost arrival can
-// slow the kernel down but never hang it.
-__device__ __forceinline__ void producer_sync(unsigned int *cnt, unsigned int target, int lane) {
+// Publish: make this wave's LDS writes visible, then count one arrival.
+__device__ __forceinline__ void lds_arrive(unsigned int *cnt, int lane) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Bounded wait until `*cnt` reaches `target`.  Every wave leaves the loop
+// after at most 2^22 polls, so a lost arrival can slow the kernel down but
+// never hang it.
+__device__ __forceinline__ void lds_wait(unsigned int *cnt, unsigned int target) {
     for (int it = 0; it < (1 << 22); ++it) {
         if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
         __builtin_amdgcn_s_sleep(1);
@@ -502,14 +515,52 @@ __device__ __forceinline__ void producer_sync(unsigned int *cnt, unsigned int ta
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// S^T = gamma_C S^T + K^T diag(gamma_C / gamma) U for one 16-column tile,
+// shared by the carry wave and its output-wave replica.
+template <int KT, typename Raw, typename Der>
+__device__ __forceinline__ void state_update(f32x4 (&St)[KT], const Raw &R, const Der &D, const bf16x4 (&ub)[4],
+                                             int KS, int lane) {
+    const int lg = lane >> 4;
+    f32x4 us[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 sc = *reinterpret_cast<const float4 *>(&D.sc[16 * i + 4 * lg]);
+        const f32x4 u = __builtin_convertvector(ub[i], f32x4);
+        us[i] = u * f32x4{sc.x, sc.y, sc.z, sc.w};
+    }
+    const bf16x8 bW0 = cat8(bf4(us[0]), bf4(us[1])), bW1 = cat8(bf4(us[2]), bf4(us[3]));
+    const float gC = D.gam[C - 1];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) St[kt] = St[kt] * gC;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 bW = h2 ? bW1 : bW0;
+        bf16x8 af[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) af[kt] = col_frag(R.k, KS, 32 * h2, 16 * kt, lane);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) St[kt] = mfma32(af[kt], bW, St[kt]);
+    }
+}
+
+// Lower tiles of Q K^T computed by producers 2 and 3.
+struct QkTilesLow {
+    static constexpr int n = 6;
+    static constexpr int ti[6] = {0, 1, 1, 2, 2, 2}, si[6] = {0, 0, 1, 0, 1, 2};
+};
+struct QkTilesRow3 {
+    static constexpr int n = 4;
+    static constexpr int ti[4] = {3, 3, 3, 3}, si[4] = {0, 1, 2, 3};
+};
+
 template <int VARIANT, int DK>
-__global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
+__global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
     constexpr bool kDecay = VARIANT != kDeltaNet;
     constexpr int KS = DK + 8;
     constexpr int KSTEP = DK / 32;
     constexpr int KT = DK / 16;
-    constexpr int HALF = DK / 2;          // key channels staged per producer wave
-    constexpr int QL = HALF / 8;          // 16-byte loads per row per producer
+    constexpr int QUART = DK / 4;         // key channels staged per producer wave
+    constexpr int QL = QUART / 8;         // 16-byte loads per row per producer
     using Lds = PipeLds<DK>;
     __shared__ Lds s;
 
@@ -525,16 +576,20 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
     const int nchunks = (T + C - 1) / C;
     auto tok = [&](int t) { return (static_cast<int64_t>(b) * T + t) * H + h; };
 
-    for (int i = tid; i < C * CS; i += NT) {
+    for (int i = tid; i < C * CS; i += NT8) {
         s.der[0].aqk[i] = static_cast<__bf16>(0.f);
         s.der[1].aqk[i] = static_cast<__bf16>(0.f);
     }
-    if (tid == 0) s.pcount = 0u;
-    __syncthreads();  // counter and cleared tiles visible before either role starts
+    if (tid == 0) {
+        s.pcount = 0u;
+        s.ucount[0] = s.ucount[1] = 0u;
+    }
+    __syncthreads();  // counters and cleared tiles visible before any role starts
 
-    if (wave < 2) {
-        // =============================== carry ===============================
-        const int vt = wave;
+    if (wave < 4) {
+        // ========================= carry and output ==========================
+        const bool is_carry = wave < 2;
+        const int vt = wave & 1;
         f32x4 St[KT];
         const int vcol = v0 + 16 * vt + lc;
         const int64_t sbase = (static_cast<int64_t>(head) * dv + vcol) * DK;
@@ -554,75 +609,59 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
             bf16x8 bS[KSTEP];
 #pragma unroll
             for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(bf4(St[2 * p]), bf4(St[2 * p + 1]));
-            f32x4 kp[4], qp[4], rhs[4], y[4];
+            // E S^T (carry) or Q S^T (output), four row tiles
+            const __bf16 *am = is_carry ? R.k : R.q;
+            f32x4 xp[4];
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) kp[ti] = qp[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ti = 0; ti < 4; ++ti) xp[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int p = 0; p < KSTEP; ++p) {
-                bf16x8 kf[4], qf[4];
+                bf16x8 af[4];
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    kf[ti] = row_frag(R.k, KS, 16 * ti, 32 * p, lane);
-                    qf[ti] = row_frag(R.q, KS, 16 * ti, 32 * p, lane);
-                }
+                for (int ti = 0; ti < 4; ++ti) af[ti] = row_frag(am, KS, 16 * ti, 32 * p, lane);
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    kp[ti] = mfma32(kf[ti], bS[p], kp[ti]);
-                    qp[ti] = mfma32(qf[ti], bS[p], qp[ti]);
-                }
+                for (int ti = 0; ti < 4; ++ti) xp[ti] = mfma32(af[ti], bS[p], xp[ti]);
             }
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                const int t = 16 * ti + 4 * lg;
-                const bf16x4 z = col_gather4(R.v, Lds::VS, 16 * ti, 16 * vt, lane);
-                const float4 be = *reinterpret_cast<const float4 *>(&D.beta[t]);
-                const float4 ga = *reinterpret_cast<const float4 *>(&D.gam[t]);
-                const float bb[4] = {be.x, be.y, be.z, be.w}, gg[4] = {ga.x, ga.y, ga.z, ga.w};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    rhs[ti][r] = bb[r] * fmaf(-gg[r], kp[ti][r], static_cast<float>(z[r]));
-                    y[ti][r] = gg[r] * qp[ti][r];
-                }
-            }
-            // blockwise forward solve U_i = D_i (R_i - sum_{j<i} L_ij U_j)
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            f32x4 u[4];
             bf16x4 ub[4];
-            u[0] = mfma16(blk_frag(D.dinv, DS, 0, 0, lane), bf4(rhs[0]), zero);
-            ub[0] = bf4(u[0]);
+            if (is_carry) {
+                f32x4 rhs[4];
 #pragma unroll
-            for (int i = 1; i < 4; ++i) {
-                f32x4 x = rhs[i];
+                for (int ti = 0; ti < 4; ++ti) {
+                    const int t = 16 * ti + 4 * lg;
+                    const bf16x4 z = col_gather4(R.v, Lds::VS, 16 * ti, 16 * vt, lane);
+                    const float4 be = *reinterpret_cast<const float4 *>(&D.beta[t]);
+                    const float4 ga = *reinterpret_cast<const float4 *>(&D.gam[t]);
+                    const float bb[4] = {be.x, be.y, be.z, be.w}, gg[4] = {ga.x, ga.y, ga.z, ga.w};
 #pragma unroll
-                for (int j = 0; j < i; ++j)
-                    x = mfma16(blk_frag(D.lnb, DS, 16 * (i * (i - 1) / 2 + j), 0, lane), ub[j], x);
-                u[i] = mfma16(blk_frag(D.dinv, DS, 16 * i, 0, lane), bf4(x), zero);
-                ub[i] = bf4(u[i]);
-            }
-            // state update first (the next chunk waits on it), then the output
-            const float4 s0 = *reinterpret_cast<const float4 *>(&D.sc[4 * lg]);
-            const float4 s1 = *reinterpret_cast<const float4 *>(&D.sc[16 + 4 * lg]);
-            const float4 s2 = *reinterpret_cast<const float4 *>(&D.sc[32 + 4 * lg]);
-            const float4 s3 = *reinterpret_cast<const float4 *>(&D.sc[48 + 4 * lg]);
-            const f32x4 us0 = u[0] * f32x4{s0.x, s0.y, s0.z, s0.w};
-            const f32x4 us1 = u[1] * f32x4{s1.x, s1.y, s1.z, s1.w};
-            const f32x4 us2 = u[2] * f32x4{s2.x, s2.y, s2.z, s2.w};
-            const f32x4 us3 = u[3] * f32x4{s3.x, s3.y, s3.z, s3.w};
-            const bf16x8 bW0 = cat8(bf4(us0), bf4(us1)), bW1 = cat8(bf4(us2), bf4(us3));
-            const float gC = D.gam[C - 1];
-            const bf16x8 bU0 = cat8(ub[0], ub[1]), bU1 = cat8(ub[2], ub[3]);
+                    for (int r = 0; r < 4; ++r) rhs[ti][r] = bb[r] * fmaf(-gg[r], xp[ti][r], static_cast<float>(z[r]));
+                }
+                // blockwise forward solve U_i = D_i (R_i - sum_{j<i} L_ij U_j)
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                ub[0] = bf4(mfma16(blk_frag(D.dinv, DS, 0, 0, lane), bf4(rhs[0]), zero));
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) St[kt] = St[kt] * gC;
+                for (int i = 1; i < 4; ++i) {
+                    f32x4 x = rhs[i];
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const bf16x8 bW = h2 ? bW1 : bW0;
-                bf16x8 af[KT];
+                    for (int j = 0; j < i; ++j)
+                        x = mfma16(blk_frag(D.lnb, DS, 16 * (i * (i - 1) / 2 + j), 0, lane), ub[j], x);
+                    ub[i] = bf4(mfma16(blk_frag(D.dinv, DS, 16 * i, 0, lane), bf4(x), zero));
+                }
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt) af[kt] = col_frag(R.k, KS, 32 * h2, 16 * kt, lane);
+                for (int i = 0; i < 4; ++i) s.uh[vt][i][lane] = ub[i];
+                lds_arrive(&s.ucount[vt], lane);
+                state_update<KT>(St, R, D, ub, KS, lane);
+            } else {
+                lds_wait(&s.ucount[vt], static_cast<unsigned int>(c + 1));
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt) St[kt] = mfma32(af[kt], bW, St[kt]);
-            }
-            {
+                for (int i = 0; i < 4; ++i) ub[i] = s.uh[vt][i][lane];
+                // Y = gamma Q S^T + lower(Q K^T * Gamma) U
+                f32x4 y[4];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    const float4 ga = *reinterpret_cast<const float4 *>(&D.gam[16 * ti + 4 * lg]);
+                    y[ti] = xp[ti] * f32x4{ga.x, ga.y, ga.z, ga.w};
+                }
+                const bf16x8 bU0 = cat8(ub[0], ub[1]), bU1 = cat8(ub[2], ub[3]);
                 bf16x8 yf[6];
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) yf[ti] = row_frag(D.aqk, CS, 16 * ti, 0, lane);
@@ -632,23 +671,23 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
                 for (int ti = 0; ti < 4; ++ti) y[ti] = mfma32(yf[ti], bU0, y[ti]);
                 y[2] = mfma32(yf[4], bU1, y[2]);
                 y[3] = mfma32(yf[5], bU1, y[3]);
-            }
-            __bf16 *ys = s.ys[vt];
+                __bf16 *ys = s.ys[vt];
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti)
+                for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ys[(16 * ti + 4 * lg + r) * 24 + lc] = static_cast<__bf16>(y[ti][r]);
-            // each lane stores one 32-byte output row segment
-            const int t0 = c * C;
-            if (t0 + lane < T) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(&ys[lane * 24]);
-                uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.out) + tok(t0 + lane) * dv + v0 + 16 * vt);
-                dst[0] = src[0];
-                dst[1] = src[1];
+                    for (int r = 0; r < 4; ++r) ys[(16 * ti + 4 * lg + r) * 24 + lc] = static_cast<__bf16>(y[ti][r]);
+                const int t0 = c * C;
+                if (t0 + lane < T) {  // each lane stores one 32-byte output row segment
+                    const uint4 *src = reinterpret_cast<const uint4 *>(&ys[lane * 24]);
+                    uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.out) + tok(t0 + lane) * dv + v0 + 16 * vt);
+                    dst[0] = src[0];
+                    dst[1] = src[1];
+                }
+                state_update<KT>(St, R, D, ub, KS, lane);
             }
             lds_barrier();
         }
-        if (a.state_out) {
+        if (is_carry && a.state_out) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
                 *reinterpret_cast<float4 *>(a.state_out + sbase + 16 * kt + 4 * lg) =
@@ -656,12 +695,12 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
         }
     } else {
         // ============================= producers =============================
-        const int pw = wave - 2;  // 0: keys/queries [0, DK/2), decay; 1: [DK/2, DK), beta
+        const int pw = wave - 4;  // key/query channels [pw*DK/4, (pw+1)*DK/4); value columns 8pw..8pw+7
         const uint16_t *gq = static_cast<const uint16_t *>(a.q);
         const uint16_t *gk = static_cast<const uint16_t *>(a.k);
         const uint16_t *gv = static_cast<const uint16_t *>(a.v);
         const uint16_t *gsc = static_cast<const uint16_t *>(pw == 0 ? a.alpha : a.beta);
-        uint4 rq[QL], rk[QL], rv[2];
+        uint4 rq[QL], rk[QL], rv;
         uint32_t rs = 0u;   // raw bf16 bits of the decay (pw 0) or beta (pw 1)
         bool rok = false;   // this lane's row lies inside the sequence
         // Loads read a clamped, always valid row; rows past the end are
@@ -673,12 +712,11 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
             const int64_t o = tok(min(t, T - 1));
 #pragma unroll
             for (int i = 0; i < QL; ++i) {
-                rq[i] = *reinterpret_cast<const uint4 *>(gq + o * DK + pw * HALF + 8 * i);
-                rk[i] = *reinterpret_cast<const uint4 *>(gk + o * DK + pw * HALF + 8 * i);
+                rq[i] = *reinterpret_cast<const uint4 *>(gq + o * DK + pw * QUART + 8 * i);
+                rk[i] = *reinterpret_cast<const uint4 *>(gk + o * DK + pw * QUART + 8 * i);
             }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) rv[i] = *reinterpret_cast<const uint4 *>(gv + o * dv + v0 + 16 * pw + 8 * i);
-            if (pw == 1 || kDecay) rs = static_cast<uint32_t>(gsc[o]);
+            rv = *reinterpret_cast<const uint4 *>(gv + o * dv + v0 + 8 * pw);
+            if (pw == 1 || (pw == 0 && kDecay)) rs = static_cast<uint32_t>(gsc[o]);
         };
         auto commit = [&](int c) {
             typename Lds::Raw &R = s.raw[c & 1];
@@ -687,63 +725,62 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
                 const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
                 for (int i = 0; i < QL; ++i) rq[i] = rk[i] = z;
-                rv[0] = rv[1] = z;
+                rv = z;
             }
 #pragma unroll
             for (int i = 0; i < QL; ++i) {
-                *reinterpret_cast<uint4 *>(&R.q[t * KS + pw * HALF + 8 * i]) = rq[i];
-                *reinterpret_cast<uint4 *>(&R.k[t * KS + pw * HALF + 8 * i]) = rk[i];
+                *reinterpret_cast<uint4 *>(&R.q[t * KS + pw * QUART + 8 * i]) = rq[i];
+                *reinterpret_cast<uint4 *>(&R.k[t * KS + pw * QUART + 8 * i]) = rk[i];
             }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4 *>(&R.v[t * Lds::VS + 16 * pw + 8 * i]) = rv[i];
+            *reinterpret_cast<uint4 *>(&R.v[t * Lds::VS + 8 * pw]) = rv;
             if (pw == 0) {
                 const float al = bf16_bits_to_f32(static_cast<uint16_t>(rs));
                 R.la[t] = (kDecay && rok) ? fmaxf(__builtin_amdgcn_logf(al), -200.f) : 0.f;
-            } else {
+            } else if (pw == 1) {
                 R.beta[t] = rok ? bf16_bits_to_f32(static_cast<uint16_t>(rs)) : 0.f;
             }
         };
-        // State-independent matrices of chunk c from its staged streams.
+        // State-independent matrices of chunk c, a quarter per producer.
         auto derive = [&](int c) {
             const typename Lds::Raw &R = s.raw[c & 1];
             typename Lds::Der &D = s.der[c & 1];
-            // gate prefix sums (each producer keeps its own copy)
-            const float g = wave_prefix_sum(R.la[lane]);
-            const float gl = __shfl(g, 63, 64);
+            const float g = wave_prefix_sum(R.la[lane]);  // every producer keeps its own copy
             float *gw = s.gw[pw];
             gw[lane] = g;
-            // key fragments of the four row tiles, loaded once
-            bf16x8 kf[4][KSTEP];
+            float gt[4][4], bt[4][4], gs[4];
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                for (int p = 0; p < KSTEP; ++p) kf[ti][p] = row_frag(R.k, KS, 16 * ti, 32 * p, lane);
+            for (int ti = 0; ti < 4; ++ti) {
+                const float4 g4 = *reinterpret_cast<const float4 *>(&gw[16 * ti + 4 * lg]);
+                const float4 b4 = *reinterpret_cast<const float4 *>(&R.beta[16 * ti + 4 * lg]);
+                gt[ti][0] = g4.x; gt[ti][1] = g4.y; gt[ti][2] = g4.z; gt[ti][3] = g4.w;
+                bt[ti][0] = b4.x; bt[ti][1] = b4.y; bt[ti][2] = b4.z; bt[ti][3] = b4.w;
+                gs[ti] = gw[16 * ti + lc];
+            }
             if (pw == 0) {
+                // gates, diagonal tiles of E K^T -> L_ii (fp32), their inverses
+                const float gl = __shfl(g, 63, 64);
                 D.gam[lane] = exp2_fast(g);
                 D.sc[lane] = exp2_fast(gl - g);
                 D.beta[lane] = R.beta[lane];
-                // diagonal tiles of E K^T -> L_ii (fp32), then their inverses
-                f32x4 accd[4];
+                f32x4 acc[4];
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) accd[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ti = 0; ti < 4; ++ti) acc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int p = 0; p < KSTEP; ++p)
+                for (int p = 0; p < KSTEP; ++p) {
+                    bf16x8 kf[4];
 #pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) accd[ti] = mfma32(kf[ti][p], kf[ti][p], accd[ti]);
+                    for (int ti = 0; ti < 4; ++ti) kf[ti] = row_frag(R.k, KS, 16 * ti, 32 * p, lane);
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    const f32x4 acc = accd[ti];
-                    const float gs = gw[16 * ti + lc];
-                    const float4 gt4 = *reinterpret_cast<const float4 *>(&gw[16 * ti + 4 * lg]);
-                    const float4 bt4 = *reinterpret_cast<const float4 *>(&R.beta[16 * ti + 4 * lg]);
-                    const float gt[4] = {gt4.x, gt4.y, gt4.z, gt4.w}, bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+                    for (int ti = 0; ti < 4; ++ti) acc[ti] = mfma32(kf[ti], kf[ti], acc[ti]);
+                }
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int tr = 4 * lg + r;
-                        const float val = lc < tr ? bt[r] * exp2_fast(gt[r] - gs) * acc[r] : 0.f;
+                        const float val = lc < tr ? bt[ti][r] * exp2_fast(gt[ti][r] - gs[ti]) * acc[ti][r] : 0.f;
                         s.ld[ti * 272 + tr * 16 + lc] = val;
                     }
-                }
                 // forward substitution: lane = (block lg, column lc)
                 const float *L = &s.ld[lg * 272];
                 float x[16];
@@ -770,57 +807,59 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
                 }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) D.dinv[(16 * lg + i) * DS + lc] = static_cast<__bf16>(x[i]);
-            } else {
-                // strictly lower off-diagonal tiles of E K^T -> -L blocks, and
-                // the lower tiles of Q K^T -> Aqk; all 16 accumulators built
-                // with their chains interleaved, then masked and stored
-                bf16x8 qf[4][KSTEP];
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                    for (int p = 0; p < KSTEP; ++p) qf[ti][p] = row_frag(R.q, KS, 16 * ti, 32 * p, lane);
+            } else if (pw == 1) {
+                // strictly lower off-diagonal tiles of E K^T -> -L blocks
                 constexpr int TI[NLB] = {1, 2, 2, 3, 3, 3}, SI[NLB] = {0, 0, 1, 0, 1, 2};
-                f32x4 accl[NLB], accq[10];
+                f32x4 acc[NLB];
 #pragma unroll
-                for (int j = 0; j < NLB; ++j) accl[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int j = 0; j < 10; ++j) accq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < NLB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p) {
+                    bf16x8 kf[4];
 #pragma unroll
-                    for (int j = 0; j < NLB; ++j) accl[j] = mfma32(kf[TI[j]][p], kf[SI[j]][p], accl[j]);
-                    int j = 0;
+                    for (int ti = 0; ti < 4; ++ti) kf[ti] = row_frag(R.k, KS, 16 * ti, 32 * p, lane);
 #pragma unroll
-                    for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                        for (int si = 0; si <= ti; ++si, ++j) accq[j] = mfma32(qf[ti][p], kf[si][p], accq[j]);
-                }
-                float gt[4][4], bt[4][4], gs[4];
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    const float4 g4 = *reinterpret_cast<const float4 *>(&gw[16 * ti + 4 * lg]);
-                    const float4 b4 = *reinterpret_cast<const float4 *>(&R.beta[16 * ti + 4 * lg]);
-                    gt[ti][0] = g4.x; gt[ti][1] = g4.y; gt[ti][2] = g4.z; gt[ti][3] = g4.w;
-                    bt[ti][0] = b4.x; bt[ti][1] = b4.y; bt[ti][2] = b4.z; bt[ti][3] = b4.w;
-                    gs[ti] = gw[16 * ti + lc];
+                    for (int j = 0; j < NLB; ++j) acc[j] = mfma32(kf[TI[j]], kf[SI[j]], acc[j]);
                 }
 #pragma unroll
                 for (int j = 0; j < NLB; ++j)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         D.lnb[(16 * j + 4 * lg + r) * DS + lc] = static_cast<__bf16>(
-                            -(bt[TI[j]][r] * exp2_fast(gt[TI[j]][r] - gs[SI[j]]) * accl[j][r]));
-                int j = 0;
+                            -(bt[TI[j]][r] * exp2_fast(gt[TI[j]][r] - gs[SI[j]]) * acc[j][r]));
+            } else {
+                // lower tiles of Q K^T -> Aqk: rows 0-2 (6 tiles) or row 3 (4 tiles)
+                auto qk_tiles = [&](auto tiles) {
+                    constexpr int NJ = decltype(tiles)::n;
+                    f32x4 acc[NJ];
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti)
+                    for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int si = 0; si <= ti; ++si, ++j)
+                    for (int p = 0; p < KSTEP; ++p) {
+                        bf16x8 kf[4], qf[4];
+#pragma unroll
+                        for (int ti = 0; ti < 4; ++ti) {
+                            kf[ti] = row_frag(R.k, KS, 16 * ti, 32 * p, lane);
+                            qf[ti] = row_frag(R.q, KS, 16 * ti, 32 * p, lane);
+                        }
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j) acc[j] = mfma32(qf[tiles.ti[j]], kf[tiles.si[j]], acc[j]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const int ti = tiles.ti[j], si = tiles.si[j];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int tr = 4 * lg + r;
-                            const float val = (si < ti || lc <= tr) ? accq[j][r] * exp2_fast(gt[ti][r] - gs[si]) : 0.f;
+                            const float val = (si < ti || lc <= tr) ? acc[j][r] * exp2_fast(gt[ti][r] - gs[si]) : 0.f;
                             D.aqk[(16 * ti + tr) * CS + 16 * si + lc] = static_cast<__bf16>(val);
                         }
+                    }
+                };
+                if (pw == 2)
+                    qk_tiles(QkTilesLow{});
+                else
+                    qk_tiles(QkTilesRow3{});
             }
         };
 
@@ -828,8 +867,9 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
         if (nchunks > 0) {
             fetch(0);
             commit(0);
-            target += 2;
-            producer_sync(&s.pcount, target, lane);
+            target += 4;
+            lds_arrive(&s.pcount, lane);
+            lds_wait(&s.pcount, target);
             if (nchunks > 1) fetch(1);
             derive(0);
         }
@@ -837,8 +877,9 @@ __global__ __launch_bounds__(NT) void delta_chunked_pipe_kernel(DeltaArgs a) {
         for (int c = 0; c < nchunks; ++c) {
             if (c + 1 < nchunks) {
                 commit(c + 1);
-                target += 2;
-                producer_sync(&s.pcount, target, lane);
+                target += 4;
+                lds_arrive(&s.pcount, lane);
+                lds_wait(&s.pcount, target);
                 if (c + 2 < nchunks) fetch(c + 2);
                 derive(c + 1);
             }
@@ -853,11 +894,11 @@ hipError_t launch_var(const DeltaArgs &a, hipStream_t stream) {
     constexpr bool kPipe = VARIANT != kGatedDeltaNet2;
     switch (a.dk) {
         case 64:
-            if constexpr (kPipe) delta_chunked_pipe_kernel<VARIANT, 64><<<blocks, NT, 0, stream>>>(a);
+            if constexpr (kPipe) delta_chunked_pipe_kernel<VARIANT, 64><<<blocks, NT8, 0, stream>>>(a);
             else delta_chunked_kernel<VARIANT, 64><<<blocks, NT, 0, stream>>>(a);
             break;
         case 128:
-            if constexpr (kPipe) delta_chunked_pipe_kernel<VARIANT, 128><<<blocks, NT, 0, stream>>>(a);
+            if constexpr (kPipe) delta_chunked_pipe_kernel<VARIANT, 128><<<blocks, NT8, 0, stream>>>(a);
             else delta_chunked_kernel<VARIANT, 128><<<blocks, NT, 0, stream>>>(a);
             break;
         default: return hipErrorInvalidValue;
