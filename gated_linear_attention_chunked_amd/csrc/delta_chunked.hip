@@ -72,6 +72,29 @@ __device__ __forceinline__ bf16x8 row_frag(const __bf16 *m, int stride, int r0, 
     const __bf16 *p = m + (r0 + (lane & 15)) * stride + c0 + 4 * (lane >> 4);
     return cat8(lds4(p), lds4(p + 16));
 }
+// A wave-uniform integer the compiler cannot see through (one scalar move).
+__device__ __forceinline__ int opaque(int x) {
+    int r;
+    asm("s_mov_b32 %0, %1" : "=s"(r) : "s"(x));
+    return r;
+}
+// The same fragment read as two independent 8-byte LDS loads.  Each load's
+// uniform offset passes through opaque(), so no two loads share a base
+// register and the compiler cannot fuse them into ds_read2_b64: on gfx950 a
+// conflict-free ds_read_b64 takes about 2 cycles, while ds_read2_b64 of the
+// same bytes takes 7.5 (14.8 at these row strides).
+typedef __attribute__((address_space(3))) const bf16x4 lds_bf16x4_t;
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+__device__ __forceinline__ bf16x8 row_frag2(const __bf16 *m, int stride, int r0, int c0, int lane, int) {
+    const uint32_t lane_off = 2u * static_cast<uint32_t>((lane & 15) * stride + 4 * (lane >> 4));
+    const uint32_t u = lds_address(m) + 2u * static_cast<uint32_t>(r0 * stride + c0);
+    const uint32_t a0 = lane_off + static_cast<uint32_t>(opaque(static_cast<int>(u)));
+    const uint32_t a1 = lane_off + static_cast<uint32_t>(opaque(static_cast<int>(u + 32u)));
+    return cat8(*reinterpret_cast<lds_bf16x4_t *>(static_cast<uintptr_t>(a0)),
+                *reinterpret_cast<lds_bf16x4_t *>(static_cast<uintptr_t>(a1)));
+}
 // Column gather with the gfx950 LDS transpose read.  Within each 16-lane
 // group g, lane m supplies the 8-byte piece m[r0 + 4g + m/4][c0 + 4(m%4) ..]
 // and lane i receives m[r0 + 4g + j][c0 + i] in slot j = 0..3: four
@@ -465,10 +488,11 @@ struct PipeLds {
     };
     Raw raw[2];
     Der der[2];
-    alignas(16) float ld[4 * 272];     // diagonal blocks of L, fp32 (block stride padded)
+    alignas(16) float ld[4 * 16 * 20]; // diagonal blocks of L, fp32, stored by column: [block][col][row]
     alignas(16) float gw[4][C];        // per-producer copy of the gate prefix sums
     alignas(16) __bf16 ys[2][C * 24];  // output staging, one 64x16 tile per output wave
     alignas(16) bf16x4 uh[2][4][64];   // U of the current chunk, per tile, fragment order
+    alignas(16) bf16x4 sh[2][2][DK / 16][64];  // bf16 state fragments: [parity][tile][16-row block]
     unsigned int pcount;               // producer arrivals
     unsigned int ucount[2];            // U publications per tile
 };
@@ -497,6 +521,34 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     x += dpp_shift<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
     x += dpp_shift<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
     return x;
+}
+
+// Value of lane n of this lane's 16-lane row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xf, 0xf, false));
+}
+
+// Column c of (I + L)^{-1} for a unit lower-triangular 16x16 block whose
+// strictly lower part L arrives by columns: lane c of a 16-lane row holds
+// column c (lcol[i] = L[i][c]).  Forward substitution x_i = -sum_{m<i}
+// L[i][m] x_m, with L[i][m] broadcast from lane m of the row, in fp32.
+template <int M = 0>
+__device__ __forceinline__ void fsub_terms(float &acc, const float (&lcol)[16], const float (&x)[16], int i) {
+    if constexpr (M < 15) {
+        if (M < i) acc = fmaf(row_bcast<M>(lcol[i]), x[M], acc);
+        fsub_terms<M + 1>(acc, lcol, x, i);
+    }
+}
+__device__ __forceinline__ void unit_lower_inverse_column(const float (&lcol)[16], float (&x)[16], int c) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = i == c ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+        float acc = 0.f;
+        fsub_terms(acc, lcol, x, i);
+        if (i > c) x[i] = -acc;
+    }
 }
 
 // Publish: make this wave's LDS writes visible, then count one arrival.
@@ -559,8 +611,6 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
     constexpr int KS = DK + 8;
     constexpr int KSTEP = DK / 32;
     constexpr int KT = DK / 16;
-    constexpr int QUART = DK / 4;         // key channels staged per producer wave
-    constexpr int QL = QUART / 8;         // 16-byte loads per row per producer
     using Lds = PipeLds<DK>;
     __shared__ Lds s;
 
@@ -575,6 +625,8 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
     const int lg = lane >> 4, lc = lane & 15;
     const int nchunks = (T + C - 1) / C;
     auto tok = [&](int t) { return (static_cast<int64_t>(b) * T + t) * H + h; };
+    // 16, from an argument the compiler cannot constant-fold (T >= 0 always)
+    const int sixteen = __builtin_amdgcn_readfirstlane(16 + (a.T < 0 ? 1 : 0));
 
     for (int i = tid; i < C * CS; i += NT8) {
         s.der[0].aqk[i] = static_cast<__bf16>(0.f);
@@ -593,22 +645,36 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
         f32x4 St[KT];
         const int vcol = v0 + 16 * vt + lc;
         const int64_t sbase = (static_cast<int64_t>(head) * dv + vcol) * DK;
+        // carry: publish the bf16 B-operand fragments of S^T for chunk `c`
+        auto publish_state = [&](int c) {
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            if (a.state_in) {
-                const float4 x = *reinterpret_cast<const float4 *>(a.state_in + sbase + 16 * kt + 4 * lg);
-                St[kt] = f32x4{x.x, x.y, x.z, x.w};
-            } else {
-                St[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < KT; ++kt) s.sh[c & 1][vt][kt][lane] = bf4(St[kt]);
+        };
+        if (is_carry) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                if (a.state_in) {
+                    const float4 x = *reinterpret_cast<const float4 *>(a.state_in + sbase + 16 * kt + 4 * lg);
+                    St[kt] = f32x4{x.x, x.y, x.z, x.w};
+                } else {
+                    St[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             }
+            publish_state(0);
         }
-        lds_barrier();  // chunk 0 staged and derived
+        lds_barrier();  // chunk 0 staged and derived, initial state published
         for (int c = 0; c < nchunks; ++c) {
             const typename Lds::Raw &R = s.raw[c & 1];
             const typename Lds::Der &D = s.der[c & 1];
             bf16x8 bS[KSTEP];
+            if (is_carry) {
 #pragma unroll
-            for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(bf4(St[2 * p]), bf4(St[2 * p + 1]));
+                for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(bf4(St[2 * p]), bf4(St[2 * p + 1]));
+            } else {
+#pragma unroll
+                for (int p = 0; p < KSTEP; ++p)
+                    bS[p] = cat8(s.sh[c & 1][vt][2 * p][lane], s.sh[c & 1][vt][2 * p + 1][lane]);
+            }
             // E S^T (carry) or Q S^T (output), four row tiles
             const __bf16 *am = is_carry ? R.k : R.q;
             f32x4 xp[4];
@@ -618,11 +684,10 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
             for (int p = 0; p < KSTEP; ++p) {
                 bf16x8 af[4];
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) af[ti] = row_frag(am, KS, 16 * ti, 32 * p, lane);
+                for (int ti = 0; ti < 4; ++ti) af[ti] = row_frag2(am, KS, 16 * ti, 32 * p, lane, sixteen);
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) xp[ti] = mfma32(af[ti], bS[p], xp[ti]);
             }
-            bf16x4 ub[4];
             if (is_carry) {
                 f32x4 rhs[4];
 #pragma unroll
@@ -637,6 +702,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
                 }
                 // blockwise forward solve U_i = D_i (R_i - sum_{j<i} L_ij U_j)
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                bf16x4 ub[4];
                 ub[0] = bf4(mfma16(blk_frag(D.dinv, DS, 0, 0, lane), bf4(rhs[0]), zero));
 #pragma unroll
                 for (int i = 1; i < 4; ++i) {
@@ -650,8 +716,10 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
                 for (int i = 0; i < 4; ++i) s.uh[vt][i][lane] = ub[i];
                 lds_arrive(&s.ucount[vt], lane);
                 state_update<KT>(St, R, D, ub, KS, lane);
+                if (c + 1 < nchunks) publish_state(c + 1);
             } else {
                 lds_wait(&s.ucount[vt], static_cast<unsigned int>(c + 1));
+                bf16x4 ub[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ub[i] = s.uh[vt][i][lane];
                 // Y = gamma Q S^T + lower(Q K^T * Gamma) U
@@ -664,9 +732,9 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
                 const bf16x8 bU0 = cat8(ub[0], ub[1]), bU1 = cat8(ub[2], ub[3]);
                 bf16x8 yf[6];
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) yf[ti] = row_frag(D.aqk, CS, 16 * ti, 0, lane);
-                yf[4] = row_frag(D.aqk, CS, 32, 32, lane);
-                yf[5] = row_frag(D.aqk, CS, 48, 32, lane);
+                for (int ti = 0; ti < 4; ++ti) yf[ti] = row_frag2(D.aqk, CS, 16 * ti, 0, lane, sixteen);
+                yf[4] = row_frag2(D.aqk, CS, 32, 32, lane, sixteen);
+                yf[5] = row_frag2(D.aqk, CS, 48, 32, lane, sixteen);
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) y[ti] = mfma32(yf[ti], bU0, y[ti]);
                 y[2] = mfma32(yf[4], bU1, y[2]);
@@ -678,12 +746,11 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
                     for (int r = 0; r < 4; ++r) ys[(16 * ti + 4 * lg + r) * 24 + lc] = static_cast<__bf16>(y[ti][r]);
                 const int t0 = c * C;
                 if (t0 + lane < T) {  // each lane stores one 32-byte output row segment
-                    const uint4 *src = reinterpret_cast<const uint4 *>(&ys[lane * 24]);
-                    uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.out) + tok(t0 + lane) * dv + v0 + 16 * vt);
-                    dst[0] = src[0];
-                    dst[1] = src[1];
+                    const uint2 *src = reinterpret_cast<const uint2 *>(&ys[lane * 24]);
+                    uint2 *dst = reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + tok(t0 + lane) * dv + v0 + 16 * vt);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dst[i] = src[i];
                 }
-                state_update<KT>(St, R, D, ub, KS, lane);
             }
             lds_barrier();
         }
@@ -695,49 +762,67 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
         }
     } else {
         // ============================= producers =============================
-        const int pw = wave - 4;  // key/query channels [pw*DK/4, (pw+1)*DK/4); value columns 8pw..8pw+7
+        const int pw = wave - 4;  // stages token rows [16pw, 16pw + 16) of each chunk
         const uint16_t *gq = static_cast<const uint16_t *>(a.q);
         const uint16_t *gk = static_cast<const uint16_t *>(a.k);
         const uint16_t *gv = static_cast<const uint16_t *>(a.v);
         const uint16_t *gsc = static_cast<const uint16_t *>(pw == 0 ? a.alpha : a.beta);
-        uint4 rq[QL], rk[QL], rv;
-        uint32_t rs = 0u;   // raw bf16 bits of the decay (pw 0) or beta (pw 1)
-        bool rok = false;   // this lane's row lies inside the sequence
-        // Loads read a clamped, always valid row; rows past the end are
-        // replaced by padding at commit, so no loaded value is consumed here
-        // and the loads stay in flight until the next chunk's staging.
-        auto fetch = [&](int c) {  // lane = token row of chunk c
-            const int t = c * C + lane;
-            rok = t < T;
-            const int64_t o = tok(min(t, T - 1));
+        // Coalesced staging: a dk-wide bf16 row is DK/8 16-byte pieces, so
+        // one load instruction covers 64*8/DK consecutive rows; a row of the
+        // workgroup's 32 value columns is 4 pieces (16 rows per instruction).
+        constexpr int PPR = DK / 8;             // 16-byte pieces per q/k row
+        constexpr int RPI = 64 / PPR;           // rows per load instruction
+        constexpr int NQK = 16 / RPI;           // instructions per producer per stream
+        uint4 rq[NQK], rk[NQK], rv;
+        uint32_t rs = 0u;    // raw bf16 bits of the decay (pw 0) or beta (pw 1) of row `lane`
+        uint32_t okm = 0u;   // bit i: row of q/k load i inside the sequence; bit NQK: v row; bit NQK+1: gate row
+        // Loads read clamped, always valid rows; rows past the end are replaced
+        // by padding at commit, so no loaded value is consumed here and the
+        // loads stay in flight until the next chunk's staging.
+        auto fetch = [&](int c) {
+            const int t0 = c * C;
+            okm = 0u;
 #pragma unroll
-            for (int i = 0; i < QL; ++i) {
-                rq[i] = *reinterpret_cast<const uint4 *>(gq + o * DK + pw * QUART + 8 * i);
-                rk[i] = *reinterpret_cast<const uint4 *>(gk + o * DK + pw * QUART + 8 * i);
+            for (int i = 0; i < NQK; ++i) {
+                const int t = t0 + 16 * pw + RPI * i + lane / PPR;
+                okm |= (t < T ? 1u : 0u) << i;
+                const int64_t o = tok(min(t, T - 1)) * DK + (lane % PPR) * 8;
+                rq[i] = *reinterpret_cast<const uint4 *>(gq + o);
+                rk[i] = *reinterpret_cast<const uint4 *>(gk + o);
             }
-            rv = *reinterpret_cast<const uint4 *>(gv + o * dv + v0 + 8 * pw);
-            if (pw == 1 || (pw == 0 && kDecay)) rs = static_cast<uint32_t>(gsc[o]);
+            {
+                const int t = t0 + 16 * pw + (lane >> 2);
+                okm |= (t < T ? 1u : 0u) << NQK;
+                rv = *reinterpret_cast<const uint4 *>(gv + tok(min(t, T - 1)) * dv + v0 + 8 * (lane & 3));
+            }
+            if (pw <= 1) {
+                const int t = t0 + lane;
+                okm |= (t < T ? 1u : 0u) << (NQK + 1);
+                if (pw == 1 || kDecay) rs = static_cast<uint32_t>(gsc[tok(min(t, T - 1))]);
+            }
         };
+        // rows past the end become zeros (a bitwise mask keeps the registers
+        // out of the select-of-aggregates form that lands them in scratch)
+        auto masked = [](uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); };
         auto commit = [&](int c) {
             typename Lds::Raw &R = s.raw[c & 1];
-            const int t = lane;
-            if (!rok) {
-                const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < QL; ++i) rq[i] = rk[i] = z;
-                rv = z;
+            for (int i = 0; i < NQK; ++i) {
+                const int row = 16 * pw + RPI * i + lane / PPR;
+                const uint32_t m = 0u - ((okm >> i) & 1u);
+                *reinterpret_cast<uint4 *>(&R.q[row * KS + (lane % PPR) * 8]) = masked(rq[i], m);
+                *reinterpret_cast<uint4 *>(&R.k[row * KS + (lane % PPR) * 8]) = masked(rk[i], m);
             }
-#pragma unroll
-            for (int i = 0; i < QL; ++i) {
-                *reinterpret_cast<uint4 *>(&R.q[t * KS + pw * QUART + 8 * i]) = rq[i];
-                *reinterpret_cast<uint4 *>(&R.k[t * KS + pw * QUART + 8 * i]) = rk[i];
+            {
+                const int row = 16 * pw + (lane >> 2);
+                *reinterpret_cast<uint4 *>(&R.v[row * Lds::VS + 8 * (lane & 3)]) = masked(rv, 0u - ((okm >> NQK) & 1u));
             }
-            *reinterpret_cast<uint4 *>(&R.v[t * Lds::VS + 8 * pw]) = rv;
+            const bool gok = (okm >> (NQK + 1)) & 1u;
             if (pw == 0) {
                 const float al = bf16_bits_to_f32(static_cast<uint16_t>(rs));
-                R.la[t] = (kDecay && rok) ? fmaxf(__builtin_amdgcn_logf(al), -200.f) : 0.f;
+                R.la[lane] = (kDecay && gok) ? fmaxf(__builtin_amdgcn_logf(al), -200.f) : 0.f;
             } else if (pw == 1) {
-                R.beta[t] = rok ? bf16_bits_to_f32(static_cast<uint16_t>(rs)) : 0.f;
+                R.beta[lane] = gok ? bf16_bits_to_f32(static_cast<uint16_t>(rs)) : 0.f;
             }
         };
         // State-independent matrices of chunk c, a quarter per producer.
@@ -769,42 +854,32 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
                 for (int p = 0; p < KSTEP; ++p) {
                     bf16x8 kf[4];
 #pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) kf[ti] = row_frag(R.k, KS, 16 * ti, 32 * p, lane);
+                    for (int ti = 0; ti < 4; ++ti) kf[ti] = row_frag2(R.k, KS, 16 * ti, 32 * p, lane, sixteen);
 #pragma unroll
                     for (int ti = 0; ti < 4; ++ti) acc[ti] = mfma32(kf[ti], kf[ti], acc[ti]);
                 }
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti)
+                for (int ti = 0; ti < 4; ++ti) {
+                    float val[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int tr = 4 * lg + r;
-                        const float val = lc < tr ? bt[ti][r] * exp2_fast(gt[ti][r] - gs[ti]) * acc[ti][r] : 0.f;
-                        s.ld[ti * 272 + tr * 16 + lc] = val;
+                        val[r] = lc < tr ? bt[ti][r] * exp2_fast(gt[ti][r] - gs[ti]) * acc[ti][r] : 0.f;
                     }
-                // forward substitution: lane = (block lg, column lc)
-                const float *L = &s.ld[lg * 272];
-                float x[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) x[i] = i == lc ? 1.f : 0.f;
-#pragma unroll
-                for (int i = 1; i < 16; ++i) {
-                    float row[16];
-#pragma unroll
-                    for (int m4 = 0; m4 < 4; ++m4) {
-                        const float4 v4 = *reinterpret_cast<const float4 *>(&L[i * 16 + 4 * m4]);
-                        row[4 * m4] = v4.x;
-                        row[4 * m4 + 1] = v4.y;
-                        row[4 * m4 + 2] = v4.z;
-                        row[4 * m4 + 3] = v4.w;
-                    }
-                    float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-                    for (int m = 0; m < i; ++m) {
-                        if (m & 1) acc1 = fmaf(row[m], x[m], acc1);
-                        else acc0 = fmaf(row[m], x[m], acc0);
-                    }
-                    if (i > lc) x[i] = -(acc0 + acc1);
+                    float *dst = &s.ld[(ti * 16 + lc) * 20 + 4 * lg];  // column lc, rows 4lg..4lg+3
+                    *reinterpret_cast<float2 *>(dst) = make_float2(val[0], val[1]);
+                    *reinterpret_cast<float2 *>(dst + 2) = make_float2(val[2], val[3]);
                 }
+                // inverses of the diagonal blocks: lane = (block lg, column lc)
+                float lcol[16], x[16];
+                const float *src = &s.ld[(lg * 16 + lc) * 20];
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const float2 v2 = *reinterpret_cast<const float2 *>(src + i);
+                    lcol[i] = v2.x;
+                    lcol[i + 1] = v2.y;
+                }
+                unit_lower_inverse_column(lcol, x, lc);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) D.dinv[(16 * lg + i) * DS + lc] = static_cast<__bf16>(x[i]);
             } else if (pw == 1) {
@@ -817,7 +892,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
                 for (int p = 0; p < KSTEP; ++p) {
                     bf16x8 kf[4];
 #pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) kf[ti] = row_frag(R.k, KS, 16 * ti, 32 * p, lane);
+                    for (int ti = 0; ti < 4; ++ti) kf[ti] = row_frag2(R.k, KS, 16 * ti, 32 * p, lane, sixteen);
 #pragma unroll
                     for (int j = 0; j < NLB; ++j) acc[j] = mfma32(kf[TI[j]], kf[SI[j]], acc[j]);
                 }
@@ -839,8 +914,8 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
                         bf16x8 kf[4], qf[4];
 #pragma unroll
                         for (int ti = 0; ti < 4; ++ti) {
-                            kf[ti] = row_frag(R.k, KS, 16 * ti, 32 * p, lane);
-                            qf[ti] = row_frag(R.q, KS, 16 * ti, 32 * p, lane);
+                            kf[ti] = row_frag2(R.k, KS, 16 * ti, 32 * p, lane, sixteen);
+                            qf[ti] = row_frag2(R.q, KS, 16 * ti, 32 * p, lane, sixteen);
                         }
 #pragma unroll
                         for (int j = 0; j < NJ; ++j) acc[j] = mfma32(qf[tiles.ti[j]], kf[tiles.si[j]], acc[j]);
