@@ -38,6 +38,8 @@
 // with the same order (rows 4g..4g+3 and 16+4g..16+4g+3 of each 32-block).
 // The same trick feeds U and the right-hand side to the next products without
 // an LDS round trip.
+#include <type_traits>
+
 #include "device_common.h"
 #include "lam_internal.h"
 
@@ -72,28 +74,16 @@ __device__ __forceinline__ bf16x8 row_frag(const __bf16 *m, int stride, int r0, 
     const __bf16 *p = m + (r0 + (lane & 15)) * stride + c0 + 4 * (lane >> 4);
     return cat8(lds4(p), lds4(p + 16));
 }
-// A wave-uniform integer the compiler cannot see through (one scalar move).
-__device__ __forceinline__ int opaque(int x) {
-    int r;
-    asm("s_mov_b32 %0, %1" : "=s"(r) : "s"(x));
-    return r;
-}
-// The same fragment read as two independent 8-byte LDS loads.  Each load's
-// uniform offset passes through opaque(), so no two loads share a base
-// register and the compiler cannot fuse them into ds_read2_b64: on gfx950 a
+// The same fragment read as two independent 8-byte LDS loads.  The loads
+// are volatile, so the compiler keeps them as single ds_read_b64 with
+// immediate offsets instead of fusing the pair into ds_read2_b64: on gfx950 a
 // conflict-free ds_read_b64 takes about 2 cycles, while ds_read2_b64 of the
 // same bytes takes 7.5 (14.8 at these row strides).
-typedef __attribute__((address_space(3))) const bf16x4 lds_bf16x4_t;
-__device__ __forceinline__ uint32_t lds_address(const void *p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
-}
-__device__ __forceinline__ bf16x8 row_frag2(const __bf16 *m, int stride, int r0, int c0, int lane, int) {
-    const uint32_t lane_off = 2u * static_cast<uint32_t>((lane & 15) * stride + 4 * (lane >> 4));
-    const uint32_t u = lds_address(m) + 2u * static_cast<uint32_t>(r0 * stride + c0);
-    const uint32_t a0 = lane_off + static_cast<uint32_t>(opaque(static_cast<int>(u)));
-    const uint32_t a1 = lane_off + static_cast<uint32_t>(opaque(static_cast<int>(u + 32u)));
-    return cat8(*reinterpret_cast<lds_bf16x4_t *>(static_cast<uintptr_t>(a0)),
-                *reinterpret_cast<lds_bf16x4_t *>(static_cast<uintptr_t>(a1)));
+typedef __attribute__((address_space(3))) volatile const bf16x4 vlds_bf16x4_t;
+__device__ __forceinline__ bf16x8 row_frag2(const __bf16 *m, int stride, int r0, int c0, int lane) {
+    const auto p = reinterpret_cast<__attribute__((address_space(3))) const __bf16 *>(
+        (__attribute__((address_space(3))) const void *)(m + (r0 + (lane & 15)) * stride + c0 + 4 * (lane >> 4)));
+    return cat8(*reinterpret_cast<vlds_bf16x4_t *>(p), *reinterpret_cast<vlds_bf16x4_t *>(p + 16));
 }
 // Column gather with the gfx950 LDS transpose read.  Within each 16-lane
 // group g, lane m supplies the 8-byte piece m[r0 + 4g + m/4][c0 + 4(m%4) ..]
@@ -448,53 +438,62 @@ __global__ __launch_bounds__(NT) void delta_chunked_kernel(DeltaArgs a) {
 
 // ===========================================================================
 // Pipelined schedule (DeltaNet, Gated DeltaNet): 8 waves per workgroup, two
-// per SIMD, in three roles.
-//   carry  (waves 0-1, one 16-column tile of the slice each): the critical
-//          path E S^T -> right-hand side -> blockwise solve -> state update;
-//          U is published to LDS as soon as the solve ends.
-//   output (waves 2-3, same tiles): Q S^T while the carry solves, then Y from
-//          the published U, the output store, and a replica of the state
-//          update (the same MFMA sequence on the same operands, so the two
-//          copies of the state stay bit-identical without a state handoff).
-//   producers (waves 4-7): stage chunk c+1 into the other half of a
-//          double-buffered LDS set and compute its state-independent
-//          matrices, a quarter each.
-// All eight waves meet at one LDS barrier per chunk.  Producers order their
-// staging writes before their tile reads, and each output wave waits for its
-// carry wave's U, through bounded LDS counters.  Only producers issue global
-// loads (two chunks ahead), so carry waves never wait on HBM.
+// per SIMD, in three roles.  With D_i = (I + L_ii)^{-1} the inverse of
+// diagonal block i of I + L, G~_ij = Gamma * (E_i K_j^T) and Z = E S^T, block
+// row i of the solve is
+//     U_i = D_i diag(beta)_i Z'_i - D_i diag(beta gamma)_i Z_i + sum_{j<i} M_ij U_j,
+//     M_ij = -D_i diag(beta)_i G~_ij                (Z' = the targets V)
+// so everything but Z is state-independent.
+//   carry  (waves 0-1, one 16-column tile each): Z = E S^T on MFMA, the
+//          block solve above on 16x16x16 MFMA (a four-link chain), publish U,
+//          then the state update accumulated in registers.
+//   output (waves 2-3, same tiles): Q S^T from the carry's bf16 state, then
+//          Y = diag(gamma) Q S^T + Aqk U once U is published; stores y.
+//   producers (waves 4-7): stage chunk c+1 into LDS (loads issued two chunks
+//          ahead).  Producer i then owns block row i: its E K^T tiles, the
+//          inverse of its diagonal block (fp32 forward substitution), its M_ij,
+//          plus 4 - i tiles of Q K^T for Aqk, so every producer computes five
+//          Gram tiles and needs nothing from the others after staging.
+// All eight waves meet at one LDS barrier per chunk; the hand-offs inside a
+// chunk go through bounded LDS counters.  The chunk loop is unrolled by the
+// double-buffer parity so every LDS address is a per-lane base plus a
+// constant.
 // ===========================================================================
 constexpr int NLB = 6;     // strictly lower 16x16 blocks of a 64-row chunk
-constexpr int NT8 = 512;   // threads per workgroup of the pipelined schedule
+constexpr int NQB = 10;    // lower 16x16 blocks including the diagonal
+constexpr int NT8 = 512;   // threads per workgroup of the WY schedule
+constexpr int LTS = 20;    // column stride (floats) of the fp32 diagonal blocks
 
 template <int DK>
-struct PipeLds {
+struct WyLds {
     static constexpr int KS = DK + 8;
     static constexpr int VS = BV + 8;
-    struct Raw {  // staged token streams of one chunk
+    struct Raw {  // token rows of one chunk, double-buffered (carry/output read chunk c)
         alignas(16) __bf16 q[C * KS];
         alignas(16) __bf16 k[C * KS];
-        alignas(16) __bf16 v[C * VS];    // the workgroup's value columns
-        alignas(16) float la[C];         // log2 of the decay (0 for padding)
-        alignas(16) float beta[C];
+        alignas(16) __bf16 v[C * VS];          // the workgroup's value columns
     };
-    struct Der {  // state-independent matrices of one chunk
-        alignas(16) __bf16 aqk[C * CS];          // lower(Q K^T) * Gamma
-        alignas(16) __bf16 lnb[NLB * 16 * DS];   // -L, strictly lower blocks
-        alignas(16) __bf16 dinv[4 * 16 * DS];    // (I + L_ii)^{-1}
-        alignas(16) float gam[C];                // gamma_t
-        alignas(16) float sc[C];                 // gamma_C / gamma_t
-        alignas(16) float beta[C];
+    struct Der {  // state-independent matrices of one chunk, double-buffered
+        alignas(16) bf16x4 aqk[NQB][64];       // lower(Q K^T * Gamma) blocks, A-operand order
+        alignas(16) bf16x4 dtil[4][64];        // D_i diag(beta)_i, A-operand order
+        alignas(16) bf16x4 dhn[4][64];         // -D_i diag(beta gamma)_i
+        alignas(16) bf16x4 mij[NLB][64];       // M_ij
+        alignas(16) float gam[C];              // gamma_t
+        alignas(16) float sc[C];               // gamma_C / gamma_t
     };
     Raw raw[2];
     Der der[2];
-    alignas(16) float ld[4 * 16 * 20]; // diagonal blocks of L, fp32, stored by column: [block][col][row]
-    alignas(16) float gw[4][C];        // per-producer copy of the gate prefix sums
-    alignas(16) __bf16 ys[2][C * 24];  // output staging, one 64x16 tile per output wave
-    alignas(16) bf16x4 uh[2][4][64];   // U of the current chunk, per tile, fragment order
-    alignas(16) bf16x4 sh[2][2][DK / 16][64];  // bf16 state fragments: [parity][tile][16-row block]
-    unsigned int pcount;               // producer arrivals
-    unsigned int ucount[2];            // U publications per tile
+    // producer-only, single-buffered: the chunk being derived
+    alignas(16) float la[C];                   // log2 of the decay (0 for padding)
+    alignas(16) float beta[C];                 // beta (0 for padding)
+    alignas(16) float g[C];                    // prefix sums of la
+    alignas(16) float lt[4][16 * LTS];         // diagonal blocks of L, fp32, by column
+    // carry -> output
+    alignas(16) bf16x4 uh[2][4][64];           // U of the current chunk, per tile
+    alignas(16) bf16x4 sh[2][DK / 16][64];     // bf16 state fragments per tile
+    unsigned int pcount;                       // producer arrivals
+    unsigned int ucount[2];                    // U publications per tile
+    unsigned int scount[2];                    // state fragments consumed per tile
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -522,32 +521,29 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     x += dpp_shift<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
     return x;
 }
-
-// Value of lane n of this lane's 16-lane row (DPP row_newbcast).
+// Value of lane N of this lane's quad (DPP quad_perm [N, N, N, N]).
 template <int N>
-__device__ __forceinline__ float row_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xf, 0xf, false));
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), N * 0x55, 0xf, 0xf, false));
 }
-
-// Column c of (I + L)^{-1} for a unit lower-triangular 16x16 block whose
-// strictly lower part L arrives by columns: lane c of a 16-lane row holds
-// column c (lcol[i] = L[i][c]).  Forward substitution x_i = -sum_{m<i}
-// L[i][m] x_m, with L[i][m] broadcast from lane m of the row, in fp32.
-template <int M = 0>
-__device__ __forceinline__ void fsub_terms(float &acc, const float (&lcol)[16], const float (&x)[16], int i) {
-    if constexpr (M < 15) {
-        if (M < i) acc = fmaf(row_bcast<M>(lcol[i]), x[M], acc);
-        fsub_terms<M + 1>(acc, lcol, x, i);
-    }
+// Value of the other lane of this lane's pair (DPP quad_perm [1, 0, 3, 2]).
+__device__ __forceinline__ float quad_swap(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));
 }
-__device__ __forceinline__ void unit_lower_inverse_column(const float (&lcol)[16], float (&x)[16], int c) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = i == c ? 1.f : 0.f;
-#pragma unroll
-    for (int i = 1; i < 16; ++i) {
-        float acc = 0.f;
-        fsub_terms(acc, lcol, x, i);
-        if (i > c) x[i] = -acc;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two floats rounded to bf16 (nearest even), `lo` in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+template <int I>
+using ic = std::integral_constant<int, I>;
+// Calls f(ic<I>) for I = 0 .. N-1.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &f) {
+    if constexpr (I < N) {
+        f(ic<I>{});
+        static_for<N, I + 1>(f);
     }
 }
 
@@ -567,8 +563,7 @@ __device__ __forceinline__ void lds_wait(unsigned int *cnt, unsigned int target)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// S^T = gamma_C S^T + K^T diag(gamma_C / gamma) U for one 16-column tile,
-// shared by the carry wave and its output-wave replica.
+// S^T = gamma_C S^T + K^T diag(gamma_C / gamma) U for one 16-column tile.
 template <int KT, typename Raw, typename Der>
 __device__ __forceinline__ void state_update(f32x4 (&St)[KT], const Raw &R, const Der &D, const bf16x4 (&ub)[4],
                                              int KS, int lane) {
@@ -595,23 +590,16 @@ __device__ __forceinline__ void state_update(f32x4 (&St)[KT], const Raw &R, cons
     }
 }
 
-// Lower tiles of Q K^T computed by producers 2 and 3.
-struct QkTilesLow {
-    static constexpr int n = 6;
-    static constexpr int ti[6] = {0, 1, 1, 2, 2, 2}, si[6] = {0, 0, 1, 0, 1, 2};
-};
-struct QkTilesRow3 {
-    static constexpr int n = 4;
-    static constexpr int ti[4] = {3, 3, 3, 3}, si[4] = {0, 1, 2, 3};
-};
+__device__ __forceinline__ constexpr int lower_block(int i, int j) { return i * (i - 1) / 2 + j; }  // j < i
+__device__ __forceinline__ constexpr int tri_block(int i, int j) { return i * (i + 1) / 2 + j; }    // j <= i
 
 template <int VARIANT, int DK>
-__global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
+__global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
     constexpr bool kDecay = VARIANT != kDeltaNet;
     constexpr int KS = DK + 8;
     constexpr int KSTEP = DK / 32;
     constexpr int KT = DK / 16;
-    using Lds = PipeLds<DK>;
+    using Lds = WyLds<DK>;
     __shared__ Lds s;
 
     const int T = static_cast<int>(a.T), H = static_cast<int>(a.H), dv = a.dv;
@@ -625,18 +613,13 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
     const int lg = lane >> 4, lc = lane & 15;
     const int nchunks = (T + C - 1) / C;
     auto tok = [&](int t) { return (static_cast<int64_t>(b) * T + t) * H + h; };
-    // 16, from an argument the compiler cannot constant-fold (T >= 0 always)
-    const int sixteen = __builtin_amdgcn_readfirstlane(16 + (a.T < 0 ? 1 : 0));
 
-    for (int i = tid; i < C * CS; i += NT8) {
-        s.der[0].aqk[i] = static_cast<__bf16>(0.f);
-        s.der[1].aqk[i] = static_cast<__bf16>(0.f);
-    }
     if (tid == 0) {
         s.pcount = 0u;
         s.ucount[0] = s.ucount[1] = 0u;
+        s.scount[0] = s.scount[1] = 0u;
     }
-    __syncthreads();  // counters and cleared tiles visible before any role starts
+    __syncthreads();  // counters visible before any role starts
 
     if (wave < 4) {
         // ========================= carry and output ==========================
@@ -645,10 +628,9 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
         f32x4 St[KT];
         const int vcol = v0 + 16 * vt + lc;
         const int64_t sbase = (static_cast<int64_t>(head) * dv + vcol) * DK;
-        // carry: publish the bf16 B-operand fragments of S^T for chunk `c`
-        auto publish_state = [&](int c) {
+        auto publish_state = [&]() {
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) s.sh[c & 1][vt][kt][lane] = bf4(St[kt]);
+            for (int kt = 0; kt < KT; ++kt) s.sh[vt][kt][lane] = bf4(St[kt]);
         };
         if (is_carry) {
 #pragma unroll
@@ -660,20 +642,25 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
                     St[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             }
-            publish_state(0);
+            publish_state();
         }
-        lds_barrier();  // chunk 0 staged and derived, initial state published
-        for (int c = 0; c < nchunks; ++c) {
-            const typename Lds::Raw &R = s.raw[c & 1];
-            const typename Lds::Der &D = s.der[c & 1];
+        // output rows: this lane stores rows 4lg + 2(lc&1) + {0, 1} of each
+        // 16-row tile, columns (lc & ~1) + {0, 1} of its tile
+        const bool odd = lc & 1;
+        const int64_t hdv = static_cast<int64_t>(H) * dv;
+        const uint32_t yoff = static_cast<uint32_t>((4 * lg + (odd ? 2 : 0)) * hdv + v0 + 16 * vt + (lc & ~1));
+        auto step = [&](auto par, int c) {
+            constexpr int P = decltype(par)::value;
+            const typename Lds::Raw &R = s.raw[P];
+            const typename Lds::Der &D = s.der[P];
             bf16x8 bS[KSTEP];
             if (is_carry) {
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(bf4(St[2 * p]), bf4(St[2 * p + 1]));
             } else {
 #pragma unroll
-                for (int p = 0; p < KSTEP; ++p)
-                    bS[p] = cat8(s.sh[c & 1][vt][2 * p][lane], s.sh[c & 1][vt][2 * p + 1][lane]);
+                for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(s.sh[vt][2 * p][lane], s.sh[vt][2 * p + 1][lane]);
+                lds_arrive(&s.scount[vt], lane);  // the carry may overwrite sh from here on
             }
             // E S^T (carry) or Q S^T (output), four row tiles
             const __bf16 *am = is_carry ? R.k : R.q;
@@ -684,39 +671,35 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
             for (int p = 0; p < KSTEP; ++p) {
                 bf16x8 af[4];
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) af[ti] = row_frag2(am, KS, 16 * ti, 32 * p, lane, sixteen);
+                for (int ti = 0; ti < 4; ++ti) af[ti] = row_frag2(am, KS, 16 * ti, 32 * p, lane);
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) xp[ti] = mfma32(af[ti], bS[p], xp[ti]);
             }
             if (is_carry) {
-                f32x4 rhs[4];
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    const int t = 16 * ti + 4 * lg;
-                    const bf16x4 z = col_gather4(R.v, Lds::VS, 16 * ti, 16 * vt, lane);
-                    const float4 be = *reinterpret_cast<const float4 *>(&D.beta[t]);
-                    const float4 ga = *reinterpret_cast<const float4 *>(&D.gam[t]);
-                    const float bb[4] = {be.x, be.y, be.z, be.w}, gg[4] = {ga.x, ga.y, ga.z, ga.w};
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) rhs[ti][r] = bb[r] * fmaf(-gg[r], xp[ti][r], static_cast<float>(z[r]));
-                }
-                // blockwise forward solve U_i = D_i (R_i - sum_{j<i} L_ij U_j)
+                // U_i = D~_i V_i - D^_i Z_i + sum_{j<i} M_ij U_j
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                f32x4 u[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    u[i] = mfma16(D.dtil[i][lane], col_gather4(R.v, Lds::VS, 16 * i, 16 * vt, lane), zero);
+                    u[i] = mfma16(D.dhn[i][lane], bf4(xp[i]), u[i]);
+                }
                 bf16x4 ub[4];
-                ub[0] = bf4(mfma16(blk_frag(D.dinv, DS, 0, 0, lane), bf4(rhs[0]), zero));
+                ub[0] = bf4(u[0]);
 #pragma unroll
                 for (int i = 1; i < 4; ++i) {
-                    f32x4 x = rhs[i];
 #pragma unroll
-                    for (int j = 0; j < i; ++j)
-                        x = mfma16(blk_frag(D.lnb, DS, 16 * (i * (i - 1) / 2 + j), 0, lane), ub[j], x);
-                    ub[i] = bf4(mfma16(blk_frag(D.dinv, DS, 16 * i, 0, lane), bf4(x), zero));
+                    for (int j = 0; j < i; ++j) u[i] = mfma16(D.mij[lower_block(i, j)][lane], ub[j], u[i]);
+                    ub[i] = bf4(u[i]);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) s.uh[vt][i][lane] = ub[i];
                 lds_arrive(&s.ucount[vt], lane);
                 state_update<KT>(St, R, D, ub, KS, lane);
-                if (c + 1 < nchunks) publish_state(c + 1);
+                if (c + 1 < nchunks) {
+                    lds_wait(&s.scount[vt], static_cast<unsigned int>(c + 1));
+                    publish_state();
+                }
             } else {
                 lds_wait(&s.ucount[vt], static_cast<unsigned int>(c + 1));
                 bf16x4 ub[4];
@@ -730,29 +713,37 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
                     y[ti] = xp[ti] * f32x4{ga.x, ga.y, ga.z, ga.w};
                 }
                 const bf16x8 bU0 = cat8(ub[0], ub[1]), bU1 = cat8(ub[2], ub[3]);
-                bf16x8 yf[6];
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) yf[ti] = row_frag2(D.aqk, CS, 16 * ti, 0, lane, sixteen);
-                yf[4] = row_frag2(D.aqk, CS, 32, 32, lane, sixteen);
-                yf[5] = row_frag2(D.aqk, CS, 48, 32, lane, sixteen);
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) y[ti] = mfma32(yf[ti], bU0, y[ti]);
-                y[2] = mfma32(yf[4], bU1, y[2]);
-                y[3] = mfma32(yf[5], bU1, y[3]);
-                __bf16 *ys = s.ys[vt];
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) ys[(16 * ti + 4 * lg + r) * 24 + lc] = static_cast<__bf16>(y[ti][r]);
+                const bf16x4 z4 = {};
+                y[0] = mfma32(cat8(D.aqk[tri_block(0, 0)][lane], z4), bU0, y[0]);
+                y[1] = mfma32(cat8(D.aqk[tri_block(1, 0)][lane], D.aqk[tri_block(1, 1)][lane]), bU0, y[1]);
+                y[2] = mfma32(cat8(D.aqk[tri_block(2, 0)][lane], D.aqk[tri_block(2, 1)][lane]), bU0, y[2]);
+                y[2] = mfma32(cat8(D.aqk[tri_block(2, 2)][lane], z4), bU1, y[2]);
+                y[3] = mfma32(cat8(D.aqk[tri_block(3, 0)][lane], D.aqk[tri_block(3, 1)][lane]), bU0, y[3]);
+                y[3] = mfma32(cat8(D.aqk[tri_block(3, 2)][lane], D.aqk[tri_block(3, 3)][lane]), bU1, y[3]);
+                // Store straight from the accumulators: lanes 2m and 2m+1 (columns
+                // 2m, 2m+1) trade two rows each, so every lane writes two
+                // 4-byte column pairs per tile.
                 const int t0 = c * C;
-                if (t0 + lane < T) {  // each lane stores one 32-byte output row segment
-                    const uint2 *src = reinterpret_cast<const uint2 *>(&ys[lane * 24]);
-                    uint2 *dst = reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + tok(t0 + lane) * dv + v0 + 16 * vt);
+                uint16_t *yo = static_cast<uint16_t *>(a.out) + tok(t0) * dv;
+                const int lim = T - t0 - (4 * lg + (odd ? 2 : 0));  // rows of this lane left in the sequence
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dst[i] = src[i];
+                for (int ti = 0; ti < 4; ++ti) {
+                    const float s0 = odd ? y[ti][0] : y[ti][2], s1 = odd ? y[ti][1] : y[ti][3];
+                    const float r0 = quad_swap(s0), r1 = quad_swap(s1);
+                    // even lane: rows 0, 1 as (own, partner); odd lane: rows 2, 3 as (partner, own)
+                    const float lo0 = odd ? r0 : y[ti][0], hi0 = odd ? y[ti][2] : r0;
+                    const float lo1 = odd ? r1 : y[ti][1], hi1 = odd ? y[ti][3] : r1;
+                    uint16_t *p = yo + yoff + static_cast<uint32_t>(16 * ti * hdv);
+                    if (16 * ti < lim) *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(lo0, hi0);
+                    if (16 * ti + 1 < lim) *reinterpret_cast<uint32_t *>(p + hdv) = pack_bf16x2(lo1, hi1);
                 }
             }
             lds_barrier();
+        };
+        lds_barrier();  // chunk 0 staged and derived, initial state published
+        for (int c = 0; c < nchunks; c += 2) {
+            step(ic<0>{}, c);
+            if (c + 1 < nchunks) step(ic<1>{}, c + 1);
         }
         if (is_carry && a.state_out) {
 #pragma unroll
@@ -773,6 +764,9 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
         constexpr int PPR = DK / 8;             // 16-byte pieces per q/k row
         constexpr int RPI = 64 / PPR;           // rows per load instruction
         constexpr int NQK = 16 / RPI;           // instructions per producer per stream
+        const uint32_t hdk = static_cast<uint32_t>(H * DK), hdv = static_cast<uint32_t>(H * dv);
+        const int qrow = 16 * pw + lane / PPR;  // chunk row of this lane's first q/k piece
+        const int vrow = 16 * pw + (lane >> 2);
         uint4 rq[NQK], rk[NQK], rv;
         uint32_t rs = 0u;    // raw bf16 bits of the decay (pw 0) or beta (pw 1) of row `lane`
         uint32_t okm = 0u;   // bit i: row of q/k load i inside the sequence; bit NQK: v row; bit NQK+1: gate row
@@ -780,185 +774,194 @@ __global__ __launch_bounds__(NT8) void delta_chunked_pipe_kernel(DeltaArgs a) {
         // by padding at commit, so no loaded value is consumed here and the
         // loads stay in flight until the next chunk's staging.
         auto fetch = [&](int c) {
-            const int t0 = c * C;
+            const int t0 = c * C, last = T - 1 - t0;
+            const int64_t base = tok(t0);
+            const uint16_t *q0 = gq + base * DK, *k0 = gk + base * DK;
             okm = 0u;
 #pragma unroll
             for (int i = 0; i < NQK; ++i) {
-                const int t = t0 + 16 * pw + RPI * i + lane / PPR;
-                okm |= (t < T ? 1u : 0u) << i;
-                const int64_t o = tok(min(t, T - 1)) * DK + (lane % PPR) * 8;
-                rq[i] = *reinterpret_cast<const uint4 *>(gq + o);
-                rk[i] = *reinterpret_cast<const uint4 *>(gk + o);
+                const int r = qrow + RPI * i;
+                okm |= (r <= last ? 1u : 0u) << i;
+                const uint32_t o = static_cast<uint32_t>(min(r, last)) * hdk + (lane % PPR) * 8;
+                rq[i] = *reinterpret_cast<const uint4 *>(q0 + o);
+                rk[i] = *reinterpret_cast<const uint4 *>(k0 + o);
             }
-            {
-                const int t = t0 + 16 * pw + (lane >> 2);
-                okm |= (t < T ? 1u : 0u) << NQK;
-                rv = *reinterpret_cast<const uint4 *>(gv + tok(min(t, T - 1)) * dv + v0 + 8 * (lane & 3));
-            }
+            okm |= (vrow <= last ? 1u : 0u) << NQK;
+            rv = *reinterpret_cast<const uint4 *>(gv + base * dv + static_cast<uint32_t>(min(vrow, last)) * hdv +
+                                                  v0 + 8 * (lane & 3));
             if (pw <= 1) {
-                const int t = t0 + lane;
-                okm |= (t < T ? 1u : 0u) << (NQK + 1);
-                if (pw == 1 || kDecay) rs = static_cast<uint32_t>(gsc[tok(min(t, T - 1))]);
+                okm |= (lane <= last ? 1u : 0u) << (NQK + 1);
+                if (pw == 1 || kDecay) rs = static_cast<uint32_t>(gsc[base + static_cast<uint32_t>(min(lane, last)) * H]);
             }
         };
         // rows past the end become zeros (a bitwise mask keeps the registers
         // out of the select-of-aggregates form that lands them in scratch)
         auto masked = [](uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); };
-        auto commit = [&](int c) {
-            typename Lds::Raw &R = s.raw[c & 1];
+        auto commit = [&](auto par) {
+            typename Lds::Raw &R = s.raw[decltype(par)::value];
 #pragma unroll
             for (int i = 0; i < NQK; ++i) {
-                const int row = 16 * pw + RPI * i + lane / PPR;
+                const int row = qrow + RPI * i;
                 const uint32_t m = 0u - ((okm >> i) & 1u);
                 *reinterpret_cast<uint4 *>(&R.q[row * KS + (lane % PPR) * 8]) = masked(rq[i], m);
                 *reinterpret_cast<uint4 *>(&R.k[row * KS + (lane % PPR) * 8]) = masked(rk[i], m);
             }
-            {
-                const int row = 16 * pw + (lane >> 2);
-                *reinterpret_cast<uint4 *>(&R.v[row * Lds::VS + 8 * (lane & 3)]) = masked(rv, 0u - ((okm >> NQK) & 1u));
-            }
+            *reinterpret_cast<uint4 *>(&R.v[vrow * Lds::VS + 8 * (lane & 3)]) = masked(rv, 0u - ((okm >> NQK) & 1u));
             const bool gok = (okm >> (NQK + 1)) & 1u;
             if (pw == 0) {
                 const float al = bf16_bits_to_f32(static_cast<uint16_t>(rs));
-                R.la[lane] = (kDecay && gok) ? fmaxf(__builtin_amdgcn_logf(al), -200.f) : 0.f;
+                s.la[lane] = (kDecay && gok) ? fmaxf(__builtin_amdgcn_logf(al), -200.f) : 0.f;
             } else if (pw == 1) {
-                R.beta[lane] = gok ? bf16_bits_to_f32(static_cast<uint16_t>(rs)) : 0.f;
+                s.beta[lane] = gok ? bf16_bits_to_f32(static_cast<uint16_t>(rs)) : 0.f;
             }
         };
-        // State-independent matrices of chunk c, a quarter per producer.
-        auto derive = [&](int c) {
-            const typename Lds::Raw &R = s.raw[c & 1];
-            typename Lds::Der &D = s.der[c & 1];
-            const float g = wave_prefix_sum(R.la[lane]);  // every producer keeps its own copy
-            float *gw = s.gw[pw];
-            gw[lane] = g;
-            float gt[4][4], bt[4][4], gs[4];
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                const float4 g4 = *reinterpret_cast<const float4 *>(&gw[16 * ti + 4 * lg]);
-                const float4 b4 = *reinterpret_cast<const float4 *>(&R.beta[16 * ti + 4 * lg]);
-                gt[ti][0] = g4.x; gt[ti][1] = g4.y; gt[ti][2] = g4.z; gt[ti][3] = g4.w;
-                bt[ti][0] = b4.x; bt[ti][1] = b4.y; bt[ti][2] = b4.z; bt[ti][3] = b4.w;
-                gs[ti] = gw[16 * ti + lc];
-            }
-            if (pw == 0) {
-                // gates, diagonal tiles of E K^T -> L_ii (fp32), their inverses
-                const float gl = __shfl(g, 63, 64);
-                D.gam[lane] = exp2_fast(g);
-                D.sc[lane] = exp2_fast(gl - g);
-                D.beta[lane] = R.beta[lane];
-                f32x4 acc[4];
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) acc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < KSTEP; ++p) {
-                    bf16x8 kf[4];
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) kf[ti] = row_frag2(R.k, KS, 16 * ti, 32 * p, lane, sixteen);
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) acc[ti] = mfma32(kf[ti], kf[ti], acc[ti]);
-                }
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    float val[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int tr = 4 * lg + r;
-                        val[r] = lc < tr ? bt[ti][r] * exp2_fast(gt[ti][r] - gs[ti]) * acc[ti][r] : 0.f;
-                    }
-                    float *dst = &s.ld[(ti * 16 + lc) * 20 + 4 * lg];  // column lc, rows 4lg..4lg+3
-                    *reinterpret_cast<float2 *>(dst) = make_float2(val[0], val[1]);
-                    *reinterpret_cast<float2 *>(dst + 2) = make_float2(val[2], val[3]);
-                }
-                // inverses of the diagonal blocks: lane = (block lg, column lc)
-                float lcol[16], x[16];
-                const float *src = &s.ld[(lg * 16 + lc) * 20];
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    const float2 v2 = *reinterpret_cast<const float2 *>(src + i);
-                    lcol[i] = v2.x;
-                    lcol[i + 1] = v2.y;
-                }
-                unit_lower_inverse_column(lcol, x, lc);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) D.dinv[(16 * lg + i) * DS + lc] = static_cast<__bf16>(x[i]);
-            } else if (pw == 1) {
-                // strictly lower off-diagonal tiles of E K^T -> -L blocks
-                constexpr int TI[NLB] = {1, 2, 2, 3, 3, 3}, SI[NLB] = {0, 0, 1, 0, 1, 2};
-                f32x4 acc[NLB];
-#pragma unroll
-                for (int j = 0; j < NLB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < KSTEP; ++p) {
-                    bf16x8 kf[4];
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) kf[ti] = row_frag2(R.k, KS, 16 * ti, 32 * p, lane, sixteen);
-#pragma unroll
-                    for (int j = 0; j < NLB; ++j) acc[j] = mfma32(kf[TI[j]], kf[SI[j]], acc[j]);
-                }
-#pragma unroll
-                for (int j = 0; j < NLB; ++j)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        D.lnb[(16 * j + 4 * lg + r) * DS + lc] = static_cast<__bf16>(
-                            -(bt[TI[j]][r] * exp2_fast(gt[TI[j]][r] - gs[SI[j]]) * acc[j][r]));
-            } else {
-                // lower tiles of Q K^T -> Aqk: rows 0-2 (6 tiles) or row 3 (4 tiles)
-                auto qk_tiles = [&](auto tiles) {
-                    constexpr int NJ = decltype(tiles)::n;
-                    f32x4 acc[NJ];
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int p = 0; p < KSTEP; ++p) {
-                        bf16x8 kf[4], qf[4];
-#pragma unroll
-                        for (int ti = 0; ti < 4; ++ti) {
-                            kf[ti] = row_frag2(R.k, KS, 16 * ti, 32 * p, lane, sixteen);
-                            qf[ti] = row_frag2(R.q, KS, 16 * ti, 32 * p, lane, sixteen);
-                        }
-#pragma unroll
-                        for (int j = 0; j < NJ; ++j) acc[j] = mfma32(qf[tiles.ti[j]], kf[tiles.si[j]], acc[j]);
-                    }
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const int ti = tiles.ti[j], si = tiles.si[j];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int tr = 4 * lg + r;
-                            const float val = (si < ti || lc <= tr) ? acc[j][r] * exp2_fast(gt[ti][r] - gs[si]) : 0.f;
-                            D.aqk[(16 * ti + tr) * CS + 16 * si + lc] = static_cast<__bf16>(val);
-                        }
-                    }
-                };
-                if (pw == 2)
-                    qk_tiles(QkTilesLow{});
-                else
-                    qk_tiles(QkTilesRow3{});
-            }
-        };
-
         unsigned int target = 0;
-        if (nchunks > 0) {
-            fetch(0);
-            commit(0);
+        auto psync = [&]() {
             target += 4;
             lds_arrive(&s.pcount, lane);
             lds_wait(&s.pcount, target);
+        };
+        // State-independent matrices of the chunk in buffer `par`.
+        auto derive = [&](auto par) {
+            const typename Lds::Raw &R = s.raw[decltype(par)::value];
+            typename Lds::Der &D = s.der[decltype(par)::value];
+            // gate prefix sums; every producer writes the same values
+            const float g = wave_prefix_sum(s.la[lane]);
+            s.g[lane] = g;
+            if (pw == 0) {
+                const float gl = __shfl(g, 63, 64);
+                D.gam[lane] = exp2_fast(g);
+                D.sc[lane] = exp2_fast(gl - g);
+            }
+            // ---- Gram tiles: producer i takes E K^T tiles (i, j <= i) and Q K^T
+            // tiles (3 - i, j <= 3 - i): five per producer.
+            auto work = [&](auto ic_) {
+                constexpr int I = decltype(ic_)::value;   // block row of L owned here
+                constexpr int QI = 3 - I;                 // block row of Aqk computed here
+                constexpr int NK = (I > QI ? I : QI) + 1; // key fragments needed
+                f32x4 acc[5];
+#pragma unroll
+                for (int j = 0; j < 5; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < KSTEP; ++p) {
+                    bf16x8 kf[NK];
+#pragma unroll
+                    for (int j = 0; j < NK; ++j) kf[j] = row_frag2(R.k, KS, 16 * j, 32 * p, lane);
+                    const bf16x8 qf = row_frag2(R.q, KS, 16 * QI, 32 * p, lane);
+#pragma unroll
+                    for (int j = 0; j <= I; ++j) acc[j] = mfma32(kf[I], kf[j], acc[j]);
+#pragma unroll
+                    for (int j = 0; j <= QI; ++j) acc[I + 1 + j] = mfma32(kf[j], qf, acc[I + 1 + j]);
+                }
+                // Aqk tiles: lane (lg, lc) holds Aqk[t = 16QI + lc][s = 16j + 4lg + r]
+                {
+                    const float gt = s.g[16 * QI + lc];
+#pragma unroll
+                    for (int j = 0; j <= QI; ++j) {
+                        const float4 gs4 = *reinterpret_cast<const float4 *>(&s.g[16 * j + 4 * lg]);
+                        const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
+                        f32x4 x;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float e = kDecay ? exp2_fast(gt - gs[r]) : 1.f;
+                            x[r] = (j < QI || 4 * lg + r <= lc) ? acc[I + 1 + j][r] * e : 0.f;
+                        }
+                        D.aqk[tri_block(QI, j)][lane] = bf4(x);
+                    }
+                }
+                // E K^T tiles: lane (lg, lc) holds G[t = 16I + 4lg + r][s = 16j + lc]
+                const float4 gt4 = *reinterpret_cast<const float4 *>(&s.g[16 * I + 4 * lg]);
+                const float gt[4] = {gt4.x, gt4.y, gt4.z, gt4.w};
+                bf16x4 gneg[I > 0 ? I : 1];   // -G~_ij in accumulator order
+#pragma unroll
+                for (int j = 0; j <= I; ++j) {
+                    const float gs = s.g[16 * j + lc];
+                    f32x4 x;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float e = kDecay ? exp2_fast(gt[r] - gs) : 1.f;
+                        x[r] = (j < I || lc < 4 * lg + r) ? acc[j][r] * e : 0.f;
+                    }
+                    if (j == I) {
+                        const float4 bt4 = *reinterpret_cast<const float4 *>(&s.beta[16 * I + 4 * lg]);
+                        *reinterpret_cast<float4 *>(&s.lt[I][lc * LTS + 4 * lg]) =
+                            make_float4(bt4.x * x[0], bt4.y * x[1], bt4.z * x[2], bt4.w * x[3]);
+                    } else {
+                        gneg[j] = bf4(-x);
+                    }
+                }
+                // D_I = (I + L_II)^{-1} by forward substitution in fp32;
+                // lane = (column col, row quad q)
+                const int col = lane >> 2, q = lane & 3;
+                const float *lt = s.lt[I];
+                float x[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == col) ? 1.f : 0.f;
+                auto sweep = [&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    const float4 l4 = *reinterpret_cast<const float4 *>(&lt[j * LTS + 4 * q]);  // L[4q + r][j]
+                    const float xj = quad_bcast<j / 4>(x[j % 4]);                              // X[j][col]
+                    x[0] = fmaf(-l4.x, xj, x[0]);
+                    x[1] = fmaf(-l4.y, xj, x[1]);
+                    x[2] = fmaf(-l4.z, xj, x[2]);
+                    x[3] = fmaf(-l4.w, xj, x[3]);
+                };
+                static_for<15>(sweep);
+                // D diag(beta) and -D diag(beta gamma): element (row, col) goes to
+                // A-operand lane (col / 4) * 16 + row, slot col % 4
+                const float bcol = s.beta[16 * I + col];
+                const float bgcol = -bcol * (kDecay ? exp2_fast(s.g[16 * I + col]) : 1.f);
+                __bf16 *dt = reinterpret_cast<__bf16 *>(&D.dtil[I][0]);
+                __bf16 *dh = reinterpret_cast<__bf16 *>(&D.dhn[I][0]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int e = ((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3);
+                    dt[e] = static_cast<__bf16>(x[r] * bcol);
+                    dh[e] = static_cast<__bf16>(x[r] * bgcol);
+                }
+                // M_Ij = -D~_I G~_Ij, computed transposed (A = -G~^T from the
+                // accumulators, B = D~_I^T from its A-operand fragment) so the
+                // result comes out in A-operand order
+                if constexpr (I > 0) {
+                    const bf16x4 dfrag = D.dtil[I][lane];
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < I; ++j) D.mij[lower_block(I, j)][lane] = bf4(mfma16(gneg[j], dfrag, zero));
+                }
+            };
+            if (pw == 0) work(ic<0>{});
+            else if (pw == 1) work(ic<1>{});
+            else if (pw == 2) work(ic<2>{});
+            else work(ic<3>{});
+        };
+
+        if (nchunks > 0) {
+            fetch(0);
+            commit(ic<0>{});
+            psync();
             if (nchunks > 1) fetch(1);
-            derive(0);
+            derive(ic<0>{});
         }
         lds_barrier();  // chunk 0 staged and derived
-        for (int c = 0; c < nchunks; ++c) {
+        for (int c = 0; c < nchunks; c += 2) {
+            // during chunk c: stage and derive chunk c + 1 (buffer 1)
             if (c + 1 < nchunks) {
-                commit(c + 1);
-                target += 4;
-                lds_arrive(&s.pcount, lane);
-                lds_wait(&s.pcount, target);
+                commit(ic<1>{});
+                psync();
                 if (c + 2 < nchunks) fetch(c + 2);
-                derive(c + 1);
+                derive(ic<1>{});
             }
             lds_barrier();
+            if (c + 1 < nchunks) {
+                // during chunk c + 1: chunk c + 2 (buffer 0)
+                if (c + 2 < nchunks) {
+                    commit(ic<0>{});
+                    psync();
+                    if (c + 3 < nchunks) fetch(c + 3);
+                    derive(ic<0>{});
+                }
+                lds_barrier();
+            }
         }
     }
 }
@@ -969,11 +972,11 @@ hipError_t launch_var(const DeltaArgs &a, hipStream_t stream) {
     constexpr bool kPipe = VARIANT != kGatedDeltaNet2;
     switch (a.dk) {
         case 64:
-            if constexpr (kPipe) delta_chunked_pipe_kernel<VARIANT, 64><<<blocks, NT8, 0, stream>>>(a);
+            if constexpr (kPipe) delta_chunked_wy_kernel<VARIANT, 64><<<blocks, NT8, 0, stream>>>(a);
             else delta_chunked_kernel<VARIANT, 64><<<blocks, NT, 0, stream>>>(a);
             break;
         case 128:
-            if constexpr (kPipe) delta_chunked_pipe_kernel<VARIANT, 128><<<blocks, NT8, 0, stream>>>(a);
+            if constexpr (kPipe) delta_chunked_wy_kernel<VARIANT, 128><<<blocks, NT8, 0, stream>>>(a);
             else delta_chunked_kernel<VARIANT, 128><<<blocks, NT, 0, stream>>>(a);
             break;
         default: return hipErrorInvalidValue;
