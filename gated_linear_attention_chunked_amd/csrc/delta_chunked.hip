@@ -38,6 +38,7 @@
 // with the same order (rows 4g..4g+3 and 16+4g..16+4g+3 of each 32-block).
 // The same trick feeds U and the right-hand side to the next products without
 // an LDS round trip.
+#include <array>
 #include <type_traits>
 
 #include "device_common.h"
@@ -474,12 +475,12 @@ struct WyLds {
         alignas(16) __bf16 v[C * VS];          // the workgroup's value columns
     };
     struct Der {  // state-independent matrices of one chunk, double-buffered
-        alignas(16) bf16x4 aqk[NQB][64];       // lower(Q K^T * Gamma) blocks, A-operand order
         alignas(16) bf16x4 dtil[4][64];        // D_i diag(beta)_i, A-operand order
         alignas(16) bf16x4 dhn[4][64];         // -D_i diag(beta gamma)_i
         alignas(16) bf16x4 mij[NLB][64];       // M_ij
         alignas(16) float gam[C];              // gamma_t
         alignas(16) float sc[C];               // gamma_C / gamma_t
+        alignas(16) float g[C];                // log2 gamma_t
     };
     Raw raw[2];
     Der der[2];
@@ -488,12 +489,17 @@ struct WyLds {
     alignas(16) float beta[C];                 // beta (0 for padding)
     alignas(16) float g[C];                    // prefix sums of la
     alignas(16) float lt[4][16 * LTS];         // diagonal blocks of L, fp32, by column
+    alignas(16) bf16x4 gx[3][64];              // -G~_3j (j < 3), made by producers 0 and 1 for producer 3
+    // output waves: lower(Q K^T * Gamma) blocks of the current chunk, A-operand order
+    alignas(16) bf16x4 aqk[NQB][64];
     // carry -> output
     alignas(16) bf16x4 uh[2][4][64];           // U of the current chunk, per tile
     alignas(16) bf16x4 sh[2][DK / 16][64];     // bf16 state fragments per tile
     unsigned int pcount;                       // producer arrivals
     unsigned int ucount[2];                    // U publications per tile
     unsigned int scount[2];                    // state fragments consumed per tile
+    unsigned int acount;                       // Aqk halves published by the output waves
+    unsigned int gcount;                       // row-3 Gram blocks published by producers 0, 1
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -525,16 +531,6 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 template <int N>
 __device__ __forceinline__ float quad_bcast(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), N * 0x55, 0xf, 0xf, false));
-}
-// Value of the other lane of this lane's pair (DPP quad_perm [1, 0, 3, 2]).
-__device__ __forceinline__ float quad_swap(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));
-}
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-// Two floats rounded to bf16 (nearest even), `lo` in the low half.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 template <int I>
 using ic = std::integral_constant<int, I>;
@@ -568,6 +564,12 @@ template <int KT, typename Raw, typename Der>
 __device__ __forceinline__ void state_update(f32x4 (&St)[KT], const Raw &R, const Der &D, const bf16x4 (&ub)[4],
                                              int KS, int lane) {
     const int lg = lane >> 4;
+    // operand reads first, then the scaling of U while they are in flight
+    bf16x8 af[2][KT];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) af[h2][kt] = col_frag(R.k, KS, 32 * h2, 16 * kt, lane);
     f32x4 us[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -580,16 +582,40 @@ __device__ __forceinline__ void state_update(f32x4 (&St)[KT], const Raw &R, cons
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) St[kt] = St[kt] * gC;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 bW = h2 ? bW1 : bW0;
-        bf16x8 af[KT];
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) af[kt] = col_frag(R.k, KS, 32 * h2, 16 * kt, lane);
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) St[kt] = mfma32(af[kt], bW, St[kt]);
-    }
+        for (int kt = 0; kt < KT; ++kt) St[kt] = mfma32(af[h2][kt], h2 ? bW1 : bW0, St[kt]);
 }
 
+// Q K^T tiles per output wave: block rows {0, 3} (set A) or {1, 2} (set B)
+// of the lower 4x4 block triangle, five tiles each.
+struct TilesA {
+    static constexpr int ti[5] = {0, 3, 3, 3, 3}, si[5] = {0, 0, 1, 2, 3};
+    static constexpr int nk = 4;  // key fragments used
+};
+struct TilesB {
+    static constexpr int ti[5] = {1, 1, 2, 2, 2}, si[5] = {0, 1, 0, 1, 2};
+    static constexpr int nk = 3;
+};
+// E K^T tiles per producer i: three each for producers 0-2, which also take
+// the off-diagonal tiles of block row 3, so producer 3 only forms (3, 3).
+template <int I> struct RowTiles;
+template <> struct RowTiles<0> {
+    static constexpr int n = 3, kmask = 0xb;
+    static constexpr int ti[3] = {0, 3, 3}, si[3] = {0, 0, 1};
+};
+template <> struct RowTiles<1> {
+    static constexpr int n = 3, kmask = 0xf;
+    static constexpr int ti[3] = {1, 1, 3}, si[3] = {0, 1, 2};
+};
+template <> struct RowTiles<2> {
+    static constexpr int n = 3, kmask = 0x7;
+    static constexpr int ti[3] = {2, 2, 2}, si[3] = {0, 1, 2};
+};
+template <> struct RowTiles<3> {
+    static constexpr int n = 1, kmask = 0x8;
+    static constexpr int ti[1] = {3}, si[1] = {3};
+};
 __device__ __forceinline__ constexpr int lower_block(int i, int j) { return i * (i - 1) / 2 + j; }  // j < i
 __device__ __forceinline__ constexpr int tri_block(int i, int j) { return i * (i + 1) / 2 + j; }    // j <= i
 
@@ -618,6 +644,8 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
         s.pcount = 0u;
         s.ucount[0] = s.ucount[1] = 0u;
         s.scount[0] = s.scount[1] = 0u;
+        s.acount = 0u;
+        s.gcount = 0u;
     }
     __syncthreads();  // counters visible before any role starts
 
@@ -644,52 +672,57 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
             }
             publish_state();
         }
-        // output rows: this lane stores rows 4lg + 2(lc&1) + {0, 1} of each
-        // 16-row tile, columns (lc & ~1) + {0, 1} of its tile
-        const bool odd = lc & 1;
+        // The output is computed transposed (Y^T = S Q^T + U^T Aqk^T, the same
+        // fragments with the operands swapped), so lane (lg, lc) holds value
+        // columns 16vt + 4lg .. +3 of token 16ti + lc: one 8-byte store per tile.
         const int64_t hdv = static_cast<int64_t>(H) * dv;
-        const uint32_t yoff = static_cast<uint32_t>((4 * lg + (odd ? 2 : 0)) * hdv + v0 + 16 * vt + (lc & ~1));
+        const uint32_t yoff = static_cast<uint32_t>(lc * hdv + v0 + 16 * vt + 4 * lg);
         auto step = [&](auto par, int c) {
             constexpr int P = decltype(par)::value;
             const typename Lds::Raw &R = s.raw[P];
             const typename Lds::Der &D = s.der[P];
             bf16x8 bS[KSTEP];
             if (is_carry) {
+                // Every read that does not depend on the state goes out first:
+                // the key fragments of Z, then the value blocks and the solve
+                // matrices, so their latency overlaps the Z products.
+                bf16x8 kf[KSTEP][4];
+#pragma unroll
+                for (int p = 0; p < KSTEP; ++p)
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) kf[p][ti] = row_frag2(R.k, KS, 16 * ti, 32 * p, lane);
+                bf16x4 vb[4], dt[4], dh[4], mj[NLB];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    vb[i] = col_gather4(R.v, Lds::VS, 16 * i, 16 * vt, lane);
+                    dt[i] = D.dtil[i][lane];
+                    dh[i] = D.dhn[i][lane];
+                }
+#pragma unroll
+                for (int i = 0; i < NLB; ++i) mj[i] = D.mij[i][lane];
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(bf4(St[2 * p]), bf4(St[2 * p + 1]));
-            } else {
+                // Z = E S^T, four row tiles
+                f32x4 xp[4];
 #pragma unroll
-                for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(s.sh[vt][2 * p][lane], s.sh[vt][2 * p + 1][lane]);
-                lds_arrive(&s.scount[vt], lane);  // the carry may overwrite sh from here on
-            }
-            // E S^T (carry) or Q S^T (output), four row tiles
-            const __bf16 *am = is_carry ? R.k : R.q;
-            f32x4 xp[4];
+                for (int ti = 0; ti < 4; ++ti) xp[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) xp[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int p = 0; p < KSTEP; ++p)
 #pragma unroll
-            for (int p = 0; p < KSTEP; ++p) {
-                bf16x8 af[4];
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) af[ti] = row_frag2(am, KS, 16 * ti, 32 * p, lane);
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) xp[ti] = mfma32(af[ti], bS[p], xp[ti]);
-            }
-            if (is_carry) {
+                    for (int ti = 0; ti < 4; ++ti) xp[ti] = mfma32(kf[p][ti], bS[p], xp[ti]);
                 // U_i = D~_i V_i - D^_i Z_i + sum_{j<i} M_ij U_j
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                 f32x4 u[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    u[i] = mfma16(D.dtil[i][lane], col_gather4(R.v, Lds::VS, 16 * i, 16 * vt, lane), zero);
-                    u[i] = mfma16(D.dhn[i][lane], bf4(xp[i]), u[i]);
-                }
+                for (int i = 0; i < 4; ++i) u[i] = mfma16(dt[i], vb[i], zero);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[i] = mfma16(dh[i], bf4(xp[i]), u[i]);
                 bf16x4 ub[4];
                 ub[0] = bf4(u[0]);
 #pragma unroll
                 for (int i = 1; i < 4; ++i) {
 #pragma unroll
-                    for (int j = 0; j < i; ++j) u[i] = mfma16(D.mij[lower_block(i, j)][lane], ub[j], u[i]);
+                    for (int j = 0; j < i; ++j) u[i] = mfma16(mj[lower_block(i, j)], ub[j], u[i]);
                     ub[i] = bf4(u[i]);
                 }
 #pragma unroll
@@ -701,41 +734,79 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
                     publish_state();
                 }
             } else {
+#pragma unroll
+                for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(s.sh[vt][2 * p][lane], s.sh[vt][2 * p + 1][lane]);
+                lds_arrive(&s.scount[vt], lane);  // the carry may overwrite sh from here on
+                // One pass over dk: Q S^T (four row tiles) and five tiles of
+                // K Q^T, which come out as Aqk in A-operand order: output wave 0
+                // takes block rows {0, 3}, wave 1 rows {1, 2}.
+                auto pass = [&](auto tiles) {
+                    using Tl = decltype(tiles);
+                    f32x4 xq[4], aq[5];
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) xq[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < 5; ++j) aq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int p = 0; p < KSTEP; ++p) {
+                        bf16x8 qf[4], kf[Tl::nk];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) qf[i] = row_frag2(R.q, KS, 16 * i, 32 * p, lane);
+#pragma unroll
+                        for (int i = 0; i < Tl::nk; ++i) kf[i] = row_frag2(R.k, KS, 16 * i, 32 * p, lane);
+#pragma unroll
+                        for (int ti = 0; ti < 4; ++ti) xq[ti] = mfma32(bS[p], qf[ti], xq[ti]);
+#pragma unroll
+                        for (int j = 0; j < 5; ++j) aq[j] = mfma32(kf[Tl::si[j]], qf[Tl::ti[j]], aq[j]);
+                    }
+                    // lane (lg, lc): Aqk[t = 16ti + lc][s = 16si + 4lg + r]
+#pragma unroll
+                    for (int j = 0; j < 5; ++j) {
+                        const int ti = Tl::ti[j], si = Tl::si[j];
+                        const float gt = D.g[16 * ti + lc];
+                        const float4 gs4 = *reinterpret_cast<const float4 *>(&D.g[16 * si + 4 * lg]);
+                        const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
+                        f32x4 x;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            // exponent clamped at 0 so masked entries stay finite
+                            const float v = kDecay ? aq[j][r] * exp2_fast(fminf(gt - gs[r], 0.f)) : aq[j][r];
+                            x[r] = (si < ti || 4 * lg + r <= lc) ? v : 0.f;
+                        }
+                        s.aqk[tri_block(ti, si)][lane] = bf4(x);
+                    }
+                    return std::array<f32x4, 4>{xq[0], xq[1], xq[2], xq[3]};
+                };
+                const std::array<f32x4, 4> xq = vt == 0 ? pass(TilesA{}) : pass(TilesB{});
+                lds_arrive(&s.acount, lane);
                 lds_wait(&s.ucount[vt], static_cast<unsigned int>(c + 1));
                 bf16x4 ub[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ub[i] = s.uh[vt][i][lane];
-                // Y = gamma Q S^T + lower(Q K^T * Gamma) U
+                lds_wait(&s.acount, static_cast<unsigned int>(2 * (c + 1)));
+                // Y^T = S Q^T diag(gamma) + U^T lower(Q K^T * Gamma)^T
                 f32x4 y[4];
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    const float4 ga = *reinterpret_cast<const float4 *>(&D.gam[16 * ti + 4 * lg]);
-                    y[ti] = xp[ti] * f32x4{ga.x, ga.y, ga.z, ga.w};
-                }
-                const bf16x8 bU0 = cat8(ub[0], ub[1]), bU1 = cat8(ub[2], ub[3]);
+                for (int ti = 0; ti < 4; ++ti) y[ti] = xq[ti] * D.gam[16 * ti + lc];
+                const bf16x8 aU0 = cat8(ub[0], ub[1]), aU1 = cat8(ub[2], ub[3]);
                 const bf16x4 z4 = {};
-                y[0] = mfma32(cat8(D.aqk[tri_block(0, 0)][lane], z4), bU0, y[0]);
-                y[1] = mfma32(cat8(D.aqk[tri_block(1, 0)][lane], D.aqk[tri_block(1, 1)][lane]), bU0, y[1]);
-                y[2] = mfma32(cat8(D.aqk[tri_block(2, 0)][lane], D.aqk[tri_block(2, 1)][lane]), bU0, y[2]);
-                y[2] = mfma32(cat8(D.aqk[tri_block(2, 2)][lane], z4), bU1, y[2]);
-                y[3] = mfma32(cat8(D.aqk[tri_block(3, 0)][lane], D.aqk[tri_block(3, 1)][lane]), bU0, y[3]);
-                y[3] = mfma32(cat8(D.aqk[tri_block(3, 2)][lane], D.aqk[tri_block(3, 3)][lane]), bU1, y[3]);
-                // Store straight from the accumulators: lanes 2m and 2m+1 (columns
-                // 2m, 2m+1) trade two rows each, so every lane writes two
-                // 4-byte column pairs per tile.
+                y[0] = mfma32(aU0, cat8(s.aqk[tri_block(0, 0)][lane], z4), y[0]);
+                y[1] = mfma32(aU0, cat8(s.aqk[tri_block(1, 0)][lane], s.aqk[tri_block(1, 1)][lane]), y[1]);
+                y[2] = mfma32(aU0, cat8(s.aqk[tri_block(2, 0)][lane], s.aqk[tri_block(2, 1)][lane]), y[2]);
+                y[2] = mfma32(aU1, cat8(s.aqk[tri_block(2, 2)][lane], z4), y[2]);
+                y[3] = mfma32(aU0, cat8(s.aqk[tri_block(3, 0)][lane], s.aqk[tri_block(3, 1)][lane]), y[3]);
+                y[3] = mfma32(aU1, cat8(s.aqk[tri_block(3, 2)][lane], s.aqk[tri_block(3, 3)][lane]), y[3]);
                 const int t0 = c * C;
-                uint16_t *yo = static_cast<uint16_t *>(a.out) + tok(t0) * dv;
-                const int lim = T - t0 - (4 * lg + (odd ? 2 : 0));  // rows of this lane left in the sequence
+                uint16_t *yo = static_cast<uint16_t *>(a.out) + tok(t0) * dv + yoff;
+                if (t0 + C <= T) {
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
-                    const float s0 = odd ? y[ti][0] : y[ti][2], s1 = odd ? y[ti][1] : y[ti][3];
-                    const float r0 = quad_swap(s0), r1 = quad_swap(s1);
-                    // even lane: rows 0, 1 as (own, partner); odd lane: rows 2, 3 as (partner, own)
-                    const float lo0 = odd ? r0 : y[ti][0], hi0 = odd ? y[ti][2] : r0;
-                    const float lo1 = odd ? r1 : y[ti][1], hi1 = odd ? y[ti][3] : r1;
-                    uint16_t *p = yo + yoff + static_cast<uint32_t>(16 * ti * hdv);
-                    if (16 * ti < lim) *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(lo0, hi0);
-                    if (16 * ti + 1 < lim) *reinterpret_cast<uint32_t *>(p + hdv) = pack_bf16x2(lo1, hi1);
+                    for (int ti = 0; ti < 4; ++ti)
+                        *reinterpret_cast<bf16x4 *>(yo + static_cast<uint32_t>(16 * ti * hdv)) = bf4(y[ti]);
+                } else {
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti)
+                        if (t0 + 16 * ti + lc < T)
+                            *reinterpret_cast<bf16x4 *>(yo + static_cast<uint32_t>(16 * ti * hdv)) = bf4(y[ti]);
                 }
             }
             lds_barrier();
@@ -821,8 +892,10 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
             lds_arrive(&s.pcount, lane);
             lds_wait(&s.pcount, target);
         };
+        unsigned int nderived = 0;  // chunks derived so far, this one included
         // State-independent matrices of the chunk in buffer `par`.
         auto derive = [&](auto par) {
+            ++nderived;
             const typename Lds::Raw &R = s.raw[decltype(par)::value];
             typename Lds::Der &D = s.der[decltype(par)::value];
             // gate prefix sums; every producer writes the same values
@@ -830,81 +903,69 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
             s.g[lane] = g;
             if (pw == 0) {
                 const float gl = __shfl(g, 63, 64);
+                D.g[lane] = g;
                 D.gam[lane] = exp2_fast(g);
                 D.sc[lane] = exp2_fast(gl - g);
             }
-            // ---- Gram tiles: producer i takes E K^T tiles (i, j <= i) and Q K^T
-            // tiles (3 - i, j <= 3 - i): five per producer.
+            // ---- E K^T tiles of block row i (i + 1 tiles) on producer i
             auto work = [&](auto ic_) {
                 constexpr int I = decltype(ic_)::value;   // block row of L owned here
-                constexpr int QI = 3 - I;                 // block row of Aqk computed here
-                constexpr int NK = (I > QI ? I : QI) + 1; // key fragments needed
-                f32x4 acc[5];
+                using Tl = RowTiles<I>;
+                constexpr int NT = Tl::n;
+                f32x4 acc[NT];
 #pragma unroll
-                for (int j = 0; j < 5; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p) {
-                    bf16x8 kf[NK];
+                    bf16x8 kf[4];
 #pragma unroll
-                    for (int j = 0; j < NK; ++j) kf[j] = row_frag2(R.k, KS, 16 * j, 32 * p, lane);
-                    const bf16x8 qf = row_frag2(R.q, KS, 16 * QI, 32 * p, lane);
+                    for (int j = 0; j < 4; ++j)
+                        if ((Tl::kmask >> j) & 1) kf[j] = row_frag2(R.k, KS, 16 * j, 32 * p, lane);
 #pragma unroll
-                    for (int j = 0; j <= I; ++j) acc[j] = mfma32(kf[I], kf[j], acc[j]);
-#pragma unroll
-                    for (int j = 0; j <= QI; ++j) acc[I + 1 + j] = mfma32(kf[j], qf, acc[I + 1 + j]);
+                    for (int j = 0; j < NT; ++j) acc[j] = mfma32(kf[Tl::ti[j]], kf[Tl::si[j]], acc[j]);
                 }
-                // Aqk tiles: lane (lg, lc) holds Aqk[t = 16QI + lc][s = 16j + 4lg + r]
-                {
-                    const float gt = s.g[16 * QI + lc];
+                // E K^T tiles: lane (lg, lc) holds G[t = 16ti + 4lg + r][s = 16si + lc]
+                bf16x4 gneg[4];   // -G~_Ij in accumulator order (own block row only)
 #pragma unroll
-                    for (int j = 0; j <= QI; ++j) {
-                        const float4 gs4 = *reinterpret_cast<const float4 *>(&s.g[16 * j + 4 * lg]);
-                        const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
-                        f32x4 x;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float e = kDecay ? exp2_fast(gt - gs[r]) : 1.f;
-                            x[r] = (j < QI || 4 * lg + r <= lc) ? acc[I + 1 + j][r] * e : 0.f;
-                        }
-                        D.aqk[tri_block(QI, j)][lane] = bf4(x);
-                    }
-                }
-                // E K^T tiles: lane (lg, lc) holds G[t = 16I + 4lg + r][s = 16j + lc]
-                const float4 gt4 = *reinterpret_cast<const float4 *>(&s.g[16 * I + 4 * lg]);
-                const float gt[4] = {gt4.x, gt4.y, gt4.z, gt4.w};
-                bf16x4 gneg[I > 0 ? I : 1];   // -G~_ij in accumulator order
-#pragma unroll
-                for (int j = 0; j <= I; ++j) {
-                    const float gs = s.g[16 * j + lc];
+                for (int j = 0; j < NT; ++j) {
+                    const int ti = Tl::ti[j], si = Tl::si[j];
+                    const float4 gt4 = *reinterpret_cast<const float4 *>(&s.g[16 * ti + 4 * lg]);
+                    const float gt[4] = {gt4.x, gt4.y, gt4.z, gt4.w};
+                    const float gs = s.g[16 * si + lc];
                     f32x4 x;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float e = kDecay ? exp2_fast(gt[r] - gs) : 1.f;
-                        x[r] = (j < I || lc < 4 * lg + r) ? acc[j][r] * e : 0.f;
+                        const float v = kDecay ? acc[j][r] * exp2_fast(fminf(gt[r] - gs, 0.f)) : acc[j][r];
+                        x[r] = (si < ti || lc < 4 * lg + r) ? v : 0.f;
                     }
-                    if (j == I) {
-                        const float4 bt4 = *reinterpret_cast<const float4 *>(&s.beta[16 * I + 4 * lg]);
-                        *reinterpret_cast<float4 *>(&s.lt[I][lc * LTS + 4 * lg]) =
+                    if (si == ti) {
+                        const float4 bt4 = *reinterpret_cast<const float4 *>(&s.beta[16 * ti + 4 * lg]);
+                        *reinterpret_cast<float4 *>(&s.lt[ti][lc * LTS + 4 * lg]) =
                             make_float4(bt4.x * x[0], bt4.y * x[1], bt4.z * x[2], bt4.w * x[3]);
+                    } else if (ti == I) {
+                        gneg[si] = bf4(-x);
                     } else {
-                        gneg[j] = bf4(-x);
+                        s.gx[si][lane] = bf4(-x);  // row 3 block computed for producer 3
                     }
                 }
+                if constexpr (I < 2) lds_arrive(&s.gcount, lane);
                 // D_I = (I + L_II)^{-1} by forward substitution in fp32;
                 // lane = (column col, row quad q)
                 const int col = lane >> 2, q = lane & 3;
-                const float *lt = s.lt[I];
+                typedef __attribute__((address_space(3))) volatile const f32x4 vlds_f4;
+                const auto lt = reinterpret_cast<__attribute__((address_space(3))) const float *>(
+                    (__attribute__((address_space(3))) const void *)&s.lt[I][4 * q]);
+                f32x4 lj[15];   // L[4q + r][j] for every column j, all reads issued together
+#pragma unroll
+                for (int j = 0; j < 15; ++j) lj[j] = *reinterpret_cast<vlds_f4 *>(lt + j * LTS);
                 float x[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == col) ? 1.f : 0.f;
                 auto sweep = [&](auto jc) {
                     constexpr int j = decltype(jc)::value;
-                    const float4 l4 = *reinterpret_cast<const float4 *>(&lt[j * LTS + 4 * q]);  // L[4q + r][j]
-                    const float xj = quad_bcast<j / 4>(x[j % 4]);                              // X[j][col]
-                    x[0] = fmaf(-l4.x, xj, x[0]);
-                    x[1] = fmaf(-l4.y, xj, x[1]);
-                    x[2] = fmaf(-l4.z, xj, x[2]);
-                    x[3] = fmaf(-l4.w, xj, x[3]);
+                    const float xj = quad_bcast<j / 4>(x[j % 4]);  // X[j][col]
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) x[r] = fmaf(-lj[j][r], xj, x[r]);
                 };
                 static_for<15>(sweep);
                 // D diag(beta) and -D diag(beta gamma): element (row, col) goes to
@@ -923,6 +984,11 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
                 // accumulators, B = D~_I^T from its A-operand fragment) so the
                 // result comes out in A-operand order
                 if constexpr (I > 0) {
+                    if constexpr (I == 3) {
+                        lds_wait(&s.gcount, 2u * nderived);  // blocks (3,0), (3,1), (3,2) from producers 0, 1
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) gneg[j] = s.gx[j][lane];
+                    }
                     const bf16x4 dfrag = D.dtil[I][lane];
                     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -938,8 +1004,8 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
         if (nchunks > 0) {
             fetch(0);
             commit(ic<0>{});
-            psync();
             if (nchunks > 1) fetch(1);
+            psync();
             derive(ic<0>{});
         }
         lds_barrier();  // chunk 0 staged and derived
@@ -947,8 +1013,8 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
             // during chunk c: stage and derive chunk c + 1 (buffer 1)
             if (c + 1 < nchunks) {
                 commit(ic<1>{});
-                psync();
                 if (c + 2 < nchunks) fetch(c + 2);
+                psync();
                 derive(ic<1>{});
             }
             lds_barrier();
@@ -956,8 +1022,8 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
                 // during chunk c + 1: chunk c + 2 (buffer 0)
                 if (c + 2 < nchunks) {
                     commit(ic<0>{});
-                    psync();
                     if (c + 3 < nchunks) fetch(c + 3);
+                    psync();
                     derive(ic<0>{});
                 }
                 lds_barrier();
