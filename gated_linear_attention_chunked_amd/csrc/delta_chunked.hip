@@ -838,31 +838,37 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
         const uint32_t hdk = static_cast<uint32_t>(H * DK), hdv = static_cast<uint32_t>(H * dv);
         const int qrow = 16 * pw + lane / PPR;  // chunk row of this lane's first q/k piece
         const int vrow = 16 * pw + (lane >> 2);
-        uint4 rq[NQK], rk[NQK], rv;
-        uint32_t rs = 0u;    // raw bf16 bits of the decay (pw 0) or beta (pw 1) of row `lane`
-        uint32_t okm = 0u;   // bit i: row of q/k load i inside the sequence; bit NQK: v row; bit NQK+1: gate row
+        // Two staging sets, one per chunk parity: loads run two chunks ahead.
+        struct Stage {
+            uint4 q[NQK], k[NQK], v;
+            uint32_t rs;   // raw bf16 bits of the decay (pw 0) or beta (pw 1) of row `lane`
+            uint32_t okm;  // bit i: row of q/k load i inside the sequence; bit NQK: v row; bit NQK+1: gate row
+        };
+        Stage st[2];
         // Loads read clamped, always valid rows; rows past the end are replaced
         // by padding at commit, so no loaded value is consumed here and the
-        // loads stay in flight until the next chunk's staging.
-        auto fetch = [&](int c) {
+        // loads stay in flight until that chunk's staging.
+        auto fetch = [&](auto par, int c) {
+            Stage &g = st[decltype(par)::value];
             const int t0 = c * C, last = T - 1 - t0;
             const int64_t base = tok(t0);
             const uint16_t *q0 = gq + base * DK, *k0 = gk + base * DK;
-            okm = 0u;
+            g.okm = 0u;
 #pragma unroll
             for (int i = 0; i < NQK; ++i) {
                 const int r = qrow + RPI * i;
-                okm |= (r <= last ? 1u : 0u) << i;
+                g.okm |= (r <= last ? 1u : 0u) << i;
                 const uint32_t o = static_cast<uint32_t>(min(r, last)) * hdk + (lane % PPR) * 8;
-                rq[i] = *reinterpret_cast<const uint4 *>(q0 + o);
-                rk[i] = *reinterpret_cast<const uint4 *>(k0 + o);
+                g.q[i] = *reinterpret_cast<const uint4 *>(q0 + o);
+                g.k[i] = *reinterpret_cast<const uint4 *>(k0 + o);
             }
-            okm |= (vrow <= last ? 1u : 0u) << NQK;
-            rv = *reinterpret_cast<const uint4 *>(gv + base * dv + static_cast<uint32_t>(min(vrow, last)) * hdv +
-                                                  v0 + 8 * (lane & 3));
+            g.okm |= (vrow <= last ? 1u : 0u) << NQK;
+            g.v = *reinterpret_cast<const uint4 *>(gv + base * dv + static_cast<uint32_t>(min(vrow, last)) * hdv +
+                                                   v0 + 8 * (lane & 3));
+            g.rs = 0u;
             if (pw <= 1) {
-                okm |= (lane <= last ? 1u : 0u) << (NQK + 1);
-                if (pw == 1 || kDecay) rs = static_cast<uint32_t>(gsc[base + static_cast<uint32_t>(min(lane, last)) * H]);
+                g.okm |= (lane <= last ? 1u : 0u) << (NQK + 1);
+                if (pw == 1 || kDecay) g.rs = static_cast<uint32_t>(gsc[base + static_cast<uint32_t>(min(lane, last)) * H]);
             }
         };
         // rows past the end become zeros (a bitwise mask keeps the registers
@@ -870,20 +876,21 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
         auto masked = [](uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); };
         auto commit = [&](auto par) {
             typename Lds::Raw &R = s.raw[decltype(par)::value];
+            const Stage &g = st[decltype(par)::value];
 #pragma unroll
             for (int i = 0; i < NQK; ++i) {
                 const int row = qrow + RPI * i;
-                const uint32_t m = 0u - ((okm >> i) & 1u);
-                *reinterpret_cast<uint4 *>(&R.q[row * KS + (lane % PPR) * 8]) = masked(rq[i], m);
-                *reinterpret_cast<uint4 *>(&R.k[row * KS + (lane % PPR) * 8]) = masked(rk[i], m);
+                const uint32_t m = 0u - ((g.okm >> i) & 1u);
+                *reinterpret_cast<uint4 *>(&R.q[row * KS + (lane % PPR) * 8]) = masked(g.q[i], m);
+                *reinterpret_cast<uint4 *>(&R.k[row * KS + (lane % PPR) * 8]) = masked(g.k[i], m);
             }
-            *reinterpret_cast<uint4 *>(&R.v[vrow * Lds::VS + 8 * (lane & 3)]) = masked(rv, 0u - ((okm >> NQK) & 1u));
-            const bool gok = (okm >> (NQK + 1)) & 1u;
+            *reinterpret_cast<uint4 *>(&R.v[vrow * Lds::VS + 8 * (lane & 3)]) = masked(g.v, 0u - ((g.okm >> NQK) & 1u));
+            const bool gok = (g.okm >> (NQK + 1)) & 1u;
             if (pw == 0) {
-                const float al = bf16_bits_to_f32(static_cast<uint16_t>(rs));
+                const float al = bf16_bits_to_f32(static_cast<uint16_t>(g.rs));
                 s.la[lane] = (kDecay && gok) ? fmaxf(__builtin_amdgcn_logf(al), -200.f) : 0.f;
             } else if (pw == 1) {
-                s.beta[lane] = gok ? bf16_bits_to_f32(static_cast<uint16_t>(rs)) : 0.f;
+                s.beta[lane] = gok ? bf16_bits_to_f32(static_cast<uint16_t>(g.rs)) : 0.f;
             }
         };
         unsigned int target = 0;
@@ -955,17 +962,15 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
                 typedef __attribute__((address_space(3))) volatile const f32x4 vlds_f4;
                 const auto lt = reinterpret_cast<__attribute__((address_space(3))) const float *>(
                     (__attribute__((address_space(3))) const void *)&s.lt[I][4 * q]);
-                f32x4 lj[15];   // L[4q + r][j] for every column j, all reads issued together
-#pragma unroll
-                for (int j = 0; j < 15; ++j) lj[j] = *reinterpret_cast<vlds_f4 *>(lt + j * LTS);
                 float x[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == col) ? 1.f : 0.f;
                 auto sweep = [&](auto jc) {
                     constexpr int j = decltype(jc)::value;
-                    const float xj = quad_bcast<j / 4>(x[j % 4]);  // X[j][col]
+                    const f32x4 lj = *reinterpret_cast<vlds_f4 *>(lt + j * LTS);  // L[4q + r][j]
+                    const float xj = quad_bcast<j / 4>(x[j % 4]);                // X[j][col]
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) x[r] = fmaf(-lj[j][r], xj, x[r]);
+                    for (int r = 0; r < 4; ++r) x[r] = fmaf(-lj[r], xj, x[r]);
                 };
                 static_for<15>(sweep);
                 // D diag(beta) and -D diag(beta gamma): element (row, col) goes to
@@ -1002,27 +1007,28 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
         };
 
         if (nchunks > 0) {
-            fetch(0);
+            fetch(ic<0>{}, 0);
+            if (nchunks > 1) fetch(ic<1>{}, 1);
             commit(ic<0>{});
-            if (nchunks > 1) fetch(1);
+            if (nchunks > 2) fetch(ic<0>{}, 2);
             psync();
             derive(ic<0>{});
         }
         lds_barrier();  // chunk 0 staged and derived
         for (int c = 0; c < nchunks; c += 2) {
-            // during chunk c: stage and derive chunk c + 1 (buffer 1)
+            // during chunk c: stage and derive chunk c + 1 (buffers 1)
             if (c + 1 < nchunks) {
                 commit(ic<1>{});
-                if (c + 2 < nchunks) fetch(c + 2);
+                if (c + 3 < nchunks) fetch(ic<1>{}, c + 3);
                 psync();
                 derive(ic<1>{});
             }
             lds_barrier();
             if (c + 1 < nchunks) {
-                // during chunk c + 1: chunk c + 2 (buffer 0)
+                // during chunk c + 1: chunk c + 2 (buffers 0)
                 if (c + 2 < nchunks) {
                     commit(ic<0>{});
-                    if (c + 3 < nchunks) fetch(c + 3);
+                    if (c + 4 < nchunks) fetch(ic<0>{}, c + 4);
                     psync();
                     derive(ic<0>{});
                 }
