@@ -58,6 +58,26 @@ def algorithmic_flops(w) -> int:
     return n_th * 7 * w.dk * w.dv
 
 
+def measured_traffic(w, ran: str):
+    """HBM bytes per launch from the committed rocprofv3 counter record
+    (profiles/traffic.json), or None when that record was taken on another
+    workload or on a different revision of the kernel source."""
+    import hashlib
+
+    if ran != "chunked" or w.variant == "vla":
+        return None
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "gated_linear_attention_chunked_amd", "csrc", "delta_chunked.hip")
+    try:
+        rec = json.load(open(path))["kernels"]["delta_chunked.hip"]
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sha256") != sha or rec.get("workload") != w.name:
+        return None
+    return float(rec["bytes_per_launch"])
+
+
 def cpu_threads(chains: int) -> int:
     try:
         avail = len(os.sched_getaffinity(0))
@@ -180,7 +200,7 @@ def main():
     aflops = algorithmic_flops(w)
     achieved_gbs = abytes / mean_launch_s / 1e9
     roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(w, ran),
                 "algorithmic_bytes_per_launch": abytes,
                 "mean_launch_us": mean_launch_s * 1e6,
                 "median_launch_us": float(np.median(launch_ms)) * 1e3,
