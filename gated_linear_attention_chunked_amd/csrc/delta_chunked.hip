@@ -16,28 +16,17 @@
 // Every exponent is g_t - g_s with s <= t (or g_C - g_t), so no factor exceeds
 // one and strong decays underflow to zero instead of overflowing.
 //
-// Schedule.  One workgroup (4 waves) per (b, h, 32-wide slice of dv); rows of
-// W are independent, so slices never communicate.  The workgroup walks the
-// chunks in order.  Per chunk:
-//   staging   q, k (row-major and transposed), v (transposed, fp32) and the
-//             gates into LDS from registers prefetched during the previous
-//             chunk;
-//   prologue  (all waves) wave prefix scan of log a; the lower 16x16 tiles of
-//             E K^T and Q K^T on 16x16x32 bf16 MFMA; masks and gates applied
-//             in fp32; the four diagonal 16x16 blocks of I + L inverted by
-//             forward substitution in fp32;
-//   carry     (waves 0 and 1, one 16-column tile of the slice each) E S^T and
-//             Q S^T on MFMA, the right-hand side, a blockwise forward solve on
-//             16x16x16 MFMA (U_i = D_i (R_i - sum_{j<i} L_ij U_j)), Y, and the
-//             state update accumulated straight into the state registers.
+// Schedule: one workgroup of 8 waves per (b, h, 32-wide slice of dv); rows of
+// W are independent, so slices never communicate.  Waves are split into a
+// carry, an output and a producer role; see the pipelined schedule below.
 // The state slice S^T (dk x 16 per carry wave) lives in MFMA accumulator
 // layout for the whole scan.  An accumulator tile holds 4 consecutive rows per
 // lane, while a B operand wants 8 consecutive reduction indices; since a
 // contraction does not care how its reduction index is ordered, two stacked
 // accumulator tiles serve directly as a B operand if the A operand is read
 // with the same order (rows 4g..4g+3 and 16+4g..16+4g+3 of each 32-block).
-// The same trick feeds U and the right-hand side to the next products without
-// an LDS round trip.
+// The same trick feeds U and the solve's right-hand sides to the next
+// products without an LDS round trip.
 #include <array>
 #include <type_traits>
 
@@ -53,9 +42,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;    // chunk length (tokens)
 constexpr int BV = 32;   // dv columns per workgroup
-constexpr int NT = 256;  // threads per workgroup (4 waves)
-constexpr int CS = C + 8;  // row stride (elements) of C-wide bf16 LDS tiles
-constexpr int DS = 24;     // row stride of the 16x16 diagonal inverses
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -67,14 +53,7 @@ __device__ __forceinline__ bf16x4 bf4(f32x4 x) { return __builtin_convertvector(
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-__device__ __forceinline__ bf16x4 lds4(const __bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
 
-// A operand of a 16x16x32 product from a row-major bf16 LDS matrix: rows
-// r0..r0+15, reduction columns c0..c0+31 taken in accumulator order.
-__device__ __forceinline__ bf16x8 row_frag(const __bf16 *m, int stride, int r0, int c0, int lane) {
-    const __bf16 *p = m + (r0 + (lane & 15)) * stride + c0 + 4 * (lane >> 4);
-    return cat8(lds4(p), lds4(p + 16));
-}
 // The same fragment read as two independent 8-byte LDS loads.  The loads
 // are volatile, so the compiler keeps them as single ds_read_b64 with
 // immediate offsets instead of fusing the pair into ds_read2_b64: on gfx950 a
@@ -102,341 +81,6 @@ __device__ __forceinline__ bf16x4 col_gather4(const __bf16 *m, int stride, int r
 __device__ __forceinline__ bf16x8 col_frag(const __bf16 *m, int stride, int r0, int c0, int lane) {
     return cat8(col_gather4(m, stride, r0, c0, lane), col_gather4(m, stride, r0 + 16, c0, lane));
 }
-// A operand of a 16x16x16 product: the 16x16 block at (r0, c0).
-__device__ __forceinline__ bf16x4 blk_frag(const __bf16 *m, int stride, int r0, int c0, int lane) {
-    return lds4(m + (r0 + (lane & 15)) * stride + c0 + 4 * (lane >> 4));
-}
-
-struct Raw16 {  // 16 bytes of bf16 from global memory
-    uint4 u;
-};
-
-template <int VARIANT, int DK>
-struct ChunkLds {
-    static constexpr bool kGates2 = VARIANT == kGatedDeltaNet2;
-    static constexpr int KS = DK + 8;  // row stride of dk-wide bf16 tiles
-    alignas(16) __bf16 q[C * KS];
-    alignas(16) __bf16 k[C * KS];
-    alignas(16) __bf16 e[kGates2 ? C * KS : 8];  // erase-gated keys (Gated DeltaNet-2)
-    alignas(16) __bf16 kt[DK * CS];              // keys transposed: [dk][t]
-    alignas(16) float vt[BV * (C + 4)];          // value targets transposed: [v][t]
-    alignas(16) __bf16 aqk[C * CS];              // lower(Q K^T) * Gamma
-    alignas(16) __bf16 ln[C * CS];               // -L (strictly lower blocks used)
-    alignas(16) __bf16 dinv[4 * 16 * DS];        // inverses of the diagonal blocks of I + L
-    alignas(16) float ld[4 * 16 * 17];           // diagonal blocks of L (fp32)
-    alignas(16) float loga[C];
-    alignas(16) float beta[C];
-    alignas(16) float g[C];
-    alignas(16) float gam[C];
-    alignas(16) float sc[C];
-    alignas(16) __bf16 y[C * (BV + 8)];
-};
-
-template <int VARIANT, int DK>
-__global__ __launch_bounds__(NT) void delta_chunked_kernel(DeltaArgs a) {
-    constexpr bool kGates2 = VARIANT == kGatedDeltaNet2;
-    constexpr bool kDecay = VARIANT != kDeltaNet;
-    constexpr int KS = DK + 8;
-    constexpr int KSTEP = DK / 32;   // 32-wide reduction steps over dk
-    constexpr int KT = DK / 16;      // 16-row tiles of S^T
-    constexpr int ROW16 = DK / 8;    // 16-byte pieces per dk-row
-    constexpr int QK_LOADS = C * ROW16 / NT;
-    static_assert(QK_LOADS * NT == C * ROW16, "q/k staging");
-
-    __shared__ ChunkLds<VARIANT, DK> s;
-
-    const int T = static_cast<int>(a.T), H = static_cast<int>(a.H), dv = a.dv;
-    const int slices = dv / BV;
-    int head, slice;
-    xcd_group_map(blockIdx.x, static_cast<int>(a.B * a.H), slices, head, slice);
-    const int b = head / H, h = head % H;
-    const int v0 = slice * BV;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lg = lane >> 4, lc = lane & 15;
-
-    const uint16_t *gq = static_cast<const uint16_t *>(a.q);
-    const uint16_t *gk = static_cast<const uint16_t *>(a.k);
-    const uint16_t *gv = static_cast<const uint16_t *>(a.v);
-    const uint16_t *geb = static_cast<const uint16_t *>(a.erase_b);
-    const uint16_t *gww = static_cast<const uint16_t *>(a.write_w);
-    const uint16_t *gal = static_cast<const uint16_t *>(a.alpha);
-    const uint16_t *gbe = static_cast<const uint16_t *>(a.beta);
-    auto tok = [&](int t) { return (static_cast<int64_t>(b) * T + t) * H + h; };
-
-    // Upper tiles (0,1) and (2,3) of Q K^T enter the 32-wide reduction blocks of
-    // the Y product; they are never written, so clear them once.
-    for (int i = tid; i < C * CS; i += NT) s.aqk[i] = static_cast<__bf16>(0.f);
-
-    // ---------------------------------------------------------- state
-    // Carry waves 0, 1 own S^T[:, 16*wave .. 16*wave+15] as KT accumulator tiles.
-    const bool carry = wave < 2;
-    f32x4 St[KT];
-    {
-        const int v = v0 + 16 * (wave & 1) + lc;
-        const int64_t base = (static_cast<int64_t>(head) * dv + v) * DK;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            if (carry && a.state_in) {
-                const float4 x = *reinterpret_cast<const float4 *>(a.state_in + base + 16 * kt + 4 * lg);
-                St[kt] = f32x4{x.x, x.y, x.z, x.w};
-            } else {
-                St[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-    }
-
-    // ---------------------------------------------------------- prefetch
-    Raw16 rq[QK_LOADS], rk[QK_LOADS], re[kGates2 ? QK_LOADS : 1];
-    Raw16 rv, rw;
-    float rsc = 0.f;  // thread t < 64: log a_t; 64 <= t < 128: beta_t
-    const int nchunks = (T + C - 1) / C;
-    auto fetch = [&](int c) {
-        const int t0 = c * C;
-#pragma unroll
-        for (int i = 0; i < QK_LOADS; ++i) {
-            const int idx = tid + NT * i, row = idx / ROW16, part = idx % ROW16;
-            const bool ok = t0 + row < T;
-            const int64_t off = tok(t0 + row) * DK + part * 8;
-            rq[i].u = ok ? *reinterpret_cast<const uint4 *>(gq + off) : make_uint4(0, 0, 0, 0);
-            rk[i].u = ok ? *reinterpret_cast<const uint4 *>(gk + off) : make_uint4(0, 0, 0, 0);
-            if constexpr (kGates2)
-                re[i].u = ok ? *reinterpret_cast<const uint4 *>(geb + off) : make_uint4(0, 0, 0, 0);
-        }
-        {
-            const int row = tid >> 2, part = tid & 3;  // 64 rows x 4 pieces of 8
-            const bool ok = t0 + row < T;
-            const int64_t off = tok(t0 + row) * dv + v0 + part * 8;
-            rv.u = ok ? *reinterpret_cast<const uint4 *>(gv + off) : make_uint4(0, 0, 0, 0);
-            if constexpr (kGates2)
-                rw.u = ok ? *reinterpret_cast<const uint4 *>(gww + off) : make_uint4(0, 0, 0, 0);
-        }
-        if (tid < 2 * C) {
-            const int t = tid & (C - 1);
-            const bool ok = t0 + t < T;
-            if (tid < C) {
-                float la = 0.f;
-                if (kDecay && ok) la = fmaxf(logf(bf16_bits_to_f32(gal[tok(t0 + t)])), -150.f);
-                rsc = la;
-            } else {
-                rsc = ok ? bf16_bits_to_f32(gbe[tok(t0 + t)]) : 0.f;
-            }
-        }
-    };
-    auto unpack = [](uint32_t w, float &lo, float &hi) {
-        lo = __uint_as_float(w << 16);
-        hi = __uint_as_float(w & 0xffff0000u);
-    };
-    auto commit = [&]() {
-#pragma unroll
-        for (int i = 0; i < QK_LOADS; ++i) {
-            const int idx = tid + NT * i, row = idx / ROW16, part = idx % ROW16;
-            *reinterpret_cast<uint4 *>(&s.q[row * KS + part * 8]) = rq[i].u;
-            *reinterpret_cast<uint4 *>(&s.k[row * KS + part * 8]) = rk[i].u;
-            const uint32_t kw[4] = {rk[i].u.x, rk[i].u.y, rk[i].u.z, rk[i].u.w};
-            uint16_t *ktp = reinterpret_cast<uint16_t *>(s.kt);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                ktp[(part * 8 + 2 * j) * CS + row] = static_cast<uint16_t>(kw[j] & 0xffffu);
-                ktp[(part * 8 + 2 * j + 1) * CS + row] = static_cast<uint16_t>(kw[j] >> 16);
-            }
-            if constexpr (kGates2) {
-                const uint32_t bw[4] = {re[i].u.x, re[i].u.y, re[i].u.z, re[i].u.w};
-                uint32_t ew[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float k0, k1, b0, b1;
-                    unpack(kw[j], k0, k1);
-                    unpack(bw[j], b0, b1);
-                    ew[j] = static_cast<uint32_t>(f32_to_bf16_bits(k0 * b0)) |
-                            (static_cast<uint32_t>(f32_to_bf16_bits(k1 * b1)) << 16);
-                }
-                *reinterpret_cast<uint4 *>(&s.e[row * KS + part * 8]) = make_uint4(ew[0], ew[1], ew[2], ew[3]);
-            }
-        }
-        {
-            const int row = tid >> 2, part = tid & 3;
-            const uint32_t vw[4] = {rv.u.x, rv.u.y, rv.u.z, rv.u.w};
-            const uint32_t ww[4] = {rw.u.x, rw.u.y, rw.u.z, rw.u.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float x0, x1;
-                unpack(vw[j], x0, x1);
-                if constexpr (kGates2) {
-                    float w0, w1;
-                    unpack(ww[j], w0, w1);
-                    x0 *= w0;
-                    x1 *= w1;
-                }
-                s.vt[(part * 8 + 2 * j) * (C + 4) + row] = x0;
-                s.vt[(part * 8 + 2 * j + 1) * (C + 4) + row] = x1;
-            }
-        }
-        if (tid < C)
-            s.loga[tid] = rsc;
-        else if (tid < 2 * C)
-            s.beta[tid - C] = rsc;
-    };
-
-    if (nchunks > 0) fetch(0);
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * C;
-        const int nvalid = min(C, T - t0);
-        __syncthreads();  // LDS of the previous chunk is no longer read
-        commit();
-        __syncthreads();
-        if (c + 1 < nchunks) fetch(c + 1);
-
-        // ---- gate prefix scan (wave 0): g, gamma = exp(g), sc = exp(g_C - g)
-        if (wave == 0) {
-            float x = s.loga[lane];
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float y = __shfl_up(x, o, 64);
-                if (lane >= o) x += y;
-            }
-            const float gl = __shfl(x, 63, 64);
-            s.g[lane] = x;
-            s.gam[lane] = expf(x);
-            s.sc[lane] = expf(gl - x);
-        }
-        __syncthreads();
-
-        // ---- lower tiles of E K^T (-> L) and Q K^T (-> Aqk), 20 tiles over 4 waves
-        for (int job = wave; job < 20; job += 4) {
-            const bool isqk = job >= 10;
-            int jj = isqk ? job - 10 : job, ti = 0;
-            while (jj > ti) { jj -= ti + 1; ++ti; }
-            const int si = jj;
-            const __bf16 *am = isqk ? s.q : (kGates2 ? s.e : s.k);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int p = 0; p < KSTEP; ++p)
-                acc = mfma32(row_frag(am, KS, 16 * ti, 32 * p, lane), row_frag(s.k, KS, 16 * si, 32 * p, lane), acc);
-            const int scol = 16 * si + lc;
-            const float gs = s.g[scol];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * ti + 4 * lg + r;
-                const float gm = expf(fminf(s.g[t] - gs, 0.f));
-                if (isqk) {
-                    const float val = scol <= t ? acc[r] * gm : 0.f;
-                    s.aqk[t * CS + scol] = static_cast<__bf16>(val);
-                } else {
-                    const float val = scol < t ? s.beta[t] * gm * acc[r] : 0.f;
-                    if (ti == si)
-                        s.ld[(ti * 16 + (t & 15)) * 17 + lc] = val;
-                    else
-                        s.ln[t * CS + scol] = static_cast<__bf16>(-val);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- inverses of the diagonal blocks of I + L (wave w: block w; lane = column)
-        if (lane < 16) {
-            const float *L = &s.ld[wave * 16 * 17];
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = i == lane ? 1.f : 0.f;
-#pragma unroll
-            for (int i = 1; i < 16; ++i) {
-                float acc = 0.f;
-#pragma unroll
-                for (int m = 0; m < i; ++m) acc = fmaf(L[i * 17 + m], x[m], acc);
-                if (i > lane) x[i] = -acc;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s.dinv[(wave * 16 + i) * DS + lane] = static_cast<__bf16>(x[i]);
-        }
-        __syncthreads();
-
-        // ---- carry (waves 0, 1)
-        if (carry) {
-            const int vt = wave;  // 16-column tile within the slice
-            bf16x8 bS[KSTEP];
-#pragma unroll
-            for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(bf4(St[2 * p]), bf4(St[2 * p + 1]));
-            const __bf16 *em = kGates2 ? s.e : s.k;
-            f32x4 rhs[4], y[4];
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                f32x4 kp = {0.f, 0.f, 0.f, 0.f}, qp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < KSTEP; ++p) {
-                    kp = mfma32(row_frag(em, KS, 16 * ti, 32 * p, lane), bS[p], kp);
-                    qp = mfma32(row_frag(s.q, KS, 16 * ti, 32 * p, lane), bS[p], qp);
-                }
-                const int t = 16 * ti + 4 * lg;
-                const float4 z = *reinterpret_cast<const float4 *>(&s.vt[(16 * vt + lc) * (C + 4) + t]);
-                const float zz[4] = {z.x, z.y, z.z, z.w};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    rhs[ti][r] = s.beta[t + r] * fmaf(-s.gam[t + r], kp[r], zz[r]);
-                    y[ti][r] = s.gam[t + r] * qp[r];
-                }
-            }
-            // blockwise forward solve: U_i = D_i (R_i - sum_{j<i} L_ij U_j)
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            f32x4 u[4];
-            bf16x4 ub[4];
-            u[0] = mfma16(blk_frag(s.dinv, DS, 0, 0, lane), bf4(rhs[0]), zero);
-            ub[0] = bf4(u[0]);
-#pragma unroll
-            for (int i = 1; i < 4; ++i) {
-                f32x4 x = rhs[i];
-#pragma unroll
-                for (int j = 0; j < i; ++j) x = mfma16(blk_frag(s.ln, CS, 16 * i, 16 * j, lane), ub[j], x);
-                u[i] = mfma16(blk_frag(s.dinv, DS, 16 * i, 0, lane), bf4(x), zero);
-                ub[i] = bf4(u[i]);
-            }
-            // Y = gamma Q S^T + lower(Q K^T * Gamma) U
-            const bf16x8 bU0 = cat8(ub[0], ub[1]), bU1 = cat8(ub[2], ub[3]);
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                y[ti] = mfma32(row_frag(s.aqk, CS, 16 * ti, 0, lane), bU0, y[ti]);
-                if (ti >= 2) y[ti] = mfma32(row_frag(s.aqk, CS, 16 * ti, 32, lane), bU1, y[ti]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    s.y[(16 * ti + 4 * lg + r) * (BV + 8) + 16 * vt + lc] = static_cast<__bf16>(y[ti][r]);
-            }
-            // S^T = gamma_C S^T + K^T diag(gamma_C / gamma) U
-            f32x4 us[4];
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) us[ti][r] = u[ti][r] * s.sc[16 * ti + 4 * lg + r];
-            const bf16x8 bW0 = cat8(bf4(us[0]), bf4(us[1])), bW1 = cat8(bf4(us[2]), bf4(us[3]));
-            const float gC = s.gam[C - 1];
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                f32x4 acc = St[kt] * gC;
-                acc = mfma32(row_frag(s.kt, CS, 16 * kt, 0, lane), bW0, acc);
-                acc = mfma32(row_frag(s.kt, CS, 16 * kt, 32, lane), bW1, acc);
-                St[kt] = acc;
-            }
-        }
-        __syncthreads();
-
-        // ---- store the output tile (nvalid rows x 32 columns)
-        {
-            const int row = tid >> 2, part = tid & 3;
-            if (row < nvalid) {
-                const uint4 x = *reinterpret_cast<const uint4 *>(&s.y[row * (BV + 8) + part * 8]);
-                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.out) + tok(t0 + row) * dv + v0 + part * 8) = x;
-            }
-        }
-    }
-
-    if (carry && a.state_out) {
-        const int v = v0 + 16 * wave + lc;
-        const int64_t base = (static_cast<int64_t>(head) * dv + v) * DK;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-            *reinterpret_cast<float4 *>(a.state_out + base + 16 * kt + 4 * lg) =
-                make_float4(St[kt][0], St[kt][1], St[kt][2], St[kt][3]);
-    }
-}
-
 // ===========================================================================
 // Pipelined schedule (DeltaNet, Gated DeltaNet): 8 waves per workgroup, two
 // per SIMD, in three roles.  With D_i = (I + L_ii)^{-1} the inverse of
@@ -465,14 +109,15 @@ constexpr int NQB = 10;    // lower 16x16 blocks including the diagonal
 constexpr int NT8 = 512;   // threads per workgroup of the WY schedule
 constexpr int LTS = 20;    // column stride (floats) of the fp32 diagonal blocks
 
-template <int DK>
+template <int DK, bool GATES2>
 struct WyLds {
     static constexpr int KS = DK + 8;
     static constexpr int VS = BV + 8;
     struct Raw {  // token rows of one chunk, double-buffered (carry/output read chunk c)
         alignas(16) __bf16 q[C * KS];
         alignas(16) __bf16 k[C * KS];
-        alignas(16) __bf16 v[C * VS];          // the workgroup's value columns
+        alignas(16) __bf16 e[GATES2 ? C * KS : 8];  // erase-gated keys b * k (Gated DeltaNet-2)
+        alignas(16) __bf16 v[C * VS];          // value targets of the workgroup's columns (w * v for Gated DeltaNet-2)
     };
     struct Der {  // state-independent matrices of one chunk, double-buffered
         alignas(16) bf16x4 dtil[4][64];        // D_i diag(beta)_i, A-operand order
@@ -599,21 +244,22 @@ struct TilesB {
 };
 // E K^T tiles per producer i: three each for producers 0-2, which also take
 // the off-diagonal tiles of block row 3, so producer 3 only forms (3, 3).
+// tmask / smask: the 16-row blocks used as rows (E) and as columns (K).
 template <int I> struct RowTiles;
 template <> struct RowTiles<0> {
-    static constexpr int n = 3, kmask = 0xb;
+    static constexpr int n = 3, tmask = 0x9, smask = 0x3;
     static constexpr int ti[3] = {0, 3, 3}, si[3] = {0, 0, 1};
 };
 template <> struct RowTiles<1> {
-    static constexpr int n = 3, kmask = 0xf;
+    static constexpr int n = 3, tmask = 0xa, smask = 0x7;
     static constexpr int ti[3] = {1, 1, 3}, si[3] = {0, 1, 2};
 };
 template <> struct RowTiles<2> {
-    static constexpr int n = 3, kmask = 0x7;
+    static constexpr int n = 3, tmask = 0x4, smask = 0x7;
     static constexpr int ti[3] = {2, 2, 2}, si[3] = {0, 1, 2};
 };
 template <> struct RowTiles<3> {
-    static constexpr int n = 1, kmask = 0x8;
+    static constexpr int n = 1, tmask = 0x8, smask = 0x8;
     static constexpr int ti[1] = {3}, si[1] = {3};
 };
 __device__ __forceinline__ constexpr int lower_block(int i, int j) { return i * (i - 1) / 2 + j; }  // j < i
@@ -625,7 +271,8 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
     constexpr int KS = DK + 8;
     constexpr int KSTEP = DK / 32;
     constexpr int KT = DK / 16;
-    using Lds = WyLds<DK>;
+    constexpr bool kGates2 = VARIANT == kGatedDeltaNet2;
+    using Lds = WyLds<DK, kGates2>;
     __shared__ Lds s;
 
     const int T = static_cast<int>(a.T), H = static_cast<int>(a.H), dv = a.dv;
@@ -690,7 +337,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p)
 #pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) kf[p][ti] = row_frag2(R.k, KS, 16 * ti, 32 * p, lane);
+                    for (int ti = 0; ti < 4; ++ti) kf[p][ti] = row_frag2(kGates2 ? R.e : R.k, KS, 16 * ti, 32 * p, lane);
                 bf16x4 vb[4], dt[4], dh[4], mj[NLB];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -839,17 +486,24 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
         const int qrow = 16 * pw + lane / PPR;  // chunk row of this lane's first q/k piece
         const int vrow = 16 * pw + (lane >> 2);
         // Two staging sets, one per chunk parity: loads run two chunks ahead.
+        // NS staging sets: loads run NS chunks ahead.  Gated DeltaNet-2 stages
+        // two more streams (erase and write gates) and keeps one set.
+        constexpr int NS = kGates2 ? 1 : 2;
+        constexpr int NQKG = kGates2 ? NQK : 1;
+        const uint16_t *geb = static_cast<const uint16_t *>(a.erase_b);
+        const uint16_t *gww = static_cast<const uint16_t *>(a.write_w);
         struct Stage {
             uint4 q[NQK], k[NQK], v;
+            uint4 b[NQKG], w;  // erase / write gates (Gated DeltaNet-2)
             uint32_t rs;   // raw bf16 bits of the decay (pw 0) or beta (pw 1) of row `lane`
             uint32_t okm;  // bit i: row of q/k load i inside the sequence; bit NQK: v row; bit NQK+1: gate row
         };
-        Stage st[2];
+        Stage st[NS];
         // Loads read clamped, always valid rows; rows past the end are replaced
         // by padding at commit, so no loaded value is consumed here and the
         // loads stay in flight until that chunk's staging.
         auto fetch = [&](auto par, int c) {
-            Stage &g = st[decltype(par)::value];
+            Stage &g = st[decltype(par)::value % NS];
             const int t0 = c * C, last = T - 1 - t0;
             const int64_t base = tok(t0);
             const uint16_t *q0 = gq + base * DK, *k0 = gk + base * DK;
@@ -861,10 +515,12 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
                 const uint32_t o = static_cast<uint32_t>(min(r, last)) * hdk + (lane % PPR) * 8;
                 g.q[i] = *reinterpret_cast<const uint4 *>(q0 + o);
                 g.k[i] = *reinterpret_cast<const uint4 *>(k0 + o);
+                if constexpr (kGates2) g.b[i] = *reinterpret_cast<const uint4 *>(geb + base * DK + o);
             }
             g.okm |= (vrow <= last ? 1u : 0u) << NQK;
-            g.v = *reinterpret_cast<const uint4 *>(gv + base * dv + static_cast<uint32_t>(min(vrow, last)) * hdv +
-                                                   v0 + 8 * (lane & 3));
+            const uint32_t ov = static_cast<uint32_t>(min(vrow, last)) * hdv + v0 + 8 * (lane & 3);
+            g.v = *reinterpret_cast<const uint4 *>(gv + base * dv + ov);
+            if constexpr (kGates2) g.w = *reinterpret_cast<const uint4 *>(gww + base * dv + ov);
             g.rs = 0u;
             if (pw <= 1) {
                 g.okm |= (lane <= last ? 1u : 0u) << (NQK + 1);
@@ -874,17 +530,34 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
         // rows past the end become zeros (a bitwise mask keeps the registers
         // out of the select-of-aggregates form that lands them in scratch)
         auto masked = [](uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); };
+        // elementwise product of eight bf16 pairs, rounded to bf16 (nearest even)
+        auto mul8 = [](uint4 x, uint4 y) {
+            const uint32_t xa[4] = {x.x, x.y, x.z, x.w}, ya[4] = {y.x, y.y, y.z, y.w};
+            uint32_t r[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float lo = bf16_bits_to_f32(static_cast<uint16_t>(xa[j])) * bf16_bits_to_f32(static_cast<uint16_t>(ya[j]));
+                const float hi = bf16_bits_to_f32(static_cast<uint16_t>(xa[j] >> 16)) *
+                                 bf16_bits_to_f32(static_cast<uint16_t>(ya[j] >> 16));
+                r[j] = static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+            }
+            return make_uint4(r[0], r[1], r[2], r[3]);
+        };
         auto commit = [&](auto par) {
             typename Lds::Raw &R = s.raw[decltype(par)::value];
-            const Stage &g = st[decltype(par)::value];
+            const Stage &g = st[decltype(par)::value % NS];
 #pragma unroll
             for (int i = 0; i < NQK; ++i) {
                 const int row = qrow + RPI * i;
                 const uint32_t m = 0u - ((g.okm >> i) & 1u);
                 *reinterpret_cast<uint4 *>(&R.q[row * KS + (lane % PPR) * 8]) = masked(g.q[i], m);
                 *reinterpret_cast<uint4 *>(&R.k[row * KS + (lane % PPR) * 8]) = masked(g.k[i], m);
+                if constexpr (kGates2)
+                    *reinterpret_cast<uint4 *>(&R.e[row * KS + (lane % PPR) * 8]) = masked(mul8(g.k[i], g.b[i]), m);
             }
-            *reinterpret_cast<uint4 *>(&R.v[vrow * Lds::VS + 8 * (lane & 3)]) = masked(g.v, 0u - ((g.okm >> NQK) & 1u));
+            const uint32_t mv = 0u - ((g.okm >> NQK) & 1u);
+            *reinterpret_cast<uint4 *>(&R.v[vrow * Lds::VS + 8 * (lane & 3)]) =
+                masked(kGates2 ? mul8(g.v, g.w) : g.v, mv);
             const bool gok = (g.okm >> (NQK + 1)) & 1u;
             if (pw == 0) {
                 const float al = bf16_bits_to_f32(static_cast<uint16_t>(g.rs));
@@ -924,12 +597,17 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
                 for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p) {
-                    bf16x8 kf[4];
+                    bf16x8 kf[4], ef[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if ((Tl::kmask >> j) & 1) kf[j] = row_frag2(R.k, KS, 16 * j, 32 * p, lane);
+                    for (int j = 0; j < 4; ++j) {  // key rows as columns (smask) and, unless E is
+                                                    // separate, as rows (tmask); E rows for Gated DeltaNet-2
+                        if (((kGates2 ? Tl::smask : Tl::smask | Tl::tmask) >> j) & 1)
+                            kf[j] = row_frag2(R.k, KS, 16 * j, 32 * p, lane);
+                        if (kGates2 && ((Tl::tmask >> j) & 1)) ef[j] = row_frag2(R.e, KS, 16 * j, 32 * p, lane);
+                    }
 #pragma unroll
-                    for (int j = 0; j < NT; ++j) acc[j] = mfma32(kf[Tl::ti[j]], kf[Tl::si[j]], acc[j]);
+                    for (int j = 0; j < NT; ++j)
+                        acc[j] = mfma32(kGates2 ? ef[Tl::ti[j]] : kf[Tl::ti[j]], kf[Tl::si[j]], acc[j]);
                 }
                 // E K^T tiles: lane (lg, lc) holds G[t = 16ti + 4lg + r][s = 16si + lc]
                 bf16x4 gneg[4];   // -G~_Ij in accumulator order (own block row only)
@@ -1006,32 +684,25 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
             else work(ic<3>{});
         };
 
+        // Preparing chunk n: stage it from its set, refill that set with
+        // chunk n + NS, then derive chunk n.
+        auto prepare = [&](auto par, int n) {
+            commit(par);
+            if (n + NS < nchunks) fetch(par, n + NS);
+            psync();
+            derive(par);
+        };
         if (nchunks > 0) {
             fetch(ic<0>{}, 0);
-            if (nchunks > 1) fetch(ic<1>{}, 1);
-            commit(ic<0>{});
-            if (nchunks > 2) fetch(ic<0>{}, 2);
-            psync();
-            derive(ic<0>{});
+            if (NS == 2 && nchunks > 1) fetch(ic<1>{}, 1);
+            prepare(ic<0>{}, 0);
         }
         lds_barrier();  // chunk 0 staged and derived
         for (int c = 0; c < nchunks; c += 2) {
-            // during chunk c: stage and derive chunk c + 1 (buffers 1)
-            if (c + 1 < nchunks) {
-                commit(ic<1>{});
-                if (c + 3 < nchunks) fetch(ic<1>{}, c + 3);
-                psync();
-                derive(ic<1>{});
-            }
+            if (c + 1 < nchunks) prepare(ic<1>{}, c + 1);  // during chunk c: chunk c + 1 (buffers 1)
             lds_barrier();
             if (c + 1 < nchunks) {
-                // during chunk c + 1: chunk c + 2 (buffers 0)
-                if (c + 2 < nchunks) {
-                    commit(ic<0>{});
-                    if (c + 4 < nchunks) fetch(ic<0>{}, c + 4);
-                    psync();
-                    derive(ic<0>{});
-                }
+                if (c + 2 < nchunks) prepare(ic<0>{}, c + 2);  // during chunk c + 1: chunk c + 2 (buffers 0)
                 lds_barrier();
             }
         }
@@ -1041,16 +712,9 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
 template <int VARIANT>
 hipError_t launch_var(const DeltaArgs &a, hipStream_t stream) {
     const unsigned blocks = static_cast<unsigned>(a.B * a.H * (a.dv / BV));
-    constexpr bool kPipe = VARIANT != kGatedDeltaNet2;
     switch (a.dk) {
-        case 64:
-            if constexpr (kPipe) delta_chunked_wy_kernel<VARIANT, 64><<<blocks, NT8, 0, stream>>>(a);
-            else delta_chunked_kernel<VARIANT, 64><<<blocks, NT, 0, stream>>>(a);
-            break;
-        case 128:
-            if constexpr (kPipe) delta_chunked_wy_kernel<VARIANT, 128><<<blocks, NT8, 0, stream>>>(a);
-            else delta_chunked_kernel<VARIANT, 128><<<blocks, NT, 0, stream>>>(a);
-            break;
+        case 64: delta_chunked_wy_kernel<VARIANT, 64><<<blocks, NT8, 0, stream>>>(a); break;
+        case 128: delta_chunked_wy_kernel<VARIANT, 128><<<blocks, NT8, 0, stream>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
