@@ -40,12 +40,28 @@ struct IoBF16 {
 };
 
 // ------------------------------------------------------------- reductions
-// Sum over aligned groups of W lanes (W a power of two <= 64); every lane of
-// the group receives the group's sum.
+// Sum over aligned groups of W lanes (W in {1, 2, 4, 8, 16, 64}); every lane
+// of the group receives the group's sum.  Within a 16-lane row the partial
+// sums move by DPP (quad swaps, then the 8- and 16-lane mirrors), which stay
+// in the vector ALU; a whole-wave sum then adds the four row sums read out
+// with readlane.  Each step adds a lane and its partner in both orders, so
+// every lane of a group ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int m = W / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 64, "group width");
+    if constexpr (W >= 2) x += dpp_mov<0xb1>(x);   // quad_perm [1,0,3,2]: partner lane ^ 1
+    if constexpr (W >= 4) x += dpp_mov<0x4e>(x);   // quad_perm [2,3,0,1]: partner lane ^ 2
+    if constexpr (W >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror: lane 7 - i of the 8
+    if constexpr (W >= 16) x += dpp_mov<0x140>(x); // row_mirror: lane 15 - i of the row
+    if constexpr (W == 64) {
+        const int xi = __float_as_int(x);
+        x = (__int_as_float(__builtin_amdgcn_readlane(xi, 0)) + __int_as_float(__builtin_amdgcn_readlane(xi, 16))) +
+            (__int_as_float(__builtin_amdgcn_readlane(xi, 32)) + __int_as_float(__builtin_amdgcn_readlane(xi, 48)));
+    }
     return x;
 }
 
