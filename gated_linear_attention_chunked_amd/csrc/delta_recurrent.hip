@@ -140,21 +140,40 @@ __global__ __launch_bounds__(kThreads) void delta_recurrent_kernel(DeltaArgs a) 
         if (t0 + TT < T) fetch(t0 + TT);  // overlaps the loads with this tile's math
 
         const int nt = min(TT, T - t0);
-        for (int t = 0; t < nt; ++t) {
-            float kk[CPT];
-            float p1 = 0.f, p2 = 0.f, p3 = 0.f;
+        // Per-token operands of this lane, read one token ahead so the LDS
+        // latency overlaps the previous token's update.
+        struct Tok {
+            float k[CPT], q[CPT], dec[kChanDecay ? CPT : 1], er[kGates2 ? CPT : 1];
+            float be, al, target;
+        };
+        auto load = [&](int t, Tok &o) {
 #pragma unroll
             for (int m = 0; m < CPT; ++m) {
                 const int j = lr + TPR * m;
-                const float kj = sk[t][j], qj = sq[t][j];
-                kk[m] = kj;
+                o.k[m] = sk[t][j];
+                o.q[m] = sq[t][j];
+                if constexpr (kChanDecay) o.dec[m] = sdec[t][j];
+                if constexpr (kGates2) o.er[m] = serase[t][j];
+            }
+            o.be = sbeta[t];
+            o.al = kScalarDecay ? salpha[t] : 1.f;
+            o.target = sv[t][rl];
+            if constexpr (kGates2) o.target *= swrite[t][rl];
+        };
+        Tok cur, nxt;
+        load(0, cur);
+        for (int t = 0; t < nt; ++t) {
+            if (t + 1 < nt) load(t + 1, nxt);
+            float p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+            for (int m = 0; m < CPT; ++m) {
+                const float kj = cur.k[m], qj = cur.q[m];
                 float rk_ = kj, rq_ = qj;
                 if constexpr (kChanDecay) {
-                    const float d = sdec[t][j];
-                    rk_ = d * kj;
-                    rq_ = d * qj;
+                    rk_ = cur.dec[m] * kj;
+                    rq_ = cur.dec[m] * qj;
                 }
-                if constexpr (kGates2) rk_ = serase[t][j] * kj;
+                if constexpr (kGates2) rk_ = cur.er[m] * kj;
                 p1 = fmaf(W[m], rk_, p1);
                 p2 = fmaf(W[m], rq_, p2);
                 p3 = fmaf(kj, qj, p3);
@@ -162,20 +181,16 @@ __global__ __launch_bounds__(kThreads) void delta_recurrent_kernel(DeltaArgs a) 
             p1 = group_sum<TPR>(p1);
             p2 = group_sum<TPR>(p2);
             p3 = group_sum<TPR>(p3);
-            const float be = sbeta[t];
-            const float al = kScalarDecay ? salpha[t] : 1.f;
-            float target = sv[t][rl];
-            if constexpr (kGates2) target *= swrite[t][rl];
-            const float r = target - al * p1;
-            const float br = be * r;
-            const float y = fmaf(br, p3, al * p2);
+            const float r = cur.target - cur.al * p1;
+            const float br = cur.be * r;
+            const float y = fmaf(br, p3, cur.al * p2);
 #pragma unroll
             for (int m = 0; m < CPT; ++m) {
-                float dec = al;
-                if constexpr (kChanDecay) dec = sdec[t][lr + TPR * m];
-                W[m] = fmaf(br, kk[m], dec * W[m]);
+                const float dec = kChanDecay ? cur.dec[m] : cur.al;
+                W[m] = fmaf(br, cur.k[m], dec * W[m]);
             }
             if (lr == 0) sy[t][rl] = y;
+            cur = nxt;
         }
         __syncthreads();
         // store the output tile: ROWS contiguous values per token

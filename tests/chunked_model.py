@@ -90,6 +90,40 @@ def delta_chunked(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None
     return out, state_out
 
 
+def kda_blocks_by_levels(K, Q, lg):
+    """Kimi Delta's two decayed Gram blocks of one 16-token chunk, formed the
+    way the chunked kernel's exact path forms them: entry (t, s), s < t, at
+    level b = highest set bit of t ^ s, with both factors taken against the
+    reference token m = (t & ~(2b - 1)) + b - 1 (so s <= m < t and each factor
+    is at most 1); the diagonal of Aqk undecayed.  lg: [16, dk] running log
+    decay.  Returns (Akk, Aqk) with Akk_ts = sum_c k_tc k_sc exp(lg_tc - lg_sc)
+    for s < t (zero elsewhere) and Aqk_ts the same with q_t, for s <= t."""
+    n = K.shape[0]
+    assert n == 16
+    Akk = np.zeros((n, n))
+    Aqk = np.zeros((n, n))
+    for b in (8, 4, 2, 1):
+        rows = np.zeros((n, K.shape[1]))   # exp(lg_t - lg_m) for t in the upper half of its block
+        cols = np.zeros((n, K.shape[1]))   # exp(lg_m - lg_s) for s in the lower half
+        for t in range(n):
+            m = (t & ~(2 * b - 1)) + b - 1
+            if t & b:
+                rows[t] = np.exp(lg[t] - lg[m])
+            else:
+                cols[t] = np.exp(lg[m] - lg[t])
+        assert rows.max(initial=0) <= 1 and cols.max(initial=0) <= 1
+        gk = (K * rows) @ (K * cols).T
+        gq = (Q * rows) @ (K * cols).T
+        for t in range(n):
+            for s in range(n):
+                x = t ^ s
+                if b <= x < 2 * b and t & b:
+                    Akk[t, s] = gk[t, s]
+                    Aqk[t, s] = gq[t, s]
+    Aqk[np.diag_indices(n)] = np.sum(Q * K, axis=1)
+    return Akk, Aqk
+
+
 def vla_chunked(q, k, v, p, A_in=None, S_in=None, C=64):
     B, T, H, d = q.shape
     out = np.zeros((B, T, H, d))

@@ -472,6 +472,28 @@ def test_chunked_form_equals_recurrence(variant, C):
     assert np.max(np.abs(s2 - st)) <= 1e-12 * np.max(np.abs(st))
 
 
+@pytest.mark.parametrize("scale", [0.3, 3.0, 30.0])
+def test_kda_level_blocks_equal_direct(scale):
+    """The reference-token levels that form Kimi Delta's decayed Gram blocks
+    without overflow cover every (t, s) with s <= t exactly once and equal
+    the direct per-channel sum, also for decays far below 2^-100 per chunk."""
+    r = rng0(92)
+    n, dk = 16, 24
+    K, Q = r.standard_normal((n, dk)), r.standard_normal((n, dk))
+    lg = np.cumsum(-scale * r.exponential(size=(n, dk)), axis=0)
+    Akk, Aqk = chunked_model.kda_blocks_by_levels(K, Q, lg)
+    t, s = np.tril_indices(n)
+    direct_k = np.zeros((n, n))
+    direct_q = np.zeros((n, n))
+    for i, j in zip(t, s):
+        w = np.exp(lg[i] - lg[j])
+        direct_q[i, j] = np.sum(Q[i] * K[j] * w)
+        if i > j:
+            direct_k[i, j] = np.sum(K[i] * K[j] * w)
+    np.testing.assert_allclose(Akk, direct_k, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(Aqk, direct_q, rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("C", [1, 4, 16, 64])
 def test_vla_chunked_form_equals_recurrence(C):
     r = rng0(91)

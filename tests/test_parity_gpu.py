@@ -175,7 +175,7 @@ def test_full_workload(name):
 
 
 # ---------------------------------------------------- chunked schedule
-CHUNKED = ["deltanet", "gdn", "gdn2"]
+CHUNKED = ["deltanet", "gdn", "kda", "gdn2"]
 
 
 @pytest.mark.parametrize("variant", CHUNKED)
@@ -194,16 +194,35 @@ def test_chunked_every_element(variant, dk, dv, T, gate_mu):
     U.check(w, got, ref, label=w.name)
 
 
-@pytest.mark.parametrize("variant", ["gdn", "gdn2"])
+@pytest.mark.parametrize("variant", ["gdn", "kda", "gdn2"])
 def test_chunked_zero_and_unit_decays(variant):
-    """alpha = 0 (memory cleared) and alpha = 1 tokens mixed into one chunk."""
+    """alpha = 0 (memory cleared) and alpha = 1 tokens mixed into one chunk;
+    for Kimi Delta also single channels cleared while the rest decay slowly."""
     w = _w(variant, "bf16", 1, 150, 2, 128, 128, seed=7100, gate_mu=-2.0)
     x = I.make_inputs(w)
     x["alpha"][:, 10:13] = 0.0
     x["alpha"][:, 70:90] = 1.0
+    if variant == "kda":
+        x["alpha"][:, 40, :, 3] = 0.0
+        x["alpha"][:, 100:104, 1, 60:70] = 0.0
     got = U.run_gpu(w, x, algo="chunked")
     ref = U.run_oracle(w, x)
     U.check(w, got, ref, label="zero/unit decays " + variant)
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+@pytest.mark.parametrize("gate_mu", [6.0, 4.5, 3.0])
+def test_kda_chunked_strong_channel_decay(dk, gate_mu):
+    """Per-channel decays strong enough that a 16-token chunk decays some
+    channels below 2^-100 (every chunk at mu = 6, some at mu = 4.5), which
+    the chunked Kimi Delta kernel handles without factoring the decay."""
+    w = _w("kda", "bf16", 2, 333, 2, dk, 64, seed=7200 + dk, gate_mu=gate_mu)
+    x = I.make_inputs(w)
+    s0 = (np.random.default_rng(dk).standard_normal((2, 2, 64, dk)) * 0.2).astype(np.float32)
+    s0 = s0.astype(np.float64)
+    got = U.run_gpu(w, x, algo="chunked", state_in=s0)
+    ref = U.run_oracle(w, x, state_in=s0)
+    U.check(w, got, ref, label=w.name + f" mu={gate_mu}")
 
 
 def test_chunked_rejects_unsupported():
@@ -211,7 +230,7 @@ def test_chunked_rejects_unsupported():
 
     import gated_linear_attention_chunked_amd as lam
 
-    w = _w("kda", "bf16", 1, 70, 1, 128, 128, seed=1)
+    w = _w("kda", "bf16", 1, 70, 1, 96, 128, seed=1)
     g = I.to_device(I.make_inputs(w), "bf16", "cuda")
     with pytest.raises(lam.LamError) as e:
         lam.forward("kda", g["q"], g["k"], g["v"], g["beta"], alpha=g["alpha"], algo="chunked")
