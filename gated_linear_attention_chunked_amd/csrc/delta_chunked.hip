@@ -419,7 +419,14 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
                 if constexpr (kGates2) g.b[i] = *reinterpret_cast<const uint4 *>(geb + base * DK + o);
             }
             g.okm |= (vrow <= last ? 1u : 0u) << NQK;
-            const uint32_t ov = static_cast<uint32_t>(min(vrow, last)) * hdv + v0 + 8 * (lane & 3);
+            // Row product and column offset stay separate instructions: fused,
+            // they become a 64-bit multiply-add whose undefined upper addend
+            // half may be allocated to an in-flight load's destination, and
+            // the load-counter wait for that register would drain the other
+            // staging set.
+            uint32_t ov = static_cast<uint32_t>(min(vrow, last)) * hdv;
+            asm("" : "+v"(ov));
+            ov += v0 + 8 * (lane & 3);
             g.v = *reinterpret_cast<const uint4 *>(gv + base * dv + ov);
             if constexpr (kGates2) g.w = *reinterpret_cast<const uint4 *>(gww + base * dv + ov);
             g.rs = 0u;
@@ -538,15 +545,30 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
                 // D_I = (I + L_II)^{-1} by forward substitution in fp32;
                 // lane = (column col, row quad q)
                 const int col = lane >> 2, q = lane & 3;
-                typedef __attribute__((address_space(3))) volatile const f32x4 vlds_f4;
+                // each column piece is read as two 8-byte loads: on gfx950 a
+                // 16-byte LDS read costs several times two 8-byte reads
+                typedef float f32x2 __attribute__((ext_vector_type(2)));
+                typedef __attribute__((address_space(3))) volatile const f32x2 vlds_f2;
                 const auto lt = reinterpret_cast<__attribute__((address_space(3))) const float *>(
                     (__attribute__((address_space(3))) const void *)&s.lt[I][4 * q]);
+                auto ltcol = [&](int j) {
+                    const f32x2 lo = *reinterpret_cast<vlds_f2 *>(lt + j * LTS);
+                    const f32x2 hi = *reinterpret_cast<vlds_f2 *>(lt + j * LTS + 2);
+                    return f32x4{lo[0], lo[1], hi[0], hi[1]};
+                };
                 float x[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == col) ? 1.f : 0.f;
+                // The columns of L do not depend on X: each is read PF steps
+                // before its use, so the sweep does not wait on LDS latency.
+                constexpr int PF = 3;
+                f32x4 lw[PF + 1];
+#pragma unroll
+                for (int j = 0; j < PF; ++j) lw[j] = ltcol(j);
                 auto sweep = [&](auto jc) {
                     constexpr int j = decltype(jc)::value;
-                    const f32x4 lj = *reinterpret_cast<vlds_f4 *>(lt + j * LTS);  // L[4q + r][j]
+                    if constexpr (j + PF < 15) lw[(j + PF) % (PF + 1)] = ltcol(j + PF);
+                    const f32x4 lj = lw[j % (PF + 1)];                           // L[4q + r][j]
                     const float xj = quad_bcast<j / 4>(x[j % 4]);                // X[j][col]
 #pragma unroll
                     for (int r = 0; r < 4; ++r) x[r] = fmaf(-lj[r], xj, x[r]);
@@ -586,26 +608,39 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
         };
 
         // Preparing chunk n: stage it from its set, refill that set with
-        // chunk n + NS, then derive chunk n.
+        // chunk n + NS, then derive chunk n.  The refill is issued on every
+        // path (past the end it reloads the last chunk, which is never
+        // staged), so the loads in flight always form the same queue and the
+        // staging waits only for the older set.
         auto prepare = [&](auto par, int n) {
             commit(par);
-            if (n + NS < nchunks) fetch(par, n + NS);
+            fetch(par, min(n + NS, nchunks - 1));
             psync();
             derive(par);
         };
         if (nchunks > 0) {
             fetch(ic<0>{}, 0);
-            if (NS == 2 && nchunks > 1) fetch(ic<1>{}, 1);
+            if constexpr (NS == 2) fetch(ic<1>{}, min(1, nchunks - 1));
             prepare(ic<0>{}, 0);
         }
         lds_barrier();  // chunk 0 staged and derived
-        for (int c = 0; c < nchunks; c += 2) {
-            if (c + 1 < nchunks) prepare(ic<1>{}, c + 1);  // during chunk c: chunk c + 1 (buffers 1)
+        // One barrier per chunk, as in the carry and output loop.  The loop
+        // has a single exit and every trip runs both prepares, so each path
+        // around it issues the same loads in the same order and a staging
+        // set's wait leaves the other set in flight.
+        int c = 0;
+        for (; c + 2 < nchunks; c += 2) {
+            prepare(ic<1>{}, c + 1);  // during chunk c: chunk c + 1 (buffers 1)
             lds_barrier();
-            if (c + 1 < nchunks) {
-                if (c + 2 < nchunks) prepare(ic<0>{}, c + 2);  // during chunk c + 1: chunk c + 2 (buffers 0)
-                lds_barrier();
-            }
+            prepare(ic<0>{}, c + 2);  // during chunk c + 1: chunk c + 2 (buffers 0)
+            lds_barrier();
+        }
+        if (c + 1 < nchunks) {  // chunks c and c + 1 remain
+            prepare(ic<1>{}, c + 1);
+            lds_barrier();
+            lds_barrier();
+        } else if (c < nchunks) {  // chunk c remains
+            lds_barrier();
         }
     }
 }
