@@ -43,16 +43,23 @@ namespace lam {
 namespace {
 
 constexpr int C16 = 16;      // chunk length (tokens)
-constexpr int KBV = 32;      // dv columns per workgroup
 constexpr int NSLOT = 4;     // one derived-chunk slot per producer
-constexpr int KNT = 512;     // threads per workgroup
 constexpr int KLTS = 20;     // column stride (floats) of the fp32 L block
 constexpr float kFastLimit = 100.f;  // largest 2^x used by the factored Gram
 
-template <int DK>
+// NVT 16-column value tiles per workgroup: one carry and one output wave
+// each, plus four producers.
+template <int NVT>
+struct KdaShape {
+    static constexpr int BV = 16 * NVT;       // dv columns per workgroup
+    static constexpr int NW = 2 * NVT + 4;    // waves
+    static constexpr int NT = 64 * NW;        // threads
+};
+
+template <int DK, int NVT>
 struct KdaLds {
     static constexpr int KS = DK + 8;
-    static constexpr int VS = KBV + 8;
+    static constexpr int VS = KdaShape<NVT>::BV + 8;
     struct Slot {  // state-independent data of one chunk
         alignas(16) __bf16 kd[C16 * KS];   // k * Gam
         alignas(16) __bf16 ke[C16 * KS];   // k * Gam_C / Gam
@@ -71,19 +78,28 @@ struct KdaLds {
     };
     Slot slot[NSLOT];
     Scratch scr[4];
-    alignas(16) bf16x4 uh[2][2][64];               // U per chunk parity and tile
-    alignas(16) bf16x4 sh[2][2][DK / 16][64];      // bf16 state per parity and tile
+    // A producer publishes chunk c only after every consumer has finished
+    // chunk c - 4, so the carry can run at most four chunks ahead of the
+    // output: four U buffers need no further check, and with five state
+    // buffers neither does the bf16 state (two when LDS is short, guarded by
+    // the output's read count).
+    static constexpr int NUB = 4;
+    static constexpr int NSB = NVT == 1 ? 5 : 2;
+    static constexpr bool kStateGuard = NSB < 5;
+    alignas(16) bf16x4 uh[NUB][NVT][64];           // U per chunk and tile
+    alignas(16) bf16x4 sh[NSB][NVT][DK / 16][64];  // bf16 state per chunk and tile
     unsigned int ready[NSLOT];   // chunks published per slot
-    unsigned int cons[4];        // chunks finished per consumer wave (carry 0-1, output 2-3)
-    unsigned int uc[2], uo[2];   // U published / consumed per tile
-    unsigned int sp[2], so[2];   // bf16 state published / consumed per tile
+    unsigned int cons[NVT];      // chunks finished per output wave
+    unsigned int uc[NVT];        // U published per tile
+    unsigned int sp[NVT], so[NVT];   // bf16 state published / read per tile
 };
 
-template <int DK>
-__global__ __launch_bounds__(KNT) void kda_chunked_kernel(DeltaArgs a) {
+template <int DK, int NVT>
+__global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArgs a) {
+    constexpr int KBV = KdaShape<NVT>::BV;
     constexpr int KS = DK + 8, VS = KBV + 8;
     constexpr int KSTEP = DK / 32, KT = DK / 16, CH = DK / 64;  // CH: key channels per producer lane
-    using Lds = KdaLds<DK>;
+    using Lds = KdaLds<DK, NVT>;
     __shared__ Lds s;
 
     const int T = static_cast<int>(a.T), H = static_cast<int>(a.H), dv = a.dv;
@@ -99,17 +115,15 @@ __global__ __launch_bounds__(KNT) void kda_chunked_kernel(DeltaArgs a) {
 
     if (tid == 0) {
         for (int i = 0; i < NSLOT; ++i) s.ready[i] = 0u;
-        for (int i = 0; i < 4; ++i) s.cons[i] = 0u;
-        s.uc[0] = s.uc[1] = s.uo[0] = s.uo[1] = 0u;
-        s.sp[0] = s.sp[1] = s.so[0] = s.so[1] = 0u;
+        for (int i = 0; i < NVT; ++i) s.cons[i] = s.uc[i] = s.sp[i] = s.so[i] = 0u;
     }
     __syncthreads();
 
-    if (wave < 4) {
-        const int vt = wave & 1;
+    if (wave < 2 * NVT) {
+        const int vt = wave % NVT;
         const int vcol = v0 + 16 * vt + lc;
         const int64_t sbase = (static_cast<int64_t>(head) * dv + vcol) * DK;
-        if (wave < 2) {
+        if (wave < NVT) {
             // ================================ carry ================================
             f32x4 St[KT];
             if (a.state_in) {
@@ -140,8 +154,7 @@ __global__ __launch_bounds__(KNT) void kda_chunked_kernel(DeltaArgs a) {
                 for (int p = 0; p < KSTEP; ++p) z = mfma32(kf[p], cat8(bf4(St[2 * p]), bf4(St[2 * p + 1])), z);
                 const f32x4 rhs = __builtin_convertvector(vb, f32x4) - z;
                 const bf16x4 ub = bf4(mfma16(dtf, bf4(rhs), f32x4{0.f, 0.f, 0.f, 0.f}));
-                lds_wait(&s.uo[vt], static_cast<unsigned int>(max(c - 1, 0)));  // U(c-2) read
-                s.uh[c & 1][vt][lane] = ub;
+                s.uh[c & 3][vt][lane] = ub;
                 lds_arrive(&s.uc[vt], lane);
                 // S^T <- diag(Gam_C) S^T + (K*Gam_C/Gam)^T U
                 bf16x4 kef[KT];
@@ -153,11 +166,14 @@ __global__ __launch_bounds__(KNT) void kda_chunked_kernel(DeltaArgs a) {
                     St[kt] = St[kt] * f32x4{g4.x, g4.y, g4.z, g4.w};
                     St[kt] = mfma16(kef[kt], ub, St[kt]);
                 }
-                lds_wait(&s.so[vt], static_cast<unsigned int>(c));  // S(c-1) read from this buffer
+                // S(c + 1 - NSB) has been read from this buffer
+                if constexpr (Lds::kStateGuard) lds_wait(&s.so[vt], static_cast<unsigned int>(c + 2 - Lds::NSB));
+                {
+                    auto &dst = s.sh[(c + 1) % Lds::NSB][vt];
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt) s.sh[(c + 1) & 1][vt][kt][lane] = bf4(St[kt]);
-                lds_arrive(&s.sp[vt], lane);
-                lds_arrive(&s.cons[wave], lane);  // done with slot c
+                    for (int kt = 0; kt < KT; ++kt) dst[kt][lane] = bf4(St[kt]);
+                }
+                lds_arrive(&s.sp[vt], lane);  // also releases slot c: its last read precedes this
             }
             if (a.state_out) {
 #pragma unroll
@@ -174,26 +190,25 @@ __global__ __launch_bounds__(KNT) void kda_chunked_kernel(DeltaArgs a) {
                 bf16x8 bS[KSTEP];
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p)
-                    bS[p] = cat8(s.sh[c & 1][vt][2 * p][lane], s.sh[c & 1][vt][2 * p + 1][lane]);
-                lds_arrive(&s.so[vt], lane);
+                    bS[p] = cat8(s.sh[c % Lds::NSB][vt][2 * p][lane], s.sh[c % Lds::NSB][vt][2 * p + 1][lane]);
+                if constexpr (Lds::kStateGuard) lds_arrive(&s.so[vt], lane);
                 // Y^T = S (Q*Gam)^T + U^T Aqk^T: lane (g, i) holds columns 4g + r of token i
                 f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p) y = mfma32(bS[p], row_frag2(Sl.qd, KS, 0, 32 * p, lane), y);
                 const bf16x4 aq = Sl.aqk[lane];
                 lds_wait(&s.uc[vt], static_cast<unsigned int>(c + 1));
-                const bf16x4 ub = s.uh[c & 1][vt][lane];
-                lds_arrive(&s.uo[vt], lane);
+                const bf16x4 ub = s.uh[c & 3][vt][lane];
                 y = mfma16(ub, aq, y);
                 const int t = c * C16 + lc;
                 if (t < T)
                     *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(a.out) + tok(t) * dv + v0 + 16 * vt + 4 * lg) = bf4(y);
-                lds_arrive(&s.cons[wave], lane);
+                lds_arrive(&s.cons[vt], lane);
             }
         }
     } else {
         // ============================== producers ==============================
-        const int pw = wave - 4;
+        const int pw = wave - 2 * NVT;
         typename Lds::Scratch &X = s.scr[pw];
         typename Lds::Slot &Sl = s.slot[pw];
         const uint16_t *gq = static_cast<const uint16_t *>(a.q);
@@ -206,21 +221,36 @@ __global__ __launch_bounds__(KNT) void kda_chunked_kernel(DeltaArgs a) {
         // row lane/4, columns 8 (lane % 4) ..; beta of token lane (lanes 0-15).
         using Pk = std::conditional_t<CH == 2, uint32_t, uint16_t>;
         Pk rk[C16], rq[C16], ra[C16];
+        // value rows: KBV/8 lanes per row, 8 columns each (lanes past row 15 idle)
+        constexpr int VLPR = KBV / 8;
+        const int vrow = lane / VLPR, vcol = 8 * (lane % VLPR);
         uint4 rv;
         uint16_t rb = 0;
-        int nval = 0;  // tokens of the staged chunk inside the sequence
-        auto fetch = [&](int n) {
-            const int t0 = n * C16;
-            nval = min(C16, T - t0);
+        int nval = 0, nnext = 0;  // tokens inside the sequence: chunk being derived, staged chunk
+        // fetch_kq: keys and queries (the bulk); fetch_rest: decays, value
+        // rows and beta.  Both clamp rows to the sequence.  A row's offset is
+        // the same for the whole wave (scalar arithmetic); only the lane's
+        // channel offset is per lane.
+        const int64_t hdk = static_cast<int64_t>(H) * DK;
+        const uint16_t *lk = gk + CH * lane, *lq = gq + CH * lane, *la = gal + CH * lane;
+        auto fetch_kq = [&](int n) {
+            const int t0 = n * C16, nn = min(C16, T - t0);
+            const int64_t r0 = tok(t0) * DK;
 #pragma unroll
             for (int t = 0; t < C16; ++t) {
-                const int64_t o = tok(t0 + min(t, nval - 1)) * DK + CH * lane;
-                rk[t] = *reinterpret_cast<const Pk *>(gk + o);
-                rq[t] = *reinterpret_cast<const Pk *>(gq + o);
-                ra[t] = *reinterpret_cast<const Pk *>(gal + o);
+                const int64_t o = r0 + min(t, nn - 1) * hdk;
+                rk[t] = *reinterpret_cast<const Pk *>(lk + o);
+                rq[t] = *reinterpret_cast<const Pk *>(lq + o);
             }
-            rv = *reinterpret_cast<const uint4 *>(gv + tok(t0 + min(lane >> 2, nval - 1)) * dv + v0 + 8 * (lane & 3));
-            if (lane < C16) rb = gbe[tok(t0 + min(lane, nval - 1))];
+        };
+        auto fetch_rest = [&](int n) {
+            const int t0 = n * C16;
+            nnext = min(C16, T - t0);
+            const int64_t r0 = tok(t0) * DK;
+#pragma unroll
+            for (int t = 0; t < C16; ++t) ra[t] = *reinterpret_cast<const Pk *>(la + r0 + min(t, nnext - 1) * hdk);
+            rv = *reinterpret_cast<const uint4 *>(gv + tok(t0 + min(vrow, nnext - 1)) * dv + v0 + vcol);
+            if (lane < C16) rb = gbe[tok(t0 + min(lane, nnext - 1))];
         };
         // channel j of a packed pair, widened
         auto chan = [](Pk x, int j) { return bf16_bits_to_f32(static_cast<uint16_t>(x >> (16 * j))); };
@@ -233,11 +263,18 @@ __global__ __launch_bounds__(KNT) void kda_chunked_kernel(DeltaArgs a) {
                 m[t * KS + lane] = static_cast<__bf16>(x[0]);
             }
         };
-        if (pw < nchunks) fetch(pw);
+        if (pw < nchunks) {
+            fetch_kq(pw);
+            fetch_rest(pw);
+        }
         for (int n = pw; n < nchunks; n += 4) {
+            nval = nnext;
             if (n >= 4) {  // chunk n - 4 released by every consumer wave
 #pragma unroll
-                for (int w = 0; w < 4; ++w) lds_wait(&s.cons[w], static_cast<unsigned int>(n - 3));
+                for (int w = 0; w < NVT; ++w) {
+                    lds_wait(&s.sp[w], static_cast<unsigned int>(n - 2));    // carry w past chunk n - 4
+                    lds_wait(&s.cons[w], static_cast<unsigned int>(n - 3));  // output w done with it
+                }
             }
             // padding rows: zero key and query, decay 1
             if (nval < C16) {
@@ -273,30 +310,44 @@ __global__ __launch_bounds__(KNT) void kda_chunked_kernel(DeltaArgs a) {
 #pragma unroll
             for (int m = 1; m < 64; m <<= 1) emax = fmaxf(emax, __shfl_xor(emax, m, 64));
             const bool fast = emax <= kFastLimit;
-            // scaled tiles
+            float gcp[CH];  // Gam_C per channel
 #pragma unroll
-            for (int t = 0; t < C16; ++t) {
-                float kd[CH], qd[CH], ke[CH], kb[CH];
+            for (int j = 0; j < CH; ++j) gcp[j] = exp2_fast(gcx[j]);
+            // scaled tiles (the factored form's branch taken once per chunk)
+            auto tiles = [&](auto fc) {
+                constexpr bool F = decltype(fc)::value;
 #pragma unroll
-                for (int j = 0; j < CH; ++j) {
-                    const float kv = chan(rk[t], j), qv = chan(rq[t], j);
-                    const float e1 = exp2_fast(G[t][j]);
-                    kd[j] = kv * e1;
-                    qd[j] = qv * e1;
-                    ke[j] = kv * exp2_fast(gcx[j] - G[t][j]);
-                    kb[j] = kv * exp2_fast(-G[t][j]);
+                for (int t = 0; t < C16; ++t) {
+                    float kd[CH], qd[CH], ke[CH], kb[CH];
+#pragma unroll
+                    for (int j = 0; j < CH; ++j) {
+                        const float kv = chan(rk[t], j), qv = chan(rq[t], j);
+                        const float e1 = exp2_fast(G[t][j]);
+                        kd[j] = kv * e1;
+                        qd[j] = qv * e1;
+                        if constexpr (F) {  // 2^{-G} is finite here: 2^{G_C - G} as a product
+                            const float eb = exp2_fast(-G[t][j]);
+                            kb[j] = kv * eb;
+                            ke[j] = kv * (gcp[j] * eb);
+                        } else {
+                            kb[j] = 0.f;
+                            ke[j] = kv * exp2_fast(gcx[j] - G[t][j]);
+                        }
+                    }
+                    put(Sl.kd, t, kd);
+                    put(Sl.qd, t, qd);
+                    put(Sl.ke, t, ke);
+                    if constexpr (F) put(X.kb, t, kb);
                 }
-                put(Sl.kd, t, kd);
-                put(Sl.qd, t, qd);
-                put(Sl.ke, t, ke);
-                if (fast) put(X.kb, t, kb);
-            }
+            };
+            if (fast) tiles(std::true_type{});
+            else tiles(std::false_type{});
 #pragma unroll
-            for (int j = 0; j < CH; ++j) Sl.gc[CH * lane + j] = exp2_fast(gcx[j]);
+            for (int j = 0; j < CH; ++j) Sl.gc[CH * lane + j] = gcp[j];
             {
-                const uint32_t m = (lane >> 2) < nval ? 0xffffffffu : 0u;
-                *reinterpret_cast<uint4 *>(&Sl.v[(lane >> 2) * VS + 8 * (lane & 3)]) =
-                    make_uint4(rv.x & m, rv.y & m, rv.z & m, rv.w & m);
+                const uint32_t m = vrow < nval ? 0xffffffffu : 0u;
+                if (vrow < C16)
+                    *reinterpret_cast<uint4 *>(&Sl.v[vrow * VS + vcol]) = make_uint4(rv.x & m, rv.y & m, rv.z & m, rv.w & m);
             }
             if (lane < C16) X.beta[lane] = lane < nval ? bf16_bits_to_f32(rb) : 0.f;
             wave_lds_fence();
@@ -411,7 +462,9 @@ __global__ __launch_bounds__(KNT) void kda_chunked_kernel(DeltaArgs a) {
                 for (int r = 0; r < 4; ++r) dt[((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3)] = static_cast<__bf16>(x[r] * bcol);
             }
             lds_arrive(&s.ready[pw], lane);
-            if (n + 4 < nchunks) fetch(n + 4);
+            // this producer's next chunk (past the end: the last chunk again, unused)
+            fetch_kq(min(n + 4, nchunks - 1));
+            fetch_rest(min(n + 4, nchunks - 1));
         }
     }
 }
@@ -419,18 +472,27 @@ __global__ __launch_bounds__(KNT) void kda_chunked_kernel(DeltaArgs a) {
 }  // namespace
 
 bool kda_chunked_supported(const DeltaArgs &a) {
-    return a.variant == kKimiDelta && a.dtype == kBF16 && (a.dk == 64 || a.dk == 128) && a.dv % KBV == 0;
+    return a.variant == kKimiDelta && a.dtype == kBF16 && (a.dk == 64 || a.dk == 128) && a.dv % 16 == 0;
 }
 
-hipError_t launch_kda_chunked(const DeltaArgs &a, hipStream_t stream) {
-    if (!kda_chunked_supported(a)) return hipErrorNotSupported;
-    const unsigned blocks = static_cast<unsigned>(a.B * a.H * (a.dv / KBV));
+template <int NVT>
+static hipError_t launch_nvt(const DeltaArgs &a, hipStream_t stream) {
+    const unsigned blocks = static_cast<unsigned>(a.B * a.H * (a.dv / KdaShape<NVT>::BV));
     switch (a.dk) {
-        case 64: kda_chunked_kernel<64><<<blocks, KNT, 0, stream>>>(a); break;
-        case 128: kda_chunked_kernel<128><<<blocks, KNT, 0, stream>>>(a); break;
+        case 64: kda_chunked_kernel<64, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a); break;
+        case 128: kda_chunked_kernel<128, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// Two value tiles per workgroup share the producers' work; with fewer than
+// 256 such workgroups the chip has idle compute units, and one tile per
+// workgroup doubles the number of chains running at once.
+hipError_t launch_kda_chunked(const DeltaArgs &a, hipStream_t stream) {
+    if (!kda_chunked_supported(a)) return hipErrorNotSupported;
+    if (a.dv % 32 == 0 && a.B * a.H * (a.dv / 32) >= 256) return launch_nvt<2>(a, stream);
+    return launch_nvt<1>(a, stream);
 }
 
 }  // namespace lam

@@ -225,6 +225,19 @@ def test_kda_chunked_strong_channel_decay(dk, gate_mu):
     U.check(w, got, ref, label=w.name + f" mu={gate_mu}")
 
 
+@pytest.mark.parametrize("B,H,dk,dv", [(1, 2, 128, 96), (2, 3, 64, 32), (8, 8, 128, 128)])
+def test_kda_chunked_tile_shapes(B, H, dk, dv):
+    """One 16-column value tile per workgroup (grids of fewer than 256
+    two-tile slices) and two per workgroup (B8 H8 dv128: 256 slices)."""
+    w = _w("kda", "bf16", B, 70, H, dk, dv, seed=7300 + dv, gate_mu=1.0)
+    x = I.make_inputs(w)
+    s0 = (np.random.default_rng(dv).standard_normal((B, H, dv, dk)) * 0.2).astype(np.float32)
+    s0 = s0.astype(np.float64)
+    got = U.run_gpu(w, x, algo="chunked", state_in=s0)
+    ref = U.run_oracle(w, x, state_in=s0)
+    U.check(w, got, ref, label=w.name)
+
+
 def test_chunked_rejects_unsupported():
     import torch
 
