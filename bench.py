@@ -188,24 +188,40 @@ def main():
     tokens = w.B * w.T
     value = tokens * args.steps / wall
     if w.variant == "vla":
-        ran = "recurrent"
+        # the VLA entry point runs the chunked schedule for any T > 0 unless told otherwise
+        ran = args.algo if args.algo != "auto" else ("chunked" if w.T > 0 else "recurrent")
     else:
         ran = args.algo if args.algo != "auto" else lam.select_algo(w.variant, w.dtype, w.T, w.dk, w.dv)
-    # arithmetic type: the recurrent schedule and fp32 storage compute in fp32;
-    # the chunked schedule on bf16 storage feeds bf16 operands to the matrix
-    # cores (fp32 accumulate, fp32 state)
-    arith_dtype = "bf16" if (ran == "chunked" and w.dtype == "bf16") else "f32"
+    # arithmetic type: the recurrent schedules and fp32 storage compute in
+    # fp32; the delta-rule chunked schedule on bf16 storage feeds bf16
+    # operands to the matrix cores (fp32 accumulate, fp32 state); the VLA
+    # chunked schedule uses fp32 matrix-core products for every dtype
+    arith_dtype = "bf16" if (ran == "chunked" and w.dtype == "bf16" and w.variant != "vla") else "f32"
     mean_launch_s = float(np.mean(launch_ms)) / 1e3
     abytes = algorithmic_bytes(w)
     aflops = algorithmic_flops(w)
     achieved_gbs = abytes / mean_launch_s / 1e9
-    roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(w, ran),
+    # the binding roofline: HBM bytes, or the algorithmic flops on the unit
+    # the schedule computes them with (matrix cores for the chunked schedules,
+    # the fp32 vector ALU for the recurrent ones), whichever takes longer
+    if ran == "chunked":
+        cpeak, cbound = (MFMA_BF16_PEAK_TFS if arith_dtype == "bf16" else FP32_PEAK_TFS), "mfma"
+    else:
+        cpeak, cbound = FP32_PEAK_TFS, "alu"
+    achieved_tfs = aflops / mean_launch_s / 1e12
+    if aflops / (cpeak * 1e12) > abytes / (HBM_PEAK_GBS * 1e9):
+        roofline = {"bound": cbound, "achieved": achieved_tfs, "peak": cpeak, "unit": "TFLOP/s",
+                    "frac": achieved_tfs / cpeak}
+    else:
+        roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved_gbs / HBM_PEAK_GBS}
+    roofline.update({"traffic": measured_traffic(w, ran),
                 "algorithmic_bytes_per_launch": abytes,
                 "mean_launch_us": mean_launch_s * 1e6,
                 "median_launch_us": float(np.median(launch_ms)) * 1e3,
                 "min_launch_us": float(np.min(launch_ms)) * 1e3,
-                "algorithmic_tflops": aflops / mean_launch_s / 1e12}
+                "achieved_GBps": achieved_gbs,
+                "algorithmic_tflops": achieved_tfs})
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4

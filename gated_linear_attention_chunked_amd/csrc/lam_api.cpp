@@ -137,7 +137,6 @@ lam_status lam_vla_forward(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
     if (algo < LAM_ALGO_AUTO || algo > LAM_ALGO_CHUNKED) return LAM_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 0 || d <= 0) return LAM_ERR_INVALID_ARG;
     if (!supported_head(d)) return LAM_ERR_UNSUPPORTED;
-    if (algo == LAM_ALGO_CHUNKED) return LAM_ERR_UNSUPPORTED;
     int64_t n, nst;
     if (!elems(B, T, H, d, n) || !elems(B, 1, H, d * d, nst)) return LAM_ERR_INVALID_ARG;
     if (B * H > (INT64_C(1) << 24) || T > INT_MAX / 2) return LAM_ERR_INVALID_ARG;
@@ -173,6 +172,9 @@ lam_status lam_vla_forward(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
     a.A_out = A_out;
     a.S_out = S_out;
     if (T == 0 && !A_out && !S_out) return LAM_OK;
+    if (algo != LAM_ALGO_RECURRENT && T > 0 && lam::vla_chunked_supported(a))
+        return from_hip(lam::launch_vla_chunked(a, stream));
+    if (algo == LAM_ALGO_CHUNKED && T > 0) return LAM_ERR_UNSUPPORTED;
     return from_hip(lam::launch_vla_recurrent(a, stream));
 }
 

@@ -41,6 +41,10 @@ hipError_t launch_vla_recurrent(const VlaArgs &a, hipStream_t stream);
 // chunked kernel is built for the variant / dtype / head sizes.
 bool delta_chunked_supported(const DeltaArgs &a);
 hipError_t launch_delta_chunked(const DeltaArgs &a, hipStream_t stream);
+// VLA chunked schedule (fp32 matrix cores, any dtype of the token streams).
+bool vla_chunked_supported(const VlaArgs &a);
+hipError_t launch_vla_chunked(const VlaArgs &a, hipStream_t stream);
+
 // Kimi Delta (per-channel decay) has its own chunked kernel.
 bool kda_chunked_supported(const DeltaArgs &a);
 hipError_t launch_kda_chunked(const DeltaArgs &a, hipStream_t stream);

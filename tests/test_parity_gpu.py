@@ -119,12 +119,13 @@ def test_bitwise_reproducible(variant):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [32, 64, 96, 128])
-def test_vla_small(d, dtype):
+def test_vla_small(d, dtype, algo):
     w = I.Workload(f"vla_{dtype}_B2_T75_H3_d{d}", "vla", dtype, 2, 75, 3, d, d, seed=6000 + d)
     x = I.make_inputs(w)
-    got = U.run_gpu(w, x)
+    got = U.run_gpu(w, x, algo=algo)
     ref = U.run_oracle(w, x)
     if dtype == "f32":
         U.check(w, got, ref, label=w.name)
@@ -135,17 +136,32 @@ def test_vla_small(d, dtype):
             assert U.errs(g, r)[1] <= 1e-4
 
 
-def test_vla_initial_state_and_chaining():
-    w = I.Workload("vla_f32_B1_T90_H2_d32", "vla", "f32", 1, 90, 2, 32, 32, seed=6100)
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
+@pytest.mark.parametrize("d", [32, 96])
+def test_vla_initial_state_and_chaining(d, algo):
+    """Two calls chained through (A, S): a ragged split (40 + 50 tokens), so
+    the second call starts from a non-identity penalty inverse and a non-zero
+    state."""
+    w = I.Workload(f"vla_f32_B1_T90_H2_d{d}", "vla", "f32", 1, 90, 2, d, d, seed=6100 + d)
     x = I.make_inputs(w)
     ref = U.run_oracle(w, x)
     first = {k: v[:, :40] for k, v in x.items()}
     second = {k: v[:, 40:] for k, v in x.items()}
     w1, w2 = w.replace(T=40), w.replace(T=50)
-    g1 = U.run_gpu(w1, first)
-    g2 = U.run_gpu(w2, second, A_in=g1[1], S_in=g1[2])
+    g1 = U.run_gpu(w1, first, algo=algo)
+    g2 = U.run_gpu(w2, second, A_in=g1[1], S_in=g1[2], algo=algo)
     got = (np.concatenate([g1[0], g2[0]], 1), g2[1], g2[2])
-    U.check(w, got, ref, label="vla chained")
+    U.check(w, got, ref, label="vla chained " + algo)
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 48, 301])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+def test_vla_chunked_lengths(d, T):
+    """The 16-token chunked schedule: a single token, one short and one full
+    chunk, a ragged tail, several chunks."""
+    w = I.Workload(f"vla_f32_B1_T{T}_H2_d{d}", "vla", "f32", 1, T, 2, d, d, seed=6200 + T + d)
+    x = I.make_inputs(w)
+    U.check(w, U.run_gpu(w, x, algo="chunked"), U.run_oracle(w, x), label=w.name)
 
 
 # ------------------------------------------------------------ full sizes
