@@ -58,22 +58,42 @@ def algorithmic_flops(w) -> int:
     return n_th * 7 * w.dk * w.dv
 
 
-def measured_traffic(w, ran: str):
-    """HBM bytes per launch from the committed rocprofv3 counter record
-    (profiles/traffic.json), or None when that record was taken on another
-    workload or on a different revision of the kernel source."""
+KERNEL_SOURCES = {  # schedule -> kernel source per variant family
+    ("chunked", "delta"): "delta_chunked.hip",
+    ("chunked", "kda"): "kda_chunked.hip",
+    ("chunked", "vla"): "vla_chunked.hip",
+    ("recurrent", "delta"): "delta_recurrent.hip",
+    ("recurrent", "kda"): "delta_recurrent.hip",
+    ("recurrent", "vla"): "vla_recurrent.hip",
+}
+SHARED_HEADERS = ("chunk_common.h", "device_common.h", "lam_internal.h")
+
+
+def kernel_source_hash(ran: str, variant: str):
+    """(source file name, sha256 over that source and the shared headers)."""
     import hashlib
 
-    if ran != "chunked" or w.variant == "vla":
-        return None
+    fam = variant if variant in ("kda", "vla") else "delta"
+    name = KERNEL_SOURCES[(ran, fam)]
+    csrc = os.path.join(ROOT, "gated_linear_attention_chunked_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (name,) + SHARED_HEADERS:
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return name, h.hexdigest()
+
+
+def measured_traffic(w, ran: str):
+    """HBM bytes per launch from the committed rocprofv3 counter record
+    (profiles/traffic.json), or None when there is no record for this
+    workload and schedule, or it was taken on a different revision of the
+    kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "gated_linear_attention_chunked_amd", "csrc", "delta_chunked.hip")
     try:
-        rec = json.load(open(path))["kernels"]["delta_chunked.hip"]
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        rec = json.load(open(path))["workloads"][w.name]
+        name, sha = kernel_source_hash(ran, w.variant)
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("sha256") != sha or rec.get("workload") != w.name:
+    if rec.get("schedule") != ran or rec.get("source") != name or rec.get("sha256") != sha:
         return None
     return float(rec["bytes_per_launch"])
 
