@@ -61,7 +61,9 @@ template <int D>
 struct VlaLds {
     static constexpr int DS = D + 4;  // row stride of the token-row tiles
     static constexpr int TS = VC + 4; // row stride of the transposed tiles
-    alignas(16) float p[VC * DS], kh[VC * DS], qh[VC * DS], v[VC * DS];
+    // token-row tiles, double-buffered: chunk c is consumed while chunk c + 1
+    // is staged and its features are computed
+    alignas(16) float p[2][VC * DS], kh[2][VC * DS], qh[2][VC * DS], v[2][VC * DS];
     alignas(16) float pa[VC * DS];      // P A^T
     alignas(16) float ah[VC * DS];      // alphahat rows
     alignas(16) float zt[D * TS];       // Z^T
@@ -160,9 +162,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
         const int e = tid + NT * u;
         eoff[u] = static_cast<uint32_t>((e / D) * H * D + e % D);
     }
-    auto fetch = [&](int c0) {
-        const int n = min(VC, T - c0);
-        const int64_t base = tok(c0);
+    auto fetch = [&](int c0) {  // past the end: the last chunk again (never used)
+        const int cc = min(c0, ((T - 1) / VC) * VC);
+        const int n = min(VC, T - cc);
+        const int64_t base = tok(cc);
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
             const int e = tid + NT * u, t = e / D;
@@ -174,73 +177,87 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
             rp[u] = IO::ld(a.p, base + o);
         }
     };
-    if (T > 0) fetch(0);
-
-    for (int c0 = 0; c0 < T; c0 += VC) {
-        const int n = min(VC, T - c0);
-        // ---- stage the chunk (padding rows: p = v = 0, features zeroed below)
+    // staged registers into buffer bi (rows past n: p = v = 0, features zeroed)
+    auto stage = [&](int bi, int n) {
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
             const int e = tid + NT * u, t = e / D, j = e % D;
             const bool ok = t < n;
-            s.p[t * DS + j] = ok ? rp[u] : 0.f;
-            s.v[t * DS + j] = ok ? rv[u] : 0.f;
-            s.kh[t * DS + j] = rk[u];
-            s.qh[t * DS + j] = rq[u];
+            s.p[bi][t * DS + j] = ok ? rp[u] : 0.f;
+            s.v[bi][t * DS + j] = ok ? rv[u] : 0.f;
+            s.kh[bi][t * DS + j] = rk[u];
+            s.qh[bi][t * DS + j] = rq[u];
         }
+    };
+    // khat, qhat = unit(ELU(x) + 1) in place in buffer bi, zero past row n.
+    // NWF waves share the rows (this wave is the wi-th: rows wi, wi + NWF, ...),
+    // all of its rows at once.
+    auto features = [&](auto nwf, int bi, int n, int wi) {
+        constexpr int NWF = decltype(nwf)::value;
+        constexpr int PER = (D + 63) / 64, RPW = (VC + NWF - 1) / NWF;
+        float *KH = s.kh[bi], *QH = s.qh[bi];
+        float fk[RPW][PER], fq[RPW][PER], ssk[RPW], ssq[RPW];
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+            const int t = wi + NWF * rr;
+            ssk[rr] = ssq[rr] = 0.f;
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                // read a valid element unconditionally and mask the value,
+                // so the reads of all rows go out together
+                const int j = lane + 64 * u;
+                const float okf = (t < VC && j < D) ? 1.f : 0.f;
+                const int o = min(t, VC - 1) * DS + min(j, D - 1);
+                fk[rr][u] = elu1(KH[o]) * okf;
+                fq[rr][u] = elu1(QH[o]) * okf;
+                ssk[rr] = fmaf(fk[rr][u], fk[rr][u], ssk[rr]);
+                ssq[rr] = fmaf(fq[rr][u], fq[rr][u], ssq[rr]);
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+            ssk[rr] = group_sum<64>(ssk[rr]);
+            ssq[rr] = group_sum<64>(ssq[rr]);
+        }
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+            const int t = wi + NWF * rr;
+            const float ik = t < n ? __builtin_amdgcn_rsqf(ssk[rr]) : 0.f;
+            const float iq = t < n ? __builtin_amdgcn_rsqf(ssq[rr]) : 0.f;
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int j = lane + 64 * u;
+                if (t < VC && j < D) {
+                    KH[t * DS + j] = fk[rr][u] * ik;
+                    QH[t * DS + j] = fq[rr][u] * iq;
+                }
+            }
+        }
+    };
+    if (T > 0) {
+        fetch(0);
+        stage(0, min(VC, T));
+        fetch(VC);
         __syncthreads();
-        if (c0 + VC < T) fetch(c0 + VC);
-        // ---- features: khat, qhat = unit(ELU(x) + 1); zero past the end.
-        // Wave w takes rows w, w + NW, ...; all its rows at once.
-        {
-            constexpr int PER = (D + 63) / 64, RPW = (VC + NW - 1) / NW;
-            float fk[RPW][PER], fq[RPW][PER], ssk[RPW], ssq[RPW];
-#pragma unroll
-            for (int rr = 0; rr < RPW; ++rr) {
-                const int t = w + NW * rr;
-                ssk[rr] = ssq[rr] = 0.f;
-#pragma unroll
-                for (int u = 0; u < PER; ++u) {
-                    // read a valid element unconditionally and mask the value,
-                    // so the reads of all rows go out together
-                    const int j = lane + 64 * u;
-                    const float okf = (t < VC && j < D) ? 1.f : 0.f;
-                    const int o = min(t, VC - 1) * DS + min(j, D - 1);
-                    fk[rr][u] = elu1(s.kh[o]) * okf;
-                    fq[rr][u] = elu1(s.qh[o]) * okf;
-                    ssk[rr] = fmaf(fk[rr][u], fk[rr][u], ssk[rr]);
-                    ssq[rr] = fmaf(fq[rr][u], fq[rr][u], ssq[rr]);
-                }
-            }
-#pragma unroll
-            for (int rr = 0; rr < RPW; ++rr) {
-                ssk[rr] = group_sum<64>(ssk[rr]);
-                ssq[rr] = group_sum<64>(ssq[rr]);
-            }
-#pragma unroll
-            for (int rr = 0; rr < RPW; ++rr) {
-                const int t = w + NW * rr;
-                const float ik = t < n ? __builtin_amdgcn_rsqf(ssk[rr]) : 0.f;
-                const float iq = t < n ? __builtin_amdgcn_rsqf(ssq[rr]) : 0.f;
-#pragma unroll
-                for (int u = 0; u < PER; ++u) {
-                    const int j = lane + 64 * u;
-                    if (t < VC && j < D) {
-                        s.kh[t * DS + j] = fk[rr][u] * ik;
-                        s.qh[t * DS + j] = fq[rr][u] * iq;
-                    }
-                }
-            }
-        }
+        features(icst<NW>{}, 0, min(VC, T), w);
+    }
+
+    for (int c0 = 0; c0 < T; c0 += VC) {
+        const int n = min(VC, T - c0), n1 = min(VC, T - c0 - VC);  // rows of this chunk, of the next
+        const int cb = (c0 / VC) & 1, nb = cb ^ 1;
+        const float *P = s.p[cb], *KH = s.kh[cb], *QH = s.qh[cb], *V = s.v[cb];
+        // ---- stage chunk c + 1 into the other buffer, refill the registers
+        stage(nb, n1);
+        fetch(c0 + 2 * VC);
         __syncthreads();
         // ---- products against the chunk-start state (tile w of each):
         // Pa = P A^T, KA = Khat A^T, KS = Khat S^T, QS = Qhat S^T
         f32x4 pa = {0.f, 0.f, 0.f, 0.f}, ka = pa, ks = pa, qs = pa;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const f32x4 pr = lds4(&s.p[i * DS + 16 * q + 4 * g]);
-            const f32x4 kr = lds4(&s.kh[i * DS + 16 * q + 4 * g]);
-            const f32x4 qr = lds4(&s.qh[i * DS + 16 * q + 4 * g]);
+            const f32x4 pr = lds4(&P[i * DS + 16 * q + 4 * g]);
+            const f32x4 kr = lds4(&KH[i * DS + 16 * q + 4 * g]);
+            const f32x4 qr = lds4(&QH[i * DS + 16 * q + 4 * g]);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 pa = mfma4(pr[m], AT[q][m], pa);
@@ -253,13 +270,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
         f32x4 rr;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            rr[r] = s.v[(4 * g + r) * DS + col] - ks[r];
+            rr[r] = V[(4 * g + r) * DS + col] - ks[r];
             s.pa[(4 * g + r) * DS + col] = pa[r];
         }
         __syncthreads();
         // ---- Pa X^T (16 x 32), waves 0 and 1: column c of it stored as row c of g0t
         if (w < 2) {
-            const float *xs = w == 0 ? s.p : s.kh;
+            const float *xs = w == 0 ? P : KH;
             f32x4 g0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
@@ -318,6 +335,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             unit_lower_inverse(s.lt, s.wop, lane);
+        } else {
+            // meanwhile the other waves map the features of chunk c + 1
+            features(icst<NW - 1>{}, nb, n1, w - 1);
         }
         __syncthreads();
         // ---- Z = (I + C)^{-1} Pa, N = KA - E Z (tile w); Z^T to LDS; |N_t|^2 partials
@@ -368,7 +388,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
             f32x4 km = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
-                const f32x4 kr = lds4(&s.kh[i * DS + 16 * q + 4 * g]);
+                const f32x4 kr = lds4(&KH[i * DS + 16 * q + 4 * g]);
                 const f32x4 ar = lds4(&s.ah[i * DS + 16 * q + 4 * g]);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) km = mfma4(kr[m], ar[m], km);
@@ -387,7 +407,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const f32x4 ar = lds4(&s.ah[i * DS + 16 * q + 4 * g]);
-                const f32x4 qr = lds4(&s.qh[i * DS + 16 * q + 4 * g]);
+                const f32x4 qr = lds4(&QH[i * DS + 16 * q + 4 * g]);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) aq = mfma4(ar[m], qr[m], aq);
             }
