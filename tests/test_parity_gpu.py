@@ -254,6 +254,25 @@ def test_kda_chunked_tile_shapes(B, H, dk, dv):
     U.check(w, got, ref, label=w.name)
 
 
+@pytest.mark.parametrize("T", [16, 33, 70, 300])
+@pytest.mark.parametrize("dk", [64, 128])
+def test_kda_chunked_two_tiles_repeat(T, dk):
+    """Two value tiles per workgroup (B8 H8 dv128), chunk counts from one
+    to past the slot ring, with and without a decay strong enough to take
+    the exact form; each case runs twice and must match bit for bit, since
+    the hand-offs between the waves must not change any result."""
+    for mu in (1.0, 5.0):
+        w = _w("kda", "bf16", 8, T, 8, dk, 128, seed=7500 + T + dk, gate_mu=mu)
+        x = I.make_inputs(w)
+        s0 = (np.random.default_rng(T).standard_normal((8, 8, 128, dk)) * 0.2).astype(np.float64)
+        r1 = U.run_gpu(w, x, algo="chunked", state_in=s0)
+        r2 = U.run_gpu(w, x, algo="chunked", state_in=s0)
+        for a, b in zip(r1, r2):
+            np.testing.assert_array_equal(a, b)
+        ref = U.run_oracle(w, x, state_in=s0)
+        U.check(w, r1, ref, label=w.name + f" mu={mu}")
+
+
 def test_chunked_rejects_unsupported():
     import torch
 
