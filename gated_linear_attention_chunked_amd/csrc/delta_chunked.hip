@@ -16,9 +16,18 @@
 // Every exponent is g_t - g_s with s <= t (or g_C - g_t), so no factor exceeds
 // one and strong decays underflow to zero instead of overflowing.
 //
-// Schedule: one workgroup of 8 waves per (b, h, 32-wide slice of dv); rows of
-// W are independent, so slices never communicate.  Waves are split into a
-// carry, an output and a producer role; see the pipelined schedule below.
+// Two kernels per call:
+//   derivation: one workgroup per (sequence, head, chunk), all chunks at once.
+//          It forms everything that does not depend on the state (the
+//          inverses of the diagonal blocks of I + L, the off-diagonal coupling
+//          blocks, the gate prefix sums, the lower blocks of Q K^T * Gamma)
+//          and writes it to a workspace block of 12.75 KB per chunk.
+//   scan:  one workgroup of 8 waves per (b, h, 32-wide slice of dv); rows of
+//          W are independent, so slices never communicate.  Waves are split
+//          into a carry, an output and a producer role; see the pipelined
+//          schedule below.  The four slices of a head read the same workspace
+//          blocks, so the derivation is done once per head instead of once
+//          per slice.
 // The state slice S^T (dk x 16 per carry wave) lives in MFMA accumulator
 // layout for the whole scan.  An accumulator tile holds 4 consecutive rows per
 // lane, while a B operand wants 8 consecutive reduction indices; since a
@@ -40,23 +49,21 @@ constexpr int C = 64;    // chunk length (tokens)
 constexpr int BV = 32;   // dv columns per workgroup
 
 // ===========================================================================
-// Pipelined schedule (DeltaNet, Gated DeltaNet): 8 waves per workgroup, two
-// per SIMD, in three roles.  With D_i = (I + L_ii)^{-1} the inverse of
-// diagonal block i of I + L, G~_ij = Gamma * (E_i K_j^T) and Z = E S^T, block
-// row i of the solve is
+// With D_i = (I + L_ii)^{-1} the inverse of diagonal block i of I + L,
+// G~_ij = Gamma * (E_i K_j^T) and Z = E S^T, block row i of the solve is
 //     U_i = D_i diag(beta)_i Z'_i - D_i diag(beta gamma)_i Z_i + sum_{j<i} M_ij U_j,
 //     M_ij = -D_i diag(beta)_i G~_ij                (Z' = the targets V)
-// so everything but Z is state-independent.
+// so everything but Z is state-independent: the derivation kernel forms it,
+// together with the output's intra-chunk matrix Aqk = lower(Q K^T * Gamma).
+//
+// Pipelined scan: 8 waves per workgroup, two per SIMD, in three roles.
 //   carry  (waves 0-1, one 16-column tile each): Z = E S^T on MFMA, the
 //          block solve above on 16x16x16 MFMA (a four-link chain), publish U,
 //          then the state update accumulated in registers.
 //   output (waves 2-3, same tiles): Q S^T from the carry's bf16 state, then
 //          Y = diag(gamma) Q S^T + Aqk U once U is published; stores y.
-//   producers (waves 4-7): stage chunk c+1 into LDS (loads issued two chunks
-//          ahead).  Producer i then owns block row i: its E K^T tiles, the
-//          inverse of its diagonal block (fp32 forward substitution), its M_ij,
-//          plus 4 - i tiles of Q K^T for Aqk, so every producer computes five
-//          Gram tiles and needs nothing from the others after staging.
+//   producers (waves 4-7): stage chunk c+1 into LDS, its token rows and its
+//          derived block (loads issued two chunks ahead).
 // All eight waves meet at one LDS barrier per chunk; the hand-offs inside a
 // chunk go through bounded LDS counters.  The chunk loop is unrolled by the
 // double-buffer parity so every LDS address is a per-lane base plus a
@@ -64,8 +71,23 @@ constexpr int BV = 32;   // dv columns per workgroup
 // ===========================================================================
 constexpr int NLB = 6;     // strictly lower 16x16 blocks of a 64-row chunk
 constexpr int NQB = 10;    // lower 16x16 blocks including the diagonal
-constexpr int NT8 = 512;   // threads per workgroup of the WY schedule
+constexpr int NT8 = 512;   // threads per workgroup of the scan
+constexpr int NTD = 256;   // threads per workgroup of the derivation
 constexpr int LTS = 20;    // column stride (floats) of the fp32 diagonal blocks
+
+// State-independent matrices of one chunk.  The derivation kernel writes one
+// block per (sequence, head, chunk); the scan copies it into LDS unchanged.
+struct DerBlock {
+    bf16x4 dtil[4][64];        // D_i diag(beta)_i, A-operand order
+    bf16x4 dhn[4][64];         // -D_i diag(beta gamma)_i
+    bf16x4 mij[NLB][64];       // M_ij
+    float gam[C];              // gamma_t
+    float sc[C];               // gamma_C / gamma_t
+    float g[C];                // log2 gamma_t
+    bf16x4 aqk[NQB][64];       // lower(Q K^T * Gamma) blocks, A-operand order of the output's product
+};
+static_assert(sizeof(DerBlock) % 256 == 0, "workspace blocks stay 256-byte aligned");
+constexpr int kDerPieces = static_cast<int>(sizeof(DerBlock) / 16);  // 16-byte pieces
 
 template <int DK, bool GATES2>
 struct WyLds {
@@ -77,37 +99,35 @@ struct WyLds {
         alignas(16) __bf16 e[GATES2 ? C * KS : 8];  // erase-gated keys b * k (Gated DeltaNet-2)
         alignas(16) __bf16 v[C * VS];          // value targets of the workgroup's columns (w * v for Gated DeltaNet-2)
     };
-    struct Der {  // state-independent matrices of one chunk, double-buffered
-        alignas(16) bf16x4 dtil[4][64];        // D_i diag(beta)_i, A-operand order
-        alignas(16) bf16x4 dhn[4][64];         // -D_i diag(beta gamma)_i
-        alignas(16) bf16x4 mij[NLB][64];       // M_ij
-        alignas(16) float gam[C];              // gamma_t
-        alignas(16) float sc[C];               // gamma_C / gamma_t
-        alignas(16) float g[C];                // log2 gamma_t
-    };
     Raw raw[2];
-    Der der[2];
-    // producer-only, single-buffered: the chunk being derived
-    alignas(16) float la[C];                   // log2 of the decay (0 for padding)
-    alignas(16) float beta[C];                 // beta (0 for padding)
-    alignas(16) float g[C];                    // prefix sums of la
-    alignas(16) float lt[4][16 * LTS];         // diagonal blocks of L, fp32, by column
-    alignas(16) bf16x4 gx[3][64];              // -G~_3j (j < 3), made by producers 0 and 1 for producer 3
-    // output waves: lower(Q K^T * Gamma) blocks of the current chunk, A-operand order
-    alignas(16) bf16x4 aqk[NQB][64];
+    alignas(16) DerBlock der[2];
     // carry -> output
     alignas(16) bf16x4 uh[2][4][64];           // U of the current chunk, per tile
     alignas(16) bf16x4 sh[2][DK / 16][64];     // bf16 state fragments per tile
-    unsigned int pcount;                       // producer arrivals
     unsigned int ucount[2];                    // U publications per tile
     unsigned int scount[2];                    // state fragments consumed per tile
-    unsigned int acount;                       // Aqk halves published by the output waves
-    unsigned int gcount;                       // row-3 Gram blocks published by producers 0, 1
 };
 
+// rows past the end become zeros (a bitwise mask keeps the registers out of
+// the select-of-aggregates form that lands them in scratch)
+__device__ __forceinline__ uint4 masked(uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); }
+// elementwise product of eight bf16 pairs, rounded to bf16 (nearest even)
+__device__ __forceinline__ uint4 mul8(uint4 x, uint4 y) {
+    const uint32_t xa[4] = {x.x, x.y, x.z, x.w}, ya[4] = {y.x, y.y, y.z, y.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float lo = bf16_bits_to_f32(static_cast<uint16_t>(xa[j])) * bf16_bits_to_f32(static_cast<uint16_t>(ya[j]));
+        const float hi = bf16_bits_to_f32(static_cast<uint16_t>(xa[j] >> 16)) *
+                         bf16_bits_to_f32(static_cast<uint16_t>(ya[j] >> 16));
+        r[j] = static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+    }
+    return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
 // S^T = gamma_C S^T + K^T diag(gamma_C / gamma) U for one 16-column tile.
-template <int KT, typename Raw, typename Der>
-__device__ __forceinline__ void state_update(f32x4 (&St)[KT], const Raw &R, const Der &D, const bf16x4 (&ub)[4],
+template <int KT, typename Raw>
+__device__ __forceinline__ void state_update(f32x4 (&St)[KT], const Raw &R, const DerBlock &D, const bf16x4 (&ub)[4],
                                              int KS, int lane) {
     const int lg = lane >> 4;
     // operand reads first, then the scaling of U while they are in flight
@@ -133,18 +153,8 @@ __device__ __forceinline__ void state_update(f32x4 (&St)[KT], const Raw &R, cons
         for (int kt = 0; kt < KT; ++kt) St[kt] = mfma32(af[h2][kt], h2 ? bW1 : bW0, St[kt]);
 }
 
-// Q K^T tiles per output wave: block rows {0, 3} (set A) or {1, 2} (set B)
-// of the lower 4x4 block triangle, five tiles each.
-struct TilesA {
-    static constexpr int ti[5] = {0, 3, 3, 3, 3}, si[5] = {0, 0, 1, 2, 3};
-    static constexpr int nk = 4;  // key fragments used
-};
-struct TilesB {
-    static constexpr int ti[5] = {1, 1, 2, 2, 2}, si[5] = {0, 1, 0, 1, 2};
-    static constexpr int nk = 3;
-};
-// E K^T tiles per producer i: three each for producers 0-2, which also take
-// the off-diagonal tiles of block row 3, so producer 3 only forms (3, 3).
+// E K^T tiles per derivation wave i: three each for waves 0-2, which also
+// take the off-diagonal tiles of block row 3, so wave 3 only forms (3, 3).
 // tmask / smask: the 16-row blocks used as rows (E) and as columns (K).
 template <int I> struct RowTiles;
 template <> struct RowTiles<0> {
@@ -166,8 +176,257 @@ template <> struct RowTiles<3> {
 __device__ __forceinline__ constexpr int lower_block(int i, int j) { return i * (i - 1) / 2 + j; }  // j < i
 __device__ __forceinline__ constexpr int tri_block(int i, int j) { return i * (i + 1) / 2 + j; }    // j <= i
 
+// ============================== derivation ==============================
+template <int DK, bool GATES2>
+struct DeriveLds {
+    static constexpr int KS = DK + 8;
+    alignas(16) __bf16 k[C * KS];
+    alignas(16) __bf16 e[GATES2 ? C * KS : 8];
+    alignas(16) float la[C];                   // log2 of the decay (0 for padding)
+    alignas(16) float beta[C];                 // beta (0 for padding)
+    alignas(16) float g[C];                    // prefix sums of la
+    alignas(16) float lt[4][16 * LTS];         // diagonal blocks of L, fp32, by column
+    alignas(16) bf16x4 gx[3][64];              // -G~_3j (j < 3), made by waves 0 and 1 for wave 3
+    alignas(16) DerBlock d;
+    unsigned int gcount;                       // row-3 Gram blocks published by waves 0, 1
+};
+
+// One workgroup of four waves per (sequence, head, chunk); wave i stages key
+// rows [16i, 16i + 16) and then owns block row i of L: its E K^T tiles, the
+// inverse of its diagonal block (fp32 forward substitution) and its M_ij.
+// It also forms block row i of Aqk from its own query rows, which it reads
+// from global memory straight into fragments.
 template <int VARIANT, int DK>
-__global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
+__global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, DerBlock *__restrict__ out) {
+    constexpr bool kDecay = VARIANT != kDeltaNet;
+    constexpr bool kGates2 = VARIANT == kGatedDeltaNet2;
+    constexpr int KS = DK + 8;
+    constexpr int KSTEP = DK / 32;
+    using Lds = DeriveLds<DK, kGates2>;
+    __shared__ Lds s;
+
+    const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
+    const int nchunks = (T + C - 1) / C;
+    const int task = blockIdx.x;
+    const int head = task / nchunks, c = task - head * nchunks;
+    const int b = head / H, h = head % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lg = lane >> 4, lc = lane & 15;
+    const int t0 = c * C, last = T - 1 - t0;
+    const int64_t base = (static_cast<int64_t>(b) * T + t0) * H + h;  // token index of chunk row 0
+
+    // ---- staging: a dk-wide row is DK/8 16-byte pieces, 64*8/DK rows per load
+    constexpr int PPR = DK / 8, RPI = 64 / PPR, NQK = 16 / RPI;
+    const uint32_t hdk = static_cast<uint32_t>(H * DK);
+    const int krow = 16 * w + lane / PPR;
+    const uint16_t *k0 = static_cast<const uint16_t *>(a.k) + base * DK;
+    const uint16_t *b0 = static_cast<const uint16_t *>(a.erase_b) + base * DK;
+    uint4 kr[NQK], br[kGates2 ? NQK : 1];
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+        const uint32_t o = static_cast<uint32_t>(min(krow + RPI * i, last)) * hdk + (lane % PPR) * 8;
+        kr[i] = *reinterpret_cast<const uint4 *>(k0 + o);
+        if constexpr (kGates2) br[i] = *reinterpret_cast<const uint4 *>(b0 + o);
+    }
+    // query fragments of block row w: lane (lg, lc) holds row 16w + lc,
+    // columns 32p + 4lg .. +3 and 32p + 16 + 4lg .. +3 (zero past the end)
+    bf16x4 qlo[KSTEP], qhi[KSTEP];
+    {
+        const int qr = 16 * w + lc;
+        const uint16_t *qp = static_cast<const uint16_t *>(a.q) + base * DK +
+                             static_cast<uint32_t>(min(qr, last)) * hdk + 4 * lg;
+        const bf16x4 zq = {};
+#pragma unroll
+        for (int p = 0; p < KSTEP; ++p) {
+            qlo[p] = *reinterpret_cast<const bf16x4 *>(qp + 32 * p);
+            qhi[p] = *reinterpret_cast<const bf16x4 *>(qp + 32 * p + 16);
+        }
+        if (qr > last) {
+#pragma unroll
+            for (int p = 0; p < KSTEP; ++p) qlo[p] = qhi[p] = zq;
+        }
+    }
+    // decay (wave 0) or beta (wave 1) of row `lane`
+    uint16_t rs = 0;
+    if (w == 1 || (w == 0 && kDecay)) {
+        const uint16_t *gsc = static_cast<const uint16_t *>(w == 0 ? a.alpha : a.beta);
+        rs = gsc[base + static_cast<int64_t>(min(lane, last)) * H];
+    }
+    if (tid == 0) s.gcount = 0u;
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+        const int row = krow + RPI * i;
+        const uint32_t m = row <= last ? 0xffffffffu : 0u;
+        *reinterpret_cast<uint4 *>(&s.k[row * KS + (lane % PPR) * 8]) = masked(kr[i], m);
+        if constexpr (kGates2) *reinterpret_cast<uint4 *>(&s.e[row * KS + (lane % PPR) * 8]) = masked(mul8(kr[i], br[i]), m);
+    }
+    if (w == 0) s.la[lane] = (kDecay && lane <= last) ? fmaxf(__builtin_amdgcn_logf(bf16_bits_to_f32(rs)), -200.f) : 0.f;
+    if (w == 1) s.beta[lane] = lane <= last ? bf16_bits_to_f32(rs) : 0.f;
+    __syncthreads();
+
+    // ---- gate prefix sums
+    DerBlock &D = s.d;
+    if (w == 0) {
+        const float g = wave_prefix_sum(s.la[lane]);
+        const float gl = __shfl(g, 63, 64);
+        s.g[lane] = g;
+        D.g[lane] = g;
+        D.gam[lane] = exp2_fast(g);
+        D.sc[lane] = exp2_fast(gl - g);
+    }
+    __syncthreads();
+
+    // ---- E K^T tiles, inverse of the diagonal block and M of block row I
+    auto work = [&](auto ic_) {
+        constexpr int I = decltype(ic_)::value;
+        using Tl = RowTiles<I>;
+        constexpr int NT = Tl::n;
+        f32x4 acc[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < KSTEP; ++p) {
+            bf16x8 kf[4], ef[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {  // key rows as columns (smask) and, unless E is
+                                            // separate, as rows (tmask); E rows for Gated DeltaNet-2
+                if (((kGates2 ? Tl::smask : Tl::smask | Tl::tmask) >> j) & 1)
+                    kf[j] = row_frag2(s.k, KS, 16 * j, 32 * p, lane);
+                if (kGates2 && ((Tl::tmask >> j) & 1)) ef[j] = row_frag2(s.e, KS, 16 * j, 32 * p, lane);
+            }
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[j] = mfma32(kGates2 ? ef[Tl::ti[j]] : kf[Tl::ti[j]], kf[Tl::si[j]], acc[j]);
+        }
+        // E K^T tiles: lane (lg, lc) holds G[t = 16ti + 4lg + r][s = 16si + lc]
+        bf16x4 gneg[4];   // -G~_Ij in accumulator order (own block row only)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int ti = Tl::ti[j], si = Tl::si[j];
+            const float4 gt4 = *reinterpret_cast<const float4 *>(&s.g[16 * ti + 4 * lg]);
+            const float gt[4] = {gt4.x, gt4.y, gt4.z, gt4.w};
+            const float gs = s.g[16 * si + lc];
+            f32x4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = kDecay ? acc[j][r] * exp2_fast(fminf(gt[r] - gs, 0.f)) : acc[j][r];
+                x[r] = (si < ti || lc < 4 * lg + r) ? v : 0.f;
+            }
+            if (si == ti) {
+                const float4 bt4 = *reinterpret_cast<const float4 *>(&s.beta[16 * ti + 4 * lg]);
+                *reinterpret_cast<float4 *>(&s.lt[ti][lc * LTS + 4 * lg]) =
+                    make_float4(bt4.x * x[0], bt4.y * x[1], bt4.z * x[2], bt4.w * x[3]);
+            } else if (ti == I) {
+                gneg[si] = bf4(-x);
+            } else {
+                s.gx[si][lane] = bf4(-x);  // row 3 block computed for wave 3
+            }
+        }
+        if constexpr (I < 2) lds_arrive(&s.gcount, lane);
+        // D_I = (I + L_II)^{-1} by forward substitution in fp32;
+        // lane = (column col, row quad q)
+        const int col = lane >> 2, q = lane & 3;
+        // each column piece is read as two 8-byte loads: on gfx950 a 16-byte
+        // LDS read costs several times two 8-byte reads
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(3))) volatile const f32x2 vlds_f2;
+        const auto lt = reinterpret_cast<__attribute__((address_space(3))) const float *>(
+            (__attribute__((address_space(3))) const void *)&s.lt[I][4 * q]);
+        auto ltcol = [&](int j) {
+            const f32x2 lo = *reinterpret_cast<vlds_f2 *>(lt + j * LTS);
+            const f32x2 hi = *reinterpret_cast<vlds_f2 *>(lt + j * LTS + 2);
+            return f32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == col) ? 1.f : 0.f;
+        // The columns of L do not depend on X: each is read PF steps before
+        // its use, so the sweep does not wait on LDS latency.
+        constexpr int PF = 3;
+        f32x4 lw[PF + 1];
+#pragma unroll
+        for (int j = 0; j < PF; ++j) lw[j] = ltcol(j);
+        auto sweep = [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr (j + PF < 15) lw[(j + PF) % (PF + 1)] = ltcol(j + PF);
+            const f32x4 lj = lw[j % (PF + 1)];                           // L[4q + r][j]
+            const float xj = quad_bcast<j / 4>(x[j % 4]);                // X[j][col]
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = fmaf(-lj[r], xj, x[r]);
+        };
+        static_for<15>(sweep);
+        // D diag(beta) and -D diag(beta gamma): element (row, col) goes to
+        // A-operand lane (col / 4) * 16 + row, slot col % 4
+        const float bcol = s.beta[16 * I + col];
+        const float bgcol = -bcol * (kDecay ? exp2_fast(s.g[16 * I + col]) : 1.f);
+        __bf16 *dt = reinterpret_cast<__bf16 *>(&D.dtil[I][0]);
+        __bf16 *dh = reinterpret_cast<__bf16 *>(&D.dhn[I][0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = ((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3);
+            dt[e] = static_cast<__bf16>(x[r] * bcol);
+            dh[e] = static_cast<__bf16>(x[r] * bgcol);
+        }
+        // M_Ij = -D~_I G~_Ij, computed transposed (A = -G~^T from the
+        // accumulators, B = D~_I^T from its A-operand fragment) so the result
+        // comes out in A-operand order
+        if constexpr (I > 0) {
+            if constexpr (I == 3) {
+                lds_wait(&s.gcount, 2u);  // blocks (3,0), (3,1), (3,2) from waves 0, 1
+#pragma unroll
+                for (int j = 0; j < 3; ++j) gneg[j] = s.gx[j][lane];
+            }
+            wave_lds_fence();  // this wave's D~_I pieces before the fragment read
+            const bf16x4 dfrag = D.dtil[I][lane];
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < I; ++j) D.mij[lower_block(I, j)][lane] = bf4(mfma16(gneg[j], dfrag, zero));
+        }
+    };
+    if (w == 0) work(ic<0>{});
+    else if (w == 1) work(ic<1>{});
+    else if (w == 2) work(ic<2>{});
+    else work(ic<3>{});
+
+    // ---- Aqk tiles (w, j), j <= w: lane (lg, lc) holds Aqk[t = 16w + lc][s = 16j + 4lg + r]
+    {
+        f32x4 acc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < KSTEP; ++p) {
+            const bf16x8 qf = cat8(qlo[p], qhi[p]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j <= w) acc[j] = mfma32(row_frag2(s.k, KS, 16 * j, 32 * p, lane), qf, acc[j]);
+        }
+        const float gt = s.g[16 * w + lc];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j > w) continue;
+            const float4 gs4 = *reinterpret_cast<const float4 *>(&s.g[16 * j + 4 * lg]);
+            const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
+            f32x4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // exponent clamped at 0 so masked entries stay finite
+                const float v = kDecay ? acc[j][r] * exp2_fast(fminf(gt - gs[r], 0.f)) : acc[j][r];
+                x[r] = (j < w || 4 * lg + r <= lc) ? v : 0.f;
+            }
+            D.aqk[tri_block(w, j)][lane] = bf4(x);
+        }
+    }
+    __syncthreads();
+
+    // ---- the block, 16 bytes per thread and pass
+    const uint4 *src = reinterpret_cast<const uint4 *>(&s.d);
+    uint4 *dst = reinterpret_cast<uint4 *>(out + task);
+    for (int i = tid; i < kDerPieces; i += NTD) dst[i] = src[i];
+}
+
+// ================================= scan =================================
+template <int VARIANT, int DK>
+__global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, const DerBlock *__restrict__ der) {
     constexpr bool kDecay = VARIANT != kDeltaNet;
     constexpr int KS = DK + 8;
     constexpr int KSTEP = DK / 32;
@@ -189,11 +448,8 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
     auto tok = [&](int t) { return (static_cast<int64_t>(b) * T + t) * H + h; };
 
     if (tid == 0) {
-        s.pcount = 0u;
         s.ucount[0] = s.ucount[1] = 0u;
         s.scount[0] = s.scount[1] = 0u;
-        s.acount = 0u;
-        s.gcount = 0u;
     }
     __syncthreads();  // counters visible before any role starts
 
@@ -228,7 +484,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
         auto step = [&](auto par, int c) {
             constexpr int P = decltype(par)::value;
             const typename Lds::Raw &R = s.raw[P];
-            const typename Lds::Der &D = s.der[P];
+            const DerBlock &D = s.der[P];
             bf16x8 bS[KSTEP];
             if (is_carry) {
                 // Every read that does not depend on the state goes out first:
@@ -285,65 +541,37 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(s.sh[vt][2 * p][lane], s.sh[vt][2 * p + 1][lane]);
                 lds_arrive(&s.scount[vt], lane);  // the carry may overwrite sh from here on
-                // One pass over dk: Q S^T (four row tiles) and five tiles of
-                // K Q^T, which come out as Aqk in A-operand order: output wave 0
-                // takes block rows {0, 3}, wave 1 rows {1, 2}.
-                auto pass = [&](auto tiles) {
-                    using Tl = decltype(tiles);
-                    f32x4 xq[4], aq[5];
+                // Q S^T, four row tiles
+                f32x4 xq[4];
 #pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) xq[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ti = 0; ti < 4; ++ti) xq[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int j = 0; j < 5; ++j) aq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int p = 0; p < KSTEP; ++p) {
+                    bf16x8 qf[4];
 #pragma unroll
-                    for (int p = 0; p < KSTEP; ++p) {
-                        bf16x8 qf[4], kf[Tl::nk];
+                    for (int i = 0; i < 4; ++i) qf[i] = row_frag2(R.q, KS, 16 * i, 32 * p, lane);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) qf[i] = row_frag2(R.q, KS, 16 * i, 32 * p, lane);
+                    for (int ti = 0; ti < 4; ++ti) xq[ti] = mfma32(bS[p], qf[ti], xq[ti]);
+                }
+                bf16x4 aq[NQB];
 #pragma unroll
-                        for (int i = 0; i < Tl::nk; ++i) kf[i] = row_frag2(R.k, KS, 16 * i, 32 * p, lane);
-#pragma unroll
-                        for (int ti = 0; ti < 4; ++ti) xq[ti] = mfma32(bS[p], qf[ti], xq[ti]);
-#pragma unroll
-                        for (int j = 0; j < 5; ++j) aq[j] = mfma32(kf[Tl::si[j]], qf[Tl::ti[j]], aq[j]);
-                    }
-                    // lane (lg, lc): Aqk[t = 16ti + lc][s = 16si + 4lg + r]
-#pragma unroll
-                    for (int j = 0; j < 5; ++j) {
-                        const int ti = Tl::ti[j], si = Tl::si[j];
-                        const float gt = D.g[16 * ti + lc];
-                        const float4 gs4 = *reinterpret_cast<const float4 *>(&D.g[16 * si + 4 * lg]);
-                        const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
-                        f32x4 x;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            // exponent clamped at 0 so masked entries stay finite
-                            const float v = kDecay ? aq[j][r] * exp2_fast(fminf(gt - gs[r], 0.f)) : aq[j][r];
-                            x[r] = (si < ti || 4 * lg + r <= lc) ? v : 0.f;
-                        }
-                        s.aqk[tri_block(ti, si)][lane] = bf4(x);
-                    }
-                    return std::array<f32x4, 4>{xq[0], xq[1], xq[2], xq[3]};
-                };
-                const std::array<f32x4, 4> xq = vt == 0 ? pass(TilesA{}) : pass(TilesB{});
-                lds_arrive(&s.acount, lane);
+                for (int i = 0; i < NQB; ++i) aq[i] = D.aqk[i][lane];
                 lds_wait(&s.ucount[vt], static_cast<unsigned int>(c + 1));
                 bf16x4 ub[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ub[i] = s.uh[vt][i][lane];
-                lds_wait(&s.acount, static_cast<unsigned int>(2 * (c + 1)));
                 // Y^T = S Q^T diag(gamma) + U^T lower(Q K^T * Gamma)^T
                 f32x4 y[4];
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) y[ti] = xq[ti] * D.gam[16 * ti + lc];
                 const bf16x8 aU0 = cat8(ub[0], ub[1]), aU1 = cat8(ub[2], ub[3]);
                 const bf16x4 z4 = {};
-                y[0] = mfma32(aU0, cat8(s.aqk[tri_block(0, 0)][lane], z4), y[0]);
-                y[1] = mfma32(aU0, cat8(s.aqk[tri_block(1, 0)][lane], s.aqk[tri_block(1, 1)][lane]), y[1]);
-                y[2] = mfma32(aU0, cat8(s.aqk[tri_block(2, 0)][lane], s.aqk[tri_block(2, 1)][lane]), y[2]);
-                y[2] = mfma32(aU1, cat8(s.aqk[tri_block(2, 2)][lane], z4), y[2]);
-                y[3] = mfma32(aU0, cat8(s.aqk[tri_block(3, 0)][lane], s.aqk[tri_block(3, 1)][lane]), y[3]);
-                y[3] = mfma32(aU1, cat8(s.aqk[tri_block(3, 2)][lane], s.aqk[tri_block(3, 3)][lane]), y[3]);
+                y[0] = mfma32(aU0, cat8(aq[tri_block(0, 0)], z4), y[0]);
+                y[1] = mfma32(aU0, cat8(aq[tri_block(1, 0)], aq[tri_block(1, 1)]), y[1]);
+                y[2] = mfma32(aU0, cat8(aq[tri_block(2, 0)], aq[tri_block(2, 1)]), y[2]);
+                y[2] = mfma32(aU1, cat8(aq[tri_block(2, 2)], z4), y[2]);
+                y[3] = mfma32(aU0, cat8(aq[tri_block(3, 0)], aq[tri_block(3, 1)]), y[3]);
+                y[3] = mfma32(aU1, cat8(aq[tri_block(3, 2)], aq[tri_block(3, 3)]), y[3]);
                 const int t0 = c * C;
                 uint16_t *yo = static_cast<uint16_t *>(a.out) + tok(t0) * dv + yoff;
                 if (t0 + C <= T) {
@@ -359,7 +587,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
             }
             lds_barrier();
         };
-        lds_barrier();  // chunk 0 staged and derived, initial state published
+        lds_barrier();  // chunk 0 staged, initial state published
         for (int c = 0; c < nchunks; c += 2) {
             step(ic<0>{}, c);
             if (c + 1 < nchunks) step(ic<1>{}, c + 1);
@@ -376,7 +604,6 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
         const uint16_t *gq = static_cast<const uint16_t *>(a.q);
         const uint16_t *gk = static_cast<const uint16_t *>(a.k);
         const uint16_t *gv = static_cast<const uint16_t *>(a.v);
-        const uint16_t *gsc = static_cast<const uint16_t *>(pw == 0 ? a.alpha : a.beta);
         // Coalesced staging: a dk-wide bf16 row is DK/8 16-byte pieces, so
         // one load instruction covers 64*8/DK consecutive rows; a row of the
         // workgroup's 32 value columns is 4 pieces (16 rows per instruction).
@@ -386,7 +613,11 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
         const uint32_t hdk = static_cast<uint32_t>(H * DK), hdv = static_cast<uint32_t>(H * dv);
         const int qrow = 16 * pw + lane / PPR;  // chunk row of this lane's first q/k piece
         const int vrow = 16 * pw + (lane >> 2);
-        // Two staging sets, one per chunk parity: loads run two chunks ahead.
+        // Pieces of the derived block: 64pw + lane + 256j, j < 4, where they exist.
+        const int dp0 = 64 * pw + lane;
+        constexpr int NDP = (kDerPieces + 255) / 256;
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 *gder = reinterpret_cast<const u32x4 *>(der + static_cast<int64_t>(head) * nchunks);
         // NS staging sets: loads run NS chunks ahead.  Gated DeltaNet-2 stages
         // two more streams (erase and write gates) and keeps one set.
         constexpr int NS = kGates2 ? 1 : 2;
@@ -396,8 +627,8 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
         struct Stage {
             uint4 q[NQK], k[NQK], v;
             uint4 b[NQKG], w;  // erase / write gates (Gated DeltaNet-2)
-            uint32_t rs;   // raw bf16 bits of the decay (pw 0) or beta (pw 1) of row `lane`
-            uint32_t okm;  // bit i: row of q/k load i inside the sequence; bit NQK: v row; bit NQK+1: gate row
+            u32x4 d[NDP];      // pieces of the derived block
+            uint32_t okm;      // bit i: row of q/k load i inside the sequence; bit NQK: v row
         };
         Stage st[NS];
         // Loads read clamped, always valid rows; rows past the end are replaced
@@ -429,27 +660,9 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
             ov += v0 + 8 * (lane & 3);
             g.v = *reinterpret_cast<const uint4 *>(gv + base * dv + ov);
             if constexpr (kGates2) g.w = *reinterpret_cast<const uint4 *>(gww + base * dv + ov);
-            g.rs = 0u;
-            if (pw <= 1) {
-                g.okm |= (lane <= last ? 1u : 0u) << (NQK + 1);
-                if (pw == 1 || kDecay) g.rs = static_cast<uint32_t>(gsc[base + static_cast<uint32_t>(min(lane, last)) * H]);
-            }
-        };
-        // rows past the end become zeros (a bitwise mask keeps the registers
-        // out of the select-of-aggregates form that lands them in scratch)
-        auto masked = [](uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); };
-        // elementwise product of eight bf16 pairs, rounded to bf16 (nearest even)
-        auto mul8 = [](uint4 x, uint4 y) {
-            const uint32_t xa[4] = {x.x, x.y, x.z, x.w}, ya[4] = {y.x, y.y, y.z, y.w};
-            uint32_t r[4];
+            const u32x4 *src = gder + static_cast<int64_t>(c) * kDerPieces;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float lo = bf16_bits_to_f32(static_cast<uint16_t>(xa[j])) * bf16_bits_to_f32(static_cast<uint16_t>(ya[j]));
-                const float hi = bf16_bits_to_f32(static_cast<uint16_t>(xa[j] >> 16)) *
-                                 bf16_bits_to_f32(static_cast<uint16_t>(ya[j] >> 16));
-                r[j] = static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
-            }
-            return make_uint4(r[0], r[1], r[2], r[3]);
+            for (int j = 0; j < NDP; ++j) g.d[j] = src[min(dp0 + 256 * j, kDerPieces - 1)];
         };
         auto commit = [&](auto par) {
             typename Lds::Raw &R = s.raw[decltype(par)::value];
@@ -466,164 +679,26 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
             const uint32_t mv = 0u - ((g.okm >> NQK) & 1u);
             *reinterpret_cast<uint4 *>(&R.v[vrow * Lds::VS + 8 * (lane & 3)]) =
                 masked(kGates2 ? mul8(g.v, g.w) : g.v, mv);
-            const bool gok = (g.okm >> (NQK + 1)) & 1u;
-            if (pw == 0) {
-                const float al = bf16_bits_to_f32(static_cast<uint16_t>(g.rs));
-                s.la[lane] = (kDecay && gok) ? fmaxf(__builtin_amdgcn_logf(al), -200.f) : 0.f;
-            } else if (pw == 1) {
-                s.beta[lane] = gok ? bf16_bits_to_f32(static_cast<uint16_t>(g.rs)) : 0.f;
-            }
+            u32x4 *dd = reinterpret_cast<u32x4 *>(&s.der[decltype(par)::value]);
+#pragma unroll
+            for (int j = 0; j < NDP; ++j)
+                if (dp0 + 256 * j < kDerPieces) dd[dp0 + 256 * j] = g.d[j];
         };
-        unsigned int target = 0;
-        auto psync = [&]() {
-            target += 4;
-            lds_arrive(&s.pcount, lane);
-            lds_wait(&s.pcount, target);
-        };
-        unsigned int nderived = 0;  // chunks derived so far, this one included
-        // State-independent matrices of the chunk in buffer `par`.
-        auto derive = [&](auto par) {
-            ++nderived;
-            const typename Lds::Raw &R = s.raw[decltype(par)::value];
-            typename Lds::Der &D = s.der[decltype(par)::value];
-            // gate prefix sums; every producer writes the same values
-            const float g = wave_prefix_sum(s.la[lane]);
-            s.g[lane] = g;
-            if (pw == 0) {
-                const float gl = __shfl(g, 63, 64);
-                D.g[lane] = g;
-                D.gam[lane] = exp2_fast(g);
-                D.sc[lane] = exp2_fast(gl - g);
-            }
-            // ---- E K^T tiles of block row i (i + 1 tiles) on producer i
-            auto work = [&](auto ic_) {
-                constexpr int I = decltype(ic_)::value;   // block row of L owned here
-                using Tl = RowTiles<I>;
-                constexpr int NT = Tl::n;
-                f32x4 acc[NT];
-#pragma unroll
-                for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < KSTEP; ++p) {
-                    bf16x8 kf[4], ef[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {  // key rows as columns (smask) and, unless E is
-                                                    // separate, as rows (tmask); E rows for Gated DeltaNet-2
-                        if (((kGates2 ? Tl::smask : Tl::smask | Tl::tmask) >> j) & 1)
-                            kf[j] = row_frag2(R.k, KS, 16 * j, 32 * p, lane);
-                        if (kGates2 && ((Tl::tmask >> j) & 1)) ef[j] = row_frag2(R.e, KS, 16 * j, 32 * p, lane);
-                    }
-#pragma unroll
-                    for (int j = 0; j < NT; ++j)
-                        acc[j] = mfma32(kGates2 ? ef[Tl::ti[j]] : kf[Tl::ti[j]], kf[Tl::si[j]], acc[j]);
-                }
-                // E K^T tiles: lane (lg, lc) holds G[t = 16ti + 4lg + r][s = 16si + lc]
-                bf16x4 gneg[4];   // -G~_Ij in accumulator order (own block row only)
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const int ti = Tl::ti[j], si = Tl::si[j];
-                    const float4 gt4 = *reinterpret_cast<const float4 *>(&s.g[16 * ti + 4 * lg]);
-                    const float gt[4] = {gt4.x, gt4.y, gt4.z, gt4.w};
-                    const float gs = s.g[16 * si + lc];
-                    f32x4 x;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float v = kDecay ? acc[j][r] * exp2_fast(fminf(gt[r] - gs, 0.f)) : acc[j][r];
-                        x[r] = (si < ti || lc < 4 * lg + r) ? v : 0.f;
-                    }
-                    if (si == ti) {
-                        const float4 bt4 = *reinterpret_cast<const float4 *>(&s.beta[16 * ti + 4 * lg]);
-                        *reinterpret_cast<float4 *>(&s.lt[ti][lc * LTS + 4 * lg]) =
-                            make_float4(bt4.x * x[0], bt4.y * x[1], bt4.z * x[2], bt4.w * x[3]);
-                    } else if (ti == I) {
-                        gneg[si] = bf4(-x);
-                    } else {
-                        s.gx[si][lane] = bf4(-x);  // row 3 block computed for producer 3
-                    }
-                }
-                if constexpr (I < 2) lds_arrive(&s.gcount, lane);
-                // D_I = (I + L_II)^{-1} by forward substitution in fp32;
-                // lane = (column col, row quad q)
-                const int col = lane >> 2, q = lane & 3;
-                // each column piece is read as two 8-byte loads: on gfx950 a
-                // 16-byte LDS read costs several times two 8-byte reads
-                typedef float f32x2 __attribute__((ext_vector_type(2)));
-                typedef __attribute__((address_space(3))) volatile const f32x2 vlds_f2;
-                const auto lt = reinterpret_cast<__attribute__((address_space(3))) const float *>(
-                    (__attribute__((address_space(3))) const void *)&s.lt[I][4 * q]);
-                auto ltcol = [&](int j) {
-                    const f32x2 lo = *reinterpret_cast<vlds_f2 *>(lt + j * LTS);
-                    const f32x2 hi = *reinterpret_cast<vlds_f2 *>(lt + j * LTS + 2);
-                    return f32x4{lo[0], lo[1], hi[0], hi[1]};
-                };
-                float x[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == col) ? 1.f : 0.f;
-                // The columns of L do not depend on X: each is read PF steps
-                // before its use, so the sweep does not wait on LDS latency.
-                constexpr int PF = 3;
-                f32x4 lw[PF + 1];
-#pragma unroll
-                for (int j = 0; j < PF; ++j) lw[j] = ltcol(j);
-                auto sweep = [&](auto jc) {
-                    constexpr int j = decltype(jc)::value;
-                    if constexpr (j + PF < 15) lw[(j + PF) % (PF + 1)] = ltcol(j + PF);
-                    const f32x4 lj = lw[j % (PF + 1)];                           // L[4q + r][j]
-                    const float xj = quad_bcast<j / 4>(x[j % 4]);                // X[j][col]
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) x[r] = fmaf(-lj[r], xj, x[r]);
-                };
-                static_for<15>(sweep);
-                // D diag(beta) and -D diag(beta gamma): element (row, col) goes to
-                // A-operand lane (col / 4) * 16 + row, slot col % 4
-                const float bcol = s.beta[16 * I + col];
-                const float bgcol = -bcol * (kDecay ? exp2_fast(s.g[16 * I + col]) : 1.f);
-                __bf16 *dt = reinterpret_cast<__bf16 *>(&D.dtil[I][0]);
-                __bf16 *dh = reinterpret_cast<__bf16 *>(&D.dhn[I][0]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int e = ((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3);
-                    dt[e] = static_cast<__bf16>(x[r] * bcol);
-                    dh[e] = static_cast<__bf16>(x[r] * bgcol);
-                }
-                // M_Ij = -D~_I G~_Ij, computed transposed (A = -G~^T from the
-                // accumulators, B = D~_I^T from its A-operand fragment) so the
-                // result comes out in A-operand order
-                if constexpr (I > 0) {
-                    if constexpr (I == 3) {
-                        lds_wait(&s.gcount, 2u * nderived);  // blocks (3,0), (3,1), (3,2) from producers 0, 1
-#pragma unroll
-                        for (int j = 0; j < 3; ++j) gneg[j] = s.gx[j][lane];
-                    }
-                    const bf16x4 dfrag = D.dtil[I][lane];
-                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int j = 0; j < I; ++j) D.mij[lower_block(I, j)][lane] = bf4(mfma16(gneg[j], dfrag, zero));
-                }
-            };
-            if (pw == 0) work(ic<0>{});
-            else if (pw == 1) work(ic<1>{});
-            else if (pw == 2) work(ic<2>{});
-            else work(ic<3>{});
-        };
-
-        // Preparing chunk n: stage it from its set, refill that set with
-        // chunk n + NS, then derive chunk n.  The refill is issued on every
-        // path (past the end it reloads the last chunk, which is never
-        // staged), so the loads in flight always form the same queue and the
-        // staging waits only for the older set.
+        // Preparing chunk n: stage it from its set, then refill that set with
+        // chunk n + NS.  The refill is issued on every path (past the end it
+        // reloads the last chunk, which is never staged), so the loads in
+        // flight always form the same queue and the staging waits only for
+        // the older set.
         auto prepare = [&](auto par, int n) {
             commit(par);
             fetch(par, min(n + NS, nchunks - 1));
-            psync();
-            derive(par);
         };
         if (nchunks > 0) {
             fetch(ic<0>{}, 0);
             if constexpr (NS == 2) fetch(ic<1>{}, min(1, nchunks - 1));
             prepare(ic<0>{}, 0);
         }
-        lds_barrier();  // chunk 0 staged and derived
+        lds_barrier();  // chunk 0 staged
         // One barrier per chunk, as in the carry and output loop.  The loop
         // has a single exit and every trip runs both prepares, so each path
         // around it issues the same loads in the same order and a staging
@@ -645,15 +720,49 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a) {
     }
 }
 
+// The stream-ordered pool keeps freed workspace for the next call instead of
+// returning it to the device at every synchronisation.
+void keep_pool_memory() {
+    static bool done[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || done[dev]) return;
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+        uint64_t keep = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    }
+    done[dev] = true;
+}
+
+template <int VARIANT, int DK>
+hipError_t launch_dk(const DeltaArgs &a, hipStream_t stream) {
+    const int64_t nchunks = (a.T + C - 1) / C;
+    const int64_t tasks = a.B * a.H * nchunks;
+    const unsigned blocks = static_cast<unsigned>(a.B * a.H * (a.dv / BV));
+    if (tasks > 0x7fffffff) return hipErrorInvalidValue;
+    DerBlock *der = nullptr;
+    if (tasks > 0) {
+        keep_pool_memory();
+        hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&der), static_cast<size_t>(tasks) * sizeof(DerBlock), stream);
+        if (e != hipSuccess) return e;
+        delta_chunked_derive_kernel<VARIANT, DK><<<static_cast<unsigned>(tasks), NTD, 0, stream>>>(a, der);
+    }
+    delta_chunked_wy_kernel<VARIANT, DK><<<blocks, NT8, 0, stream>>>(a, der);
+    const hipError_t e = hipGetLastError();
+    if (der) {
+        const hipError_t f = hipFreeAsync(der, stream);
+        if (e == hipSuccess && f != hipSuccess) return f;
+    }
+    return e;
+}
+
 template <int VARIANT>
 hipError_t launch_var(const DeltaArgs &a, hipStream_t stream) {
-    const unsigned blocks = static_cast<unsigned>(a.B * a.H * (a.dv / BV));
     switch (a.dk) {
-        case 64: delta_chunked_wy_kernel<VARIANT, 64><<<blocks, NT8, 0, stream>>>(a); break;
-        case 128: delta_chunked_wy_kernel<VARIANT, 128><<<blocks, NT8, 0, stream>>>(a); break;
+        case 64: return launch_dk<VARIANT, 64>(a, stream);
+        case 128: return launch_dk<VARIANT, 128>(a, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace
