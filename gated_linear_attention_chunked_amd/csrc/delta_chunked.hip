@@ -21,7 +21,8 @@
 //          It forms everything that does not depend on the state (the
 //          inverses of the diagonal blocks of I + L, the off-diagonal coupling
 //          blocks, the gate prefix sums, the lower blocks of Q K^T * Gamma)
-//          and writes it to a workspace block of 12.75 KB per chunk.
+//          and writes it to a workspace block of 12.75 KB per chunk (a device
+//          buffer the library keeps per stream).
 //   scan:  one workgroup of 8 waves per (b, h, 32-wide slice of dv); rows of
 //          W are independent, so slices never communicate.  Waves are split
 //          into a carry, an output and a producer role; see the pipelined
@@ -37,7 +38,10 @@
 // The same trick feeds U and the solve's right-hand sides to the next
 // products without an LDS round trip.
 #include <array>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "chunk_common.h"
 #include "lam_internal.h"
@@ -720,18 +724,34 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
     }
 }
 
-// The stream-ordered pool keeps freed workspace for the next call instead of
-// returning it to the device at every synchronisation.
-void keep_pool_memory() {
-    static bool done[64] = {};
+// Workspace of the derived blocks, cached per (device, stream) and grown on
+// demand.  Calls on one stream run in order, so they share it; calls on
+// different streams get their own.  A stream-ordered allocator would do the
+// same without the cache, but its free and reuse make the host wait for the
+// device on every call, which leaves the device idle between calls.
+hipError_t derived_workspace(hipStream_t stream, size_t bytes, void **ptr) {
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> cache;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || done[dev]) return;
-    hipMemPool_t pool;
-    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-        uint64_t keep = UINT64_MAX;
-        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    std::pair<void *, size_t> &w = cache[{dev, stream}];
+    if (w.second < bytes) {
+        if (w.first) {
+            // the old buffer may still be read by this stream's queued work
+            e = hipStreamSynchronize(stream);
+            if (e == hipSuccess) e = hipFree(w.first);
+            w = {nullptr, 0};
+            if (e != hipSuccess) return e;
+        }
+        void *p = nullptr;
+        e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) return e;
+        w = {p, bytes};
     }
-    done[dev] = true;
+    *ptr = w.first;
+    return hipSuccess;
 }
 
 template <int VARIANT, int DK>
@@ -742,18 +762,14 @@ hipError_t launch_dk(const DeltaArgs &a, hipStream_t stream) {
     if (tasks > 0x7fffffff) return hipErrorInvalidValue;
     DerBlock *der = nullptr;
     if (tasks > 0) {
-        keep_pool_memory();
-        hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&der), static_cast<size_t>(tasks) * sizeof(DerBlock), stream);
+        void *ws = nullptr;
+        const hipError_t e = derived_workspace(stream, static_cast<size_t>(tasks) * sizeof(DerBlock), &ws);
         if (e != hipSuccess) return e;
+        der = static_cast<DerBlock *>(ws);
         delta_chunked_derive_kernel<VARIANT, DK><<<static_cast<unsigned>(tasks), NTD, 0, stream>>>(a, der);
     }
     delta_chunked_wy_kernel<VARIANT, DK><<<blocks, NT8, 0, stream>>>(a, der);
-    const hipError_t e = hipGetLastError();
-    if (der) {
-        const hipError_t f = hipFreeAsync(der, stream);
-        if (e == hipSuccess && f != hipSuccess) return f;
-    }
-    return e;
+    return hipGetLastError();
 }
 
 template <int VARIANT>

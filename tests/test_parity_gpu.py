@@ -119,6 +119,40 @@ def test_bitwise_reproducible(variant):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("variant", ["gdn", "gdn2"])
+def test_chunked_streams_and_workspace_growth(variant):
+    """The chunked delta scan keeps its derived-block workspace per stream:
+    calls queued on two streams at once, and a small call after a large one
+    on the same stream, must give the results of isolated calls."""
+    import torch
+
+    import gated_linear_attention_chunked_amd as lam
+
+    shapes = [(2, 900, 4, 128, 128), (3, 130, 2, 64, 64)]
+    ws = [_w(variant, "bf16", *sh, seed=5100 + i) for i, sh in enumerate(shapes)]
+    xs = [I.make_inputs(w) for w in ws]
+    alone = [U.run_gpu(w, x, algo="chunked") for w, x in zip(ws, xs)]
+    gs = [I.to_device(x, "bf16", "cuda") for x in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    res = []
+    for rep in range(3):
+        for g, st in zip(gs, streams):
+            with torch.cuda.stream(st):
+                res.append(lam.forward(variant, g["q"], g["k"], g["v"], g["beta"], alpha=g.get("alpha"),
+                                       erase_b=g.get("erase_b"), write_w=g.get("write_w"), algo="chunked",
+                                       stream=st))
+    torch.cuda.synchronize()
+    for i, (out, st) in enumerate(res):
+        ref = alone[i % 2]
+        assert np.array_equal(out.float().cpu().numpy().astype(np.float64), ref[0])
+        assert np.array_equal(st.cpu().numpy().astype(np.float64), ref[1])
+    # the large workload's workspace, then the small one on the same stream
+    small_again = U.run_gpu(ws[1], xs[1], algo="chunked")
+    for a, b in zip(small_again, alone[1]):
+        assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("algo", ["recurrent", "chunked"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [32, 64, 96, 128])
