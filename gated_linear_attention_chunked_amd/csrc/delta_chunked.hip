@@ -724,36 +724,6 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
     }
 }
 
-// Workspace of the derived blocks, cached per (device, stream) and grown on
-// demand.  Calls on one stream run in order, so they share it; calls on
-// different streams get their own.  A stream-ordered allocator would do the
-// same without the cache, but its free and reuse make the host wait for the
-// device on every call, which leaves the device idle between calls.
-hipError_t derived_workspace(hipStream_t stream, size_t bytes, void **ptr) {
-    static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> cache;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(mu);
-    std::pair<void *, size_t> &w = cache[{dev, stream}];
-    if (w.second < bytes) {
-        if (w.first) {
-            // the old buffer may still be read by this stream's queued work
-            e = hipStreamSynchronize(stream);
-            if (e == hipSuccess) e = hipFree(w.first);
-            w = {nullptr, 0};
-            if (e != hipSuccess) return e;
-        }
-        void *p = nullptr;
-        e = hipMalloc(&p, bytes);
-        if (e != hipSuccess) return e;
-        w = {p, bytes};
-    }
-    *ptr = w.first;
-    return hipSuccess;
-}
-
 template <int VARIANT, int DK>
 hipError_t launch_dk(const DeltaArgs &a, hipStream_t stream) {
     const int64_t nchunks = (a.T + C - 1) / C;
@@ -782,6 +752,36 @@ hipError_t launch_var(const DeltaArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Workspace of the derived blocks of the chunked schedules, cached per
+// (device, stream) and grown on demand.  Calls on one stream run in order, so they share it; calls on
+// different streams get their own.  A stream-ordered allocator would do the
+// same without the cache, but its free and reuse make the host wait for the
+// device on every call, which leaves the device idle between calls.
+hipError_t derived_workspace(hipStream_t stream, size_t bytes, void **ptr) {
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    std::pair<void *, size_t> &w = cache[{dev, stream}];
+    if (w.second < bytes) {
+        if (w.first) {
+            // the old buffer may still be read by this stream's queued work
+            e = hipStreamSynchronize(stream);
+            if (e == hipSuccess) e = hipFree(w.first);
+            w = {nullptr, 0};
+            if (e != hipSuccess) return e;
+        }
+        void *p = nullptr;
+        e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) return e;
+        w = {p, bytes};
+    }
+    *ptr = w.first;
+    return hipSuccess;
+}
 
 bool delta_chunked_supported(const DeltaArgs &a) {
     if (a.variant == kKimiDelta) return kda_chunked_supported(a);

@@ -22,16 +22,20 @@
 // C = 16 makes the Gram a single 16x16 block, so one factorisation serves the
 // whole chunk.
 //
-// Schedule: one workgroup of 8 waves per (b, h, 32-column value slice).
-//   carry  (waves 0-1, one 16-column tile each): Z = (K*Gam) S^T, the 16x16
+// Two kernels per call:
+//   derivation: one wave per (sequence, head, chunk), all chunks at once.  It
+//          forms everything that does not depend on the state: the scaled
+//          key and query tiles K*Gam, K*Gam_C/Gam, Q*Gam, the Aqk block,
+//          (I + L)^{-1} diag(beta) and Gam_C, and writes them to a workspace
+//          block per chunk.
+//   scan:  one workgroup per (b, h, value slice of 16 NVT columns):
+//   carry  (NVT waves, one 16-column tile each): Z = (K*Gam) S^T, the 16x16
 //          solve on one MFMA, U published, state update S^T <- diag(Gam_C)
 //          S^T + (K*Gam_C/Gam)^T U, bf16 copy of S published for the output.
-//   output (waves 2-3): Y^T = S (Q*Gam)^T + U^T Aqk^T, 8-byte row stores.
-//   producers (waves 4-7): producer p derives every fourth chunk (p, p+4, ...)
-//          into its own LDS slot: loads one chunk ahead in registers, the
-//          per-channel prefix sums and powers of two (lane = channel pair),
-//          the scaled key/query tiles, the Gram and Aqk blocks, the fp32
-//          inverse of I + L and D diag(beta).
+//   output (NVT waves): Y^T = S (Q*Gam)^T + U^T Aqk^T, 8-byte row stores.
+//   producers (4 waves): producer p copies every fourth chunk's block
+//          (p, p+4, ...) and the slice's value rows into its own LDS slot,
+//          loads issued four chunks ahead.
 // There is no workgroup barrier in the chunk loop: slots, U and the bf16
 // state move between roles through bounded LDS counters.
 #include <type_traits>
@@ -43,7 +47,7 @@ namespace lam {
 namespace {
 
 constexpr int C16 = 16;      // chunk length (tokens)
-constexpr int NSLOT = 4;     // one derived-chunk slot per producer
+constexpr int NSLOT = 4;     // one chunk slot per producer
 constexpr int KLTS = 20;     // column stride (floats) of the fp32 L block
 constexpr float kFastLimit = 100.f;  // largest 2^x used by the factored Gram
 
@@ -56,28 +60,35 @@ struct KdaShape {
     static constexpr int NT = 64 * NW;        // threads
 };
 
+// State-independent data of one chunk as the derivation kernel stores it:
+// token rows unpadded, fragments in the order the scan reads them.
+template <int DK>
+struct KdaBlock {
+    __bf16 kd[C16 * DK];   // k * Gam
+    __bf16 ke[C16 * DK];   // k * Gam_C / Gam
+    __bf16 qd[C16 * DK];   // q * Gam
+    bf16x4 aqk[64];        // lower((Q*Gam)(K/Gam)^T), B-operand order: lane (g, i) holds [t = i][s = 4g + r]
+    bf16x4 dt[64];         // (I + L)^{-1} diag(beta), A-operand order
+    float gc[DK];          // Gam_C per channel
+    static constexpr int kRowPieces = 3 * C16 * DK / 8;      // 16-byte pieces of kd, ke, qd
+    static constexpr int kPieces = kRowPieces + 64 + DK / 4;  // all 16-byte pieces
+};
+static_assert(sizeof(KdaBlock<64>) % 256 == 0 && sizeof(KdaBlock<128>) % 256 == 0, "blocks stay 256-byte aligned");
+
 template <int DK, int NVT>
 struct KdaLds {
     static constexpr int KS = DK + 8;
     static constexpr int VS = KdaShape<NVT>::BV + 8;
-    struct Slot {  // state-independent data of one chunk
-        alignas(16) __bf16 kd[C16 * KS];   // k * Gam
-        alignas(16) __bf16 ke[C16 * KS];   // k * Gam_C / Gam
-        alignas(16) __bf16 qd[C16 * KS];   // q * Gam
+    struct Slot {  // one chunk: its block (token rows padded to KS) and value rows
+        alignas(16) __bf16 kd[C16 * KS];
+        alignas(16) __bf16 ke[C16 * KS];
+        alignas(16) __bf16 qd[C16 * KS];
+        alignas(16) bf16x4 aqk[64];
+        alignas(16) bf16x4 dt[64];
+        alignas(16) float gc[DK];
         alignas(16) __bf16 v[C16 * VS];    // value targets of the workgroup's columns
-        alignas(16) bf16x4 aqk[64];        // lower((Q*Gam)(K/Gam)^T), B-operand order: lane (g, i) holds [t = i][s = 4g + r]
-        alignas(16) bf16x4 dt[64];         // (I + L)^{-1} diag(beta), A-operand order
-        alignas(16) float gc[DK];          // Gam_C per channel
-    };
-    struct Scratch {  // per producer
-        alignas(16) __bf16 kb[C16 * KS];   // k / Gam (factored form); column tile (exact form)
-        alignas(16) __bf16 ka[C16 * KS];   // exact form: row tiles of k and q
-        alignas(16) __bf16 qa[C16 * KS];
-        alignas(16) float lt[16 * KLTS];   // L by column
-        alignas(16) float beta[C16];
     };
     Slot slot[NSLOT];
-    Scratch scr[4];
     // A producer publishes chunk c only after every consumer has finished
     // chunk c - 4, so the carry can run at most four chunks ahead of the
     // output: four U buffers need no further check, and with five state
@@ -94,11 +105,259 @@ struct KdaLds {
     unsigned int sp[NVT], so[NVT];   // bf16 state published / read per tile
 };
 
+// ============================== derivation ==============================
+template <int DK>
+struct KdaDeriveLds {
+    static constexpr int KS = DK + 8;
+    alignas(16) __bf16 a[C16 * KS];    // k * Gam (factored form); row tiles of k (exact form)
+    alignas(16) __bf16 b[C16 * KS];    // q * Gam (factored form); row tiles of q (exact form)
+    alignas(16) __bf16 kb[C16 * KS];   // k / Gam (factored form); column tile (exact form)
+    alignas(16) float lt[16 * KLTS];   // L by column
+    alignas(16) float beta[C16];
+    alignas(16) bf16x4 dt[64];
+};
+
+// One wave per (sequence, head, chunk).  Lane owns key channels CH*lane ..
+// CH*lane + CH - 1 for all 16 tokens (one packed load per token and tensor);
+// beta of token lane (lanes 0-15).
+template <int DK>
+__global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK> *__restrict__ out) {
+    constexpr int KS = DK + 8;
+    constexpr int KSTEP = DK / 32, CH = DK / 64;
+    __shared__ KdaDeriveLds<DK> s;
+
+    const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
+    const int nchunks = (T + C16 - 1) / C16;
+    const int task = blockIdx.x;
+    const int head = task / nchunks, n = task - head * nchunks;
+    const int b = head / H, h = head % H;
+    const int lane = threadIdx.x;
+    const int lg = lane >> 4, lc = lane & 15;
+    KdaBlock<DK> &o = out[task];
+
+    const uint16_t *gq = static_cast<const uint16_t *>(a.q);
+    const uint16_t *gk = static_cast<const uint16_t *>(a.k);
+    const uint16_t *gal = static_cast<const uint16_t *>(a.alpha);
+    const uint16_t *gbe = static_cast<const uint16_t *>(a.beta);
+    using Pk = std::conditional_t<CH == 2, uint32_t, uint16_t>;
+    Pk rk[C16], rq[C16], ra[C16];
+    const int t0 = n * C16, nval = min(C16, T - t0);
+    const int64_t hdk = static_cast<int64_t>(H) * DK;
+    const int64_t r0 = ((static_cast<int64_t>(b) * T + t0) * H + h) * DK + CH * lane;
+#pragma unroll
+    for (int t = 0; t < C16; ++t) {
+        const int64_t off = r0 + min(t, nval - 1) * hdk;
+        rk[t] = *reinterpret_cast<const Pk *>(gk + off);
+        rq[t] = *reinterpret_cast<const Pk *>(gq + off);
+        ra[t] = *reinterpret_cast<const Pk *>(gal + off);
+    }
+    const uint16_t rb = gbe[(static_cast<int64_t>(b) * T + t0 + min(lane & 15, nval - 1)) * H + h];
+    // padding rows: zero key and query, decay 1
+    if (nval < C16) {
+        const Pk one = CH == 2 ? Pk(0x3f803f80u) : Pk(0x3f80u);
+#pragma unroll
+        for (int t = 0; t < C16; ++t) {
+            if (t >= nval) {
+                rk[t] = 0;
+                rq[t] = 0;
+                ra[t] = one;
+            }
+        }
+    }
+    // channel j of a packed pair, widened
+    auto chan = [](Pk x, int j) { return bf16_bits_to_f32(static_cast<uint16_t>(x >> (16 * j))); };
+    // CH consecutive bf16 of row t, channels CH*lane ..
+    auto put = [&](__bf16 *m, int stride, int t, const float (&x)[CH]) {
+        if constexpr (CH == 2) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<bf16x2 *>(m + t * stride + 2 * lane) = bf16x2{static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1])};
+        } else {
+            m[t * stride + lane] = static_cast<__bf16>(x[0]);
+        }
+    };
+    // per-channel log2 decay prefix sums over the chunk
+    float G[C16][CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < C16; ++t) {
+            const float la = fmaxf(__builtin_amdgcn_logf(chan(ra[t], j)), -200.f);
+            acc += la;
+            G[t][j] = acc;
+        }
+    }
+    float gcx[CH], emax = 0.f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        gcx[j] = G[C16 - 1][j];
+        emax = fmaxf(emax, -gcx[j]);
+    }
+    // wave max of the largest exponent 2^{-G}
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) emax = fmaxf(emax, __shfl_xor(emax, m, 64));
+    const bool fast = emax <= kFastLimit;
+    float gcp[CH];  // Gam_C per channel
+#pragma unroll
+    for (int j = 0; j < CH; ++j) gcp[j] = exp2_fast(gcx[j]);
+    // scaled tiles (the factored form's branch taken once per chunk): all
+    // three go to the block, and the factored form also keeps k * Gam,
+    // q * Gam and k / Gam in LDS for its products
+    auto tiles = [&](auto fc) {
+        constexpr bool F = decltype(fc)::value;
+#pragma unroll
+        for (int t = 0; t < C16; ++t) {
+            float kd[CH], qd[CH], ke[CH], kb[CH];
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const float kv = chan(rk[t], j), qv = chan(rq[t], j);
+                const float e1 = exp2_fast(G[t][j]);
+                kd[j] = kv * e1;
+                qd[j] = qv * e1;
+                if constexpr (F) {  // 2^{-G} is finite here: 2^{G_C - G} as a product
+                    const float eb = exp2_fast(-G[t][j]);
+                    kb[j] = kv * eb;
+                    ke[j] = kv * (gcp[j] * eb);
+                } else {
+                    kb[j] = 0.f;
+                    ke[j] = kv * exp2_fast(gcx[j] - G[t][j]);
+                }
+            }
+            put(o.kd, DK, t, kd);
+            put(o.qd, DK, t, qd);
+            put(o.ke, DK, t, ke);
+            if constexpr (F) {
+                put(s.a, KS, t, kd);
+                put(s.b, KS, t, qd);
+                put(s.kb, KS, t, kb);
+            }
+        }
+    };
+    if (fast) tiles(std::true_type{});
+    else tiles(std::false_type{});
+#pragma unroll
+    for (int j = 0; j < CH; ++j) o.gc[CH * lane + j] = gcp[j];
+    if (lane < C16) s.beta[lane] = lane < nval ? bf16_bits_to_f32(rb) : 0.f;
+    wave_lds_fence();
+    // Gram block G[t][s] (lane (g, i): t = 4g + r, s = i) and the
+    // Aqk block as (K/Gam)(Q*Gam)^T (lane (g, i): s = 4g + r, t = i)
+    f32x4 gr = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+    if (fast) {
+#pragma unroll
+        for (int p = 0; p < KSTEP; ++p) {
+            const bf16x8 kdf = row_frag2(s.a, KS, 0, 32 * p, lane);
+            const bf16x8 kbf = row_frag2(s.kb, KS, 0, 32 * p, lane);
+            const bf16x8 qdf = row_frag2(s.b, KS, 0, 32 * p, lane);
+            gr = mfma32(kdf, kbf, gr);
+            aq = mfma32(kbf, qdf, aq);
+        }
+    } else {
+        // Exact form for chunks whose decay leaves the factored range.
+        // Entry (t, s), s < t, is formed at level b = highest set bit of
+        // t ^ s: t and s then sit on either side of the reference token
+        // m = (t & ~(2b - 1)) + b - 1, and
+        //   2^{G_t - G_s} = 2^{G_t - G_m} 2^{G_m - G_s}
+        // with both factors <= 1.  Each level is one masked product over
+        // tiles whose rows are scaled against their own block's reference;
+        // entries of other levels are discarded.  The last level (b = 0)
+        // gives the diagonal of Aqk, undecayed.
+        auto level = [&](auto bi) {
+            constexpr int bl = decltype(bi)::value == 4 ? 0 : 8 >> decltype(bi)::value;
+            auto row = [&](auto tc) {
+                constexpr int t = decltype(tc)::value;
+                float ak[CH], aqv[CH], bk[CH];
+#pragma unroll
+                for (int j = 0; j < CH; ++j) {
+                    const float kv = chan(rk[t], j), qv = chan(rq[t], j);
+                    float rf = 1.f, cf = 1.f;
+                    if constexpr (bl != 0) {
+                        constexpr int m = (t & ~(2 * bl - 1)) + bl - 1;
+                        if constexpr ((t & bl) != 0) {
+                            rf = exp2_fast(G[t][j] - G[m][j]);
+                            cf = 0.f;
+                        } else {
+                            rf = 0.f;
+                            cf = exp2_fast(G[m][j] - G[t][j]);
+                        }
+                    }
+                    ak[j] = kv * rf;
+                    aqv[j] = qv * rf;
+                    bk[j] = kv * cf;
+                }
+                if constexpr (bl != 0) put(s.a, KS, t, ak);
+                put(s.b, KS, t, aqv);
+                put(s.kb, KS, t, bk);
+            };
+            static_for<C16>(row);
+            wave_lds_fence();
+            f32x4 g2 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < KSTEP; ++p) {
+                const bf16x8 kbf = row_frag2(s.kb, KS, 0, 32 * p, lane);
+                if constexpr (bl != 0) g2 = mfma32(row_frag2(s.a, KS, 0, 32 * p, lane), kbf, g2);
+                a2 = mfma32(kbf, row_frag2(s.b, KS, 0, 32 * p, lane), a2);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int x = (4 * lg + r) ^ lc;  // same for both layouts
+                if constexpr (bl != 0) {
+                    const bool at = x >= bl && x < 2 * bl;
+                    if (at && ((4 * lg + r) & bl)) gr[r] = g2[r];  // t = 4g + r, s = i
+                    if (at && (lc & bl)) aq[r] = a2[r];            // s = 4g + r, t = i
+                } else if (x == 0) {
+                    aq[r] = a2[r];
+                }
+            }
+            wave_lds_fence();  // tiles are rewritten by the next level
+            __builtin_amdgcn_sched_barrier(0);  // one level's values live at a time
+        };
+        static_for<5>(level);
+    }
+    // L = beta_t G (s < t) by column; Aqk (s <= t)
+    {
+        const float4 bt4 = *reinterpret_cast<const float4 *>(&s.beta[4 * lg]);
+        const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+        float l[4];
+        f32x4 x;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            l[r] = lc < 4 * lg + r ? bt[r] * gr[r] : 0.f;
+            x[r] = 4 * lg + r <= lc ? aq[r] : 0.f;
+        }
+        *reinterpret_cast<float4 *>(&s.lt[lc * KLTS + 4 * lg]) = make_float4(l[0], l[1], l[2], l[3]);
+        o.aqk[lane] = bf4(x);
+    }
+    wave_lds_fence();
+    // D = (I + L)^{-1}: forward substitution in fp32, lane = (column, row quad)
+    {
+        const int col = lane >> 2, q = lane & 3;
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == col) ? 1.f : 0.f;
+        auto sweep = [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const float4 l4 = *reinterpret_cast<const float4 *>(&s.lt[j * KLTS + 4 * q]);
+            const float xj = quad_bcast<j / 4>(x[j % 4]);
+            x[0] = fmaf(-l4.x, xj, x[0]);
+            x[1] = fmaf(-l4.y, xj, x[1]);
+            x[2] = fmaf(-l4.z, xj, x[2]);
+            x[3] = fmaf(-l4.w, xj, x[3]);
+        };
+        static_for<15>(sweep);
+        const float bcol = s.beta[col];
+        __bf16 *dt = reinterpret_cast<__bf16 *>(&s.dt[0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dt[((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3)] = static_cast<__bf16>(x[r] * bcol);
+    }
+    wave_lds_fence();
+    o.dt[lane] = s.dt[lane];
+}
+
 template <int DK, int NVT>
-__global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArgs a) {
+__global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArgs a, const KdaBlock<DK> *__restrict__ der) {
     constexpr int KBV = KdaShape<NVT>::BV;
     constexpr int KS = DK + 8, VS = KBV + 8;
-    constexpr int KSTEP = DK / 32, KT = DK / 16, CH = DK / 64;  // CH: key channels per producer lane
+    constexpr int KSTEP = DK / 32, KT = DK / 16;
     using Lds = KdaLds<DK, NVT>;
     __shared__ Lds s;
 
@@ -208,67 +467,51 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
         }
     } else {
         // ============================== producers ==============================
+        // Producer pw copies chunks pw, pw + 4, ...: the chunk's block, 16-byte
+        // piece p = 64i + lane per load, and the slice's value rows (KBV/8
+        // lanes per row, 8 columns each; lanes past row 15 idle).
         const int pw = wave - 2 * NVT;
-        typename Lds::Scratch &X = s.scr[pw];
         typename Lds::Slot &Sl = s.slot[pw];
-        const uint16_t *gq = static_cast<const uint16_t *>(a.q);
-        const uint16_t *gk = static_cast<const uint16_t *>(a.k);
+        using Blk = KdaBlock<DK>;
+        constexpr int NPL = (Blk::kPieces + 63) / 64;  // block pieces per lane
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 *gder = reinterpret_cast<const u32x4 *>(der + static_cast<int64_t>(head) * nchunks);
         const uint16_t *gv = static_cast<const uint16_t *>(a.v);
-        const uint16_t *gal = static_cast<const uint16_t *>(a.alpha);
-        const uint16_t *gbe = static_cast<const uint16_t *>(a.beta);
-        // Staged chunk: lane owns key channels CH*lane .. CH*lane + CH - 1
-        // (one packed load per token and tensor) for all 16 tokens; value
-        // row lane/4, columns 8 (lane % 4) ..; beta of token lane (lanes 0-15).
-        using Pk = std::conditional_t<CH == 2, uint32_t, uint16_t>;
-        Pk rk[C16], rq[C16], ra[C16];
-        // value rows: KBV/8 lanes per row, 8 columns each (lanes past row 15 idle)
         constexpr int VLPR = KBV / 8;
         const int vrow = lane / VLPR, vcol = 8 * (lane % VLPR);
+        u32x4 rd[NPL];
         uint4 rv;
-        uint16_t rb = 0;
-        int nval = 0, nnext = 0;  // tokens inside the sequence: chunk being derived, staged chunk
-        // fetch_kq: keys and queries (the bulk); fetch_rest: decays, value
-        // rows and beta.  Both clamp rows to the sequence.  A row's offset is
-        // the same for the whole wave (scalar arithmetic); only the lane's
-        // channel offset is per lane.
-        const int64_t hdk = static_cast<int64_t>(H) * DK;
-        const uint16_t *lk = gk + CH * lane, *lq = gq + CH * lane, *la = gal + CH * lane;
-        auto fetch_kq = [&](int n) {
-            const int t0 = n * C16, nn = min(C16, T - t0);
-            const int64_t r0 = tok(t0) * DK;
+        int nnext = 0;  // tokens inside the sequence of the staged chunk
+        auto fetch = [&](int n) {
+            const u32x4 *src = gder + static_cast<int64_t>(n) * (sizeof(Blk) / 16);
 #pragma unroll
-            for (int t = 0; t < C16; ++t) {
-                const int64_t o = r0 + min(t, nn - 1) * hdk;
-                rk[t] = *reinterpret_cast<const Pk *>(lk + o);
-                rq[t] = *reinterpret_cast<const Pk *>(lq + o);
-            }
-        };
-        auto fetch_rest = [&](int n) {
+            for (int i = 0; i < NPL; ++i) rd[i] = src[min(64 * i + lane, Blk::kPieces - 1)];
             const int t0 = n * C16;
             nnext = min(C16, T - t0);
-            const int64_t r0 = tok(t0) * DK;
-#pragma unroll
-            for (int t = 0; t < C16; ++t) ra[t] = *reinterpret_cast<const Pk *>(la + r0 + min(t, nnext - 1) * hdk);
             rv = *reinterpret_cast<const uint4 *>(gv + tok(t0 + min(vrow, nnext - 1)) * dv + v0 + vcol);
-            if (lane < C16) rb = gbe[tok(t0 + min(lane, nnext - 1))];
         };
-        // channel j of a packed pair, widened
-        auto chan = [](Pk x, int j) { return bf16_bits_to_f32(static_cast<uint16_t>(x >> (16 * j))); };
-        // CH consecutive bf16 of row t, channels CH*lane ..
-        auto put = [&](__bf16 *m, int t, const float (&x)[CH]) {
-            if constexpr (CH == 2) {
-                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                *reinterpret_cast<bf16x2 *>(m + t * KS + 2 * lane) = bf16x2{static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1])};
-            } else {
-                m[t * KS + lane] = static_cast<__bf16>(x[0]);
+        // LDS place of block piece p: token-row pieces go to padded rows
+        auto commit = [&](int nval) {
+            __bf16 *rows = Sl.kd;  // kd, ke, qd are consecutive C16*KS arrays
+            u32x4 *tail = reinterpret_cast<u32x4 *>(&Sl.aqk[0]);  // aqk, dt, gc are consecutive
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) {
+                const int p = 64 * i + lane;
+                if (p < Blk::kRowPieces) {
+                    constexpr int PPR = DK / 8;  // pieces per row
+                    const int r = p / PPR;       // row among the 3 * 16
+                    *reinterpret_cast<u32x4 *>(rows + r * KS + 8 * (p % PPR)) = rd[i];
+                } else if (p < Blk::kPieces) {
+                    tail[p - Blk::kRowPieces] = rd[i];
+                }
             }
+            const uint32_t m = vrow < nval ? 0xffffffffu : 0u;
+            if (vrow < C16)
+                *reinterpret_cast<uint4 *>(&Sl.v[vrow * VS + vcol]) = make_uint4(rv.x & m, rv.y & m, rv.z & m, rv.w & m);
         };
-        if (pw < nchunks) {
-            fetch_kq(pw);
-            fetch_rest(pw);
-        }
+        if (pw < nchunks) fetch(pw);
         for (int n = pw; n < nchunks; n += 4) {
-            nval = nnext;
+            const int nval = nnext;
             if (n >= 4) {  // chunk n - 4 released by every consumer wave
 #pragma unroll
                 for (int w = 0; w < NVT; ++w) {
@@ -276,195 +519,10 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
                     lds_wait(&s.cons[w], static_cast<unsigned int>(n - 3));  // output w done with it
                 }
             }
-            // padding rows: zero key and query, decay 1
-            if (nval < C16) {
-                const Pk one = CH == 2 ? Pk(0x3f803f80u) : Pk(0x3f80u);
-#pragma unroll
-                for (int t = 0; t < C16; ++t) {
-                    if (t >= nval) {
-                        rk[t] = 0;
-                        rq[t] = 0;
-                        ra[t] = one;
-                    }
-                }
-            }
-            // per-channel log2 decay prefix sums over the chunk
-            float G[C16][CH];
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                float acc = 0.f;
-#pragma unroll
-                for (int t = 0; t < C16; ++t) {
-                    const float la = fmaxf(__builtin_amdgcn_logf(chan(ra[t], j)), -200.f);
-                    acc += la;
-                    G[t][j] = acc;
-                }
-            }
-            float gcx[CH], emax = 0.f;
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                gcx[j] = G[C16 - 1][j];
-                emax = fmaxf(emax, -gcx[j]);
-            }
-            // wave max of the largest exponent 2^{-G}
-#pragma unroll
-            for (int m = 1; m < 64; m <<= 1) emax = fmaxf(emax, __shfl_xor(emax, m, 64));
-            const bool fast = emax <= kFastLimit;
-            float gcp[CH];  // Gam_C per channel
-#pragma unroll
-            for (int j = 0; j < CH; ++j) gcp[j] = exp2_fast(gcx[j]);
-            // scaled tiles (the factored form's branch taken once per chunk)
-            auto tiles = [&](auto fc) {
-                constexpr bool F = decltype(fc)::value;
-#pragma unroll
-                for (int t = 0; t < C16; ++t) {
-                    float kd[CH], qd[CH], ke[CH], kb[CH];
-#pragma unroll
-                    for (int j = 0; j < CH; ++j) {
-                        const float kv = chan(rk[t], j), qv = chan(rq[t], j);
-                        const float e1 = exp2_fast(G[t][j]);
-                        kd[j] = kv * e1;
-                        qd[j] = qv * e1;
-                        if constexpr (F) {  // 2^{-G} is finite here: 2^{G_C - G} as a product
-                            const float eb = exp2_fast(-G[t][j]);
-                            kb[j] = kv * eb;
-                            ke[j] = kv * (gcp[j] * eb);
-                        } else {
-                            kb[j] = 0.f;
-                            ke[j] = kv * exp2_fast(gcx[j] - G[t][j]);
-                        }
-                    }
-                    put(Sl.kd, t, kd);
-                    put(Sl.qd, t, qd);
-                    put(Sl.ke, t, ke);
-                    if constexpr (F) put(X.kb, t, kb);
-                }
-            };
-            if (fast) tiles(std::true_type{});
-            else tiles(std::false_type{});
-#pragma unroll
-            for (int j = 0; j < CH; ++j) Sl.gc[CH * lane + j] = gcp[j];
-            {
-                const uint32_t m = vrow < nval ? 0xffffffffu : 0u;
-                if (vrow < C16)
-                    *reinterpret_cast<uint4 *>(&Sl.v[vrow * VS + vcol]) = make_uint4(rv.x & m, rv.y & m, rv.z & m, rv.w & m);
-            }
-            if (lane < C16) X.beta[lane] = lane < nval ? bf16_bits_to_f32(rb) : 0.f;
-            wave_lds_fence();
-            // Gram block G[t][s] (lane (g, i): t = 4g + r, s = i) and the
-            // Aqk block as (K/Gam)(Q*Gam)^T (lane (g, i): s = 4g + r, t = i)
-            f32x4 gr = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-            if (fast) {
-#pragma unroll
-                for (int p = 0; p < KSTEP; ++p) {
-                    const bf16x8 kdf = row_frag2(Sl.kd, KS, 0, 32 * p, lane);
-                    const bf16x8 kbf = row_frag2(X.kb, KS, 0, 32 * p, lane);
-                    const bf16x8 qdf = row_frag2(Sl.qd, KS, 0, 32 * p, lane);
-                    gr = mfma32(kdf, kbf, gr);
-                    aq = mfma32(kbf, qdf, aq);
-                }
-            } else {
-                // Exact form for chunks whose decay leaves the factored range.
-                // Entry (t, s), s < t, is formed at level b = highest set bit
-                // of t ^ s: t and s then sit on either side of the reference
-                // token m = (t & ~(2b - 1)) + b - 1, and
-                //   2^{G_t - G_s} = 2^{G_t - G_m} 2^{G_m - G_s}
-                // with both factors <= 1.  Each level is one masked product
-                // over tiles whose rows are scaled against their own block's
-                // reference; entries of other levels are discarded.  The last
-                // level (b = 0) gives the diagonal of Aqk, undecayed.
-                auto level = [&](auto bi) {
-                    constexpr int b = decltype(bi)::value == 4 ? 0 : 8 >> decltype(bi)::value;
-                    auto row = [&](auto tc) {
-                        constexpr int t = decltype(tc)::value;
-                        float ak[CH], aqv[CH], bk[CH];
-#pragma unroll
-                        for (int j = 0; j < CH; ++j) {
-                            const float kv = chan(rk[t], j), qv = chan(rq[t], j);
-                            float rf = 1.f, cf = 1.f;
-                            if constexpr (b != 0) {
-                                constexpr int m = (t & ~(2 * b - 1)) + b - 1;
-                                if constexpr ((t & b) != 0) {
-                                    rf = exp2_fast(G[t][j] - G[m][j]);
-                                    cf = 0.f;
-                                } else {
-                                    rf = 0.f;
-                                    cf = exp2_fast(G[m][j] - G[t][j]);
-                                }
-                            }
-                            ak[j] = kv * rf;
-                            aqv[j] = qv * rf;
-                            bk[j] = kv * cf;
-                        }
-                        if constexpr (b != 0) put(X.ka, t, ak);
-                        put(X.qa, t, aqv);
-                        put(X.kb, t, bk);
-                    };
-                    static_for<C16>(row);
-                    wave_lds_fence();
-                    f32x4 g2 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int p = 0; p < KSTEP; ++p) {
-                        const bf16x8 kbf = row_frag2(X.kb, KS, 0, 32 * p, lane);
-                        if constexpr (b != 0) g2 = mfma32(row_frag2(X.ka, KS, 0, 32 * p, lane), kbf, g2);
-                        a2 = mfma32(kbf, row_frag2(X.qa, KS, 0, 32 * p, lane), a2);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int x = (4 * lg + r) ^ lc;  // same for both layouts
-                        if constexpr (b != 0) {
-                            const bool at = x >= b && x < 2 * b;
-                            if (at && ((4 * lg + r) & b)) gr[r] = g2[r];  // t = 4g + r, s = i
-                            if (at && (lc & b)) aq[r] = a2[r];            // s = 4g + r, t = i
-                        } else if (x == 0) {
-                            aq[r] = a2[r];
-                        }
-                    }
-                    wave_lds_fence();  // tiles are rewritten by the next level
-                    __builtin_amdgcn_sched_barrier(0);  // one level's values live at a time
-                };
-                static_for<5>(level);
-            }
-            // L = beta_t G (s < t) by column; Aqk (s <= t)
-            {
-                const float4 bt4 = *reinterpret_cast<const float4 *>(&X.beta[4 * lg]);
-                const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
-                float l[4];
-                f32x4 x;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    l[r] = lc < 4 * lg + r ? bt[r] * gr[r] : 0.f;
-                    x[r] = 4 * lg + r <= lc ? aq[r] : 0.f;
-                }
-                *reinterpret_cast<float4 *>(&X.lt[lc * KLTS + 4 * lg]) = make_float4(l[0], l[1], l[2], l[3]);
-                Sl.aqk[lane] = bf4(x);
-            }
-            wave_lds_fence();
-            // D = (I + L)^{-1}: forward substitution in fp32, lane = (column, row quad)
-            {
-                const int col = lane >> 2, q = lane & 3;
-                float x[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == col) ? 1.f : 0.f;
-                auto sweep = [&](auto jc) {
-                    constexpr int j = decltype(jc)::value;
-                    const float4 l4 = *reinterpret_cast<const float4 *>(&X.lt[j * KLTS + 4 * q]);
-                    const float xj = quad_bcast<j / 4>(x[j % 4]);
-                    x[0] = fmaf(-l4.x, xj, x[0]);
-                    x[1] = fmaf(-l4.y, xj, x[1]);
-                    x[2] = fmaf(-l4.z, xj, x[2]);
-                    x[3] = fmaf(-l4.w, xj, x[3]);
-                };
-                static_for<15>(sweep);
-                const float bcol = X.beta[col];
-                __bf16 *dt = reinterpret_cast<__bf16 *>(&Sl.dt[0]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dt[((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3)] = static_cast<__bf16>(x[r] * bcol);
-            }
+            commit(nval);
             lds_arrive(&s.ready[pw], lane);
             // this producer's next chunk (past the end: the last chunk again, unused)
-            fetch_kq(min(n + 4, nchunks - 1));
-            fetch_rest(min(n + 4, nchunks - 1));
+            fetch(min(n + 4, nchunks - 1));
         }
     }
 }
@@ -475,15 +533,30 @@ bool kda_chunked_supported(const DeltaArgs &a) {
     return a.variant == kKimiDelta && a.dtype == kBF16 && (a.dk == 64 || a.dk == 128) && a.dv % 16 == 0;
 }
 
+template <int DK, int NVT>
+static hipError_t launch_dk(const DeltaArgs &a, hipStream_t stream) {
+    const unsigned blocks = static_cast<unsigned>(a.B * a.H * (a.dv / KdaShape<NVT>::BV));
+    const int64_t tasks = a.B * a.H * ((a.T + C16 - 1) / C16);
+    if (tasks > 0x7fffffff) return hipErrorInvalidValue;
+    KdaBlock<DK> *der = nullptr;
+    if (tasks > 0) {
+        void *ws = nullptr;
+        const hipError_t e = derived_workspace(stream, static_cast<size_t>(tasks) * sizeof(KdaBlock<DK>), &ws);
+        if (e != hipSuccess) return e;
+        der = static_cast<KdaBlock<DK> *>(ws);
+        kda_derive_kernel<DK><<<static_cast<unsigned>(tasks), 64, 0, stream>>>(a, der);
+    }
+    kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a, der);
+    return hipGetLastError();
+}
+
 template <int NVT>
 static hipError_t launch_nvt(const DeltaArgs &a, hipStream_t stream) {
-    const unsigned blocks = static_cast<unsigned>(a.B * a.H * (a.dv / KdaShape<NVT>::BV));
     switch (a.dk) {
-        case 64: kda_chunked_kernel<64, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a); break;
-        case 128: kda_chunked_kernel<128, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a); break;
+        case 64: return launch_dk<64, NVT>(a, stream);
+        case 128: return launch_dk<128, NVT>(a, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 // Two value tiles per workgroup share the producers' work; with fewer than

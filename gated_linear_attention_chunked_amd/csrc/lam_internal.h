@@ -45,6 +45,11 @@ hipError_t launch_delta_chunked(const DeltaArgs &a, hipStream_t stream);
 bool vla_chunked_supported(const VlaArgs &a);
 hipError_t launch_vla_chunked(const VlaArgs &a, hipStream_t stream);
 
+// Device workspace of `bytes` for the chunked schedules' derived blocks, kept
+// per (device, stream) and grown on demand.  Work queued on `stream` may use
+// it until the next call on that stream that asks for more.
+hipError_t derived_workspace(hipStream_t stream, size_t bytes, void **ptr);
+
 // Kimi Delta (per-channel decay) has its own chunked kernel.
 bool kda_chunked_supported(const DeltaArgs &a);
 hipError_t launch_kda_chunked(const DeltaArgs &a, hipStream_t stream);
