@@ -398,39 +398,59 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) s.sh[0][vt][kt][lane] = bf4(St[kt]);
             lds_arrive(&s.sp[vt], lane);
-#pragma unroll 1
-            for (int c = 0; c < nchunks; ++c) {
+            // Operands of a chunk that do not depend on the state, read one
+            // chunk ahead: the next slot's reads go out while this chunk's
+            // state-update products run.
+            bf16x8 kf[KSTEP];
+            bf16x4 vb, dtf, kef[KT];
+            float4 gcv[KT];
+            auto load_ops = [&](int c) {
                 const typename Lds::Slot &Sl = s.slot[c & 3];
                 lds_wait(&s.ready[c & 3], static_cast<unsigned int>(c / 4 + 1));
-                bf16x8 kf[KSTEP];
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p) kf[p] = row_frag2(Sl.kd, KS, 0, 32 * p, lane);
-                const bf16x4 vb = col_gather4(Sl.v, VS, 0, 16 * vt, lane);
-                const bf16x4 dtf = Sl.dt[lane];
-                // Z = (K*Gam) S^T: lane (g, i) holds rows t = 4g + r, column i
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                vb = col_gather4(Sl.v, VS, 0, 16 * vt, lane);
+                dtf = Sl.dt[lane];
 #pragma unroll
-                for (int p = 0; p < KSTEP; ++p) z = mfma32(kf[p], cat8(bf4(St[2 * p]), bf4(St[2 * p + 1])), z);
-                const f32x4 rhs = __builtin_convertvector(vb, f32x4) - z;
+                for (int kt = 0; kt < KT; ++kt) {
+                    kef[kt] = col_gather4(Sl.ke, KS, 0, 16 * kt, lane);
+                    gcv[kt] = *reinterpret_cast<const float4 *>(&Sl.gc[16 * kt + 4 * lg]);
+                }
+            };
+            // bf16 copy of the state: B operand of the next Z and the output's copy
+            bf16x4 Sb[KT];
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) Sb[kt] = bf4(St[kt]);
+            if (nchunks > 0) load_ops(0);
+#pragma unroll 1
+            for (int c = 0; c < nchunks; ++c) {
+                // Z = (K*Gam) S^T: lane (g, i) holds rows t = 4g + r, column i;
+                // two independent accumulation chains
+                f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < KSTEP; p += 2) {
+                    z0 = mfma32(kf[p], cat8(Sb[2 * p], Sb[2 * p + 1]), z0);
+                    z1 = mfma32(kf[p + 1], cat8(Sb[2 * p + 2], Sb[2 * p + 3]), z1);
+                }
+                const f32x4 rhs = __builtin_convertvector(vb, f32x4) - (z0 + z1);
                 const bf16x4 ub = bf4(mfma16(dtf, bf4(rhs), f32x4{0.f, 0.f, 0.f, 0.f}));
                 s.uh[c & 3][vt][lane] = ub;
                 lds_arrive(&s.uc[vt], lane);
                 // S^T <- diag(Gam_C) S^T + (K*Gam_C/Gam)^T U
-                bf16x4 kef[KT];
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt) kef[kt] = col_gather4(Sl.ke, KS, 0, 16 * kt, lane);
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) {
-                    const float4 g4 = *reinterpret_cast<const float4 *>(&Sl.gc[16 * kt + 4 * lg]);
-                    St[kt] = St[kt] * f32x4{g4.x, g4.y, g4.z, g4.w};
+                    St[kt] = St[kt] * f32x4{gcv[kt].x, gcv[kt].y, gcv[kt].z, gcv[kt].w};
                     St[kt] = mfma16(kef[kt], ub, St[kt]);
                 }
+                if (c + 1 < nchunks) load_ops(c + 1);
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) Sb[kt] = bf4(St[kt]);
                 // S(c + 1 - NSB) has been read from this buffer
                 if constexpr (Lds::kStateGuard) lds_wait(&s.so[vt], static_cast<unsigned int>(c + 2 - Lds::NSB));
                 {
                     auto &dst = s.sh[(c + 1) % Lds::NSB][vt];
 #pragma unroll
-                    for (int kt = 0; kt < KT; ++kt) dst[kt][lane] = bf4(St[kt]);
+                    for (int kt = 0; kt < KT; ++kt) dst[kt][lane] = Sb[kt];
                 }
                 lds_arrive(&s.sp[vt], lane);  // also releases slot c: its last read precedes this
             }
@@ -445,20 +465,28 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
             for (int c = 0; c < nchunks; ++c) {
                 const typename Lds::Slot &Sl = s.slot[c & 3];
                 lds_wait(&s.ready[c & 3], static_cast<unsigned int>(c / 4 + 1));
+                // state-independent operands first
+                bf16x8 qf[KSTEP];
+#pragma unroll
+                for (int p = 0; p < KSTEP; ++p) qf[p] = row_frag2(Sl.qd, KS, 0, 32 * p, lane);
+                const bf16x4 aq = Sl.aqk[lane];
                 lds_wait(&s.sp[vt], static_cast<unsigned int>(c + 1));
                 bf16x8 bS[KSTEP];
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p)
                     bS[p] = cat8(s.sh[c % Lds::NSB][vt][2 * p][lane], s.sh[c % Lds::NSB][vt][2 * p + 1][lane]);
                 if constexpr (Lds::kStateGuard) lds_arrive(&s.so[vt], lane);
-                // Y^T = S (Q*Gam)^T + U^T Aqk^T: lane (g, i) holds columns 4g + r of token i
-                f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                // Y^T = S (Q*Gam)^T + U^T Aqk^T: lane (g, i) holds columns 4g + r of
+                // token i; two independent accumulation chains
+                f32x4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int p = 0; p < KSTEP; ++p) y = mfma32(bS[p], row_frag2(Sl.qd, KS, 0, 32 * p, lane), y);
-                const bf16x4 aq = Sl.aqk[lane];
+                for (int p = 0; p < KSTEP; p += 2) {
+                    y0 = mfma32(bS[p], qf[p], y0);
+                    y1 = mfma32(bS[p + 1], qf[p + 1], y1);
+                }
                 lds_wait(&s.uc[vt], static_cast<unsigned int>(c + 1));
                 const bf16x4 ub = s.uh[c & 3][vt][lane];
-                y = mfma16(ub, aq, y);
+                const f32x4 y = mfma16(ub, aq, y0 + y1);
                 const int t = c * C16 + lc;
                 if (t < T)
                     *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(a.out) + tok(t) * dv + v0 + 16 * vt + 4 * lg) = bf4(y);
