@@ -30,9 +30,12 @@
 //          block per chunk.
 //   scan:  one workgroup per (b, h, value slice of 16 NVT columns):
 //   carry  (NVT waves, one 16-column tile each): Z = (K*Gam) S^T, the 16x16
-//          solve on one MFMA, U published, state update S^T <- diag(Gam_C)
-//          S^T + (K*Gam_C/Gam)^T U, bf16 copy of S published for the output.
-//   output (NVT waves): Y^T = S (Q*Gam)^T + U^T Aqk^T, 8-byte row stores.
+//          solve on one MFMA, state update S^T <- diag(Gam_C) S^T +
+//          (K*Gam_C/Gam)^T U, bf16 copy of S published for the output.
+//   output (NVT waves): from the published bf16 S it forms U exactly as the
+//          carry does (same operands, same order), then Y^T = S (Q*Gam)^T +
+//          U^T Aqk^T, 8-byte row stores.  Recomputing U costs the output five
+//          products and takes a hand-off off the carry's chain.
 //   producers (4 waves): producer p copies every fourth chunk's block
 //          (p, p+4, ...) and the slice's value rows into its own LDS slot,
 //          loads issued four chunks ahead.
@@ -91,17 +94,13 @@ struct KdaLds {
     Slot slot[NSLOT];
     // A producer publishes chunk c only after every consumer has finished
     // chunk c - 4, so the carry can run at most four chunks ahead of the
-    // output: four U buffers need no further check, and with five state
-    // buffers neither does the bf16 state (two when LDS is short, guarded by
-    // the output's read count).
-    static constexpr int NUB = 4;
+    // output: with five state buffers the bf16 state needs no further check
+    // (two when LDS is short, guarded by the output's read count).
     static constexpr int NSB = NVT == 1 ? 5 : 2;
     static constexpr bool kStateGuard = NSB < 5;
-    alignas(16) bf16x4 uh[NUB][NVT][64];           // U per chunk and tile
     alignas(16) bf16x4 sh[NSB][NVT][DK / 16][64];  // bf16 state per chunk and tile
     unsigned int ready[NSLOT];   // chunks published per slot
     unsigned int cons[NVT];      // chunks finished per output wave
-    unsigned int uc[NVT];        // U published per tile
     unsigned int sp[NVT], so[NVT];   // bf16 state published / read per tile
 };
 
@@ -374,7 +373,7 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
 
     if (tid == 0) {
         for (int i = 0; i < NSLOT; ++i) s.ready[i] = 0u;
-        for (int i = 0; i < NVT; ++i) s.cons[i] = s.uc[i] = s.sp[i] = s.so[i] = 0u;
+        for (int i = 0; i < NVT; ++i) s.cons[i] = s.sp[i] = s.so[i] = 0u;
     }
     __syncthreads();
 
@@ -434,8 +433,6 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
                 }
                 const f32x4 rhs = __builtin_convertvector(vb, f32x4) - (z0 + z1);
                 const bf16x4 ub = bf4(mfma16(dtf, bf4(rhs), f32x4{0.f, 0.f, 0.f, 0.f}));
-                s.uh[c & 3][vt][lane] = ub;
-                lds_arrive(&s.uc[vt], lane);
                 // S^T <- diag(Gam_C) S^T + (K*Gam_C/Gam)^T U
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) {
@@ -466,10 +463,15 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
                 const typename Lds::Slot &Sl = s.slot[c & 3];
                 lds_wait(&s.ready[c & 3], static_cast<unsigned int>(c / 4 + 1));
                 // state-independent operands first
-                bf16x8 qf[KSTEP];
+                bf16x8 qf[KSTEP], kf[KSTEP];
 #pragma unroll
-                for (int p = 0; p < KSTEP; ++p) qf[p] = row_frag2(Sl.qd, KS, 0, 32 * p, lane);
+                for (int p = 0; p < KSTEP; ++p) {
+                    qf[p] = row_frag2(Sl.qd, KS, 0, 32 * p, lane);
+                    kf[p] = row_frag2(Sl.kd, KS, 0, 32 * p, lane);
+                }
                 const bf16x4 aq = Sl.aqk[lane];
+                const bf16x4 vb = col_gather4(Sl.v, VS, 0, 16 * vt, lane);
+                const bf16x4 dtf = Sl.dt[lane];
                 lds_wait(&s.sp[vt], static_cast<unsigned int>(c + 1));
                 bf16x8 bS[KSTEP];
 #pragma unroll
@@ -479,13 +481,17 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
                 // Y^T = S (Q*Gam)^T + U^T Aqk^T: lane (g, i) holds columns 4g + r of
                 // token i; two independent accumulation chains
                 f32x4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
+                f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int p = 0; p < KSTEP; p += 2) {
+                    z0 = mfma32(kf[p], bS[p], z0);
+                    z1 = mfma32(kf[p + 1], bS[p + 1], z1);
                     y0 = mfma32(bS[p], qf[p], y0);
                     y1 = mfma32(bS[p + 1], qf[p + 1], y1);
                 }
-                lds_wait(&s.uc[vt], static_cast<unsigned int>(c + 1));
-                const bf16x4 ub = s.uh[c & 3][vt][lane];
+                // U exactly as the carry forms it, from the same bf16 state
+                const f32x4 rhs = __builtin_convertvector(vb, f32x4) - (z0 + z1);
+                const bf16x4 ub = bf4(mfma16(dtf, bf4(rhs), f32x4{0.f, 0.f, 0.f, 0.f}));
                 const f32x4 y = mfma16(ub, aq, y0 + y1);
                 const int t = c * C16 + lc;
                 if (t < T)
