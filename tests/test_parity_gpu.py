@@ -119,6 +119,22 @@ def test_bitwise_reproducible(variant):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("variant,T,dk", [("gdn", 1024, 128), ("gdn", 1093, 64), ("deltanet", 1100, 128),
+                                          ("gdn2", 1030, 128), ("gdn", 2047, 128)])
+def test_chunked_long_sequences(variant, T, dk):
+    """Sixteen chunks and more, even and odd chunk counts, a ragged tail and
+    a carried-in state; two runs agree bit for bit."""
+    w = _w(variant, "bf16", 1, T, 2, dk, 64, seed=7700 + T)
+    x = I.make_inputs(w)
+    s0 = (np.random.default_rng(T).standard_normal((1, 2, 64, dk)) * 0.2).astype(np.float64)
+    got = U.run_gpu(w, x, algo="chunked", state_in=s0)
+    again = U.run_gpu(w, x, algo="chunked", state_in=s0)
+    for a_, b_ in zip(got, again):
+        assert np.array_equal(a_, b_)
+    ref = U.run_oracle(w, x, state_in=s0)
+    U.check(w, got, ref, label=w.name)
+
+
 @pytest.mark.parametrize("variant", ["gdn", "gdn2"])
 def test_chunked_streams_and_workspace_growth(variant):
     """The chunked delta scan keeps its derived-block workspace per stream:
