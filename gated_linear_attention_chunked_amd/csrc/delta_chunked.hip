@@ -20,15 +20,17 @@
 //   derivation: one workgroup per (sequence, head, chunk), all chunks at once.
 //          It forms everything that does not depend on the state (the
 //          inverses of the diagonal blocks of I + L, the off-diagonal coupling
-//          blocks, the gate prefix sums, the lower blocks of Q K^T * Gamma)
-//          and writes it to a workspace block of 12.75 KB per chunk (a device
-//          buffer the library keeps per stream).
+//          blocks and the gate prefix sums) from the keys, decays and betas
+//          alone, and writes it to a workspace block of 7.75 KB per chunk (a
+//          device buffer the library keeps per stream).
 //   scan:  one workgroup of 8 waves per (b, h, 32-wide slice of dv); rows of
 //          W are independent, so slices never communicate.  Waves are split
 //          into a carry, an output and a producer role; see the pipelined
 //          schedule below.  The four slices of a head read the same workspace
-//          blocks, so the derivation is done once per head instead of once
-//          per slice.
+//          blocks, so the solve's derivation is done once per head instead of
+//          once per slice; the output waves form lower(Q K^T * Gamma) from
+//          the staged query and key rows, which spares the derivation a read
+//          of the queries.
 // The state slice S^T (dk x 16 per carry wave) lives in MFMA accumulator
 // layout for the whole scan.  An accumulator tile holds 4 consecutive rows per
 // lane, while a B operand wants 8 consecutive reduction indices; since a
@@ -57,15 +59,17 @@ constexpr int BV = 32;   // dv columns per workgroup
 // G~_ij = Gamma * (E_i K_j^T) and Z = E S^T, block row i of the solve is
 //     U_i = D_i diag(beta)_i Z'_i - D_i diag(beta gamma)_i Z_i + sum_{j<i} M_ij U_j,
 //     M_ij = -D_i diag(beta)_i G~_ij                (Z' = the targets V)
-// so everything but Z is state-independent: the derivation kernel forms it,
-// together with the output's intra-chunk matrix Aqk = lower(Q K^T * Gamma).
+// so everything but Z is state-independent: the derivation kernel forms it.
+// The output's intra-chunk matrix Aqk = lower(Q K^T * Gamma) is formed by
+// the scan's output waves from the query and key rows they already hold.
 //
 // Pipelined scan: 8 waves per workgroup, two per SIMD, in three roles.
 //   carry  (waves 0-1, one 16-column tile each): Z = E S^T on MFMA, the
 //          block solve above on 16x16x16 MFMA (a four-link chain), publish U,
 //          then the state update accumulated in registers.
-//   output (waves 2-3, same tiles): Q S^T from the carry's bf16 state, then
-//          Y = diag(gamma) Q S^T + Aqk U once U is published; stores y.
+//   output (waves 2-3, same tiles): Q S^T from the carry's bf16 state and
+//          Aqk from the staged rows, then Y = diag(gamma) Q S^T + Aqk U once
+//          U is published; stores y.
 //   producers (waves 4-7): stage chunk c+1 into LDS, its token rows and its
 //          derived block (loads issued two chunks ahead).
 // All eight waves meet at one LDS barrier per chunk; the hand-offs inside a
@@ -88,7 +92,6 @@ struct DerBlock {
     float gam[C];              // gamma_t
     float sc[C];               // gamma_C / gamma_t
     float g[C];                // log2 gamma_t
-    bf16x4 aqk[NQB][64];       // lower(Q K^T * Gamma) blocks, A-operand order of the output's product
 };
 static_assert(sizeof(DerBlock) % 256 == 0, "workspace blocks stay 256-byte aligned");
 constexpr int kDerPieces = static_cast<int>(sizeof(DerBlock) / 16);  // 16-byte pieces
@@ -110,6 +113,9 @@ struct WyLds {
     alignas(16) bf16x4 sh[2][DK / 16][64];     // bf16 state fragments per tile
     unsigned int ucount[2];                    // U publications per tile
     unsigned int scount[2];                    // state fragments consumed per tile
+    // output wave <-> output wave: halves of lower(Q K^T * Gamma)
+    alignas(16) bf16x4 aqx[2][NQB][64];
+    unsigned int acount;                       // halves published
 };
 
 // rows past the end become zeros (a bitwise mask keeps the registers out of
@@ -198,8 +204,6 @@ struct DeriveLds {
 // One workgroup of four waves per (sequence, head, chunk); wave i stages key
 // rows [16i, 16i + 16) and then owns block row i of L: its E K^T tiles, the
 // inverse of its diagonal block (fp32 forward substitution) and its M_ij.
-// It also forms block row i of Aqk from its own query rows, which it reads
-// from global memory straight into fragments.
 template <int VARIANT, int DK>
 __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, DerBlock *__restrict__ out) {
     constexpr bool kDecay = VARIANT != kDeltaNet;
@@ -232,24 +236,6 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
         const uint32_t o = static_cast<uint32_t>(min(krow + RPI * i, last)) * hdk + (lane % PPR) * 8;
         kr[i] = *reinterpret_cast<const uint4 *>(k0 + o);
         if constexpr (kGates2) br[i] = *reinterpret_cast<const uint4 *>(b0 + o);
-    }
-    // query fragments of block row w: lane (lg, lc) holds row 16w + lc,
-    // columns 32p + 4lg .. +3 and 32p + 16 + 4lg .. +3 (zero past the end)
-    bf16x4 qlo[KSTEP], qhi[KSTEP];
-    {
-        const int qr = 16 * w + lc;
-        const uint16_t *qp = static_cast<const uint16_t *>(a.q) + base * DK +
-                             static_cast<uint32_t>(min(qr, last)) * hdk + 4 * lg;
-        const bf16x4 zq = {};
-#pragma unroll
-        for (int p = 0; p < KSTEP; ++p) {
-            qlo[p] = *reinterpret_cast<const bf16x4 *>(qp + 32 * p);
-            qhi[p] = *reinterpret_cast<const bf16x4 *>(qp + 32 * p + 16);
-        }
-        if (qr > last) {
-#pragma unroll
-            for (int p = 0; p < KSTEP; ++p) qlo[p] = qhi[p] = zq;
-        }
     }
     // decay (wave 0) or beta (wave 1) of row `lane`
     uint16_t rs = 0;
@@ -392,34 +378,6 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
     else if (w == 2) work(ic<2>{});
     else work(ic<3>{});
 
-    // ---- Aqk tiles (w, j), j <= w: lane (lg, lc) holds Aqk[t = 16w + lc][s = 16j + 4lg + r]
-    {
-        f32x4 acc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < KSTEP; ++p) {
-            const bf16x8 qf = cat8(qlo[p], qhi[p]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (j <= w) acc[j] = mfma32(row_frag2(s.k, KS, 16 * j, 32 * p, lane), qf, acc[j]);
-        }
-        const float gt = s.g[16 * w + lc];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j > w) continue;
-            const float4 gs4 = *reinterpret_cast<const float4 *>(&s.g[16 * j + 4 * lg]);
-            const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
-            f32x4 x;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // exponent clamped at 0 so masked entries stay finite
-                const float v = kDecay ? acc[j][r] * exp2_fast(fminf(gt - gs[r], 0.f)) : acc[j][r];
-                x[r] = (j < w || 4 * lg + r <= lc) ? v : 0.f;
-            }
-            D.aqk[tri_block(w, j)][lane] = bf4(x);
-        }
-    }
     __syncthreads();
 
     // ---- the block, 16 bytes per thread and pass
@@ -454,6 +412,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
     if (tid == 0) {
         s.ucount[0] = s.ucount[1] = 0u;
         s.scount[0] = s.scount[1] = 0u;
+        s.acount = 0u;
     }
     __syncthreads();  // counters visible before any role starts
 
@@ -545,21 +504,74 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(s.sh[vt][2 * p][lane], s.sh[vt][2 * p + 1][lane]);
                 lds_arrive(&s.scount[vt], lane);  // the carry may overwrite sh from here on
-                // Q S^T, four row tiles
+                // Q S^T (four row tiles), and the lower blocks (i, j <= i) of
+                // K Q^T from the same query fragments.  The two output waves
+                // split those blocks by key block j (j in {0, 3} and
+                // j in {1, 2}, five blocks each) and swap halves through LDS.
+                // Block (i, j) comes out with lane (lg, lc) holding
+                // [s = 16j + 4lg + r][t = 16i + lc], the B-operand order of
+                // the product with U^T below.
                 f32x4 xq[4];
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) xq[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < KSTEP; ++p) {
-                    bf16x8 qf[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) qf[i] = row_frag2(R.q, KS, 16 * i, 32 * p, lane);
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) xq[ti] = mfma32(bS[p], qf[ti], xq[ti]);
-                }
                 bf16x4 aq[NQB];
+                auto own_half = [&](auto half) {
+                    constexpr int J0 = decltype(half)::value ? 1 : 0, J1 = decltype(half)::value ? 2 : 3;
+                    auto mine = [](int j) { return j == J0 || j == J1; };
+                    f32x4 ka[NQB];
 #pragma unroll
-                for (int i = 0; i < NQB; ++i) aq[i] = D.aqk[i][lane];
+                    for (int ti = 0; ti < 4; ++ti) xq[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < NQB; ++i) ka[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int p = 0; p < KSTEP; ++p) {
+                        bf16x8 qf[4], kq[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            qf[i] = row_frag2(R.q, KS, 16 * i, 32 * p, lane);
+                            if (mine(i)) kq[i] = row_frag2(R.k, KS, 16 * i, 32 * p, lane);
+                        }
+#pragma unroll
+                        for (int ti = 0; ti < 4; ++ti) xq[ti] = mfma32(bS[p], qf[ti], xq[ti]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j <= i; ++j)
+                                if (mine(j)) ka[tri_block(i, j)] = mfma32(kq[j], qf[i], ka[tri_block(i, j)]);
+                    }
+                    // Aqk = lower(Q K^T * Gamma): entry (t, s) scaled by
+                    // 2^(g_t - g_s), exponent clamped at 0 so masked entries
+                    // stay finite, and zero above the diagonal
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float gt = kDecay ? D.g[16 * i + lc] : 0.f;
+#pragma unroll
+                        for (int j = 0; j <= i; ++j) {
+                            if (!mine(j)) continue;
+                            float gs[4] = {0.f, 0.f, 0.f, 0.f};
+                            if constexpr (kDecay) {
+                                const float4 gs4 = *reinterpret_cast<const float4 *>(&D.g[16 * j + 4 * lg]);
+                                gs[0] = gs4.x, gs[1] = gs4.y, gs[2] = gs4.z, gs[3] = gs4.w;
+                            }
+                            f32x4 x;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float v = kDecay ? ka[tri_block(i, j)][r] * exp2_fast(fminf(gt - gs[r], 0.f))
+                                                       : ka[tri_block(i, j)][r];
+                                x[r] = (j < i || 4 * lg + r <= lc) ? v : 0.f;
+                            }
+                            aq[tri_block(i, j)] = bf4(x);
+                            s.aqx[P][tri_block(i, j)][lane] = aq[tri_block(i, j)];
+                        }
+                    }
+                    lds_arrive(&s.acount, lane);
+                    lds_wait(&s.acount, static_cast<unsigned int>(2 * (c + 1)));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j <= i; ++j)
+                            if (!mine(j)) aq[tri_block(i, j)] = s.aqx[P][tri_block(i, j)][lane];
+                };
+                if (vt == 0) own_half(ic<0>{});
+                else own_half(ic<1>{});
                 lds_wait(&s.ucount[vt], static_cast<unsigned int>(c + 1));
                 bf16x4 ub[4];
 #pragma unroll
