@@ -20,25 +20,38 @@
 // further (alpha near zero somewhere) takes an exact path instead: each entry
 // is summed channel by channel with 2^{G_tc - G_sc} <= 1 evaluated directly.
 // C = 16 makes the Gram a single 16x16 block, so one factorisation serves the
-// whole chunk.
+// whole sub-chunk.
+//
+// The scan steps over pairs of 16-token sub-chunks (32 tokens).  Both
+// sub-chunks act on the state at the pair start: the odd one's K * Gam and
+// Q * Gam carry the even one's decay, the even one's K * Gam_C / Gam the odd
+// one's, and the coupling between them is a 16x16 block per product,
+//   G_10 = (K_1 * Gam_1)(K_0 * Gam_C0 / Gam_0)^T,  Aqk_10 = (Q_1 * Gam_1)(K_0 * Gam_C0 / Gam_0)^T,
+// whose factors split at the last even token and are both at most 1, so
+// they need no exact form.  Then U_0 = T_00 (V_0 - Z_0),
+// U_1 = T_11 (V_1 - Z_1) + M_10 U_0 with M_10 = -T_11 G_10, and one 32-token
+// state update: one more dependent product than a 16-token step, for half
+// as many steps.
 //
 // Two kernels per call:
-//   derivation: one wave per (sequence, head, chunk), all chunks at once.  It
+//   derivation: one wave per (sequence, head, sub-chunk), all sub-chunks at
+//          once (a wholly padded odd sub-chunk completes the last pair).  It
 //          forms everything that does not depend on the state: the scaled
-//          key and query tiles K*Gam, K*Gam_C/Gam, Q*Gam, the Aqk block,
-//          (I + L)^{-1} diag(beta) and Gam_C, and writes them to a workspace
-//          block per chunk.
+//          key and query tiles, the Aqk block, (I + L)^{-1} diag(beta), the
+//          pair's Gam_C and (odd sub-chunks) M_10 and Aqk_10, and writes them
+//          to a workspace block per sub-chunk.
 //   scan:  one workgroup per (b, h, value slice of 16 NVT columns):
-//   carry  (NVT waves, one 16-column tile each): Z = (K*Gam) S^T, the 16x16
-//          solve on one MFMA, state update S^T <- diag(Gam_C) S^T +
-//          (K*Gam_C/Gam)^T U, bf16 copy of S published for the output.
+//   carry  (NVT waves, one 16-column tile each): Z = (K*Gam) S^T for both
+//          sub-chunks, the two 16x16 solves and the coupling on three MFMA,
+//          state update S^T <- diag(Gam_C) S^T + (K*Gam_C/Gam)^T U over the
+//          32 tokens, bf16 copy of S published for the output.
 //   output (NVT waves): from the published bf16 S it forms U exactly as the
 //          carry does (same operands, same order), then Y^T = S (Q*Gam)^T +
-//          U^T Aqk^T, 8-byte row stores.  Recomputing U costs the output five
-//          products and takes a hand-off off the carry's chain.
-//   producers (4 waves): producer p copies every fourth chunk's block
+//          U^T Aqk^T, 8-byte row stores.  Recomputing U costs the output a
+//          few products and takes a hand-off off the carry's chain.
+//   producers (4 waves): producer p copies every fourth pair's two blocks
 //          (p, p+4, ...) and the slice's value rows into its own LDS slot,
-//          loads issued four chunks ahead.
+//          loads issued four pairs ahead.
 // There is no workgroup barrier in the chunk loop: slots, U and the bf16
 // state move between roles through bounded LDS counters.
 #include <type_traits>
@@ -72,9 +85,11 @@ struct KdaBlock {
     __bf16 qd[C16 * DK];   // q * Gam
     bf16x4 aqk[64];        // lower((Q*Gam)(K/Gam)^T), B-operand order: lane (g, i) holds [t = i][s = 4g + r]
     bf16x4 dt[64];         // (I + L)^{-1} diag(beta), A-operand order
-    float gc[DK];          // Gam_C per channel
-    static constexpr int kRowPieces = 3 * C16 * DK / 8;      // 16-byte pieces of kd, ke, qd
-    static constexpr int kPieces = kRowPieces + 64 + DK / 4;  // all 16-byte pieces
+    float gc[DK];          // even sub-chunk: Gam_C of the pair, per channel
+    bf16x4 mx[64];         // odd sub-chunk: M_10 = -(I + L_11)^{-1} diag(beta_1) G_10, A-operand order
+    bf16x4 ax[64];         // odd sub-chunk: cross block of Aqk, B-operand order: lane (g, i) holds [t = i][s = 4g + r]
+    static constexpr int kRowPieces = 3 * C16 * DK / 8;            // 16-byte pieces of kd, ke, qd
+    static constexpr int kPieces = kRowPieces + 64 + DK / 4 + 64;  // all 16-byte pieces
 };
 static_assert(sizeof(KdaBlock<64>) % 256 == 0 && sizeof(KdaBlock<128>) % 256 == 0, "blocks stay 256-byte aligned");
 
@@ -82,14 +97,16 @@ template <int DK, int NVT>
 struct KdaLds {
     static constexpr int KS = DK + 8;
     static constexpr int VS = KdaShape<NVT>::BV + 8;
-    struct Slot {  // one chunk: its block (token rows padded to KS) and value rows
-        alignas(16) __bf16 kd[C16 * KS];
-        alignas(16) __bf16 ke[C16 * KS];
-        alignas(16) __bf16 qd[C16 * KS];
-        alignas(16) bf16x4 aqk[64];
-        alignas(16) bf16x4 dt[64];
-        alignas(16) float gc[DK];
-        alignas(16) __bf16 v[C16 * VS];    // value targets of the workgroup's columns
+    struct Slot {  // one pair of sub-chunks: their blocks (token rows padded to KS) and value rows
+        alignas(16) __bf16 kd[2 * C16 * KS];   // rows 0-15 even sub-chunk, 16-31 odd
+        alignas(16) __bf16 ke[2 * C16 * KS];
+        alignas(16) __bf16 qd[2 * C16 * KS];
+        alignas(16) bf16x4 aqk[2][64];
+        alignas(16) bf16x4 dt[2][64];
+        alignas(16) float gc[DK];              // Gam_C of the pair
+        alignas(16) bf16x4 mx[64];
+        alignas(16) bf16x4 ax[64];
+        alignas(16) __bf16 v[2 * C16 * VS];    // value targets of the workgroup's columns
     };
     Slot slot[NSLOT];
     // A producer publishes chunk c only after every consumer has finished
@@ -111,6 +128,7 @@ struct KdaDeriveLds {
     alignas(16) __bf16 a[C16 * KS];    // k * Gam (factored form); row tiles of k (exact form)
     alignas(16) __bf16 b[C16 * KS];    // q * Gam (factored form); row tiles of q (exact form)
     alignas(16) __bf16 kb[C16 * KS];   // k / Gam (factored form); column tile (exact form)
+    alignas(16) __bf16 k0[C16 * KS];   // odd sub-chunk: the even one's k * Gam_C / Gam (cross blocks)
     alignas(16) float lt[16 * KLTS];   // L by column
     alignas(16) float beta[C16];
     alignas(16) bf16x4 dt[64];
@@ -126,9 +144,10 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
     __shared__ KdaDeriveLds<DK> s;
 
     const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
-    const int nchunks = (T + C16 - 1) / C16;
+    const int nsub = 2 * ((T + 2 * C16 - 1) / (2 * C16));  // sub-chunks per head, pairs complete
     const int task = blockIdx.x;
-    const int head = task / nchunks, n = task - head * nchunks;
+    const int head = task / nsub, n = task - head * nsub;
+    const bool odd = (n & 1) != 0;
     const int b = head / H, h = head % H;
     const int lane = threadIdx.x;
     const int lg = lane >> 4, lc = lane & 15;
@@ -139,20 +158,26 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
     const uint16_t *gal = static_cast<const uint16_t *>(a.alpha);
     const uint16_t *gbe = static_cast<const uint16_t *>(a.beta);
     using Pk = std::conditional_t<CH == 2, uint32_t, uint16_t>;
-    Pk rk[C16], rq[C16], ra[C16];
-    const int t0 = n * C16, nval = min(C16, T - t0);
-    const int64_t hdk = static_cast<int64_t>(H) * DK;
-    const int64_t r0 = ((static_cast<int64_t>(b) * T + t0) * H + h) * DK + CH * lane;
+    // this sub-chunk's rows, and the decays (odd: also the keys) of the other
+    // sub-chunk of its pair; rows are read clamped into the sequence (an odd
+    // sub-chunk may lie wholly past its end) and padded below
+    Pk rk[C16], rq[C16], ra[C16], rap[C16], rkp[C16];
+    const int t0 = n * C16, nval = T - t0;         // nval <= 0: all padding
+    const int tp0 = (n ^ 1) * C16, npv = T - tp0;
+    const int64_t hb = static_cast<int64_t>(b) * T * H + h;  // token index of (b, 0, h)
+    auto row = [&](int t) { return (hb + static_cast<int64_t>(min(t, T - 1)) * H) * DK + CH * lane; };
 #pragma unroll
     for (int t = 0; t < C16; ++t) {
-        const int64_t off = r0 + min(t, nval - 1) * hdk;
+        const int64_t off = row(t0 + t), offp = row(tp0 + t);
         rk[t] = *reinterpret_cast<const Pk *>(gk + off);
         rq[t] = *reinterpret_cast<const Pk *>(gq + off);
         ra[t] = *reinterpret_cast<const Pk *>(gal + off);
+        rap[t] = *reinterpret_cast<const Pk *>(gal + offp);
+        rkp[t] = odd ? *reinterpret_cast<const Pk *>(gk + offp) : Pk(0);
     }
-    const uint16_t rb = gbe[(static_cast<int64_t>(b) * T + t0 + min(lane & 15, nval - 1)) * H + h];
+    const uint16_t rb = gbe[hb + static_cast<int64_t>(min(t0 + (lane & 15), T - 1)) * H];
     // padding rows: zero key and query, decay 1
-    if (nval < C16) {
+    {
         const Pk one = CH == 2 ? Pk(0x3f803f80u) : Pk(0x3f80u);
 #pragma unroll
         for (int t = 0; t < C16; ++t) {
@@ -160,6 +185,10 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
                 rk[t] = 0;
                 rq[t] = 0;
                 ra[t] = one;
+            }
+            if (t >= npv) {
+                rkp[t] = 0;
+                rap[t] = one;
             }
         }
     }
@@ -186,6 +215,29 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
             G[t][j] = acc;
         }
     }
+    // the partner's log2 Gam_C; an odd sub-chunk also stages the even one's
+    // k * Gam_C / Gam rows for the cross blocks (its own decay never enters them)
+    float gpx[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < C16; ++t) acc += fmaxf(__builtin_amdgcn_logf(chan(rap[t], j)), -200.f);
+        gpx[j] = acc;
+    }
+    if (odd) {
+        float acc[CH] = {};
+#pragma unroll
+        for (int t = 0; t < C16; ++t) {
+            float k0[CH];
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                acc[j] += fmaxf(__builtin_amdgcn_logf(chan(rap[t], j)), -200.f);
+                k0[j] = chan(rkp[t], j) * exp2_fast(gpx[j] - acc[j]);
+            }
+            put(s.k0, KS, t, k0);
+        }
+    }
     float gcx[CH], emax = 0.f;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
@@ -196,9 +248,23 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) emax = fmaxf(emax, __shfl_xor(emax, m, 64));
     const bool fast = emax <= kFastLimit;
-    float gcp[CH];  // Gam_C per channel
+    float gcp[CH], gcq[CH];  // Gam_C per channel, own and the partner's
 #pragma unroll
-    for (int j = 0; j < CH; ++j) gcp[j] = exp2_fast(gcx[j]);
+    for (int j = 0; j < CH; ++j) {
+        gcp[j] = exp2_fast(gcx[j]);
+        gcq[j] = exp2_fast(gpx[j]);
+    }
+    // Tiles go to the block relative to the pair: the odd sub-chunk's k * Gam
+    // and q * Gam also carry the even one's decay (they act on the state at
+    // the pair start), the even sub-chunk's k * Gam_C / Gam also the odd
+    // one's (it enters the state at the pair end).  Products within the
+    // sub-chunk use the local tiles.
+    float sdq[CH], se[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        sdq[j] = odd ? gcq[j] : 1.f;
+        se[j] = odd ? 1.f : gcq[j];
+    }
     // scaled tiles (the factored form's branch taken once per chunk): all
     // three go to the block, and the factored form also keeps k * Gam,
     // q * Gam and k / Gam in LDS for its products
@@ -222,9 +288,16 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
                     ke[j] = kv * exp2_fast(gcx[j] - G[t][j]);
                 }
             }
-            put(o.kd, DK, t, kd);
-            put(o.qd, DK, t, qd);
-            put(o.ke, DK, t, ke);
+            float kdo[CH], qdo[CH], keo[CH];
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                kdo[j] = kd[j] * sdq[j];
+                qdo[j] = qd[j] * sdq[j];
+                keo[j] = ke[j] * se[j];
+            }
+            put(o.kd, DK, t, kdo);
+            put(o.qd, DK, t, qdo);
+            put(o.ke, DK, t, keo);
             if constexpr (F) {
                 put(s.a, KS, t, kd);
                 put(s.b, KS, t, qd);
@@ -235,8 +308,8 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
     if (fast) tiles(std::true_type{});
     else tiles(std::false_type{});
 #pragma unroll
-    for (int j = 0; j < CH; ++j) o.gc[CH * lane + j] = gcp[j];
-    if (lane < C16) s.beta[lane] = lane < nval ? bf16_bits_to_f32(rb) : 0.f;
+    for (int j = 0; j < CH; ++j) o.gc[CH * lane + j] = gcp[j] * gcq[j];  // the pair's (read from even blocks)
+    if (lane < C16) s.beta[lane] = lane < nval ? bf16_bits_to_f32(rb) : 0.f;  // zero on padding rows
     wave_lds_fence();
     // Gram block G[t][s] (lane (g, i): t = 4g + r, s = i) and the
     // Aqk block as (K/Gam)(Q*Gam)^T (lane (g, i): s = 4g + r, t = i)
@@ -350,6 +423,67 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
     }
     wave_lds_fence();
     o.dt[lane] = s.dt[lane];
+    if (!odd) return;
+    // Cross blocks of the pair (odd sub-chunk t, even sub-chunk s): each
+    // entry sum_c x_tc k_sc 2^{G_tc - G_sc} splits at the last even token
+    // into 2^{G_tc} (this sub-chunk's own decay) and 2^{Gp_15c - Gp_sc} (the
+    // even one's decay to its end), both at most 1, so the local tiles give
+    // it exactly:  G_10 = (K_1 * Gam_1) (K_0 * Gam_C0 / Gam_0)^T and
+    // Aqk_10 = (Q_1 * Gam_1) (K_0 * Gam_C0 / Gam_0)^T.
+    wave_lds_fence();
+#pragma unroll
+    for (int t = 0; t < C16; ++t) {
+        float kd[CH], qd[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const float e1 = exp2_fast(G[t][j]);
+            kd[j] = chan(rk[t], j) * e1;
+            qd[j] = chan(rq[t], j) * e1;
+        }
+        put(s.a, KS, t, kd);
+        put(s.b, KS, t, qd);
+    }
+    wave_lds_fence();
+    f32x4 g10 = {0.f, 0.f, 0.f, 0.f}, a10 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < KSTEP; ++p) {
+        const bf16x8 k0f = row_frag2(s.k0, KS, 0, 32 * p, lane);
+        g10 = mfma32(row_frag2(s.a, KS, 0, 32 * p, lane), k0f, g10);  // lane (g, i): [t = 4g + r][s = i]
+        a10 = mfma32(k0f, row_frag2(s.b, KS, 0, 32 * p, lane), a10);  // lane (g, i): [s = 4g + r][t = i]
+    }
+    o.ax[lane] = bf4(a10);
+    // M_10 = -T_11 G_10 with T_11 = (I + L_11)^{-1} diag(beta_1), formed
+    // transposed (A = -G_10^T from the accumulator, B = T_11^T from its
+    // A-operand fragment) so it comes out in A-operand order
+    o.mx[lane] = bf4(mfma16(bf4(-g10), s.dt[lane], f32x4{0.f, 0.f, 0.f, 0.f}));
+}
+
+// U of a pair of sub-chunks from the bf16 state at the pair start:
+//   Z_i = (K*Gam)_i S^T (pair-relative tiles), U_0 = T_00 (V_0 - Z_0),
+//   U_1 = T_11 (V_1 - Z_1) + M_10 U_0.
+// The carry and the output wave both call this on the same operands, so both
+// get the same U bit for bit.  Lane (g, i) holds rows t = 4g + r, column i.
+template <int KSTEP, int KT>
+__device__ __forceinline__ void pair_solve(const bf16x8 (&kf0)[KSTEP], const bf16x8 (&kf1)[KSTEP], const bf16x4 (&Sb)[KT],
+                                           bf16x4 vb0, bf16x4 vb1, bf16x4 dt0, bf16x4 dt1, bf16x4 mxf, bf16x4 &ub0,
+                                           bf16x4 &ub1) {
+    f32x4 z00 = {0.f, 0.f, 0.f, 0.f}, z01 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 z10 = {0.f, 0.f, 0.f, 0.f}, z11 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < KSTEP; p += 2) {  // two independent accumulation chains per sub-chunk
+        const bf16x8 b0 = cat8(Sb[2 * p], Sb[2 * p + 1]), b1 = cat8(Sb[2 * p + 2], Sb[2 * p + 3]);
+        z00 = mfma32(kf0[p], b0, z00);
+        z01 = mfma32(kf0[p + 1], b1, z01);
+        z10 = mfma32(kf1[p], b0, z10);
+        z11 = mfma32(kf1[p + 1], b1, z11);
+    }
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 r0 = __builtin_convertvector(vb0, f32x4) - (z00 + z01);
+    const f32x4 r1 = __builtin_convertvector(vb1, f32x4) - (z10 + z11);
+    const f32x4 u0 = mfma16(dt0, bf4(r0), zero);
+    const f32x4 u1 = mfma16(dt1, bf4(r1), zero);
+    ub0 = bf4(u0);
+    ub1 = bf4(mfma16(mxf, ub0, u1));
 }
 
 template <int DK, int NVT>
@@ -368,7 +502,7 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = lane >> 4, lc = lane & 15;
-    const int nchunks = (T + C16 - 1) / C16;
+    const int npairs = (T + 2 * C16 - 1) / (2 * C16);  // steps of two 16-token sub-chunks
     auto tok = [&](int t) { return (static_cast<int64_t>(b) * T + t) * H + h; };
 
     if (tid == 0) {
@@ -397,22 +531,28 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) s.sh[0][vt][kt][lane] = bf4(St[kt]);
             lds_arrive(&s.sp[vt], lane);
-            // Operands of a chunk that do not depend on the state, read one
-            // chunk ahead: the next slot's reads go out while this chunk's
+            // Operands of a pair that do not depend on the state, read one
+            // pair ahead: the next slot's reads go out while this pair's
             // state-update products run.
-            bf16x8 kf[KSTEP];
-            bf16x4 vb, dtf, kef[KT];
+            bf16x8 kf0[KSTEP], kf1[KSTEP], kef[KT];
+            bf16x4 vb0, vb1, dt0, dt1, mxf;
             float4 gcv[KT];
             auto load_ops = [&](int c) {
                 const typename Lds::Slot &Sl = s.slot[c & 3];
                 lds_wait(&s.ready[c & 3], static_cast<unsigned int>(c / 4 + 1));
 #pragma unroll
-                for (int p = 0; p < KSTEP; ++p) kf[p] = row_frag2(Sl.kd, KS, 0, 32 * p, lane);
-                vb = col_gather4(Sl.v, VS, 0, 16 * vt, lane);
-                dtf = Sl.dt[lane];
+                for (int p = 0; p < KSTEP; ++p) {
+                    kf0[p] = row_frag2(Sl.kd, KS, 0, 32 * p, lane);
+                    kf1[p] = row_frag2(Sl.kd, KS, C16, 32 * p, lane);
+                }
+                vb0 = col_gather4(Sl.v, VS, 0, 16 * vt, lane);
+                vb1 = col_gather4(Sl.v, VS, C16, 16 * vt, lane);
+                dt0 = Sl.dt[0][lane];
+                dt1 = Sl.dt[1][lane];
+                mxf = Sl.mx[lane];
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) {
-                    kef[kt] = col_gather4(Sl.ke, KS, 0, 16 * kt, lane);
+                    kef[kt] = col_frag(Sl.ke, KS, 0, 16 * kt, lane);
                     gcv[kt] = *reinterpret_cast<const float4 *>(&Sl.gc[16 * kt + 4 * lg]);
                 }
             };
@@ -420,26 +560,19 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
             bf16x4 Sb[KT];
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) Sb[kt] = bf4(St[kt]);
-            if (nchunks > 0) load_ops(0);
+            if (npairs > 0) load_ops(0);
 #pragma unroll 1
-            for (int c = 0; c < nchunks; ++c) {
-                // Z = (K*Gam) S^T: lane (g, i) holds rows t = 4g + r, column i;
-                // two independent accumulation chains
-                f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < KSTEP; p += 2) {
-                    z0 = mfma32(kf[p], cat8(Sb[2 * p], Sb[2 * p + 1]), z0);
-                    z1 = mfma32(kf[p + 1], cat8(Sb[2 * p + 2], Sb[2 * p + 3]), z1);
-                }
-                const f32x4 rhs = __builtin_convertvector(vb, f32x4) - (z0 + z1);
-                const bf16x4 ub = bf4(mfma16(dtf, bf4(rhs), f32x4{0.f, 0.f, 0.f, 0.f}));
-                // S^T <- diag(Gam_C) S^T + (K*Gam_C/Gam)^T U
+            for (int c = 0; c < npairs; ++c) {
+                bf16x4 ub0, ub1;
+                pair_solve(kf0, kf1, Sb, vb0, vb1, dt0, dt1, mxf, ub0, ub1);
+                // S^T <- diag(Gam_C) S^T + [K*Gam_C/Gam]^T [U_0; U_1] over the 32 tokens
+                const bf16x8 bU = cat8(ub0, ub1);
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) {
                     St[kt] = St[kt] * f32x4{gcv[kt].x, gcv[kt].y, gcv[kt].z, gcv[kt].w};
-                    St[kt] = mfma16(kef[kt], ub, St[kt]);
+                    St[kt] = mfma32(kef[kt], bU, St[kt]);
                 }
-                if (c + 1 < nchunks) load_ops(c + 1);
+                if (c + 1 < npairs) load_ops(c + 1);
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) Sb[kt] = bf4(St[kt]);
                 // S(c + 1 - NSB) has been read from this buffer
@@ -459,104 +592,134 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
             }
         } else {
             // ================================ output ===============================
-            for (int c = 0; c < nchunks; ++c) {
+            for (int c = 0; c < npairs; ++c) {
                 const typename Lds::Slot &Sl = s.slot[c & 3];
                 lds_wait(&s.ready[c & 3], static_cast<unsigned int>(c / 4 + 1));
                 // state-independent operands first
-                bf16x8 qf[KSTEP], kf[KSTEP];
+                bf16x8 qf0[KSTEP], qf1[KSTEP], kf0[KSTEP], kf1[KSTEP];
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p) {
-                    qf[p] = row_frag2(Sl.qd, KS, 0, 32 * p, lane);
-                    kf[p] = row_frag2(Sl.kd, KS, 0, 32 * p, lane);
+                    qf0[p] = row_frag2(Sl.qd, KS, 0, 32 * p, lane);
+                    qf1[p] = row_frag2(Sl.qd, KS, C16, 32 * p, lane);
+                    kf0[p] = row_frag2(Sl.kd, KS, 0, 32 * p, lane);
+                    kf1[p] = row_frag2(Sl.kd, KS, C16, 32 * p, lane);
                 }
-                const bf16x4 aq = Sl.aqk[lane];
-                const bf16x4 vb = col_gather4(Sl.v, VS, 0, 16 * vt, lane);
-                const bf16x4 dtf = Sl.dt[lane];
+                const bf16x4 aq0 = Sl.aqk[0][lane], aq1 = Sl.aqk[1][lane], axf = Sl.ax[lane];
+                const bf16x4 vb0 = col_gather4(Sl.v, VS, 0, 16 * vt, lane);
+                const bf16x4 vb1 = col_gather4(Sl.v, VS, C16, 16 * vt, lane);
+                const bf16x4 dt0 = Sl.dt[0][lane], dt1 = Sl.dt[1][lane], mxf = Sl.mx[lane];
                 lds_wait(&s.sp[vt], static_cast<unsigned int>(c + 1));
-                bf16x8 bS[KSTEP];
+                bf16x4 Sb[KT];
 #pragma unroll
-                for (int p = 0; p < KSTEP; ++p)
-                    bS[p] = cat8(s.sh[c % Lds::NSB][vt][2 * p][lane], s.sh[c % Lds::NSB][vt][2 * p + 1][lane]);
+                for (int kt = 0; kt < KT; ++kt) Sb[kt] = s.sh[c % Lds::NSB][vt][kt][lane];
                 if constexpr (Lds::kStateGuard) lds_arrive(&s.so[vt], lane);
+                // U exactly as the carry forms it, from the same bf16 state
+                bf16x4 ub0, ub1;
+                pair_solve(kf0, kf1, Sb, vb0, vb1, dt0, dt1, mxf, ub0, ub1);
                 // Y^T = S (Q*Gam)^T + U^T Aqk^T: lane (g, i) holds columns 4g + r of
-                // token i; two independent accumulation chains
-                f32x4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
-                f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+                // token i; two independent accumulation chains per sub-chunk
+                f32x4 y00 = {0.f, 0.f, 0.f, 0.f}, y01 = {0.f, 0.f, 0.f, 0.f};
+                f32x4 y10 = {0.f, 0.f, 0.f, 0.f}, y11 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int p = 0; p < KSTEP; p += 2) {
-                    z0 = mfma32(kf[p], bS[p], z0);
-                    z1 = mfma32(kf[p + 1], bS[p + 1], z1);
-                    y0 = mfma32(bS[p], qf[p], y0);
-                    y1 = mfma32(bS[p + 1], qf[p + 1], y1);
+                    const bf16x8 b0 = cat8(Sb[2 * p], Sb[2 * p + 1]), b1 = cat8(Sb[2 * p + 2], Sb[2 * p + 3]);
+                    y00 = mfma32(b0, qf0[p], y00);
+                    y01 = mfma32(b1, qf0[p + 1], y01);
+                    y10 = mfma32(b0, qf1[p], y10);
+                    y11 = mfma32(b1, qf1[p + 1], y11);
                 }
-                // U exactly as the carry forms it, from the same bf16 state
-                const f32x4 rhs = __builtin_convertvector(vb, f32x4) - (z0 + z1);
-                const bf16x4 ub = bf4(mfma16(dtf, bf4(rhs), f32x4{0.f, 0.f, 0.f, 0.f}));
-                const f32x4 y = mfma16(ub, aq, y0 + y1);
-                const int t = c * C16 + lc;
-                if (t < T)
-                    *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(a.out) + tok(t) * dv + v0 + 16 * vt + 4 * lg) = bf4(y);
+                const f32x4 y0 = mfma16(ub0, aq0, y00 + y01);
+                const f32x4 y1 = mfma16(ub1, aq1, mfma16(ub0, axf, y10 + y11));
+                const int t = c * (2 * C16) + lc;
+                uint16_t *yo = static_cast<uint16_t *>(a.out) + v0 + 16 * vt + 4 * lg;
+                if (t < T) *reinterpret_cast<bf16x4 *>(yo + tok(t) * dv) = bf4(y0);
+                if (t + C16 < T) *reinterpret_cast<bf16x4 *>(yo + tok(t + C16) * dv) = bf4(y1);
                 lds_arrive(&s.cons[vt], lane);
             }
         }
     } else {
         // ============================== producers ==============================
-        // Producer pw copies chunks pw, pw + 4, ...: the chunk's block, 16-byte
-        // piece p = 64i + lane per load, and the slice's value rows (KBV/8
-        // lanes per row, 8 columns each; lanes past row 15 idle).
+        // Producer pw copies pairs pw, pw + 4, ...: the pair's two blocks,
+        // 16-byte piece p = 64i + lane per load, and the slice's 32 value rows
+        // (KBV/8 lanes per row, 8 columns each).
         const int pw = wave - 2 * NVT;
         typename Lds::Slot &Sl = s.slot[pw];
         using Blk = KdaBlock<DK>;
-        constexpr int NPL = (Blk::kPieces + 63) / 64;  // block pieces per lane
+        constexpr int NP2 = 2 * Blk::kPieces;          // pieces of the two blocks of a pair
+        constexpr int NPL = (NP2 + 63) / 64;           // pieces per lane
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 *gder = reinterpret_cast<const u32x4 *>(der + static_cast<int64_t>(head) * nchunks);
+        const u32x4 *gder = reinterpret_cast<const u32x4 *>(der + static_cast<int64_t>(head) * 2 * npairs);
         const uint16_t *gv = static_cast<const uint16_t *>(a.v);
-        constexpr int VLPR = KBV / 8;
+        constexpr int VLPR = KBV / 8;                  // lanes per value row
+        constexpr int VRPL = 64 / VLPR;                // value rows per load
+        constexpr int NVL = 2 * C16 / VRPL;            // value loads per pair
         const int vrow = lane / VLPR, vcol = 8 * (lane % VLPR);
         u32x4 rd[NPL];
-        uint4 rv;
-        int nnext = 0;  // tokens inside the sequence of the staged chunk
+        uint4 rv[NVL];
+        int nnext = 0;  // tokens inside the sequence from the staged pair's start
         auto fetch = [&](int n) {
-            const u32x4 *src = gder + static_cast<int64_t>(n) * (sizeof(Blk) / 16);
+            const u32x4 *src = gder + static_cast<int64_t>(n) * (2 * sizeof(Blk) / 16);
 #pragma unroll
-            for (int i = 0; i < NPL; ++i) rd[i] = src[min(64 * i + lane, Blk::kPieces - 1)];
-            const int t0 = n * C16;
-            nnext = min(C16, T - t0);
-            rv = *reinterpret_cast<const uint4 *>(gv + tok(t0 + min(vrow, nnext - 1)) * dv + v0 + vcol);
+            for (int i = 0; i < NPL; ++i) rd[i] = src[min(64 * i + lane, NP2 - 1)];
+            const int t0 = n * 2 * C16;
+            nnext = T - t0;
+#pragma unroll
+            for (int j = 0; j < NVL; ++j)
+                rv[j] = *reinterpret_cast<const uint4 *>(gv + tok(min(t0 + vrow + VRPL * j, T - 1)) * dv + v0 + vcol);
         };
-        // LDS place of block piece p: token-row pieces go to padded rows
+        // LDS place of piece p: token-row pieces go to padded rows (the odd
+        // block's below the even one's); the even block supplies the pair's
+        // Gam_C, the odd block the cross blocks
         auto commit = [&](int nval) {
-            __bf16 *rows = Sl.kd;  // kd, ke, qd are consecutive C16*KS arrays
-            u32x4 *tail = reinterpret_cast<u32x4 *>(&Sl.aqk[0]);  // aqk, dt, gc are consecutive
+            constexpr int PPR = DK / 8;  // pieces per row
 #pragma unroll
             for (int i = 0; i < NPL; ++i) {
                 const int p = 64 * i + lane;
-                if (p < Blk::kRowPieces) {
-                    constexpr int PPR = DK / 8;  // pieces per row
-                    const int r = p / PPR;       // row among the 3 * 16
-                    *reinterpret_cast<u32x4 *>(rows + r * KS + 8 * (p % PPR)) = rd[i];
-                } else if (p < Blk::kPieces) {
-                    tail[p - Blk::kRowPieces] = rd[i];
+                if (p >= NP2) continue;
+                const int blk = p >= Blk::kPieces ? 1 : 0;
+                const int q = p - blk * Blk::kPieces;
+                if (q < Blk::kRowPieces) {
+                    const int r = q / PPR;       // row among the 3 * 16 of the block
+                    const int tsr = r / C16;     // kd, ke, qd
+                    __bf16 *rows = tsr == 0 ? Sl.kd : (tsr == 1 ? Sl.ke : Sl.qd);
+                    *reinterpret_cast<u32x4 *>(rows + (C16 * blk + r % C16) * KS + 8 * (q % PPR)) = rd[i];
+                } else {
+                    const int e = q - Blk::kRowPieces;
+                    if (e < 32) {
+                        reinterpret_cast<u32x4 *>(&Sl.aqk[blk][0])[e] = rd[i];
+                    } else if (e < 64) {
+                        reinterpret_cast<u32x4 *>(&Sl.dt[blk][0])[e - 32] = rd[i];
+                    } else if (e < 64 + DK / 4) {
+                        if (blk == 0) reinterpret_cast<u32x4 *>(&Sl.gc[0])[e - 64] = rd[i];
+                    } else if (blk == 1) {
+                        const int x = e - 64 - DK / 4;
+                        if (x < 32) reinterpret_cast<u32x4 *>(&Sl.mx[0])[x] = rd[i];
+                        else reinterpret_cast<u32x4 *>(&Sl.ax[0])[x - 32] = rd[i];
+                    }
                 }
             }
-            const uint32_t m = vrow < nval ? 0xffffffffu : 0u;
-            if (vrow < C16)
-                *reinterpret_cast<uint4 *>(&Sl.v[vrow * VS + vcol]) = make_uint4(rv.x & m, rv.y & m, rv.z & m, rv.w & m);
+#pragma unroll
+            for (int j = 0; j < NVL; ++j) {
+                const int row = vrow + VRPL * j;
+                const uint32_t m = row < nval ? 0xffffffffu : 0u;
+                *reinterpret_cast<uint4 *>(&Sl.v[row * VS + vcol]) =
+                    make_uint4(rv[j].x & m, rv[j].y & m, rv[j].z & m, rv[j].w & m);
+            }
         };
-        if (pw < nchunks) fetch(pw);
-        for (int n = pw; n < nchunks; n += 4) {
+        if (pw < npairs) fetch(pw);
+        for (int n = pw; n < npairs; n += 4) {
             const int nval = nnext;
-            if (n >= 4) {  // chunk n - 4 released by every consumer wave
+            if (n >= 4) {  // pair n - 4 released by every consumer wave
 #pragma unroll
                 for (int w = 0; w < NVT; ++w) {
-                    lds_wait(&s.sp[w], static_cast<unsigned int>(n - 2));    // carry w past chunk n - 4
+                    lds_wait(&s.sp[w], static_cast<unsigned int>(n - 2));    // carry w past pair n - 4
                     lds_wait(&s.cons[w], static_cast<unsigned int>(n - 3));  // output w done with it
                 }
             }
             commit(nval);
             lds_arrive(&s.ready[pw], lane);
-            // this producer's next chunk (past the end: the last chunk again, unused)
-            fetch(min(n + 4, nchunks - 1));
+            // this producer's next pair (past the end: the last pair again, unused)
+            fetch(min(n + 4, npairs - 1));
         }
     }
 }
@@ -570,7 +733,7 @@ bool kda_chunked_supported(const DeltaArgs &a) {
 template <int DK, int NVT>
 static hipError_t launch_dk(const DeltaArgs &a, hipStream_t stream) {
     const unsigned blocks = static_cast<unsigned>(a.B * a.H * (a.dv / KdaShape<NVT>::BV));
-    const int64_t tasks = a.B * a.H * ((a.T + C16 - 1) / C16);
+    const int64_t tasks = a.B * a.H * 2 * ((a.T + 2 * C16 - 1) / (2 * C16));  // sub-chunks, pairs complete
     if (tasks > 0x7fffffff) return hipErrorInvalidValue;
     KdaBlock<DK> *der = nullptr;
     if (tasks > 0) {
