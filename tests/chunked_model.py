@@ -159,3 +159,55 @@ def vla_chunked(q, k, v, p, A_in=None, S_in=None, C=64):
             A_out[b, h] = A
             S_out[b, h] = S
     return out, A_out, S_out
+
+
+def kda_paired(q, k, v, beta, alpha, state_in=None):
+    """Kimi Delta stepped over pairs of 16-token sub-chunks, in the form the
+    chunked kernel evaluates: each sub-chunk's tiles are formed locally (its
+    own running decay), then made relative to the pair (the odd sub-chunk's
+    K*G and Q*G times the even one's end decay g0, the even one's K*gC/G
+    times the odd one's g1), both sub-chunks act on the state at the pair
+    start, and they are coupled by the cross blocks
+        G10 = (K1*G1)(K0*g0/G0)^T,  A10 = (Q1*G1)(K0*g0/G0)^T,
+        U0 = T00 (V0 - Z0),  U1 = T11 (V1 - Z1) - T11 G10 U0,
+    with Tii = (I + Lii)^-1 diag(beta_i).  A ragged tail is padded with zero
+    keys, queries and values, decay 1 and beta 0."""
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    n2 = -(-T // 32) * 32
+    pad = lambda x, fill: np.concatenate([x, np.full((x.shape[0], n2 - T) + x.shape[2:], fill)], axis=1)
+    q, k, v, beta, alpha = pad(q, 0.0), pad(k, 0.0), pad(v, 0.0), pad(beta, 0.0), pad(alpha, 1.0)
+    out = np.zeros((B, n2, H, dv))
+    state_out = np.zeros((B, H, dv, dk))
+    tril = np.tril(np.ones((16, 16)))
+    stril = np.tril(np.ones((16, 16)), -1)
+
+    def local(t0, b, h):
+        K, Q, V = k[b, t0:t0 + 16, h], q[b, t0:t0 + 16, h], v[b, t0:t0 + 16, h]
+        be = beta[b, t0:t0 + 16, h]
+        lg = np.cumsum(np.log(alpha[b, t0:t0 + 16, h]), axis=0)
+        D = np.where(tril[:, :, None] > 0, lg[:, None, :] - lg[None, :, :], -np.inf)
+        Gm = np.exp(D)
+        Akk = np.einsum("tc,sc,tsc->ts", K, K, Gm)
+        Aqk = np.einsum("tc,sc,tsc->ts", Q, K, Gm) * tril
+        Tm = np.linalg.inv(np.eye(16) + stril * (be[:, None] * Akk)) * be[None, :]
+        G = np.exp(lg)
+        return dict(kd=K * G, qd=Q * G, ke=K * np.exp(lg[-1] - lg), gc=G[-1], aqk=Aqk, T=Tm, V=V)
+
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dv, dk)) if state_in is None else state_in[b, h].copy()
+            for t0 in range(0, n2, 32):
+                x0, x1 = local(t0, b, h), local(t0 + 16, b, h)
+                G10 = x1["kd"] @ x0["ke"].T
+                A10 = x1["qd"] @ x0["ke"].T
+                M10 = -x1["T"] @ G10
+                kd1, qd1 = x1["kd"] * x0["gc"], x1["qd"] * x0["gc"]
+                ke0 = x0["ke"] * x1["gc"]
+                U0 = x0["T"] @ (x0["V"] - x0["kd"] @ S.T)
+                U1 = x1["T"] @ (x1["V"] - kd1 @ S.T) + M10 @ U0
+                out[b, t0:t0 + 16, h] = x0["qd"] @ S.T + x0["aqk"] @ U0
+                out[b, t0 + 16:t0 + 32, h] = qd1 @ S.T + A10 @ U0 + x1["aqk"] @ U1
+                S = S * (x0["gc"] * x1["gc"])[None, :] + U0.T @ ke0 + U1.T @ x1["ke"]
+            state_out[b, h] = S
+    return out[:, :T], state_out

@@ -472,6 +472,20 @@ def test_chunked_form_equals_recurrence(variant, C):
     assert np.max(np.abs(s2 - st)) <= 1e-12 * np.max(np.abs(st))
 
 
+@pytest.mark.parametrize("T", [5, 16, 32, 47, 83])
+def test_kda_paired_form_equals_recurrence(T):
+    """Kimi Delta stepped over pairs of 16-token sub-chunks (the chunked
+    kernel's form: pair-relative tiles, cross blocks split at the sub-chunk
+    boundary, U1 coupled to U0 through -T11 G10) equals the token-by-token
+    oracle to ~1e-12 relative, for lengths that end inside the even or the
+    odd sub-chunk of the last pair, with a carried-in state."""
+    d = _rand_delta(93, B=1, T=T, H=2, dk=16, dv=12, variant="kda", weak=False)
+    out, st = _run("kda", d)
+    o2, s2 = chunked_model.kda_paired(d["q"], d["k"], d["v"], d["beta"], d["alpha"], state_in=d["state_in"])
+    assert np.max(np.abs(o2 - out)) <= 1e-12 * np.max(np.abs(out))
+    assert np.max(np.abs(s2 - st)) <= 1e-12 * np.max(np.abs(st))
+
+
 @pytest.mark.parametrize("scale", [0.3, 3.0, 30.0])
 def test_kda_level_blocks_equal_direct(scale):
     """The reference-token levels that form Kimi Delta's decayed Gram blocks
