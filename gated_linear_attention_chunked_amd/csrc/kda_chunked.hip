@@ -134,9 +134,10 @@ struct KdaDeriveLds {
     alignas(16) bf16x4 dt[64];
 };
 
-// One wave per (sequence, head, chunk).  Lane owns key channels CH*lane ..
-// CH*lane + CH - 1 for all 16 tokens (one packed load per token and tensor);
-// beta of token lane (lanes 0-15).
+// One wave per (sequence, head, pair of 16-token sub-chunks), the even
+// sub-chunk first.  Lane owns key channels CH*lane .. CH*lane + CH - 1 for all
+// 16 tokens of a sub-chunk (one packed load per token and tensor); beta of
+// token lane (lanes 0-15).
 template <int DK>
 __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK> *__restrict__ out) {
     constexpr int KS = DK + 8;
@@ -144,318 +145,304 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
     __shared__ KdaDeriveLds<DK> s;
 
     const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
-    const int nsub = 2 * ((T + 2 * C16 - 1) / (2 * C16));  // sub-chunks per head, pairs complete
+    const int npair = (T + 2 * C16 - 1) / (2 * C16);  // pairs per head (the last may end in padding)
     const int task = blockIdx.x;
-    const int head = task / nsub, n = task - head * nsub;
-    const bool odd = (n & 1) != 0;
+    const int head = task / npair, pr = task - head * npair;
     const int b = head / H, h = head % H;
     const int lane = threadIdx.x;
     const int lg = lane >> 4, lc = lane & 15;
-    KdaBlock<DK> &o = out[task];
 
     const uint16_t *gq = static_cast<const uint16_t *>(a.q);
     const uint16_t *gk = static_cast<const uint16_t *>(a.k);
     const uint16_t *gal = static_cast<const uint16_t *>(a.alpha);
     const uint16_t *gbe = static_cast<const uint16_t *>(a.beta);
     using Pk = std::conditional_t<CH == 2, uint32_t, uint16_t>;
-    // this sub-chunk's rows, and the decays (odd: also the keys) of the other
-    // sub-chunk of its pair; rows are read clamped into the sequence (an odd
-    // sub-chunk may lie wholly past its end) and padded below
-    Pk rk[C16], rq[C16], ra[C16], rap[C16], rkp[C16];
-    const int t0 = n * C16, nval = T - t0;         // nval <= 0: all padding
-    const int tp0 = (n ^ 1) * C16, npv = T - tp0;
     const int64_t hb = static_cast<int64_t>(b) * T * H + h;  // token index of (b, 0, h)
+    // rows are read clamped into the sequence (the odd sub-chunk may lie
+    // wholly past its end) and padded: zero key and query, decay 1
     auto row = [&](int t) { return (hb + static_cast<int64_t>(min(t, T - 1)) * H) * DK + CH * lane; };
-#pragma unroll
-    for (int t = 0; t < C16; ++t) {
-        const int64_t off = row(t0 + t), offp = row(tp0 + t);
-        rk[t] = *reinterpret_cast<const Pk *>(gk + off);
-        rq[t] = *reinterpret_cast<const Pk *>(gq + off);
-        ra[t] = *reinterpret_cast<const Pk *>(gal + off);
-        rap[t] = *reinterpret_cast<const Pk *>(gal + offp);
-        rkp[t] = odd ? *reinterpret_cast<const Pk *>(gk + offp) : Pk(0);
-    }
-    const uint16_t rb = gbe[hb + static_cast<int64_t>(min(t0 + (lane & 15), T - 1)) * H];
-    // padding rows: zero key and query, decay 1
-    {
-        const Pk one = CH == 2 ? Pk(0x3f803f80u) : Pk(0x3f80u);
+    const Pk one = CH == 2 ? Pk(0x3f803f80u) : Pk(0x3f80u);
+    float gprev[CH];  // log2 Gam_C of the even sub-chunk, kept for the odd one
+#pragma unroll 1
+    for (int sub = 0; sub < 2; ++sub) {
+        const int n = 2 * pr + sub;
+        const bool odd = sub != 0;
+        KdaBlock<DK> &o = out[2 * task + sub];
+        wave_lds_fence();  // the previous sub-chunk's LDS reads before this one's writes
+        Pk rk[C16], rq[C16], ra[C16];
+        const int t0 = n * C16, nval = T - t0;  // nval <= 0: all padding
 #pragma unroll
         for (int t = 0; t < C16; ++t) {
-            if (t >= nval) {
-                rk[t] = 0;
-                rq[t] = 0;
-                ra[t] = one;
+            const int64_t off = row(t0 + t);
+            rk[t] = t < nval ? *reinterpret_cast<const Pk *>(gk + off) : Pk(0);
+            rq[t] = t < nval ? *reinterpret_cast<const Pk *>(gq + off) : Pk(0);
+            ra[t] = t < nval ? *reinterpret_cast<const Pk *>(gal + off) : one;
+        }
+        const uint16_t rb = gbe[hb + static_cast<int64_t>(min(t0 + (lane & 15), T - 1)) * H];
+        // channel j of a packed pair, widened
+        auto chan = [](Pk x, int j) { return bf16_bits_to_f32(static_cast<uint16_t>(x >> (16 * j))); };
+        // CH consecutive bf16 of row t, channels CH*lane ..
+        auto put = [&](__bf16 *m, int stride, int t, const float (&x)[CH]) {
+            if constexpr (CH == 2) {
+                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                *reinterpret_cast<bf16x2 *>(m + t * stride + 2 * lane) = bf16x2{static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1])};
+            } else {
+                m[t * stride + lane] = static_cast<__bf16>(x[0]);
             }
-            if (t >= npv) {
-                rkp[t] = 0;
-                rap[t] = one;
+        };
+        // per-channel log2 decay prefix sums over the chunk
+        float G[C16][CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            float acc = 0.f;
+#pragma unroll
+            for (int t = 0; t < C16; ++t) {
+                const float la = fmaxf(__builtin_amdgcn_logf(chan(ra[t], j)), -200.f);
+                acc += la;
+                G[t][j] = acc;
             }
         }
-    }
-    // channel j of a packed pair, widened
-    auto chan = [](Pk x, int j) { return bf16_bits_to_f32(static_cast<uint16_t>(x >> (16 * j))); };
-    // CH consecutive bf16 of row t, channels CH*lane ..
-    auto put = [&](__bf16 *m, int stride, int t, const float (&x)[CH]) {
-        if constexpr (CH == 2) {
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<bf16x2 *>(m + t * stride + 2 * lane) = bf16x2{static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1])};
+        // the other sub-chunk's log2 Gam_C: the odd one's from its decays (read
+        // here, summed as its own pass sums them), the even one's kept
+        float gpx[CH];
+        if (!odd) {
+            Pk rap[C16];
+#pragma unroll
+            for (int t = 0; t < C16; ++t)
+                rap[t] = t < nval - C16 ? *reinterpret_cast<const Pk *>(gal + row(t0 + C16 + t)) : one;
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                float acc = 0.f;
+#pragma unroll
+                for (int t = 0; t < C16; ++t) acc += fmaxf(__builtin_amdgcn_logf(chan(rap[t], j)), -200.f);
+                gpx[j] = acc;
+            }
         } else {
-            m[t * stride + lane] = static_cast<__bf16>(x[0]);
+#pragma unroll
+            for (int j = 0; j < CH; ++j) gpx[j] = gprev[j];
         }
-    };
-    // per-channel log2 decay prefix sums over the chunk
-    float G[C16][CH];
+        float gcx[CH], emax = 0.f;
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-        float acc = 0.f;
-#pragma unroll
-        for (int t = 0; t < C16; ++t) {
-            const float la = fmaxf(__builtin_amdgcn_logf(chan(ra[t], j)), -200.f);
-            acc += la;
-            G[t][j] = acc;
+        for (int j = 0; j < CH; ++j) {
+            gcx[j] = G[C16 - 1][j];
+            emax = fmaxf(emax, -gcx[j]);
         }
-    }
-    // the partner's log2 Gam_C; an odd sub-chunk also stages the even one's
-    // k * Gam_C / Gam rows for the cross blocks (its own decay never enters them)
-    float gpx[CH];
+        // wave max of the largest exponent 2^{-G}
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-        float acc = 0.f;
+        for (int m = 1; m < 64; m <<= 1) emax = fmaxf(emax, __shfl_xor(emax, m, 64));
+        const bool fast = emax <= kFastLimit;
+        float gcp[CH], gcq[CH];  // Gam_C per channel, own and the partner's
 #pragma unroll
-        for (int t = 0; t < C16; ++t) acc += fmaxf(__builtin_amdgcn_logf(chan(rap[t], j)), -200.f);
-        gpx[j] = acc;
-    }
-    if (odd) {
-        float acc[CH] = {};
-#pragma unroll
-        for (int t = 0; t < C16; ++t) {
-            float k0[CH];
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                acc[j] += fmaxf(__builtin_amdgcn_logf(chan(rap[t], j)), -200.f);
-                k0[j] = chan(rkp[t], j) * exp2_fast(gpx[j] - acc[j]);
-            }
-            put(s.k0, KS, t, k0);
+        for (int j = 0; j < CH; ++j) {
+            gcp[j] = exp2_fast(gcx[j]);
+            gcq[j] = exp2_fast(gpx[j]);
         }
-    }
-    float gcx[CH], emax = 0.f;
+        // Tiles go to the block relative to the pair: the odd sub-chunk's k * Gam
+        // and q * Gam also carry the even one's decay (they act on the state at
+        // the pair start), the even sub-chunk's k * Gam_C / Gam also the odd
+        // one's (it enters the state at the pair end).  Products within the
+        // sub-chunk use the local tiles.
+        float sdq[CH], se[CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-        gcx[j] = G[C16 - 1][j];
-        emax = fmaxf(emax, -gcx[j]);
-    }
-    // wave max of the largest exponent 2^{-G}
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) emax = fmaxf(emax, __shfl_xor(emax, m, 64));
-    const bool fast = emax <= kFastLimit;
-    float gcp[CH], gcq[CH];  // Gam_C per channel, own and the partner's
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-        gcp[j] = exp2_fast(gcx[j]);
-        gcq[j] = exp2_fast(gpx[j]);
-    }
-    // Tiles go to the block relative to the pair: the odd sub-chunk's k * Gam
-    // and q * Gam also carry the even one's decay (they act on the state at
-    // the pair start), the even sub-chunk's k * Gam_C / Gam also the odd
-    // one's (it enters the state at the pair end).  Products within the
-    // sub-chunk use the local tiles.
-    float sdq[CH], se[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-        sdq[j] = odd ? gcq[j] : 1.f;
-        se[j] = odd ? 1.f : gcq[j];
-    }
-    // scaled tiles (the factored form's branch taken once per chunk): all
-    // three go to the block, and the factored form also keeps k * Gam,
-    // q * Gam and k / Gam in LDS for its products
-    auto tiles = [&](auto fc) {
-        constexpr bool F = decltype(fc)::value;
-#pragma unroll
-        for (int t = 0; t < C16; ++t) {
-            float kd[CH], qd[CH], ke[CH], kb[CH];
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                const float kv = chan(rk[t], j), qv = chan(rq[t], j);
-                const float e1 = exp2_fast(G[t][j]);
-                kd[j] = kv * e1;
-                qd[j] = qv * e1;
-                if constexpr (F) {  // 2^{-G} is finite here: 2^{G_C - G} as a product
-                    const float eb = exp2_fast(-G[t][j]);
-                    kb[j] = kv * eb;
-                    ke[j] = kv * (gcp[j] * eb);
-                } else {
-                    kb[j] = 0.f;
-                    ke[j] = kv * exp2_fast(gcx[j] - G[t][j]);
-                }
-            }
-            float kdo[CH], qdo[CH], keo[CH];
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                kdo[j] = kd[j] * sdq[j];
-                qdo[j] = qd[j] * sdq[j];
-                keo[j] = ke[j] * se[j];
-            }
-            put(o.kd, DK, t, kdo);
-            put(o.qd, DK, t, qdo);
-            put(o.ke, DK, t, keo);
-            if constexpr (F) {
-                put(s.a, KS, t, kd);
-                put(s.b, KS, t, qd);
-                put(s.kb, KS, t, kb);
-            }
+        for (int j = 0; j < CH; ++j) {
+            sdq[j] = odd ? gcq[j] : 1.f;
+            se[j] = odd ? 1.f : gcq[j];
         }
-    };
-    if (fast) tiles(std::true_type{});
-    else tiles(std::false_type{});
+        // scaled tiles (the factored form's branch taken once per chunk): all
+        // three go to the block, and the factored form also keeps k * Gam,
+        // q * Gam and k / Gam in LDS for its products
+        auto tiles = [&](auto fc) {
+            constexpr bool F = decltype(fc)::value;
 #pragma unroll
-    for (int j = 0; j < CH; ++j) o.gc[CH * lane + j] = gcp[j] * gcq[j];  // the pair's (read from even blocks)
-    if (lane < C16) s.beta[lane] = lane < nval ? bf16_bits_to_f32(rb) : 0.f;  // zero on padding rows
-    wave_lds_fence();
-    // Gram block G[t][s] (lane (g, i): t = 4g + r, s = i) and the
-    // Aqk block as (K/Gam)(Q*Gam)^T (lane (g, i): s = 4g + r, t = i)
-    f32x4 gr = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-    if (fast) {
-#pragma unroll
-        for (int p = 0; p < KSTEP; ++p) {
-            const bf16x8 kdf = row_frag2(s.a, KS, 0, 32 * p, lane);
-            const bf16x8 kbf = row_frag2(s.kb, KS, 0, 32 * p, lane);
-            const bf16x8 qdf = row_frag2(s.b, KS, 0, 32 * p, lane);
-            gr = mfma32(kdf, kbf, gr);
-            aq = mfma32(kbf, qdf, aq);
-        }
-    } else {
-        // Exact form for chunks whose decay leaves the factored range.
-        // Entry (t, s), s < t, is formed at level b = highest set bit of
-        // t ^ s: t and s then sit on either side of the reference token
-        // m = (t & ~(2b - 1)) + b - 1, and
-        //   2^{G_t - G_s} = 2^{G_t - G_m} 2^{G_m - G_s}
-        // with both factors <= 1.  Each level is one masked product over
-        // tiles whose rows are scaled against their own block's reference;
-        // entries of other levels are discarded.  The last level (b = 0)
-        // gives the diagonal of Aqk, undecayed.
-        auto level = [&](auto bi) {
-            constexpr int bl = decltype(bi)::value == 4 ? 0 : 8 >> decltype(bi)::value;
-            auto row = [&](auto tc) {
-                constexpr int t = decltype(tc)::value;
-                float ak[CH], aqv[CH], bk[CH];
+            for (int t = 0; t < C16; ++t) {
+                float kd[CH], qd[CH], ke[CH], kb[CH];
 #pragma unroll
                 for (int j = 0; j < CH; ++j) {
                     const float kv = chan(rk[t], j), qv = chan(rq[t], j);
-                    float rf = 1.f, cf = 1.f;
-                    if constexpr (bl != 0) {
-                        constexpr int m = (t & ~(2 * bl - 1)) + bl - 1;
-                        if constexpr ((t & bl) != 0) {
-                            rf = exp2_fast(G[t][j] - G[m][j]);
-                            cf = 0.f;
-                        } else {
-                            rf = 0.f;
-                            cf = exp2_fast(G[m][j] - G[t][j]);
-                        }
+                    const float e1 = exp2_fast(G[t][j]);
+                    kd[j] = kv * e1;
+                    qd[j] = qv * e1;
+                    if constexpr (F) {  // 2^{-G} is finite here: 2^{G_C - G} as a product
+                        const float eb = exp2_fast(-G[t][j]);
+                        kb[j] = kv * eb;
+                        ke[j] = kv * (gcp[j] * eb);
+                    } else {
+                        kb[j] = 0.f;
+                        ke[j] = kv * exp2_fast(gcx[j] - G[t][j]);
                     }
-                    ak[j] = kv * rf;
-                    aqv[j] = qv * rf;
-                    bk[j] = kv * cf;
                 }
-                if constexpr (bl != 0) put(s.a, KS, t, ak);
-                put(s.b, KS, t, aqv);
-                put(s.kb, KS, t, bk);
-            };
-            static_for<C16>(row);
-            wave_lds_fence();
-            f32x4 g2 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+                float kdo[CH], qdo[CH], keo[CH];
+#pragma unroll
+                for (int j = 0; j < CH; ++j) {
+                    kdo[j] = kd[j] * sdq[j];
+                    qdo[j] = qd[j] * sdq[j];
+                    keo[j] = ke[j] * se[j];
+                }
+                put(o.kd, DK, t, kdo);
+                put(o.qd, DK, t, qdo);
+                put(o.ke, DK, t, keo);
+                if (!odd) put(s.k0, KS, t, ke);  // local k * Gam_C / Gam for the odd sub-chunk's cross blocks
+                if constexpr (F) {
+                    put(s.a, KS, t, kd);
+                    put(s.b, KS, t, qd);
+                    put(s.kb, KS, t, kb);
+                }
+            }
+        };
+        if (fast) tiles(std::true_type{});
+        else tiles(std::false_type{});
+#pragma unroll
+        for (int j = 0; j < CH; ++j) o.gc[CH * lane + j] = gcp[j] * gcq[j];  // the pair's (read from even blocks)
+        if (lane < C16) s.beta[lane] = lane < nval ? bf16_bits_to_f32(rb) : 0.f;  // zero on padding rows
+        wave_lds_fence();
+        // Gram block G[t][s] (lane (g, i): t = 4g + r, s = i) and the
+        // Aqk block as (K/Gam)(Q*Gam)^T (lane (g, i): s = 4g + r, t = i)
+        f32x4 gr = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+        if (fast) {
 #pragma unroll
             for (int p = 0; p < KSTEP; ++p) {
+                const bf16x8 kdf = row_frag2(s.a, KS, 0, 32 * p, lane);
                 const bf16x8 kbf = row_frag2(s.kb, KS, 0, 32 * p, lane);
-                if constexpr (bl != 0) g2 = mfma32(row_frag2(s.a, KS, 0, 32 * p, lane), kbf, g2);
-                a2 = mfma32(kbf, row_frag2(s.b, KS, 0, 32 * p, lane), a2);
+                const bf16x8 qdf = row_frag2(s.b, KS, 0, 32 * p, lane);
+                gr = mfma32(kdf, kbf, gr);
+                aq = mfma32(kbf, qdf, aq);
             }
+        } else {
+            // Exact form for chunks whose decay leaves the factored range.
+            // Entry (t, s), s < t, is formed at level b = highest set bit of
+            // t ^ s: t and s then sit on either side of the reference token
+            // m = (t & ~(2b - 1)) + b - 1, and
+            //   2^{G_t - G_s} = 2^{G_t - G_m} 2^{G_m - G_s}
+            // with both factors <= 1.  Each level is one masked product over
+            // tiles whose rows are scaled against their own block's reference;
+            // entries of other levels are discarded.  The last level (b = 0)
+            // gives the diagonal of Aqk, undecayed.
+            auto level = [&](auto bi) {
+                constexpr int bl = decltype(bi)::value == 4 ? 0 : 8 >> decltype(bi)::value;
+                auto row = [&](auto tc) {
+                    constexpr int t = decltype(tc)::value;
+                    float ak[CH], aqv[CH], bk[CH];
+#pragma unroll
+                    for (int j = 0; j < CH; ++j) {
+                        const float kv = chan(rk[t], j), qv = chan(rq[t], j);
+                        float rf = 1.f, cf = 1.f;
+                        if constexpr (bl != 0) {
+                            constexpr int m = (t & ~(2 * bl - 1)) + bl - 1;
+                            if constexpr ((t & bl) != 0) {
+                                rf = exp2_fast(G[t][j] - G[m][j]);
+                                cf = 0.f;
+                            } else {
+                                rf = 0.f;
+                                cf = exp2_fast(G[m][j] - G[t][j]);
+                            }
+                        }
+                        ak[j] = kv * rf;
+                        aqv[j] = qv * rf;
+                        bk[j] = kv * cf;
+                    }
+                    if constexpr (bl != 0) put(s.a, KS, t, ak);
+                    put(s.b, KS, t, aqv);
+                    put(s.kb, KS, t, bk);
+                };
+                static_for<C16>(row);
+                wave_lds_fence();
+                f32x4 g2 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < KSTEP; ++p) {
+                    const bf16x8 kbf = row_frag2(s.kb, KS, 0, 32 * p, lane);
+                    if constexpr (bl != 0) g2 = mfma32(row_frag2(s.a, KS, 0, 32 * p, lane), kbf, g2);
+                    a2 = mfma32(kbf, row_frag2(s.b, KS, 0, 32 * p, lane), a2);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int x = (4 * lg + r) ^ lc;  // same for both layouts
+                    if constexpr (bl != 0) {
+                        const bool at = x >= bl && x < 2 * bl;
+                        if (at && ((4 * lg + r) & bl)) gr[r] = g2[r];  // t = 4g + r, s = i
+                        if (at && (lc & bl)) aq[r] = a2[r];            // s = 4g + r, t = i
+                    } else if (x == 0) {
+                        aq[r] = a2[r];
+                    }
+                }
+                wave_lds_fence();  // tiles are rewritten by the next level
+                __builtin_amdgcn_sched_barrier(0);  // one level's values live at a time
+            };
+            static_for<5>(level);
+        }
+        // L = beta_t G (s < t) by column; Aqk (s <= t)
+        {
+            const float4 bt4 = *reinterpret_cast<const float4 *>(&s.beta[4 * lg]);
+            const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+            float l[4];
+            f32x4 x;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int x = (4 * lg + r) ^ lc;  // same for both layouts
-                if constexpr (bl != 0) {
-                    const bool at = x >= bl && x < 2 * bl;
-                    if (at && ((4 * lg + r) & bl)) gr[r] = g2[r];  // t = 4g + r, s = i
-                    if (at && (lc & bl)) aq[r] = a2[r];            // s = 4g + r, t = i
-                } else if (x == 0) {
-                    aq[r] = a2[r];
-                }
+                l[r] = lc < 4 * lg + r ? bt[r] * gr[r] : 0.f;
+                x[r] = 4 * lg + r <= lc ? aq[r] : 0.f;
             }
-            wave_lds_fence();  // tiles are rewritten by the next level
-            __builtin_amdgcn_sched_barrier(0);  // one level's values live at a time
-        };
-        static_for<5>(level);
-    }
-    // L = beta_t G (s < t) by column; Aqk (s <= t)
-    {
-        const float4 bt4 = *reinterpret_cast<const float4 *>(&s.beta[4 * lg]);
-        const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
-        float l[4];
-        f32x4 x;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            l[r] = lc < 4 * lg + r ? bt[r] * gr[r] : 0.f;
-            x[r] = 4 * lg + r <= lc ? aq[r] : 0.f;
+            *reinterpret_cast<float4 *>(&s.lt[lc * KLTS + 4 * lg]) = make_float4(l[0], l[1], l[2], l[3]);
+            o.aqk[lane] = bf4(x);
         }
-        *reinterpret_cast<float4 *>(&s.lt[lc * KLTS + 4 * lg]) = make_float4(l[0], l[1], l[2], l[3]);
-        o.aqk[lane] = bf4(x);
-    }
-    wave_lds_fence();
-    // D = (I + L)^{-1}: forward substitution in fp32, lane = (column, row quad)
-    {
-        const int col = lane >> 2, q = lane & 3;
-        float x[4];
+        wave_lds_fence();
+        // D = (I + L)^{-1}: forward substitution in fp32, lane = (column, row quad)
+        {
+            const int col = lane >> 2, q = lane & 3;
+            float x[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == col) ? 1.f : 0.f;
-        auto sweep = [&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            const float4 l4 = *reinterpret_cast<const float4 *>(&s.lt[j * KLTS + 4 * q]);
-            const float xj = quad_bcast<j / 4>(x[j % 4]);
-            x[0] = fmaf(-l4.x, xj, x[0]);
-            x[1] = fmaf(-l4.y, xj, x[1]);
-            x[2] = fmaf(-l4.z, xj, x[2]);
-            x[3] = fmaf(-l4.w, xj, x[3]);
-        };
-        static_for<15>(sweep);
-        const float bcol = s.beta[col];
-        __bf16 *dt = reinterpret_cast<__bf16 *>(&s.dt[0]);
+            for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == col) ? 1.f : 0.f;
+            auto sweep = [&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                const float4 l4 = *reinterpret_cast<const float4 *>(&s.lt[j * KLTS + 4 * q]);
+                const float xj = quad_bcast<j / 4>(x[j % 4]);
+                x[0] = fmaf(-l4.x, xj, x[0]);
+                x[1] = fmaf(-l4.y, xj, x[1]);
+                x[2] = fmaf(-l4.z, xj, x[2]);
+                x[3] = fmaf(-l4.w, xj, x[3]);
+            };
+            static_for<15>(sweep);
+            const float bcol = s.beta[col];
+            __bf16 *dt = reinterpret_cast<__bf16 *>(&s.dt[0]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dt[((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3)] = static_cast<__bf16>(x[r] * bcol);
-    }
-    wave_lds_fence();
-    o.dt[lane] = s.dt[lane];
-    if (!odd) return;
-    // Cross blocks of the pair (odd sub-chunk t, even sub-chunk s): each
-    // entry sum_c x_tc k_sc 2^{G_tc - G_sc} splits at the last even token
-    // into 2^{G_tc} (this sub-chunk's own decay) and 2^{Gp_15c - Gp_sc} (the
-    // even one's decay to its end), both at most 1, so the local tiles give
-    // it exactly:  G_10 = (K_1 * Gam_1) (K_0 * Gam_C0 / Gam_0)^T and
-    // Aqk_10 = (Q_1 * Gam_1) (K_0 * Gam_C0 / Gam_0)^T.
-    wave_lds_fence();
-#pragma unroll
-    for (int t = 0; t < C16; ++t) {
-        float kd[CH], qd[CH];
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const float e1 = exp2_fast(G[t][j]);
-            kd[j] = chan(rk[t], j) * e1;
-            qd[j] = chan(rq[t], j) * e1;
+            for (int r = 0; r < 4; ++r) dt[((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3)] = static_cast<__bf16>(x[r] * bcol);
         }
-        put(s.a, KS, t, kd);
-        put(s.b, KS, t, qd);
-    }
-    wave_lds_fence();
-    f32x4 g10 = {0.f, 0.f, 0.f, 0.f}, a10 = {0.f, 0.f, 0.f, 0.f};
+        wave_lds_fence();
+        o.dt[lane] = s.dt[lane];
 #pragma unroll
-    for (int p = 0; p < KSTEP; ++p) {
-        const bf16x8 k0f = row_frag2(s.k0, KS, 0, 32 * p, lane);
-        g10 = mfma32(row_frag2(s.a, KS, 0, 32 * p, lane), k0f, g10);  // lane (g, i): [t = 4g + r][s = i]
-        a10 = mfma32(k0f, row_frag2(s.b, KS, 0, 32 * p, lane), a10);  // lane (g, i): [s = 4g + r][t = i]
+        for (int j = 0; j < CH; ++j) gprev[j] = gcx[j];
+        if (!odd) continue;
+        // Cross blocks of the pair (odd sub-chunk t, even sub-chunk s): each
+        // entry sum_c x_tc k_sc 2^{G_tc - G_sc} splits at the last even token
+        // into 2^{G_tc} (this sub-chunk's own decay) and 2^{Gp_15c - Gp_sc} (the
+        // even one's decay to its end), both at most 1, so the local tiles give
+        // it exactly:  G_10 = (K_1 * Gam_1) (K_0 * Gam_C0 / Gam_0)^T and
+        // Aqk_10 = (Q_1 * Gam_1) (K_0 * Gam_C0 / Gam_0)^T.
+        wave_lds_fence();
+#pragma unroll
+        for (int t = 0; t < C16; ++t) {
+            float kd[CH], qd[CH];
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const float e1 = exp2_fast(G[t][j]);
+                kd[j] = chan(rk[t], j) * e1;
+                qd[j] = chan(rq[t], j) * e1;
+            }
+            put(s.a, KS, t, kd);
+            put(s.b, KS, t, qd);
+        }
+        wave_lds_fence();
+        f32x4 g10 = {0.f, 0.f, 0.f, 0.f}, a10 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < KSTEP; ++p) {
+            const bf16x8 k0f = row_frag2(s.k0, KS, 0, 32 * p, lane);
+            g10 = mfma32(row_frag2(s.a, KS, 0, 32 * p, lane), k0f, g10);  // lane (g, i): [t = 4g + r][s = i]
+            a10 = mfma32(k0f, row_frag2(s.b, KS, 0, 32 * p, lane), a10);  // lane (g, i): [s = 4g + r][t = i]
+        }
+        o.ax[lane] = bf4(a10);
+        // M_10 = -T_11 G_10 with T_11 = (I + L_11)^{-1} diag(beta_1), formed
+        // transposed (A = -G_10^T from the accumulator, B = T_11^T from its
+        // A-operand fragment) so it comes out in A-operand order
+        o.mx[lane] = bf4(mfma16(bf4(-g10), s.dt[lane], f32x4{0.f, 0.f, 0.f, 0.f}));
     }
-    o.ax[lane] = bf4(a10);
-    // M_10 = -T_11 G_10 with T_11 = (I + L_11)^{-1} diag(beta_1), formed
-    // transposed (A = -G_10^T from the accumulator, B = T_11^T from its
-    // A-operand fragment) so it comes out in A-operand order
-    o.mx[lane] = bf4(mfma16(bf4(-g10), s.dt[lane], f32x4{0.f, 0.f, 0.f, 0.f}));
 }
 
 // U of a pair of sub-chunks from the bf16 state at the pair start:
@@ -733,7 +720,8 @@ bool kda_chunked_supported(const DeltaArgs &a) {
 template <int DK, int NVT>
 static hipError_t launch_dk(const DeltaArgs &a, hipStream_t stream) {
     const unsigned blocks = static_cast<unsigned>(a.B * a.H * (a.dv / KdaShape<NVT>::BV));
-    const int64_t tasks = a.B * a.H * 2 * ((a.T + 2 * C16 - 1) / (2 * C16));  // sub-chunks, pairs complete
+    const int64_t pairs = a.B * a.H * ((a.T + 2 * C16 - 1) / (2 * C16));  // derivation waves
+    const int64_t tasks = 2 * pairs;                                        // blocks (sub-chunks)
     if (tasks > 0x7fffffff) return hipErrorInvalidValue;
     KdaBlock<DK> *der = nullptr;
     if (tasks > 0) {
@@ -741,7 +729,7 @@ static hipError_t launch_dk(const DeltaArgs &a, hipStream_t stream) {
         const hipError_t e = derived_workspace(stream, static_cast<size_t>(tasks) * sizeof(KdaBlock<DK>), &ws);
         if (e != hipSuccess) return e;
         der = static_cast<KdaBlock<DK> *>(ws);
-        kda_derive_kernel<DK><<<static_cast<unsigned>(tasks), 64, 0, stream>>>(a, der);
+        kda_derive_kernel<DK><<<static_cast<unsigned>(pairs), 64, 0, stream>>>(a, der);
     }
     kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a, der);
     return hipGetLastError();
