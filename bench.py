@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="batch rows timed on the CPU oracle (default: the whole workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of untimed steps before the warm-up steps, so the device clocks settle")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of the plain device copy timed beside the scan (0 = skip)")
     args = ap.parse_args()
@@ -189,6 +191,17 @@ def main():
                         erase_b=g.get("erase_b"), write_w=g.get("write_w"), algo=args.algo,
                         out=o[0], state_out=o[1])
 
+    # Clock settling: the device raises its clocks only after some
+    # milliseconds of sustained work, so before the W warm-up steps the step
+    # runs untimed for --settle-s seconds (synchronising every few steps, so
+    # the time is device time, not host submission time).
+    t_settle = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(8):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -275,6 +288,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle_s,
         "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
