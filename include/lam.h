@@ -30,12 +30,27 @@
  *   for VLA's q, k, v, p, out); per-token scalars (beta, scalar alpha)
  *   [B,T,H]; states [B,H,dv,dk] (VLA: A and S [B,H,d,d]).
  *   dtype: every per-token stream and `out` share one storage dtype
- *   (LAM_F32 or LAM_BF16); states are always fp32; all arithmetic is fp32.
+ *   (LAM_F32 or LAM_BF16); states are always fp32, and so are every
+ *   accumulation and every element-wise step.  The chunked delta-rule
+ *   schedule on LAM_BF16 storage feeds bf16 operands to the matrix cores
+ *   (products accumulated in fp32); all other schedules compute in fp32.
  *   alpha is the decay itself, in [0, 1]; beta, erase_b, write_w are used as
  *   given (gate squashing happens upstream).  Delta-rule q and k are used as
  *   given (normalise upstream); VLA takes raw q and k.
- *   Pointers: device memory owned by the caller.  The library allocates no
- *   device memory, keeps no pointer after returning, and uses no workspace.
+ *   Pointers: device memory owned by the caller; the library keeps none of
+ *   them after returning.
+ *   Workspace: the chunked delta-rule schedule (LAM_ALGO_CHUNKED on
+ *   LAM_BF16 storage, or AUTO when it picks it) writes state-independent
+ *   per-chunk blocks to a device workspace between its two kernels: 7,936 B
+ *   per (b, h, 64-token chunk) for DeltaNet, Gated DeltaNet and Gated
+ *   DeltaNet-2 at dk = 128, and 14,848 B per (b, h, 16-token sub-chunk,
+ *   counted in whole pairs) for Kimi Delta at dk = 128.  The library owns it:
+ *   one buffer per (device, stream), allocated with hipMalloc on that
+ *   stream's first such call and grown when a call needs more (growing waits
+ *   for the stream's queued work, then frees the old buffer), kept until the
+ *   process ends.  Calls on one stream run in order and share it; calls on
+ *   different streams use different buffers.  An allocation failure returns
+ *   LAM_ERR_HIP.  The other schedules use no memory beyond their arguments.
  *   A NULL initial state means zero memory (VLA: A = I, S = 0); a NULL
  *   final-state pointer means the final state is not written.  A final-state
  *   buffer may be the same buffer as its initial state; `out` must not
