@@ -120,10 +120,13 @@ def test_bitwise_reproducible(variant):
 
 
 @pytest.mark.parametrize("variant,T,dk", [("gdn", 1024, 128), ("gdn", 1093, 64), ("deltanet", 1100, 128),
-                                          ("gdn2", 1030, 128), ("gdn", 2047, 128)])
+                                          ("gdn2", 1030, 128), ("gdn", 2047, 128),
+                                          ("kda", 1280, 128), ("kda", 1297, 64)])
 def test_chunked_long_sequences(variant, T, dk):
     """Sixteen chunks and more, even and odd chunk counts, a ragged tail and
-    a carried-in state; two runs agree bit for bit."""
+    a carried-in state; two runs agree bit for bit.  Kimi Delta: 40 pairs of
+    16-token sub-chunks, and 41 pairs whose last ends in a padded odd
+    sub-chunk, many times round the producers' slot ring."""
     w = _w(variant, "bf16", 1, T, 2, dk, 64, seed=7700 + T)
     x = I.make_inputs(w)
     s0 = (np.random.default_rng(T).standard_normal((1, 2, 64, dk)) * 0.2).astype(np.float64)
