@@ -121,17 +121,15 @@ struct WyLds {
 // rows past the end become zeros (a bitwise mask keeps the registers out of
 // the select-of-aggregates form that lands them in scratch)
 __device__ __forceinline__ uint4 masked(uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); }
-// elementwise product of eight bf16 pairs, rounded to bf16 (nearest even)
+// elementwise product of eight bf16 pairs, rounded to bf16 (nearest even):
+// widened exactly, multiplied in fp32, narrowed by the packed conversion
 __device__ __forceinline__ uint4 mul8(uint4 x, uint4 y) {
-    const uint32_t xa[4] = {x.x, x.y, x.z, x.w}, ya[4] = {y.x, y.y, y.z, y.w};
-    uint32_t r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float lo = bf16_bits_to_f32(static_cast<uint16_t>(xa[j])) * bf16_bits_to_f32(static_cast<uint16_t>(ya[j]));
-        const float hi = bf16_bits_to_f32(static_cast<uint16_t>(xa[j] >> 16)) *
-                         bf16_bits_to_f32(static_cast<uint16_t>(ya[j] >> 16));
-        r[j] = static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
-    }
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    typedef float f32x8 __attribute__((ext_vector_type(8)));
+    const bf16x8 xb = __builtin_bit_cast(bf16x8, u32x4v{x.x, x.y, x.z, x.w});
+    const bf16x8 yb = __builtin_bit_cast(bf16x8, u32x4v{y.x, y.y, y.z, y.w});
+    const f32x8 pr = __builtin_convertvector(xb, f32x8) * __builtin_convertvector(yb, f32x8);
+    const u32x4v r = __builtin_bit_cast(u32x4v, __builtin_convertvector(pr, bf16x8));
     return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
