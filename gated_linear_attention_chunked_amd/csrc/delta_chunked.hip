@@ -632,9 +632,9 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
         constexpr int NDP = (kDerPieces + 255) / 256;
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         const u32x4 *gder = reinterpret_cast<const u32x4 *>(der + static_cast<int64_t>(head) * nchunks);
-        // NS staging sets: loads run NS chunks ahead.  Gated DeltaNet-2 stages
-        // two more streams (erase and write gates) and keeps one set.
-        constexpr int NS = kGates2 ? 1 : 2;
+        // Two staging sets: loads run two chunks ahead (Gated DeltaNet-2
+        // stages two more streams, the erase and write gates, in each set).
+        constexpr int NS = 2;
         constexpr int NQKG = kGates2 ? NQK : 1;
         const uint16_t *geb = static_cast<const uint16_t *>(a.erase_b);
         const uint16_t *gww = static_cast<const uint16_t *>(a.write_w);
