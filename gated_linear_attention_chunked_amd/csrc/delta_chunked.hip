@@ -21,7 +21,7 @@
 //          It forms everything that does not depend on the state (the
 //          inverses of the diagonal blocks of I + L, the off-diagonal coupling
 //          blocks and the gate prefix sums) from the keys, decays and betas
-//          alone, and writes it to a workspace block of 7.75 KB per chunk (a
+//          alone, and writes it to a workspace block of 5.75 KB per chunk (a
 //          device buffer the library keeps per stream).
 //   scan:  one workgroup of 8 waves per (b, h, 32-wide slice of dv); rows of
 //          W are independent, so slices never communicate.  Waves are split
@@ -87,7 +87,6 @@ constexpr int LTS = 20;    // column stride (floats) of the fp32 diagonal blocks
 // block per (sequence, head, chunk); the scan copies it into LDS unchanged.
 struct DerBlock {
     bf16x4 dtil[4][64];        // D_i diag(beta)_i, A-operand order
-    bf16x4 dhn[4][64];         // -D_i diag(beta gamma)_i
     bf16x4 mij[NLB][64];       // M_ij
     float gam[C];              // gamma_t
     float sc[C];               // gamma_C / gamma_t
@@ -343,17 +342,15 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
             for (int r = 0; r < 4; ++r) x[r] = fmaf(-lj[r], xj, x[r]);
         };
         static_for<15>(sweep);
-        // D diag(beta) and -D diag(beta gamma): element (row, col) goes to
-        // A-operand lane (col / 4) * 16 + row, slot col % 4
+        // D diag(beta): element (row, col) goes to A-operand lane
+        // (col / 4) * 16 + row, slot col % 4 (the scan scales its columns by
+        // -gamma for the state term)
         const float bcol = s.beta[16 * I + col];
-        const float bgcol = -bcol * (kDecay ? exp2_fast(s.g[16 * I + col]) : 1.f);
         __bf16 *dt = reinterpret_cast<__bf16 *>(&D.dtil[I][0]);
-        __bf16 *dh = reinterpret_cast<__bf16 *>(&D.dhn[I][0]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int e = ((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3);
             dt[e] = static_cast<__bf16>(x[r] * bcol);
-            dh[e] = static_cast<__bf16>(x[r] * bgcol);
         }
         // M_Ij = -D~_I G~_Ij, computed transposed (A = -G~^T from the
         // accumulators, B = D~_I^T from its A-operand fragment) so the result
@@ -461,7 +458,13 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                 for (int i = 0; i < 4; ++i) {
                     vb[i] = col_gather4(R.v, Lds::VS, 16 * i, 16 * vt, lane);
                     dt[i] = D.dtil[i][lane];
-                    dh[i] = D.dhn[i][lane];
+                    // -D_i diag(beta gamma)_i: D~_i's columns 16i + 4lg .. +3 times -gamma
+                    if constexpr (kDecay) {
+                        const float4 gm = *reinterpret_cast<const float4 *>(&D.gam[16 * i + 4 * lg]);
+                        dh[i] = bf4(__builtin_convertvector(dt[i], f32x4) * f32x4{-gm.x, -gm.y, -gm.z, -gm.w});
+                    } else {
+                        dh[i] = -dt[i];
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < NLB; ++i) mj[i] = D.mij[i][lane];
