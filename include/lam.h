@@ -41,7 +41,7 @@
  *   them after returning.
  *   Workspace: the chunked delta-rule schedule (LAM_ALGO_CHUNKED on
  *   LAM_BF16 storage, or AUTO when it picks it) writes state-independent
- *   per-chunk blocks to a device workspace between its two kernels: 7,936 B
+ *   per-chunk blocks to a device workspace between its two kernels: 5,888 B
  *   per (b, h, 64-token chunk) for DeltaNet, Gated DeltaNet and Gated
  *   DeltaNet-2 at dk = 128, and 14,848 B per (b, h, 16-token sub-chunk,
  *   counted in whole pairs) for Kimi Delta at dk = 128.  The library owns it:
