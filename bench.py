@@ -107,25 +107,31 @@ def cpu_threads(chains: int) -> int:
     return max(1, min(avail, cap, chains))
 
 
-def cpu_baseline(w, x, batch_rows: int):
+def cpu_baseline(w, x, batch_rows: int, min_seconds: float):
     """The fp64 oracle on the first `batch_rows` batch rows (all heads, all
-    tokens) of the same inputs; tokens/s scaled to those B*T tokens."""
+    tokens) of the same inputs, repeated until at least `min_seconds` of
+    wall time have passed (one pass of the whole workload takes well under a
+    second on a many-core host); tokens/s over all repetitions."""
     import oracle
 
     sl = {k: v[:batch_rows] for k, v in x.items()}
     chains = batch_rows * w.H
     th = cpu_threads(chains)
-    t0 = time.perf_counter()
-    if w.variant == "vla":
-        oracle.vla_forward(sl["q"], sl["k"], sl["v"], sl["p"], nthreads=th)
-    else:
-        oracle.delta_forward(w.variant, sl["q"], sl["k"], sl["v"], sl["beta"], alpha=sl.get("alpha"),
-                             erase_b=sl.get("erase_b"), write_w=sl.get("write_w"), nthreads=th)
-    dt = time.perf_counter() - t0
-    return {"value": batch_rows * w.T / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        if w.variant == "vla":
+            oracle.vla_forward(sl["q"], sl["k"], sl["v"], sl["p"], nthreads=th)
+        else:
+            oracle.delta_forward(w.variant, sl["q"], sl["k"], sl["v"], sl["beta"], alpha=sl.get("alpha"),
+                                 erase_b=sl.get("erase_b"), write_w=sl.get("write_w"), nthreads=th)
+        dt += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * batch_rows * w.T / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
             "sample": f"fp64 token-by-token oracle on batch rows 0..{batch_rows - 1} of {w.B} "
                       f"(all {w.H} heads, all {w.T} tokens: {chains} chains, "
-                      f"{batch_rows * w.T} tokens) of the same inputs; {dt:.2f} s wall"}
+                      f"{batch_rows * w.T} tokens) of the same inputs, {reps} pass{'es' if reps > 1 else ''} "
+                      f"in {dt:.1f} s wall"}
 
 
 def main():
@@ -139,6 +145,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="batch rows timed on the CPU oracle (default: the whole workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle baseline until this much wall time has passed")
     ap.add_argument("--settle-s", type=float, default=0.3,
                     help="seconds of untimed steps before the warm-up steps, so the device clocks settle")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
@@ -290,7 +298,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         rows = min(w.B, args.cpu_rows or w.B)
-        cpu = cpu_baseline(w, x, rows)
+        cpu = cpu_baseline(w, x, rows, args.cpu_seconds)
 
     line = {
         "metric": "gated delta-rule fwd tokens/s, B8 T4096 H8 d128; % of HBM/MFMA roofline"
