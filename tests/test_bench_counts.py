@@ -1,0 +1,46 @@
+"""The roofline denominators bench.py reports: algorithmic bytes (every input
+read once, y and the final state written once, at the storage width) and
+algorithmic flops (7 dk dv per token-head for the delta rule, 12 d^2 for
+VLA), checked against counts worked out by hand from each workload's shapes.
+CPU only."""
+import bench
+from gated_linear_attention_chunked_amd import inputs as I
+
+# (bytes, flops) per workload, from its shapes:
+#   bytes = B*T*H * (per-token-head bytes) + final state(s) in fp32
+#   flops = B*T*H * 7*dk*dv (delta rule) or 12*d^2 (VLA)
+EXPECTED = {
+    # fp32: q, k, v, out 4 x 32 x 4 B + beta 4 B = 516 B x 512 token-heads, + 1x2x32x32x4 B state
+    "deltanet_f32_B1_T256_H2_d32": (516 * 512 + 8192, 7 * 32 * 32 * 512),
+    # bf16: q, k, v, out 4 x 128 x 2 B + alpha 2 + beta 2 = 1028 B x 262,144, + 8x8x128x128x4 B
+    "gdn_bf16_B8_T4096_H8_d128": (273_678_336, 30_064_771_072),
+    # bf16: 1028 + per-channel alpha 256 - scalar alpha 2 = 1282 B x 524,288, + 2x8x128x128x4 B
+    "kda_bf16_B2_T32768_H8_d128": (673_185_792, 60_129_542_144),
+    # bf16: 1028 + erase 256 + write 256 = 1540 B x 262,144, + state
+    "gdn2_bf16_B8_T4096_H8_d128": (407_896_064, 30_064_771_072),
+    # fp32: q, k, v, p, out 5 x 32 x 4 B = 640 B x 131,072, + A and S 2 x 4x8x32x32x4 B
+    "vla_f32_B4_T4096_H8_d32": (84_148_224, 12 * 32 * 32 * 131_072),
+    # fp32: 5 x 96 x 4 = 1920 B x 131,072, + 2 x 4x8x96x96x4 B
+    "vla_f32_B4_T4096_H8_d96": (254_017_536, 12 * 96 * 96 * 131_072),
+}
+
+
+def test_every_workload_is_counted():
+    assert set(EXPECTED) == set(I.WORKLOADS)
+
+
+def test_algorithmic_bytes_and_flops():
+    for name, (nbytes, nflops) in EXPECTED.items():
+        w = I.WORKLOADS[name]
+        assert bench.algorithmic_bytes(w) == nbytes, name
+        assert bench.algorithmic_flops(w) == nflops, name
+
+
+def test_metric_workload_is_hbm_bound_at_peak():
+    """At the published peaks the Gated DeltaNet workload's bytes take longer
+    than its flops on bf16 matrix cores (34.2 us vs 12.0 us), so its
+    roofline is HBM."""
+    w = I.WORKLOADS[I.METRIC_WORKLOAD]
+    t_hbm = bench.algorithmic_bytes(w) / (bench.HBM_PEAK_GBS * 1e9)
+    t_mfma = bench.algorithmic_flops(w) / (bench.MFMA_BF16_PEAK_TFS * 1e12)
+    assert abs(t_hbm - 34.2e-6) < 0.1e-6 and t_mfma < t_hbm
