@@ -61,15 +61,17 @@ constexpr int BV = 32;   // dv columns per workgroup
 //     M_ij = -D_i diag(beta)_i G~_ij                (Z' = the targets V)
 // so everything but Z is state-independent: the derivation kernel forms it.
 // The output's intra-chunk matrix Aqk = lower(Q K^T * Gamma) is formed by
-// the scan's output waves from the query and key rows they already hold.
+// the scan's output waves from the staged query and key rows, each the
+// blocks of its own token rows.
 //
 // Pipelined scan: 8 waves per workgroup, two per SIMD, in three roles.
 //   carry  (waves 0-1, one 16-column tile each): Z = E S^T on MFMA, the
 //          block solve above on 16x16x16 MFMA (a four-link chain), publish U,
 //          then the state update accumulated in registers.
-//   output (waves 2-3, same tiles): Q S^T from the carry's bf16 state and
-//          Aqk from the staged rows, then Y = diag(gamma) Q S^T + Aqk U once
-//          U is published; stores y.
+//   output (waves 2-3): token row tiles {0, 3} and {1, 2} for both value
+//          tiles: Q S^T from the carries' bf16 states and the Aqk blocks of
+//          their rows from the staged rows, then Y = diag(gamma) Q S^T + Aqk U
+//          once both U are published; stores y.
 //   producers (waves 4-7): stage chunk c+1 into LDS, its token rows and its
 //          derived block (loads issued two chunks ahead).
 // All eight waves meet at one LDS barrier per chunk; the hand-offs inside a
@@ -112,9 +114,6 @@ struct WyLds {
     alignas(16) bf16x4 sh[2][DK / 16][64];     // bf16 state fragments per tile
     unsigned int ucount[2];                    // U publications per tile
     unsigned int scount[2];                    // state fragments consumed per tile
-    // output wave <-> output wave: halves of lower(Q K^T * Gamma)
-    alignas(16) bf16x4 aqx[2][NQB][64];
-    unsigned int acount;                       // halves published
 };
 
 // rows past the end become zeros (a bitwise mask keeps the registers out of
@@ -407,7 +406,6 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
     if (tid == 0) {
         s.ucount[0] = s.ucount[1] = 0u;
         s.scount[0] = s.scount[1] = 0u;
-        s.acount = 0u;
     }
     __syncthreads();  // counters visible before any role starts
 
@@ -436,9 +434,9 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
         }
         // The output is computed transposed (Y^T = S Q^T + U^T Aqk^T, the same
         // fragments with the operands swapped), so lane (lg, lc) holds value
-        // columns 16vt + 4lg .. +3 of token 16ti + lc: one 8-byte store per tile.
+        // columns 4lg .. +3 of a tile for token lc of a row tile: one 8-byte
+        // store per tile.
         const int64_t hdv = static_cast<int64_t>(H) * dv;
-        const uint32_t yoff = static_cast<uint32_t>(lc * hdv + v0 + 16 * vt + 4 * lg);
         auto step = [&](auto par, int c) {
             constexpr int P = decltype(par)::value;
             const typename Lds::Raw &R = s.raw[P];
@@ -498,55 +496,66 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                 lds_arrive(&s.ucount[vt], lane);
                 state_update<KT>(St, R, D, ub, KS, lane);
                 if (c + 1 < nchunks) {
-                    lds_wait(&s.scount[vt], static_cast<unsigned int>(c + 1));
+                    lds_wait(&s.scount[vt], static_cast<unsigned int>(2 * (c + 1)));  // both output waves
                     publish_state();
                 }
             } else {
+                // Output wave vt takes token row tiles {0, 3} (vt = 0) or
+                // {1, 2} (vt = 1) for both value tiles.  The lower blocks of
+                // Aqk in its two rows are five either way, and they are the
+                // only ones its rows need, so nothing passes between the
+                // output waves; each reads half of the query fragments.
+                bf16x8 bS0[KSTEP], bS1[KSTEP];
 #pragma unroll
-                for (int p = 0; p < KSTEP; ++p) bS[p] = cat8(s.sh[vt][2 * p][lane], s.sh[vt][2 * p + 1][lane]);
-                lds_arrive(&s.scount[vt], lane);  // the carry may overwrite sh from here on
-                // Q S^T (four row tiles), and the lower blocks (i, j <= i) of
-                // K Q^T from the same query fragments.  The two output waves
-                // split those blocks by key block j (j in {0, 3} and
-                // j in {1, 2}, five blocks each) and swap halves through LDS.
-                // Block (i, j) comes out with lane (lg, lc) holding
-                // [s = 16j + 4lg + r][t = 16i + lc], the B-operand order of
-                // the product with U^T below.
-                f32x4 xq[4];
-                bf16x4 aq[NQB];
-                auto own_half = [&](auto half) {
-                    constexpr int J0 = decltype(half)::value ? 1 : 0, J1 = decltype(half)::value ? 2 : 3;
-                    auto mine = [](int j) { return j == J0 || j == J1; };
-                    f32x4 ka[NQB];
+                for (int p = 0; p < KSTEP; ++p) {
+                    bS0[p] = cat8(s.sh[0][2 * p][lane], s.sh[0][2 * p + 1][lane]);
+                    bS1[p] = cat8(s.sh[1][2 * p][lane], s.sh[1][2 * p + 1][lane]);
+                }
+                lds_arrive(&s.scount[0], lane);  // the carries may overwrite sh from here on
+                lds_arrive(&s.scount[1], lane);
+                auto rows = [&](auto owc) {
+                    constexpr int RT[2] = {decltype(owc)::value ? 1 : 0, decltype(owc)::value ? 2 : 3};
+                    // Q S^T for both value tiles, and the blocks (i, j <= i) of
+                    // K Q^T in rows i = RT[r]; block (i, j) comes out with lane
+                    // (lg, lc) holding [s = 16j + 4lg + r][t = 16i + lc], the
+                    // B-operand order of the product with U^T below
+                    f32x4 xq[2][2], ka[2][4];
 #pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) xq[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int r = 0; r < 2; ++r)
 #pragma unroll
-                    for (int i = 0; i < NQB; ++i) ka[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int p = 0; p < KSTEP; ++p) {
-                        bf16x8 qf[4], kq[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            qf[i] = row_frag2(R.q, KS, 16 * i, 32 * p, lane);
-                            if (mine(i)) kq[i] = row_frag2(R.k, KS, 16 * i, 32 * p, lane);
+                        for (int j = 0; j < 4; ++j) {
+                            ka[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                            if (j < 2) xq[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
                         }
 #pragma unroll
-                        for (int ti = 0; ti < 4; ++ti) xq[ti] = mfma32(bS[p], qf[ti], xq[ti]);
+                    for (int p = 0; p < KSTEP; ++p) {
+                        bf16x8 qf[2], kq[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
+                        for (int r = 0; r < 2; ++r) qf[r] = row_frag2(R.q, KS, 16 * RT[r], 32 * p, lane);
 #pragma unroll
-                            for (int j = 0; j <= i; ++j)
-                                if (mine(j)) ka[tri_block(i, j)] = mfma32(kq[j], qf[i], ka[tri_block(i, j)]);
+                        for (int j = 0; j <= RT[1]; ++j) kq[j] = row_frag2(R.k, KS, 16 * j, 32 * p, lane);
+#pragma unroll
+                        for (int r = 0; r < 2; ++r) {
+                            xq[r][0] = mfma32(bS0[p], qf[r], xq[r][0]);
+                            xq[r][1] = mfma32(bS1[p], qf[r], xq[r][1]);
+                        }
+#pragma unroll
+                        for (int r = 0; r < 2; ++r)
+#pragma unroll
+                            for (int j = 0; j <= RT[r]; ++j) ka[r][j] = mfma32(kq[j], qf[r], ka[r][j]);
                     }
                     // Aqk = lower(Q K^T * Gamma): entry (t, s) scaled by
                     // 2^(g_t - g_s), exponent clamped at 0 so masked entries
-                    // stay finite, and zero above the diagonal
+                    // stay finite, and zero above the diagonal; and the first
+                    // term of Y^T, S Q^T diag(gamma)
+                    bf16x4 aq[2][4];
+                    f32x4 y[2][2];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                    for (int r = 0; r < 2; ++r) {
+                        const int i = RT[r];
                         const float gt = kDecay ? D.g[16 * i + lc] : 0.f;
 #pragma unroll
-                        for (int j = 0; j <= i; ++j) {
-                            if (!mine(j)) continue;
+                        for (int j = 0; j <= RT[r]; ++j) {
                             float gs[4] = {0.f, 0.f, 0.f, 0.f};
                             if constexpr (kDecay) {
                                 const float4 gs4 = *reinterpret_cast<const float4 *>(&D.g[16 * j + 4 * lg]);
@@ -554,53 +563,46 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                             }
                             f32x4 x;
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const float v = kDecay ? ka[tri_block(i, j)][r] * exp2_fast(fminf(gt - gs[r], 0.f))
-                                                       : ka[tri_block(i, j)][r];
-                                x[r] = (j < i || 4 * lg + r <= lc) ? v : 0.f;
+                            for (int e = 0; e < 4; ++e) {
+                                const float v = kDecay ? ka[r][j][e] * exp2_fast(fminf(gt - gs[e], 0.f)) : ka[r][j][e];
+                                x[e] = (j < i || 4 * lg + e <= lc) ? v : 0.f;
                             }
-                            aq[tri_block(i, j)] = bf4(x);
-                            s.aqx[P][tri_block(i, j)][lane] = aq[tri_block(i, j)];
+                            aq[r][j] = bf4(x);
+                        }
+                        const float gm = D.gam[16 * i + lc];
+                        y[r][0] = xq[r][0] * gm;
+                        y[r][1] = xq[r][1] * gm;
+                    }
+                    lds_wait(&s.ucount[0], static_cast<unsigned int>(c + 1));
+                    lds_wait(&s.ucount[1], static_cast<unsigned int>(c + 1));
+                    // Y^T += U^T Aqk^T, per value tile
+                    const bf16x4 z4 = {};
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        bf16x4 ub[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ub[i] = i <= RT[1] ? s.uh[t][i][lane] : z4;
+                        const bf16x8 aU0 = cat8(ub[0], ub[1]), aU1 = cat8(ub[2], ub[3]);
+#pragma unroll
+                        for (int r = 0; r < 2; ++r) {
+                            const int i = RT[r];
+                            y[r][t] = mfma32(aU0, cat8(aq[r][0], i >= 1 ? aq[r][1] : z4), y[r][t]);
+                            if (i >= 2) y[r][t] = mfma32(aU1, cat8(aq[r][2], i >= 3 ? aq[r][3] : z4), y[r][t]);
                         }
                     }
-                    lds_arrive(&s.acount, lane);
-                    lds_wait(&s.acount, static_cast<unsigned int>(2 * (c + 1)));
+                    const int t0 = c * C;
+                    uint16_t *yo = static_cast<uint16_t *>(a.out) + tok(t0) * dv +
+                                   static_cast<uint32_t>(lc * hdv + v0 + 4 * lg);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                    for (int r = 0; r < 2; ++r)
 #pragma unroll
-                        for (int j = 0; j <= i; ++j)
-                            if (!mine(j)) aq[tri_block(i, j)] = s.aqx[P][tri_block(i, j)][lane];
+                        for (int t = 0; t < 2; ++t)
+                            if (t0 + 16 * RT[r] + lc < T)
+                                *reinterpret_cast<bf16x4 *>(yo + static_cast<uint32_t>(16 * RT[r] * hdv + 16 * t)) =
+                                    bf4(y[r][t]);
                 };
-                if (vt == 0) own_half(ic<0>{});
-                else own_half(ic<1>{});
-                lds_wait(&s.ucount[vt], static_cast<unsigned int>(c + 1));
-                bf16x4 ub[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ub[i] = s.uh[vt][i][lane];
-                // Y^T = S Q^T diag(gamma) + U^T lower(Q K^T * Gamma)^T
-                f32x4 y[4];
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) y[ti] = xq[ti] * D.gam[16 * ti + lc];
-                const bf16x8 aU0 = cat8(ub[0], ub[1]), aU1 = cat8(ub[2], ub[3]);
-                const bf16x4 z4 = {};
-                y[0] = mfma32(aU0, cat8(aq[tri_block(0, 0)], z4), y[0]);
-                y[1] = mfma32(aU0, cat8(aq[tri_block(1, 0)], aq[tri_block(1, 1)]), y[1]);
-                y[2] = mfma32(aU0, cat8(aq[tri_block(2, 0)], aq[tri_block(2, 1)]), y[2]);
-                y[2] = mfma32(aU1, cat8(aq[tri_block(2, 2)], z4), y[2]);
-                y[3] = mfma32(aU0, cat8(aq[tri_block(3, 0)], aq[tri_block(3, 1)]), y[3]);
-                y[3] = mfma32(aU1, cat8(aq[tri_block(3, 2)], aq[tri_block(3, 3)]), y[3]);
-                const int t0 = c * C;
-                uint16_t *yo = static_cast<uint16_t *>(a.out) + tok(t0) * dv + yoff;
-                if (t0 + C <= T) {
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti)
-                        *reinterpret_cast<bf16x4 *>(yo + static_cast<uint32_t>(16 * ti * hdv)) = bf4(y[ti]);
-                } else {
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti)
-                        if (t0 + 16 * ti + lc < T)
-                            *reinterpret_cast<bf16x4 *>(yo + static_cast<uint32_t>(16 * ti * hdv)) = bf4(y[ti]);
-                }
+                if (vt == 0) rows(ic<0>{});
+                else rows(ic<1>{});
             }
             lds_barrier();
         };
