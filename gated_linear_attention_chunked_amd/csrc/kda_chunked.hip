@@ -54,6 +54,8 @@
 //          loads issued four pairs ahead.
 // There is no workgroup barrier in the chunk loop: slots, U and the bf16
 // state move between roles through bounded LDS counters.
+#include <map>
+#include <mutex>
 #include <type_traits>
 
 #include "chunk_common.h"
@@ -139,7 +141,8 @@ struct KdaDeriveLds {
 // 16 tokens of a sub-chunk (one packed load per token and tensor); beta of
 // token lane (lanes 0-15).
 template <int DK>
-__global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK> *__restrict__ out) {
+__global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK> *__restrict__ out, int64_t Ts,
+                                                        int64_t tb) {
     constexpr int KS = DK + 8;
     constexpr int KSTEP = DK / 32, CH = DK / 64;
     __shared__ KdaDeriveLds<DK> s;
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
     const uint16_t *gal = static_cast<const uint16_t *>(a.alpha);
     const uint16_t *gbe = static_cast<const uint16_t *>(a.beta);
     using Pk = std::conditional_t<CH == 2, uint32_t, uint16_t>;
-    const int64_t hb = static_cast<int64_t>(b) * T * H + h;  // token index of (b, 0, h)
+    const int64_t hb = (static_cast<int64_t>(b) * Ts + tb) * H + h;  // token index of (b, tb, h)
     // rows are read clamped into the sequence (the odd sub-chunk may lie
     // wholly past its end) and padded: zero key and query, decay 1
     auto row = [&](int t) { return (hb + static_cast<int64_t>(min(t, T - 1)) * H) * DK + CH * lane; };
@@ -474,7 +477,8 @@ __device__ __forceinline__ void pair_solve(const bf16x8 (&kf0)[KSTEP], const bf1
 }
 
 template <int DK, int NVT>
-__global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArgs a, const KdaBlock<DK> *__restrict__ der) {
+__global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArgs a, const KdaBlock<DK> *__restrict__ der,
+                                                                         int64_t Ts, int64_t tb) {
     constexpr int KBV = KdaShape<NVT>::BV;
     constexpr int KS = DK + 8, VS = KBV + 8;
     constexpr int KSTEP = DK / 32, KT = DK / 16;
@@ -490,7 +494,7 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = lane >> 4, lc = lane & 15;
     const int npairs = (T + 2 * C16 - 1) / (2 * C16);  // steps of two 16-token sub-chunks
-    auto tok = [&](int t) { return (static_cast<int64_t>(b) * T + t) * H + h; };
+    auto tok = [&](int t) { return (static_cast<int64_t>(b) * Ts + tb + t) * H + h; };
 
     if (tid == 0) {
         for (int i = 0; i < NSLOT; ++i) s.ready[i] = 0u;
@@ -717,21 +721,86 @@ bool kda_chunked_supported(const DeltaArgs &a) {
     return a.variant == kKimiDelta && a.dtype == kBF16 && (a.dk == 64 || a.dk == 128) && a.dv % 16 == 0;
 }
 
+// Helper stream and events of one (device, caller stream), made on first use
+// and kept for the life of the process.
+struct KdaAux {
+    hipStream_t aux = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+static hipError_t kda_aux(hipStream_t stream, KdaAux *out) {
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, KdaAux> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    KdaAux &x = cache[{dev, stream}];
+    if (!x.aux) e = hipStreamCreateWithFlags(&x.aux, hipStreamNonBlocking);
+    if (e == hipSuccess && !x.fork) e = hipEventCreateWithFlags(&x.fork, hipEventDisableTiming);
+    if (e == hipSuccess && !x.join) e = hipEventCreateWithFlags(&x.join, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    *out = x;
+    return hipSuccess;
+}
+
+// With fewer scan workgroups than compute units, the derivation of the
+// later pairs can run on the idle units while the scan works through the
+// first ones.  The sequences are cut at a pair boundary: the derivation of
+// the first part, then its scan (ending in a state buffer); the second
+// part's derivation on a helper stream, ordered after the first derivation
+// (and so after everything queued before this call); then the second scan,
+// after it and from that state.
+constexpr int kSplitMinPairs = 1024;  // derivation tasks below which one part is kept
+constexpr int kSplitMinSteps = 64;    // pairs per sequence below which one part is kept
+
 template <int DK, int NVT>
 static hipError_t launch_dk(const DeltaArgs &a, hipStream_t stream) {
     const unsigned blocks = static_cast<unsigned>(a.B * a.H * (a.dv / KdaShape<NVT>::BV));
-    const int64_t pairs = a.B * a.H * ((a.T + 2 * C16 - 1) / (2 * C16));  // derivation waves
-    const int64_t tasks = 2 * pairs;                                        // blocks (sub-chunks)
+    const int64_t np = (a.T + 2 * C16 - 1) / (2 * C16);  // pairs per sequence
+    const int64_t pairs = a.B * a.H * np;                // derivation waves
+    const int64_t tasks = 2 * pairs;                     // blocks (sub-chunks)
     if (tasks > 0x7fffffff) return hipErrorInvalidValue;
-    KdaBlock<DK> *der = nullptr;
-    if (tasks > 0) {
-        void *ws = nullptr;
-        const hipError_t e = derived_workspace(stream, static_cast<size_t>(tasks) * sizeof(KdaBlock<DK>), &ws);
-        if (e != hipSuccess) return e;
-        der = static_cast<KdaBlock<DK> *>(ws);
-        kda_derive_kernel<DK><<<static_cast<unsigned>(pairs), 64, 0, stream>>>(a, der);
+    if (tasks == 0) {
+        kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a, nullptr, a.T, 0);
+        return hipGetLastError();
     }
-    kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a, der);
+    const bool split = blocks <= 128 && np >= kSplitMinSteps && pairs >= kSplitMinPairs;
+    const size_t der_bytes = static_cast<size_t>(tasks) * sizeof(KdaBlock<DK>);
+    const size_t st_bytes = split ? static_cast<size_t>(a.B * a.H * a.dv * a.dk) * sizeof(float) : 0;
+    void *ws = nullptr;
+    hipError_t e = derived_workspace(stream, der_bytes + st_bytes, &ws);
+    if (e != hipSuccess) return e;
+    KdaBlock<DK> *der = static_cast<KdaBlock<DK> *>(ws);
+    if (!split) {
+        kda_derive_kernel<DK><<<static_cast<unsigned>(pairs), 64, 0, stream>>>(a, der, a.T, 0);
+        kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a, der, a.T, 0);
+        return hipGetLastError();
+    }
+    KdaAux x;
+    e = kda_aux(stream, &x);
+    if (e != hipSuccess) return e;
+    // first part: a quarter of the pairs.  Its scan then lasts about as long
+    // as the second part's derivation beside it (both slow down while they
+    // share the chip); a fifth or a third of the pairs measured slower.
+    const int64_t npA = np / 4, TA = 2 * C16 * npA;
+    DeltaArgs pa = a, pb = a;
+    float *mid = reinterpret_cast<float *>(static_cast<char *>(ws) + der_bytes);
+    pa.T = TA;
+    pa.state_out = mid;
+    pb.T = a.T - TA;
+    pb.state_in = mid;
+    KdaBlock<DK> *derA = der, *derB = der + 2 * a.B * a.H * npA;
+    kda_derive_kernel<DK><<<static_cast<unsigned>(a.B * a.H * npA), 64, 0, stream>>>(pa, derA, a.T, 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipEventRecord(x.fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(x.aux, x.fork, 0)) != hipSuccess) return e;
+    kda_derive_kernel<DK><<<static_cast<unsigned>(a.B * a.H * (np - npA)), 64, 0, x.aux>>>(pb, derB, a.T, TA);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipEventRecord(x.join, x.aux)) != hipSuccess) return e;
+    kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(pa, derA, a.T, 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, x.join, 0)) != hipSuccess) return e;
+    kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(pb, derB, a.T, TA);
     return hipGetLastError();
 }
 

@@ -44,7 +44,16 @@
  *   per-chunk blocks to a device workspace between its two kernels: 5,888 B
  *   per (b, h, 64-token chunk) for DeltaNet, Gated DeltaNet and Gated
  *   DeltaNet-2 at dk = 128, and 14,848 B per (b, h, 16-token sub-chunk,
- *   counted in whole pairs) for Kimi Delta at dk = 128.  The library owns it:
+ *   counted in whole pairs) for Kimi Delta at dk = 128.  Kimi Delta with at
+ *   most 128 scan workgroups (B * H * dv / 16 <= 128), at least 64 pairs per
+ *   sequence and at least 1024 pairs in all cuts each sequence at a quarter
+ *   of its pairs: it adds a B * H * dv * dk fp32 state buffer to the
+ *   workspace, and derives the second part on a helper stream (created with
+ *   hipStreamNonBlocking at default priority, one per (device, stream), with
+ *   two events, kept until the process ends).  The helper waits for the
+ *   first part's derivation on the caller's stream, and the caller's stream
+ *   waits for the helper before the second scan, so the call stays ordered on
+ *   the caller's stream as a whole.  The library owns the workspace:
  *   one buffer per (device, stream), allocated with hipMalloc on that
  *   stream's first such call and grown when a call needs more (growing waits
  *   for the stream's queued work, then frees the old buffer), kept until the

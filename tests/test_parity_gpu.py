@@ -279,6 +279,37 @@ def test_chunked_zero_and_unit_decays(variant):
     U.check(w, got, ref, label="zero/unit decays " + variant)
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 32)])
+def test_kda_chunked_two_parts(dk, dv):
+    """Kimi Delta with few scan workgroups and many pairs: the sequence is
+    scanned in two launches chained through a state buffer, the second
+    part's derivation on a helper stream.  Every element against the oracle,
+    with a ragged tail and a carried-in state updated in place; two calls in
+    a row (the second reusing the workspace, the helper stream and its
+    events) agree bit for bit."""
+    import torch
+
+    import gated_linear_attention_chunked_amd as lam
+
+    w = _w("kda", "bf16", 1, 8213, 4, dk, dv, seed=9100 + dk)
+    x = I.make_inputs(w)
+    assert (w.T + 31) // 32 * w.B * w.H >= 1024  # the two-part launch
+    s0 = (np.random.default_rng(dk).standard_normal((1, 4, dv, dk)) * 0.2).astype(np.float64)
+    g = I.to_device(x, w.dtype, "cuda")
+    runs = []
+    for _ in range(2):
+        st = torch.from_numpy(s0.astype(np.float32)).cuda()
+        out, st2 = lam.forward("kda", g["q"], g["k"], g["v"], g["beta"], alpha=g["alpha"], state_in=st,
+                               state_out=st, algo="chunked")
+        torch.cuda.synchronize()
+        assert st2.data_ptr() == st.data_ptr()
+        runs.append((out.float().cpu().numpy().astype(np.float64), st.cpu().numpy().astype(np.float64)))
+    for a_, b_ in zip(runs[0], runs[1]):
+        assert np.array_equal(a_, b_)
+    ref = U.run_oracle(w, x, state_in=s0)
+    U.check(w, runs[0], ref, label=w.name + " two parts")
+
+
 @pytest.mark.parametrize("dk", [64, 128])
 @pytest.mark.parametrize("gate_mu", [6.0, 4.5, 3.0])
 def test_kda_chunked_strong_channel_decay(dk, gate_mu):
