@@ -107,6 +107,16 @@ def cpu_threads(chains: int) -> int:
     return max(1, min(avail, cap, chains))
 
 
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x, batch_rows: int, min_seconds: float):
     """The fp64 oracle on the first `batch_rows` batch rows (all heads, all
     tokens) of the same inputs, repeated until at least `min_seconds` of
@@ -128,6 +138,7 @@ def cpu_baseline(w, x, batch_rows: int, min_seconds: float):
         dt += time.perf_counter() - t0
         reps += 1
     return {"value": reps * batch_rows * w.T / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
             "sample": f"fp64 token-by-token oracle on batch rows 0..{batch_rows - 1} of {w.B} "
                       f"(all {w.H} heads, all {w.T} tokens: {chains} chains, "
                       f"{batch_rows * w.T} tokens) of the same inputs, {reps} pass{'es' if reps > 1 else ''} "
@@ -188,16 +199,23 @@ def main():
             outs.append((torch.empty((w.B, w.T, w.H, w.dv), dtype=g["q"].dtype, device=dev),
                          torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)))
     stream = torch.cuda.current_stream()
+    # one caller-owned workspace for every step: the steps run in order on
+    # one stream, so each may reuse it
+    if w.variant == "vla":
+        nws = lam.vla_workspace_size(w.dtype, w.B, w.T, w.H, w.dk, algo=args.algo)
+    else:
+        nws = lam.workspace_size(w.variant, w.dtype, w.B, w.T, w.H, w.dk, w.dv, algo=args.algo)
+    wsp = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
 
     def step(i):
         g, o = copies[i % len(copies)], outs[i % len(outs)]
         if w.variant == "vla":
             lam.vla_forward(g["q"], g["k"], g["v"], g["p"], algo=args.algo, out=o[0], A_out=o[1],
-                            S_out=o[2])
+                            S_out=o[2], workspace=wsp)
         else:
             lam.forward(w.variant, g["q"], g["k"], g["v"], g["beta"], alpha=g.get("alpha"),
                         erase_b=g.get("erase_b"), write_w=g.get("write_w"), algo=args.algo,
-                        out=o[0], state_out=o[1])
+                        out=o[0], state_out=o[1], workspace=wsp)
 
     # Clock settling: the device raises its clocks only after some
     # milliseconds of sustained work, so before the W warm-up steps the step
@@ -273,6 +291,8 @@ def main():
                 "mean_launch_us": mean_launch_s * 1e6,
                 "single_call_median_us": float(np.median(launch_ms)) * 1e3,
                 "single_call_min_us": float(np.min(launch_ms)) * 1e3,
+                "single_call_p90_us": float(np.percentile(launch_ms, 90)) * 1e3,
+                "workspace_bytes": nws,
                 "achieved_GBps": achieved_gbs,
                 "algorithmic_tflops": achieved_tfs})
 

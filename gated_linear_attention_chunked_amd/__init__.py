@@ -16,7 +16,9 @@ import ctypes
 import os
 import threading
 
-__all__ = ["forward", "vla_forward", "select_algo", "library", "LamError", "VARIANTS", "ALGOS", "LIB_PATH"]
+__all__ = ["forward", "vla_forward", "select_algo", "workspace_size", "vla_workspace_size",
+           "set_device_checks", "library", "LamError", "LamDeviceError", "VARIANTS", "ALGOS",
+           "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblam.so")
 VARIANTS = {"deltanet": 0, "gdn": 1, "kda": 2, "gdn2": 3}
@@ -24,8 +26,11 @@ ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
 DTYPES = {"f32": 0, "bf16": 1}
 STATUS = {0: "LAM_OK", 1: "LAM_ERR_INVALID_ARG", 2: "LAM_ERR_UNSUPPORTED", 3: "LAM_ERR_HIP"}
 
+DEVICE_WAIT_TIMEOUT = 0x1   # bit of workspace word 0 (status block)
+
 _lock = threading.Lock()
 _lib = None
+_device_checks = False
 
 
 class LamError(RuntimeError):
@@ -33,6 +38,23 @@ class LamError(RuntimeError):
         self.status = status
         super().__init__(f"{what}: {STATUS.get(status, status)} "
                          f"({library().lam_status_string(status).decode()})")
+
+
+class LamDeviceError(RuntimeError):
+    """A call's kernels reported a problem through the workspace status word."""
+
+    def __init__(self, flags: int, what: str):
+        self.flags = flags
+        super().__init__(f"{what}: device status 0x{flags:x}"
+                         + (" (a bounded in-kernel wait ran out)" if flags & DEVICE_WAIT_TIMEOUT else ""))
+
+
+def set_device_checks(on: bool) -> None:
+    """When on, every call synchronises the device after enqueueing its work
+    and raises LamDeviceError if the workspace status word is not zero (for
+    tests; it serialises the host with the device)."""
+    global _device_checks
+    _device_checks = bool(on)
 
 
 def library() -> ctypes.CDLL:
@@ -45,10 +67,16 @@ def library() -> ctypes.CDLL:
                                    "`python -m gated_linear_attention_chunked_amd.build`")
             lib = ctypes.CDLL(LIB_PATH)
             i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
-            lib.lam_forward.argtypes = [ci, ci, i64, i64, i64, i64, i64] + [vp] * 10 + [ci, vp]
+            sz = ctypes.c_size_t
+            lib.lam_forward.argtypes = [ci, ci, i64, i64, i64, i64, i64] + [vp] * 10 + [vp, sz, ci, vp]
             lib.lam_forward.restype = ci
-            lib.lam_vla_forward.argtypes = [ci, i64, i64, i64, i64] + [vp] * 9 + [ci, vp]
+            lib.lam_forward_workspace_size.argtypes = [ci, ci, i64, i64, i64, i64, i64, ci,
+                                                       ctypes.POINTER(sz)]
+            lib.lam_forward_workspace_size.restype = ci
+            lib.lam_vla_forward.argtypes = [ci, i64, i64, i64, i64] + [vp] * 9 + [vp, sz, ci, vp]
             lib.lam_vla_forward.restype = ci
+            lib.lam_vla_workspace_size.argtypes = [ci, i64, i64, i64, i64, ci, ctypes.POINTER(sz)]
+            lib.lam_vla_workspace_size.restype = ci
             lib.lam_status_string.argtypes = [ci]
             lib.lam_status_string.restype = ctypes.c_char_p
             lib.lam_abi_version.restype = ci
@@ -64,6 +92,56 @@ def select_algo(variant, dtype, T, dk, dv) -> str:
     if r < 0:
         raise ValueError("arguments the library would reject")
     return {v: k for k, v in ALGOS.items()}[r]
+
+
+def workspace_size(variant, dtype, B, T, H, dk, dv, algo="auto") -> int:
+    """Bytes of workspace ``forward`` needs for these arguments (0: none)."""
+    n = ctypes.c_size_t(0)
+    rc = library().lam_forward_workspace_size(VARIANTS[variant], DTYPES[dtype], B, T, H, dk, dv,
+                                              ALGOS[algo], ctypes.byref(n))
+    if rc != 0:
+        raise LamError(rc, "lam_forward_workspace_size")
+    return int(n.value)
+
+
+def vla_workspace_size(dtype, B, T, H, d, algo="auto") -> int:
+    """Bytes of workspace ``vla_forward`` needs for these arguments (0: none)."""
+    n = ctypes.c_size_t(0)
+    rc = library().lam_vla_workspace_size(DTYPES[dtype], B, T, H, d, ALGOS[algo], ctypes.byref(n))
+    if rc != 0:
+        raise LamError(rc, "lam_vla_workspace_size")
+    return int(n.value)
+
+
+def _workspace(nbytes, workspace, device, stream):
+    """The caller's workspace (a uint8 tensor of at least nbytes on `device`),
+    or a fresh one from torch's allocator, tied to `stream`."""
+    import torch
+
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or workspace.device != device or not workspace.is_contiguous():
+            raise ValueError(f"workspace: expected a contiguous uint8 tensor on {device}")
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace: {workspace.numel()} bytes, the call needs {nbytes}")
+        return workspace
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):  # allocated in `stream`'s order, reused only after it
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _after_call(ws, what):
+    if not _device_checks:
+        return
+    import torch
+
+    torch.cuda.synchronize()
+    if ws is not None:
+        flags = int(ws[:4].view(torch.int32).item())
+        if flags:
+            raise LamDeviceError(flags, what)
 
 
 def _ptr(t):
@@ -101,15 +179,17 @@ def _stream(stream):
 
 
 def forward(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None, state_in=None, *,
-            algo="auto", out=None, state_out=None, with_state=True, stream=None):
+            algo="auto", out=None, state_out=None, with_state=True, stream=None, workspace=None):
     """Delta-rule family forward scan.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H]; alpha: [B,T,H]
     ("gdn", "gdn2") or [B,T,H,dk] ("kda"), unused for "deltanet"; erase_b
     [B,T,H,dk] and write_w [B,T,H,dv] for "gdn2".  All per-token tensors share
     one dtype (float32 or bfloat16) and device.  state_in: fp32 [B,H,dv,dk]
-    or None (zero memory).  Returns (out [B,T,H,dv], state_out fp32
-    [B,H,dv,dk] or None).
+    or None (zero memory).  ``workspace``: optional uint8 device tensor of at
+    least ``workspace_size(...)`` bytes (default: a fresh one from torch's
+    caching allocator).  Returns (out [B,T,H,dv], state_out fp32 [B,H,dv,dk]
+    or None).
     """
     import torch
 
@@ -139,17 +219,24 @@ def forward(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None, stat
     if with_state and state_out is None:
         state_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     _check(state_out, "state_out", (B, H, dv, dk), torch.float32, dev)
+    nws = ctypes.c_size_t(0)
+    rc = library().lam_forward_workspace_size(var, _dtype_code(q), B, T, H, dk, dv, ALGOS[algo],
+                                              ctypes.byref(nws))
+    if rc != 0:
+        raise LamError(rc, "lam_forward_workspace_size")
+    ws = _workspace(int(nws.value), workspace, dev, stream)
     rc = library().lam_forward(var, _dtype_code(q), B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
                                _ptr(alpha), _ptr(erase_b), _ptr(write_w), _ptr(beta),
-                               _ptr(state_in), _ptr(out), _ptr(state_out), ALGOS[algo],
-                               _stream(stream))
+                               _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(ws),
+                               0 if ws is None else ws.numel(), ALGOS[algo], _stream(stream))
     if rc != 0:
         raise LamError(rc, "lam_forward")
+    _after_call(ws, "lam_forward")
     return out, state_out
 
 
 def vla_forward(q, k, v, p, A_in=None, S_in=None, *, algo="auto", out=None, A_out=None,
-                S_out=None, with_state=True, stream=None):
+                S_out=None, with_state=True, stream=None, workspace=None):
     """VLA forward scan on raw q, k (ELU+1 features and unit norms inside).
 
     q, k, v, p: [B,T,H,d] (float32 or bfloat16); A_in, S_in: fp32 [B,H,d,d]
@@ -173,9 +260,16 @@ def vla_forward(q, k, v, p, A_in=None, S_in=None, *, algo="auto", out=None, A_ou
             S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
     for n, t in (("A_out", A_out), ("S_out", S_out)):
         _check(t, n, (B, H, d, d), torch.float32, dev)
+    nws = ctypes.c_size_t(0)
+    rc = library().lam_vla_workspace_size(_dtype_code(q), B, T, H, d, ALGOS[algo], ctypes.byref(nws))
+    if rc != 0:
+        raise LamError(rc, "lam_vla_workspace_size")
+    ws = _workspace(int(nws.value), workspace, dev, stream)
     rc = library().lam_vla_forward(_dtype_code(q), B, T, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(p),
                                    _ptr(A_in), _ptr(S_in), _ptr(out), _ptr(A_out), _ptr(S_out),
-                                   ALGOS[algo], _stream(stream))
+                                   _ptr(ws), 0 if ws is None else ws.numel(), ALGOS[algo],
+                                   _stream(stream))
     if rc != 0:
         raise LamError(rc, "lam_vla_forward")
+    _after_call(ws, "lam_vla_forward")
     return out, A_out, S_out

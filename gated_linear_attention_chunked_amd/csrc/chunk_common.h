@@ -105,15 +105,20 @@ __device__ __forceinline__ void lds_arrive(unsigned int *cnt, int lane) {
     if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 // Bounded wait until `*cnt` reaches `target`.  Every wave leaves the loop
-// after at most 2^22 polls, so a lost arrival can slow the kernel down but
-// never hang it.
-__device__ __forceinline__ void lds_wait(unsigned int *cnt, unsigned int target) {
+// after at most 2^22 polls, so a lost arrival can never hang the kernel; a
+// wave that runs out ORs LAM_DEVICE_WAIT_TIMEOUT (bit 0) into the call's
+// device status word (word 0 of the workspace) with a vector atomic, so the
+// host can tell that this call's outputs are not to be trusted.
+__device__ __forceinline__ void lds_wait(unsigned int *cnt, unsigned int target, unsigned int *status) {
     for (int it = 0; it < (1 << 22); ++it) {
-        if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+            return;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
+    __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
-
 
 }  // namespace lam

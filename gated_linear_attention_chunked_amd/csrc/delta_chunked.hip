@@ -21,8 +21,8 @@
 //          It forms everything that does not depend on the state (the
 //          inverses of the diagonal blocks of I + L, the off-diagonal coupling
 //          blocks and the gate prefix sums) from the keys, decays and betas
-//          alone, and writes it to a workspace block of 5.75 KB per chunk (a
-//          device buffer the library keeps per stream).
+//          alone, and writes it to a workspace block of 5.75 KB per chunk (in
+//          the caller's workspace, after its status block).
 //   scan:  one workgroup of 8 waves per (b, h, 32-wide slice of dv); rows of
 //          W are independent, so slices never communicate.  Waves are split
 //          into a carry, an output and a producer role; see the pipelined
@@ -39,11 +39,7 @@
 // with the same order (rows 4g..4g+3 and 16+4g..16+4g+3 of each 32-block).
 // The same trick feeds U and the solve's right-hand sides to the next
 // products without an LDS round trip.
-#include <array>
-#include <map>
-#include <mutex>
 #include <type_traits>
-#include <utility>
 
 #include "chunk_common.h"
 #include "lam_internal.h"
@@ -194,14 +190,16 @@ struct DeriveLds {
     alignas(16) float lt[4][16 * LTS];         // diagonal blocks of L, fp32, by column
     alignas(16) bf16x4 gx[3][64];              // -G~_3j (j < 3), made by waves 0 and 1 for wave 3
     alignas(16) DerBlock d;
-    unsigned int gcount;                       // row-3 Gram blocks published by waves 0, 1
 };
 
 // One workgroup of four waves per (sequence, head, chunk); wave i stages key
 // rows [16i, 16i + 16) and then owns block row i of L: its E K^T tiles, the
 // inverse of its diagonal block (fp32 forward substitution) and its M_ij.
+// As the call's first kernel it also clears the status word that the scan's
+// bounded waits report into.
 template <int VARIANT, int DK>
-__global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, DerBlock *__restrict__ out) {
+__global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, DerBlock *__restrict__ out,
+                                                                   unsigned int *status) {
     constexpr bool kDecay = VARIANT != kDeltaNet;
     constexpr bool kGates2 = VARIANT == kGatedDeltaNet2;
     constexpr int KS = DK + 8;
@@ -219,6 +217,7 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
     const int lg = lane >> 4, lc = lane & 15;
     const int t0 = c * C, last = T - 1 - t0;
     const int64_t base = (static_cast<int64_t>(b) * T + t0) * H + h;  // token index of chunk row 0
+    if (task == 0 && tid == 0) *status = 0u;
 
     // ---- staging: a dk-wide row is DK/8 16-byte pieces, 64*8/DK rows per load
     constexpr int PPR = DK / 8, RPI = 64 / PPR, NQK = 16 / RPI;
@@ -239,7 +238,6 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
         const uint16_t *gsc = static_cast<const uint16_t *>(w == 0 ? a.alpha : a.beta);
         rs = gsc[base + static_cast<int64_t>(min(lane, last)) * H];
     }
-    if (tid == 0) s.gcount = 0u;
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
         const int row = krow + RPI * i;
@@ -247,7 +245,7 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
         *reinterpret_cast<uint4 *>(&s.k[row * KS + (lane % PPR) * 8]) = masked(kr[i], m);
         if constexpr (kGates2) *reinterpret_cast<uint4 *>(&s.e[row * KS + (lane % PPR) * 8]) = masked(mul8(kr[i], br[i]), m);
     }
-    if (w == 0) s.la[lane] = (kDecay && lane <= last) ? fmaxf(__builtin_amdgcn_logf(bf16_bits_to_f32(rs)), -200.f) : 0.f;
+    if (w == 0) s.la[lane] = (kDecay && lane <= last) ? log2_decay(bf16_bits_to_f32(rs)) : 0.f;
     if (w == 1) s.beta[lane] = lane <= last ? bf16_bits_to_f32(rs) : 0.f;
     __syncthreads();
 
@@ -263,8 +261,11 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
     }
     __syncthreads();
 
-    // ---- E K^T tiles, inverse of the diagonal block and M of block row I
-    auto work = [&](auto ic_) {
+    // ---- E K^T tiles of block row I (phase 1), then the inverse of its
+    // diagonal block and its M (phase 2); between them waves 0 and 1 hand
+    // the row-3 Gram blocks to wave 3 through one barrier
+    bf16x4 gneg[4];   // -G~_Ij in accumulator order (own block row only)
+    auto gram = [&](auto ic_) {
         constexpr int I = decltype(ic_)::value;
         using Tl = RowTiles<I>;
         constexpr int NT = Tl::n;
@@ -285,7 +286,6 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
             for (int j = 0; j < NT; ++j) acc[j] = mfma32(kGates2 ? ef[Tl::ti[j]] : kf[Tl::ti[j]], kf[Tl::si[j]], acc[j]);
         }
         // E K^T tiles: lane (lg, lc) holds G[t = 16ti + 4lg + r][s = 16si + lc]
-        bf16x4 gneg[4];   // -G~_Ij in accumulator order (own block row only)
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             const int ti = Tl::ti[j], si = Tl::si[j];
@@ -308,7 +308,15 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
                 s.gx[si][lane] = bf4(-x);  // row 3 block computed for wave 3
             }
         }
-        if constexpr (I < 2) lds_arrive(&s.gcount, lane);
+    };
+    if (w == 0) gram(ic<0>{});
+    else if (w == 1) gram(ic<1>{});
+    else if (w == 2) gram(ic<2>{});
+    else gram(ic<3>{});
+    __syncthreads();
+
+    auto solve = [&](auto ic_) {
+        constexpr int I = decltype(ic_)::value;
         // D_I = (I + L_II)^{-1} by forward substitution in fp32;
         // lane = (column col, row quad q)
         const int col = lane >> 2, q = lane & 3;
@@ -355,8 +363,7 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
         // accumulators, B = D~_I^T from its A-operand fragment) so the result
         // comes out in A-operand order
         if constexpr (I > 0) {
-            if constexpr (I == 3) {
-                lds_wait(&s.gcount, 2u);  // blocks (3,0), (3,1), (3,2) from waves 0, 1
+            if constexpr (I == 3) {  // blocks (3,0), (3,1), (3,2) from waves 0, 1
 #pragma unroll
                 for (int j = 0; j < 3; ++j) gneg[j] = s.gx[j][lane];
             }
@@ -367,10 +374,10 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
             for (int j = 0; j < I; ++j) D.mij[lower_block(I, j)][lane] = bf4(mfma16(gneg[j], dfrag, zero));
         }
     };
-    if (w == 0) work(ic<0>{});
-    else if (w == 1) work(ic<1>{});
-    else if (w == 2) work(ic<2>{});
-    else work(ic<3>{});
+    if (w == 0) solve(ic<0>{});
+    else if (w == 1) solve(ic<1>{});
+    else if (w == 2) solve(ic<2>{});
+    else solve(ic<3>{});
 
     __syncthreads();
 
@@ -382,7 +389,8 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
 
 // ================================= scan =================================
 template <int VARIANT, int DK>
-__global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, const DerBlock *__restrict__ der) {
+__global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, const DerBlock *__restrict__ der,
+                                                               unsigned int *status) {
     constexpr bool kDecay = VARIANT != kDeltaNet;
     constexpr int KS = DK + 8;
     constexpr int KSTEP = DK / 32;
@@ -496,7 +504,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                 lds_arrive(&s.ucount[vt], lane);
                 state_update<KT>(St, R, D, ub, KS, lane);
                 if (c + 1 < nchunks) {
-                    lds_wait(&s.scount[vt], static_cast<unsigned int>(2 * (c + 1)));  // both output waves
+                    lds_wait(&s.scount[vt], static_cast<unsigned int>(2 * (c + 1)), status);  // both output waves
                     publish_state();
                 }
             } else {
@@ -573,8 +581,8 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                         y[r][0] = xq[r][0] * gm;
                         y[r][1] = xq[r][1] * gm;
                     }
-                    lds_wait(&s.ucount[0], static_cast<unsigned int>(c + 1));
-                    lds_wait(&s.ucount[1], static_cast<unsigned int>(c + 1));
+                    lds_wait(&s.ucount[0], static_cast<unsigned int>(c + 1), status);
+                    lds_wait(&s.ucount[1], static_cast<unsigned int>(c + 1), status);
                     // Y^T += U^T Aqk^T, per value tile
                     const bf16x4 z4 = {};
 #pragma unroll
@@ -744,16 +752,11 @@ hipError_t launch_dk(const DeltaArgs &a, hipStream_t stream) {
     const int64_t nchunks = (a.T + C - 1) / C;
     const int64_t tasks = a.B * a.H * nchunks;
     const unsigned blocks = static_cast<unsigned>(a.B * a.H * (a.dv / BV));
-    if (tasks > 0x7fffffff) return hipErrorInvalidValue;
-    DerBlock *der = nullptr;
-    if (tasks > 0) {
-        void *ws = nullptr;
-        const hipError_t e = derived_workspace(stream, static_cast<size_t>(tasks) * sizeof(DerBlock), &ws);
-        if (e != hipSuccess) return e;
-        der = static_cast<DerBlock *>(ws);
-        delta_chunked_derive_kernel<VARIANT, DK><<<static_cast<unsigned>(tasks), NTD, 0, stream>>>(a, der);
-    }
-    delta_chunked_wy_kernel<VARIANT, DK><<<blocks, NT8, 0, stream>>>(a, der);
+    unsigned int *status = static_cast<unsigned int *>(a.ws);
+    DerBlock *der = reinterpret_cast<DerBlock *>(static_cast<char *>(a.ws) + kStatusBytes);
+    if (tasks > 0)
+        delta_chunked_derive_kernel<VARIANT, DK><<<static_cast<unsigned>(tasks), NTD, 0, stream>>>(a, der, status);
+    delta_chunked_wy_kernel<VARIANT, DK><<<blocks, NT8, 0, stream>>>(a, der, status);
     return hipGetLastError();
 }
 
@@ -768,39 +771,17 @@ hipError_t launch_var(const DeltaArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-// Workspace of the derived blocks of the chunked schedules, cached per
-// (device, stream) and grown on demand.  Calls on one stream run in order, so they share it; calls on
-// different streams get their own.  A stream-ordered allocator would do the
-// same without the cache, but its free and reuse make the host wait for the
-// device on every call, which leaves the device idle between calls.
-hipError_t derived_workspace(hipStream_t stream, size_t bytes, void **ptr) {
-    static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> cache;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(mu);
-    std::pair<void *, size_t> &w = cache[{dev, stream}];
-    if (w.second < bytes) {
-        if (w.first) {
-            // the old buffer may still be read by this stream's queued work
-            e = hipStreamSynchronize(stream);
-            if (e == hipSuccess) e = hipFree(w.first);
-            w = {nullptr, 0};
-            if (e != hipSuccess) return e;
-        }
-        void *p = nullptr;
-        e = hipMalloc(&p, bytes);
-        if (e != hipSuccess) return e;
-        w = {p, bytes};
-    }
-    *ptr = w.first;
-    return hipSuccess;
-}
-
 bool delta_chunked_supported(const DeltaArgs &a) {
     if (a.variant == kKimiDelta) return kda_chunked_supported(a);
     return a.dtype == kBF16 && (a.dk == 64 || a.dk == 128) && a.dv % BV == 0;
+}
+
+bool delta_chunked_workspace(const DeltaArgs &a, size_t *bytes) {
+    if (a.variant == kKimiDelta) return kda_chunked_workspace(a, bytes);
+    const int64_t tasks = a.B * a.H * ((a.T + C - 1) / C);
+    if (tasks > 0x7fffffff) return false;
+    *bytes = kStatusBytes + static_cast<size_t>(tasks) * sizeof(DerBlock);
+    return true;
 }
 
 hipError_t launch_delta_chunked(const DeltaArgs &a, hipStream_t stream) {

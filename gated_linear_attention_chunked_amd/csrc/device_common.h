@@ -39,6 +39,14 @@ struct IoBF16 {
     }
 };
 
+// log2 of a decay, floored at -200 so a zero decay (log2 = -inf) becomes a
+// finite full erase; a NaN decay stays NaN (fmaxf would drop it) and so
+// propagates through the chain as it does token by token.
+__device__ __forceinline__ float log2_decay(float alpha) {
+    const float l = __builtin_amdgcn_logf(alpha);
+    return l != l ? l : fmaxf(l, -200.f);
+}
+
 // ------------------------------------------------------------- reductions
 // Sum over aligned groups of W lanes (W in {1, 2, 4, 8, 16, 64}); every lane
 // of the group receives the group's sum.  Within a 16-lane row the partial

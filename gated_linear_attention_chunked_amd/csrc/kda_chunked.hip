@@ -54,8 +54,6 @@
 //          loads issued four pairs ahead.
 // There is no workgroup barrier in the chunk loop: slots, U and the bf16
 // state move between roles through bounded LDS counters.
-#include <map>
-#include <mutex>
 #include <type_traits>
 
 #include "chunk_common.h"
@@ -142,7 +140,7 @@ struct KdaDeriveLds {
 // token lane (lanes 0-15).
 template <int DK>
 __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK> *__restrict__ out, int64_t Ts,
-                                                        int64_t tb) {
+                                                        int64_t tb, unsigned int *status) {
     constexpr int KS = DK + 8;
     constexpr int KSTEP = DK / 32, CH = DK / 64;
     __shared__ KdaDeriveLds<DK> s;
@@ -154,6 +152,7 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
     const int b = head / H, h = head % H;
     const int lane = threadIdx.x;
     const int lg = lane >> 4, lc = lane & 15;
+    if (task == 0 && lane == 0) *status = 0u;  // first kernel of the call
 
     const uint16_t *gq = static_cast<const uint16_t *>(a.q);
     const uint16_t *gk = static_cast<const uint16_t *>(a.k);
@@ -200,7 +199,7 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
             float acc = 0.f;
 #pragma unroll
             for (int t = 0; t < C16; ++t) {
-                const float la = fmaxf(__builtin_amdgcn_logf(chan(ra[t], j)), -200.f);
+                const float la = log2_decay(chan(ra[t], j));
                 acc += la;
                 G[t][j] = acc;
             }
@@ -217,7 +216,7 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
             for (int j = 0; j < CH; ++j) {
                 float acc = 0.f;
 #pragma unroll
-                for (int t = 0; t < C16; ++t) acc += fmaxf(__builtin_amdgcn_logf(chan(rap[t], j)), -200.f);
+                for (int t = 0; t < C16; ++t) acc += log2_decay(chan(rap[t], j));
                 gpx[j] = acc;
             }
         } else {
@@ -478,7 +477,7 @@ __device__ __forceinline__ void pair_solve(const bf16x8 (&kf0)[KSTEP], const bf1
 
 template <int DK, int NVT>
 __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArgs a, const KdaBlock<DK> *__restrict__ der,
-                                                                         int64_t Ts, int64_t tb) {
+                                                                         int64_t Ts, int64_t tb, unsigned int *status) {
     constexpr int KBV = KdaShape<NVT>::BV;
     constexpr int KS = DK + 8, VS = KBV + 8;
     constexpr int KSTEP = DK / 32, KT = DK / 16;
@@ -530,7 +529,7 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
             float4 gcv[KT];
             auto load_ops = [&](int c) {
                 const typename Lds::Slot &Sl = s.slot[c & 3];
-                lds_wait(&s.ready[c & 3], static_cast<unsigned int>(c / 4 + 1));
+                lds_wait(&s.ready[c & 3], static_cast<unsigned int>(c / 4 + 1), status);
 #pragma unroll
                 for (int p = 0; p < KSTEP; ++p) {
                     kf0[p] = row_frag2(Sl.kd, KS, 0, 32 * p, lane);
@@ -567,7 +566,7 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) Sb[kt] = bf4(St[kt]);
                 // S(c + 1 - NSB) has been read from this buffer
-                if constexpr (Lds::kStateGuard) lds_wait(&s.so[vt], static_cast<unsigned int>(c + 2 - Lds::NSB));
+                if constexpr (Lds::kStateGuard) lds_wait(&s.so[vt], static_cast<unsigned int>(c + 2 - Lds::NSB), status);
                 {
                     auto &dst = s.sh[(c + 1) % Lds::NSB][vt];
 #pragma unroll
@@ -585,7 +584,7 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
             // ================================ output ===============================
             for (int c = 0; c < npairs; ++c) {
                 const typename Lds::Slot &Sl = s.slot[c & 3];
-                lds_wait(&s.ready[c & 3], static_cast<unsigned int>(c / 4 + 1));
+                lds_wait(&s.ready[c & 3], static_cast<unsigned int>(c / 4 + 1), status);
                 // state-independent operands first
                 bf16x8 qf0[KSTEP], qf1[KSTEP], kf0[KSTEP], kf1[KSTEP];
 #pragma unroll
@@ -599,7 +598,7 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
                 const bf16x4 vb0 = col_gather4(Sl.v, VS, 0, 16 * vt, lane);
                 const bf16x4 vb1 = col_gather4(Sl.v, VS, C16, 16 * vt, lane);
                 const bf16x4 dt0 = Sl.dt[0][lane], dt1 = Sl.dt[1][lane], mxf = Sl.mx[lane];
-                lds_wait(&s.sp[vt], static_cast<unsigned int>(c + 1));
+                lds_wait(&s.sp[vt], static_cast<unsigned int>(c + 1), status);
                 bf16x4 Sb[KT];
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) Sb[kt] = s.sh[c % Lds::NSB][vt][kt][lane];
@@ -703,8 +702,8 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
             if (n >= 4) {  // pair n - 4 released by every consumer wave
 #pragma unroll
                 for (int w = 0; w < NVT; ++w) {
-                    lds_wait(&s.sp[w], static_cast<unsigned int>(n - 2));    // carry w past pair n - 4
-                    lds_wait(&s.cons[w], static_cast<unsigned int>(n - 3));  // output w done with it
+                    lds_wait(&s.sp[w], static_cast<unsigned int>(n - 2), status);    // carry w past pair n - 4
+                    lds_wait(&s.cons[w], static_cast<unsigned int>(n - 3), status);  // output w done with it
                 }
             }
             commit(nval);
@@ -721,86 +720,24 @@ bool kda_chunked_supported(const DeltaArgs &a) {
     return a.variant == kKimiDelta && a.dtype == kBF16 && (a.dk == 64 || a.dk == 128) && a.dv % 16 == 0;
 }
 
-// Helper stream and events of one (device, caller stream), made on first use
-// and kept for the life of the process.
-struct KdaAux {
-    hipStream_t aux = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-static hipError_t kda_aux(hipStream_t stream, KdaAux *out) {
-    static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, KdaAux> cache;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(mu);
-    KdaAux &x = cache[{dev, stream}];
-    if (!x.aux) e = hipStreamCreateWithFlags(&x.aux, hipStreamNonBlocking);
-    if (e == hipSuccess && !x.fork) e = hipEventCreateWithFlags(&x.fork, hipEventDisableTiming);
-    if (e == hipSuccess && !x.join) e = hipEventCreateWithFlags(&x.join, hipEventDisableTiming);
-    if (e != hipSuccess) return e;
-    *out = x;
-    return hipSuccess;
+bool kda_chunked_workspace(const DeltaArgs &a, size_t *bytes) {
+    const int64_t tasks = 2 * a.B * a.H * ((a.T + 2 * C16 - 1) / (2 * C16));  // blocks (sub-chunks)
+    if (tasks > 0x7fffffff) return false;
+    const size_t blk = a.dk == 64 ? sizeof(KdaBlock<64>) : sizeof(KdaBlock<128>);
+    *bytes = kStatusBytes + static_cast<size_t>(tasks) * blk;
+    return true;
 }
-
-// With fewer scan workgroups than compute units, the derivation of the
-// later pairs can run on the idle units while the scan works through the
-// first ones.  The sequences are cut at a pair boundary: the derivation of
-// the first part, then its scan (ending in a state buffer); the second
-// part's derivation on a helper stream, ordered after the first derivation
-// (and so after everything queued before this call); then the second scan,
-// after it and from that state.
-constexpr int kSplitMinPairs = 1024;  // derivation tasks below which one part is kept
-constexpr int kSplitMinSteps = 64;    // pairs per sequence below which one part is kept
 
 template <int DK, int NVT>
 static hipError_t launch_dk(const DeltaArgs &a, hipStream_t stream) {
     const unsigned blocks = static_cast<unsigned>(a.B * a.H * (a.dv / KdaShape<NVT>::BV));
     const int64_t np = (a.T + 2 * C16 - 1) / (2 * C16);  // pairs per sequence
     const int64_t pairs = a.B * a.H * np;                // derivation waves
-    const int64_t tasks = 2 * pairs;                     // blocks (sub-chunks)
-    if (tasks > 0x7fffffff) return hipErrorInvalidValue;
-    if (tasks == 0) {
-        kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a, nullptr, a.T, 0);
-        return hipGetLastError();
-    }
-    const bool split = blocks <= 128 && np >= kSplitMinSteps && pairs >= kSplitMinPairs;
-    const size_t der_bytes = static_cast<size_t>(tasks) * sizeof(KdaBlock<DK>);
-    const size_t st_bytes = split ? static_cast<size_t>(a.B * a.H * a.dv * a.dk) * sizeof(float) : 0;
-    void *ws = nullptr;
-    hipError_t e = derived_workspace(stream, der_bytes + st_bytes, &ws);
-    if (e != hipSuccess) return e;
-    KdaBlock<DK> *der = static_cast<KdaBlock<DK> *>(ws);
-    if (!split) {
-        kda_derive_kernel<DK><<<static_cast<unsigned>(pairs), 64, 0, stream>>>(a, der, a.T, 0);
-        kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a, der, a.T, 0);
-        return hipGetLastError();
-    }
-    KdaAux x;
-    e = kda_aux(stream, &x);
-    if (e != hipSuccess) return e;
-    // first part: a quarter of the pairs.  Its scan then lasts about as long
-    // as the second part's derivation beside it (both slow down while they
-    // share the chip); a fifth or a third of the pairs measured slower.
-    const int64_t npA = np / 4, TA = 2 * C16 * npA;
-    DeltaArgs pa = a, pb = a;
-    float *mid = reinterpret_cast<float *>(static_cast<char *>(ws) + der_bytes);
-    pa.T = TA;
-    pa.state_out = mid;
-    pb.T = a.T - TA;
-    pb.state_in = mid;
-    KdaBlock<DK> *derA = der, *derB = der + 2 * a.B * a.H * npA;
-    kda_derive_kernel<DK><<<static_cast<unsigned>(a.B * a.H * npA), 64, 0, stream>>>(pa, derA, a.T, 0);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = hipEventRecord(x.fork, stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(x.aux, x.fork, 0)) != hipSuccess) return e;
-    kda_derive_kernel<DK><<<static_cast<unsigned>(a.B * a.H * (np - npA)), 64, 0, x.aux>>>(pb, derB, a.T, TA);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = hipEventRecord(x.join, x.aux)) != hipSuccess) return e;
-    kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(pa, derA, a.T, 0);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(stream, x.join, 0)) != hipSuccess) return e;
-    kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(pb, derB, a.T, TA);
+    unsigned int *status = static_cast<unsigned int *>(a.ws);
+    KdaBlock<DK> *der = reinterpret_cast<KdaBlock<DK> *>(static_cast<char *>(a.ws) + kStatusBytes);
+    if (pairs > 0)
+        kda_derive_kernel<DK><<<static_cast<unsigned>(pairs), 64, 0, stream>>>(a, der, a.T, 0, status);
+    kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a, pairs > 0 ? der : nullptr, a.T, 0, status);
     return hipGetLastError();
 }
 

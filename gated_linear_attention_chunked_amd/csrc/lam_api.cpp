@@ -32,6 +32,102 @@ bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
 
 lam_status from_hip(hipError_t e) { return e == hipSuccess ? LAM_OK : LAM_ERR_HIP; }
 
+// Token-row offsets inside a chunk (up to 64 rows of H * d elements) are
+// formed in 32 bits by the kernels.
+constexpr int64_t kMaxRowElems = INT64_C(1) << 24;
+
+enum Schedule { kNone, kRecurrent, kChunked };
+
+// Shape, enum and size checks shared by lam_forward and its workspace query.
+lam_status check_delta_shape(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                             int64_t dv, int algo) {
+    if (variant < LAM_DELTANET || variant > LAM_GATED_DELTANET2) return LAM_ERR_INVALID_ARG;
+    if (dtype != LAM_F32 && dtype != LAM_BF16) return LAM_ERR_INVALID_ARG;
+    if (algo < LAM_ALGO_AUTO || algo > LAM_ALGO_CHUNKED) return LAM_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return LAM_ERR_INVALID_ARG;
+    if (!supported_head(dk) || !supported_head(dv)) return LAM_ERR_UNSUPPORTED;
+    int64_t nk, nv, ns, nst;
+    if (!elems(B, T, H, dk, nk) || !elems(B, T, H, dv, nv) || !elems(B, T, H, 1, ns) ||
+        !elems(B, 1, H, dk * dv, nst))
+        return LAM_ERR_INVALID_ARG;
+    // grid size and 32-bit in-chain indices
+    if (B * H > (INT64_C(1) << 24) || T > INT_MAX / 2) return LAM_ERR_INVALID_ARG;
+    if (H * (dk > dv ? dk : dv) > kMaxRowElems) return LAM_ERR_INVALID_ARG;
+    return LAM_OK;
+}
+
+// The schedule a validated call runs and the workspace it needs.
+lam_status plan_delta(const lam::DeltaArgs &a, int algo, Schedule *sched, size_t *ws) {
+    *ws = 0;
+    *sched = kNone;
+    if (a.B == 0 || a.H == 0) return LAM_OK;
+    const bool chunked_ok = lam::delta_chunked_supported(a);
+    if (algo == LAM_ALGO_CHUNKED && !chunked_ok) return LAM_ERR_UNSUPPORTED;
+    if (a.T == 0) {  // nothing to scan: the initial state is copied (recurrent kernel)
+        *sched = kRecurrent;
+        return LAM_OK;
+    }
+    if (algo == LAM_ALGO_RECURRENT || !chunked_ok) {
+        *sched = kRecurrent;
+        return LAM_OK;
+    }
+    if (!lam::delta_chunked_workspace(a, ws)) return LAM_ERR_INVALID_ARG;
+    *sched = kChunked;
+    return LAM_OK;
+}
+
+lam::DeltaArgs shape_args(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                          int64_t dv) {
+    lam::DeltaArgs a{};
+    a.variant = variant;
+    a.dtype = dtype;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.dk = static_cast<int>(dk);
+    a.dv = static_cast<int>(dv);
+    return a;
+}
+
+lam_status check_vla_shape(int dtype, int64_t B, int64_t T, int64_t H, int64_t d, int algo) {
+    if (dtype != LAM_F32 && dtype != LAM_BF16) return LAM_ERR_INVALID_ARG;
+    if (algo < LAM_ALGO_AUTO || algo > LAM_ALGO_CHUNKED) return LAM_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 0 || d <= 0) return LAM_ERR_INVALID_ARG;
+    if (!supported_head(d)) return LAM_ERR_UNSUPPORTED;
+    int64_t n, nst;
+    if (!elems(B, T, H, d, n) || !elems(B, 1, H, d * d, nst)) return LAM_ERR_INVALID_ARG;
+    if (B * H > (INT64_C(1) << 24) || T > INT_MAX / 2) return LAM_ERR_INVALID_ARG;
+    if (H * d > kMaxRowElems) return LAM_ERR_INVALID_ARG;
+    return LAM_OK;
+}
+
+lam_status plan_vla(const lam::VlaArgs &a, int algo, Schedule *sched, size_t *ws) {
+    *ws = 0;
+    *sched = kNone;
+    if (a.B == 0 || a.H == 0) return LAM_OK;
+    const bool chunked_ok = lam::vla_chunked_supported(a);
+    if (algo == LAM_ALGO_CHUNKED && !chunked_ok) return LAM_ERR_UNSUPPORTED;
+    if (a.T == 0 || algo == LAM_ALGO_RECURRENT || !chunked_ok) {
+        *sched = kRecurrent;
+        return LAM_OK;
+    }
+    if (!lam::vla_chunked_workspace(a, ws)) return LAM_ERR_INVALID_ARG;
+    *sched = kChunked;
+    return LAM_OK;
+}
+
+// The workspace a call needs: present, large enough, aligned, and clear of
+// every other argument.
+bool workspace_ok(const void *ws, size_t have, size_t need, const void *const *args,
+                  const int64_t *arg_bytes, int nargs) {
+    if (need == 0) return true;
+    if (!ws || have < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return false;
+    if (need > static_cast<size_t>(INT64_MAX)) return false;
+    for (int i = 0; i < nargs; ++i)
+        if (overlaps(ws, static_cast<int64_t>(need), args[i], arg_bytes[i])) return false;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -46,7 +142,7 @@ const char *lam_status_string(lam_status s) {
     return "unknown status";
 }
 
-int lam_abi_version(void) { return 100; }
+int lam_abi_version(void) { return 200; }
 
 int lam_select_algo(int variant, int dtype, int64_t T, int64_t dk, int64_t dv) {
     if (variant < LAM_DELTANET || variant > LAM_GATED_DELTANET2) return -1;
@@ -63,25 +159,30 @@ int lam_select_algo(int variant, int dtype, int64_t T, int64_t dk, int64_t dv) {
     return (T > 0 && lam::delta_chunked_supported(a)) ? LAM_ALGO_CHUNKED : LAM_ALGO_RECURRENT;
 }
 
+lam_status lam_forward_workspace_size(int variant, int dtype, int64_t B, int64_t T, int64_t H,
+                                      int64_t dk, int64_t dv, int algo, size_t *bytes) {
+    if (!bytes) return LAM_ERR_INVALID_ARG;
+    *bytes = 0;
+    lam_status st = check_delta_shape(variant, dtype, B, T, H, dk, dv, algo);
+    if (st != LAM_OK) return st;
+    Schedule sched;
+    return plan_delta(shape_args(variant, dtype, B, T, H, dk, dv), algo, &sched, bytes);
+}
+
 lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
                        int64_t dv, const void *q, const void *k, const void *v,
                        const void *alpha, const void *erase_b, const void *write_w,
                        const void *beta, const float *state_in, void *out, float *state_out,
-                       int algo, hipStream_t stream) {
-    if (variant < LAM_DELTANET || variant > LAM_GATED_DELTANET2) return LAM_ERR_INVALID_ARG;
-    if (dtype != LAM_F32 && dtype != LAM_BF16) return LAM_ERR_INVALID_ARG;
-    if (algo < LAM_ALGO_AUTO || algo > LAM_ALGO_CHUNKED) return LAM_ERR_INVALID_ARG;
-    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return LAM_ERR_INVALID_ARG;
-    if (!supported_head(dk) || !supported_head(dv)) return LAM_ERR_UNSUPPORTED;
-    int64_t nk, nv, ns, nst;
-    if (!elems(B, T, H, dk, nk) || !elems(B, T, H, dv, nv) || !elems(B, T, H, 1, ns) ||
-        !elems(B, 1, H, dk * dv, nst))
-        return LAM_ERR_INVALID_ARG;
-    // grid and 32-bit in-chain indices
-    if (B * H > (INT64_C(1) << 24) || T > INT_MAX / 2) return LAM_ERR_INVALID_ARG;
+                       void *workspace, size_t workspace_bytes, int algo, hipStream_t stream) {
+    lam_status st = check_delta_shape(variant, dtype, B, T, H, dk, dv, algo);
+    if (st != LAM_OK) return st;
     if (B == 0 || H == 0) return LAM_OK;
-    const bool need_state_copy = T == 0;
-    if (!need_state_copy) {
+    int64_t nk, nv, ns, nst;
+    elems(B, T, H, dk, nk);
+    elems(B, T, H, dv, nv);
+    elems(B, T, H, 1, ns);
+    elems(B, 1, H, dk * dv, nst);
+    if (T > 0) {
         if (!q || !k || !v || !beta || !out) return LAM_ERR_INVALID_ARG;
         if (variant != LAM_DELTANET && !alpha) return LAM_ERR_INVALID_ARG;
         if (variant == LAM_GATED_DELTANET2 && (!erase_b || !write_w)) return LAM_ERR_INVALID_ARG;
@@ -100,14 +201,7 @@ lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, 
         overlaps(state_out, nst * 4, state_in, nst * 4))
         return LAM_ERR_INVALID_ARG;
 
-    lam::DeltaArgs a;
-    a.variant = variant;
-    a.dtype = dtype;
-    a.B = B;
-    a.T = T;
-    a.H = H;
-    a.dk = static_cast<int>(dk);
-    a.dv = static_cast<int>(dv);
+    lam::DeltaArgs a = shape_args(variant, dtype, B, T, H, dk, dv);
     a.q = q;
     a.k = k;
     a.v = v;
@@ -119,28 +213,48 @@ lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, 
     a.out = out;
     a.state_out = state_out;
 
+    Schedule sched;
+    size_t need;
+    st = plan_delta(a, algo, &sched, &need);
+    if (st != LAM_OK) return st;
+    const void *args[] = {q, k, v, a.alpha, a.erase_b, a.write_w, beta, state_in, out, state_out};
+    const int64_t arg_bytes[] = {nk * es, nk * es, nv * es, alpha_bytes, nk * es, nv * es, ns * es,
+                                 nst * 4, out_bytes, nst * 4};
+    if (!workspace_ok(workspace, workspace_bytes, need, args, arg_bytes, 10)) return LAM_ERR_INVALID_ARG;
+    a.ws = need ? workspace : nullptr;
+
     if (T == 0 && !state_out) return LAM_OK;
-    if (algo == LAM_ALGO_CHUNKED) {
-        if (!lam::delta_chunked_supported(a)) return LAM_ERR_UNSUPPORTED;
-        return from_hip(lam::launch_delta_chunked(a, stream));
-    }
-    if (algo == LAM_ALGO_AUTO && T > 0 && lam::delta_chunked_supported(a))
-        return from_hip(lam::launch_delta_chunked(a, stream));
+    if (sched == kChunked) return from_hip(lam::launch_delta_chunked(a, stream));
     return from_hip(lam::launch_delta_recurrent(a, stream));
+}
+
+lam_status lam_vla_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, int64_t d, int algo,
+                                  size_t *bytes) {
+    if (!bytes) return LAM_ERR_INVALID_ARG;
+    *bytes = 0;
+    lam_status st = check_vla_shape(dtype, B, T, H, d, algo);
+    if (st != LAM_OK) return st;
+    lam::VlaArgs a{};
+    a.dtype = dtype;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.d = static_cast<int>(d);
+    Schedule sched;
+    return plan_vla(a, algo, &sched, bytes);
 }
 
 lam_status lam_vla_forward(int dtype, int64_t B, int64_t T, int64_t H, int64_t d,
                            const void *q, const void *k, const void *v, const void *p,
                            const float *A_in, const float *S_in, void *out, float *A_out,
-                           float *S_out, int algo, hipStream_t stream) {
-    if (dtype != LAM_F32 && dtype != LAM_BF16) return LAM_ERR_INVALID_ARG;
-    if (algo < LAM_ALGO_AUTO || algo > LAM_ALGO_CHUNKED) return LAM_ERR_INVALID_ARG;
-    if (B < 0 || T < 0 || H < 0 || d <= 0) return LAM_ERR_INVALID_ARG;
-    if (!supported_head(d)) return LAM_ERR_UNSUPPORTED;
-    int64_t n, nst;
-    if (!elems(B, T, H, d, n) || !elems(B, 1, H, d * d, nst)) return LAM_ERR_INVALID_ARG;
-    if (B * H > (INT64_C(1) << 24) || T > INT_MAX / 2) return LAM_ERR_INVALID_ARG;
+                           float *S_out, void *workspace, size_t workspace_bytes, int algo,
+                           hipStream_t stream) {
+    lam_status st = check_vla_shape(dtype, B, T, H, d, algo);
+    if (st != LAM_OK) return st;
     if (B == 0 || H == 0) return LAM_OK;
+    int64_t n, nst;
+    elems(B, T, H, d, n);
+    elems(B, 1, H, d * d, nst);
     if (T > 0 && (!q || !k || !v || !p || !out)) return LAM_ERR_INVALID_ARG;
     const int64_t es = dtype == LAM_BF16 ? 2 : 4;
     const int64_t ob = n * es;
@@ -156,7 +270,7 @@ lam_status lam_vla_forward(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
             if (o && i && o != i && overlaps(o, nst * 4, i, nst * 4)) return LAM_ERR_INVALID_ARG;
     if (A_out && S_out && overlaps(A_out, nst * 4, S_out, nst * 4)) return LAM_ERR_INVALID_ARG;
 
-    lam::VlaArgs a;
+    lam::VlaArgs a{};
     a.dtype = dtype;
     a.B = B;
     a.T = T;
@@ -171,10 +285,16 @@ lam_status lam_vla_forward(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
     a.out = out;
     a.A_out = A_out;
     a.S_out = S_out;
+    Schedule sched;
+    size_t need;
+    st = plan_vla(a, algo, &sched, &need);
+    if (st != LAM_OK) return st;
+    const void *args[] = {q, k, v, p, A_in, S_in, out, A_out, S_out};
+    const int64_t arg_bytes[] = {ob, ob, ob, ob, nst * 4, nst * 4, ob, nst * 4, nst * 4};
+    if (!workspace_ok(workspace, workspace_bytes, need, args, arg_bytes, 9)) return LAM_ERR_INVALID_ARG;
+    a.ws = need ? workspace : nullptr;
     if (T == 0 && !A_out && !S_out) return LAM_OK;
-    if (algo != LAM_ALGO_RECURRENT && T > 0 && lam::vla_chunked_supported(a))
-        return from_hip(lam::launch_vla_chunked(a, stream));
-    if (algo == LAM_ALGO_CHUNKED && T > 0) return LAM_ERR_UNSUPPORTED;
+    if (sched == kChunked) return from_hip(lam::launch_vla_chunked(a, stream));
     return from_hip(lam::launch_vla_recurrent(a, stream));
 }
 

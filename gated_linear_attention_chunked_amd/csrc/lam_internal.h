@@ -2,7 +2,8 @@
 // kernel translation units.  Not installed; not part of the ABI.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace lam {
@@ -20,6 +21,9 @@ struct DeltaArgs {
     const float *state_in;
     void *out;
     float *state_out;
+    // Caller-provided workspace (chunked schedules only): the status block
+    // (kStatusBytes, word 0 = device error bits), then the derived blocks.
+    void *ws;
 };
 
 struct VlaArgs {
@@ -30,7 +34,12 @@ struct VlaArgs {
     const float *A_in, *S_in;
     void *out;
     float *A_out, *S_out;
+    void *ws;
 };
+
+// Size of the status block at the start of every workspace; the derived
+// blocks follow it, so they keep the workspace's 256-byte alignment.
+constexpr size_t kStatusBytes = 256;
 
 // Each launcher enqueues its kernels on `stream` and returns the HIP status of
 // the launch.  The caller has validated every argument.
@@ -40,18 +49,21 @@ hipError_t launch_vla_recurrent(const VlaArgs &a, hipStream_t stream);
 // Chunked schedule: returns hipErrorNotSupported (without launching) when no
 // chunked kernel is built for the variant / dtype / head sizes.
 bool delta_chunked_supported(const DeltaArgs &a);
+// Workspace bytes of the chunked schedule for a.B, a.T, a.H, a.dk, a.dv
+// (status block included); false when the call has more chunk tasks than
+// one grid takes.
+bool delta_chunked_workspace(const DeltaArgs &a, size_t *bytes);
+// Enqueues the chunked kernels; a.ws holds at least
+// delta_chunked_workspace(a) bytes.
 hipError_t launch_delta_chunked(const DeltaArgs &a, hipStream_t stream);
 // VLA chunked schedule (fp32 matrix cores, any dtype of the token streams).
 bool vla_chunked_supported(const VlaArgs &a);
+bool vla_chunked_workspace(const VlaArgs &a, size_t *bytes);
 hipError_t launch_vla_chunked(const VlaArgs &a, hipStream_t stream);
-
-// Device workspace of `bytes` for the chunked schedules' derived blocks, kept
-// per (device, stream) and grown on demand.  Work queued on `stream` may use
-// it until the next call on that stream that asks for more.
-hipError_t derived_workspace(hipStream_t stream, size_t bytes, void **ptr);
 
 // Kimi Delta (per-channel decay) has its own chunked kernel.
 bool kda_chunked_supported(const DeltaArgs &a);
+bool kda_chunked_workspace(const DeltaArgs &a, size_t *bytes);
 hipError_t launch_kda_chunked(const DeltaArgs &a, hipStream_t stream);
 
 }  // namespace lam

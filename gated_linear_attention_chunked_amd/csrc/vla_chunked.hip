@@ -477,6 +477,12 @@ bool vla_chunked_supported(const VlaArgs &a) {
     return a.d == 32 || a.d == 64 || a.d == 96 || a.d == 128;
 }
 
+// The single-kernel schedule keeps every intermediate in LDS and registers.
+bool vla_chunked_workspace(const VlaArgs &, size_t *bytes) {
+    *bytes = 0;
+    return true;
+}
+
 hipError_t launch_vla_chunked(const VlaArgs &a, hipStream_t stream) {
     if (!vla_chunked_supported(a)) return hipErrorNotSupported;
     return a.dtype == kBF16 ? launch_io<IoBF16>(a, stream) : launch_io<IoF32>(a, stream);

@@ -39,27 +39,28 @@
  *   given (normalise upstream); VLA takes raw q and k.
  *   Pointers: device memory owned by the caller; the library keeps none of
  *   them after returning.
- *   Workspace: the chunked delta-rule schedule (LAM_ALGO_CHUNKED on
- *   LAM_BF16 storage, or AUTO when it picks it) writes state-independent
- *   per-chunk blocks to a device workspace between its two kernels: 5,888 B
- *   per (b, h, 64-token chunk) for DeltaNet, Gated DeltaNet and Gated
- *   DeltaNet-2 at dk = 128, and 14,848 B per (b, h, 16-token sub-chunk,
- *   counted in whole pairs) for Kimi Delta at dk = 128.  Kimi Delta with at
- *   most 128 scan workgroups (B * H * dv / 16 <= 128), at least 64 pairs per
- *   sequence and at least 1024 pairs in all cuts each sequence at a quarter
- *   of its pairs: it adds a B * H * dv * dk fp32 state buffer to the
- *   workspace, and derives the second part on a helper stream (created with
- *   hipStreamNonBlocking at default priority, one per (device, stream), with
- *   two events, kept until the process ends).  The helper waits for the
- *   first part's derivation on the caller's stream, and the caller's stream
- *   waits for the helper before the second scan, so the call stays ordered on
- *   the caller's stream as a whole.  The library owns the workspace:
- *   one buffer per (device, stream), allocated with hipMalloc on that
- *   stream's first such call and grown when a call needs more (growing waits
- *   for the stream's queued work, then frees the old buffer), kept until the
- *   process ends.  Calls on one stream run in order and share it; calls on
- *   different streams use different buffers.  An allocation failure returns
- *   LAM_ERR_HIP.  The other schedules use no memory beyond their arguments.
+ *   Workspace: the chunked schedules write state-independent per-chunk
+ *   blocks to a device workspace between their kernels, which the caller
+ *   provides: lam_forward_workspace_size / lam_vla_workspace_size give its
+ *   size for a call's arguments (0 when the schedule the call runs needs
+ *   none; then `workspace` may be NULL).  It must be device memory of at
+ *   least that many bytes, 256-byte aligned, on the device `stream` belongs
+ *   to, and not overlap any argument; too small or misaligned returns
+ *   LAM_ERR_INVALID_ARG before any HIP call.  The call reads and writes it
+ *   only through the work it enqueues on `stream`, so the caller may reuse
+ *   it for any later work ordered after the call on that stream.  Sizes at
+ *   dk = 128: 5,888 B per (b, h, 64-token chunk) for DeltaNet, Gated
+ *   DeltaNet and Gated DeltaNet-2 (24.1 MB at B8 T4096 H8), and 14,848 B per
+ *   (b, h, 16-token sub-chunk, counted in whole pairs) for Kimi Delta
+ *   (487 MB at B2 T32768 H8), plus the 256-byte status block.
+ *   Status block: the first 256 bytes of a workspace.  Word 0 (uint32)
+ *   receives LAM_DEVICE_* bits from the call's kernels: the call's first
+ *   kernel sets it to 0, and a later kernel ORs in LAM_DEVICE_WAIT_TIMEOUT if
+ *   one of its bounded in-kernel waits between waves ran out (the outputs of
+ *   that call are then not trustworthy).  Read it after the call completes.
+ *   The library allocates no device or host memory, creates no stream or
+ *   event, never synchronises, and keeps no state between calls: everything
+ *   a call touches is in its arguments.
  *   A NULL initial state means zero memory (VLA: A = I, S = 0); a NULL
  *   final-state pointer means the final state is not written.  A final-state
  *   buffer may be the same buffer as its initial state; `out` must not
@@ -71,12 +72,20 @@
  *   Work is enqueued on `stream` (NULL = default stream) and the call returns
  *   at once; a failed launch returns LAM_ERR_HIP, and faults during execution
  *   surface at the caller's next synchronisation.  No exception crosses the
- *   ABI and the library prints nothing.  Calls are re-entrant and results are
- *   bitwise reproducible run to run.
+ *   ABI and the library prints nothing.  Calls are re-entrant: calls that do
+ *   not share a workspace may run concurrently from any threads and streams;
+ *   calls that share one must be ordered on one stream.  Results are bitwise
+ *   reproducible run to run.
+ *   Limits (LAM_ERR_INVALID_ARG beyond them): B * H <= 2^24, T <= 2^30 - 1,
+ *   H * max(dk, dv) <= 2^24 (token-row offsets within a chunk stay in 32
+ *   bits), and at most 2^31 - 1 chunk tasks per call.
+ *   Non-finite inputs are not checked: NaN and Inf propagate through the
+ *   recurrence into later outputs and the final state of their chain.
  */
 #ifndef LAM_H
 #define LAM_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -92,6 +101,9 @@ typedef enum {
 } lam_variant;
 
 typedef enum { LAM_F32 = 0, LAM_BF16 = 1 } lam_dtype;
+
+/* Bits of word 0 of a workspace's status block. */
+#define LAM_DEVICE_WAIT_TIMEOUT 0x1u
 
 typedef enum {
     LAM_OK = 0,
@@ -124,6 +136,8 @@ typedef enum {
  *   state_in     [B,H,dv,dk] fp32 or NULL (zero memory)
  *   out          [B,T,H,dv]                         required, written
  *   state_out    [B,H,dv,dk] fp32 or NULL; may equal state_in
+ *   workspace    device scratch of workspace_bytes (see Workspace above);
+ *                NULL allowed when the size query returns 0
  *   algo         lam_algo
  *   stream       HIP stream the work is enqueued on
  */
@@ -131,7 +145,15 @@ lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, 
                        int64_t dv, const void *q, const void *k, const void *v,
                        const void *alpha, const void *erase_b, const void *write_w,
                        const void *beta, const float *state_in, void *out, float *state_out,
-                       int algo, hipStream_t stream);
+                       void *workspace, size_t workspace_bytes, int algo, hipStream_t stream);
+
+/*
+ * Bytes of workspace lam_forward needs for these arguments (0: none),
+ * written to *bytes.  Returns the status lam_forward would return for a
+ * shape, dtype, variant or algorithm it rejects (pointers are not examined).
+ */
+lam_status lam_forward_workspace_size(int variant, int dtype, int64_t B, int64_t T, int64_t H,
+                                      int64_t dk, int64_t dv, int algo, size_t *bytes);
 
 /*
  * VLA forward scan over a [B,T] block (dk = dv = d, d in {32, 64, 96, 128}).
@@ -139,11 +161,17 @@ lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, 
  *   A_in, S_in   [B,H,d,d] fp32 or NULL (A = I, S = 0)
  *   out          [B,T,H,d] written
  *   A_out, S_out [B,H,d,d] fp32 or NULL; each may equal its input buffer
+ *   workspace    as for lam_forward, sized by lam_vla_workspace_size
  */
 lam_status lam_vla_forward(int dtype, int64_t B, int64_t T, int64_t H, int64_t d,
                            const void *q, const void *k, const void *v, const void *p,
                            const float *A_in, const float *S_in, void *out, float *A_out,
-                           float *S_out, int algo, hipStream_t stream);
+                           float *S_out, void *workspace, size_t workspace_bytes, int algo,
+                           hipStream_t stream);
+
+/* Bytes of workspace lam_vla_forward needs (0: none); as above. */
+lam_status lam_vla_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, int64_t d,
+                                  int algo, size_t *bytes);
 
 /*
  * The schedule LAM_ALGO_AUTO runs for these arguments: LAM_ALGO_RECURRENT or

@@ -18,6 +18,20 @@ def pytest_collection_modifyitems(config, items):
     pass
 
 
+@pytest.fixture(autouse=True)
+def _device_status_checks(request):
+    """GPU tests run with the binding's device checks on: every library call
+    synchronises and fails if its workspace status word reports that a
+    bounded in-kernel wait ran out."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    import gated_linear_attention_chunked_amd as lam
+
+    lam.set_device_checks(True)
+    yield
+
+
 @pytest.fixture(scope="session")
 def oracle_lib():
     import oracle

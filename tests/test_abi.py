@@ -36,7 +36,8 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert {"lam_forward", "lam_vla_forward", "lam_status_string", "lam_abi_version"} <= set(names)
+    assert {"lam_forward", "lam_vla_forward", "lam_forward_workspace_size", "lam_vla_workspace_size",
+            "lam_status_string", "lam_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -53,15 +54,15 @@ def test_status_strings_and_version(lib):
     for s in range(4):
         assert lib.lam_status_string(s)
     assert lib.lam_status_string(99) == b"unknown status"
-    assert lib.lam_abi_version() == 100
+    assert lib.lam_abi_version() == 200
 
 
 def _fwd(lib, variant=1, dtype=1, B=2, T=8, H=2, dk=64, dv=64, q=FAKE, k=FAKE + 0x10000000,
          v=FAKE + 0x20000000, alpha=FAKE + 0x30000000, eb=FAKE + 0x40000000,
          ww=FAKE + 0x50000000, beta=FAKE + 0x60000000, sin=None, out=FAKE + 0x70000000,
-         sout=None, algo=0):
+         sout=None, ws=None, ws_bytes=0, algo=0):
     return lib.lam_forward(variant, dtype, B, T, H, dk, dv, q, k, v, alpha, eb, ww, beta, sin,
-                           out, sout, algo, None)
+                           out, sout, ws, ws_bytes, algo, None)
 
 
 def test_forward_rejects_bad_enums(lib):
@@ -81,6 +82,10 @@ def test_forward_rejects_bad_sizes(lib):
     assert _fwd(lib, dv=256) == UNSUPPORTED
     assert _fwd(lib, B=1 << 40, T=1 << 30) == INVALID       # element count overflows
     assert _fwd(lib, B=1 << 20, H=1 << 10) == INVALID       # too many chains for one grid
+    # token-row offsets inside a chunk are 32-bit: H * max(dk, dv) <= 2^24
+    assert _fwd(lib, B=1, H=(1 << 17) + 1, dk=128, dv=64) == INVALID
+    assert _fwd(lib, B=1, H=(1 << 17) + 1, dk=64, dv=128) == INVALID
+    assert _vla(lib, B=1, H=(1 << 17) + 1, d=128) == INVALID
 
 
 def test_forward_rejects_missing_pointers(lib):
@@ -107,9 +112,9 @@ def test_forward_empty_batch_is_a_noop(lib):
 
 def _vla(lib, dtype=0, B=1, T=8, H=2, d=32, q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000,
          p=FAKE + 0x30000000, Ain=None, Sin=None, out=FAKE + 0x40000000, Aout=None, Sout=None,
-         algo=0):
-    return lib.lam_vla_forward(dtype, B, T, H, d, q, k, v, p, Ain, Sin, out, Aout, Sout, algo,
-                               None)
+         ws=None, ws_bytes=0, algo=0):
+    return lib.lam_vla_forward(dtype, B, T, H, d, q, k, v, p, Ain, Sin, out, Aout, Sout, ws,
+                               ws_bytes, algo, None)
 
 
 def test_vla_rejects_bad_arguments(lib):
@@ -133,3 +138,47 @@ def test_binding_fails_loudly_without_gpu_tensors():
     q = torch.zeros(1, 4, 1, 32)
     with pytest.raises(ValueError):
         lam.forward("deltanet", q, q, q, torch.zeros(1, 4, 1))
+
+
+def _ws_size(lib, variant=1, dtype=1, B=2, T=8, H=2, dk=64, dv=64, algo=0):
+    n = ctypes.c_size_t(12345)
+    rc = lib.lam_forward_workspace_size(variant, dtype, B, T, H, dk, dv, algo, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size_query(lib):
+    # chunked delta schedule: 256-byte status block + 5,888 B per (b, h, 64-token chunk)
+    assert _ws_size(lib, 1, 1, 8, 4096, 8, 128, 128) == (OK, 256 + 8 * 8 * 64 * 5888)
+    assert _ws_size(lib, 3, 1, 8, 4096, 8, 128, 128) == (OK, 256 + 8 * 8 * 64 * 5888)
+    assert _ws_size(lib, 0, 1, 1, 65, 1, 128, 128) == (OK, 256 + 2 * 5888)   # ragged: whole chunks
+    # Kimi Delta: 14,848 B per 16-token sub-chunk at dk = 128, counted in pairs
+    assert _ws_size(lib, 2, 1, 2, 32768, 8, 128, 128) == (OK, 256 + 2 * 8 * 2048 * 14848)
+    assert _ws_size(lib, 2, 1, 1, 17, 1, 128, 128) == (OK, 256 + 2 * 14848)
+    # schedules with no workspace
+    assert _ws_size(lib, 1, 0, 8, 4096, 8, 128, 128) == (OK, 0)              # fp32 storage: recurrent
+    assert _ws_size(lib, 1, 1, 8, 4096, 8, 128, 128, algo=1) == (OK, 0)      # recurrent asked for
+    assert _ws_size(lib, 1, 1, 8, 0, 8, 128, 128) == (OK, 0)                 # T = 0: state copy
+    assert _ws_size(lib, 1, 1, 0, 100, 8, 128, 128) == (OK, 0)               # empty batch
+    # the statuses lam_forward would return
+    assert _ws_size(lib, 1, 0, 8, 64, 8, 128, 128, algo=2)[0] == UNSUPPORTED  # fp32 chunked
+    assert _ws_size(lib, 9)[0] == INVALID
+    assert _ws_size(lib, dk=48)[0] == UNSUPPORTED
+    assert _ws_size(lib, B=-1)[0] == INVALID
+    assert lib.lam_forward_workspace_size(1, 1, 1, 8, 1, 64, 64, 0, None) == INVALID
+    n = ctypes.c_size_t(7)
+    assert lib.lam_vla_workspace_size(0, 4, 4096, 8, 32, 0, ctypes.byref(n)) == OK
+    assert lib.lam_vla_workspace_size(0, 4, 4096, 8, 40, 0, ctypes.byref(n)) == UNSUPPORTED
+
+
+WS = FAKE + 0x90000000  # 256-byte aligned, clear of every other fake argument
+
+
+def test_forward_rejects_bad_workspace(lib):
+    rc, need = _ws_size(lib)
+    assert rc == OK and need > 0
+    assert _fwd(lib) == INVALID                                     # none given
+    assert _fwd(lib, ws=WS, ws_bytes=need - 1) == INVALID           # too small
+    assert _fwd(lib, ws=WS + 64, ws_bytes=need) == INVALID          # not 256-byte aligned
+    assert _fwd(lib, ws=FAKE, ws_bytes=need) == INVALID             # overlaps q
+    assert _fwd(lib, ws=FAKE + 0x70000000, ws_bytes=need) == INVALID  # overlaps out
+    assert _fwd(lib, sout=WS + 1024, ws=WS, ws_bytes=need) == INVALID  # overlaps state_out

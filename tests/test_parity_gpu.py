@@ -138,11 +138,15 @@ def test_chunked_long_sequences(variant, T, dk):
     U.check(w, got, ref, label=w.name)
 
 
-@pytest.mark.parametrize("variant", ["gdn", "gdn2"])
-def test_chunked_streams_and_workspace_growth(variant):
-    """The chunked delta scan keeps its derived-block workspace per stream:
-    calls queued on two streams at once, and a small call after a large one
-    on the same stream, must give the results of isolated calls."""
+@pytest.mark.parametrize("variant", ["gdn", "gdn2", "kda"])
+def test_chunked_workspaces_streams_and_threads(variant):
+    """The caller owns the workspace.  Calls queued on two streams with a
+    workspace each, a small call reusing a large call's workspace on one
+    stream, and calls from two host threads on one stream (each with a
+    workspace from torch's allocator) must all give the results of isolated
+    calls, bit for bit."""
+    import threading
+
     import torch
 
     import gated_linear_attention_chunked_amd as lam
@@ -152,24 +156,78 @@ def test_chunked_streams_and_workspace_growth(variant):
     xs = [I.make_inputs(w) for w in ws]
     alone = [U.run_gpu(w, x, algo="chunked") for w, x in zip(ws, xs)]
     gs = [I.to_device(x, "bf16", "cuda") for x in xs]
+
+    def call(g, **kw):
+        return lam.forward(variant, g["q"], g["k"], g["v"], g["beta"], alpha=g.get("alpha"),
+                           erase_b=g.get("erase_b"), write_w=g.get("write_w"), algo="chunked", **kw)
+
+    def same(res, ref):
+        out, st = res
+        assert np.array_equal(out.float().cpu().numpy().astype(np.float64), ref[0])
+        assert np.array_equal(st.cpu().numpy().astype(np.float64), ref[1])
+
+    need = [lam.workspace_size(variant, "bf16", *sh, algo="chunked") for sh in shapes]
+    assert need[0] > need[1] > 0
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [torch.empty(n, dtype=torch.uint8, device="cuda") for n in need]
     torch.cuda.synchronize()
     res = []
     for rep in range(3):
-        for g, st in zip(gs, streams):
+        for g, st, w_ in zip(gs, streams, wss):
             with torch.cuda.stream(st):
-                res.append(lam.forward(variant, g["q"], g["k"], g["v"], g["beta"], alpha=g.get("alpha"),
-                                       erase_b=g.get("erase_b"), write_w=g.get("write_w"), algo="chunked",
-                                       stream=st))
+                res.append(call(g, stream=st, workspace=w_))
     torch.cuda.synchronize()
-    for i, (out, st) in enumerate(res):
-        ref = alone[i % 2]
-        assert np.array_equal(out.float().cpu().numpy().astype(np.float64), ref[0])
-        assert np.array_equal(st.cpu().numpy().astype(np.float64), ref[1])
-    # the large workload's workspace, then the small one on the same stream
-    small_again = U.run_gpu(ws[1], xs[1], algo="chunked")
-    for a, b in zip(small_again, alone[1]):
-        assert np.array_equal(a, b)
+    for i, r in enumerate(res):
+        same(r, alone[i % 2])
+    # one workspace, a large call then a small one on the same stream
+    big = torch.empty(need[0], dtype=torch.uint8, device="cuda")
+    r0 = call(gs[0], workspace=big)
+    r1 = call(gs[1], workspace=big)
+    torch.cuda.synchronize()
+    same(r0, alone[0])
+    same(r1, alone[1])
+    # two host threads on the current stream, each call with its own workspace
+    out = [None] * 6
+    errs = []
+
+    def worker(j):
+        try:
+            for i in range(3):
+                out[3 * j + i] = call(gs[(i + j) % 2])
+        except Exception as e:  # reported below
+            errs.append(e)
+
+    th = [threading.Thread(target=worker, args=(j,)) for j in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errs, errs
+    for j in range(2):
+        for i in range(3):
+            same(out[3 * j + i], alone[(i + j) % 2])
+
+
+def test_workspace_too_small_is_rejected():
+    import torch
+
+    import gated_linear_attention_chunked_amd as lam
+
+    w = _w("gdn", "bf16", 1, 200, 2, 128, 128, seed=5)
+    g = I.to_device(I.make_inputs(w), "bf16", "cuda")
+    need = lam.workspace_size("gdn", "bf16", 1, 200, 2, 128, 128)
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        lam.forward("gdn", g["q"], g["k"], g["v"], g["beta"], alpha=g["alpha"], workspace=small)
+    # through the C ABI directly (the binding's own size check bypassed)
+    lib = lam.library()
+    out = torch.empty_like(g["v"])
+    rc = lib.lam_forward(1, 1, 1, 200, 2, 128, 128, g["q"].data_ptr(), g["k"].data_ptr(),
+                         g["v"].data_ptr(), g["alpha"].data_ptr(), None, None, g["beta"].data_ptr(),
+                         None, out.data_ptr(), None, small.data_ptr(), small.numel(), 0,
+                         torch.cuda.current_stream().cuda_stream)
+    assert rc == 1  # LAM_ERR_INVALID_ARG, before any work is enqueued
 
 
 @pytest.mark.parametrize("algo", ["recurrent", "chunked"])
@@ -280,34 +338,32 @@ def test_chunked_zero_and_unit_decays(variant):
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 64), (64, 32)])
-def test_kda_chunked_two_parts(dk, dv):
-    """Kimi Delta with few scan workgroups and many pairs: the sequence is
-    scanned in two launches chained through a state buffer, the second
-    part's derivation on a helper stream.  Every element against the oracle,
-    with a ragged tail and a carried-in state updated in place; two calls in
-    a row (the second reusing the workspace, the helper stream and its
-    events) agree bit for bit."""
+def test_kda_chunked_long_in_place(dk, dv):
+    """Kimi Delta over a long sequence with few scan workgroups: every
+    element against the oracle, with a ragged tail and a carried-in state
+    updated in place; two calls in a row (the second reusing the first's
+    workspace) agree bit for bit."""
     import torch
 
     import gated_linear_attention_chunked_amd as lam
 
     w = _w("kda", "bf16", 1, 8213, 4, dk, dv, seed=9100 + dk)
     x = I.make_inputs(w)
-    assert (w.T + 31) // 32 * w.B * w.H >= 1024  # the two-part launch
     s0 = (np.random.default_rng(dk).standard_normal((1, 4, dv, dk)) * 0.2).astype(np.float64)
     g = I.to_device(x, w.dtype, "cuda")
+    wsp = torch.empty(lam.workspace_size("kda", "bf16", 1, 8213, 4, dk, dv), dtype=torch.uint8, device="cuda")
     runs = []
     for _ in range(2):
         st = torch.from_numpy(s0.astype(np.float32)).cuda()
         out, st2 = lam.forward("kda", g["q"], g["k"], g["v"], g["beta"], alpha=g["alpha"], state_in=st,
-                               state_out=st, algo="chunked")
+                               state_out=st, algo="chunked", workspace=wsp)
         torch.cuda.synchronize()
         assert st2.data_ptr() == st.data_ptr()
         runs.append((out.float().cpu().numpy().astype(np.float64), st.cpu().numpy().astype(np.float64)))
     for a_, b_ in zip(runs[0], runs[1]):
         assert np.array_equal(a_, b_)
     ref = U.run_oracle(w, x, state_in=s0)
-    U.check(w, runs[0], ref, label=w.name + " two parts")
+    U.check(w, runs[0], ref, label=w.name + " long, in place")
 
 
 @pytest.mark.parametrize("dk", [64, 128])
@@ -372,3 +428,55 @@ def test_chunked_rejects_unsupported():
     with pytest.raises(lam.LamError):
         lam.forward("gdn", g["q"], g["k"], g["v"], g["beta"], alpha=g["alpha"], algo="chunked")
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("variant", ["deltanet", "gdn", "gdn2", "kda"])
+def test_chunked_every_element_full_grid(variant):
+    """B8 H8 at d128: 64 heads, so the scan's XCD-grouped block-to-head map
+    takes its grouped branch; every element against the oracle (ragged
+    length, two full chunks plus a tail)."""
+    w = _w(variant, "bf16", 8, 130, 8, 128, 128, seed=7300, gate_mu=0.0)
+    x = I.make_inputs(w)
+    U.check(w, U.run_gpu(w, x, algo="chunked"), U.run_oracle(w, x), label=w.name)
+
+
+def _plant(w, x):
+    """A NaN in chain (0, 1) at token 100 (the decay, or the key for
+    DeltaNet) and +Inf in chain (1, 0) at token 70, value channel 5."""
+    x = {k_: v_.copy() for k_, v_ in x.items()}
+    if w.variant == "deltanet":
+        x["k"][0, 100, 1, 3] = np.nan
+    elif w.variant == "kda":
+        x["alpha"][0, 100, 1, 7] = np.nan
+    else:
+        x["alpha"][0, 100, 1] = np.nan
+    x["v"][1, 70, 0, 5] = np.inf
+    return x
+
+
+@pytest.mark.parametrize("algo", ["recurrent", "chunked"])
+@pytest.mark.parametrize("variant", DELTA)
+def test_non_finite_inputs_propagate(variant, algo):
+    """Non-finite inputs neither crash nor leak: chains without them match
+    the oracle at the usual gates; in a chain with one, every output the
+    oracle makes non-finite is non-finite too, and the final state is
+    non-finite where the oracle's is.  Rows before the planted token match
+    the oracle, except that the chunked schedule may also turn earlier rows
+    of the planted token's own 64-token chunk non-finite (its masked
+    in-chunk products multiply zeros by the non-finite values)."""
+    w = _w(variant, "bf16", 2, 150, 2, 64, 64, seed=7400)
+    x = _plant(w, I.make_inputs(w))
+    got = U.run_gpu(w, x, algo=algo)
+    ref = U.run_oracle(w, x)
+    clean = [(0, 0), (1, 1)]
+    U.check(w, U.pick_chains(got, clean), U.pick_chains(ref, clean), label=w.name + " clean chains")
+    for (b, h), t_bad in (((0, 1), 100), ((1, 0), 70)):
+        y, yr = got[0][b, :, h], ref[0][b, :, h]
+        bad_ref = ~np.isfinite(yr)
+        assert bad_ref[t_bad:].any() and not bad_ref[:t_bad].any()
+        assert np.all(~np.isfinite(y[bad_ref])), (b, h)
+        first = t_bad if algo == "recurrent" else (t_bad // 64) * 64
+        assert np.all(np.isfinite(y[:first]))
+        assert np.max(np.abs(y[:first] - yr[:first])) <= U.BF16_ABS
+        s, sr = got[1][b, h], ref[1][b, h]
+        assert np.all(~np.isfinite(s[~np.isfinite(sr)]))
