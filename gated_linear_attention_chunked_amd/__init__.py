@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblam.so")
 VARIANTS = {"deltanet": 0, "gdn": 1, "kda": 2, "gdn2": 3}
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
 DTYPES = {"f32": 0, "bf16": 1}
-STATUS = {0: "LAM_OK", 1: "LAM_ERR_INVALID_ARG", 2: "LAM_ERR_UNSUPPORTED", 3: "LAM_ERR_HIP"}
+STATUS = {0: "LAM_OK", 1: "LAM_ERR_INVALID_ARG", 2: "LAM_ERR_UNSUPPORTED", 3: "LAM_ERR_HIP",
+          4: "LAM_ERR_SCRATCH_LIMIT"}
 
 DEVICE_WAIT_TIMEOUT = 0x1   # bit of workspace word 0 (status block)
 
@@ -70,6 +71,8 @@ def library() -> ctypes.CDLL:
             sz = ctypes.c_size_t
             lib.lam_forward.argtypes = [ci, ci, i64, i64, i64, i64, i64] + [vp] * 10 + [vp, sz, ci, vp]
             lib.lam_forward.restype = ci
+            lib.lam_forward_noalloc.argtypes = [ci, ci, i64, i64, i64, i64, i64] + [vp] * 10 + [ci, vp]
+            lib.lam_forward_noalloc.restype = ci
             lib.lam_forward_workspace_size.argtypes = [ci, ci, i64, i64, i64, i64, i64, ci,
                                                        ctypes.POINTER(sz)]
             lib.lam_forward_workspace_size.restype = ci

@@ -138,6 +138,7 @@ const char *lam_status_string(lam_status s) {
         case LAM_ERR_INVALID_ARG: return "invalid argument";
         case LAM_ERR_UNSUPPORTED: return "unsupported shape, dtype or algorithm";
         case LAM_ERR_HIP: return "HIP launch failure";
+        case LAM_ERR_SCRATCH_LIMIT: return "call needs more workspace than the no-allocation scratch holds";
     }
     return "unknown status";
 }

@@ -109,7 +109,8 @@ typedef enum {
     LAM_OK = 0,
     LAM_ERR_INVALID_ARG = 1,
     LAM_ERR_UNSUPPORTED = 2,
-    LAM_ERR_HIP = 3
+    LAM_ERR_HIP = 3,
+    LAM_ERR_SCRATCH_LIMIT = 4   /* lam_forward_noalloc: the call needs more than its scratch */
 } lam_status;
 
 /* Evaluation schedule.  Both compute the same scan; they differ only in
@@ -172,6 +173,27 @@ lam_status lam_vla_forward(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
 /* Bytes of workspace lam_vla_forward needs (0: none); as above. */
 lam_status lam_vla_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, int64_t d,
                                   int algo, size_t *bytes);
+
+/*
+ * lam_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  The
+ * same arguments, schedules, kernels and results as lam_forward, with the
+ * workspace replaced by a fixed device array inside the library of
+ * LAM_NOALLOC_SCRATCH_BYTES (32 MiB; it covers the chunked delta schedules at
+ * B8 T4096 H8 d128, 24.1 MB), held on each GPU the library runs on until the
+ * process ends.  A call whose lam_forward_workspace_size exceeds it returns
+ * LAM_ERR_SCRATCH_LIMIT before any HIP call.  Nothing is allocated or freed;
+ * the first call on a device looks up that device's array address (the
+ * stream must belong to the current device).  Every call on one GPU shares
+ * that GPU's array: calls that may overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.
+ */
+#define LAM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+lam_status lam_forward_noalloc(int variant, int dtype, int64_t B, int64_t T, int64_t H,
+                               int64_t dk, int64_t dv, const void *q, const void *k,
+                               const void *v, const void *alpha, const void *erase_b,
+                               const void *write_w, const void *beta, const float *state_in,
+                               void *out, float *state_out, int algo, hipStream_t stream);
 
 /*
  * The schedule LAM_ALGO_AUTO runs for these arguments: LAM_ALGO_RECURRENT or

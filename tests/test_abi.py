@@ -51,7 +51,7 @@ def test_select_algo(lib):
 
 
 def test_status_strings_and_version(lib):
-    for s in range(4):
+    for s in range(5):
         assert lib.lam_status_string(s)
     assert lib.lam_status_string(99) == b"unknown status"
     assert lib.lam_abi_version() == 200
