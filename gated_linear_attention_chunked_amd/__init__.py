@@ -20,7 +20,10 @@ __all__ = ["forward", "vla_forward", "select_algo", "workspace_size", "vla_works
            "set_device_checks", "library", "LamError", "LamDeviceError", "VARIANTS", "ALGOS",
            "LIB_PATH"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblam.so")
+# LAM_LIBRARY names another build of the same library (the sanitizer tests
+# load an ASan/UBSan build of the argument checks through it).
+LIB_PATH = os.environ.get("LAM_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "liblam.so")
 VARIANTS = {"deltanet": 0, "gdn": 1, "kda": 2, "gdn2": 3}
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
 DTYPES = {"f32": 0, "bf16": 1}

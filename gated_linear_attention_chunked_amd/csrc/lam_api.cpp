@@ -132,7 +132,7 @@ bool workspace_ok(const void *ws, size_t have, size_t need, const void *const *a
 
 extern "C" {
 
-const char *lam_status_string(lam_status s) {
+const char *lam_status_string(int s) {
     switch (s) {
         case LAM_OK: return "ok";
         case LAM_ERR_INVALID_ARG: return "invalid argument";

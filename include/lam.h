@@ -203,8 +203,9 @@ lam_status lam_forward_noalloc(int variant, int dtype, int64_t B, int64_t T, int
  */
 int lam_select_algo(int variant, int dtype, int64_t T, int64_t dk, int64_t dv);
 
-/* Static, NUL-terminated description of a status code. */
-const char *lam_status_string(lam_status status);
+/* Static, NUL-terminated description of a status code (any int; values that
+ * are not a lam_status give "unknown status"). */
+const char *lam_status_string(int status);
 
 /* ABI version of this header (major * 100 + minor). */
 int lam_abi_version(void);

@@ -28,6 +28,10 @@ _LIBS = {
     "f64": os.path.join(_HERE, "liblam_oracle.so"),
     "f32": os.path.join(_HERE, "liblam_oracle_f32.so"),
 }
+# LAM_ORACLE_LIB / LAM_ORACLE_LIB_F32 name other builds of the same source
+# (the sanitizer tests run the pins against an ASan/UBSan build); they are
+# loaded as they are, never rebuilt.
+_OVERRIDE = {"f64": os.environ.get("LAM_ORACLE_LIB"), "f32": os.environ.get("LAM_ORACLE_LIB_F32")}
 _lock = threading.Lock()
 _loaded: dict[str, ctypes.CDLL] = {}
 
@@ -56,8 +60,9 @@ def build(force: bool = True) -> None:
 def _lib(prec: str = "f64") -> ctypes.CDLL:
     with _lock:
         if prec not in _loaded:
-            path = _LIBS[prec]
-            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            path = _OVERRIDE[prec] or _LIBS[prec]
+            if not _OVERRIDE[prec] and (not os.path.exists(path) or
+                                        os.path.getmtime(path) < os.path.getmtime(_SRC)):
                 build(force=False)
             lib = ctypes.CDLL(path)
             dp = ctypes.c_void_p
