@@ -7,23 +7,36 @@
 // the gate, S <- S + (v - S khat) alphahat^T; keys and queries pass through
 // ELU+1 and unit normalisation; y = S qhat.
 //
-// Chunked form over C = 16 tokens (rows = tokens; A, S at the chunk start):
-//   Pa = P A^T, KA = Khat A^T, F = Z X^T with X = [P; Khat] (16 x 32):
-//     F_t = (Pa X^T)_t - sum_{s<t} c_ts F_s,  c_ts = F_s[p_t] / D_s,
-//     D_t = 1 + F_t[p_t]                     (z_t = A_{t-1} p_t, D_t = 1 + p_t.z_t)
-//   Z = (I + C)^{-1} Pa,  N = KA - E Z with E_ts = F_s[khat_t] / D_s (s <= t),
-//   alphahat_t = N_t / |N_t|,  A <- A - Z^T D^{-1} Z,
-//   U = (I + strict(Khat Ahat^T))^{-1} (V - Khat S^T),
-//   Y = Qhat S^T + lower(Qhat Ahat^T) U,  S <- S + U^T Ahat.
-// The sequential part is the 16-step recurrence for F (one wave, lanes over
-// its 32 columns) and two 16x16 unit-lower inverses; everything else is
-// 16x16x4 fp32 MFMA products.
+// A is the inverse of the penalty M = A_0^{-1} + sum_s p_s p_s^T (section
+// 2.2: the Sherman-Morrison step keeps A = M^{-1} exactly), so the penalty at
+// any token is a prefix sum, and A there is its inverse.  That makes the
+// gates parallel over the sequence: it is cut into segments, the inverse
+// penalty at each segment start is formed directly, and the rank-1 steps
+// then run inside the segments concurrently.  The gates do not depend on
+// the state, so the state scan runs afterwards, split over value rows.
 //
-// Schedule: one workgroup of D/16 waves per (b, h) chain.  Wave w keeps
-// column tile w of A^T and of S^T as fp32 accumulator tiles in registers,
-// so every product against the state and every state update is local to
-// the wave; chunk tiles move between waves through LDS, one barrier per
-// phase.
+// Four kernels per call (segments of SEG tokens, chunks of C = 16 tokens):
+//   gram:    per (b, h, segment): G = P^T P over the segment's tokens (fp32).
+//   inverse: per (b, h, segment > 0): M = A_0^{-1} + sum of the earlier
+//            segments' G, inverted by Gauss-Jordan in fp64 (M is symmetric
+//            positive definite, so no pivoting) -> A at the segment start.
+//   alpha:   per (b, h, segment): from that A, the chunked rank-1 steps over
+//            the segment's chunks (rows = tokens; A at the chunk start):
+//              Pa = P A^T, KA = Khat A^T, F = Z X^T with X = [P; Khat]:
+//              F_t = (Pa X^T)_t - sum_{s<t} c_ts F_s, c_ts = F_s[p_t] / D_s,
+//              D_t = 1 + F_t[p_t]          (z_t = A_{t-1} p_t, D_t = 1 + p_t.z_t)
+//              Z = (I + C)^{-1} Pa, N = KA - E Z with E_ts = F_s[khat_t] / D_s
+//              (s <= t), alphahat_t = N_t / |N_t|, A <- A - Z^T D^{-1} Z;
+//            then the state-independent operands of each chunk's state step,
+//            Tc = (I + strict(Khat Ahat^T))^{-1} and Aq = lower(Qhat Ahat^T),
+//            written with khat, qhat and alphahat to a per-chunk record.
+//   state:   per (b, h, 16 value rows of S): the generalised delta scan
+//              U = Tc (V - Khat S^T), Y = Qhat S^T + Aq U, S <- S + U^T Ahat,
+//            with the key dimension of S^T split over the workgroup's D/16
+//            waves (one 16 x 16 accumulator tile each) and the partial
+//            products summed through LDS, one barrier per chunk.
+// The last segment's alpha workgroup writes A_out; the state workgroups
+// write S_out.
 #include "device_common.h"
 #include "lam_internal.h"
 
@@ -47,6 +60,22 @@ template <int I>
 struct icst {
     static constexpr int value = I;
 };
+// Workgroup barrier that orders LDS only.  Threads of these kernels share
+// data only through LDS, and a plain __syncthreads() would also wait for
+// every global load in flight (the next chunks' prefetch) at each barrier.
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// f(icst<0>) ... f(icst<N - 1>)
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &f) {
+    if constexpr (I < N) {
+        f(icst<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
 // f(icst<0>) ... f(icst<14>)
 template <int I = 0, typename F>
 __device__ __forceinline__ void static_for15(F &f) {
@@ -56,27 +85,6 @@ __device__ __forceinline__ void static_for15(F &f) {
     }
 }
 __device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
-
-template <int D>
-struct VlaLds {
-    static constexpr int DS = D + 4;  // row stride of the token-row tiles
-    static constexpr int TS = VC + 4; // row stride of the transposed tiles
-    // token-row tiles, double-buffered: chunk c is consumed while chunk c + 1
-    // is staged and its features are computed
-    alignas(16) float p[2][VC * DS], kh[2][VC * DS], qh[2][VC * DS], v[2][VC * DS];
-    alignas(16) float pa[VC * DS];      // P A^T
-    alignas(16) float ah[VC * DS];      // alphahat rows
-    alignas(16) float zt[D * TS];       // Z^T
-    alignas(16) float at[D * TS];       // alphahat^T
-    alignas(16) float g0t[2 * VC * TS]; // (Pa X^T)^T: column c of Pa X^T as a row
-    alignas(16) float e[VC * TS];       // E, rows t
-    alignas(16) float lt[VC * VLTS];    // strictly lower matrix by column (C, then strict(Khat Ahat^T))
-    alignas(16) f32x4 wop[64];          // (I + C)^{-1}, A-operand order
-    alignas(16) f32x4 top[64];          // (I + strict(Khat Ahat^T))^{-1}, A-operand order
-    alignas(16) f32x4 aq[64];           // lower(Qhat Ahat^T), A-operand order
-    alignas(16) float rd[VC];           // 1 / D_t
-    alignas(16) float part[D / 16][VC]; // per-wave partial |N_t|^2
-};
 
 // Value of lane N of this lane's quad (DPP quad_perm [N, N, N, N]).
 template <int N>
@@ -111,26 +119,272 @@ __device__ __forceinline__ void unit_lower_inverse(const float *lt, f32x4 *out, 
     for (int r = 0; r < 4; ++r) o[((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3)] = x[r];
 }
 
-template <typename IO, int D>
-__global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
-    constexpr int NW = D / 16, NT = 64 * NW, NQ = D / 16;
-    constexpr int DS = VlaLds<D>::DS, TS = VlaLds<D>::TS;
-    __shared__ VlaLds<D> s;
 
+constexpr int NT64 = 64;  // lanes per wave
+
+// Tokens per segment of the inverse-penalty chain.  Each segment past the
+// first costs one d x d inversion; longer segments lengthen the chain inside
+// each alpha workgroup.
+__host__ __device__ constexpr int seg_len(int D) { return D <= 32 ? 128 : 256; }
+
+// Per-chunk record the alpha kernel writes for the state kernel.
+template <int D>
+struct VlaChunk {
+    float kh[VC * D];        // khat rows (zero past the end of the sequence)
+    float qh[VC * D];        // qhat rows
+    f32x4 aht[D / 16][64];   // alphahat^T tiles, A-operand order: lane (g, i) of tile j holds ahat[4g + m][16j + i]
+    f32x4 top[64];           // (I + strict(Khat Ahat^T))^{-1}, A-operand order
+    f32x4 aq[64];            // lower(Qhat Ahat^T), A-operand order
+};
+
+// Workspace layout of one call (after the status block): G and the segment-
+// start inverses, one D x D fp32 matrix per (b, h, segment), then the chunk
+// records per (b, h, chunk).
+struct VlaLayout {
+    int64_t nseg, nch;
+    size_t g_off, a_off, rec_off, bytes;
+};
+template <int D>
+VlaLayout vla_layout(int64_t B, int64_t T, int64_t H) {
+    VlaLayout L;
+    L.nseg = (T + seg_len(D) - 1) / seg_len(D);
+    L.nch = (T + VC - 1) / VC;
+    const size_t mat = static_cast<size_t>(B * H * L.nseg) * D * D * sizeof(float);
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    L.g_off = kStatusBytes;
+    L.a_off = up(L.g_off + mat);
+    L.rec_off = up(L.a_off + mat);
+    L.bytes = L.rec_off + static_cast<size_t>(B * H * L.nch) * sizeof(VlaChunk<D>);
+    return L;
+}
+
+// ================================ gram ================================
+// One workgroup of D/16 waves per (b, h, segment s < nseg - 1); wave w forms
+// column tile w of G = P^T P over the segment, on and below the diagonal
+// blocks (G is symmetric: the blocks above are written as their mirrors).  Chunk tiles go through LDS
+// transposed (PT[channel][token]), so both operands are float4 reads.
+template <typename IO, int D>
+__global__ __launch_bounds__(64 * (D / 16)) void vla_gram_kernel(VlaArgs a, float *__restrict__ G, int nseg,
+                                                                  unsigned int *status) {
+    constexpr int NW = D / 16, NT = 64 * NW, NQ = D / 16, TS = VC + 4, EPT = VC * D / NT;
+    constexpr int SEG = seg_len(D);
+    __shared__ float pt[D * TS];
     const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
-    const int b = blockIdx.x / H, h = blockIdx.x % H;
+    const int nm1 = nseg - 1;
+    const int head = blockIdx.x / nm1, sg = blockIdx.x % nm1;
+    const int b = head / H, h = head % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, i = lane & 15;
-    const int64_t sb = (static_cast<int64_t>(b) * H + h) * D * D;
-    const int col = 16 * w + i;  // this lane's column of the wave's tiles
+    if (blockIdx.x == 0 && tid == 0) *status = 0u;  // first kernel of the call
+    const int t0 = sg * SEG, t1 = min(T, t0 + SEG);
+    auto tok = [&](int t) { return ((static_cast<int64_t>(b) * T + t) * H + h) * D; };
+    float rp[EPT];
+    auto fetch = [&](int c0) {
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int e = tid + NT * u, t = e / D, j = e % D;
+            rp[u] = c0 + t < t1 ? IO::ld(a.p, tok(c0 + t) + j) : 0.f;
+        }
+    };
+    f32x4 acc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    fetch(t0);
+    for (int c0 = t0; c0 < t1; c0 += VC) {
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int e = tid + NT * u;
+            pt[(e % D) * TS + e / D] = rp[u];
+        }
+        lds_sync();
+        if (c0 + VC < t1) fetch(c0 + VC);
+        const f32x4 bw = lds4(&pt[(16 * w + i) * TS + 4 * g]);  // P[4g + m][16w + i]
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            if (q < w) continue;  // G is symmetric: blocks on and below the diagonal
+            const f32x4 aq4 = lds4(&pt[(16 * q + i) * TS + 4 * g]);  // P[4g + m][16q + i]
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[q] = mfma4(aq4[m], bw[m], acc[q]);
+        }
+        lds_sync();
+    }
+    // acc[q] lane (g, i): G[16q + 4g + r][16w + i] for blocks q >= w; the
+    // blocks above the diagonal are their mirror images (four consecutive
+    // floats of row 16w + i per lane)
+    float *out = G + (static_cast<int64_t>(head) * nseg + sg) * D * D;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+        if (q >= w) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[(16 * q + 4 * g + r) * D + 16 * w + i] = acc[q][r];
+            if (q > w)
+                *reinterpret_cast<float4 *>(&out[(16 * w + i) * D + 16 * q + 4 * g]) =
+                    make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+        }
+}
 
-    // A^T and S^T column tile w: AT[q] = A^T[16q + 4g + r][col] = A[col][16q + 4g + r]
-    f32x4 AT[NQ], ST[NQ];
+// =============================== inverse ===============================
+// In-place Gauss-Jordan inversion of the symmetric positive definite D x D
+// matrix held in registers by a 16 x 16 grid of threads (thread (ti, tj) owns
+// rows ti + 16a, columns tj + 16c).  Step k: the owners of row k and column k
+// publish them; every element then takes
+//   M[k][k] = 1/p, M[k][j] = M[k][j]/p, M[i][k] = -M[i][k]/p,
+//   M[i][j] -= M[i][k] M[k][j] / p   (p = M[k][k], old values throughout),
+// written as one rank-1 update (below).  M's eigenvalues lie in [1, 1 + the
+// largest of sum p p^T] (A_0 has eigenvalues in (0, 1]), so the pivots stay
+// well away from zero.
+// The row and column buffers alternate by step parity (16 steps per block,
+// so the parity also alternates across blocks), so one barrier per step
+// orders both their writes and the reads of the step before.
+template <int D>
+__device__ __forceinline__ void gj_invert(double (&M)[D / 16][D / 16], double (*rowbuf)[D], double (*colbuf)[D],
+                                          int ti, int tj) {
+    constexpr int RD = D / 16;
+    // pivot k = 16 kq + kr: the block index kq is a compile-time constant in
+    // each unrolled copy, so M is only ever indexed statically (a runtime
+    // index would move it to scratch memory)
+    auto steps = [&](auto kqc) {
+        constexpr int kq = decltype(kqc)::value;
+#pragma unroll 1
+        for (int kr = 0; kr < 16; ++kr) {
+            const int k = 16 * kq + kr, pb = kr & 1;
+            if (ti == kr) {
+#pragma unroll
+                for (int c = 0; c < RD; ++c) rowbuf[pb][tj + 16 * c] = M[kq][c];
+            }
+            if (tj == kr) {
+#pragma unroll
+                for (int r = 0; r < RD; ++r) colbuf[pb][ti + 16 * r] = M[r][kq];
+            }
+            lds_sync();
+            // 1/p by the hardware reciprocal and two Newton steps (each
+            // squares the relative error: 2^-23 -> 2^-46 -> below fp64 rounding)
+            const double pv = rowbuf[pb][k];
+            double ip = __builtin_amdgcn_rcp(pv);
+            ip = fma(ip, fma(-pv, ip, 1.0), ip);
+            ip = fma(ip, fma(-pv, ip, 1.0), ip);
+            // The whole step is one rank-1 update M -= c r^T, with
+            //   c_i = M[i][k] (i != k), c_k = p - 1,
+            //   r_j = M[k][j] / p (j != k), r_k = 1 + 1/p,
+            // which gives row k -> M[k][j] / p, column k -> -M[i][k] / p and
+            // M[k][k] -> p - (p - 1)(1 + 1/p) = 1/p.
+            double rk[RD], ck[RD];
+#pragma unroll
+            for (int c = 0; c < RD; ++c) {
+                const bool isk = c == kq && tj == kr;
+                rk[c] = isk ? 1.0 + ip : rowbuf[pb][tj + 16 * c] * ip;
+            }
+#pragma unroll
+            for (int r = 0; r < RD; ++r) {
+                const bool isk = r == kq && ti == kr;
+                ck[r] = isk ? pv - 1.0 : colbuf[pb][ti + 16 * r];
+            }
+#pragma unroll
+            for (int r = 0; r < RD; ++r)
+#pragma unroll
+                for (int c = 0; c < RD; ++c) M[r][c] = fma(-ck[r], rk[c], M[r][c]);
+        }
+    };
+    static_for<RD>(steps);
+}
+
+// One workgroup of 256 threads per (b, h, segment s >= 1): M = A_0^{-1} +
+// sum_{s' < s} G_s' in fp64, then A_s = M^{-1} (written as fp32).
+template <int D>
+__global__ __launch_bounds__(256) void vla_inverse_kernel(VlaArgs a, const float *__restrict__ G,
+                                                          float *__restrict__ Aseg, int nseg) {
+    constexpr int RD = D / 16;
+    __shared__ double rowbuf[2][D], colbuf[2][D];
+    const int nm1 = nseg - 1;
+    int head, sm1;
+    xcd_group_map(blockIdx.x, static_cast<int>(a.B * a.H), nm1, head, sm1);
+    const int sg = sm1 + 1;
+    const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
+    const int64_t sb = static_cast<int64_t>(head) * D * D;
+    double M[RD][RD];
+    if (a.A_in) {  // A_0^{-1}
+#pragma unroll
+        for (int r = 0; r < RD; ++r)
+#pragma unroll
+            for (int c = 0; c < RD; ++c) M[r][c] = a.A_in[sb + (ti + 16 * r) * D + tj + 16 * c];
+        gj_invert<D>(M, rowbuf, colbuf, ti, tj);
+    } else {
+#pragma unroll
+        for (int r = 0; r < RD; ++r)
+#pragma unroll
+            for (int c = 0; c < RD; ++c) M[r][c] = (ti + 16 * r == tj + 16 * c) ? 1.0 : 0.0;
+    }
+    // the earlier segments' G
+    const float *g0 = G + static_cast<int64_t>(head) * nseg * D * D;
+#pragma unroll 1
+    for (int s = 0; s < sg; ++s) {
+        const float *gs = g0 + static_cast<int64_t>(s) * D * D;
+#pragma unroll
+        for (int r = 0; r < RD; ++r)
+#pragma unroll
+            for (int c = 0; c < RD; ++c) M[r][c] += gs[(ti + 16 * r) * D + tj + 16 * c];
+    }
+    gj_invert<D>(M, rowbuf, colbuf, ti, tj);
+    float *out = Aseg + (static_cast<int64_t>(head) * nseg + sg) * D * D;
+#pragma unroll
+    for (int r = 0; r < RD; ++r)
+#pragma unroll
+        for (int c = 0; c < RD; ++c) out[(ti + 16 * r) * D + tj + 16 * c] = static_cast<float>(M[r][c]);
+}
+
+// ================================ alpha ================================
+template <int D>
+struct AlphaLds {
+    static constexpr int DS = D + 4;  // row stride of the token-row tiles
+    static constexpr int TS = VC + 4; // row stride of the transposed tiles
+    // token-row tiles, double-buffered: chunk c is consumed while chunk c + 1
+    // is staged and its features are computed
+    alignas(16) float p[2][VC * DS], kh[2][VC * DS], qh[2][VC * DS];
+    alignas(16) float pa[VC * DS];      // P A^T
+    alignas(16) float ah[VC * DS];      // alphahat rows
+    alignas(16) float zt[D * TS];       // Z^T
+    alignas(16) float g0t[2 * VC * TS]; // (Pa X^T)^T: column c of Pa X^T as a row
+    alignas(16) float e[VC * TS];       // E, rows t
+    alignas(16) float lt[VC * VLTS];    // strictly lower matrix by column (C, then strict(Khat Ahat^T))
+    alignas(16) f32x4 wop[64];          // (I + C)^{-1}, A-operand order
+    alignas(16) f32x4 top[64];          // (I + strict(Khat Ahat^T))^{-1}, A-operand order
+    alignas(16) f32x4 aq[64];           // lower(Qhat Ahat^T), A-operand order
+    alignas(16) float rd[VC];           // 1 / D_t
+    alignas(16) float part[D / 16][VC]; // per-wave partial |N_t|^2
+};
+
+// One workgroup of D/16 waves per (b, h, segment).  Wave w keeps column tile
+// w of A^T as fp32 accumulator tiles.
+template <typename IO, int D>
+__global__ __launch_bounds__(64 * (D / 16)) void vla_alpha_kernel(VlaArgs a, const float *__restrict__ Aseg,
+                                                                  VlaChunk<D> *__restrict__ rec, int nseg,
+                                                                  unsigned int *status) {
+    constexpr int NW = D / 16, NT = 64 * NW, NQ = D / 16;
+    constexpr int DS = AlphaLds<D>::DS, TS = AlphaLds<D>::TS;
+    constexpr int SEG = seg_len(D);
+    __shared__ AlphaLds<D> s;
+
+    const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
+    const int head = blockIdx.x / nseg, sg = blockIdx.x % nseg;
+    const int b = head / H, h = head % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, i = lane & 15;
+    const int64_t sb = static_cast<int64_t>(head) * D * D;
+    const int col = 16 * w + i;  // this lane's column of the wave's tiles
+    const int seg0 = sg * SEG, seg1 = min(T, seg0 + SEG);
+    const int nch = (T + VC - 1) / VC;
+    if (nseg == 1 && blockIdx.x == 0 && tid == 0) *status = 0u;  // first kernel of the call
+
+    // A^T column tile w: AT[q] = A^T[16q + 4g + r][col] = A[col][16q + 4g + r]
+    const float *a0 = sg > 0 ? Aseg + (static_cast<int64_t>(head) * nseg + sg) * D * D
+                             : (a.A_in ? a.A_in + sb : nullptr);
+    f32x4 AT[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        if (a.A_in) {
-            const float4 x = *reinterpret_cast<const float4 *>(a.A_in + sb + static_cast<int64_t>(col) * D + 16 * q + 4 * g);
+        if (a0) {
+            const float4 x = *reinterpret_cast<const float4 *>(a0 + static_cast<int64_t>(col) * D + 16 * q + 4 * g);
             AT[q] = f32x4{x.x, x.y, x.z, x.w};
         } else {
             f32x4 x;
@@ -139,23 +393,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
             AT[q] = x;
         }
     }
-    if (a.S_in) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const float4 x = *reinterpret_cast<const float4 *>(a.S_in + sb + static_cast<int64_t>(col) * D + 16 * q + 4 * g);
-            ST[q] = f32x4{x.x, x.y, x.z, x.w};
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) ST[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
 
     // raw inputs of one chunk staged in registers: element e = tid + NT * u of
     // each 16 x D tile (token e / D, channel e % D)
     constexpr int EPT = VC * D / NT;  // = 4
-    float rq[EPT], rk[EPT], rv[EPT], rp[EPT];
+    float rq[EPT], rk[EPT], rp[EPT];
     auto tok = [&](int t) { return ((static_cast<int64_t>(b) * T + t) * H + h) * D; };
-    // this thread's elements sit at fixed offsets from the chunk's first row
     uint32_t eoff[EPT];
 #pragma unroll
     for (int u = 0; u < EPT; ++u) {
@@ -169,151 +412,136 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
             const int e = tid + NT * u, t = e / D;
-            // rows past the end reread the last row (never used)
             const uint32_t o = t < n ? eoff[u] : static_cast<uint32_t>((n - 1) * H * D + e % D);
             rq[u] = IO::ld(a.q, base + o);
             rk[u] = IO::ld(a.k, base + o);
-            rv[u] = IO::ld(a.v, base + o);
             rp[u] = IO::ld(a.p, base + o);
         }
     };
-    // staged registers into buffer bi (rows past n: p = v = 0, features zeroed)
+    // staged registers into buffer bi (rows past n: p = 0, features zeroed)
     auto stage = [&](int bi, int n) {
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
             const int e = tid + NT * u, t = e / D, j = e % D;
-            const bool ok = t < n;
-            s.p[bi][t * DS + j] = ok ? rp[u] : 0.f;
-            s.v[bi][t * DS + j] = ok ? rv[u] : 0.f;
+            s.p[bi][t * DS + j] = t < n ? rp[u] : 0.f;
             s.kh[bi][t * DS + j] = rk[u];
             s.qh[bi][t * DS + j] = rq[u];
         }
     };
-    // khat, qhat = unit(ELU(x) + 1) in place in buffer bi, zero past row n.
-    // NWF waves share the rows (this wave is the wi-th: rows wi, wi + NWF, ...),
-    // all of its rows at once.
-    auto features = [&](auto nwf, int bi, int n, int wi) {
-        constexpr int NWF = decltype(nwf)::value;
-        constexpr int PER = (D + 63) / 64, RPW = (VC + NWF - 1) / NWF;
-        float *KH = s.kh[bi], *QH = s.qh[bi];
-        float fk[RPW][PER], fq[RPW][PER], ssk[RPW], ssq[RPW];
+    // khat (or qhat) = unit(ELU(x) + 1) in place for the 16 rows of tile X,
+    // zero past row n, by one wave: lane (g, i) maps token i, channels
+    // 16q + 4g .. 16q + 4g + 3; the squared norm adds the lane's terms, then
+    // the four lane groups' partial sums (the same bits in every lane).
+    auto features = [&](float *X, int n) {
+        f32x4 f[NQ];
+        float ss = 0.f;
 #pragma unroll
-        for (int rr = 0; rr < RPW; ++rr) {
-            const int t = wi + NWF * rr;
-            ssk[rr] = ssq[rr] = 0.f;
+        for (int q = 0; q < NQ; ++q) {
+            f32x4 x = lds4(&X[i * DS + 16 * q + 4 * g]);
 #pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                // read a valid element unconditionally and mask the value,
-                // so the reads of all rows go out together
-                const int j = lane + 64 * u;
-                const float okf = (t < VC && j < D) ? 1.f : 0.f;
-                const int o = min(t, VC - 1) * DS + min(j, D - 1);
-                fk[rr][u] = elu1(KH[o]) * okf;
-                fq[rr][u] = elu1(QH[o]) * okf;
-                ssk[rr] = fmaf(fk[rr][u], fk[rr][u], ssk[rr]);
-                ssq[rr] = fmaf(fq[rr][u], fq[rr][u], ssq[rr]);
+            for (int m = 0; m < 4; ++m) {
+                x[m] = elu1(x[m]);
+                ss = fmaf(x[m], x[m], ss);
             }
+            f[q] = x;
         }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        const float inv = __builtin_amdgcn_rsqf(ss);
 #pragma unroll
-        for (int rr = 0; rr < RPW; ++rr) {
-            ssk[rr] = group_sum<64>(ssk[rr]);
-            ssq[rr] = group_sum<64>(ssq[rr]);
-        }
-#pragma unroll
-        for (int rr = 0; rr < RPW; ++rr) {
-            const int t = wi + NWF * rr;
-            const float ik = t < n ? __builtin_amdgcn_rsqf(ssk[rr]) : 0.f;
-            const float iq = t < n ? __builtin_amdgcn_rsqf(ssq[rr]) : 0.f;
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const int j = lane + 64 * u;
-                if (t < VC && j < D) {
-                    KH[t * DS + j] = fk[rr][u] * ik;
-                    QH[t * DS + j] = fq[rr][u] * iq;
-                }
-            }
-        }
+        for (int q = 0; q < NQ; ++q)
+            *reinterpret_cast<f32x4 *>(&X[i * DS + 16 * q + 4 * g]) =
+                i < n ? f[q] * inv : f32x4{0.f, 0.f, 0.f, 0.f};
     };
-    if (T > 0) {
-        fetch(0);
-        stage(0, min(VC, T));
-        fetch(VC);
-        __syncthreads();
-        features(icst<NW>{}, 0, min(VC, T), w);
+    constexpr int WQF = NW > 2 ? 2 : 1;  // wave mapping the queries during the recurrence
+    if (seg0 < seg1) {
+        fetch(seg0);
+        stage(0, min(VC, seg1 - seg0));
+        fetch(seg0 + VC);
+        lds_sync();
+        if (w == 0) features(s.kh[0], min(VC, seg1 - seg0));
+        if (w == 1) features(s.qh[0], min(VC, seg1 - seg0));
     }
 
-    for (int c0 = 0; c0 < T; c0 += VC) {
-        const int n = min(VC, T - c0), n1 = min(VC, T - c0 - VC);  // rows of this chunk, of the next
-        const int cb = (c0 / VC) & 1, nb = cb ^ 1;
-        const float *P = s.p[cb], *KH = s.kh[cb], *QH = s.qh[cb], *V = s.v[cb];
+    for (int c0 = seg0; c0 < seg1; c0 += VC) {
+        const int n = min(VC, seg1 - c0), n1 = max(0, min(VC, seg1 - c0 - VC));  // rows of this chunk, of the next
+        const int cb = ((c0 - seg0) / VC) & 1, nb = cb ^ 1;
+        const float *P = s.p[cb], *KH = s.kh[cb], *QH = s.qh[cb];
+        VlaChunk<D> &R = rec[static_cast<int64_t>(head) * nch + c0 / VC];
         // ---- stage chunk c + 1 into the other buffer, refill the registers
         stage(nb, n1);
         fetch(c0 + 2 * VC);
-        __syncthreads();
-        // ---- products against the chunk-start state (tile w of each):
-        // Pa = P A^T, KA = Khat A^T, KS = Khat S^T, QS = Qhat S^T
-        f32x4 pa = {0.f, 0.f, 0.f, 0.f}, ka = pa, ks = pa, qs = pa;
+        lds_sync();
+        // ---- products against the chunk-start inverse penalty (tile w):
+        // Pa = P A^T, KA = Khat A^T (two accumulators each: even and odd
+        // reduction steps, so the dependent chains are half as long)
+        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 pa, ka;
+        {
+            f32x4 pa2[2] = {zero4, zero4}, ka2[2] = {zero4, zero4};
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const f32x4 pr = lds4(&P[i * DS + 16 * q + 4 * g]);
-            const f32x4 kr = lds4(&KH[i * DS + 16 * q + 4 * g]);
-            const f32x4 qr = lds4(&QH[i * DS + 16 * q + 4 * g]);
+            for (int q = 0; q < NQ; ++q) {
+                const f32x4 pr = lds4(&P[i * DS + 16 * q + 4 * g]);
+                const f32x4 kr = lds4(&KH[i * DS + 16 * q + 4 * g]);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                pa = mfma4(pr[m], AT[q][m], pa);
-                ka = mfma4(kr[m], AT[q][m], ka);
-                ks = mfma4(kr[m], ST[q][m], ks);
-                qs = mfma4(qr[m], ST[q][m], qs);
+                for (int m = 0; m < 4; ++m) {
+                    pa2[m & 1] = mfma4(pr[m], AT[q][m], pa2[m & 1]);
+                    ka2[m & 1] = mfma4(kr[m], AT[q][m], ka2[m & 1]);
+                }
             }
+            pa = pa2[0] + pa2[1];
+            ka = ka2[0] + ka2[1];
         }
-        // R = V - Khat S^T (tile w, accumulator order)
-        f32x4 rr;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            rr[r] = V[(4 * g + r) * DS + col] - ks[r];
-            s.pa[(4 * g + r) * DS + col] = pa[r];
+        for (int r = 0; r < 4; ++r) s.pa[(4 * g + r) * DS + col] = pa[r];
+        // the chunk's features go to its record (rows past the end are zero)
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int e = tid + NT * u, t = e / D, j = e % D;
+            R.kh[e] = KH[t * DS + j];
+            R.qh[e] = QH[t * DS + j];
         }
-        __syncthreads();
+        lds_sync();
         // ---- Pa X^T (16 x 32), waves 0 and 1: column c of it stored as row c of g0t
         if (w < 2) {
             const float *xs = w == 0 ? P : KH;
-            f32x4 g0 = {0.f, 0.f, 0.f, 0.f};
+            f32x4 g2[2] = {zero4, zero4};
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const f32x4 ar = lds4(&s.pa[i * DS + 16 * q + 4 * g]);
                 const f32x4 br = lds4(&xs[i * DS + 16 * q + 4 * g]);
 #pragma unroll
-                for (int m = 0; m < 4; ++m) g0 = mfma4(ar[m], br[m], g0);
+                for (int m = 0; m < 4; ++m) g2[m & 1] = mfma4(ar[m], br[m], g2[m & 1]);
             }
+            const f32x4 g0 = g2[0] + g2[1];
             // g0 lane (g, i): (Pa X^T)[t = 4g + r][16w + i]
             *reinterpret_cast<f32x4 *>(&s.g0t[(16 * w + i) * TS + 4 * g]) = g0;
         }
-        __syncthreads();
+        lds_sync();
         // ---- wave 0: the recurrence for F, then Z's coefficients inverted
         if (w == 0) {
-            // lane c < 32 keeps column c of F: F[s] = F_s[c]
+            // lane c < 32 keeps column c of F: F[s] = F_s[c].  Right-looking:
+            // once F_s is final, its term -c_ts F_s (c_ts = F_s[p_t] / D_s,
+            // column t of F_s, held by lane t) goes into every later row at
+            // once, so each step's critical path is one row's last update.
             const int c = lane & 31;
-            float gcol[VC], F[VC], rdv[VC];
+            float acc[VC], F[VC], rdv[VC];
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4) {
                 const f32x4 x = lds4(&s.g0t[c * TS + 4 * t4]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) gcol[4 * t4 + r] = x[r];
+                for (int r = 0; r < 4; ++r) acc[4 * t4 + r] = x[r];
             }
 #pragma unroll
-            for (int t = 0; t < VC; ++t) {
-                // c_ts = F_s[p_t] / D_s: column t of row s, held by lane t;
-                // four partial sums keep the chain short
-                float acc[4] = {gcol[t], 0.f, 0.f, 0.f};
+            for (int s2 = 0; s2 < VC; ++s2) {
+                F[s2] = acc[s2];
+                const float ds = 1.f + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(F[s2]), s2));
+                rdv[s2] = __builtin_amdgcn_rcpf(ds);
 #pragma unroll
-                for (int s2 = 0; s2 < t; ++s2) {
+                for (int t = s2 + 1; t < VC; ++t) {
                     const float cts = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(F[s2]), t)) * rdv[s2];
-                    acc[s2 & 3] = fmaf(-cts, F[s2], acc[s2 & 3]);
+                    acc[t] = fmaf(-cts, F[s2], acc[t]);
                 }
-                const float f = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-                F[t] = f;
-                const float dt = 1.f + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), t));
-                rdv[t] = __builtin_amdgcn_rcpf(dt);
             }
             // C (strictly lower, by column s): C_ts = F_s[t] / D_s, lanes t < 16
             // E (rows t): E_ts = F_s[16 + t] / D_s for s <= t, lanes 16 + t
@@ -336,10 +564,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             unit_lower_inverse(s.lt, s.wop, lane);
         } else {
-            // meanwhile the other waves map the features of chunk c + 1
-            features(icst<NW - 1>{}, nb, n1, w - 1);
+            // meanwhile other waves map the features of chunk c + 1
+            if (w == 1) features(s.kh[nb], n1);
+            if (w == WQF) features(s.qh[nb], n1);
         }
-        __syncthreads();
+        lds_sync();
         // ---- Z = (I + C)^{-1} Pa, N = KA - E Z (tile w); Z^T to LDS; |N_t|^2 partials
         f32x4 z = {0.f, 0.f, 0.f, 0.f}, nn = ka;
         {
@@ -356,8 +585,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
             const float sq = group_sum<16>(nn[r] * nn[r]);
             if (i == 0) s.part[w][4 * g + r] = sq;
         }
-        __syncthreads();
-        // ---- alphahat (tile w) to LDS by rows and by columns; A^T -= Z^T D^{-1} Z
+        lds_sync();
+        // ---- alphahat (tile w) to LDS by rows and to the record; A^T -= Z^T D^{-1} Z
         f32x4 ah;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -368,7 +597,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
             ah[r] = nn[r] * (t < n ? __builtin_amdgcn_rsqf(ss) : 0.f);
             s.ah[t * DS + col] = ah[r];
         }
-        *reinterpret_cast<f32x4 *>(&s.at[col * TS + 4 * g]) = ah;
+        R.aht[w][lane] = ah;
         {
             const f32x4 rd4 = lds4(&s.rd[4 * g]);
             f32x4 zd;
@@ -382,17 +611,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
                 for (int m = 0; m < 4; ++m) AT[q] = mfma4(za[m], zd[m], AT[q]);
             }
         }
-        __syncthreads();
+        lds_sync();
         // ---- wave 0: strict(Khat Ahat^T) by column, inverted; wave 1: lower(Qhat Ahat^T)
         if (w == 0) {
-            f32x4 km = {0.f, 0.f, 0.f, 0.f};
+            f32x4 km2[2] = {zero4, zero4};
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const f32x4 kr = lds4(&KH[i * DS + 16 * q + 4 * g]);
                 const f32x4 ar = lds4(&s.ah[i * DS + 16 * q + 4 * g]);
 #pragma unroll
-                for (int m = 0; m < 4; ++m) km = mfma4(kr[m], ar[m], km);
+                for (int m = 0; m < 4; ++m) km2[m & 1] = mfma4(kr[m], ar[m], km2[m & 1]);
             }
+            const f32x4 km = km2[0] + km2[1];
             // km lane (g, i): (Khat Ahat^T)[t = 4g + r][s = i]; column s = i of the strict part
             f32x4 x;
 #pragma unroll
@@ -402,61 +632,192 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_chunked_kernel(VlaArgs a) {
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             unit_lower_inverse(s.lt, s.top, lane);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            R.top[lane] = s.top[lane];
         } else if (w == 1) {
-            f32x4 aq = {0.f, 0.f, 0.f, 0.f};
+            f32x4 aq2[2] = {zero4, zero4};
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const f32x4 ar = lds4(&s.ah[i * DS + 16 * q + 4 * g]);
                 const f32x4 qr = lds4(&QH[i * DS + 16 * q + 4 * g]);
 #pragma unroll
-                for (int m = 0; m < 4; ++m) aq = mfma4(ar[m], qr[m], aq);
+                for (int m = 0; m < 4; ++m) aq2[m & 1] = mfma4(ar[m], qr[m], aq2[m & 1]);
             }
+            f32x4 aq = aq2[0] + aq2[1];
             // aq lane (g, i): (Ahat Qhat^T)[s = 4g + r][t = i] = (Qhat Ahat^T)[t = i][s = 4g + r]:
             // already the A operand of Y = Aq U; keep s <= t
 #pragma unroll
             for (int r = 0; r < 4; ++r) aq[r] = 4 * g + r <= i ? aq[r] : 0.f;
-            s.aq[lane] = aq;
+            R.aq[lane] = aq;
         }
-        __syncthreads();
-        // ---- U = (I + strict(Khat Ahat^T))^{-1} R, Y = QS + Aq U, S^T += Ahat^T U (tile w)
-        {
-            const f32x4 ta = s.top[lane], qa = s.aq[lane];
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) u = mfma4(ta[m], rr[m], u);
-            f32x4 y = qs;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) y = mfma4(qa[m], u[m], y);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g + r;
-                if (t < n) IO::st(a.out, tok(c0 + t) + col, y[r]);
-            }
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                const f32x4 aa = lds4(&s.at[(16 * q + i) * TS + 4 * g]);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) ST[q] = mfma4(aa[m], u[m], ST[q]);
-            }
-        }
-        __syncthreads();  // chunk tiles free for the next chunk
+        lds_sync();  // chunk tiles free for the next chunk
     }
 
+    if (a.A_out && seg1 == T) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        if (a.A_out)
+        for (int q = 0; q < NQ; ++q)
             *reinterpret_cast<float4 *>(a.A_out + sb + static_cast<int64_t>(col) * D + 16 * q + 4 * g) =
                 make_float4(AT[q][0], AT[q][1], AT[q][2], AT[q][3]);
-        if (a.S_out)
-            *reinterpret_cast<float4 *>(a.S_out + sb + static_cast<int64_t>(col) * D + 16 * q + 4 * g) =
-                make_float4(ST[q][0], ST[q][1], ST[q][2], ST[q][3]);
     }
+}
+
+// ================================ state ================================
+// Carry waves of the state kernel: D/16, one 16 x 16 tile of S^T each; with
+// two carries (d = 32) a third wave forms the output on a free SIMD, and with
+// more carries wave 3 forms it (waves take SIMDs in turn, so at d = 96 wave 3
+// is the one carry that has its SIMD to itself).
+template <int D>
+__host__ __device__ constexpr int state_waves() { return D / 16 <= 2 ? D / 16 + 1 : D / 16; }
+template <int D>
+__host__ __device__ constexpr int state_y_wave() { return D / 16 <= 2 ? D / 16 : 3; }
+
+// One workgroup per (b, h, 16 value rows of S).  Carry wave j < D/16 keeps
+// the 16 x 16 tile of S^T at key rows 16j .. 16j + 15 and the workgroup's
+// value columns; the products over the key dimension are summed across the
+// waves through LDS (fixed order, so every wave forms the same sums).
+template <typename IO, int D>
+__global__ __launch_bounds__(64 * state_waves<D>()) void vla_state_kernel(VlaArgs a, const VlaChunk<D> *__restrict__ rec) {
+    constexpr int NW = D / 16;
+    constexpr int YW = state_y_wave<D>();  // the wave that forms the output
+    __shared__ f32x4 part[2][2][NW][64];  // [chunk parity][Khat S^T, Qhat S^T][wave][lane]
+    const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
+    int head, vt;
+    xcd_group_map(blockIdx.x, static_cast<int>(a.B * a.H), NW, head, vt);
+    const int b = head / H, h = head % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, i = lane & 15;
+    const int vcol = 16 * vt + i;
+    const int64_t sb = static_cast<int64_t>(head) * D * D;
+    const int nch = (T + VC - 1) / VC;
+    auto tok = [&](int t) { return ((static_cast<int64_t>(b) * T + t) * H + h) * D; };
+
+    // ST lane (g, i): S^T[16w + 4g + r][vcol] = S[vcol][16w + 4g + r]
+    f32x4 ST = {0.f, 0.f, 0.f, 0.f};
+    if (a.S_in && w < NW) {
+        const float4 x = *reinterpret_cast<const float4 *>(a.S_in + sb + static_cast<int64_t>(vcol) * D + 16 * w + 4 * g);
+        ST = f32x4{x.x, x.y, x.z, x.w};
+    }
+    const VlaChunk<D> *R0 = rec + static_cast<int64_t>(head) * nch;
+    const bool is_carry = w < NW, is_y = w == YW;
+    struct Ops {
+        f32x4 kh, qh, aht, top, aq;
+        float v[4];
+    };
+    // Every wave issues the same loads whatever its role (an output-only wave
+    // reads the last carry's operands and ignores them): with role-dependent
+    // loads the compiler's load-counter waits would drain the whole ring.
+    const int wc = min(w, NW - 1);
+    auto load = [&](int c, Ops &o) {  // past the end: the last chunk again (never used)
+        const int cc = min(c, nch - 1);
+        const VlaChunk<D> &R = R0[cc];
+        o.kh = *reinterpret_cast<const f32x4 *>(&R.kh[i * D + 16 * wc + 4 * g]);
+        o.qh = *reinterpret_cast<const f32x4 *>(&R.qh[i * D + 16 * wc + 4 * g]);
+        o.aht = R.aht[wc][lane];
+        o.aq = R.aq[lane];
+        o.top = R.top[lane];
+        const int t0 = cc * VC, n = min(VC, T - t0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = min(4 * g + r, n - 1);
+            o.v[r] = IO::ld(a.v, tok(t0 + t) + vcol);
+        }
+    };
+    // one chunk's step from its operand set
+    auto step = [&](const Ops &cur, int c) {
+        const int p = c & 1, t0 = c * VC, n = min(VC, T - t0);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        if (is_carry) {
+            // partial Khat S^T and Qhat S^T over this wave's key rows (two
+            // accumulators per product keep the dependent chains short)
+            f32x4 pk0 = mfma4(cur.kh[0], ST[0], zero), pk1 = mfma4(cur.kh[1], ST[1], zero);
+            f32x4 pq0 = mfma4(cur.qh[0], ST[0], zero), pq1 = mfma4(cur.qh[1], ST[1], zero);
+            pk0 = mfma4(cur.kh[2], ST[2], pk0);
+            pk1 = mfma4(cur.kh[3], ST[3], pk1);
+            pq0 = mfma4(cur.qh[2], ST[2], pq0);
+            pq1 = mfma4(cur.qh[3], ST[3], pq1);
+            part[p][0][w][lane] = pk0 + pk1;
+            part[p][1][w][lane] = pq0 + pq1;
+        }
+        lds_sync();
+        // R = V - Khat S^T (rows past the end: v = 0 and khat = 0, so R = 0)
+        f32x4 z = part[p][0][0][lane];
+#pragma unroll
+        for (int j = 1; j < NW; ++j) z += part[p][0][j][lane];
+        f32x4 rr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rr[r] = (4 * g + r < n ? cur.v[r] : 0.f) - z[r];
+        // U = Tc R (every wave forms it, bit for bit the same)
+        f32x4 u0 = mfma4(cur.top[0], rr[0], zero), u1 = mfma4(cur.top[1], rr[1], zero);
+        u0 = mfma4(cur.top[2], rr[2], u0);
+        u1 = mfma4(cur.top[3], rr[3], u1);
+        const f32x4 u = u0 + u1;
+        if (is_carry) {
+            // S^T += Ahat^T U (this wave's key rows)
+            f32x4 d0 = mfma4(cur.aht[0], u[0], zero), d1 = mfma4(cur.aht[1], u[1], zero);
+            d0 = mfma4(cur.aht[2], u[2], d0);
+            d1 = mfma4(cur.aht[3], u[3], d1);
+            ST += d0 + d1;
+        }
+        if (is_y) {  // Y = Qhat S^T + Aq U
+            f32x4 y = part[p][1][0][lane];
+#pragma unroll
+            for (int j = 1; j < NW; ++j) y += part[p][1][j][lane];
+            f32x4 y1 = mfma4(cur.aq[1], u[1], zero);
+            y = mfma4(cur.aq[0], u[0], y);
+            y1 = mfma4(cur.aq[3], u[3], y1);
+            y = mfma4(cur.aq[2], u[2], y);
+            y += y1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r < n) IO::st(a.out, tok(t0 + 4 * g + r) + vcol, y[r]);
+        }
+    };
+    // A ring of NS operand sets: the loads run NS chunks ahead (the records
+    // come from L2 or HBM, a step takes a few hundred cycles); every trip
+    // refills each set it consumes (past the end: the last chunk again,
+    // never used), so the loads in flight always form the same queue.
+    constexpr int NS = 4;
+    Ops o[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) load(j, o[j]);
+    int c = 0;
+    for (; c + NS <= nch; c += NS) {
+        auto trip = [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            step(o[j], c + j);
+            load(c + j + NS, o[j]);
+        };
+        static_for<NS>(trip);
+    }
+    auto tail = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if (c + j < nch) step(o[j], c + j);
+    };
+    static_for<NS>(tail);
+    if (a.S_out && is_carry)
+        *reinterpret_cast<float4 *>(a.S_out + sb + static_cast<int64_t>(vcol) * D + 16 * w + 4 * g) =
+            make_float4(ST[0], ST[1], ST[2], ST[3]);
 }
 
 template <typename IO, int D>
 hipError_t launch_d(const VlaArgs &a, hipStream_t stream) {
-    const unsigned blocks = static_cast<unsigned>(a.B * a.H);
-    vla_chunked_kernel<IO, D><<<dim3(blocks), dim3(64 * (D / 16)), 0, stream>>>(a);
+    const VlaLayout L = vla_layout<D>(a.B, a.T, a.H);
+    char *ws = static_cast<char *>(a.ws);
+    unsigned int *status = reinterpret_cast<unsigned int *>(ws);
+    float *G = reinterpret_cast<float *>(ws + L.g_off);
+    float *Aseg = reinterpret_cast<float *>(ws + L.a_off);
+    VlaChunk<D> *rec = reinterpret_cast<VlaChunk<D> *>(ws + L.rec_off);
+    const int nseg = static_cast<int>(L.nseg);
+    const unsigned heads = static_cast<unsigned>(a.B * a.H);
+    if (nseg > 1) {
+        vla_gram_kernel<IO, D><<<heads * (nseg - 1), 64 * (D / 16), 0, stream>>>(a, G, nseg, status);
+        vla_inverse_kernel<D><<<heads * (nseg - 1), 256, 0, stream>>>(a, G, Aseg, nseg);
+    }
+    vla_alpha_kernel<IO, D><<<heads * nseg, 64 * (D / 16), 0, stream>>>(a, Aseg, rec, nseg, status);
+    vla_state_kernel<IO, D><<<heads * (D / 16), 64 * state_waves<D>(), 0, stream>>>(a, rec);
     return hipGetLastError();
 }
 
@@ -477,9 +838,17 @@ bool vla_chunked_supported(const VlaArgs &a) {
     return a.d == 32 || a.d == 64 || a.d == 96 || a.d == 128;
 }
 
-// The single-kernel schedule keeps every intermediate in LDS and registers.
-bool vla_chunked_workspace(const VlaArgs &, size_t *bytes) {
-    *bytes = 0;
+bool vla_chunked_workspace(const VlaArgs &a, size_t *bytes) {
+    VlaLayout L;
+    switch (a.d) {
+        case 32: L = vla_layout<32>(a.B, a.T, a.H); break;
+        case 64: L = vla_layout<64>(a.B, a.T, a.H); break;
+        case 96: L = vla_layout<96>(a.B, a.T, a.H); break;
+        case 128: L = vla_layout<128>(a.B, a.T, a.H); break;
+        default: return false;
+    }
+    if (a.B * a.H * L.nseg > 0x7fffffff) return false;
+    *bytes = L.bytes;
     return true;
 }
 

@@ -480,3 +480,23 @@ def test_non_finite_inputs_propagate(variant, algo):
         assert np.max(np.abs(y[:first] - yr[:first])) <= U.BF16_ABS
         s, sr = got[1][b, h], ref[1][b, h]
         assert np.all(~np.isfinite(s[~np.isfinite(sr)]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+def test_vla_chunked_segments_chained(d, dtype):
+    """Sequences long enough for several segments of the inverse-penalty
+    chain (each segment past the first starts from an inverted penalty), in
+    two calls chained through (A, S), so the second call's segment starts
+    also invert the carried-in A; every element against the oracle."""
+    w = I.Workload(f"vla_{dtype}_B2_T700_H2_d{d}", "vla", dtype, 2, 700, 2, d, d, seed=6300 + d)
+    x = I.make_inputs(w)
+    ref = U.run_oracle(w, x)
+    first = {k: v[:, :290] for k, v in x.items()}
+    second = {k: v[:, 290:] for k, v in x.items()}
+    g1 = U.run_gpu(w.replace(T=290), first, algo="chunked")
+    g2 = U.run_gpu(w.replace(T=410), second, A_in=g1[1], S_in=g1[2], algo="chunked")
+    got = (np.concatenate([g1[0], g2[0]], 1), g2[1], g2[2])
+    # fp32 arithmetic throughout: A and S are held to the fp32 gate for
+    # either storage dtype; bf16 outputs take the bf16 gates
+    U.check(w, got, ref, label=w.name + " chained", exact_f32=True)
