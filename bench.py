@@ -30,11 +30,14 @@ MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 matrix-core peak
 FP32_PEAK_TFS = 157.3
 
 
-def algorithmic_bytes(w) -> int:
+def algorithmic_bytes(w, decode=False) -> int:
     """Every input read once, out and the final state written once (no
-    initial state), in the storage dtype."""
+    initial state), in the storage dtype.  A decode step also reads the
+    state it updates."""
     es = 2 if w.dtype == "bf16" else 4
     n_th = w.B * w.T * w.H
+    if decode:
+        return algorithmic_bytes(w) + w.B * w.H * w.dv * w.dk * 4
     if w.variant == "vla":
         per = 5 * w.dk * es                                   # q, k, v, p, out
         state = 2 * w.B * w.H * w.dk * w.dk * 4               # A_out, S_out
@@ -134,7 +137,8 @@ def cpu_baseline(w, x, batch_rows: int, min_seconds: float):
             oracle.vla_forward(sl["q"], sl["k"], sl["v"], sl["p"], nthreads=th)
         else:
             oracle.delta_forward(w.variant, sl["q"], sl["k"], sl["v"], sl["beta"], alpha=sl.get("alpha"),
-                                 erase_b=sl.get("erase_b"), write_w=sl.get("write_w"), nthreads=th)
+                                 erase_b=sl.get("erase_b"), write_w=sl.get("write_w"),
+                                 state_in=sl.get("state_in"), nthreads=th)
         dt += time.perf_counter() - t0
         reps += 1
     return {"value": reps * batch_rows * w.T / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
@@ -185,13 +189,21 @@ def main():
         sys.exit(1)
 
     name = args.workload or I.METRIC_WORKLOAD
-    w = I.WORKLOADS[name]
+    decode = name in I.DECODE_WORKLOADS
+    w = I.DECODE_WORKLOADS[name] if decode else I.WORKLOADS[name]
     x = I.make_inputs(w)
     dev = torch.device("cuda:0")
     copies = [I.to_device(x, w.dtype, dev) for _ in range(max(1, args.copies))]
+    if decode:  # one token per stream: [N, 1, H, d] -> [N, H, d]
+        copies = [{n: t[:, 0].contiguous() for n, t in g.items()} for g in copies]
+        s0 = np.random.default_rng(w.seed).standard_normal((w.B, w.H, w.dv, w.dk)) * 0.1
+        x["state_in"] = s0.astype(np.float32).astype(np.float64)
     outs = []
     for g in copies:
-        if w.variant == "vla":
+        if decode:
+            outs.append((torch.empty((w.B, w.H, w.dv), dtype=g["q"].dtype, device=dev),
+                         torch.from_numpy(x["state_in"].astype(np.float32)).to(dev)))
+        elif w.variant == "vla":
             outs.append((torch.empty((w.B, w.T, w.H, w.dv), dtype=g["q"].dtype, device=dev),
                          torch.empty((w.B, w.H, w.dk, w.dk), dtype=torch.float32, device=dev),
                          torch.empty((w.B, w.H, w.dk, w.dk), dtype=torch.float32, device=dev)))
@@ -201,7 +213,9 @@ def main():
     stream = torch.cuda.current_stream()
     # one caller-owned workspace for every step: the steps run in order on
     # one stream, so each may reuse it
-    if w.variant == "vla":
+    if decode:
+        nws = 0
+    elif w.variant == "vla":
         nws = lam.vla_workspace_size(w.dtype, w.B, w.T, w.H, w.dk, algo=args.algo)
     else:
         nws = lam.workspace_size(w.variant, w.dtype, w.B, w.T, w.H, w.dk, w.dv, algo=args.algo)
@@ -209,7 +223,10 @@ def main():
 
     def step(i):
         g, o = copies[i % len(copies)], outs[i % len(outs)]
-        if w.variant == "vla":
+        if decode:
+            lam.step(w.variant, g["q"], g["k"], g["v"], g["beta"], alpha=g.get("alpha"),
+                     erase_b=g.get("erase_b"), write_w=g.get("write_w"), state=o[1], out=o[0])
+        elif w.variant == "vla":
             lam.vla_forward(g["q"], g["k"], g["v"], g["p"], algo=args.algo, out=o[0], A_out=o[1],
                             S_out=o[2], workspace=wsp)
         else:
@@ -258,7 +275,9 @@ def main():
 
     tokens = w.B * w.T
     value = tokens * args.steps / wall
-    if w.variant == "vla":
+    if decode:
+        ran = "step"
+    elif w.variant == "vla":
         # the VLA entry point runs the chunked schedule for any T > 0 unless told otherwise
         ran = args.algo if args.algo != "auto" else ("chunked" if w.T > 0 else "recurrent")
     else:
@@ -269,7 +288,7 @@ def main():
     # chunked schedule uses fp32 matrix-core products for every dtype
     arith_dtype = "bf16" if (ran == "chunked" and w.dtype == "bf16" and w.variant != "vla") else "f32"
     mean_launch_s = mean_launch_ms / 1e3
-    abytes = algorithmic_bytes(w)
+    abytes = algorithmic_bytes(w, decode)
     aflops = algorithmic_flops(w)
     achieved_gbs = abytes / mean_launch_s / 1e9
     # the binding roofline: HBM bytes, or the algorithmic flops on the unit
@@ -277,6 +296,8 @@ def main():
     # the fp32 vector ALU for the recurrent ones), whichever takes longer
     if ran == "chunked":
         cpeak, cbound = (MFMA_BF16_PEAK_TFS if arith_dtype == "bf16" else FP32_PEAK_TFS), "mfma"
+    elif ran == "step":
+        cpeak, cbound = FP32_PEAK_TFS, "alu"
     else:
         cpeak, cbound = FP32_PEAK_TFS, "alu"
     achieved_tfs = aflops / mean_launch_s / 1e12
@@ -319,10 +340,13 @@ def main():
     if not args.no_cpu_baseline:
         rows = min(w.B, args.cpu_rows or w.B)
         cpu = cpu_baseline(w, x, rows, args.cpu_seconds)
+        if decode:
+            cpu["sample"] = cpu["sample"].replace("tokens)", "tokens, one decode step each from the same state)")
 
     line = {
         "metric": "gated delta-rule fwd tokens/s, B8 T4096 H8 d128; % of HBM/MFMA roofline"
-        if name == I.METRIC_WORKLOAD else f"{w.variant} fwd tokens/s, {name}",
+        if name == I.METRIC_WORKLOAD else (f"{w.variant} decode tokens/s (one token per stream per call), {name}"
+                                           if decode else f"{w.variant} fwd tokens/s, {name}"),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,

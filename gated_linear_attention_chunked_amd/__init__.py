@@ -16,7 +16,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["forward", "vla_forward", "select_algo", "workspace_size", "vla_workspace_size",
+__all__ = ["forward", "vla_forward", "step", "vla_step", "select_algo", "workspace_size", "vla_workspace_size",
            "set_device_checks", "library", "LamError", "LamDeviceError", "VARIANTS", "ALGOS",
            "LIB_PATH"]
 
@@ -83,6 +83,10 @@ def library() -> ctypes.CDLL:
             lib.lam_vla_forward.restype = ci
             lib.lam_vla_workspace_size.argtypes = [ci, i64, i64, i64, i64, ci, ctypes.POINTER(sz)]
             lib.lam_vla_workspace_size.restype = ci
+            lib.lam_step.argtypes = [ci, ci, i64, i64, i64, i64] + [vp] * 9 + [vp]
+            lib.lam_step.restype = ci
+            lib.lam_vla_step.argtypes = [ci, i64, i64, i64] + [vp] * 7 + [vp]
+            lib.lam_vla_step.restype = ci
             lib.lam_status_string.argtypes = [ci]
             lib.lam_status_string.restype = ctypes.c_char_p
             lib.lam_abi_version.restype = ci
@@ -279,3 +283,71 @@ def vla_forward(q, k, v, p, A_in=None, S_in=None, *, algo="auto", out=None, A_ou
         raise LamError(rc, "lam_vla_forward")
     _after_call(ws, "lam_vla_forward")
     return out, A_out, S_out
+
+
+def step(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None, *, state, out=None,
+         stream=None):
+    """One-token decode step for N streams, the memory updated in place.
+
+    q, k: [N,H,dk]; v: [N,H,dv]; beta: [N,H]; alpha: [N,H] ("gdn", "gdn2") or
+    [N,H,dk] ("kda"); erase_b [N,H,dk] and write_w [N,H,dv] for "gdn2";
+    state: fp32 [N,H,dv,dk], read and overwritten.  Returns out [N,H,dv].
+    """
+    import torch
+
+    var = VARIANTS[variant]
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    dt, dev = q.dtype, q.device
+    _check(q, "q", (N, H, dk), dt, dev)
+    _check(k, "k", (N, H, dk), dt, dev)
+    _check(v, "v", (N, H, dv), dt, dev)
+    _check(beta, "beta", (N, H), dt, dev)
+    if var == VARIANTS["kda"]:
+        _check(alpha, "alpha", (N, H, dk), dt, dev)
+    elif var != VARIANTS["deltanet"]:
+        _check(alpha, "alpha", (N, H), dt, dev)
+    else:
+        alpha = None
+    if var == VARIANTS["gdn2"]:
+        _check(erase_b, "erase_b", (N, H, dk), dt, dev)
+        _check(write_w, "write_w", (N, H, dv), dt, dev)
+    else:
+        erase_b = write_w = None
+    if state is None:
+        raise ValueError("state: required (updated in place)")
+    _check(state, "state", (N, H, dv, dk), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dt, device=dev)
+    _check(out, "out", (N, H, dv), dt, dev)
+    rc = library().lam_step(var, _dtype_code(q), N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                            _ptr(erase_b), _ptr(write_w), _ptr(beta), _ptr(state), _ptr(out),
+                            _stream(stream))
+    if rc != 0:
+        raise LamError(rc, "lam_step")
+    _after_call(None, "lam_step")
+    return out
+
+
+def vla_step(q, k, v, p, A, S, *, out=None, stream=None):
+    """One-token VLA step for N streams: q, k, v, p [N,H,d]; A and S fp32
+    [N,H,d,d] updated in place.  Returns out [N,H,d]."""
+    import torch
+
+    N, H, d = q.shape
+    dt, dev = q.dtype, q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("p", p)):
+        _check(t, n, (N, H, d), dt, dev)
+    if A is None or S is None:
+        raise ValueError("A and S: required (updated in place)")
+    _check(A, "A", (N, H, d, d), torch.float32, dev)
+    _check(S, "S", (N, H, d, d), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, d), dtype=dt, device=dev)
+    _check(out, "out", (N, H, d), dt, dev)
+    rc = library().lam_vla_step(_dtype_code(q), N, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(p), _ptr(A),
+                                _ptr(S), _ptr(out), _stream(stream))
+    if rc != 0:
+        raise LamError(rc, "lam_vla_step")
+    _after_call(None, "lam_vla_step")
+    return out

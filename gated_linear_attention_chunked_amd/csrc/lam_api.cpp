@@ -229,6 +229,61 @@ lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, 
     return from_hip(lam::launch_delta_recurrent(a, stream));
 }
 
+lam_status lam_step(int variant, int dtype, int64_t N, int64_t H, int64_t dk, int64_t dv,
+                    const void *q, const void *k, const void *v, const void *alpha,
+                    const void *erase_b, const void *write_w, const void *beta, float *state,
+                    void *out, hipStream_t stream) {
+    lam_status st = check_delta_shape(variant, dtype, N, 1, H, dk, dv, LAM_ALGO_RECURRENT);
+    if (st != LAM_OK) return st;
+    if (N == 0 || H == 0) return LAM_OK;
+    if (!state) return LAM_ERR_INVALID_ARG;
+    lam::DeltaArgs a = shape_args(variant, dtype, N, 1, H, dk, dv);
+    if (!lam::delta_step_supported(a))  // dk = 96: the token-recurrent kernel, one token
+        return lam_forward(variant, dtype, N, 1, H, dk, dv, q, k, v, alpha, erase_b, write_w, beta,
+                           state, out, state, nullptr, 0, LAM_ALGO_RECURRENT, stream);
+    // the argument checks of a one-token lam_forward (no workspace: recurrent)
+    int64_t nk, nv, ns, nst;
+    elems(N, 1, H, dk, nk);
+    elems(N, 1, H, dv, nv);
+    elems(N, 1, H, 1, ns);
+    elems(N, 1, H, dk * dv, nst);
+    if (!q || !k || !v || !beta || !out) return LAM_ERR_INVALID_ARG;
+    if (variant != LAM_DELTANET && !alpha) return LAM_ERR_INVALID_ARG;
+    if (variant == LAM_GATED_DELTANET2 && (!erase_b || !write_w)) return LAM_ERR_INVALID_ARG;
+    const int64_t es = dtype == LAM_BF16 ? 2 : 4;
+    const int64_t ob = nv * es;
+    const int64_t alpha_bytes = (variant == LAM_KIMI_DELTA ? nk : ns) * es;
+    if (overlaps(out, ob, q, nk * es) || overlaps(out, ob, k, nk * es) || overlaps(out, ob, v, nv * es) ||
+        overlaps(out, ob, beta, ns * es) ||
+        (variant != LAM_DELTANET && overlaps(out, ob, alpha, alpha_bytes)) ||
+        (variant == LAM_GATED_DELTANET2 &&
+         (overlaps(out, ob, erase_b, nk * es) || overlaps(out, ob, write_w, nv * es))) ||
+        overlaps(out, ob, state, nst * 4))
+        return LAM_ERR_INVALID_ARG;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = variant == LAM_DELTANET ? nullptr : alpha;
+    a.erase_b = variant == LAM_GATED_DELTANET2 ? erase_b : nullptr;
+    a.write_w = variant == LAM_GATED_DELTANET2 ? write_w : nullptr;
+    a.beta = beta;
+    a.state_in = state;
+    a.out = out;
+    a.state_out = state;
+    return from_hip(lam::launch_delta_step(a, stream));
+}
+
+lam_status lam_vla_step(int dtype, int64_t N, int64_t H, int64_t d, const void *q, const void *k,
+                        const void *v, const void *p, float *A, float *S, void *out,
+                        hipStream_t stream) {
+    lam_status st = check_vla_shape(dtype, N, 1, H, d, LAM_ALGO_RECURRENT);
+    if (st != LAM_OK) return st;
+    if (N == 0 || H == 0) return LAM_OK;
+    if (!A || !S) return LAM_ERR_INVALID_ARG;
+    return lam_vla_forward(dtype, N, 1, H, d, q, k, v, p, A, S, out, A, S, nullptr, 0,
+                           LAM_ALGO_RECURRENT, stream);
+}
+
 lam_status lam_vla_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, int64_t d, int algo,
                                   size_t *bytes) {
     if (!bytes) return LAM_ERR_INVALID_ARG;

@@ -61,6 +61,10 @@ bool vla_chunked_supported(const VlaArgs &a);
 bool vla_chunked_workspace(const VlaArgs &a, size_t *bytes);
 hipError_t launch_vla_chunked(const VlaArgs &a, hipStream_t stream);
 
+// One-token decode step, memory updated in place (state_in == state_out).
+bool delta_step_supported(const DeltaArgs &a);
+hipError_t launch_delta_step(const DeltaArgs &a, hipStream_t stream);
+
 // Kimi Delta (per-channel decay) has its own chunked kernel.
 bool kda_chunked_supported(const DeltaArgs &a);
 bool kda_chunked_workspace(const DeltaArgs &a, size_t *bytes);

@@ -73,6 +73,15 @@ WORKLOADS = {
 # The throughput workload: Gated DeltaNet, bf16 streams, fp32 state.
 METRIC_WORKLOAD = "gdn_bf16_B8_T4096_H8_d128"
 
+# Decode workloads: one token for each of B streams per call, the fp32 state
+# (B x H x dv x dk) resident in HBM and updated in place.
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("gdn_step_bf16_N256_H8_d128", "gdn", "bf16", 256, 1, 8, 128, 128, seed=9, gate_mu=2.0),
+    )
+}
+
 
 def round_f32(x: np.ndarray) -> np.ndarray:
     """float64 -> float32, round to nearest even (numpy's cast)."""

@@ -175,6 +175,38 @@ lam_status lam_vla_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, in
                                   int algo, size_t *bytes);
 
 /*
+ * One-token decode step for N concurrent streams: the rule above applied to
+ * one token per (stream, head), the memory updated in place ("Mechanisms,
+ * trade-offs and cross-layer routing of linear-attention architectures",
+ * "Technical details"; the fixed-size state that lets a stream decode with no
+ * cache of past tokens is section 5 of the VLA summary).  Equivalent to
+ * lam_forward with B = N, T = 1 and state_in = state_out = state.
+ *   q, k         [N,H,dk]     v, out  [N,H,dv]     beta, scalar alpha [N,H]
+ *   alpha        Kimi Delta: [N,H,dk]; erase_b [N,H,dk], write_w [N,H,dv]
+ *                (Gated DeltaNet-2)
+ *   state        [N,H,dv,dk] fp32, required, read and overwritten
+ * Needs no workspace.  The step reads and writes the whole state once, so it
+ * is bound by HBM; dk in {32, 64, 128} runs a dedicated kernel, dk = 96 the
+ * token-recurrent one.  Errors as lam_forward (state NULL or overlapping
+ * out: LAM_ERR_INVALID_ARG).
+ */
+lam_status lam_step(int variant, int dtype, int64_t N, int64_t H, int64_t dk, int64_t dv,
+                    const void *q, const void *k, const void *v, const void *alpha,
+                    const void *erase_b, const void *write_w, const void *beta, float *state,
+                    void *out, hipStream_t stream);
+
+/*
+ * One-token VLA step for N concurrent streams ("Technical summary:
+ * Variational Linear Attention (VLA)", sections 2.2-2.3 and 5): q, k, v, p
+ * [N,H,d], A and S [N,H,d,d] fp32 updated in place (both required), out
+ * [N,H,d].  Equivalent to lam_vla_forward with T = 1 and in-place states, on
+ * the token-recurrent kernel.
+ */
+lam_status lam_vla_step(int dtype, int64_t N, int64_t H, int64_t d, const void *q, const void *k,
+                        const void *v, const void *p, float *A, float *S, void *out,
+                        hipStream_t stream);
+
+/*
  * lam_forward for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation).  The
  * same arguments, schedules, kernels and results as lam_forward, with the

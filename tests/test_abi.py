@@ -37,7 +37,8 @@ def _declared():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert {"lam_forward", "lam_vla_forward", "lam_forward_workspace_size", "lam_vla_workspace_size",
-            "lam_status_string", "lam_abi_version"} <= set(names)
+            "lam_step", "lam_vla_step", "lam_forward_noalloc", "lam_status_string",
+            "lam_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -182,3 +183,25 @@ def test_forward_rejects_bad_workspace(lib):
     assert _fwd(lib, ws=FAKE, ws_bytes=need) == INVALID             # overlaps q
     assert _fwd(lib, ws=FAKE + 0x70000000, ws_bytes=need) == INVALID  # overlaps out
     assert _fwd(lib, sout=WS + 1024, ws=WS, ws_bytes=need) == INVALID  # overlaps state_out
+
+
+def _step(lib, variant=1, dtype=1, N=4, H=2, dk=64, dv=64, q=FAKE, k=FAKE + 0x10000000,
+          v=FAKE + 0x20000000, alpha=FAKE + 0x30000000, eb=FAKE + 0x40000000, ww=FAKE + 0x50000000,
+          beta=FAKE + 0x60000000, state=FAKE + 0x80000000, out=FAKE + 0x70000000):
+    return lib.lam_step(variant, dtype, N, H, dk, dv, q, k, v, alpha, eb, ww, beta, state, out, None)
+
+
+def test_step_rejects_bad_arguments(lib):
+    assert _step(lib, variant=7) == INVALID
+    assert _step(lib, dtype=3) == INVALID
+    assert _step(lib, N=-1) == INVALID
+    assert _step(lib, dk=48) == UNSUPPORTED
+    assert _step(lib, state=None) == INVALID                   # the state is updated in place
+    for name in ("q", "k", "v", "beta", "out"):
+        assert _step(lib, **{name: None}) == INVALID, name
+    assert _step(lib, alpha=None) == INVALID
+    assert _step(lib, variant=3, eb=None) == INVALID
+    assert _step(lib, out=FAKE + 0x80000000 + 64) == INVALID   # out inside the state
+    assert _step(lib, N=0, q=None, k=None, v=None, beta=None, out=None, state=None) == OK
+    assert lib.lam_vla_step(0, 2, 2, 32, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == INVALID
+    assert lib.lam_vla_step(0, 2, 2, 40, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED

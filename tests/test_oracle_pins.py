@@ -428,6 +428,40 @@ def test_vla_chained_calls_equal_one_call():
     np.testing.assert_allclose(S2, S, rtol=1e-13, atol=1e-13)
 
 
+# ------------------------------------ decode: one token at a time (P-9)
+@pytest.mark.parametrize("variant", ["deltanet", "gdn", "kda", "gdn2"])
+def test_token_by_token_equals_one_call(variant):
+    """A decode step is the scan over one token with the state carried in and
+    out: T one-token calls chained through the state give the T-token scan."""
+    d = _rand_delta(72, B=2, T=9, H=2, variant=variant)
+    out, st = _run(variant, d)
+    keys = ("q", "k", "v", "beta", "alpha", "erase_b", "write_w")
+    state, outs = d.get("state_in"), []
+    for t in range(9):
+        dt = dict(d, **{n: d[n][:, t:t + 1] for n in keys if d.get(n) is not None}, state_in=state)
+        o, state = _run(variant, dt)
+        outs.append(o)
+    np.testing.assert_allclose(np.concatenate(outs, axis=1), out, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(state, st, rtol=1e-13, atol=1e-13)
+
+
+def test_vla_token_by_token_equals_one_call():
+    r = rng0(73)
+    B, T, H, d = 1, 8, 2, 5
+    q, k, v = (r.standard_normal((B, T, H, d)) for _ in range(3))
+    p = r.standard_normal((B, T, H, d)) / np.sqrt(d)
+    out, A, S = oracle.vla_forward(q, k, v, p)
+    A_t = S_t = None
+    outs = []
+    for t in range(T):
+        o, A_t, S_t = oracle.vla_forward(q[:, t:t + 1], k[:, t:t + 1], v[:, t:t + 1], p[:, t:t + 1],
+                                         A_in=A_t, S_in=S_t)
+        outs.append(o)
+    np.testing.assert_allclose(np.concatenate(outs, 1), out, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(A_t, A, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(S_t, S, rtol=1e-13, atol=1e-13)
+
+
 # ---------------------------------------- layout, causality, independence
 @pytest.mark.parametrize("variant", ["gdn", "kda", "gdn2"])
 def test_chains_are_independent_and_layout_is_row_major(variant):

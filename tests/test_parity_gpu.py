@@ -500,3 +500,70 @@ def test_vla_chunked_segments_chained(d, dtype):
     # fp32 arithmetic throughout: A and S are held to the fp32 gate for
     # either storage dtype; bf16 outputs take the bf16 gates
     U.check(w, got, ref, label=w.name + " chained", exact_f32=True)
+
+
+def _step_run(w, x, s0):
+    """lam.step over the T tokens of x one at a time (state in place)."""
+    import torch
+
+    import gated_linear_attention_chunked_amd as lam
+
+    g = I.to_device(x, w.dtype, "cuda")
+    state = torch.from_numpy(s0.astype(np.float32)).cuda()
+    outs = []
+    for t in range(w.T):
+        sl = lambda n: None if g.get(n) is None else g[n][:, t].contiguous()
+        outs.append(lam.step(w.variant, sl("q"), sl("k"), sl("v"), sl("beta"), alpha=sl("alpha"),
+                             erase_b=sl("erase_b"), write_w=sl("write_w"), state=state))
+    torch.cuda.synchronize()
+    return (torch.stack(outs, 1).float().cpu().numpy().astype(np.float64),
+            state.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", DELTA)
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (32, 96), (96, 64), (128, 32)])
+def test_step_matches_scan(variant, dtype, dk, dv):
+    """The decode step, one token at a time for N streams with the memory
+    updated in place, against the oracle's scan over the same tokens from the
+    same initial memory; every element.  dk = 96 takes the token-recurrent
+    kernel, the others the dedicated step kernel."""
+    w = _w(variant, dtype, 5, 12, 3, dk, dv, seed=7600 + dk + dv, gate_mu=0.0)
+    x = I.make_inputs(w)
+    s0 = (np.random.default_rng(dk + dv).standard_normal((5, 3, dv, dk)) * 0.2).astype(np.float32)
+    got = _step_run(w, x, s0)
+    ref = U.run_oracle(w, x, state_in=s0.astype(np.float64))
+    U.check(w, got, ref, label=w.name + " step", exact_f32=True)
+
+
+@pytest.mark.parametrize("variant", ["gdn", "kda"])
+def test_step_full_decode_shape(variant):
+    """One step at the decode bench shape (256 streams x 8 heads, d = 128,
+    bf16 tokens) from a random fp32 memory: every element."""
+    w = _w(variant, "bf16", 256, 1, 8, 128, 128, seed=7650, gate_mu=2.0)
+    x = I.make_inputs(w)
+    s0 = (np.random.default_rng(3).standard_normal((256, 8, 128, 128)) * 0.1).astype(np.float32)
+    got = _step_run(w, x, s0)
+    ref = U.run_oracle(w, x, state_in=s0.astype(np.float64))
+    U.check(w, got, ref, label=w.name + " step", exact_f32=True)
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+def test_vla_step_matches_scan(d):
+    """lam_vla_step, one token at a time for N streams with A and S updated
+    in place, against the oracle's VLA scan; every element."""
+    import torch
+
+    import gated_linear_attention_chunked_amd as lam
+
+    w = I.Workload(f"vla_f32_B3_T10_H2_d{d}", "vla", "f32", 3, 10, 2, d, d, seed=7700 + d)
+    x = I.make_inputs(w)
+    g = I.to_device(x, "f32", "cuda")
+    A = torch.eye(d, device="cuda").expand(3, 2, d, d).contiguous()
+    S = torch.zeros(3, 2, d, d, device="cuda")
+    outs = [lam.vla_step(*(g[n][:, t].contiguous() for n in ("q", "k", "v", "p")), A, S)
+            for t in range(w.T)]
+    torch.cuda.synchronize()
+    got = (torch.stack(outs, 1).cpu().numpy().astype(np.float64), A.cpu().numpy().astype(np.float64),
+           S.cpu().numpy().astype(np.float64))
+    U.check(w, got, U.run_oracle(w, x), label=w.name + " step")
