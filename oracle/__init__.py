@@ -71,6 +71,8 @@ def _lib(prec: str = "f64") -> ctypes.CDLL:
             lib.oracle_delta_forward.restype = ctypes.c_int
             lib.oracle_vla_forward.argtypes = [L, L, L, L] + [dp] * 13 + [ctypes.c_int]
             lib.oracle_vla_forward.restype = ctypes.c_int
+            lib.oracle_delta_backward.argtypes = [ctypes.c_int, L, L, L, L, L] + [dp] * 18 + [ctypes.c_int]
+            lib.oracle_delta_backward.restype = ctypes.c_int
             lib.oracle_real_bytes.restype = ctypes.c_int
             _loaded[prec] = lib
         return _loaded[prec]
@@ -129,6 +131,50 @@ def delta_forward(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None
     if rc != 0:
         raise RuntimeError("oracle_delta_forward failed")
     return out, state_out
+
+
+def delta_backward(variant, q, k, v, beta, dout, alpha=None, erase_b=None, write_w=None,
+                   state_in=None, dstate_out=None, nthreads=0, precision="f64"):
+    """Gradients of sum(dout * out) + sum(dstate_out * state_out) for the
+    forward of ``delta_forward`` on the same inputs (reverse-mode adjoint,
+    token by token).  Returns a dict of float64 arrays: dq, dk, dv, dbeta,
+    dalpha (gated variants), derase_b and dwrite_w (gdn2), dstate_in."""
+    var = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    q = _in(q)
+    B, T, H, dk = q.shape
+    k = _in(k, (B, T, H, dk))
+    v = _in(v)
+    dv = v.shape[3]
+    beta = _in(beta, (B, T, H))
+    dout = _in(dout, (B, T, H, dv))
+    if var == DELTANET:
+        alpha = None
+    elif var == KIMI_DELTA:
+        alpha = _in(alpha, (B, T, H, dk))
+    else:
+        alpha = _in(alpha, (B, T, H))
+    if var == GATED_DELTANET2:
+        erase_b = _in(erase_b, (B, T, H, dk))
+        write_w = _in(write_w, (B, T, H, dv))
+    else:
+        erase_b = write_w = None
+    state_in = _in(state_in, (B, H, dv, dk))
+    dstate_out = _in(dstate_out, (B, H, dv, dk))
+    g = {"dq": np.zeros((B, T, H, dk)), "dk": np.zeros((B, T, H, dk)), "dv": np.zeros((B, T, H, dv)),
+         "dbeta": np.zeros((B, T, H)), "dstate_in": np.zeros((B, H, dv, dk))}
+    if alpha is not None:
+        g["dalpha"] = np.zeros(alpha.shape)
+    if var == GATED_DELTANET2:
+        g["derase_b"] = np.zeros((B, T, H, dk))
+        g["dwrite_w"] = np.zeros((B, T, H, dv))
+    rc = _lib(precision).oracle_delta_backward(
+        var, B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase_b), _ptr(write_w),
+        _ptr(beta), _ptr(state_in), _ptr(dout), _ptr(dstate_out), _ptr(g["dq"]), _ptr(g["dk"]),
+        _ptr(g["dv"]), _ptr(g.get("dalpha")), _ptr(g.get("derase_b")), _ptr(g.get("dwrite_w")),
+        _ptr(g["dbeta"]), _ptr(g["dstate_in"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_delta_backward failed")
+    return g
 
 
 def vla_forward(q, k, v, p, A_in=None, S_in=None, diagnostics=False, nthreads=0,

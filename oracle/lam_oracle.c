@@ -177,6 +177,221 @@ int oracle_delta_forward(int variant, long B, long T, long H, long dk, long dv,
     return failed ? -1 : 0;
 }
 
+/*
+ * Backward pass of the delta-rule family, one (b, h) chain: the gradients of
+ * L = sum_t <dout_t, y_t> + <dstate_out, W_T> with respect to every input,
+ * by reverse-mode differentiation of the per-token steps above (the pages
+ * give the forward rule only; this is that rule's adjoint, derived here and
+ * pinned against central finite differences of oracle_delta_forward).
+ *
+ * Forward, per token (kk = read key, z = target, W~ = decayed memory):
+ *   W~ = decay(W_{t-1});  r = z - W~ kk;  W_t = W~ + beta r k^T;  y_t = W_t q.
+ * Reverse, with G the adjoint of W_t (G = dstate_out, or 0, before the last
+ * token), for t = T-1 .. 0:
+ *   G     += dout_t q^T                         (the read)
+ *   dq_t   = W_t^T dout_t
+ *   g      = G k                                (rows of G along the write key)
+ *   dbeta_t = r . g;  dz = beta g               (the write's scale and target)
+ *   dk_t   = beta G^T r + (read key's part of -beta W~^T g)
+ *   dW~    = G - beta g kk^T
+ *   decay: Gated DeltaNet(-2): dalpha_t = <dW~, W_{t-1}>, G = alpha dW~;
+ *          Kimi Delta: dalpha_t[j] = sum_i dW~_ij W_{t-1,ij}, G = dW~ diag(alpha);
+ *          DeltaNet: G = dW~.
+ *   Gated DeltaNet-2 (kk = b*k, z = w*v): dv = w*dz, dw = v*dz,
+ *          dkk = -beta W~^T g, db = k*dkk, dk_t += b*dkk; the others: dv = dz,
+ *          dk_t += dkk.
+ * After token 0, dstate_in = G.  The forward states W_0 .. W_{T-1} are kept
+ * (T dv dk reals per chain), which is the plain way to have them in reverse.
+ */
+static void delta_chain_bwd(int variant, long b, long h, long T, long H, long dk, long dv,
+                            const double *q, const double *k, const double *v,
+                            const double *alpha, const double *erase_b,
+                            const double *write_w, const double *beta,
+                            const double *state_in, const double *dout,
+                            const double *dstate_out, double *dq, double *dkg,
+                            double *dvg, double *dalpha, double *derase_b,
+                            double *dwrite_w, double *dbeta, double *dstate_in,
+                            real *Ws, real *Wt, real *G, real *kk, real *z, real *r,
+                            real *g, real *dkk) {
+    const long n = dv * dk;
+    /* forward, keeping W_{t-1} for every t */
+    for (long i = 0; i < n; ++i) Ws[i] = state_in ? (real)state_in[st(b, h, H, dv, dk) + i] : (real)0;
+    for (long t = 0; t < T; ++t) {
+        real *Wp = Ws + t * n, *Wn = Ws + (t + 1) * n;
+        const double *kt = k + tok(b, t, h, T, H, dk);
+        const double *vt = v + tok(b, t, h, T, H, dv);
+        const real bt = (real)beta[tok(b, t, h, T, H, 1)];
+        for (long i = 0; i < n; ++i) Wn[i] = Wp[i];
+        if (variant == ORACLE_GATED_DELTANET || variant == ORACLE_GATED_DELTANET2) {
+            const real a = (real)alpha[tok(b, t, h, T, H, 1)];
+            for (long i = 0; i < n; ++i) Wn[i] = a * Wn[i];
+        } else if (variant == ORACLE_KIMI_DELTA) {
+            const double *at = alpha + tok(b, t, h, T, H, dk);
+            for (long i = 0; i < dv; ++i)
+                for (long j = 0; j < dk; ++j) Wn[i * dk + j] = Wn[i * dk + j] * (real)at[j];
+        }
+        for (long j = 0; j < dk; ++j) kk[j] = (real)kt[j];
+        for (long i = 0; i < dv; ++i) z[i] = (real)vt[i];
+        if (variant == ORACLE_GATED_DELTANET2) {
+            const double *bt_ = erase_b + tok(b, t, h, T, H, dk);
+            const double *wt_ = write_w + tok(b, t, h, T, H, dv);
+            for (long j = 0; j < dk; ++j) kk[j] = (real)bt_[j] * kk[j];
+            for (long i = 0; i < dv; ++i) z[i] = (real)wt_[i] * z[i];
+        }
+        for (long i = 0; i < dv; ++i) {
+            real pred = 0;
+            for (long j = 0; j < dk; ++j) pred += Wn[i * dk + j] * kk[j];
+            r[i] = z[i] - pred;
+        }
+        for (long i = 0; i < dv; ++i)
+            for (long j = 0; j < dk; ++j) Wn[i * dk + j] += bt * r[i] * (real)kt[j];
+    }
+    /* reverse */
+    for (long i = 0; i < n; ++i) G[i] = dstate_out ? (real)dstate_out[st(b, h, H, dv, dk) + i] : (real)0;
+    for (long t = T - 1; t >= 0; --t) {
+        const real *Wp = Ws + t * n;
+        const double *kt = k + tok(b, t, h, T, H, dk);
+        const double *qt = q + tok(b, t, h, T, H, dk);
+        const double *vt = v + tok(b, t, h, T, H, dv);
+        const double *yt = dout + tok(b, t, h, T, H, dv);
+        const real bt = (real)beta[tok(b, t, h, T, H, 1)];
+        /* recompute this token's forward quantities from W_{t-1} */
+        for (long i = 0; i < n; ++i) Wt[i] = Wp[i];
+        if (variant == ORACLE_GATED_DELTANET || variant == ORACLE_GATED_DELTANET2) {
+            const real a = (real)alpha[tok(b, t, h, T, H, 1)];
+            for (long i = 0; i < n; ++i) Wt[i] = a * Wt[i];
+        } else if (variant == ORACLE_KIMI_DELTA) {
+            const double *at = alpha + tok(b, t, h, T, H, dk);
+            for (long i = 0; i < dv; ++i)
+                for (long j = 0; j < dk; ++j) Wt[i * dk + j] = Wt[i * dk + j] * (real)at[j];
+        }
+        /* Wt holds W~ here */
+        for (long j = 0; j < dk; ++j) kk[j] = (real)kt[j];
+        for (long i = 0; i < dv; ++i) z[i] = (real)vt[i];
+        if (variant == ORACLE_GATED_DELTANET2) {
+            const double *bt_ = erase_b + tok(b, t, h, T, H, dk);
+            const double *wt_ = write_w + tok(b, t, h, T, H, dv);
+            for (long j = 0; j < dk; ++j) kk[j] = (real)bt_[j] * kk[j];
+            for (long i = 0; i < dv; ++i) z[i] = (real)wt_[i] * z[i];
+        }
+        for (long i = 0; i < dv; ++i) {
+            real pred = 0;
+            for (long j = 0; j < dk; ++j) pred += Wt[i * dk + j] * kk[j];
+            r[i] = z[i] - pred;
+        }
+        /* the read: G += dout q^T, dq = W_t^T dout (W_t = W~ + beta r k^T) */
+        for (long i = 0; i < dv; ++i)
+            for (long j = 0; j < dk; ++j) G[i * dk + j] += (real)yt[i] * (real)qt[j];
+        double *dqt = dq + tok(b, t, h, T, H, dk);
+        for (long j = 0; j < dk; ++j) {
+            real acc = 0;
+            for (long i = 0; i < dv; ++i) acc += (Wt[i * dk + j] + bt * r[i] * (real)kt[j]) * (real)yt[i];
+            dqt[j] = (double)acc;
+        }
+        /* the write */
+        real dbt = 0;
+        for (long i = 0; i < dv; ++i) {
+            real acc = 0;
+            for (long j = 0; j < dk; ++j) acc += G[i * dk + j] * (real)kt[j];
+            g[i] = acc;
+            dbt += r[i] * acc;
+        }
+        dbeta[tok(b, t, h, T, H, 1)] = (double)dbt;
+        double *dvt = dvg + tok(b, t, h, T, H, dv);
+        for (long i = 0; i < dv; ++i) {
+            const real dzi = bt * g[i];
+            if (variant == ORACLE_GATED_DELTANET2) {
+                dvt[i] = (double)((real)write_w[tok(b, t, h, T, H, dv) + i] * dzi);
+                dwrite_w[tok(b, t, h, T, H, dv) + i] = (double)((real)vt[i] * dzi);
+            } else {
+                dvt[i] = (double)dzi;
+            }
+        }
+        double *dkt = dkg + tok(b, t, h, T, H, dk);
+        for (long j = 0; j < dk; ++j) {
+            real acc = 0, acc2 = 0;
+            for (long i = 0; i < dv; ++i) {
+                acc += G[i * dk + j] * r[i];
+                acc2 += Wt[i * dk + j] * g[i];
+            }
+            dkk[j] = -bt * acc2;
+            dkt[j] = (double)(bt * acc);
+        }
+        if (variant == ORACLE_GATED_DELTANET2) {
+            const double *bt_ = erase_b + tok(b, t, h, T, H, dk);
+            for (long j = 0; j < dk; ++j) {
+                dkt[j] += (double)((real)bt_[j] * dkk[j]);
+                derase_b[tok(b, t, h, T, H, dk) + j] = (double)((real)kt[j] * dkk[j]);
+            }
+        } else {
+            for (long j = 0; j < dk; ++j) dkt[j] += (double)dkk[j];
+        }
+        /* dW~ = G - beta g kk^T, into G */
+        for (long i = 0; i < dv; ++i)
+            for (long j = 0; j < dk; ++j) G[i * dk + j] -= bt * g[i] * kk[j];
+        /* the decay */
+        if (variant == ORACLE_GATED_DELTANET || variant == ORACLE_GATED_DELTANET2) {
+            const real a = (real)alpha[tok(b, t, h, T, H, 1)];
+            real acc = 0;
+            for (long i = 0; i < n; ++i) acc += G[i] * Wp[i];
+            dalpha[tok(b, t, h, T, H, 1)] = (double)acc;
+            for (long i = 0; i < n; ++i) G[i] = a * G[i];
+        } else if (variant == ORACLE_KIMI_DELTA) {
+            const double *at = alpha + tok(b, t, h, T, H, dk);
+            double *dat = dalpha + tok(b, t, h, T, H, dk);
+            for (long j = 0; j < dk; ++j) {
+                real acc = 0;
+                for (long i = 0; i < dv; ++i) acc += G[i * dk + j] * Wp[i * dk + j];
+                dat[j] = (double)acc;
+            }
+            for (long i = 0; i < dv; ++i)
+                for (long j = 0; j < dk; ++j) G[i * dk + j] = G[i * dk + j] * (real)at[j];
+        }
+    }
+    if (dstate_in)
+        for (long i = 0; i < n; ++i) dstate_in[st(b, h, H, dv, dk) + i] = (double)G[i];
+}
+
+/*
+ * oracle_delta_backward: gradients of L = sum <dout, out> + <dstate_out,
+ * state_out> for the forward of oracle_delta_forward (same input layouts).
+ * dout [B,T,H,dv] required; dstate_out [B,H,dv,dk] or NULL (zero).  Outputs:
+ * dq, dk [B,T,H,dk]; dv [B,T,H,dv]; dbeta [B,T,H]; dalpha like alpha (NULL
+ * for DeltaNet); derase_b, dwrite_w like erase_b, write_w (Gated DeltaNet-2
+ * only); dstate_in [B,H,dv,dk] or NULL.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_delta_backward(int variant, long B, long T, long H, long dk, long dv,
+                          const double *q, const double *k, const double *v,
+                          const double *alpha, const double *erase_b,
+                          const double *write_w, const double *beta,
+                          const double *state_in, const double *dout,
+                          const double *dstate_out, double *dq, double *dkg,
+                          double *dvg, double *dalpha, double *derase_b,
+                          double *dwrite_w, double *dbeta, double *dstate_in,
+                          int nthreads) {
+    if (variant < ORACLE_DELTANET || variant > ORACLE_GATED_DELTANET2) return -1;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return -1;
+    if (!q || !k || !v || !beta || !dout || !dq || !dkg || !dvg || !dbeta) return -1;
+    if (variant != ORACLE_DELTANET && (!alpha || !dalpha)) return -1;
+    if (variant == ORACLE_GATED_DELTANET2 && (!erase_b || !write_w || !derase_b || !dwrite_w)) return -1;
+    const long chains = B * H;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads()) \
+    reduction(| : failed)
+    for (long c = 0; c < chains; ++c) {
+        const size_t n = (size_t)(dv * dk);
+        real *buf = (real *)malloc(sizeof(real) * ((size_t)(T + 1) * n + 2 * n + 3 * (size_t)dk + 3 * (size_t)dv));
+        if (!buf) { failed = 1; continue; }
+        real *Ws = buf, *Wt = Ws + (size_t)(T + 1) * n, *G = Wt + n, *kk = G + n, *z = kk + dk, *r = z + dv,
+             *g = r + dv, *dkk = g + dv;
+        delta_chain_bwd(variant, c / H, c % H, T, H, dk, dv, q, k, v, alpha, erase_b, write_w, beta,
+                        state_in, dout, dstate_out, dq, dkg, dvg, dalpha, derase_b, dwrite_w, dbeta,
+                        dstate_in, Ws, Wt, G, kk, z, r, g, dkk);
+        free(buf);
+    }
+    return failed ? -1 : 0;
+}
+
 /* ELU(x) + 1 with ELU's scale 1: x + 1 for x > 0, exp(x) otherwise
  * ([VLA] section 2.3, the feature map of keys and queries). */
 static real elu_plus_one(real x) { return x > 0 ? x + (real)1 : (real)exp((double)x); }
