@@ -83,6 +83,10 @@ def library() -> ctypes.CDLL:
             lib.lam_vla_forward.restype = ci
             lib.lam_vla_workspace_size.argtypes = [ci, i64, i64, i64, i64, ci, ctypes.POINTER(sz)]
             lib.lam_vla_workspace_size.restype = ci
+            lib.lam_backward.argtypes = [ci, ci, i64, i64, i64, i64, i64] + [vp] * 18 + [vp, sz, vp]
+            lib.lam_backward.restype = ci
+            lib.lam_backward_workspace_size.argtypes = [ci, ci, i64, i64, i64, i64, i64, ctypes.POINTER(sz)]
+            lib.lam_backward_workspace_size.restype = ci
             lib.lam_step.argtypes = [ci, ci, i64, i64, i64, i64] + [vp] * 9 + [vp]
             lib.lam_step.restype = ci
             lib.lam_vla_step.argtypes = [ci, i64, i64, i64] + [vp] * 7 + [vp]
@@ -111,6 +115,16 @@ def workspace_size(variant, dtype, B, T, H, dk, dv, algo="auto") -> int:
                                               ALGOS[algo], ctypes.byref(n))
     if rc != 0:
         raise LamError(rc, "lam_forward_workspace_size")
+    return int(n.value)
+
+
+def backward_workspace_size(variant, dtype, B, T, H, dk, dv) -> int:
+    """Bytes of workspace ``backward`` needs for these arguments."""
+    n = ctypes.c_size_t(0)
+    rc = library().lam_backward_workspace_size(VARIANTS[variant], DTYPES[dtype], B, T, H, dk, dv,
+                                               ctypes.byref(n))
+    if rc != 0:
+        raise LamError(rc, "lam_backward_workspace_size")
     return int(n.value)
 
 
@@ -243,6 +257,66 @@ def forward(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None, stat
         raise LamError(rc, "lam_forward")
     _after_call(ws, "lam_forward")
     return out, state_out
+
+
+def backward(variant, q, k, v, beta, dout, alpha=None, erase_b=None, write_w=None, state_in=None,
+             dstate_out=None, *, with_dstate_in=True, stream=None, workspace=None):
+    """Gradients of sum(dout * out) + sum(dstate_out * state_out) for
+    ``forward(variant, q, k, v, beta, alpha, erase_b, write_w, state_in)``.
+
+    Inputs as ``forward``; dout [B,T,H,dv] in their dtype; dstate_out fp32
+    [B,H,dv,dk] or None.  Returns a dict of fp32 tensors: dq, dk, dv, dbeta,
+    dstate_in (None unless ``with_dstate_in``), and dalpha ("gdn", "gdn2",
+    "kda"), derase_b and dwrite_w ("gdn2").
+    """
+    import torch
+
+    var = VARIANTS[variant]
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    dt, dev = q.dtype, q.device
+    _check(q, "q", (B, T, H, dk), dt, dev)
+    _check(k, "k", (B, T, H, dk), dt, dev)
+    _check(v, "v", (B, T, H, dv), dt, dev)
+    _check(beta, "beta", (B, T, H), dt, dev)
+    _check(dout, "dout", (B, T, H, dv), dt, dev)
+    ashape = None
+    if var == VARIANTS["kda"]:
+        ashape = (B, T, H, dk)
+    elif var != VARIANTS["deltanet"]:
+        ashape = (B, T, H)
+    if ashape is None:
+        alpha = None
+    else:
+        _check(alpha, "alpha", ashape, dt, dev)
+    if var == VARIANTS["gdn2"]:
+        _check(erase_b, "erase_b", (B, T, H, dk), dt, dev)
+        _check(write_w, "write_w", (B, T, H, dv), dt, dev)
+    else:
+        erase_b = write_w = None
+    _check(state_in, "state_in", (B, H, dv, dk), torch.float32, dev)
+    _check(dstate_out, "dstate_out", (B, H, dv, dk), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
+         "dv": torch.empty((B, T, H, dv), **f32), "dbeta": torch.empty((B, T, H), **f32),
+         "dstate_in": torch.empty((B, H, dv, dk), **f32) if with_dstate_in else None}
+    if ashape is not None:
+        g["dalpha"] = torch.empty(ashape, **f32)
+    if var == VARIANTS["gdn2"]:
+        g["derase_b"] = torch.empty((B, T, H, dk), **f32)
+        g["dwrite_w"] = torch.empty((B, T, H, dv), **f32)
+    ws = _workspace(backward_workspace_size(variant, {torch.float32: "f32", torch.bfloat16: "bf16"}[dt],
+                                            B, T, H, dk, dv), workspace, dev, stream)
+    rc = library().lam_backward(var, _dtype_code(q), B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(alpha), _ptr(erase_b), _ptr(write_w), _ptr(beta), _ptr(state_in),
+                                _ptr(dout), _ptr(dstate_out), _ptr(g["dq"]), _ptr(g["dk"]),
+                                _ptr(g["dv"]), _ptr(g.get("dalpha")), _ptr(g.get("derase_b")),
+                                _ptr(g.get("dwrite_w")), _ptr(g["dbeta"]), _ptr(g["dstate_in"]),
+                                _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    if rc != 0:
+        raise LamError(rc, "lam_backward")
+    _after_call(ws, "lam_backward")
+    return g
 
 
 def vla_forward(q, k, v, p, A_in=None, S_in=None, *, algo="auto", out=None, A_out=None,

@@ -229,6 +229,84 @@ lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, 
     return from_hip(lam::launch_delta_recurrent(a, stream));
 }
 
+lam_status lam_backward_workspace_size(int variant, int dtype, int64_t B, int64_t T, int64_t H,
+                                       int64_t dk, int64_t dv, size_t *bytes) {
+    if (!bytes) return LAM_ERR_INVALID_ARG;
+    *bytes = 0;
+    lam_status st = check_delta_shape(variant, dtype, B, T, H, dk, dv, LAM_ALGO_RECURRENT);
+    if (st != LAM_OK) return st;
+    if (B == 0 || H == 0) return LAM_OK;
+    lam::DeltaArgs a = shape_args(variant, dtype, B, T, H, dk, dv);
+    return lam::delta_backward_workspace(a, bytes) ? LAM_OK : LAM_ERR_UNSUPPORTED;
+}
+
+lam_status lam_backward(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                        int64_t dv, const void *q, const void *k, const void *v,
+                        const void *alpha, const void *erase_b, const void *write_w,
+                        const void *beta, const float *state_in, const void *dout,
+                        const float *dstate_out, float *dq, float *dk_, float *dv_, float *dalpha,
+                        float *derase_b, float *dwrite_w, float *dbeta, float *dstate_in,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    size_t need = 0;
+    lam_status st = lam_backward_workspace_size(variant, dtype, B, T, H, dk, dv, &need);
+    if (st != LAM_OK) return st;
+    if (B == 0 || H == 0) return LAM_OK;
+    int64_t nk, nv, ns, nst;
+    elems(B, T, H, dk, nk);
+    elems(B, T, H, dv, nv);
+    elems(B, T, H, 1, ns);
+    elems(B, 1, H, dk * dv, nst);
+    const bool gated = variant != LAM_DELTANET, g2 = variant == LAM_GATED_DELTANET2;
+    if (T > 0) {
+        if (!q || !k || !v || !beta || !dout || !dq || !dk_ || !dv_ || !dbeta) return LAM_ERR_INVALID_ARG;
+        if (gated && (!alpha || !dalpha)) return LAM_ERR_INVALID_ARG;
+        if (g2 && (!erase_b || !write_w || !derase_b || !dwrite_w)) return LAM_ERR_INVALID_ARG;
+    }
+    const int64_t es = dtype == LAM_BF16 ? 2 : 4;
+    const int64_t na = variant == LAM_KIMI_DELTA ? nk : ns;
+    const void *ins[] = {q, k, v, gated ? alpha : nullptr, g2 ? erase_b : nullptr, g2 ? write_w : nullptr,
+                         beta, state_in, dout, dstate_out};
+    const int64_t inb[] = {nk * es, nk * es, nv * es, na * es, nk * es, nv * es, ns * es, nst * 4, nv * es, nst * 4};
+    void *outs[] = {dq, dk_, dv_, gated ? dalpha : nullptr, g2 ? derase_b : nullptr, g2 ? dwrite_w : nullptr,
+                    dbeta, dstate_in};
+    const int64_t outb[] = {nk * 4, nk * 4, nv * 4, na * 4, nk * 4, nv * 4, ns * 4, nst * 4};
+    for (int o = 0; o < 8; ++o) {
+        for (int i = 0; i < 10; ++i)
+            if (overlaps(outs[o], outb[o], ins[i], inb[i])) return LAM_ERR_INVALID_ARG;
+        for (int o2 = o + 1; o2 < 8; ++o2)
+            if (overlaps(outs[o], outb[o], outs[o2], outb[o2])) return LAM_ERR_INVALID_ARG;
+    }
+    const void *all[18];
+    int64_t allb[18];
+    for (int i = 0; i < 10; ++i) all[i] = ins[i], allb[i] = inb[i];
+    for (int o = 0; o < 8; ++o) all[10 + o] = outs[o], allb[10 + o] = outb[o];
+    if (!workspace_ok(workspace, workspace_bytes, need, all, allb, 18)) return LAM_ERR_INVALID_ARG;
+    if (T == 0 && !dstate_in) return LAM_OK;  // (T = 0: dstate_in = dstate_out, or zero)
+    lam::DeltaBwdArgs g{};
+    g.f = shape_args(variant, dtype, B, T, H, dk, dv);
+    g.f.q = q;
+    g.f.k = k;
+    g.f.v = v;
+    g.f.alpha = gated ? alpha : nullptr;
+    g.f.erase_b = g2 ? erase_b : nullptr;
+    g.f.write_w = g2 ? write_w : nullptr;
+    g.f.beta = beta;
+    g.f.state_in = state_in;
+    g.f.ws = workspace;
+    g.dout = dout;
+    g.dstate_out = dstate_out;
+    g.dq = dq;
+    g.dk = dk_;
+    g.dv = dv_;
+    g.dalpha = gated ? dalpha : nullptr;
+    g.derase_b = g2 ? derase_b : nullptr;
+    g.dwrite_w = g2 ? dwrite_w : nullptr;
+    g.dbeta = dbeta;
+    g.dstate_in = dstate_in;
+    g.ckpt = reinterpret_cast<float *>(static_cast<char *>(workspace) + lam::kStatusBytes);
+    return from_hip(lam::launch_delta_backward(g, stream));
+}
+
 lam_status lam_step(int variant, int dtype, int64_t N, int64_t H, int64_t dk, int64_t dv,
                     const void *q, const void *k, const void *v, const void *alpha,
                     const void *erase_b, const void *write_w, const void *beta, float *state,

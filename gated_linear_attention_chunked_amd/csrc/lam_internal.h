@@ -65,6 +65,18 @@ hipError_t launch_vla_chunked(const VlaArgs &a, hipStream_t stream);
 bool delta_step_supported(const DeltaArgs &a);
 hipError_t launch_delta_step(const DeltaArgs &a, hipStream_t stream);
 
+// Backward pass: the forward's inputs in f (out, state_out unused; ws = the
+// workspace), the output and final-state adjoints, and fp32 gradients.
+struct DeltaBwdArgs {
+    DeltaArgs f;
+    const void *dout;          // [B,T,H,dv], storage dtype
+    const float *dstate_out;   // [B,H,dv,dk] or NULL
+    float *dq, *dk, *dv, *dalpha, *derase_b, *dwrite_w, *dbeta, *dstate_in;
+    float *ckpt;               // states every 16 tokens, [B*H][chunks][dv][dk]
+};
+bool delta_backward_workspace(const DeltaArgs &a, size_t *bytes);
+hipError_t launch_delta_backward(const DeltaBwdArgs &g, hipStream_t stream);
+
 // Kimi Delta (per-channel decay) has its own chunked kernel.
 bool kda_chunked_supported(const DeltaArgs &a);
 bool kda_chunked_workspace(const DeltaArgs &a, size_t *bytes);

@@ -144,6 +144,16 @@ def make_inputs(w: Workload) -> dict:
     return out
 
 
+def make_cotangents(w: Workload, seed: int) -> tuple:
+    """Seeded adjoints for a backward pass of workload ``w``: dout
+    [B,T,H,dv] (standard normal, stored in w's dtype) and dstate_out fp32
+    [B,H,dv,dk] (standard normal), as float64 arrays of the stored values."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dout = _store(rng.standard_normal((w.B, w.T, w.H, w.dv)), w.dtype)
+    dstate = round_f32(rng.standard_normal((w.B, w.H, w.dv, w.dk))).astype(np.float64)
+    return dout, dstate
+
+
 def to_device(inputs: dict, dtype: str, device="cuda"):
     """Copy host inputs to device tensors in the storage dtype (exact: the
     host values are already representable)."""

@@ -175,6 +175,45 @@ lam_status lam_vla_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, in
                                   int algo, size_t *bytes);
 
 /*
+ * Backward pass of lam_forward's delta-rule scan: the gradients of
+ * L = sum <dout, out> + <dstate_out, state_out> with respect to q, k, v,
+ * alpha, erase_b, write_w, beta and state_in.  It is the reverse-mode
+ * adjoint of the per-token rule above ("Mechanisms, trade-offs and
+ * cross-layer routing of linear-attention architectures", "Technical
+ * details"; the pages train these layers, section "Main results"),
+ * computed in fp32 from the same inputs as the forward (it recomputes the
+ * forward; no forward outputs are needed).
+ *   forward inputs  as lam_forward (q, k, v, alpha, erase_b, write_w, beta,
+ *                   state_in), in dtype
+ *   dout            [B,T,H,dv] in dtype, required
+ *   dstate_out      [B,H,dv,dk] fp32 or NULL (zero)
+ *   gradients, fp32, written: dq, dk [B,T,H,dk]; dv [B,T,H,dv]; dbeta
+ *                   [B,T,H] (all required); dalpha like alpha (required
+ *                   unless DeltaNet); derase_b [B,T,H,dk] and dwrite_w
+ *                   [B,T,H,dv] (required for Gated DeltaNet-2); dstate_in
+ *                   [B,H,dv,dk] or NULL.  No gradient buffer may overlap
+ *                   another argument.
+ *   workspace       lam_backward_workspace_size bytes: the forward state
+ *                   every 16 tokens, B*H*ceil(T/16)*dv*dk*4 B, plus the
+ *                   status block.
+ * T = 0 writes dstate_in = dstate_out (zero if NULL).
+ * dq, dk, dbeta, dalpha and derase_b sum over the memory's dv rows, which
+ * several workgroups add into with atomics: those five are not bitwise
+ * reproducible run to run; dv, dwrite_w and dstate_in are.
+ */
+lam_status lam_backward(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                        int64_t dv, const void *q, const void *k, const void *v,
+                        const void *alpha, const void *erase_b, const void *write_w,
+                        const void *beta, const float *state_in, const void *dout,
+                        const float *dstate_out, float *dq, float *dk_, float *dv_, float *dalpha,
+                        float *derase_b, float *dwrite_w, float *dbeta, float *dstate_in,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace lam_backward needs (> 0 for any non-empty call). */
+lam_status lam_backward_workspace_size(int variant, int dtype, int64_t B, int64_t T, int64_t H,
+                                       int64_t dk, int64_t dv, size_t *bytes);
+
+/*
  * One-token decode step for N concurrent streams: the rule above applied to
  * one token per (stream, head), the memory updated in place ("Mechanisms,
  * trade-offs and cross-layer routing of linear-attention architectures",

@@ -205,3 +205,40 @@ def test_step_rejects_bad_arguments(lib):
     assert _step(lib, N=0, q=None, k=None, v=None, beta=None, out=None, state=None) == OK
     assert lib.lam_vla_step(0, 2, 2, 32, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == INVALID
     assert lib.lam_vla_step(0, 2, 2, 40, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def _bwd(lib, variant=1, dtype=1, B=2, T=8, H=2, dk=64, dv=64, ws=None, ws_bytes=0, **kw):
+    p = dict(q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, alpha=FAKE + 0x30000000,
+             eb=FAKE + 0x40000000, ww=FAKE + 0x50000000, beta=FAKE + 0x60000000, sin=None,
+             dout=FAKE + 0x70000000, dsout=None, gq=FAKE + 0x100000000, gk=FAKE + 0x110000000,
+             gv=FAKE + 0x120000000, dalpha=FAKE + 0x130000000, deb=FAKE + 0x140000000,
+             dww=FAKE + 0x150000000, dbeta=FAKE + 0x160000000, dsin=FAKE + 0x170000000)
+    p.update(kw)
+    return lib.lam_backward(variant, dtype, B, T, H, dk, dv, p["q"], p["k"], p["v"], p["alpha"], p["eb"],
+                            p["ww"], p["beta"], p["sin"], p["dout"], p["dsout"], p["gq"], p["gk"], p["gv"],
+                            p["dalpha"], p["deb"], p["dww"], p["dbeta"], p["dsin"], ws, ws_bytes, None)
+
+
+def test_backward_rejects_bad_arguments(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.lam_backward_workspace_size(1, 1, 2, 8, 2, 64, 64, ctypes.byref(n)) == OK
+    need = n.value
+    # the forward state every 16 tokens plus the 256-byte status block
+    assert need == 256 + 2 * 2 * 1 * 64 * 64 * 4
+    assert lib.lam_backward_workspace_size(1, 1, 2, 0, 2, 64, 64, ctypes.byref(n)) == OK and n.value == 256
+    assert lib.lam_backward_workspace_size(1, 1, 2, 8, 2, 48, 64, ctypes.byref(n)) == UNSUPPORTED
+    assert lib.lam_backward_workspace_size(9, 1, 2, 8, 2, 64, 64, ctypes.byref(n)) == INVALID
+    WS = FAKE + 0x200000000
+    assert _bwd(lib) == INVALID                                       # no workspace
+    assert _bwd(lib, ws=WS, ws_bytes=need - 1) == INVALID             # too small
+    for name in ("q", "k", "v", "beta", "dout", "gq", "gk", "gv", "dbeta", "alpha", "dalpha"):
+        assert _bwd(lib, ws=WS, ws_bytes=need, **{name: None}) == INVALID, name
+    assert _bwd(lib, variant=0, alpha=None, dalpha=None, eb=None, dww=None, ws=WS, ws_bytes=need,
+                q=None) == INVALID
+    for name in ("eb", "ww", "deb", "dww"):
+        assert _bwd(lib, variant=3, ws=WS, ws_bytes=need, **{name: None}) == INVALID, name
+    # a gradient inside an input, inside another gradient, or inside the workspace
+    assert _bwd(lib, gq=FAKE + 64, ws=WS, ws_bytes=need) == INVALID
+    assert _bwd(lib, gk=FAKE + 0x100000000 + 64, ws=WS, ws_bytes=need) == INVALID
+    assert _bwd(lib, dsin=WS + 512, ws=WS, ws_bytes=need) == INVALID
+    assert _bwd(lib, B=0, ws=None) == OK
