@@ -69,6 +69,9 @@ def _lib(prec: str = "f64") -> ctypes.CDLL:
             L = ctypes.c_long
             lib.oracle_delta_forward.argtypes = [ctypes.c_int, L, L, L, L, L] + [dp] * 10 + [ctypes.c_int, ctypes.c_int]
             lib.oracle_delta_forward.restype = ctypes.c_int
+            lib.oracle_delta_forward_side.argtypes = ([ctypes.c_int, L, L, L, L, L] + [dp] * 10 +
+                                                      [ctypes.c_int, dp, ctypes.c_int, ctypes.c_int])
+            lib.oracle_delta_forward_side.restype = ctypes.c_int
             lib.oracle_vla_forward.argtypes = [L, L, L, L] + [dp] * 13 + [ctypes.c_int]
             lib.oracle_vla_forward.restype = ctypes.c_int
             lib.oracle_delta_backward.argtypes = [ctypes.c_int, L, L, L, L, L] + [dp] * 18 + [ctypes.c_int]
@@ -91,14 +94,19 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+SIDES = {"residual": 1, "value": 2}
+
+
 def delta_forward(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None,
-                  state_in=None, drop_delta=False, nthreads=0, precision="f64"):
+                  state_in=None, drop_delta=False, nthreads=0, precision="f64", side=None):
     """Delta-rule family forward scan.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H]; alpha: [B,T,H] (gdn, gdn2)
     or [B,T,H,dk] (kda) or None (deltanet); erase_b: [B,T,H,dk] and write_w:
     [B,T,H,dv] (gdn2 only); state_in: [B,H,dv,dk] or None (zero memory).
-    Returns (out [B,T,H,dv], state_out [B,H,dv,dk]) as float64 arrays.
+    Returns (out [B,T,H,dv], state_out [B,H,dv,dk]) as float64 arrays, and
+    with ``side`` = "residual" or "value" a third array [B,T,H,dv]: the
+    per-token residual r (CLER) or write value (CLVR).
     ``drop_delta`` replaces the residual by the plain write target (test hook).
     """
     var = VARIANTS[variant] if isinstance(variant, str) else int(variant)
@@ -124,13 +132,37 @@ def delta_forward(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None
     state_in = _in(state_in, (B, H, dv, dk))
     out = np.zeros((B, T, H, dv), np.float64)
     state_out = np.zeros((B, H, dv, dk), np.float64)
-    rc = _lib(precision).oracle_delta_forward(
+    if side is None:
+        rc = _lib(precision).oracle_delta_forward(
+            var, B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase_b),
+            _ptr(write_w), _ptr(beta), _ptr(state_in), _ptr(out), _ptr(state_out),
+            int(bool(drop_delta)), int(nthreads))
+        if rc != 0:
+            raise RuntimeError("oracle_delta_forward failed")
+        return out, state_out
+    sd = np.zeros((B, T, H, dv), np.float64)
+    rc = _lib(precision).oracle_delta_forward_side(
         var, B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase_b),
         _ptr(write_w), _ptr(beta), _ptr(state_in), _ptr(out), _ptr(state_out),
-        int(bool(drop_delta)), int(nthreads))
+        int(bool(drop_delta)), _ptr(sd), SIDES[side], int(nthreads))
     if rc != 0:
-        raise RuntimeError("oracle_delta_forward failed")
-    return out, state_out
+        raise RuntimeError("oracle_delta_forward_side failed")
+    return out, state_out, sd
+
+
+def route(h, s, P):
+    """Cross-layer routing epilogue ([LA-arch] "Technical details", the CLVR
+    implementation): each token's signal s_t (all heads, [H*dv]) is mapped to
+    the model width by P [D, H*dv] and added to the residual stream,
+    h_t + P s_t.  h: [B,T,D]; s: [B,T,H,dv].  Returns float64 [B,T,D]."""
+    h = _in(h)
+    s = _in(s)
+    P = _in(P)
+    B, T, D = h.shape
+    n = s.shape[2] * s.shape[3]
+    if s.shape[:2] != (B, T) or P.shape != (D, n):
+        raise ValueError("route: shapes")
+    return h + s.reshape(B, T, n) @ P.T
 
 
 def delta_backward(variant, q, k, v, beta, dout, alpha=None, erase_b=None, write_w=None,

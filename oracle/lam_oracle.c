@@ -61,6 +61,12 @@ enum {
     ORACLE_GATED_DELTANET2 = 3 /* scalar alpha + erase b[dk], write w[dv]   */
 };
 
+/* Per-token side output of the delta-rule forward ([LA-arch] "Methodology"
+   and "Technical details", cross-layer routing): the internal signal s that
+   CLER / CLER-H route is the delta-rule residual r, the one CLVR routes is
+   the write value (v, or the write target z = w*v for Gated DeltaNet-2). */
+enum { ORACLE_SIDE_NONE = 0, ORACLE_SIDE_RESIDUAL = 1, ORACLE_SIDE_VALUE = 2 };
+
 /* Row-major index helpers for [B,T,H,n] token streams and [B,H,r,c] states. */
 static size_t tok(long b, long t, long h, long T, long H, long n) {
     return (((size_t)b * T + t) * H + h) * (size_t)n;
@@ -89,6 +95,7 @@ static void delta_chain(int variant, long b, long h, long T, long H, long dk,
                         const double *erase_b, const double *write_w,
                         const double *beta, const double *state_in,
                         double *out, double *state_out, int drop_delta,
+                        double *side, int side_kind,
                         real *W, real *kk, real *target, real *r) {
     for (long i = 0; i < dv * dk; ++i)
         W[i] = state_in ? (real)state_in[st(b, h, H, dv, dk) + i] : (real)0;
@@ -127,6 +134,14 @@ static void delta_chain(int variant, long b, long h, long T, long H, long dk,
             r[i] = target[i] - pred;
         }
 
+        /* cross-layer routing signal of this token: the residual (CLER) or
+           the write value (CLVR) */
+        if (side) {
+            double *sd = side + tok(b, t, h, T, H, dv);
+            for (long i = 0; i < dv; ++i)
+                sd[i] = (double)(side_kind == ORACLE_SIDE_RESIDUAL ? r[i] : target[i]);
+        }
+
         /* write along the key */
         for (long i = 0; i < dv; ++i)
             for (long j = 0; j < dk; ++j) W[i * dk + j] += bt * r[i] * (real)kt[j];
@@ -151,12 +166,39 @@ static void delta_chain(int variant, long b, long h, long T, long H, long dk,
  * [B,H,dv,dk] (NULL in = zero memory, NULL out = not written).
  * Returns 0, or -1 on a bad argument or allocation failure.
  */
+int oracle_delta_forward_side(int variant, long B, long T, long H, long dk, long dv,
+                              const double *q, const double *k, const double *v,
+                              const double *alpha, const double *erase_b,
+                              const double *write_w, const double *beta,
+                              const double *state_in, double *out,
+                              double *state_out, int drop_delta, double *side,
+                              int side_kind, int nthreads);
+
 int oracle_delta_forward(int variant, long B, long T, long H, long dk, long dv,
                          const double *q, const double *k, const double *v,
                          const double *alpha, const double *erase_b,
                          const double *write_w, const double *beta,
                          const double *state_in, double *out,
                          double *state_out, int drop_delta, int nthreads) {
+    return oracle_delta_forward_side(variant, B, T, H, dk, dv, q, k, v, alpha, erase_b, write_w,
+                                     beta, state_in, out, state_out, drop_delta, NULL,
+                                     ORACLE_SIDE_NONE, nthreads);
+}
+
+/*
+ * oracle_delta_forward_side: oracle_delta_forward that also writes the
+ * per-token routing signal to side [B,T,H,dv] (side_kind RESIDUAL: r;
+ * VALUE: the write value; NONE with side NULL: nothing).
+ */
+int oracle_delta_forward_side(int variant, long B, long T, long H, long dk, long dv,
+                              const double *q, const double *k, const double *v,
+                              const double *alpha, const double *erase_b,
+                              const double *write_w, const double *beta,
+                              const double *state_in, double *out,
+                              double *state_out, int drop_delta, double *side,
+                              int side_kind, int nthreads) {
+    if (side_kind < ORACLE_SIDE_NONE || side_kind > ORACLE_SIDE_VALUE) return -1;
+    if ((side_kind == ORACLE_SIDE_NONE) != (side == NULL)) return -1;
     if (variant < ORACLE_DELTANET || variant > ORACLE_GATED_DELTANET2) return -1;
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return -1;
     if (!q || !k || !v || !beta || !out) return -1;
@@ -170,8 +212,8 @@ int oracle_delta_forward(int variant, long B, long T, long H, long dk, long dv,
         real *buf = (real *)malloc(sizeof(real) * (size_t)(dv * dk + 2 * dk + 2 * dv));
         if (!buf) { failed = 1; continue; }
         delta_chain(variant, c / H, c % H, T, H, dk, dv, q, k, v, alpha, erase_b,
-                    write_w, beta, state_in, out, state_out, drop_delta, buf,
-                    buf + dv * dk, buf + dv * dk + dk, buf + dv * dk + dk + dv);
+                    write_w, beta, state_in, out, state_out, drop_delta, side, side_kind,
+                    buf, buf + dv * dk, buf + dv * dk + dk, buf + dv * dk + dk + dv);
         free(buf);
     }
     return failed ? -1 : 0;
