@@ -83,6 +83,10 @@ def library() -> ctypes.CDLL:
             lib.lam_vla_forward.restype = ci
             lib.lam_vla_workspace_size.argtypes = [ci, i64, i64, i64, i64, ci, ctypes.POINTER(sz)]
             lib.lam_vla_workspace_size.restype = ci
+            lib.lam_forward_side.argtypes = [ci, ci, i64, i64, i64, i64, i64] + [vp] * 10 + [ci, vp, vp, sz, ci, vp]
+            lib.lam_forward_side.restype = ci
+            lib.lam_route.argtypes = [ci, i64, i64, i64, vp, vp, vp, vp]
+            lib.lam_route.restype = ci
             lib.lam_backward.argtypes = [ci, ci, i64, i64, i64, i64, i64] + [vp] * 18 + [vp, sz, vp]
             lib.lam_backward.restype = ci
             lib.lam_backward_workspace_size.argtypes = [ci, ci, i64, i64, i64, i64, i64, ctypes.POINTER(sz)]
@@ -202,8 +206,12 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+SIDES = {None: 0, "residual": 1, "value": 2}
+
+
 def forward(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None, state_in=None, *,
-            algo="auto", out=None, state_out=None, with_state=True, stream=None, workspace=None):
+            algo="auto", out=None, state_out=None, with_state=True, stream=None, workspace=None,
+            side=None, side_out=None):
     """Delta-rule family forward scan.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H]; alpha: [B,T,H]
@@ -213,7 +221,9 @@ def forward(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None, stat
     or None (zero memory).  ``workspace``: optional uint8 device tensor of at
     least ``workspace_size(...)`` bytes (default: a fresh one from torch's
     caching allocator).  Returns (out [B,T,H,dv], state_out fp32 [B,H,dv,dk]
-    or None).
+    or None), and with ``side`` = "residual" or "value" a third tensor
+    [B,T,H,dv] in the streams' dtype: every token's delta-rule residual r
+    (CLER) or write value (CLVR), written into ``side_out`` if given.
     """
     import torch
 
@@ -249,14 +259,47 @@ def forward(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None, stat
     if rc != 0:
         raise LamError(rc, "lam_forward_workspace_size")
     ws = _workspace(int(nws.value), workspace, dev, stream)
-    rc = library().lam_forward(var, _dtype_code(q), B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
-                               _ptr(alpha), _ptr(erase_b), _ptr(write_w), _ptr(beta),
-                               _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(ws),
-                               0 if ws is None else ws.numel(), ALGOS[algo], _stream(stream))
+    if side is None:
+        rc = library().lam_forward(var, _dtype_code(q), B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(alpha), _ptr(erase_b), _ptr(write_w), _ptr(beta),
+                                   _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(ws),
+                                   0 if ws is None else ws.numel(), ALGOS[algo], _stream(stream))
+        if rc != 0:
+            raise LamError(rc, "lam_forward")
+        _after_call(ws, "lam_forward")
+        return out, state_out
+    if side_out is None:
+        side_out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check(side_out, "side_out", (B, T, H, dv), dt, dev)
+    rc = library().lam_forward_side(var, _dtype_code(q), B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(alpha), _ptr(erase_b), _ptr(write_w), _ptr(beta),
+                                    _ptr(state_in), _ptr(out), _ptr(state_out), SIDES[side],
+                                    _ptr(side_out), _ptr(ws), 0 if ws is None else ws.numel(),
+                                    ALGOS[algo], _stream(stream))
     if rc != 0:
-        raise LamError(rc, "lam_forward")
-    _after_call(ws, "lam_forward")
-    return out, state_out
+        raise LamError(rc, "lam_forward_side")
+    _after_call(ws, "lam_forward_side")
+    return out, state_out, side_out
+
+
+def route(h, s, P, *, stream=None):
+    """Routing epilogue, in place: h <- h + s P^T per token.
+
+    h: [B,T,D] (the residual stream); s: [B,T,H,dv] (a routing signal from
+    ``forward(..., side=...)``); P: [D, H*dv].  One dtype (float32 or
+    bfloat16), one device.  Returns h.
+    """
+    B, T, D = h.shape
+    N = s.shape[2] * s.shape[3]
+    dt, dev = h.dtype, h.device
+    _check(h, "h", (B, T, D), dt, dev)
+    _check(s, "s", (B, T, s.shape[2], s.shape[3]), dt, dev)
+    _check(P, "P", (D, N), dt, dev)
+    rc = library().lam_route(_dtype_code(h), B * T, D, N, _ptr(s), _ptr(P), _ptr(h), _stream(stream))
+    if rc != 0:
+        raise LamError(rc, "lam_route")
+    _after_call(None, "lam_route")
+    return h
 
 
 def backward(variant, q, k, v, beta, dout, alpha=None, erase_b=None, write_w=None, state_in=None,

@@ -9,10 +9,18 @@
 // Chunked form (derived from that rule by unrolling it over a chunk of C
 // tokens; rows = tokens, S = memory at the chunk start, g_t = sum_{j<=t}
 // log a_j, gamma_t = exp(g_t), Gamma_ts = exp(g_t - g_s) for s <= t):
-//   L  = strict_lower(diag(beta) (E K^T * Gamma))
-//   U  = (I + L)^{-1} diag(beta) (Z - diag(gamma) E S^T)
-//   Y  = diag(gamma) Q S^T + (lower(Q K^T) * Gamma) U
-//   S' = gamma_C S + U^T diag(gamma_C / gamma) K
+//   N  = strict_lower(E K^T * Gamma)
+//   R  = (I + N diag(beta))^{-1} (Z - diag(gamma) E S^T)
+//   Y  = diag(gamma) Q S^T + (lower(Q K^T) * Gamma) diag(beta) R
+//   S' = gamma_C S + R^T diag(beta gamma_C / gamma) K
+// Row t of R is token t's residual r_t, taken against the decayed memory
+// (the write is beta_t r_t k_t^T): R satisfies R = Z - diag(gamma) E S^T -
+// N diag(beta) R, which is the rule's residual with the chunk's earlier
+// writes included.  Solving for R rather than diag(beta) R keeps beta out of
+// the solve's right-hand side: the residual a caller asks for as a routing
+// signal is exactly the operand the scan carries, at any beta (zero
+// included), and beta enters only as a column scale of the products that
+// consume R.
 // Every exponent is g_t - g_s with s <= t (or g_C - g_t), so no factor exceeds
 // one and strong decays underflow to zero instead of overflowing.
 //
@@ -37,7 +45,7 @@
 // contraction does not care how its reduction index is ordered, two stacked
 // accumulator tiles serve directly as a B operand if the A operand is read
 // with the same order (rows 4g..4g+3 and 16+4g..16+4g+3 of each 32-block).
-// The same trick feeds U and the solve's right-hand sides to the next
+// The same trick feeds R and the solve's right-hand sides to the next
 // products without an LDS round trip.
 #include <type_traits>
 
@@ -51,23 +59,23 @@ constexpr int C = 64;    // chunk length (tokens)
 constexpr int BV = 32;   // dv columns per workgroup
 
 // ===========================================================================
-// With D_i = (I + L_ii)^{-1} the inverse of diagonal block i of I + L,
+// With D_i = (I + N_ii diag(beta)_i)^{-1} the inverse of diagonal block i,
 // G~_ij = Gamma * (E_i K_j^T) and Z = E S^T, block row i of the solve is
-//     U_i = D_i diag(beta)_i Z'_i - D_i diag(beta gamma)_i Z_i + sum_{j<i} M_ij U_j,
-//     M_ij = -D_i diag(beta)_i G~_ij                (Z' = the targets V)
+//     R_i = D_i Z'_i - D_i diag(gamma)_i Z_i + sum_{j<i} M_ij R_j,
+//     M_ij = -D_i G~_ij diag(beta)_j                (Z' = the targets V)
 // so everything but Z is state-independent: the derivation kernel forms it.
-// The output's intra-chunk matrix Aqk = lower(Q K^T * Gamma) is formed by
-// the scan's output waves from the staged query and key rows, each the
-// blocks of its own token rows.
+// The output's intra-chunk matrix Aqk = lower(Q K^T * Gamma) diag(beta) is
+// formed by the scan's output waves from the staged query and key rows, each
+// the blocks of its own token rows.
 //
 // Pipelined scan: 8 waves per workgroup, two per SIMD, in three roles.
 //   carry  (waves 0-1, one 16-column tile each): Z = E S^T on MFMA, the
-//          block solve above on 16x16x16 MFMA (a four-link chain), publish U,
+//          block solve above on 16x16x16 MFMA (a four-link chain), publish R,
 //          then the state update accumulated in registers.
 //   output (waves 2-3): token row tiles {0, 3} and {1, 2} for both value
 //          tiles: Q S^T from the carries' bf16 states and the Aqk blocks of
-//          their rows from the staged rows, then Y = diag(gamma) Q S^T + Aqk U
-//          once both U are published; stores y.
+//          their rows from the staged rows, then Y = diag(gamma) Q S^T + Aqk R
+//          once both R are published; stores y.
 //   producers (waves 4-7): stage chunk c+1 into LDS, its token rows and its
 //          derived block (loads issued two chunks ahead).
 // All eight waves meet at one LDS barrier per chunk; the hand-offs inside a
@@ -84,11 +92,12 @@ constexpr int LTS = 20;    // column stride (floats) of the fp32 diagonal blocks
 // State-independent matrices of one chunk.  The derivation kernel writes one
 // block per (sequence, head, chunk); the scan copies it into LDS unchanged.
 struct DerBlock {
-    bf16x4 dtil[4][64];        // D_i diag(beta)_i, A-operand order
+    bf16x4 dtil[4][64];        // D_i, A-operand order
     bf16x4 mij[NLB][64];       // M_ij
     float gam[C];              // gamma_t
-    float sc[C];               // gamma_C / gamma_t
+    float sc[C];               // beta_t gamma_C / gamma_t
     float g[C];                // log2 gamma_t
+    float beta[C];             // beta_t (zero on padding rows)
 };
 static_assert(sizeof(DerBlock) % 256 == 0, "workspace blocks stay 256-byte aligned");
 constexpr int kDerPieces = static_cast<int>(sizeof(DerBlock) / 16);  // 16-byte pieces
@@ -106,9 +115,9 @@ struct WyLds {
     Raw raw[2];
     alignas(16) DerBlock der[2];
     // carry -> output
-    alignas(16) bf16x4 uh[2][4][64];           // U of the current chunk, per tile
+    alignas(16) bf16x4 uh[2][4][64];           // R of the current chunk, per tile
     alignas(16) bf16x4 sh[2][DK / 16][64];     // bf16 state fragments per tile
-    unsigned int ucount[2];                    // U publications per tile
+    unsigned int ucount[2];                    // R publications per tile
     unsigned int scount[2];                    // state fragments consumed per tile
 };
 
@@ -127,12 +136,12 @@ __device__ __forceinline__ uint4 mul8(uint4 x, uint4 y) {
     return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
-// S^T = gamma_C S^T + K^T diag(gamma_C / gamma) U for one 16-column tile.
+// S^T = gamma_C S^T + K^T diag(beta gamma_C / gamma) R for one 16-column tile.
 template <int KT, typename Raw>
 __device__ __forceinline__ void state_update(f32x4 (&St)[KT], const Raw &R, const DerBlock &D, const bf16x4 (&ub)[4],
                                              int KS, int lane) {
     const int lg = lane >> 4;
-    // operand reads first, then the scaling of U while they are in flight
+    // operand reads first, then the scaling of R while they are in flight
     bf16x8 af[2][KT];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
@@ -257,8 +266,9 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
         s.g[lane] = g;
         D.g[lane] = g;
         D.gam[lane] = exp2_fast(g);
-        D.sc[lane] = exp2_fast(gl - g);
+        D.sc[lane] = exp2_fast(gl - g) * s.beta[lane];
     }
+    if (w == 1) D.beta[lane] = s.beta[lane];
     __syncthreads();
 
     // ---- E K^T tiles of block row I (phase 1), then the inverse of its
@@ -292,16 +302,15 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
             const float4 gt4 = *reinterpret_cast<const float4 *>(&s.g[16 * ti + 4 * lg]);
             const float gt[4] = {gt4.x, gt4.y, gt4.z, gt4.w};
             const float gs = s.g[16 * si + lc];
+            const float bs = s.beta[16 * si + lc];  // N diag(beta): column s's beta
             f32x4 x;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float v = kDecay ? acc[j][r] * exp2_fast(fminf(gt[r] - gs, 0.f)) : acc[j][r];
-                x[r] = (si < ti || lc < 4 * lg + r) ? v : 0.f;
+                x[r] = (si < ti || lc < 4 * lg + r) ? v * bs : 0.f;
             }
             if (si == ti) {
-                const float4 bt4 = *reinterpret_cast<const float4 *>(&s.beta[16 * ti + 4 * lg]);
-                *reinterpret_cast<float4 *>(&s.lt[ti][lc * LTS + 4 * lg]) =
-                    make_float4(bt4.x * x[0], bt4.y * x[1], bt4.z * x[2], bt4.w * x[3]);
+                *reinterpret_cast<float4 *>(&s.lt[ti][lc * LTS + 4 * lg]) = make_float4(x[0], x[1], x[2], x[3]);
             } else if (ti == I) {
                 gneg[si] = bf4(-x);
             } else {
@@ -317,7 +326,7 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
 
     auto solve = [&](auto ic_) {
         constexpr int I = decltype(ic_)::value;
-        // D_I = (I + L_II)^{-1} by forward substitution in fp32;
+        // D_I = (I + N_II diag(beta)_I)^{-1} by forward substitution in fp32;
         // lane = (column col, row quad q)
         const int col = lane >> 2, q = lane & 3;
         // each column piece is read as two 8-byte loads: on gfx950 a 16-byte
@@ -349,19 +358,18 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
             for (int r = 0; r < 4; ++r) x[r] = fmaf(-lj[r], xj, x[r]);
         };
         static_for<15>(sweep);
-        // D diag(beta): element (row, col) goes to A-operand lane
-        // (col / 4) * 16 + row, slot col % 4 (the scan scales its columns by
-        // -gamma for the state term)
-        const float bcol = s.beta[16 * I + col];
+        // D: element (row, col) goes to A-operand lane (col / 4) * 16 + row,
+        // slot col % 4 (the scan scales its columns by -gamma for the state
+        // term)
         __bf16 *dt = reinterpret_cast<__bf16 *>(&D.dtil[I][0]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int e = ((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3);
-            dt[e] = static_cast<__bf16>(x[r] * bcol);
+            dt[e] = static_cast<__bf16>(x[r]);
         }
-        // M_Ij = -D~_I G~_Ij, computed transposed (A = -G~^T from the
-        // accumulators, B = D~_I^T from its A-operand fragment) so the result
-        // comes out in A-operand order
+        // M_Ij = -D_I G~_Ij diag(beta)_j, computed transposed (A = -(G~
+        // diag(beta))^T from the accumulators, B = D_I^T from its A-operand
+        // fragment) so the result comes out in A-operand order
         if constexpr (I > 0) {
             if constexpr (I == 3) {  // blocks (3,0), (3,1), (3,2) from waves 0, 1
 #pragma unroll
@@ -440,7 +448,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
             }
             publish_state();
         }
-        // The output is computed transposed (Y^T = S Q^T + U^T Aqk^T, the same
+        // The output is computed transposed (Y^T = S Q^T + R^T Aqk^T, the same
         // fragments with the operands swapped), so lane (lg, lc) holds value
         // columns 4lg .. +3 of a tile for token lc of a row tile: one 8-byte
         // store per tile.
@@ -464,7 +472,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                 for (int i = 0; i < 4; ++i) {
                     vb[i] = col_gather4(R.v, Lds::VS, 16 * i, 16 * vt, lane);
                     dt[i] = D.dtil[i][lane];
-                    // -D_i diag(beta gamma)_i: D~_i's columns 16i + 4lg .. +3 times -gamma
+                    // -D_i diag(gamma)_i: D_i's columns 16i + 4lg .. +3 times -gamma
                     if constexpr (kDecay) {
                         const float4 gm = *reinterpret_cast<const float4 *>(&D.gam[16 * i + 4 * lg]);
                         dh[i] = bf4(__builtin_convertvector(dt[i], f32x4) * f32x4{-gm.x, -gm.y, -gm.z, -gm.w});
@@ -484,7 +492,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                 for (int p = 0; p < KSTEP; ++p)
 #pragma unroll
                     for (int ti = 0; ti < 4; ++ti) xp[ti] = mfma32(kf[p][ti], bS[p], xp[ti]);
-                // U_i = D~_i V_i - D^_i Z_i + sum_{j<i} M_ij U_j
+                // R_i = D_i V_i - D_i diag(gamma)_i Z_i + sum_{j<i} M_ij R_j
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                 f32x4 u[4];
 #pragma unroll
@@ -502,6 +510,20 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
 #pragma unroll
                 for (int i = 0; i < 4; ++i) s.uh[vt][i][lane] = ub[i];
                 lds_arrive(&s.ucount[vt], lane);
+                if (a.side) {  // routing signal: the residuals R (bf16, as carried) or the targets
+                    const bool res = a.side_kind == kSideResidual;
+                    uint16_t *so = static_cast<uint16_t *>(a.side) + vcol;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint2 x4 = __builtin_bit_cast(uint2, res ? ub[i] : vb[i]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int t = c * C + 16 * i + 4 * lg + r;
+                            const uint32_t w2 = r < 2 ? x4.x : x4.y;
+                            if (t < T) so[tok(t) * dv] = static_cast<uint16_t>(r & 1 ? w2 >> 16 : w2);
+                        }
+                    }
+                }
                 state_update<KT>(St, R, D, ub, KS, lane);
                 if (c + 1 < nchunks) {
                     lds_wait(&s.scount[vt], static_cast<unsigned int>(2 * (c + 1)), status);  // both output waves
@@ -526,7 +548,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                     // Q S^T for both value tiles, and the blocks (i, j <= i) of
                     // K Q^T in rows i = RT[r]; block (i, j) comes out with lane
                     // (lg, lc) holding [s = 16j + 4lg + r][t = 16i + lc], the
-                    // B-operand order of the product with U^T below
+                    // B-operand order of the product with R^T below
                     f32x4 xq[2][2], ka[2][4];
 #pragma unroll
                     for (int r = 0; r < 2; ++r)
@@ -552,10 +574,10 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
 #pragma unroll
                             for (int j = 0; j <= RT[r]; ++j) ka[r][j] = mfma32(kq[j], qf[r], ka[r][j]);
                     }
-                    // Aqk = lower(Q K^T * Gamma): entry (t, s) scaled by
-                    // 2^(g_t - g_s), exponent clamped at 0 so masked entries
-                    // stay finite, and zero above the diagonal; and the first
-                    // term of Y^T, S Q^T diag(gamma)
+                    // Aqk = lower(Q K^T * Gamma) diag(beta): entry (t, s)
+                    // scaled by 2^(g_t - g_s) beta_s, exponent clamped at 0 so
+                    // masked entries stay finite, and zero above the
+                    // diagonal; and the first term of Y^T, S Q^T diag(gamma)
                     bf16x4 aq[2][4];
                     f32x4 y[2][2];
 #pragma unroll
@@ -569,10 +591,12 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                                 const float4 gs4 = *reinterpret_cast<const float4 *>(&D.g[16 * j + 4 * lg]);
                                 gs[0] = gs4.x, gs[1] = gs4.y, gs[2] = gs4.z, gs[3] = gs4.w;
                             }
+                            const float4 bs4 = *reinterpret_cast<const float4 *>(&D.beta[16 * j + 4 * lg]);
+                            const float bs[4] = {bs4.x, bs4.y, bs4.z, bs4.w};
                             f32x4 x;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                const float v = kDecay ? ka[r][j][e] * exp2_fast(fminf(gt - gs[e], 0.f)) : ka[r][j][e];
+                                const float v = (kDecay ? ka[r][j][e] * exp2_fast(fminf(gt - gs[e], 0.f)) : ka[r][j][e]) * bs[e];
                                 x[e] = (j < i || 4 * lg + e <= lc) ? v : 0.f;
                             }
                             aq[r][j] = bf4(x);
@@ -583,7 +607,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                     }
                     lds_wait(&s.ucount[0], static_cast<unsigned int>(c + 1), status);
                     lds_wait(&s.ucount[1], static_cast<unsigned int>(c + 1), status);
-                    // Y^T += U^T Aqk^T, per value tile
+                    // Y^T += R^T Aqk^T, per value tile
                     const bf16x4 z4 = {};
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {

@@ -60,6 +60,9 @@ __global__ __launch_bounds__(kThreads) void delta_recurrent_kernel(DeltaArgs a) 
     __shared__ float serase[kGates2 ? TT : 1][kGates2 ? DK : 1];
     __shared__ float swrite[kGates2 ? TT : 1][kGates2 ? ROWS : 1];
     __shared__ float sy[TT][ROWS];
+    __shared__ float sside[TT][ROWS];  // the routing signal (residual or write value), when asked for
+    const bool side = a.side != nullptr;
+    const bool side_res = a.side_kind == kSideResidual;
 
     // ---- memory rows in registers
     float W[CPT];
@@ -189,7 +192,10 @@ __global__ __launch_bounds__(kThreads) void delta_recurrent_kernel(DeltaArgs a) 
                 const float dec = kChanDecay ? cur.dec[m] : cur.al;
                 W[m] = fmaf(br, cur.k[m], dec * W[m]);
             }
-            if (lr == 0) sy[t][rl] = y;
+            if (lr == 0) {
+                sy[t][rl] = y;
+                if (side) sside[t][rl] = side_res ? r : cur.target;
+            }
             cur = nxt;
         }
         __syncthreads();
@@ -198,6 +204,7 @@ __global__ __launch_bounds__(kThreads) void delta_recurrent_kernel(DeltaArgs a) 
             const int t = e / ROWS, i = e % ROWS;
             const int64_t gi = ((static_cast<int64_t>(b) * T + t0 + t) * H + h) * dv + slice * ROWS + i;
             IO::st(a.out, gi, sy[t][i]);
+            if (side) IO::st(a.side, gi, sside[t][i]);
         }
     }
 

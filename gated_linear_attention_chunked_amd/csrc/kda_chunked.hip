@@ -9,10 +9,13 @@
 //
 // Chunked form over C = 16 tokens (rows = tokens, S = memory at the chunk
 // start, G_t = sum_{j<=t} log2 a_j per channel, Gam_t = 2^{G_t}):
-//   L   = strict_lower(diag(beta) ((K * Gam) (K / Gam)^T))
-//   U   = (I + L)^{-1} diag(beta) (V - (K * Gam) S^T)
-//   Y   = (Q * Gam) S^T + lower((Q * Gam) (K / Gam)^T) U
-//   S'  = S diag(Gam_C) + U^T (K * Gam_C / Gam)
+//   N   = strict_lower((K * Gam) (K / Gam)^T)
+//   R   = (I + N diag(beta))^{-1} (V - (K * Gam) S^T)
+//   Y   = (Q * Gam) S^T + lower((Q * Gam) (K / Gam)^T) diag(beta) R
+//   S'  = S diag(Gam_C) + R^T diag(beta) (K * Gam_C / Gam)
+// Row t of R is token t's residual against the decayed memory (the write is
+// beta_t r_t k_t^T); beta is folded into the derived tiles that consume R,
+// so the scan carries the residual itself.
 // Every entry of the two Gram-type products is sum_c x_tc k_sc 2^{G_tc - G_sc}
 // with s <= t, at most |x_t||k_s|.  Splitting 2^{G_t - G_s} into 2^{G_t} and
 // 2^{-G_s} puts both products on MFMA; 2^{-G_s} stays finite while the decay
@@ -28,10 +31,10 @@
 // one's, and the coupling between them is a 16x16 block per product,
 //   G_10 = (K_1 * Gam_1)(K_0 * Gam_C0 / Gam_0)^T,  Aqk_10 = (Q_1 * Gam_1)(K_0 * Gam_C0 / Gam_0)^T,
 // whose factors split at the last even token and are both at most 1, so
-// they need no exact form.  Then U_0 = T_00 (V_0 - Z_0),
-// U_1 = T_11 (V_1 - Z_1) + M_10 U_0 with M_10 = -T_11 G_10, and one 32-token
-// state update: one more dependent product than a 16-token step, for half
-// as many steps.
+// they need no exact form.  Then R_0 = D_0 (V_0 - Z_0),
+// R_1 = D_1 (V_1 - Z_1) + M_10 R_0 with M_10 = -D_1 G_10 diag(beta_0) and
+// D_i = (I + N_ii diag(beta_i))^{-1}, and one 32-token state update: one
+// more dependent product than a 16-token step, for half as many steps.
 //
 // Two kernels per call:
 //   derivation: one wave per (sequence, head, sub-chunk), all sub-chunks at
@@ -43,16 +46,16 @@
 //   scan:  one workgroup per (b, h, value slice of 16 NVT columns):
 //   carry  (NVT waves, one 16-column tile each): Z = (K*Gam) S^T for both
 //          sub-chunks, the two 16x16 solves and the coupling on three MFMA,
-//          state update S^T <- diag(Gam_C) S^T + (K*Gam_C/Gam)^T U over the
+//          state update S^T <- diag(Gam_C) S^T + (beta K*Gam_C/Gam)^T R over the
 //          32 tokens, bf16 copy of S published for the output.
-//   output (NVT waves): from the published bf16 S it forms U exactly as the
+//   output (NVT waves): from the published bf16 S it forms R exactly as the
 //          carry does (same operands, same order), then Y^T = S (Q*Gam)^T +
-//          U^T Aqk^T, 8-byte row stores.  Recomputing U costs the output a
+//          R^T Aqk^T, 8-byte row stores.  Recomputing R costs the output a
 //          few products and takes a hand-off off the carry's chain.
 //   producers (4 waves): producer p copies every fourth pair's two blocks
 //          (p, p+4, ...) and the slice's value rows into its own LDS slot,
 //          loads issued four pairs ahead.
-// There is no workgroup barrier in the chunk loop: slots, U and the bf16
+// There is no workgroup barrier in the chunk loop: slots, R and the bf16
 // state move between roles through bounded LDS counters.
 #include <type_traits>
 
@@ -81,13 +84,13 @@ struct KdaShape {
 template <int DK>
 struct KdaBlock {
     __bf16 kd[C16 * DK];   // k * Gam
-    __bf16 ke[C16 * DK];   // k * Gam_C / Gam
+    __bf16 ke[C16 * DK];   // beta k * Gam_C / Gam
     __bf16 qd[C16 * DK];   // q * Gam
-    bf16x4 aqk[64];        // lower((Q*Gam)(K/Gam)^T), B-operand order: lane (g, i) holds [t = i][s = 4g + r]
-    bf16x4 dt[64];         // (I + L)^{-1} diag(beta), A-operand order
+    bf16x4 aqk[64];        // lower((Q*Gam)(K/Gam)^T) diag(beta), B-operand order: lane (g, i) holds [t = i][s = 4g + r]
+    bf16x4 dt[64];         // D = (I + N diag(beta))^{-1}, A-operand order
     float gc[DK];          // even sub-chunk: Gam_C of the pair, per channel
-    bf16x4 mx[64];         // odd sub-chunk: M_10 = -(I + L_11)^{-1} diag(beta_1) G_10, A-operand order
-    bf16x4 ax[64];         // odd sub-chunk: cross block of Aqk, B-operand order: lane (g, i) holds [t = i][s = 4g + r]
+    bf16x4 mx[64];         // odd sub-chunk: M_10 = -D_1 G_10 diag(beta_0), A-operand order
+    bf16x4 ax[64];         // odd sub-chunk: cross block of Aqk (times beta_0), B-operand order: lane (g, i) holds [t = i][s = 4g + r]
     static constexpr int kRowPieces = 3 * C16 * DK / 8;            // 16-byte pieces of kd, ke, qd
     static constexpr int kPieces = kRowPieces + 64 + DK / 4 + 64;  // all 16-byte pieces
 };
@@ -181,6 +184,8 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
             ra[t] = t < nval ? *reinterpret_cast<const Pk *>(gal + off) : one;
         }
         const uint16_t rb = gbe[hb + static_cast<int64_t>(min(t0 + (lane & 15), T - 1)) * H];
+        const float bl = (lane & 15) < nval ? bf16_bits_to_f32(rb) : 0.f;  // beta of token lane & 15
+        auto beta_of = [&](int t) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bl), t)); };
         // channel j of a packed pair, widened
         auto chan = [](Pk x, int j) { return bf16_bits_to_f32(static_cast<uint16_t>(x >> (16 * j))); };
         // CH consecutive bf16 of row t, channels CH*lane ..
@@ -273,17 +278,21 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
                         ke[j] = kv * exp2_fast(gcx[j] - G[t][j]);
                     }
                 }
-                float kdo[CH], qdo[CH], keo[CH];
+                const float bt = beta_of(t);
+                float kdo[CH], qdo[CH], keo[CH], keb[CH];
 #pragma unroll
                 for (int j = 0; j < CH; ++j) {
                     kdo[j] = kd[j] * sdq[j];
                     qdo[j] = qd[j] * sdq[j];
-                    keo[j] = ke[j] * se[j];
+                    keb[j] = ke[j] * bt;
+                    keo[j] = keb[j] * se[j];
                 }
                 put(o.kd, DK, t, kdo);
                 put(o.qd, DK, t, qdo);
                 put(o.ke, DK, t, keo);
-                if (!odd) put(s.k0, KS, t, ke);  // local k * Gam_C / Gam for the odd sub-chunk's cross blocks
+                // local beta k * Gam_C / Gam for the odd sub-chunk's cross
+                // blocks (their column scale diag(beta_0) comes with it)
+                if (!odd) put(s.k0, KS, t, keb);
                 if constexpr (F) {
                     put(s.a, KS, t, kd);
                     put(s.b, KS, t, qd);
@@ -371,22 +380,23 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
             };
             static_for<5>(level);
         }
-        // L = beta_t G (s < t) by column; Aqk (s <= t)
+        // N diag(beta) = G beta_s (s < t) by column; Aqk diag(beta) (s <= t)
         {
             const float4 bt4 = *reinterpret_cast<const float4 *>(&s.beta[4 * lg]);
-            const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+            const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};  // beta_s of Aqk's rows s = 4g + r
+            const float bs = s.beta[lc];                         // beta_s of G's column s = i
             float l[4];
             f32x4 x;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                l[r] = lc < 4 * lg + r ? bt[r] * gr[r] : 0.f;
-                x[r] = 4 * lg + r <= lc ? aq[r] : 0.f;
+                l[r] = lc < 4 * lg + r ? gr[r] * bs : 0.f;
+                x[r] = 4 * lg + r <= lc ? aq[r] * bt[r] : 0.f;
             }
             *reinterpret_cast<float4 *>(&s.lt[lc * KLTS + 4 * lg]) = make_float4(l[0], l[1], l[2], l[3]);
             o.aqk[lane] = bf4(x);
         }
         wave_lds_fence();
-        // D = (I + L)^{-1}: forward substitution in fp32, lane = (column, row quad)
+        // D = (I + N diag(beta))^{-1}: forward substitution in fp32, lane = (column, row quad)
         {
             const int col = lane >> 2, q = lane & 3;
             float x[4];
@@ -402,10 +412,9 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
                 x[3] = fmaf(-l4.w, xj, x[3]);
             };
             static_for<15>(sweep);
-            const float bcol = s.beta[col];
             __bf16 *dt = reinterpret_cast<__bf16 *>(&s.dt[0]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dt[((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3)] = static_cast<__bf16>(x[r] * bcol);
+            for (int r = 0; r < 4; ++r) dt[((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3)] = static_cast<__bf16>(x[r]);
         }
         wave_lds_fence();
         o.dt[lane] = s.dt[lane];
@@ -440,18 +449,19 @@ __global__ __launch_bounds__(64) void kda_derive_kernel(DeltaArgs a, KdaBlock<DK
             a10 = mfma32(k0f, row_frag2(s.b, KS, 0, 32 * p, lane), a10);  // lane (g, i): [s = 4g + r][t = i]
         }
         o.ax[lane] = bf4(a10);
-        // M_10 = -T_11 G_10 with T_11 = (I + L_11)^{-1} diag(beta_1), formed
-        // transposed (A = -G_10^T from the accumulator, B = T_11^T from its
-        // A-operand fragment) so it comes out in A-operand order
+        // M_10 = -D_1 G_10 diag(beta_0) (the beta_0 came with the even
+        // tile), formed transposed (A = -(G_10 diag(beta_0))^T from the
+        // accumulator, B = D_1^T from its A-operand fragment) so it comes out
+        // in A-operand order
         o.mx[lane] = bf4(mfma16(bf4(-g10), s.dt[lane], f32x4{0.f, 0.f, 0.f, 0.f}));
     }
 }
 
-// U of a pair of sub-chunks from the bf16 state at the pair start:
-//   Z_i = (K*Gam)_i S^T (pair-relative tiles), U_0 = T_00 (V_0 - Z_0),
-//   U_1 = T_11 (V_1 - Z_1) + M_10 U_0.
+// R of a pair of sub-chunks from the bf16 state at the pair start:
+//   Z_i = (K*Gam)_i S^T (pair-relative tiles), R_0 = D_0 (V_0 - Z_0),
+//   R_1 = D_1 (V_1 - Z_1) + M_10 R_0.
 // The carry and the output wave both call this on the same operands, so both
-// get the same U bit for bit.  Lane (g, i) holds rows t = 4g + r, column i.
+// get the same R bit for bit.  Lane (g, i) holds rows t = 4g + r, column i.
 template <int KSTEP, int KT>
 __device__ __forceinline__ void pair_solve(const bf16x8 (&kf0)[KSTEP], const bf16x8 (&kf1)[KSTEP], const bf16x4 (&Sb)[KT],
                                            bf16x4 vb0, bf16x4 vb1, bf16x4 dt0, bf16x4 dt1, bf16x4 mxf, bf16x4 &ub0,
@@ -555,12 +565,26 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
             for (int c = 0; c < npairs; ++c) {
                 bf16x4 ub0, ub1;
                 pair_solve(kf0, kf1, Sb, vb0, vb1, dt0, dt1, mxf, ub0, ub1);
-                // S^T <- diag(Gam_C) S^T + [K*Gam_C/Gam]^T [U_0; U_1] over the 32 tokens
+                // S^T <- diag(Gam_C) S^T + [beta K*Gam_C/Gam]^T [R_0; R_1] over the 32 tokens
                 const bf16x8 bU = cat8(ub0, ub1);
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) {
                     St[kt] = St[kt] * f32x4{gcv[kt].x, gcv[kt].y, gcv[kt].z, gcv[kt].w};
                     St[kt] = mfma32(kef[kt], bU, St[kt]);
+                }
+                if (a.side) {  // routing signal: the residuals (bf16, as carried) or the targets
+                    const bool res = a.side_kind == kSideResidual;
+                    uint16_t *so = static_cast<uint16_t *>(a.side) + v0 + 16 * vt + lc;
+#pragma unroll
+                    for (int sc = 0; sc < 2; ++sc) {
+                        const uint2 x4 = __builtin_bit_cast(uint2, res ? (sc ? ub1 : ub0) : (sc ? vb1 : vb0));
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int t = 2 * C16 * c + C16 * sc + 4 * lg + r;
+                            const uint32_t w2 = r < 2 ? x4.x : x4.y;
+                            if (t < T) so[tok(t) * dv] = static_cast<uint16_t>(r & 1 ? w2 >> 16 : w2);
+                        }
+                    }
                 }
                 if (c + 1 < npairs) load_ops(c + 1);
 #pragma unroll
@@ -603,10 +627,10 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) Sb[kt] = s.sh[c % Lds::NSB][vt][kt][lane];
                 if constexpr (Lds::kStateGuard) lds_arrive(&s.so[vt], lane);
-                // U exactly as the carry forms it, from the same bf16 state
+                // R exactly as the carry forms it, from the same bf16 state
                 bf16x4 ub0, ub1;
                 pair_solve(kf0, kf1, Sb, vb0, vb1, dt0, dt1, mxf, ub0, ub1);
-                // Y^T = S (Q*Gam)^T + U^T Aqk^T: lane (g, i) holds columns 4g + r of
+                // Y^T = S (Q*Gam)^T + R^T Aqk^T: lane (g, i) holds columns 4g + r of
                 // token i; two independent accumulation chains per sub-chunk
                 f32x4 y00 = {0.f, 0.f, 0.f, 0.f}, y01 = {0.f, 0.f, 0.f, 0.f};
                 f32x4 y10 = {0.f, 0.f, 0.f, 0.f}, y11 = {0.f, 0.f, 0.f, 0.f};

@@ -175,8 +175,21 @@ lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, 
                        const void *alpha, const void *erase_b, const void *write_w,
                        const void *beta, const float *state_in, void *out, float *state_out,
                        void *workspace, size_t workspace_bytes, int algo, hipStream_t stream) {
+    return lam_forward_side(variant, dtype, B, T, H, dk, dv, q, k, v, alpha, erase_b, write_w, beta,
+                            state_in, out, state_out, LAM_SIDE_NONE, nullptr, workspace,
+                            workspace_bytes, algo, stream);
+}
+
+lam_status lam_forward_side(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                            int64_t dv, const void *q, const void *k, const void *v,
+                            const void *alpha, const void *erase_b, const void *write_w,
+                            const void *beta, const float *state_in, void *out, float *state_out,
+                            int side, void *side_out, void *workspace, size_t workspace_bytes,
+                            int algo, hipStream_t stream) {
     lam_status st = check_delta_shape(variant, dtype, B, T, H, dk, dv, algo);
     if (st != LAM_OK) return st;
+    if (side < LAM_SIDE_NONE || side > LAM_SIDE_VALUE) return LAM_ERR_INVALID_ARG;
+    if (side == LAM_SIDE_NONE) side_out = nullptr;
     if (B == 0 || H == 0) return LAM_OK;
     int64_t nk, nv, ns, nst;
     elems(B, T, H, dk, nk);
@@ -187,9 +200,20 @@ lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, 
         if (!q || !k || !v || !beta || !out) return LAM_ERR_INVALID_ARG;
         if (variant != LAM_DELTANET && !alpha) return LAM_ERR_INVALID_ARG;
         if (variant == LAM_GATED_DELTANET2 && (!erase_b || !write_w)) return LAM_ERR_INVALID_ARG;
+        if (side != LAM_SIDE_NONE && !side_out) return LAM_ERR_INVALID_ARG;
     }
     const int64_t es = dtype == LAM_BF16 ? 2 : 4;
     const int64_t out_bytes = nv * es;
+    if (side_out) {  // the side output may overlap nothing else
+        const void *other[] = {q, k, v, variant == LAM_DELTANET ? nullptr : alpha,
+                               variant == LAM_GATED_DELTANET2 ? erase_b : nullptr,
+                               variant == LAM_GATED_DELTANET2 ? write_w : nullptr, beta, state_in,
+                               out, state_out};
+        const int64_t ob[] = {nk * es, nk * es, nv * es, (variant == LAM_KIMI_DELTA ? nk : ns) * es,
+                              nk * es, nv * es, ns * es, nst * 4, out_bytes, nst * 4};
+        for (int i = 0; i < 10; ++i)
+            if (overlaps(side_out, out_bytes, other[i], ob[i])) return LAM_ERR_INVALID_ARG;
+    }
     const int64_t alpha_bytes = (variant == LAM_KIMI_DELTA ? nk : ns) * es;
     if (overlaps(out, out_bytes, q, nk * es) || overlaps(out, out_bytes, k, nk * es) ||
         overlaps(out, out_bytes, v, nv * es) || overlaps(out, out_bytes, beta, ns * es) ||
@@ -218,15 +242,37 @@ lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, 
     size_t need;
     st = plan_delta(a, algo, &sched, &need);
     if (st != LAM_OK) return st;
-    const void *args[] = {q, k, v, a.alpha, a.erase_b, a.write_w, beta, state_in, out, state_out};
+    a.side = side_out;
+    a.side_kind = side;
+    const void *args[] = {q, k, v, a.alpha, a.erase_b, a.write_w, beta, state_in, out, state_out, side_out};
     const int64_t arg_bytes[] = {nk * es, nk * es, nv * es, alpha_bytes, nk * es, nv * es, ns * es,
-                                 nst * 4, out_bytes, nst * 4};
-    if (!workspace_ok(workspace, workspace_bytes, need, args, arg_bytes, 10)) return LAM_ERR_INVALID_ARG;
+                                 nst * 4, out_bytes, nst * 4, out_bytes};
+    if (!workspace_ok(workspace, workspace_bytes, need, args, arg_bytes, 11)) return LAM_ERR_INVALID_ARG;
     a.ws = need ? workspace : nullptr;
 
     if (T == 0 && !state_out) return LAM_OK;
     if (sched == kChunked) return from_hip(lam::launch_delta_chunked(a, stream));
     return from_hip(lam::launch_delta_recurrent(a, stream));
+}
+
+lam_status lam_route(int dtype, int64_t M, int64_t D, int64_t N, const void *s, const void *P, void *h,
+                     hipStream_t stream) {
+    if (dtype != LAM_F32 && dtype != LAM_BF16) return LAM_ERR_INVALID_ARG;
+    if (M < 0 || D <= 0 || N <= 0) return LAM_ERR_INVALID_ARG;
+    if (!lam::route_supported(D, N)) return LAM_ERR_UNSUPPORTED;
+    int64_t ns, nh, np;
+    // sizes, 32-bit column indices and the grid (256 x 128 tiles)
+    if (!mul_ok(M, N, ns) || !mul_ok(M, D, nh) || !mul_ok(D, N, np)) return LAM_ERR_INVALID_ARG;
+    if (D > INT_MAX / 2 || N > INT_MAX / 2) return LAM_ERR_INVALID_ARG;
+    if (((M + 255) / 256) * ((D + 127) / 128) > INT_MAX) return LAM_ERR_INVALID_ARG;
+    if (M == 0) return LAM_OK;
+    if (!s || !P || !h) return LAM_ERR_INVALID_ARG;
+    // rows are read as 16-byte pieces
+    const auto al = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (!al(s) || !al(P) || !al(h)) return LAM_ERR_INVALID_ARG;
+    const int64_t es = dtype == LAM_BF16 ? 2 : 4;
+    if (overlaps(h, nh * es, s, ns * es) || overlaps(h, nh * es, P, np * es)) return LAM_ERR_INVALID_ARG;
+    return from_hip(lam::launch_route(dtype, M, D, N, s, P, h, stream));
 }
 
 lam_status lam_backward_workspace_size(int variant, int dtype, int64_t B, int64_t T, int64_t H,

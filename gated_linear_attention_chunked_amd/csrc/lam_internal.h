@@ -24,7 +24,12 @@ struct DeltaArgs {
     // Caller-provided workspace (chunked schedules only): the status block
     // (kStatusBytes, word 0 = device error bits), then the derived blocks.
     void *ws;
+    // Per-token routing signal [B,T,H,dv] in the storage dtype, or NULL:
+    // the residual r (kSideResidual) or the write value (kSideValue).
+    void *side;
+    int side_kind;
 };
+enum { kSideNone = 0, kSideResidual = 1, kSideValue = 2 };
 
 struct VlaArgs {
     int dtype;
@@ -76,6 +81,11 @@ struct DeltaBwdArgs {
 };
 bool delta_backward_workspace(const DeltaArgs &a, size_t *bytes);
 hipError_t launch_delta_backward(const DeltaBwdArgs &g, hipStream_t stream);
+
+// Routing epilogue h += s P^T (s [M,N], P [D,N], h [M,D], one dtype).
+bool route_supported(int64_t D, int64_t N);
+hipError_t launch_route(int dtype, int64_t M, int64_t D, int64_t N, const void *s, const void *P, void *h,
+                        hipStream_t stream);
 
 // Kimi Delta (per-channel decay) has its own chunked kernel.
 bool kda_chunked_supported(const DeltaArgs &a);

@@ -49,8 +49,8 @@
  *   LAM_ERR_INVALID_ARG before any HIP call.  The call reads and writes it
  *   only through the work it enqueues on `stream`, so the caller may reuse
  *   it for any later work ordered after the call on that stream.  Sizes at
- *   dk = 128: 5,888 B per (b, h, 64-token chunk) for DeltaNet, Gated
- *   DeltaNet and Gated DeltaNet-2 (24.1 MB at B8 T4096 H8), and 14,848 B per
+ *   dk = 128: 6,144 B per (b, h, 64-token chunk) for DeltaNet, Gated
+ *   DeltaNet and Gated DeltaNet-2 (25.2 MB at B8 T4096 H8), and 14,848 B per
  *   (b, h, 16-token sub-chunk, counted in whole pairs) for Kimi Delta
  *   (487 MB at B2 T32768 H8), plus the 256-byte status block.
  *   Status block: the first 256 bytes of a workspace.  Word 0 (uint32)
@@ -155,6 +155,51 @@ lam_status lam_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, 
  */
 lam_status lam_forward_workspace_size(int variant, int dtype, int64_t B, int64_t T, int64_t H,
                                       int64_t dk, int64_t dv, int algo, size_t *bytes);
+
+/*
+ * Cross-layer routing signal ("Mechanisms, trade-offs and cross-layer routing
+ * of linear-attention architectures", sections "Methodology" and "Technical
+ * details"): CLER and CLER-H route each token's delta-rule residual r (the
+ * rules above: r = z - W~ e, taken against the decayed memory), CLVR routes
+ * the write value (v; z = w*v for Gated DeltaNet-2).
+ */
+typedef enum { LAM_SIDE_NONE = 0, LAM_SIDE_RESIDUAL = 1, LAM_SIDE_VALUE = 2 } lam_side;
+
+/*
+ * lam_forward that also writes the routing signal of every token:
+ *   side         lam_side (LAM_SIDE_NONE: exactly lam_forward)
+ *   side_out     [B,T,H,dv] in dtype, required unless LAM_SIDE_NONE; may not
+ *                overlap any other argument or the workspace
+ * Same workspace (lam_forward_workspace_size), schedules and errors as
+ * lam_forward.  On the chunked schedule the residual is rounded to bf16 where
+ * the scan rounds it for its own products (the value emitted is the one the
+ * memory update uses); the token-recurrent schedule computes it in fp32.
+ */
+lam_status lam_forward_side(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                            int64_t dv, const void *q, const void *k, const void *v,
+                            const void *alpha, const void *erase_b, const void *write_w,
+                            const void *beta, const float *state_in, void *out, float *state_out,
+                            int side, void *side_out, void *workspace, size_t workspace_bytes,
+                            int algo, hipStream_t stream);
+
+/*
+ * Routing epilogue: h <- h + s P^T, i.e. every token's signal s_t (all heads,
+ * N = H * dv values) mapped to the model width by P and added to the residual
+ * stream h_t (same passages: the zero-initialised projection P and
+ * epsilon = P s added to h).  The projection is a contraction on the matrix
+ * cores with fp32 accumulation; the add is fused into its epilogue (h is read
+ * once and written once).
+ *   dtype        lam_dtype of s, P and h (bf16 operands feed bf16 matrix
+ *                cores; f32 operands fp32 ones)
+ *   M            tokens (B * T), >= 0
+ *   D            model width, a multiple of 16
+ *   N            signal width, a multiple of 32
+ *   s            [M, N], P [D, N], h [M, D] (row-major), each 16-byte
+ *                aligned; h may not overlap s or P
+ * Errors as lam_forward; results are bitwise reproducible.
+ */
+lam_status lam_route(int dtype, int64_t M, int64_t D, int64_t N, const void *s, const void *P, void *h,
+                     hipStream_t stream);
 
 /*
  * VLA forward scan over a [B,T] block (dk = dv = d, d in {32, 64, 96, 128}).

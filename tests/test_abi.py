@@ -149,9 +149,9 @@ def _ws_size(lib, variant=1, dtype=1, B=2, T=8, H=2, dk=64, dv=64, algo=0):
 
 def test_workspace_size_query(lib):
     # chunked delta schedule: 256-byte status block + 5,888 B per (b, h, 64-token chunk)
-    assert _ws_size(lib, 1, 1, 8, 4096, 8, 128, 128) == (OK, 256 + 8 * 8 * 64 * 5888)
-    assert _ws_size(lib, 3, 1, 8, 4096, 8, 128, 128) == (OK, 256 + 8 * 8 * 64 * 5888)
-    assert _ws_size(lib, 0, 1, 1, 65, 1, 128, 128) == (OK, 256 + 2 * 5888)   # ragged: whole chunks
+    assert _ws_size(lib, 1, 1, 8, 4096, 8, 128, 128) == (OK, 256 + 8 * 8 * 64 * 6144)
+    assert _ws_size(lib, 3, 1, 8, 4096, 8, 128, 128) == (OK, 256 + 8 * 8 * 64 * 6144)
+    assert _ws_size(lib, 0, 1, 1, 65, 1, 128, 128) == (OK, 256 + 2 * 6144)   # ragged: whole chunks
     # Kimi Delta: 14,848 B per 16-token sub-chunk at dk = 128, counted in pairs
     assert _ws_size(lib, 2, 1, 2, 32768, 8, 128, 128) == (OK, 256 + 2 * 8 * 2048 * 14848)
     assert _ws_size(lib, 2, 1, 1, 17, 1, 128, 128) == (OK, 256 + 2 * 14848)
@@ -242,3 +242,31 @@ def test_backward_rejects_bad_arguments(lib):
     assert _bwd(lib, gk=FAKE + 0x100000000 + 64, ws=WS, ws_bytes=need) == INVALID
     assert _bwd(lib, dsin=WS + 512, ws=WS, ws_bytes=need) == INVALID
     assert _bwd(lib, B=0, ws=None) == OK
+
+
+def test_forward_side_rejects_bad_arguments(lib):
+    def fs(side=1, sout=FAKE + 0x90000000, **kw):
+        p = dict(variant=1, dtype=1, B=2, T=8, H=2, dk=64, dv=64)
+        p.update(kw)
+        return lib.lam_forward_side(p["variant"], p["dtype"], p["B"], p["T"], p["H"], p["dk"], p["dv"], FAKE,
+                                    FAKE + 0x10000000, FAKE + 0x20000000, FAKE + 0x30000000, None, None,
+                                    FAKE + 0x60000000, None, FAKE + 0x70000000, None, side, sout, None, 0, 1,
+                                    None)
+    assert fs(side=3) == INVALID
+    assert fs(side=-1) == INVALID
+    assert fs(sout=None) == INVALID                 # a side output asked for, nowhere to put it
+    assert fs(sout=FAKE + 0x70000000 + 2) == INVALID  # inside out
+    assert fs(sout=FAKE + 16) == INVALID            # inside q
+    assert fs(B=0) == OK
+
+
+def test_route_rejects_bad_arguments(lib):
+    S, P, Hh = FAKE, FAKE + 0x10000000, FAKE + 0x20000000
+    assert lib.lam_route(2, 64, 128, 256, S, P, Hh, None) == INVALID   # dtype
+    assert lib.lam_route(1, -1, 128, 256, S, P, Hh, None) == INVALID
+    assert lib.lam_route(1, 64, 120, 256, S, P, Hh, None) == UNSUPPORTED  # D % 16
+    assert lib.lam_route(1, 64, 128, 48, S, P, Hh, None) == UNSUPPORTED   # N % 32
+    assert lib.lam_route(1, 64, 128, 256, None, P, Hh, None) == INVALID
+    assert lib.lam_route(1, 64, 128, 256, S + 8, P, Hh, None) == INVALID  # not 16-byte aligned
+    assert lib.lam_route(1, 64, 128, 256, S, P, S + 64, None) == INVALID  # h inside s
+    assert lib.lam_route(1, 0, 128, 256, None, None, None, None) == OK    # no tokens
