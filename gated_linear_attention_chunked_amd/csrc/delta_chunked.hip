@@ -97,7 +97,7 @@ struct DerBlock {
     float gam[C];              // gamma_t
     float sc[C];               // beta_t gamma_C / gamma_t
     float g[C];                // log2 gamma_t
-    float beta[C];             // beta_t (zero on padding rows)
+    float gb[C];               // log2 gamma_t - log2 beta_t (+inf where beta_t = 0); DeltaNet: beta_t
 };
 static_assert(sizeof(DerBlock) % 256 == 0, "workspace blocks stay 256-byte aligned");
 constexpr int kDerPieces = static_cast<int>(sizeof(DerBlock) / 16);  // 16-byte pieces
@@ -267,8 +267,11 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
         D.g[lane] = g;
         D.gam[lane] = exp2_fast(g);
         D.sc[lane] = exp2_fast(gl - g) * s.beta[lane];
+        // the output's column scale beta_s folded into its exponent,
+        // 2^(g_t - g_s) beta_s = 2^(g_t - (g_s - log2 beta_s)); DeltaNet
+        // keeps a plain factor
+        D.gb[lane] = kDecay ? g - __log2f(s.beta[lane]) : s.beta[lane];
     }
-    if (w == 1) D.beta[lane] = s.beta[lane];
     __syncthreads();
 
     // ---- E K^T tiles of block row I (phase 1), then the inverse of its
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(NTD) void delta_chunked_derive_kernel(DeltaArgs a, 
 }
 
 // ================================= scan =================================
-template <int VARIANT, int DK>
+template <int VARIANT, int DK, bool SIDE>
 __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, const DerBlock *__restrict__ der,
                                                                unsigned int *status) {
     constexpr bool kDecay = VARIANT != kDeltaNet;
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
 #pragma unroll
                 for (int i = 0; i < 4; ++i) s.uh[vt][i][lane] = ub[i];
                 lds_arrive(&s.ucount[vt], lane);
-                if (a.side) {  // routing signal: the residuals R (bf16, as carried) or the targets
+                if constexpr (SIDE) {  // routing signal: the residuals R (bf16, as carried) or the targets
                     const bool res = a.side_kind == kSideResidual;
                     uint16_t *so = static_cast<uint16_t *>(a.side) + vcol;
 #pragma unroll
@@ -575,9 +578,11 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                             for (int j = 0; j <= RT[r]; ++j) ka[r][j] = mfma32(kq[j], qf[r], ka[r][j]);
                     }
                     // Aqk = lower(Q K^T * Gamma) diag(beta): entry (t, s)
-                    // scaled by 2^(g_t - g_s) beta_s, exponent clamped at 0 so
-                    // masked entries stay finite, and zero above the
-                    // diagonal; and the first term of Y^T, S Q^T diag(gamma)
+                    // scaled by 2^(g_t - g_s) beta_s = 2^(g_t - gb_s),
+                    // exponent clamped at 0 so masked entries stay finite
+                    // (below the diagonal it is at most log2 beta_s <= 0), and
+                    // zero above the diagonal; and the first term of Y^T,
+                    // S Q^T diag(gamma)
                     bf16x4 aq[2][4];
                     f32x4 y[2][2];
 #pragma unroll
@@ -586,17 +591,12 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                         const float gt = kDecay ? D.g[16 * i + lc] : 0.f;
 #pragma unroll
                         for (int j = 0; j <= RT[r]; ++j) {
-                            float gs[4] = {0.f, 0.f, 0.f, 0.f};
-                            if constexpr (kDecay) {
-                                const float4 gs4 = *reinterpret_cast<const float4 *>(&D.g[16 * j + 4 * lg]);
-                                gs[0] = gs4.x, gs[1] = gs4.y, gs[2] = gs4.z, gs[3] = gs4.w;
-                            }
-                            const float4 bs4 = *reinterpret_cast<const float4 *>(&D.beta[16 * j + 4 * lg]);
-                            const float bs[4] = {bs4.x, bs4.y, bs4.z, bs4.w};
+                            const float4 gs4 = *reinterpret_cast<const float4 *>(&D.gb[16 * j + 4 * lg]);
+                            const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
                             f32x4 x;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                const float v = (kDecay ? ka[r][j][e] * exp2_fast(fminf(gt - gs[e], 0.f)) : ka[r][j][e]) * bs[e];
+                                const float v = kDecay ? ka[r][j][e] * exp2_fast(fminf(gt - gs[e], 0.f)) : ka[r][j][e] * gs[e];
                                 x[e] = (j < i || 4 * lg + e <= lc) ? v : 0.f;
                             }
                             aq[r][j] = bf4(x);
@@ -780,7 +780,10 @@ hipError_t launch_dk(const DeltaArgs &a, hipStream_t stream) {
     DerBlock *der = reinterpret_cast<DerBlock *>(static_cast<char *>(a.ws) + kStatusBytes);
     if (tasks > 0)
         delta_chunked_derive_kernel<VARIANT, DK><<<static_cast<unsigned>(tasks), NTD, 0, stream>>>(a, der, status);
-    delta_chunked_wy_kernel<VARIANT, DK><<<blocks, NT8, 0, stream>>>(a, der, status);
+    if (a.side)
+        delta_chunked_wy_kernel<VARIANT, DK, true><<<blocks, NT8, 0, stream>>>(a, der, status);
+    else
+        delta_chunked_wy_kernel<VARIANT, DK, false><<<blocks, NT8, 0, stream>>>(a, der, status);
     return hipGetLastError();
 }
 

@@ -485,7 +485,7 @@ __device__ __forceinline__ void pair_solve(const bf16x8 (&kf0)[KSTEP], const bf1
     ub1 = bf4(mfma16(mxf, ub0, u1));
 }
 
-template <int DK, int NVT>
+template <int DK, int NVT, bool SIDE>
 __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArgs a, const KdaBlock<DK> *__restrict__ der,
                                                                          int64_t Ts, int64_t tb, unsigned int *status) {
     constexpr int KBV = KdaShape<NVT>::BV;
@@ -572,18 +572,17 @@ __global__ __launch_bounds__(KdaShape<NVT>::NT) void kda_chunked_kernel(DeltaArg
                     St[kt] = St[kt] * f32x4{gcv[kt].x, gcv[kt].y, gcv[kt].z, gcv[kt].w};
                     St[kt] = mfma32(kef[kt], bU, St[kt]);
                 }
-                if (a.side) {  // routing signal: the residuals (bf16, as carried) or the targets
+                if constexpr (SIDE) {  // routing signal: the residuals (bf16, as carried) or the targets
                     const bool res = a.side_kind == kSideResidual;
-                    uint16_t *so = static_cast<uint16_t *>(a.side) + v0 + 16 * vt + lc;
+                    uint16_t *so = static_cast<uint16_t *>(a.side) + vcol;
+                    const uint2 x0 = __builtin_bit_cast(uint2, ub0), y0 = __builtin_bit_cast(uint2, vb0);
+                    const uint2 x1 = __builtin_bit_cast(uint2, ub1), y1 = __builtin_bit_cast(uint2, vb1);
+                    const uint32_t w[4] = {res ? x0.x : y0.x, res ? x0.y : y0.y, res ? x1.x : y1.x, res ? x1.y : y1.y};
 #pragma unroll
-                    for (int sc = 0; sc < 2; ++sc) {
-                        const uint2 x4 = __builtin_bit_cast(uint2, res ? (sc ? ub1 : ub0) : (sc ? vb1 : vb0));
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int t = 2 * C16 * c + C16 * sc + 4 * lg + r;
-                            const uint32_t w2 = r < 2 ? x4.x : x4.y;
-                            if (t < T) so[tok(t) * dv] = static_cast<uint16_t>(r & 1 ? w2 >> 16 : w2);
-                        }
+                    for (int e = 0; e < 8; ++e) {  // sub-chunk e / 4, row 4 lg + e % 4
+                        const int t = 2 * C16 * c + C16 * (e >> 2) + 4 * lg + (e & 3);
+                        const uint32_t w2 = w[e >> 1];
+                        if (t < T) so[tok(t) * dv] = static_cast<uint16_t>(e & 1 ? w2 >> 16 : w2);
                     }
                 }
                 if (c + 1 < npairs) load_ops(c + 1);
@@ -761,7 +760,10 @@ static hipError_t launch_dk(const DeltaArgs &a, hipStream_t stream) {
     KdaBlock<DK> *der = reinterpret_cast<KdaBlock<DK> *>(static_cast<char *>(a.ws) + kStatusBytes);
     if (pairs > 0)
         kda_derive_kernel<DK><<<static_cast<unsigned>(pairs), 64, 0, stream>>>(a, der, a.T, 0, status);
-    kda_chunked_kernel<DK, NVT><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a, pairs > 0 ? der : nullptr, a.T, 0, status);
+    if (a.side)
+        kda_chunked_kernel<DK, NVT, true><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a, pairs > 0 ? der : nullptr, a.T, 0, status);
+    else
+        kda_chunked_kernel<DK, NVT, false><<<blocks, KdaShape<NVT>::NT, 0, stream>>>(a, pairs > 0 ? der : nullptr, a.T, 0, status);
     return hipGetLastError();
 }
 
