@@ -76,6 +76,8 @@ def _lib(prec: str = "f64") -> ctypes.CDLL:
             lib.oracle_vla_forward.restype = ctypes.c_int
             lib.oracle_delta_backward.argtypes = [ctypes.c_int, L, L, L, L, L] + [dp] * 18 + [ctypes.c_int]
             lib.oracle_delta_backward.restype = ctypes.c_int
+            lib.oracle_loglinear_forward.argtypes = [ctypes.c_int, L, L, L, L, L, L, L] + [dp] * 11 + [ctypes.c_int]
+            lib.oracle_loglinear_forward.restype = ctypes.c_int
             lib.oracle_real_bytes.restype = ctypes.c_int
             _loaded[prec] = lib
         return _loaded[prec]
@@ -148,6 +150,66 @@ def delta_forward(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None
     if rc != 0:
         raise RuntimeError("oracle_delta_forward_side failed")
     return out, state_out, sd
+
+
+def loglinear_levels(last_position: int) -> int:
+    """Levels the Fenwick readout needs through absolute position
+    ``last_position``: floor(log2(t)) + 2 for t >= 1 (1 for t = 0)."""
+    return 1 if last_position < 1 else int(last_position).bit_length() + 1
+
+
+def loglinear_forward(variant, q, k, v, beta, lam, alpha=None, erase_b=None, write_w=None,
+                      state_in=None, t0=0, nthreads=0, precision="f64"):
+    """Log-linear (Fenwick-tree) readout of the delta-rule family
+    ("Technical summary: adaptive memory decay for log-linear attention",
+    "Problem definition"); the readings are stated in lam_oracle.c.
+
+    Inputs as ``delta_forward``; lam [B,T,H,nL] (the per-level weights);
+    state_in [B,H,nL,dv,dk] or None (empty levels); t0 = absolute position of
+    token 0.  Returns (out [B,T,H,dv], level states [B,H,nL,dv,dk])."""
+    var = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    q = _in(q)
+    B, T, H, dk = q.shape
+    k = _in(k, (B, T, H, dk))
+    v = _in(v)
+    dv = v.shape[3]
+    beta = _in(beta, (B, T, H))
+    lam = _in(lam)
+    nL = lam.shape[3]
+    if lam.shape[:3] != (B, T, H):
+        raise ValueError("lam shape")
+    if var == DELTANET:
+        alpha = None
+    elif var == KIMI_DELTA:
+        alpha = _in(alpha, (B, T, H, dk))
+    else:
+        alpha = _in(alpha, (B, T, H))
+    if var == GATED_DELTANET2:
+        erase_b = _in(erase_b, (B, T, H, dk))
+        write_w = _in(write_w, (B, T, H, dv))
+    else:
+        erase_b = write_w = None
+    state_in = _in(state_in, (B, H, nL, dv, dk))
+    out = np.zeros((B, T, H, dv), np.float64)
+    state_out = np.zeros((B, H, nL, dv, dk), np.float64)
+    rc = _lib(precision).oracle_loglinear_forward(
+        var, B, T, H, dk, dv, nL, int(t0), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase_b),
+        _ptr(write_w), _ptr(beta), _ptr(lam), _ptr(state_in), _ptr(out), _ptr(state_out), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_loglinear_forward failed (too few levels?)")
+    return out, state_out
+
+
+def loglinear_lambda(d, W1, W2, b):
+    """Adaptive level weights ("Technical summary: adaptive memory decay for
+    log-linear attention", "Methodology", LambdaMLPSoftplus): two linear
+    layers and a softplus, h = d W1, lambda = softplus(h W2 + b), for every
+    token, head and level.  d: [..., nL]; W1: [nL, nh]; W2: [nh, nL];
+    b: [nL].  softplus(x) = log(1 + e^x), evaluated as
+    max(x, 0) + log1p(e^-|x|)."""
+    d, W1, W2, b = (np.asarray(a, np.float64) for a in (d, W1, W2, b))
+    x = (d @ W1) @ W2 + b
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
 
 
 def route(h, s, P):

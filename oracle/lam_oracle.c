@@ -557,5 +557,146 @@ int oracle_vla_forward(long B, long T, long H, long d, const double *q,
     return failed ? -1 : 0;
 }
 
+/*
+ * Log-linear (Fenwick-tree) readout of the delta-rule family, one (b, h)
+ * chain ("Technical summary: adaptive memory decay for log-linear
+ * attention", "Problem definition": the memory is a Fenwick-tree hierarchy
+ * of O(log T) levels and each step's output is the lambda^(l)_t-weighted sum
+ * of the levels' reads).
+ *
+ * Readings (the page gives neither the partition nor how the levels evolve):
+ *   - levels follow the Fenwick partition of the prefix: for the query at
+ *     absolute position t, token t itself is level 0 and an earlier token s is
+ *     level msb(t xor s) + 1 (the lowbit segments of [0, t), level l holding
+ *     2^(l-1) tokens);
+ *   - every level's memory takes the variant's transition each step (decay,
+ *     then the delta rule's erase along e with that level's own prediction:
+ *     S <- S~ - beta (S~ e) k^T), and only level 0 receives the new write
+ *     beta z k^T; so the levels sum to exactly the single memory W of the
+ *     plain scan, and lambda = 1 on every level gives the plain scan's output;
+ *   - moving to position t >= 1, levels 0 .. ctz(t) merge into level
+ *     ctz(t) + 1 (the segment of the last 2^ctz(t) tokens), leaving levels
+ *     1 .. ctz(t) empty.
+ * Per token, in this order: merge, transition of every level, write to
+ * level 0, read y = sum_l lambda_l S_l q.
+ * Levels: nL of them, S[l] at W + l*dv*dk; t0 is the absolute position of
+ * token 0 (the levels in state_in are those after position t0 - 1).
+ */
+static void loglin_chain(int variant, long b, long h, long T, long H, long dk, long dv, long nL,
+                         long t0, const double *q, const double *k, const double *v,
+                         const double *alpha, const double *erase_b, const double *write_w,
+                         const double *beta, const double *lam, const double *state_in,
+                         double *out, double *state_out, real *W, real *kk, real *target) {
+    const size_t lsz = (size_t)dv * dk;
+    const size_t sbase = st(b, h, H, nL * dv, dk);  /* [B,H,nL,dv,dk] */
+    for (size_t i = 0; i < (size_t)nL * lsz; ++i)
+        W[i] = state_in ? (real)state_in[sbase + i] : (real)0;
+
+    for (long t = 0; t < T; ++t) {
+        const long pos = t0 + t;
+        const double *kt = k + tok(b, t, h, T, H, dk);
+        const double *qt = q + tok(b, t, h, T, H, dk);
+        const double *vt = v + tok(b, t, h, T, H, dv);
+        const double *lt = lam + tok(b, t, h, T, H, nL);
+        const real bt = (real)beta[tok(b, t, h, T, H, 1)];
+
+        /* Fenwick merge: levels 0..p into level p+1, p = ctz(pos) */
+        if (pos > 0) {
+            long p = 0;
+            while (((pos >> p) & 1) == 0) ++p;
+            real *dst = W + (size_t)(p + 1) * lsz;
+            for (long l = 0; l <= p; ++l) {
+                real *src = W + (size_t)l * lsz;
+                for (size_t i = 0; i < lsz; ++i) { dst[i] += src[i]; src[i] = 0; }
+            }
+        }
+
+        /* read key and write target */
+        for (long j = 0; j < dk; ++j) kk[j] = (real)kt[j];
+        for (long i = 0; i < dv; ++i) target[i] = (real)vt[i];
+        if (variant == ORACLE_GATED_DELTANET2) {
+            const double *eb = erase_b + tok(b, t, h, T, H, dk);
+            const double *ww = write_w + tok(b, t, h, T, H, dv);
+            for (long j = 0; j < dk; ++j) kk[j] = (real)eb[j] * kk[j];
+            for (long i = 0; i < dv; ++i) target[i] = (real)ww[i] * target[i];
+        }
+
+        /* transition of every level: decay, then erase with its own prediction */
+        for (long l = 0; l < nL; ++l) {
+            real *S = W + (size_t)l * lsz;
+            if (variant == ORACLE_GATED_DELTANET || variant == ORACLE_GATED_DELTANET2) {
+                const real a = (real)alpha[tok(b, t, h, T, H, 1)];
+                for (size_t i = 0; i < lsz; ++i) S[i] = a * S[i];
+            } else if (variant == ORACLE_KIMI_DELTA) {
+                const double *at = alpha + tok(b, t, h, T, H, dk);
+                for (long i = 0; i < dv; ++i)
+                    for (long j = 0; j < dk; ++j) S[i * dk + j] = S[i * dk + j] * (real)at[j];
+            }
+            for (long i = 0; i < dv; ++i) {
+                real pred = 0;
+                for (long j = 0; j < dk; ++j) pred += S[i * dk + j] * kk[j];
+                for (long j = 0; j < dk; ++j) S[i * dk + j] -= bt * pred * (real)kt[j];
+            }
+        }
+
+        /* the new write goes to level 0 */
+        for (long i = 0; i < dv; ++i)
+            for (long j = 0; j < dk; ++j) W[i * dk + j] += bt * target[i] * (real)kt[j];
+
+        /* lambda-weighted read of the levels */
+        double *yt = out + tok(b, t, h, T, H, dv);
+        for (long i = 0; i < dv; ++i) {
+            real acc = 0;
+            for (long l = 0; l < nL; ++l) {
+                const real *S = W + (size_t)l * lsz;
+                real r = 0;
+                for (long j = 0; j < dk; ++j) r += S[i * dk + j] * (real)qt[j];
+                acc += (real)lt[l] * r;
+            }
+            yt[i] = (double)acc;
+        }
+    }
+    if (state_out)
+        for (size_t i = 0; i < (size_t)nL * lsz; ++i) state_out[sbase + i] = (double)W[i];
+}
+
+/*
+ * oracle_loglinear_forward: the log-linear readout over a [B,T] block.
+ * Layouts as oracle_delta_forward; lam [B,T,H,nL]; state_in / state_out
+ * [B,H,nL,dv,dk] (NULL in = every level empty).  The caller must give enough
+ * levels: nL >= floor(log2(t0 + T - 1)) + 2 when t0 + T >= 2 (else -1).
+ */
+int oracle_loglinear_forward(int variant, long B, long T, long H, long dk, long dv, long nL,
+                             long t0, const double *q, const double *k, const double *v,
+                             const double *alpha, const double *erase_b,
+                             const double *write_w, const double *beta, const double *lam,
+                             const double *state_in, double *out, double *state_out,
+                             int nthreads) {
+    if (variant < ORACLE_DELTANET || variant > ORACLE_GATED_DELTANET2) return -1;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || nL <= 0 || t0 < 0) return -1;
+    if (!q || !k || !v || !beta || !lam || !out) return -1;
+    if (variant != ORACLE_DELTANET && !alpha) return -1;
+    if (variant == ORACLE_GATED_DELTANET2 && (!erase_b || !write_w)) return -1;
+    const long last = t0 + T - 1;
+    if (last >= 1) {
+        long need = 1;
+        while ((1L << (need - 1)) <= last) ++need;  /* floor(log2(last)) + 2 */
+        if (nL < need) return -1;
+    }
+    const long chains = B * H;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads()) \
+    reduction(| : failed)
+    for (long c = 0; c < chains; ++c) {
+        real *buf = (real *)malloc(sizeof(real) * (size_t)(nL * dv * dk + dk + dv));
+        if (!buf) { failed = 1; continue; }
+        loglin_chain(variant, c / H, c % H, T, H, dk, dv, nL, t0, q, k, v, alpha, erase_b, write_w,
+                     beta, lam, state_in, out, state_out, buf, buf + nL * dv * dk,
+                     buf + nL * dv * dk + dk);
+        free(buf);
+    }
+    return failed ? -1 : 0;
+}
+
 /* Size of `real` in this build (8 for the fp64 oracle, 4 for the spread check). */
 int oracle_real_bytes(void) { return (int)sizeof(real); }
