@@ -87,6 +87,12 @@ def library() -> ctypes.CDLL:
             lib.lam_forward_side.restype = ci
             lib.lam_route.argtypes = [ci, i64, i64, i64, vp, vp, vp, vp]
             lib.lam_route.restype = ci
+            lib.lam_loglinear_forward.argtypes = [ci, ci, i64, i64, i64, i64, i64, i64, i64] + [vp] * 11 + [vp]
+            lib.lam_loglinear_forward.restype = ci
+            lib.lam_loglinear_levels.argtypes = [i64]
+            lib.lam_loglinear_levels.restype = i64
+            lib.lam_loglinear_lambda.argtypes = [ci, i64, i64, i64] + [vp] * 5 + [vp]
+            lib.lam_loglinear_lambda.restype = ci
             lib.lam_backward.argtypes = [ci, ci, i64, i64, i64, i64, i64] + [vp] * 18 + [vp, sz, vp]
             lib.lam_backward.restype = ci
             lib.lam_backward_workspace_size.argtypes = [ci, ci, i64, i64, i64, i64, i64, ctypes.POINTER(sz)]
@@ -280,6 +286,87 @@ def forward(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None, stat
         raise LamError(rc, "lam_forward_side")
     _after_call(ws, "lam_forward_side")
     return out, state_out, side_out
+
+
+def loglinear_levels(last_position: int) -> int:
+    """Levels the log-linear readout needs through absolute position
+    ``last_position`` (floor(log2) + 2; 1 for positions below 1)."""
+    return int(library().lam_loglinear_levels(int(last_position)))
+
+
+def loglinear_forward(variant, q, k, v, beta, lam, alpha=None, erase_b=None, write_w=None, state_in=None,
+                      *, t0=0, out=None, state_out=None, with_state=True, stream=None):
+    """Log-linear (Fenwick-tree) readout of the delta-rule family.
+
+    Inputs as ``forward``; lam: fp32 [B,T,H,nL] level weights; state_in: fp32
+    level memories [B,H,nL,dv,dk] or None; t0: absolute position of token 0.
+    Returns (out [B,T,H,dv], level states [B,H,nL,dv,dk] or None).
+    """
+    import torch
+
+    var = VARIANTS[variant]
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    nL = lam.shape[3]
+    dt, dev = q.dtype, q.device
+    _check(q, "q", (B, T, H, dk), dt, dev)
+    _check(k, "k", (B, T, H, dk), dt, dev)
+    _check(v, "v", (B, T, H, dv), dt, dev)
+    _check(beta, "beta", (B, T, H), dt, dev)
+    _check(lam, "lam", (B, T, H, nL), torch.float32, dev)
+    if var == VARIANTS["kda"]:
+        _check(alpha, "alpha", (B, T, H, dk), dt, dev)
+    elif var != VARIANTS["deltanet"]:
+        _check(alpha, "alpha", (B, T, H), dt, dev)
+    else:
+        alpha = None
+    if var == VARIANTS["gdn2"]:
+        _check(erase_b, "erase_b", (B, T, H, dk), dt, dev)
+        _check(write_w, "write_w", (B, T, H, dv), dt, dev)
+    else:
+        erase_b = write_w = None
+    _check(state_in, "state_in", (B, H, nL, dv, dk), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check(out, "out", (B, T, H, dv), dt, dev)
+    if with_state and state_out is None:
+        state_out = torch.empty((B, H, nL, dv, dk), dtype=torch.float32, device=dev)
+    _check(state_out, "state_out", (B, H, nL, dv, dk), torch.float32, dev)
+    rc = library().lam_loglinear_forward(var, _dtype_code(q), B, T, H, dk, dv, nL, int(t0), _ptr(q), _ptr(k),
+                                         _ptr(v), _ptr(alpha), _ptr(erase_b), _ptr(write_w), _ptr(beta),
+                                         _ptr(lam), _ptr(state_in), _ptr(out), _ptr(state_out),
+                                         _stream(stream))
+    if rc != 0:
+        raise LamError(rc, "lam_loglinear_forward")
+    _after_call(None, "lam_loglinear_forward")
+    return out, state_out
+
+
+def loglinear_lambda(d, W1, W2, b, *, out=None, stream=None):
+    """Adaptive level weights, softplus((d W1) W2 + b) per row.
+
+    d: [..., nL] (float32 or bfloat16); W1 [nL, nh], W2 [nh, nL], b [nL]
+    fp32.  Returns fp32 [..., nL]."""
+    import torch
+
+    nL = d.shape[-1]
+    nh = W1.shape[1]
+    dev = d.device
+    if not d.is_contiguous():
+        raise ValueError("d: must be contiguous")
+    _check(W1, "W1", (nL, nh), torch.float32, dev)
+    _check(W2, "W2", (nh, nL), torch.float32, dev)
+    _check(b, "b", (nL,), torch.float32, dev)
+    if out is None:
+        out = torch.empty(d.shape, dtype=torch.float32, device=dev)
+    _check(out, "out", tuple(d.shape), torch.float32, dev)
+    M = d.numel() // nL
+    rc = library().lam_loglinear_lambda(_dtype_code(d), M, nL, nh, _ptr(d), _ptr(W1), _ptr(W2), _ptr(b),
+                                        _ptr(out), _stream(stream))
+    if rc != 0:
+        raise LamError(rc, "lam_loglinear_lambda")
+    _after_call(None, "lam_loglinear_lambda")
+    return out
 
 
 def route(h, s, P, *, stream=None):

@@ -255,6 +255,90 @@ lam_status lam_forward_side(int variant, int dtype, int64_t B, int64_t T, int64_
     return from_hip(lam::launch_delta_recurrent(a, stream));
 }
 
+int64_t lam_loglinear_levels(int64_t last_position) {
+    if (last_position < 1) return 1;
+    int64_t n = 1;
+    while (n < 63 && (INT64_C(1) << (n - 1)) <= last_position) ++n;  // floor(log2) + 2
+    return n;
+}
+
+lam_status lam_loglinear_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                                 int64_t dv, int64_t nL, int64_t t0, const void *q, const void *k,
+                                 const void *v, const void *alpha, const void *erase_b,
+                                 const void *write_w, const void *beta, const float *lam,
+                                 const float *state_in, void *out, float *state_out,
+                                 hipStream_t stream) {
+    lam_status st = check_delta_shape(variant, dtype, B, T, H, dk, dv, LAM_ALGO_RECURRENT);
+    if (st != LAM_OK) return st;
+    if (nL < 1 || t0 < 0) return LAM_ERR_INVALID_ARG;
+    if (nL > lam::kLogLinMaxLevels) return LAM_ERR_UNSUPPORTED;
+    if (t0 > (INT64_C(1) << (lam::kLogLinMaxLevels - 1)) - 1 - T) return LAM_ERR_UNSUPPORTED;  // positions
+    const int64_t last = t0 + T - 1;
+    if (T > 0 && nL < lam_loglinear_levels(last)) return LAM_ERR_INVALID_ARG;  // too few levels
+    lam::DeltaArgs a = shape_args(variant, dtype, B, T, H, dk, dv);
+    if (!lam::loglin_supported(a, static_cast<int>(nL))) return LAM_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return LAM_OK;
+    int64_t nk, nv, ns, nst, nlv, nlam;
+    elems(B, T, H, dk, nk);
+    elems(B, T, H, dv, nv);
+    elems(B, T, H, 1, ns);
+    elems(B, 1, H, dk * dv, nst);
+    if (!mul_ok(nst, nL, nlv) || !mul_ok(ns, nL, nlam)) return LAM_ERR_INVALID_ARG;
+    if (T > 0) {
+        if (!q || !k || !v || !beta || !lam || !out) return LAM_ERR_INVALID_ARG;
+        if (variant != LAM_DELTANET && !alpha) return LAM_ERR_INVALID_ARG;
+        if (variant == LAM_GATED_DELTANET2 && (!erase_b || !write_w)) return LAM_ERR_INVALID_ARG;
+    }
+    const int64_t es = dtype == LAM_BF16 ? 2 : 4;
+    const bool gated = variant != LAM_DELTANET, g2 = variant == LAM_GATED_DELTANET2;
+    const void *ins[] = {q, k, v, gated ? alpha : nullptr, g2 ? erase_b : nullptr, g2 ? write_w : nullptr,
+                         beta, lam, state_in};
+    const int64_t inb[] = {nk * es, nk * es, nv * es, (variant == LAM_KIMI_DELTA ? nk : ns) * es, nk * es,
+                           nv * es, ns * es, nlam * 4, nlv * 4};
+    for (int i = 0; i < 9; ++i) {
+        if (overlaps(out, nv * es, ins[i], inb[i])) return LAM_ERR_INVALID_ARG;
+        if (i < 8 && overlaps(state_out, nlv * 4, ins[i], inb[i])) return LAM_ERR_INVALID_ARG;
+    }
+    if (overlaps(out, nv * es, state_out, nlv * 4)) return LAM_ERR_INVALID_ARG;
+    if (state_out && state_in && state_out != state_in && overlaps(state_out, nlv * 4, state_in, nlv * 4))
+        return LAM_ERR_INVALID_ARG;
+    if (T == 0 && !state_out) return LAM_OK;
+    lam::LogLinArgs g{};
+    g.f = a;
+    g.f.q = q;
+    g.f.k = k;
+    g.f.v = v;
+    g.f.alpha = gated ? alpha : nullptr;
+    g.f.erase_b = g2 ? erase_b : nullptr;
+    g.f.write_w = g2 ? write_w : nullptr;
+    g.f.beta = beta;
+    g.f.state_in = state_in;
+    g.f.out = out;
+    g.f.state_out = state_out;
+    g.nL = static_cast<int>(nL);
+    g.t0 = t0;
+    g.lam = lam;
+    return from_hip(lam::launch_loglin(g, stream));
+}
+
+lam_status lam_loglinear_lambda(int dtype, int64_t M, int64_t nL, int64_t nh, const void *d,
+                                const float *W1, const float *W2, const float *b, float *lam,
+                                hipStream_t stream) {
+    if (dtype != LAM_F32 && dtype != LAM_BF16) return LAM_ERR_INVALID_ARG;
+    if (M < 0 || nL < 1 || nh < 1) return LAM_ERR_INVALID_ARG;
+    if (nL > lam::kLogLinMaxLevels || nh > lam::kLogLinMaxHidden) return LAM_ERR_UNSUPPORTED;
+    int64_t n;
+    if (!mul_ok(M, nL, n) || (M + 255) / 256 > INT_MAX) return LAM_ERR_INVALID_ARG;
+    if (M == 0) return LAM_OK;
+    if (!d || !W1 || !W2 || !b || !lam) return LAM_ERR_INVALID_ARG;
+    const int64_t es = dtype == LAM_BF16 ? 2 : 4;
+    if (overlaps(lam, n * 4, d, n * es) || overlaps(lam, n * 4, W1, nL * nh * 4) ||
+        overlaps(lam, n * 4, W2, nL * nh * 4) || overlaps(lam, n * 4, b, nL * 4))
+        return LAM_ERR_INVALID_ARG;
+    return from_hip(lam::launch_loglin_lambda(dtype, M, static_cast<int>(nL), static_cast<int>(nh), d, W1, W2,
+                                              b, lam, stream));
+}
+
 lam_status lam_route(int dtype, int64_t M, int64_t D, int64_t N, const void *s, const void *P, void *h,
                      hipStream_t stream) {
     if (dtype != LAM_F32 && dtype != LAM_BF16) return LAM_ERR_INVALID_ARG;

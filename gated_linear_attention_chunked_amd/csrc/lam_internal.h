@@ -82,6 +82,22 @@ struct DeltaBwdArgs {
 bool delta_backward_workspace(const DeltaArgs &a, size_t *bytes);
 hipError_t launch_delta_backward(const DeltaBwdArgs &g, hipStream_t stream);
 
+// Log-linear (Fenwick-tree) readout: f as the plain scan (state_in /
+// state_out are level states [B,H,nL,dv,dk]), nL levels, t0 = absolute
+// position of token 0, lam = level weights [B,T,H,nL] fp32.
+constexpr int kLogLinMaxLevels = 24;   // positions below 2^23
+constexpr int kLogLinMaxHidden = 64;   // hidden width of the level-weight MLP
+struct LogLinArgs {
+    DeltaArgs f;
+    int nL;
+    int64_t t0;
+    const float *lam;
+};
+bool loglin_supported(const DeltaArgs &a, int nL);
+hipError_t launch_loglin(const LogLinArgs &g, hipStream_t stream);
+hipError_t launch_loglin_lambda(int dtype, int64_t M, int nL, int nh, const void *d, const float *W1,
+                                const float *W2, const float *b, float *lam, hipStream_t stream);
+
 // Routing epilogue h += s P^T (s [M,N], P [D,N], h [M,D], one dtype).
 bool route_supported(int64_t D, int64_t N);
 hipError_t launch_route(int dtype, int64_t M, int64_t D, int64_t N, const void *s, const void *P, void *h,

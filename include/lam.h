@@ -202,6 +202,60 @@ lam_status lam_route(int dtype, int64_t M, int64_t D, int64_t N, const void *s, 
                      hipStream_t stream);
 
 /*
+ * Log-linear (Fenwick-tree) readout of the delta-rule family ("Technical
+ * summary: adaptive memory decay for log-linear attention", "Problem
+ * definition": a Fenwick-tree hierarchy of O(log T) memory levels, each
+ * step's output the lambda^(l)_t-weighted sum of the levels' reads;
+ * "Complexity preservation": O(log T) decoding memory).  Levels, for the
+ * query at absolute position t: token t is level 0, an earlier token s is
+ * level msb(t xor s) + 1.  Every level takes the variant's transition each
+ * step (decay, then the delta rule's erase along e with that level's own
+ * prediction), level 0 alone receives the write beta z k^T, and at position
+ * t >= 1 levels 0 .. ctz(t) merge into level ctz(t) + 1; the levels sum to
+ * the plain scan's memory (lambda = 1 reproduces lam_forward).  Output
+ * y_t = sum_l lambda_t[l] S_l q_t.  Computed token by token in fp32.
+ *   variant .. beta   as lam_forward (one storage dtype)
+ *   nL           levels, 1 .. 24, at least lam_loglinear_levels(t0 + T - 1)
+ *                (LAM_ERR_INVALID_ARG if fewer)
+ *   t0           absolute position of token 0 (>= 0; t0 + T < 2^23)
+ *   lam          [B,T,H,nL] fp32 level weights (lam_loglinear_lambda makes
+ *                them), required when T > 0
+ *   state_in     [B,H,nL,dv,dk] fp32 level memories after position t0 - 1,
+ *                or NULL (all empty)
+ *   out          [B,T,H,dv] in dtype, required when T > 0
+ *   state_out    [B,H,nL,dv,dk] fp32 or NULL; may equal state_in
+ * A decode step is a call with T = 1 at t0 = the token's position, the
+ * levels updated in place.  No workspace; errors as lam_forward.
+ */
+lam_status lam_loglinear_forward(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
+                                 int64_t dv, int64_t nL, int64_t t0, const void *q, const void *k,
+                                 const void *v, const void *alpha, const void *erase_b,
+                                 const void *write_w, const void *beta, const float *lam,
+                                 const float *state_in, void *out, float *state_out,
+                                 hipStream_t stream);
+
+/* Levels the readout needs through absolute position last_position:
+ * floor(log2(last_position)) + 2, or 1 for last_position < 1. */
+int64_t lam_loglinear_levels(int64_t last_position);
+
+/*
+ * Adaptive level weights (same page, "Methodology", LambdaMLPSoftplus): two
+ * linear layers and a softplus per row, lambda = softplus((d W1) W2 + b), for
+ * every (token, head) row; the page initialises W2 = 0 and b = 0.54, so that
+ * every weight starts at softplus(0.54), about 1.
+ *   dtype        lam_dtype of d
+ *   M            rows (B * T * H), >= 0
+ *   nL           levels (1 .. 24); nh hidden width (1 .. 64; the page uses
+ *                twice the level count)
+ *   d            [M, nL] in dtype; W1 [nL, nh], W2 [nh, nL], b [nL] fp32
+ *   lam          [M, nL] fp32, written (may not overlap the inputs)
+ * softplus(x) is evaluated as max(x, 0) + log1p(exp(-|x|)).
+ */
+lam_status lam_loglinear_lambda(int dtype, int64_t M, int64_t nL, int64_t nh, const void *d,
+                                const float *W1, const float *W2, const float *b, float *lam,
+                                hipStream_t stream);
+
+/*
  * VLA forward scan over a [B,T] block (dk = dv = d, d in {32, 64, 96, 128}).
  *   q, k, v, p   [B,T,H,d] raw queries, keys, values and penalty directions
  *   A_in, S_in   [B,H,d,d] fp32 or NULL (A = I, S = 0)

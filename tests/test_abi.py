@@ -270,3 +270,29 @@ def test_route_rejects_bad_arguments(lib):
     assert lib.lam_route(1, 64, 128, 256, S + 8, P, Hh, None) == INVALID  # not 16-byte aligned
     assert lib.lam_route(1, 64, 128, 256, S, P, S + 64, None) == INVALID  # h inside s
     assert lib.lam_route(1, 0, 128, 256, None, None, None, None) == OK    # no tokens
+
+
+def test_loglinear_rejects_bad_arguments(lib):
+    lib.lam_loglinear_levels.restype = ctypes.c_int64
+    lib.lam_loglinear_levels.argtypes = [ctypes.c_int64]
+    assert [lib.lam_loglinear_levels(t) for t in (0, 1, 2, 3, 4, 4095, 4096)] == [1, 2, 3, 3, 4, 13, 14]
+
+    def ll(variant=1, dtype=1, B=2, T=8, H=2, dk=64, dv=64, nL=4, t0=0, lam=FAKE + 0x80000000, out=FAKE + 0x70000000,
+           sin=None, sout=None, alpha=FAKE + 0x30000000):
+        return lib.lam_loglinear_forward(variant, dtype, B, T, H, dk, dv, nL, t0, FAKE, FAKE + 0x10000000,
+                                         FAKE + 0x20000000, alpha, None, None, FAKE + 0x60000000, lam, sin, out,
+                                         sout, None)
+    assert ll(nL=3) == INVALID            # positions 0..7 need 4 levels
+    assert ll(t0=8, nL=4) == INVALID      # positions 8..15 need 5
+    assert ll(nL=25) == UNSUPPORTED       # more levels than the kernel holds
+    assert ll(t0=(1 << 23)) == UNSUPPORTED
+    assert ll(t0=-1) == INVALID
+    assert ll(lam=None) == INVALID
+    assert ll(alpha=None) == INVALID
+    assert ll(out=FAKE + 8) == INVALID    # out inside q
+    assert ll(sout=FAKE + 0x80000000) == INVALID  # level states inside lam
+    assert ll(B=0) == OK
+    assert lib.lam_loglinear_lambda(1, 10, 25, 8, FAKE, FAKE, FAKE, FAKE, FAKE + 0x10000000, None) == UNSUPPORTED
+    assert lib.lam_loglinear_lambda(1, 10, 4, 65, FAKE, FAKE, FAKE, FAKE, FAKE + 0x10000000, None) == UNSUPPORTED
+    assert lib.lam_loglinear_lambda(1, 10, 4, 8, FAKE, FAKE, FAKE, FAKE, FAKE + 8, None) == INVALID  # over d
+    assert lib.lam_loglinear_lambda(1, 0, 4, 8, None, None, None, None, None, None) == OK
