@@ -12,6 +12,13 @@ Printed: one JSON line with tokens/s (tokens = B*T), the roofline object of
 the scan kernel (algorithmic bytes per launch / mean launch time from HIP
 events on the launch stream, against 8 TB/s HBM) and the fp64 oracle timed
 on host cores on a bounded sample of the same workload.
+
+Other lines (``--workload NAME``): the other forward workloads, the decode
+step, and the paths beside the forward scan on the same B8 T4096 H8 d128
+Gated DeltaNet shapes -- its backward pass, the forward with the per-token
+residual side output, the routing product into a 1024-wide stream, the
+log-linear readout (13 levels) and its level-weight MLP.  Each reports its
+own roofline and its own oracle baseline.
 """
 from __future__ import annotations
 
@@ -61,6 +68,73 @@ def algorithmic_flops(w) -> int:
     return n_th * 7 * w.dk * w.dv
 
 
+# Paths beside the forward scan, benchmarked on a forward workload's shapes:
+# name -> (kind, forward workload, extra parameters)
+JOBS = {
+    "gdn_bwd_bf16_B8_T4096_H8_d128": ("backward", "gdn_bf16_B8_T4096_H8_d128", {}),
+    "gdn_side_bf16_B8_T4096_H8_d128": ("side", "gdn_bf16_B8_T4096_H8_d128", {}),
+    "route_bf16_B8_T4096_N1024_D1024": ("route", "gdn_bf16_B8_T4096_H8_d128", {"D": 1024}),
+    "gdn_loglinear_bf16_B8_T4096_H8_d128": ("loglinear", "gdn_bf16_B8_T4096_H8_d128", {}),
+    "loglinear_lambda_bf16_B8_T4096_H8_L13": ("lambda", "gdn_bf16_B8_T4096_H8_d128", {"nh": 26}),
+}
+
+
+def loglinear_levels(T: int) -> int:
+    """Fenwick levels through position T - 1: floor(log2(T - 1)) + 2."""
+    return 1 if T - 1 < 1 else (T - 1).bit_length() + 1
+
+
+def loglinear_occupancy(T: int) -> int:
+    """Sum over positions t < T of the levels the readout touches at t: the
+    levels holding earlier tokens (one per set bit of t) plus level 0."""
+    return sum(bin(t).count("1") + 1 for t in range(T))
+
+
+def job_counts(kind: str, w, extra=None):
+    """(algorithmic bytes, algorithmic flops) of one call of a job.
+
+    backward: reads the forward's inputs and dout in the storage dtype,
+      writes every gradient in fp32 (dq, dk, dv, dbeta, dalpha, Gated
+      DeltaNet-2's derase_b and dwrite_w, and dstate_in); flops 14 dk dv per
+      token-head (each of the forward's 7 dk dv matched by its adjoint twice:
+      the reverse sweep's products, recomputation not counted).
+    side: the forward's, plus the residual written once in the storage dtype.
+    route: s, P and h read once, h written once; flops 2 M N D.
+    loglinear: the forward's inputs and out, the level weights (fp32, nL per
+      token-head) and nL final level memories; flops 7 dk dv per occupied
+      level and token-head.
+    lambda: d read in the storage dtype, lambda written in fp32 (weights
+      negligible); flops 4 nL nh per row (two products).
+    """
+    extra = extra or {}
+    es = 2 if w.dtype == "bf16" else 4
+    n_th = w.B * w.T * w.H
+    state = w.B * w.H * w.dv * w.dk * 4
+    if kind == "backward":
+        nin = (2 * w.dk + 2 * w.dv + 1) * es                 # q, k, v, dout, beta
+        nout = (2 * w.dk + w.dv + 1) * 4                     # dq, dk, dv, dbeta
+        if w.variant in ("gdn", "gdn2"):
+            nin, nout = nin + es, nout + 4
+        if w.variant == "kda":
+            nin, nout = nin + w.dk * es, nout + w.dk * 4
+        if w.variant == "gdn2":
+            nin, nout = nin + (w.dk + w.dv) * es, nout + (w.dk + w.dv) * 4
+        return n_th * (nin + nout) + state, n_th * 14 * w.dk * w.dv
+    if kind == "side":
+        return algorithmic_bytes(w) + n_th * w.dv * es, algorithmic_flops(w)
+    if kind == "route":
+        M, N, D = w.B * w.T, w.H * w.dv, extra["D"]
+        return (M * N + D * N + 2 * M * D) * es, 2 * M * N * D
+    if kind == "loglinear":
+        nL = loglinear_levels(w.T)
+        nbytes = algorithmic_bytes(w) - state + n_th * nL * 4 + nL * state
+        return nbytes, w.B * w.H * loglinear_occupancy(w.T) * 7 * w.dk * w.dv
+    if kind == "lambda":
+        nL, nh = loglinear_levels(w.T), extra["nh"]
+        return n_th * nL * (es + 4), n_th * 4 * nL * nh
+    raise ValueError(kind)
+
+
 KERNEL_SOURCES = {  # schedule -> kernel source per variant family
     ("chunked", "delta"): "delta_chunked.hip",
     ("chunked", "kda"): "kda_chunked.hip",
@@ -68,6 +142,11 @@ KERNEL_SOURCES = {  # schedule -> kernel source per variant family
     ("recurrent", "delta"): "delta_recurrent.hip",
     ("recurrent", "kda"): "delta_recurrent.hip",
     ("recurrent", "vla"): "vla_recurrent.hip",
+    ("step", "delta"): "delta_step.hip",
+    ("backward", "delta"): "delta_backward.hip",
+    ("route", "delta"): "route.hip",
+    ("loglinear", "delta"): "loglin_recurrent.hip",
+    ("lambda", "delta"): "loglin_recurrent.hip",
 }
 SHARED_HEADERS = ("chunk_common.h", "device_common.h", "lam_internal.h")
 
@@ -77,7 +156,7 @@ def kernel_source_hash(ran: str, variant: str):
     import hashlib
 
     fam = variant if variant in ("kda", "vla") else "delta"
-    name = KERNEL_SOURCES[(ran, fam)]
+    name = KERNEL_SOURCES.get((ran, fam)) or KERNEL_SOURCES[(ran, "delta")]
     csrc = os.path.join(ROOT, "gated_linear_attention_chunked_amd", "csrc")
     h = hashlib.sha256()
     for f in (name,) + SHARED_HEADERS:
@@ -85,14 +164,14 @@ def kernel_source_hash(ran: str, variant: str):
     return name, h.hexdigest()
 
 
-def measured_traffic(w, ran: str):
+def measured_traffic(w, ran: str, name=None):
     """HBM bytes per launch from the committed rocprofv3 counter record
     (profiles/traffic.json), or None when there is no record for this
     workload and schedule, or it was taken on a different revision of the
     kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        rec = json.load(open(path))["workloads"][w.name]
+        rec = json.load(open(path))["workloads"][name or w.name]
         name, sha = kernel_source_hash(ran, w.variant)
     except (OSError, KeyError, ValueError):
         return None
@@ -149,6 +228,63 @@ def cpu_baseline(w, x, batch_rows: int, min_seconds: float):
                       f"in {dt:.1f} s wall"}
 
 
+def cpu_baseline_job(kind, w, x, extra, batch_rows: int, min_seconds: float, tokens: int = None):
+    """The oracle of a job on the first `batch_rows` batch rows (all heads;
+    the first `tokens` tokens when given), repeated for at least
+    `min_seconds`; tokens/s over all repetitions."""
+    import numpy as np
+
+    import oracle
+
+    T = tokens or w.T
+    sl = {k: v[:batch_rows, :T] for k, v in x.items()}
+    chains = batch_rows * w.H
+    th = cpu_threads(chains)
+    r = np.random.default_rng(w.seed + 17)
+    if kind == "backward":
+        dout = r.standard_normal(sl["v"].shape)
+        run = lambda: oracle.delta_backward(w.variant, sl["q"], sl["k"], sl["v"], sl["beta"], dout,
+                                            alpha=sl.get("alpha"), erase_b=sl.get("erase_b"),
+                                            write_w=sl.get("write_w"), nthreads=th)
+        what = "fp64 token-by-token adjoint oracle"
+    elif kind == "side":
+        run = lambda: oracle.delta_forward(w.variant, sl["q"], sl["k"], sl["v"], sl["beta"], alpha=sl.get("alpha"),
+                                           erase_b=sl.get("erase_b"), write_w=sl.get("write_w"), nthreads=th,
+                                           side="residual")
+        what = "fp64 token-by-token oracle with the residual side output"
+    elif kind == "loglinear":
+        nL = loglinear_levels(w.T)
+        lamw = r.uniform(0.5, 1.5, sl["beta"].shape + (nL,))
+        run = lambda: oracle.loglinear_forward(w.variant, sl["q"], sl["k"], sl["v"], sl["beta"], lamw,
+                                               alpha=sl.get("alpha"), erase_b=sl.get("erase_b"),
+                                               write_w=sl.get("write_w"), nthreads=th)
+        what = f"fp64 token-by-token log-linear oracle ({nL} levels)"
+    elif kind == "lambda":
+        nL, nh = loglinear_levels(w.T), extra["nh"]
+        d = r.standard_normal(sl["beta"].shape + (nL,))
+        W1, W2, b = r.standard_normal((nL, nh)), r.standard_normal((nh, nL)), r.standard_normal(nL)
+        run = lambda: oracle.loglinear_lambda(d, W1, W2, b)
+        what, th = "fp64 level-weight MLP (numpy)", 1
+    elif kind == "route":
+        D = extra["D"]
+        hh = r.standard_normal((batch_rows, T, D))
+        P = r.standard_normal((D, w.H * w.dv))
+        run = lambda: oracle.route(hh, sl["v"], P)
+        what, th = "fp64 routing product (numpy matmul)", os.cpu_count()
+    else:
+        raise ValueError(kind)
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        run()
+        dt += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * batch_rows * T / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "sample": f"{what} on batch rows 0..{batch_rows - 1} of {w.B}, tokens 0..{T - 1} of {w.T} "
+                      f"(all {w.H} heads), {reps} pass{'es' if reps > 1 else ''} in {dt:.1f} s wall"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,17 +326,49 @@ def main():
 
     name = args.workload or I.METRIC_WORKLOAD
     decode = name in I.DECODE_WORKLOADS
-    w = I.DECODE_WORKLOADS[name] if decode else I.WORKLOADS[name]
+    job = JOBS.get(name)
+    if job is None and not decode and name not in I.WORKLOADS:
+        print(f"bench.py: unknown workload {name}; known: "
+              f"{sorted(I.WORKLOADS) + sorted(I.DECODE_WORKLOADS) + sorted(JOBS)}", file=sys.stderr)
+        sys.exit(2)
+    kind, extra = (job[0], job[2]) if job else ("decode" if decode else "forward", {})
+    w = I.DECODE_WORKLOADS[name] if decode else I.WORKLOADS[job[1] if job else name]
     x = I.make_inputs(w)
     dev = torch.device("cuda:0")
     copies = [I.to_device(x, w.dtype, dev) for _ in range(max(1, args.copies))]
+    jr = np.random.default_rng(w.seed + 29)   # the jobs' extra seeded inputs
+    tdt = copies[0]["q"].dtype
     if decode:  # one token per stream: [N, 1, H, d] -> [N, H, d]
         copies = [{n: t[:, 0].contiguous() for n, t in g.items()} for g in copies]
         s0 = np.random.default_rng(w.seed).standard_normal((w.B, w.H, w.dv, w.dk)) * 0.1
         x["state_in"] = s0.astype(np.float32).astype(np.float64)
     outs = []
     for g in copies:
-        if decode:
+        if kind == "backward":
+            g["dout"] = torch.from_numpy(jr.standard_normal((w.B, w.T, w.H, w.dv)).astype(np.float32)).to(dev).to(tdt)
+            outs.append(None)
+        elif kind == "side":
+            outs.append((torch.empty((w.B, w.T, w.H, w.dv), dtype=tdt, device=dev),
+                         torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev),
+                         torch.empty((w.B, w.T, w.H, w.dv), dtype=tdt, device=dev)))
+        elif kind == "route":
+            D, N = extra["D"], w.H * w.dv
+            g["h"] = torch.from_numpy(jr.standard_normal((w.B, w.T, D)).astype(np.float32)).to(dev).to(tdt)
+            g["P"] = torch.from_numpy((jr.standard_normal((D, N)) / np.sqrt(N)).astype(np.float32)).to(dev).to(tdt)
+            outs.append(None)
+        elif kind == "loglinear":
+            nL = loglinear_levels(w.T)
+            g["lam"] = torch.from_numpy(jr.uniform(0.5, 1.5, (w.B, w.T, w.H, nL)).astype(np.float32)).to(dev)
+            outs.append((torch.empty((w.B, w.T, w.H, w.dv), dtype=tdt, device=dev),
+                         torch.empty((w.B, w.H, nL, w.dv, w.dk), dtype=torch.float32, device=dev)))
+        elif kind == "lambda":
+            nL, nh = loglinear_levels(w.T), extra["nh"]
+            g["d"] = torch.from_numpy(jr.standard_normal((w.B, w.T, w.H, nL)).astype(np.float32)).to(dev).to(tdt)
+            g["W1"] = torch.from_numpy((jr.standard_normal((nL, nh)) * 0.3).astype(np.float32)).to(dev)
+            g["W2"] = torch.from_numpy((jr.standard_normal((nh, nL)) * 0.3).astype(np.float32)).to(dev)
+            g["b"] = torch.full((nL,), 0.54, dtype=torch.float32, device=dev)
+            outs.append(torch.empty((w.B, w.T, w.H, nL), dtype=torch.float32, device=dev))
+        elif decode:
             outs.append((torch.empty((w.B, w.H, w.dv), dtype=g["q"].dtype, device=dev),
                          torch.from_numpy(x["state_in"].astype(np.float32)).to(dev)))
         elif w.variant == "vla":
@@ -213,7 +381,9 @@ def main():
     stream = torch.cuda.current_stream()
     # one caller-owned workspace for every step: the steps run in order on
     # one stream, so each may reuse it
-    if decode:
+    if kind == "backward":
+        nws = lam.backward_workspace_size(w.variant, w.dtype, w.B, w.T, w.H, w.dk, w.dv)
+    elif decode or kind in ("route", "loglinear", "lambda"):
         nws = 0
     elif w.variant == "vla":
         nws = lam.vla_workspace_size(w.dtype, w.B, w.T, w.H, w.dk, algo=args.algo)
@@ -223,7 +393,21 @@ def main():
 
     def step(i):
         g, o = copies[i % len(copies)], outs[i % len(outs)]
-        if decode:
+        if kind == "backward":
+            lam.backward(w.variant, g["q"], g["k"], g["v"], g["beta"], g["dout"], alpha=g.get("alpha"),
+                         erase_b=g.get("erase_b"), write_w=g.get("write_w"), workspace=wsp)
+        elif kind == "side":
+            lam.forward(w.variant, g["q"], g["k"], g["v"], g["beta"], alpha=g.get("alpha"), erase_b=g.get("erase_b"),
+                        write_w=g.get("write_w"), algo=args.algo, out=o[0], state_out=o[1], workspace=wsp,
+                        side="residual", side_out=o[2])
+        elif kind == "route":
+            lam.route(g["h"], g["v"], g["P"])
+        elif kind == "loglinear":
+            lam.loglinear_forward(w.variant, g["q"], g["k"], g["v"], g["beta"], g["lam"], alpha=g.get("alpha"),
+                                  erase_b=g.get("erase_b"), write_w=g.get("write_w"), out=o[0], state_out=o[1])
+        elif kind == "lambda":
+            lam.loglinear_lambda(g["d"], g["W1"], g["W2"], g["b"], out=o)
+        elif decode:
             lam.step(w.variant, g["q"], g["k"], g["v"], g["beta"], alpha=g.get("alpha"),
                      erase_b=g.get("erase_b"), write_w=g.get("write_w"), state=o[1], out=o[0])
         elif w.variant == "vla":
@@ -275,7 +459,9 @@ def main():
 
     tokens = w.B * w.T
     value = tokens * args.steps / wall
-    if decode:
+    if kind in ("backward", "route", "loglinear", "lambda"):
+        ran = kind
+    elif decode:
         ran = "step"
     elif w.variant == "vla":
         # the VLA entry point runs the chunked schedule for any T > 0 unless told otherwise
@@ -286,15 +472,18 @@ def main():
     # fp32; the delta-rule chunked schedule on bf16 storage feeds bf16
     # operands to the matrix cores (fp32 accumulate, fp32 state); the VLA
     # chunked schedule uses fp32 matrix-core products for every dtype
-    arith_dtype = "bf16" if (ran == "chunked" and w.dtype == "bf16" and w.variant != "vla") else "f32"
+    arith_dtype = "bf16" if (ran in ("chunked", "route") and w.dtype == "bf16" and w.variant != "vla") else "f32"
     mean_launch_s = mean_launch_ms / 1e3
-    abytes = algorithmic_bytes(w, decode)
-    aflops = algorithmic_flops(w)
+    if job:
+        abytes, aflops = job_counts(kind, w, extra)
+    else:
+        abytes = algorithmic_bytes(w, decode)
+        aflops = algorithmic_flops(w)
     achieved_gbs = abytes / mean_launch_s / 1e9
     # the binding roofline: HBM bytes, or the algorithmic flops on the unit
     # the schedule computes them with (matrix cores for the chunked schedules,
     # the fp32 vector ALU for the recurrent ones), whichever takes longer
-    if ran == "chunked":
+    if ran in ("chunked", "route"):
         cpeak, cbound = (MFMA_BF16_PEAK_TFS if arith_dtype == "bf16" else FP32_PEAK_TFS), "mfma"
     elif ran == "step":
         cpeak, cbound = FP32_PEAK_TFS, "alu"
@@ -307,7 +496,7 @@ def main():
     else:
         roofline = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved_gbs / HBM_PEAK_GBS}
-    roofline.update({"traffic": measured_traffic(w, ran),
+    roofline.update({"traffic": measured_traffic(w, ran, name),
                 "algorithmic_bytes_per_launch": abytes,
                 "mean_launch_us": mean_launch_s * 1e6,
                 "single_call_median_us": float(np.median(launch_ms)) * 1e3,
@@ -337,16 +526,27 @@ def main():
         del src, dst
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and job:
+        rows = min(w.B, args.cpu_rows or 1)
+        cpu = cpu_baseline_job(kind, w, x, extra, rows, args.cpu_seconds)
+    elif not args.no_cpu_baseline:
         rows = min(w.B, args.cpu_rows or w.B)
         cpu = cpu_baseline(w, x, rows, args.cpu_seconds)
         if decode:
             cpu["sample"] = cpu["sample"].replace("tokens)", "tokens, one decode step each from the same state)")
 
+    job_metric = {
+        "backward": f"{w.variant} backward tokens/s (all gradients), {name}",
+        "side": f"{w.variant} fwd tokens/s with the per-token residual side output, {name}",
+        "route": f"routing product h += s P^T tokens/s, {name}",
+        "loglinear": f"{w.variant} log-linear readout tokens/s, {name}",
+        "lambda": f"log-linear level-weight MLP tokens/s, {name}",
+    }
     line = {
         "metric": "gated delta-rule fwd tokens/s, B8 T4096 H8 d128; % of HBM/MFMA roofline"
-        if name == I.METRIC_WORKLOAD else (f"{w.variant} decode tokens/s (one token per stream per call), {name}"
-                                           if decode else f"{w.variant} fwd tokens/s, {name}"),
+        if name == I.METRIC_WORKLOAD else (job_metric[kind] if job else
+                                           (f"{w.variant} decode tokens/s (one token per stream per call), {name}"
+                                            if decode else f"{w.variant} fwd tokens/s, {name}")),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -359,9 +559,10 @@ def main():
         "vs_baseline": None,
         "dtype": arith_dtype,
         "data": "synthetic (seeded Gaussian activations, no dataset)",
-        "config": {"workload": name, "variant": w.variant, "B": w.B, "T": w.T, "H": w.H,
-                   "dk": w.dk, "dv": w.dv, "state": "fp32", "algo": ran, "storage": w.dtype,
-                   "parallelism": "single GPU"},
+        "config": dict({"workload": name, "variant": w.variant, "B": w.B, "T": w.T, "H": w.H,
+                        "dk": w.dk, "dv": w.dv, "state": "fp32", "algo": ran, "storage": w.dtype,
+                        "parallelism": "single GPU"}, **extra,
+                       **({"levels": loglinear_levels(w.T)} if kind in ("loglinear", "lambda") else {})),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -513,20 +513,6 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
 #pragma unroll
                 for (int i = 0; i < 4; ++i) s.uh[vt][i][lane] = ub[i];
                 lds_arrive(&s.ucount[vt], lane);
-                if constexpr (SIDE) {  // routing signal: the residuals R (bf16, as carried) or the targets
-                    const bool res = a.side_kind == kSideResidual;
-                    uint16_t *so = static_cast<uint16_t *>(a.side) + vcol;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint2 x4 = __builtin_bit_cast(uint2, res ? ub[i] : vb[i]);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int t = c * C + 16 * i + 4 * lg + r;
-                            const uint32_t w2 = r < 2 ? x4.x : x4.y;
-                            if (t < T) so[tok(t) * dv] = static_cast<uint16_t>(r & 1 ? w2 >> 16 : w2);
-                        }
-                    }
-                }
                 state_update<KT>(St, R, D, ub, KS, lane);
                 if (c + 1 < nchunks) {
                     lds_wait(&s.scount[vt], static_cast<unsigned int>(2 * (c + 1)), status);  // both output waves
@@ -632,6 +618,42 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                             if (t0 + 16 * RT[r] + lc < T)
                                 *reinterpret_cast<bf16x4 *>(yo + static_cast<uint32_t>(16 * RT[r] * hdv + 16 * t)) =
                                     bf4(y[r][t]);
+                    if constexpr (SIDE) {
+                        // routing signal of this wave's token rows, off the
+                        // carry's chain: the residuals R (bf16, as the carry
+                        // published them) or the staged write targets (kept
+                        // after the output's products, so its reads do not
+                        // lengthen their register lifetimes)
+                        __builtin_amdgcn_sched_barrier(0);
+                        uint16_t *sb = static_cast<uint16_t *>(a.side) + tok(t0) * dv + v0;
+                        const uint32_t h32 = static_cast<uint32_t>(hdv);
+                        if (a.side_kind == kSideResidual) {
+#pragma unroll 1
+                            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                                for (int r = 0; r < 2; ++r) {
+                                    const uint2 x4 = __builtin_bit_cast(uint2, s.uh[t][RT[r]][lane]);
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) {
+                                        const int row = 16 * RT[r] + 4 * lg + e;
+                                        const uint32_t w2 = e < 2 ? x4.x : x4.y;
+                                        if (t0 + row < T)
+                                            sb[static_cast<uint32_t>(row) * h32 + 16 * t + lc] =
+                                                static_cast<uint16_t>(e & 1 ? w2 >> 16 : w2);
+                                    }
+                                }
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                                for (int t = 0; t < 2; ++t) {
+                                    const int row = 16 * RT[r] + lc;
+                                    if (t0 + row < T)
+                                        *reinterpret_cast<uint2 *>(sb + static_cast<uint32_t>(row) * h32 + 16 * t + 4 * lg) =
+                                            *reinterpret_cast<const uint2 *>(&R.v[row * Lds::VS + 16 * t + 4 * lg]);
+                                }
+                        }
+                    }
                 };
                 if (vt == 0) rows(ic<0>{});
                 else rows(ic<1>{});

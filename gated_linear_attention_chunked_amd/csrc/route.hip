@@ -83,31 +83,43 @@ __global__ __launch_bounds__(RNT) void route_kernel(int64_t M, int D, int N, con
     // staging: piece i of the thread covers row (tid + RNT i) / 8, piece (tid % 8)
     constexpr int NA = RBM * PIECES / RNT, NB = RBD * PIECES / RNT;
     const int prow = tid / PIECES, pc = tid % PIECES;
+    // Loads are unconditional (rows and reduction indices clamped into the
+    // operands) so they stay in flight through the products; pieces outside
+    // the operands are zeroed at commit.
     uint4 ra[NA], rb[NB];
+    uint32_t okm = 0u;  // bit i: A piece i inside; bit NA + i: B piece i inside
+    const E *arow[NA];
+    const E *brow[NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) arow[i] = S + min(m0 + prow + (RNT / PIECES) * i, M - 1) * N;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) brow[i] = P + static_cast<int64_t>(min(d0 + prow + (RNT / PIECES) * i, D - 1)) * N;
     auto fetch = [&](int k0) {
         const int kk = k0 + pc * EPP;
         const bool kin = kk < N;
+        const int kc = min(kk, N - EPP);
+        okm = 0u;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            const int64_t m = m0 + prow + (RNT / PIECES) * i;
-            const bool ok = kin && m < M;
-            ra[i] = ok ? *reinterpret_cast<const uint4 *>(S + m * N + kk) : make_uint4(0u, 0u, 0u, 0u);
+            okm |= (kin && m0 + prow + (RNT / PIECES) * i < M ? 1u : 0u) << i;
+            ra[i] = *reinterpret_cast<const uint4 *>(arow[i] + kc);
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const int d = d0 + prow + (RNT / PIECES) * i;
-            const bool ok = kin && d < D;
-            rb[i] = ok ? *reinterpret_cast<const uint4 *>(P + static_cast<int64_t>(d) * N + kk)
-                       : make_uint4(0u, 0u, 0u, 0u);
+            okm |= (kin && d0 + prow + (RNT / PIECES) * i < D ? 1u : 0u) << (NA + i);
+            rb[i] = *reinterpret_cast<const uint4 *>(brow[i] + kc);
         }
     };
+    auto mask = [](uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); };
     auto commit = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < NA; ++i)
-            *reinterpret_cast<uint4 *>(&s.a[buf][(prow + (RNT / PIECES) * i) * RS + pc * EPP]) = ra[i];
+            *reinterpret_cast<uint4 *>(&s.a[buf][(prow + (RNT / PIECES) * i) * RS + pc * EPP]) =
+                mask(ra[i], 0u - ((okm >> i) & 1u));
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            *reinterpret_cast<uint4 *>(&s.b[buf][(prow + (RNT / PIECES) * i) * RS + pc * EPP]) = rb[i];
+            *reinterpret_cast<uint4 *>(&s.b[buf][(prow + (RNT / PIECES) * i) * RS + pc * EPP]) =
+                mask(rb[i], 0u - ((okm >> (NA + i)) & 1u));
     };
 
     // acc[j][i]: C^T tile of columns 64 wd + 16 j .. (rows of the transposed
@@ -174,25 +186,41 @@ __global__ __launch_bounds__(RNT) void route_kernel(int64_t M, int D, int N, con
         __syncthreads();
     }
 
-    // epilogue: h[token][4 columns] += acc, read and written once
+    // epilogue: h[token][4 columns] += acc, read and written once.  The h
+    // reads of a half tile are all issued before any is used (clamped into
+    // h, so unconditional), then added and stored where they fall inside.
+    using H4 = std::conditional_t<kBf16, bf16x4, float4>;
+    H4 *hp = static_cast<H4 *>(hv);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t m = m0 + 128 * wm + 16 * i + lc;
-        if (m >= M) continue;
+    for (int half = 0; half < 2; ++half) {
+        H4 hx[4][4];
+        int64_t off[4][4];
+        bool in[4][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int d = d0 + 64 * wd + 16 * j + 4 * lg;
-            if (d >= D) continue;
-            if constexpr (kBf16) {
-                bf16x4 *hp = reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(hv) + m * D + d);
-                const f32x4 x = __builtin_convertvector(*hp, f32x4) + acc[j][i];
-                *hp = bf4(x);
-            } else {
-                float4 *hp = reinterpret_cast<float4 *>(static_cast<float *>(hv) + m * D + d);
-                const float4 x = *hp;
-                *hp = make_float4(x.x + acc[j][i][0], x.y + acc[j][i][1], x.z + acc[j][i][2], x.w + acc[j][i][3]);
+        for (int ii = 0; ii < 4; ++ii) {
+            const int i = 4 * half + ii;
+            const int64_t m = m0 + 128 * wm + 16 * i + lc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = d0 + 64 * wd + 16 * j + 4 * lg;
+                in[ii][j] = m < M && d < D;
+                off[ii][j] = (min(m, M - 1) * D + min(d, D - 4)) / 4;
+                hx[ii][j] = hp[off[ii][j]];
             }
         }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 a4 = acc[j][4 * half + ii];
+                if constexpr (kBf16) {
+                    const f32x4 x = __builtin_convertvector(hx[ii][j], f32x4) + a4;
+                    if (in[ii][j]) hp[off[ii][j]] = bf4(x);
+                } else {
+                    const float4 x = hx[ii][j];
+                    if (in[ii][j]) hp[off[ii][j]] = make_float4(x.x + a4[0], x.y + a4[1], x.z + a4[2], x.w + a4[3]);
+                }
+            }
     }
 }
 

@@ -44,3 +44,36 @@ def test_metric_workload_is_hbm_bound_at_peak():
     t_hbm = bench.algorithmic_bytes(w) / (bench.HBM_PEAK_GBS * 1e9)
     t_mfma = bench.algorithmic_flops(w) / (bench.MFMA_BF16_PEAK_TFS * 1e12)
     assert abs(t_hbm - 34.2e-6) < 0.1e-6 and t_mfma < t_hbm
+
+
+# (bytes, flops) per call of the jobs beside the forward scan, worked out by
+# hand for B8 T4096 H8 dk = dv = 128, bf16 streams (262,144 token-heads):
+JOB_EXPECTED = {
+    # reads q, k, v, dout 4 x 128 x 2 + beta 2 + alpha 2 = 1028 B; writes dq, dk, dv
+    # 3 x 128 x 4 + dbeta 4 + dalpha 4 = 1544 B; + dstate_in 4,194,304 B.
+    # flops 14 x 128 x 128 per token-head
+    "gdn_bwd_bf16_B8_T4096_H8_d128": (2572 * 262_144 + 4_194_304, 14 * 16_384 * 262_144),
+    # the forward's 273,678,336 B + the residual 128 x 2 B per token-head
+    "gdn_side_bf16_B8_T4096_H8_d128": (273_678_336 + 256 * 262_144, 7 * 16_384 * 262_144),
+    # M = 32,768 tokens, N = 1024, D = 1024: (M N + D N + 2 M D) x 2 B; 2 M N D flops
+    "route_bf16_B8_T4096_N1024_D1024": (203_423_744, 68_719_476_736),
+    # 13 levels: forward bytes - one state + lambda 13 x 4 B per token-head + 13 states;
+    # occupancy sum over t < 4096 of popcount(t) + 1 = 4096 x 6 + 4096 = 28,672
+    "gdn_loglinear_bf16_B8_T4096_H8_d128": (273_678_336 - 4_194_304 + 52 * 262_144 + 13 * 4_194_304,
+                                            64 * 28_672 * 7 * 16_384),
+    # d (13 x 2 B) in, lambda (13 x 4 B) out per row; 4 x 13 x 26 flops per row
+    "loglinear_lambda_bf16_B8_T4096_H8_L13": (78 * 262_144, 1352 * 262_144),
+}
+
+
+def test_job_counts():
+    assert set(JOB_EXPECTED) == set(bench.JOBS)
+    for name, (nbytes, nflops) in JOB_EXPECTED.items():
+        kind, base, extra = bench.JOBS[name]
+        assert bench.job_counts(kind, I.WORKLOADS[base], extra) == (nbytes, nflops), name
+
+
+def test_loglinear_levels_and_occupancy():
+    assert [bench.loglinear_levels(T) for T in (1, 2, 3, 4, 5, 4096, 4097)] == [1, 2, 3, 3, 4, 13, 14]
+    # positions 0..7: popcounts 0,1,1,2,1,2,2,3 -> 12, plus one level 0 each -> 20
+    assert bench.loglinear_occupancy(8) == 20
