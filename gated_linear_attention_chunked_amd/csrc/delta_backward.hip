@@ -53,13 +53,31 @@ struct BwShape {
     static constexpr int ROWS = kBw / TPR;         // rows per workgroup
 };
 
-// Sum over the rows of a wave: lanes lr, lr + TPR, lr + 2 TPR, ...
+// Sum over the rows of a wave: lanes lr, lr + TPR, lr + 2 TPR, ...  The
+// partner across 16 and 32 lanes comes from gfx950's row-swap moves (with a
+// value swapped against itself, the two results are the two halves of each
+// pair, so their sum is the pair's sum in every lane); the partner across 8
+// lanes is a rotation by 8 inside each 16-lane row.  All VALU, no LDS.
+__device__ __forceinline__ float swap_sum16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Two row sums for the price of one: with a and b swapped against each other
+// across 16 lanes, the pair sums of a land in 16-lane rows 0 and 2 and those
+// of b in rows 1 and 3; one 32-lane swap then completes both.  Returns a's
+// total in lanes 0-15 (and 32-47) and b's in lanes 16-31 (and 48-63).
 template <int TPR>
-__device__ __forceinline__ float wave_rows_sum(float x) {
-    if constexpr (TPR <= 8) x += __shfl_xor(x, 8, 64);
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    return x;
+__device__ __forceinline__ float wave_rows_sum2(float a, float b) {
+    if constexpr (TPR <= 8) {  // memory rows of 8 lanes: first the partner 8 lanes on (row_ror:8)
+        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x128, 0xf, 0xf, false));
+        b += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b), 0x128, 0xf, 0xf, false));
+    }
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return swap_sum32(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
 template <int VARIANT, typename IO, int DK>
@@ -275,26 +293,27 @@ __global__ __launch_bounds__(kBw) void delta_backward_kernel(DeltaBwdArgs g) {
                     G[m] *= dcy[m];
                 }
                 if constexpr (kScalar) da = group_sum<TPR>(da);
-                // this wave's rows summed, into the token's LDS slot
+                // this wave's rows summed in pairs (dq with dk, neighbouring
+                // columns of the third gradient, dbeta with dalpha), into the
+                // token's LDS slot: first of each pair from lanes 0 .. TPR-1,
+                // second from lanes 16 .. 16+TPR-1
+                float zqk[CPT], zx[kX ? CPT / 2 : 1];
 #pragma unroll
-                for (int m = 0; m < CPT; ++m) {
-                    pq[m] = wave_rows_sum<TPR>(pq[m]);
-                    pk[m] = wave_rows_sum<TPR>(pk[m]);
-                    if constexpr (kX) px[m] = wave_rows_sum<TPR>(px[m]);
+                for (int m = 0; m < CPT; ++m) zqk[m] = wave_rows_sum2<TPR>(pq[m], pk[m]);
+                if constexpr (kX) {
+#pragma unroll
+                    for (int m = 0; m < CPT / 2; ++m) zx[m] = wave_rows_sum2<TPR>(px[2 * m], px[2 * m + 1]);
                 }
-                const float db_ = wave_rows_sum<TPR>(r * gk);
-                if constexpr (kScalar) da = wave_rows_sum<TPR>(da);
-                if (lane < TPR) {
+                const float zs = wave_rows_sum2<TPR>(r * gk, kScalar ? da : 0.f);
+                const int half = lane >> 4;  // 0: first of the pair, 1: second
+                if ((lane & 15) < TPR && lane < 32) {
 #pragma unroll
-                    for (int m = 0; m < CPT; ++m) {
-                        rq[tt][wave][lr + TPR * m] = pq[m];
-                        rk[tt][wave][lr + TPR * m] = pk[m];
-                        if constexpr (kX) rx[tt][wave][lr + TPR * m] = px[m];
+                    for (int m = 0; m < CPT; ++m) (half ? rk : rq)[tt][wave][lr + TPR * m] = zqk[m];
+                    if constexpr (kX) {
+#pragma unroll
+                        for (int m = 0; m < CPT / 2; ++m) rx[tt][wave][lr + TPR * (2 * m + half)] = zx[m];
                     }
-                    if (lane == 0) {
-                        rs[tt][wave][0] = db_;
-                        rs[tt][wave][1] = da;
-                    }
+                    if ((lane & 15) == 0) rs[tt][wave][half] = zs;
                 }
             }
             // the workgroup's sums of these HB tokens, added into the outputs
