@@ -345,10 +345,10 @@ lam_status lam_route(int dtype, int64_t M, int64_t D, int64_t N, const void *s, 
     if (M < 0 || D <= 0 || N <= 0) return LAM_ERR_INVALID_ARG;
     if (!lam::route_supported(D, N)) return LAM_ERR_UNSUPPORTED;
     int64_t ns, nh, np;
-    // sizes, 32-bit column indices and the grid (256 x 128 tiles)
+    // sizes, 32-bit column indices and the grid (128 x 128 tiles)
     if (!mul_ok(M, N, ns) || !mul_ok(M, D, nh) || !mul_ok(D, N, np)) return LAM_ERR_INVALID_ARG;
     if (D > INT_MAX / 2 || N > INT_MAX / 2) return LAM_ERR_INVALID_ARG;
-    if (((M + 255) / 256) * ((D + 127) / 128) > INT_MAX) return LAM_ERR_INVALID_ARG;
+    if (((M + 127) / 128) * ((D + 127) / 128) > INT_MAX) return LAM_ERR_INVALID_ARG;
     if (M == 0) return LAM_OK;
     if (!s || !P || !h) return LAM_ERR_INVALID_ARG;
     // rows are read as 16-byte pieces

@@ -11,11 +11,13 @@
 // fragment.  The add is fused into the epilogue, so h is read once and
 // written once.
 //
-// Schedule: one workgroup of 4 waves per 256-token x 128-column tile of h.
-// Per step of BK reduction indices the workgroup stages its s rows and P rows
-// into LDS (rows padded by 16 bytes, so the 16 lanes reading one fragment hit
-// distinct banks) while it multiplies the previous step's tiles; waves own
-// 128 x 64 sub-tiles (32 accumulator tiles of 16 x 16).  The product is formed
+// Schedule: one workgroup of 4 waves per 128-token x 128-column tile of h,
+// two workgroups per compute unit (74 KB of LDS each), so one's load waits
+// are covered by the other's products.  Per step of BK reduction indices the
+// workgroup stages its s rows and P rows into LDS (rows padded by 16 bytes,
+// so the 16 lanes reading one fragment hit distinct banks) while it
+// multiplies the previous step's tiles; waves own 64 x 64 sub-tiles (16
+// accumulator tiles of 16 x 16).  The product is formed
 // transposed, C^T = P s^T, so a lane's accumulator holds four consecutive
 // columns of h for one token: the epilogue reads, adds and writes 8 (bf16) or
 // 16 (fp32) contiguous bytes per lane and tile.  The eight column tiles of a
@@ -29,7 +31,7 @@
 namespace lam {
 namespace {
 
-constexpr int RBM = 256;    // tokens per workgroup tile
+constexpr int RBM = 128;    // tokens per workgroup tile
 constexpr int RBD = 128;    // columns of h per workgroup tile
 constexpr int RNT = 256;    // threads
 constexpr int PIECES = 8;   // 16-byte pieces per staged row (BK elements)
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(RNT) void route_kernel(int64_t M, int D, int N, con
     const int d0 = dt * RBD;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wd = wave & 1;   // sub-tile: tokens 128 wm .., columns 64 wd ..
+    const int wm = wave >> 1, wd = wave & 1;   // sub-tile: tokens 64 wm .., columns 64 wd ..
     const int lg = lane >> 4, lc = lane & 15;
     const E *S = static_cast<const E *>(sv);
     const E *P = static_cast<const E *>(pv);
@@ -123,29 +125,30 @@ __global__ __launch_bounds__(RNT) void route_kernel(int64_t M, int D, int N, con
     };
 
     // acc[j][i]: C^T tile of columns 64 wd + 16 j .. (rows of the transposed
-    // product) by tokens 128 wm + 16 i ..; lane (lg, lc) holds columns
+    // product) by tokens 64 wm + 16 i ..; lane (lg, lc) holds columns
     // 4 lg .. 4 lg + 3 of token lc
-    f32x4 acc[4][8];
+    constexpr int MI = 4;  // token tiles per wave
+    f32x4 acc[4][MI];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < MI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto multiply = [&](int buf) {
-        const E *A = s.a[buf] + (128 * wm) * RS;
+        const E *A = s.a[buf] + (64 * wm) * RS;
         const E *B = s.b[buf] + (64 * wd) * RS;
         if constexpr (kBf16) {
 #pragma unroll
             for (int k = 0; k < BK; k += 32) {
-                bf16x8 pf[4], sf[8];
+                bf16x8 pf[4], sf[MI];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) pf[j] = row_frag2(B, RS, 16 * j, k, lane);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) sf[i] = row_frag2(A, RS, 16 * i, k, lane);
+                for (int i = 0; i < MI; ++i) sf[i] = row_frag2(A, RS, 16 * i, k, lane);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[j][i] = mfma32(pf[j], sf[i], acc[j][i]);
+                    for (int i = 0; i < MI; ++i) acc[j][i] = mfma32(pf[j], sf[i], acc[j][i]);
             }
         } else {
             // four reduction indices per lane and read (16 bytes); the four
@@ -153,14 +156,14 @@ __global__ __launch_bounds__(RNT) void route_kernel(int64_t M, int D, int N, con
             // on which index each lane supplies
 #pragma unroll
             for (int k = 0; k < BK; k += 16) {
-                f32x4v pf[4], sf[8];
+                f32x4v pf[4], sf[MI];
                 typedef __attribute__((address_space(3))) const f32x4v lds_f4;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     pf[j] = *reinterpret_cast<lds_f4 *>((__attribute__((address_space(3))) const void *)(
                         B + (16 * j + lc) * RS + k + 4 * lg));
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
+                for (int i = 0; i < MI; ++i)
                     sf[i] = *reinterpret_cast<lds_f4 *>((__attribute__((address_space(3))) const void *)(
                         A + (16 * i + lc) * RS + k + 4 * lg));
 #pragma unroll
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(RNT) void route_kernel(int64_t M, int D, int N, con
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
-                        for (int i = 0; i < 8; ++i)
+                        for (int i = 0; i < MI; ++i)
                             acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x4f32(pf[j][r], sf[i][r], acc[j][i], 0, 0, 0);
             }
         }
@@ -192,14 +195,14 @@ __global__ __launch_bounds__(RNT) void route_kernel(int64_t M, int D, int N, con
     using H4 = std::conditional_t<kBf16, bf16x4, float4>;
     H4 *hp = static_cast<H4 *>(hv);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < MI / 4; ++half) {
         H4 hx[4][4];
         int64_t off[4][4];
         bool in[4][4];
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int i = 4 * half + ii;
-            const int64_t m = m0 + 128 * wm + 16 * i + lc;
+            const int64_t m = m0 + 64 * wm + 16 * i + lc;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int d = d0 + 64 * wd + 16 * j + 4 * lg;
