@@ -628,19 +628,33 @@ __global__ __launch_bounds__(NT8) void delta_chunked_wy_kernel(DeltaArgs a, cons
                         uint16_t *sb = static_cast<uint16_t *>(a.side) + tok(t0) * dv + v0;
                         const uint32_t h32 = static_cast<uint32_t>(hdv);
                         if (a.side_kind == kSideResidual) {
-#pragma unroll 1
+                            // R^T times an identity block on the matrix cores
+                            // (exact: one product by 1, the rest by 0) lands R
+                            // in y's layout, four columns of one token per
+                            // lane: 8-byte row stores instead of scattered
+                            // 2-byte ones.  Identity block for row tile i of
+                            // its 32-token half, in the product's permuted
+                            // reduction order (slots 4g .. 4g+3 hold tokens
+                            // 4g + j of the half's first 16, slots 4 .. 7
+                            // those of its second 16).
+                            bf16x4 one4, zer4;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                one4[j] = lc == 4 * lg + j ? static_cast<__bf16>(1.f) : static_cast<__bf16>(0.f);
+                                zer4[j] = static_cast<__bf16>(0.f);
+                            }
+#pragma unroll
                             for (int t = 0; t < 2; ++t)
 #pragma unroll
                                 for (int r = 0; r < 2; ++r) {
-                                    const uint2 x4 = __builtin_bit_cast(uint2, s.uh[t][RT[r]][lane]);
-#pragma unroll
-                                    for (int e = 0; e < 4; ++e) {
-                                        const int row = 16 * RT[r] + 4 * lg + e;
-                                        const uint32_t w2 = e < 2 ? x4.x : x4.y;
-                                        if (t0 + row < T)
-                                            sb[static_cast<uint32_t>(row) * h32 + 16 * t + lc] =
-                                                static_cast<uint16_t>(e & 1 ? w2 >> 16 : w2);
-                                    }
+                                    const int i = RT[r], hp = i >> 1;
+                                    const bf16x8 aR = cat8(s.uh[t][2 * hp][lane], s.uh[t][2 * hp + 1][lane]);
+                                    const f32x4 x = mfma32(aR, (i & 1) ? cat8(zer4, one4) : cat8(one4, zer4),
+                                                           f32x4{0.f, 0.f, 0.f, 0.f});
+                                    const int row = 16 * i + lc;
+                                    if (t0 + row < T)
+                                        *reinterpret_cast<bf16x4 *>(sb + static_cast<uint32_t>(row) * h32 + 16 * t + 4 * lg) =
+                                            bf4(x);
                                 }
                         } else {
 #pragma unroll
