@@ -31,6 +31,7 @@ namespace lam {
 namespace {
 
 constexpr int kLThreads = 256;
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 constexpr int LTT = 16;  // tokens per LDS tile
 
 template <int DK>
@@ -297,43 +298,74 @@ hipError_t launch_io(const LogLinArgs &g, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-// ---- adaptive level weights: one thread per (token, head) row
+// ---- adaptive level weights: one thread per (token, head) row.  NLP is
+// the level count rounded up to a multiple of 4: the weights are staged
+// zero-padded to it, so every loop has a constant trip count and the padded
+// levels add zeros; W1 is staged transposed so both products read four
+// levels' weights per (broadcast) LDS access.
 constexpr int kMlpThreads = 256;
 
-template <typename IO>
+template <typename IO, int NLP>
 __global__ __launch_bounds__(kMlpThreads) void loglin_lambda_kernel(int64_t M, int nL, int nh, const void *d,
                                                                     const float *W1, const float *W2,
                                                                     const float *bias, float *lam) {
-    __shared__ float w1[kLogLinMaxLevels * kLogLinMaxHidden], w2[kLogLinMaxHidden * kLogLinMaxLevels];
-    __shared__ float bs[kLogLinMaxLevels];
-    for (int i = threadIdx.x; i < nL * nh; i += kMlpThreads) {
-        w1[i] = W1[i];
-        w2[i] = W2[i];
+    __shared__ f32x4v w1t[kLogLinMaxHidden][NLP / 4];  // w1t[j][l] = W1[l][j]
+    __shared__ f32x4v w2s[kLogLinMaxHidden][NLP / 4];  // w2s[j][l] = W2[j][l]
+    __shared__ float bs[NLP];
+    float *w1f = reinterpret_cast<float *>(w1t), *w2f = reinterpret_cast<float *>(w2s);
+    for (int e = threadIdx.x; e < nh * NLP; e += kMlpThreads) {
+        const int jj = e / NLP, l = e % NLP;
+        w1f[e] = l < nL ? W1[l * nh + jj] : 0.f;
+        w2f[e] = l < nL ? W2[jj * nL + l] : 0.f;
     }
-    if (threadIdx.x < nL) bs[threadIdx.x] = bias[threadIdx.x];
+    if (threadIdx.x < NLP) bs[threadIdx.x] = threadIdx.x < nL ? bias[threadIdx.x] : 0.f;
     __syncthreads();
     const int64_t r = static_cast<int64_t>(blockIdx.x) * kMlpThreads + threadIdx.x;
     if (r >= M) return;
-    float x[kLogLinMaxLevels];
+    float x[NLP], o[NLP];
 #pragma unroll
-    for (int l = 0; l < kLogLinMaxLevels; ++l) x[l] = l < nL ? IO::ld(d, r * nL + l) : 0.f;
-    float o[kLogLinMaxLevels];
-#pragma unroll
-    for (int l = 0; l < kLogLinMaxLevels; ++l) o[l] = l < nL ? bs[l] : 0.f;
+    for (int l = 0; l < NLP; ++l) {
+        x[l] = l < nL ? IO::ld(d, r * nL + l) : 0.f;
+        o[l] = bs[l];
+    }
     // h = d W1 one hidden unit at a time, folded straight into h W2
-    for (int j = 0; j < nh; ++j) {
+    for (int jj = 0; jj < nh; ++jj) {
         float hj = 0.f;
 #pragma unroll
-        for (int l = 0; l < kLogLinMaxLevels; ++l)
-            if (l < nL) hj = fmaf(x[l], w1[l * nh + j], hj);
+        for (int q = 0; q < NLP / 4; ++q) {
+            const f32x4v w = w1t[jj][q];
+            hj = fmaf(x[4 * q], w[0], hj);
+            hj = fmaf(x[4 * q + 1], w[1], hj);
+            hj = fmaf(x[4 * q + 2], w[2], hj);
+            hj = fmaf(x[4 * q + 3], w[3], hj);
+        }
 #pragma unroll
-        for (int l = 0; l < kLogLinMaxLevels; ++l)
-            if (l < nL) o[l] = fmaf(hj, w2[j * nL + l], o[l]);
+        for (int q = 0; q < NLP / 4; ++q) {
+            const f32x4v w = w2s[jj][q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[4 * q + e] = fmaf(hj, w[e], o[4 * q + e]);
+        }
     }
     // softplus(x) = max(x, 0) + log1p(exp(-|x|))
 #pragma unroll
-    for (int l = 0; l < kLogLinMaxLevels; ++l)
+    for (int l = 0; l < NLP; ++l)
         if (l < nL) lam[r * nL + l] = fmaxf(o[l], 0.f) + log1pf(expf(-fabsf(o[l])));
+}
+
+template <typename IO>
+hipError_t launch_lambda_io(int64_t M, int nL, int nh, const void *d, const float *W1, const float *W2,
+                            const float *b, float *lam, hipStream_t stream) {
+    const unsigned blocks = static_cast<unsigned>((M + kMlpThreads - 1) / kMlpThreads);
+    switch ((nL + 3) / 4) {
+        case 1: loglin_lambda_kernel<IO, 4><<<blocks, kMlpThreads, 0, stream>>>(M, nL, nh, d, W1, W2, b, lam); break;
+        case 2: loglin_lambda_kernel<IO, 8><<<blocks, kMlpThreads, 0, stream>>>(M, nL, nh, d, W1, W2, b, lam); break;
+        case 3: loglin_lambda_kernel<IO, 12><<<blocks, kMlpThreads, 0, stream>>>(M, nL, nh, d, W1, W2, b, lam); break;
+        case 4: loglin_lambda_kernel<IO, 16><<<blocks, kMlpThreads, 0, stream>>>(M, nL, nh, d, W1, W2, b, lam); break;
+        case 5: loglin_lambda_kernel<IO, 20><<<blocks, kMlpThreads, 0, stream>>>(M, nL, nh, d, W1, W2, b, lam); break;
+        case 6: loglin_lambda_kernel<IO, 24><<<blocks, kMlpThreads, 0, stream>>>(M, nL, nh, d, W1, W2, b, lam); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -350,12 +382,8 @@ hipError_t launch_loglin(const LogLinArgs &g, hipStream_t stream) {
 hipError_t launch_loglin_lambda(int dtype, int64_t M, int nL, int nh, const void *d, const float *W1,
                                 const float *W2, const float *b, float *lam, hipStream_t stream) {
     if (M == 0) return hipSuccess;
-    const unsigned blocks = static_cast<unsigned>((M + kMlpThreads - 1) / kMlpThreads);
-    if (dtype == kBF16)
-        loglin_lambda_kernel<IoBF16><<<blocks, kMlpThreads, 0, stream>>>(M, nL, nh, d, W1, W2, b, lam);
-    else
-        loglin_lambda_kernel<IoF32><<<blocks, kMlpThreads, 0, stream>>>(M, nL, nh, d, W1, W2, b, lam);
-    return hipGetLastError();
+    return dtype == kBF16 ? launch_lambda_io<IoBF16>(M, nL, nh, d, W1, W2, b, lam, stream)
+                          : launch_lambda_io<IoF32>(M, nL, nh, d, W1, W2, b, lam, stream);
 }
 
 }  // namespace lam
