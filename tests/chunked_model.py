@@ -211,3 +211,114 @@ def kda_paired(q, k, v, beta, alpha, state_in=None):
                 S = S * (x0["gc"] * x1["gc"])[None, :] + U0.T @ ke0 + U1.T @ x1["ke"]
             state_out[b, h] = S
     return out[:, :T], state_out
+
+
+def delta_chunked_backward(variant, q, k, v, beta, dout, alpha=None, erase_b=None, write_w=None,
+                           state_in=None, dstate_out=None, C=64):
+    """Adjoint of the chunked form above for DeltaNet, Gated DeltaNet and
+    Gated DeltaNet-2, in the residual form the GPU evaluates: per chunk, with
+    N = strict(E K^T * Gam), A = lower(Q K^T * Gam) diag(beta) and
+    Kc = diag(beta gamma_C / gamma) K,
+        R = (I + N diag(beta))^{-1} (Z - diag(gamma) E S^T),
+        Y = diag(gamma) Q S^T + A R,   S' = gamma_C S + R^T Kc,
+    and in reverse, from dY and dS':
+        dR = A^T dY + Kc dS'^T,   dX = (I + N diag(beta))^{-T} dR,
+        dS = gamma_C dS' + dY^T diag(gamma) Q - dX^T diag(gamma) E,
+    with every other gradient a product of these chunk operands (written out
+    below).  Returns the same dict as oracle.delta_backward."""
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    g2 = variant == "gdn2"
+    out = {"dq": np.zeros((B, T, H, dk)), "dk": np.zeros((B, T, H, dk)), "dv": np.zeros((B, T, H, dv)),
+           "dbeta": np.zeros((B, T, H)), "dstate_in": np.zeros((B, H, dv, dk))}
+    if variant != "deltanet":
+        out["dalpha"] = np.zeros((B, T, H))
+    if g2:
+        out["derase_b"] = np.zeros((B, T, H, dk))
+        out["dwrite_w"] = np.zeros((B, T, H, dv))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dv, dk)) if state_in is None else state_in[b, h].copy()
+            chunks = []
+            for c0 in range(0, T, C):               # forward, keeping each chunk's operands
+                c1 = min(T, c0 + C)
+                n = c1 - c0
+                Q, K, V = q[b, c0:c1, h], k[b, c0:c1, h], v[b, c0:c1, h]
+                be = beta[b, c0:c1, h]
+                tril = np.tril(np.ones((n, n)))
+                stril = np.tril(np.ones((n, n)), -1)
+                lg = np.zeros(n) if variant == "deltanet" else np.cumsum(np.log(alpha[b, c0:c1, h]))
+                Gam = np.where(tril > 0, np.exp(np.where(tril > 0, lg[:, None] - lg[None, :], 0.0)), 0.0)
+                g = np.exp(lg)
+                E = erase_b[b, c0:c1, h] * K if g2 else K
+                Z = write_w[b, c0:c1, h] * V if g2 else V
+                Nm = stril * (E @ K.T) * Gam
+                Am = tril * (Q @ K.T) * Gam
+                M = np.eye(n) + Nm * be[None, :]
+                R = np.linalg.solve(M, Z - g[:, None] * (E @ S.T))
+                sc = be * np.exp(lg[-1] - lg)
+                chunks.append((c0, c1, S.copy(), Q, K, V, E, be, lg, g, Gam, Nm, Am, M, R, sc))
+                S = g[-1] * S + R.T @ (sc[:, None] * K)
+            dS = np.zeros((dv, dk)) if dstate_out is None else dstate_out[b, h].copy()
+            for (c0, c1, S0, Q, K, V, E, be, lg, g, Gam, Nm, Am, M, R, sc) in reversed(chunks):
+                n = c1 - c0
+                tril = np.tril(np.ones((n, n)))
+                stril = np.tril(np.ones((n, n)), -1)
+                dY = dout[b, c0:c1, h]
+                Kc = sc[:, None] * K
+                A = Am * be[None, :]
+                dR = A.T @ dY + Kc @ dS.T
+                dKc = R @ dS
+                dX = np.linalg.solve(M.T, dR)
+                dlg = np.zeros(n)
+                # S' = gamma_C S + R^T Kc
+                dgC = np.sum(dS * S0)
+                dSn = g[-1] * dS + (g[:, None] * dY).T @ Q - dX.T @ (g[:, None] * E)
+                # Y = diag(g) Q S^T + A R
+                dQ = g[:, None] * (dY @ S0)
+                dg = np.sum(dY * (Q @ S0.T), axis=1)
+                dA = (dY @ R.T) * tril
+                dbe = np.sum(dA * Am, axis=0)
+                dAm = dA * be[None, :]
+                # R = M^{-1} X, X = Z - diag(g) E S^T, M = I + N diag(beta)
+                dZ = dX
+                dE = -g[:, None] * (dX @ S0)
+                dg += -np.sum(dX * (E @ S0.T), axis=1)
+                dLp = -(dX @ R.T) * stril
+                dbe += np.sum(dLp * Nm, axis=0)
+                dNm = dLp * be[None, :]
+                # N = strict(E K^T * Gam), Am = lower(Q K^T * Gam)
+                dEK = dNm * Gam
+                dE += dEK @ K
+                dK = dEK.T @ E
+                dQK = dAm * Gam
+                dQ += dQK @ K
+                dK += dQK.T @ Q
+                dGam = dNm * (E @ K.T) + dAm * (Q @ K.T)
+                # Kc = diag(sc) K, sc = beta exp(lg_C - lg)
+                dK += sc[:, None] * dKc
+                dsc = np.sum(dKc * K, axis=1)
+                dbe += dsc * np.exp(lg[-1] - lg)
+                # the decay exponents
+                gw = dGam * Gam
+                dlg += gw.sum(axis=1) - gw.sum(axis=0)
+                dlg += dg * g
+                dlg[-1] += dgC * g[-1] + np.sum(dsc * sc)
+                dlg -= dsc * sc
+                if g2:
+                    out["derase_b"][b, c0:c1, h] = K * dE
+                    dK += erase_b[b, c0:c1, h] * dE
+                    out["dwrite_w"][b, c0:c1, h] = V * dZ
+                    out["dv"][b, c0:c1, h] = write_w[b, c0:c1, h] * dZ
+                else:
+                    dK += dE
+                    out["dv"][b, c0:c1, h] = dZ
+                out["dq"][b, c0:c1, h] = dQ
+                out["dk"][b, c0:c1, h] = dK
+                out["dbeta"][b, c0:c1, h] = dbe
+                if variant != "deltanet":
+                    dlog = np.cumsum(dlg[::-1])[::-1]          # d log(alpha_j) = sum_{t >= j} dlg_t
+                    out["dalpha"][b, c0:c1, h] = dlog / alpha[b, c0:c1, h]
+                dS = dSn
+            out["dstate_in"][b, h] = dS
+    return out
