@@ -28,13 +28,17 @@
 //              Z = (I + C)^{-1} Pa, N = KA - E Z with E_ts = F_s[khat_t] / D_s
 //              (s <= t), alphahat_t = N_t / |N_t|, A <- A - Z^T D^{-1} Z;
 //            then the state-independent operands of each chunk's state step,
-//            Tc = (I + strict(Khat Ahat^T))^{-1} and Aq = lower(Qhat Ahat^T),
-//            written with khat, qhat and alphahat to a per-chunk record.
+//            with Tc = (I + strict(Khat Ahat^T))^{-1} and Aq = lower(Qhat Ahat^T):
+//              Ktil = Tc Khat, Qtil = Qhat - Aq Ktil, Tc and Aq Tc,
+//            written with alphahat to a per-chunk record.
 //   state:   per (b, h, 16 value rows of S): the generalised delta scan
-//              U = Tc (V - Khat S^T), Y = Qhat S^T + Aq U, S <- S + U^T Ahat,
+//              U = Tc (V - Khat S^T) = Tc V - Ktil S^T,
+//              Y = Qhat S^T + Aq U = Qtil S^T + (Aq Tc) V,  S <- S + U^T Ahat,
 //            with the key dimension of S^T split over the workgroup's D/16
 //            waves (one 16 x 16 accumulator tile each) and the partial
-//            products summed through LDS, one barrier per chunk.
+//            products summed through LDS, one barrier per chunk.  Tc V and
+//            (Aq Tc) V do not depend on the state, so the only products on
+//            the chunk-to-chunk chain are Ktil S^T, Qtil S^T and the update.
 // The last segment's alpha workgroup writes A_out; the state workgroups
 // write S_out.
 #include "device_common.h"
@@ -130,11 +134,11 @@ __host__ __device__ constexpr int seg_len(int D) { return D <= 32 ? 128 : 256; }
 // Per-chunk record the alpha kernel writes for the state kernel.
 template <int D>
 struct VlaChunk {
-    float kh[VC * D];        // khat rows (zero past the end of the sequence)
-    float qh[VC * D];        // qhat rows
+    float kt[VC * D];        // Ktil = Tc Khat, rows t (zero past the end of the sequence)
+    float qt[VC * D];        // Qtil = Qhat - Aq Ktil, rows t (zero past the end)
     f32x4 aht[D / 16][64];   // alphahat^T tiles, A-operand order: lane (g, i) of tile j holds ahat[4g + m][16j + i]
-    f32x4 top[64];           // (I + strict(Khat Ahat^T))^{-1}, A-operand order
-    f32x4 aq[64];            // lower(Qhat Ahat^T), A-operand order
+    f32x4 top[64];           // Tc = (I + strict(Khat Ahat^T))^{-1}, A-operand order
+    f32x4 aqt[64];           // Aq Tc with Aq = lower(Qhat Ahat^T), A-operand order
 };
 
 // Workspace layout of one call (after the status block): G and the segment-
@@ -357,13 +361,11 @@ struct AlphaLds {
 // One workgroup of D/16 waves per (b, h, segment).  Wave w keeps column tile
 // w of A^T as fp32 accumulator tiles.
 template <typename IO, int D>
-__global__ __launch_bounds__(64 * (D / 16)) void vla_alpha_kernel(VlaArgs a, const float *__restrict__ Aseg,
-                                                                  VlaChunk<D> *__restrict__ rec, int nseg,
-                                                                  unsigned int *status) {
+__device__ __forceinline__ void vla_alpha_body(AlphaLds<D> &s, const VlaArgs &a, const float *__restrict__ Aseg,
+                                               VlaChunk<D> *__restrict__ rec, int nseg, unsigned int *status) {
     constexpr int NW = D / 16, NT = 64 * NW, NQ = D / 16;
     constexpr int DS = AlphaLds<D>::DS, TS = AlphaLds<D>::TS;
     constexpr int SEG = seg_len(D);
-    __shared__ AlphaLds<D> s;
 
     const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
     const int head = blockIdx.x / nseg, sg = blockIdx.x % nseg;
@@ -494,13 +496,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_alpha_kernel(VlaArgs a, con
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) s.pa[(4 * g + r) * DS + col] = pa[r];
-        // the chunk's features go to its record (rows past the end are zero)
-#pragma unroll
-        for (int u = 0; u < EPT; ++u) {
-            const int e = tid + NT * u, t = e / D, j = e % D;
-            R.kh[e] = KH[t * DS + j];
-            R.qh[e] = QH[t * DS + j];
-        }
         lds_sync();
         // ---- Pa X^T (16 x 32), waves 0 and 1: column c of it stored as row c of g0t
         if (w < 2) {
@@ -632,10 +627,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_alpha_kernel(VlaArgs a, con
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             unit_lower_inverse(s.lt, s.top, lane);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            R.top[lane] = s.top[lane];
         } else if (w == 1) {
             f32x4 aq2[2] = {zero4, zero4};
 #pragma unroll
@@ -650,7 +641,49 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_alpha_kernel(VlaArgs a, con
             // already the A operand of Y = Aq U; keep s <= t
 #pragma unroll
             for (int r = 0; r < 4; ++r) aq[r] = 4 * g + r <= i ? aq[r] : 0.f;
-            R.aq[lane] = aq;
+            s.aq[lane] = aq;
+        }
+        lds_sync();
+        // ---- the state step's operands (tile w): Ktil = Tc Khat, Qtil = Qhat - Aq Ktil
+        {
+            const f32x4 tc = s.top[lane], aqv = s.aq[lane];
+            // B operand at step m: Khat[4g + m][col]
+            f32x4 kb, qb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                kb[r] = KH[(4 * g + r) * DS + col];
+                qb[r] = QH[(4 * g + r) * DS + col];
+            }
+            f32x4 k0 = mfma4(tc[0], kb[0], zero4), k1 = mfma4(tc[1], kb[1], zero4);
+            k0 = mfma4(tc[2], kb[2], k0);
+            k1 = mfma4(tc[3], kb[3], k1);
+            const f32x4 kt = k0 + k1;  // lane (g, i): Ktil[4g + r][col], the B operand of Aq Ktil
+            f32x4 q0 = qb, q1 = zero4;
+            q0 = mfma4(-aqv[0], kt[0], q0);
+            q1 = mfma4(-aqv[1], kt[1], q1);
+            q0 = mfma4(-aqv[2], kt[2], q0);
+            q1 = mfma4(-aqv[3], kt[3], q1);
+            const f32x4 qt = q0 + q1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                R.kt[(4 * g + r) * D + col] = kt[r];
+                R.qt[(4 * g + r) * D + col] = qt[r];
+            }
+            if (w == 0) R.top[lane] = tc;
+            if (w == NW - 1) {
+                // (Aq Tc)^T = Tc^T Aq^T: A operand Tc^T (lane (g, i) step m:
+                // Tc[4g + m][i]), B operand Aq^T (step m: Aq[i][4g + m], the
+                // A-order aq); the product lands in Aq Tc's A-operand order
+                const float *tf = reinterpret_cast<const float *>(s.top);
+                f32x4 a0 = zero4, a1 = zero4;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float tcm = tf[((i >> 2) * 16 + 4 * g + m) * 4 + (i & 3)];
+                    if (m & 1) a1 = mfma4(tcm, aqv[m], a1);
+                    else a0 = mfma4(tcm, aqv[m], a0);
+                }
+                R.aqt[lane] = a0 + a1;
+            }
         }
         lds_sync();  // chunk tiles free for the next chunk
     }
@@ -663,6 +696,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void vla_alpha_kernel(VlaArgs a, con
     }
 }
 
+template <typename IO, int D>
+__global__ __launch_bounds__(64 * (D / 16)) void vla_alpha_kernel(VlaArgs a, const float *__restrict__ Aseg,
+                                                                   VlaChunk<D> *__restrict__ rec, int nseg,
+                                                                   unsigned int *status) {
+    __shared__ AlphaLds<D> s;
+    vla_alpha_body<IO, D>(s, a, Aseg, rec, nseg, status);
+}
 // ================================ state ================================
 // Carry waves of the state kernel: D/16, one 16 x 16 tile of S^T each; with
 // two carries (d = 32) a third wave forms the output on a free SIMD, and with
@@ -672,6 +712,10 @@ template <int D>
 __host__ __device__ constexpr int state_waves() { return D / 16 <= 2 ? D / 16 + 1 : D / 16; }
 template <int D>
 __host__ __device__ constexpr int state_y_wave() { return D / 16 <= 2 ? D / 16 : 3; }
+// The wave that forms Tc V: the output wave with two carries, else wave 2
+// (with up to four carries it has its SIMD to itself).
+template <int D>
+__host__ __device__ constexpr int state_v_wave() { return D / 16 <= 2 ? D / 16 : 2; }
 
 // One workgroup per (b, h, 16 value rows of S).  Carry wave j < D/16 keeps
 // the 16 x 16 tile of S^T at key rows 16j .. 16j + 15 and the workgroup's
@@ -681,7 +725,9 @@ template <typename IO, int D>
 __global__ __launch_bounds__(64 * state_waves<D>()) void vla_state_kernel(VlaArgs a, const VlaChunk<D> *__restrict__ rec) {
     constexpr int NW = D / 16;
     constexpr int YW = state_y_wave<D>();  // the wave that forms the output
-    __shared__ f32x4 part[2][2][NW][64];  // [chunk parity][Khat S^T, Qhat S^T][wave][lane]
+    constexpr int VW = state_v_wave<D>();  // the wave that forms Tc V
+    __shared__ f32x4 part[2][2][NW][64];  // [chunk parity][Ktil S^T, Qtil S^T][wave][lane]
+    __shared__ f32x4 tv[2][64];           // [chunk parity] Tc V
     const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
     int head, vt;
     xcd_group_map(blockIdx.x, static_cast<int>(a.B * a.H), NW, head, vt);
@@ -703,7 +749,7 @@ __global__ __launch_bounds__(64 * state_waves<D>()) void vla_state_kernel(VlaArg
     const VlaChunk<D> *R0 = rec + static_cast<int64_t>(head) * nch;
     const bool is_carry = w < NW, is_y = w == YW;
     struct Ops {
-        f32x4 kh, qh, aht, top, aq;
+        f32x4 kt, qt, aht, top, aqt;
         float v[4];
     };
     // Every wave issues the same loads whatever its role (an output-only wave
@@ -713,10 +759,10 @@ __global__ __launch_bounds__(64 * state_waves<D>()) void vla_state_kernel(VlaArg
     auto load = [&](int c, Ops &o) {  // past the end: the last chunk again (never used)
         const int cc = min(c, nch - 1);
         const VlaChunk<D> &R = R0[cc];
-        o.kh = *reinterpret_cast<const f32x4 *>(&R.kh[i * D + 16 * wc + 4 * g]);
-        o.qh = *reinterpret_cast<const f32x4 *>(&R.qh[i * D + 16 * wc + 4 * g]);
+        o.kt = *reinterpret_cast<const f32x4 *>(&R.kt[i * D + 16 * wc + 4 * g]);
+        o.qt = *reinterpret_cast<const f32x4 *>(&R.qt[i * D + 16 * wc + 4 * g]);
         o.aht = R.aht[wc][lane];
-        o.aq = R.aq[lane];
+        o.aqt = R.aqt[lane];
         o.top = R.top[lane];
         const int t0 = cc * VC, n = min(VC, T - t0);
 #pragma unroll
@@ -730,46 +776,53 @@ __global__ __launch_bounds__(64 * state_waves<D>()) void vla_state_kernel(VlaArg
         const int p = c & 1, t0 = c * VC, n = min(VC, T - t0);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         if (is_carry) {
-            // partial Khat S^T and Qhat S^T over this wave's key rows (two
+            // partial Ktil S^T and Qtil S^T over this wave's key rows (two
             // accumulators per product keep the dependent chains short)
-            f32x4 pk0 = mfma4(cur.kh[0], ST[0], zero), pk1 = mfma4(cur.kh[1], ST[1], zero);
-            f32x4 pq0 = mfma4(cur.qh[0], ST[0], zero), pq1 = mfma4(cur.qh[1], ST[1], zero);
-            pk0 = mfma4(cur.kh[2], ST[2], pk0);
-            pk1 = mfma4(cur.kh[3], ST[3], pk1);
-            pq0 = mfma4(cur.qh[2], ST[2], pq0);
-            pq1 = mfma4(cur.qh[3], ST[3], pq1);
+            f32x4 pk0 = mfma4(cur.kt[0], ST[0], zero), pk1 = mfma4(cur.kt[1], ST[1], zero);
+            f32x4 pq0 = mfma4(cur.qt[0], ST[0], zero), pq1 = mfma4(cur.qt[1], ST[1], zero);
+            pk0 = mfma4(cur.kt[2], ST[2], pk0);
+            pk1 = mfma4(cur.kt[3], ST[3], pk1);
+            pq0 = mfma4(cur.qt[2], ST[2], pq0);
+            pq1 = mfma4(cur.qt[3], ST[3], pq1);
             part[p][0][w][lane] = pk0 + pk1;
             part[p][1][w][lane] = pq0 + pq1;
         }
+        // V's rows (zero past the end), the B operand of Tc V and (Aq Tc) V
+        f32x4 vb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vb[r] = 4 * g + r < n ? cur.v[r] : 0.f;
+        if (w == VW) {
+            f32x4 a0 = mfma4(cur.top[0], vb[0], zero), a1 = mfma4(cur.top[1], vb[1], zero);
+            a0 = mfma4(cur.top[2], vb[2], a0);
+            a1 = mfma4(cur.top[3], vb[3], a1);
+            tv[p][lane] = a0 + a1;
+        }
+        f32x4 y0 = zero;
+        if (is_y) {
+            f32x4 y1 = mfma4(cur.aqt[1], vb[1], zero);
+            y0 = mfma4(cur.aqt[0], vb[0], zero);
+            y1 = mfma4(cur.aqt[3], vb[3], y1);
+            y0 = mfma4(cur.aqt[2], vb[2], y0);
+            y0 += y1;
+        }
         lds_sync();
-        // R = V - Khat S^T (rows past the end: v = 0 and khat = 0, so R = 0)
-        f32x4 z = part[p][0][0][lane];
-#pragma unroll
-        for (int j = 1; j < NW; ++j) z += part[p][0][j][lane];
-        f32x4 rr;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rr[r] = (4 * g + r < n ? cur.v[r] : 0.f) - z[r];
-        // U = Tc R (every wave forms it, bit for bit the same)
-        f32x4 u0 = mfma4(cur.top[0], rr[0], zero), u1 = mfma4(cur.top[1], rr[1], zero);
-        u0 = mfma4(cur.top[2], rr[2], u0);
-        u1 = mfma4(cur.top[3], rr[3], u1);
-        const f32x4 u = u0 + u1;
         if (is_carry) {
-            // S^T += Ahat^T U (this wave's key rows)
+            // U = Tc V - Ktil S^T (rows past the end: zero), summed in a fixed
+            // order so every wave forms the same U; then S^T += Ahat^T U
+            f32x4 z = part[p][0][0][lane];
+#pragma unroll
+            for (int j = 1; j < NW; ++j) z += part[p][0][j][lane];
+            const f32x4 u = tv[p][lane] - z;
             f32x4 d0 = mfma4(cur.aht[0], u[0], zero), d1 = mfma4(cur.aht[1], u[1], zero);
             d0 = mfma4(cur.aht[2], u[2], d0);
             d1 = mfma4(cur.aht[3], u[3], d1);
             ST += d0 + d1;
         }
-        if (is_y) {  // Y = Qhat S^T + Aq U
+        if (is_y) {  // Y = Qtil S^T + (Aq Tc) V
             f32x4 y = part[p][1][0][lane];
 #pragma unroll
             for (int j = 1; j < NW; ++j) y += part[p][1][j][lane];
-            f32x4 y1 = mfma4(cur.aq[1], u[1], zero);
-            y = mfma4(cur.aq[0], u[0], y);
-            y1 = mfma4(cur.aq[3], u[3], y1);
-            y = mfma4(cur.aq[2], u[2], y);
-            y += y1;
+            y += y0;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (4 * g + r < n) IO::st(a.out, tok(t0 + 4 * g + r) + vcol, y[r]);
