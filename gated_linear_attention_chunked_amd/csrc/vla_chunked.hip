@@ -358,12 +358,24 @@ struct AlphaLds {
     alignas(16) float part[D / 16][VC]; // per-wave partial |N_t|^2
 };
 
-// One workgroup of D/16 waves per (b, h, segment).  Wave w keeps column tile
-// w of A^T as fp32 accumulator tiles.
+// Tiles of A^T per wave in the alpha kernel.  At D = 96 the six column tiles
+// go two to a wave over three waves, and a fourth wave runs the serial parts
+// (the Sherman-Morrison recurrence and Tc): four waves spread evenly over the
+// SIMDs, so two workgroups fit on a compute unit (six one-tile waves put two
+// waves on each of SIMDs 0 and 1, and two such workgroups do not fit).
+template <int D>
+__host__ __device__ constexpr int alpha_tpw() { return D == 96 ? 2 : 1; }
+template <int D>
+__host__ __device__ constexpr int alpha_waves() { return D / 16 / alpha_tpw<D>() + (alpha_tpw<D>() > 1 ? 1 : 0); }
+
+// One workgroup per (b, h, segment).  Tile wave w keeps column tiles
+// w TPW .. w TPW + TPW - 1 of A^T as fp32 accumulator tiles.
 template <typename IO, int D>
 __device__ __forceinline__ void vla_alpha_body(AlphaLds<D> &s, const VlaArgs &a, const float *__restrict__ Aseg,
                                                VlaChunk<D> *__restrict__ rec, int nseg, unsigned int *status) {
-    constexpr int NW = D / 16, NT = 64 * NW, NQ = D / 16;
+    constexpr int NW = D / 16, NQ = D / 16;
+    constexpr int TPW = alpha_tpw<D>(), NTW = NW / TPW, NWV = alpha_waves<D>(), NT = 64 * NWV;
+    constexpr int FW = TPW > 1 ? NTW : 0;  // the wave that runs the recurrence for F and forms Tc
     constexpr int DS = AlphaLds<D>::DS, TS = AlphaLds<D>::TS;
     constexpr int SEG = seg_len(D);
 
@@ -374,31 +386,38 @@ __device__ __forceinline__ void vla_alpha_body(AlphaLds<D> &s, const VlaArgs &a,
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, i = lane & 15;
     const int64_t sb = static_cast<int64_t>(head) * D * D;
-    const int col = 16 * w + i;  // this lane's column of the wave's tiles
+    const bool tiles = w < NTW;
+    // this lane's column of tile tw of the wave (clamped for the helper wave, which has none)
+    auto colof = [&](int tw) { return 16 * (min(w, NTW - 1) * TPW + tw) + i; };
     const int seg0 = sg * SEG, seg1 = min(T, seg0 + SEG);
     const int nch = (T + VC - 1) / VC;
     if (nseg == 1 && blockIdx.x == 0 && tid == 0) *status = 0u;  // first kernel of the call
 
-    // A^T column tile w: AT[q] = A^T[16q + 4g + r][col] = A[col][16q + 4g + r]
+    // A^T column tiles: AT[tw][q] = A^T[16q + 4g + r][col] = A[col][16q + 4g + r]
     const float *a0 = sg > 0 ? Aseg + (static_cast<int64_t>(head) * nseg + sg) * D * D
                              : (a.A_in ? a.A_in + sb : nullptr);
-    f32x4 AT[NQ];
+    f32x4 AT[TPW][NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        if (a0) {
-            const float4 x = *reinterpret_cast<const float4 *>(a0 + static_cast<int64_t>(col) * D + 16 * q + 4 * g);
-            AT[q] = f32x4{x.x, x.y, x.z, x.w};
-        } else {
-            f32x4 x;
+    for (int tw = 0; tw < TPW; ++tw) {
+        const int col = colof(tw);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = (16 * q + 4 * g + r == col) ? 1.f : 0.f;
-            AT[q] = x;
+        for (int q = 0; q < NQ; ++q) {
+            if (a0) {
+                const float4 x = *reinterpret_cast<const float4 *>(a0 + static_cast<int64_t>(col) * D + 16 * q + 4 * g);
+                AT[tw][q] = f32x4{x.x, x.y, x.z, x.w};
+            } else {
+                f32x4 x;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[r] = (16 * q + 4 * g + r == col) ? 1.f : 0.f;
+                AT[tw][q] = x;
+            }
         }
     }
 
     // raw inputs of one chunk staged in registers: element e = tid + NT * u of
     // each 16 x D tile (token e / D, channel e % D)
-    constexpr int EPT = VC * D / NT;  // = 4
+    constexpr int EPT = VC * D / NT;
+    static_assert(EPT * NT == VC * D, "staging covers the tile exactly");
     float rq[EPT], rk[EPT], rp[EPT];
     auto tok = [&](int t) { return ((static_cast<int64_t>(b) * T + t) * H + h) * D; };
     uint32_t eoff[EPT];
@@ -455,7 +474,9 @@ __device__ __forceinline__ void vla_alpha_body(AlphaLds<D> &s, const VlaArgs &a,
             *reinterpret_cast<f32x4 *>(&X[i * DS + 16 * q + 4 * g]) =
                 i < n ? f[q] * inv : f32x4{0.f, 0.f, 0.f, 0.f};
     };
-    constexpr int WQF = NW > 2 ? 2 : 1;  // wave mapping the queries during the recurrence
+    // waves mapping the next chunk's keys and queries during the recurrence
+    constexpr int WKF = FW == 1 ? 2 : 1;
+    constexpr int WQF = NWV > 2 ? (FW == 2 ? 3 : 2) : 1;
     if (seg0 < seg1) {
         fetch(seg0);
         stage(0, min(VC, seg1 - seg0));
@@ -474,28 +495,36 @@ __device__ __forceinline__ void vla_alpha_body(AlphaLds<D> &s, const VlaArgs &a,
         stage(nb, n1);
         fetch(c0 + 2 * VC);
         lds_sync();
-        // ---- products against the chunk-start inverse penalty (tile w):
+        // ---- products against the chunk-start inverse penalty (per tile):
         // Pa = P A^T, KA = Khat A^T (two accumulators each: even and odd
         // reduction steps, so the dependent chains are half as long)
         const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-        f32x4 pa, ka;
-        {
-            f32x4 pa2[2] = {zero4, zero4}, ka2[2] = {zero4, zero4};
+        f32x4 pa[TPW], ka[TPW];
+        if (tiles) {
+            f32x4 pa2[TPW][2], ka2[TPW][2];
+#pragma unroll
+            for (int tw = 0; tw < TPW; ++tw) pa2[tw][0] = pa2[tw][1] = ka2[tw][0] = ka2[tw][1] = zero4;
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const f32x4 pr = lds4(&P[i * DS + 16 * q + 4 * g]);
                 const f32x4 kr = lds4(&KH[i * DS + 16 * q + 4 * g]);
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    pa2[m & 1] = mfma4(pr[m], AT[q][m], pa2[m & 1]);
-                    ka2[m & 1] = mfma4(kr[m], AT[q][m], ka2[m & 1]);
-                }
-            }
-            pa = pa2[0] + pa2[1];
-            ka = ka2[0] + ka2[1];
-        }
+                for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s.pa[(4 * g + r) * DS + col] = pa[r];
+                    for (int tw = 0; tw < TPW; ++tw) {
+                        pa2[tw][m & 1] = mfma4(pr[m], AT[tw][q][m], pa2[tw][m & 1]);
+                        ka2[tw][m & 1] = mfma4(kr[m], AT[tw][q][m], ka2[tw][m & 1]);
+                    }
+            }
+#pragma unroll
+            for (int tw = 0; tw < TPW; ++tw) {
+                pa[tw] = pa2[tw][0] + pa2[tw][1];
+                ka[tw] = ka2[tw][0] + ka2[tw][1];
+                const int col = colof(tw);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s.pa[(4 * g + r) * DS + col] = pa[tw][r];
+            }
+        }
         lds_sync();
         // ---- Pa X^T (16 x 32), waves 0 and 1: column c of it stored as row c of g0t
         if (w < 2) {
@@ -513,8 +542,8 @@ __device__ __forceinline__ void vla_alpha_body(AlphaLds<D> &s, const VlaArgs &a,
             *reinterpret_cast<f32x4 *>(&s.g0t[(16 * w + i) * TS + 4 * g]) = g0;
         }
         lds_sync();
-        // ---- wave 0: the recurrence for F, then Z's coefficients inverted
-        if (w == 0) {
+        // ---- wave FW: the recurrence for F, then Z's coefficients inverted
+        if (w == FW) {
             // lane c < 32 keeps column c of F: F[s] = F_s[c].  Right-looking:
             // once F_s is final, its term -c_ts F_s (c_ts = F_s[p_t] / D_s,
             // column t of F_s, held by lane t) goes into every later row at
@@ -560,55 +589,70 @@ __device__ __forceinline__ void vla_alpha_body(AlphaLds<D> &s, const VlaArgs &a,
             unit_lower_inverse(s.lt, s.wop, lane);
         } else {
             // meanwhile other waves map the features of chunk c + 1
-            if (w == 1) features(s.kh[nb], n1);
+            if (w == WKF) features(s.kh[nb], n1);
             if (w == WQF) features(s.qh[nb], n1);
         }
         lds_sync();
-        // ---- Z = (I + C)^{-1} Pa, N = KA - E Z (tile w); Z^T to LDS; |N_t|^2 partials
-        f32x4 z = {0.f, 0.f, 0.f, 0.f}, nn = ka;
-        {
+        // ---- Z = (I + C)^{-1} Pa, N = KA - E Z (per tile); Z^T to LDS; |N_t|^2 partials
+        f32x4 z[TPW], nn[TPW];
+        if (tiles) {
             const f32x4 wa = s.wop[lane];
             const f32x4 ea = lds4(&s.e[i * TS + 4 * g]);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) z = mfma4(wa[m], pa[m], z);
+            for (int tw = 0; tw < TPW; ++tw) {
+                z[tw] = zero4;
+                nn[tw] = ka[tw];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) nn = mfma4(-ea[m], z[m], nn);
-        }
-        *reinterpret_cast<f32x4 *>(&s.zt[col * TS + 4 * g]) = z;
+                for (int m = 0; m < 4; ++m) z[tw] = mfma4(wa[m], pa[tw][m], z[tw]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float sq = group_sum<16>(nn[r] * nn[r]);
-            if (i == 0) s.part[w][4 * g + r] = sq;
-        }
-        lds_sync();
-        // ---- alphahat (tile w) to LDS by rows and to the record; A^T -= Z^T D^{-1} Z
-        f32x4 ah;
+                for (int m = 0; m < 4; ++m) nn[tw] = mfma4(-ea[m], z[tw][m], nn[tw]);
+                const int col = colof(tw);
+                *reinterpret_cast<f32x4 *>(&s.zt[col * TS + 4 * g]) = z[tw];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * g + r;
-            float ss = 0.f;
-#pragma unroll
-            for (int u = 0; u < NW; ++u) ss += s.part[u][t];
-            ah[r] = nn[r] * (t < n ? __builtin_amdgcn_rsqf(ss) : 0.f);
-            s.ah[t * DS + col] = ah[r];
-        }
-        R.aht[w][lane] = ah;
-        {
-            const f32x4 rd4 = lds4(&s.rd[4 * g]);
-            f32x4 zd;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) zd[r] = -z[r] * rd4[r];
-            // B operand at step m: (D^{-1} Z)[4g + m][col] -- held by lane (g, i) as zd[m]
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                const f32x4 za = lds4(&s.zt[(16 * q + i) * TS + 4 * g]);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) AT[q] = mfma4(za[m], zd[m], AT[q]);
+                for (int r = 0; r < 4; ++r) {
+                    const float sq = group_sum<16>(nn[tw][r] * nn[tw][r]);
+                    if (i == 0) s.part[w * TPW + tw][4 * g + r] = sq;
+                }
             }
         }
         lds_sync();
-        // ---- wave 0: strict(Khat Ahat^T) by column, inverted; wave 1: lower(Qhat Ahat^T)
-        if (w == 0) {
+        // ---- alphahat (per tile) to LDS by rows and to the record; A^T -= Z^T D^{-1} Z
+        if (tiles) {
+            float rn[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g + r;
+                float ss = 0.f;
+#pragma unroll
+                for (int u = 0; u < NW; ++u) ss += s.part[u][t];
+                rn[r] = t < n ? __builtin_amdgcn_rsqf(ss) : 0.f;
+            }
+            const f32x4 rd4 = lds4(&s.rd[4 * g]);
+#pragma unroll
+            for (int tw = 0; tw < TPW; ++tw) {
+                const int col = colof(tw);
+                f32x4 ah;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    ah[r] = nn[tw][r] * rn[r];
+                    s.ah[(4 * g + r) * DS + col] = ah[r];
+                }
+                R.aht[w * TPW + tw][lane] = ah;
+                f32x4 zd;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zd[r] = -z[tw][r] * rd4[r];
+                // B operand at step m: (D^{-1} Z)[4g + m][col] -- held by lane (g, i) as zd[m]
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const f32x4 za = lds4(&s.zt[(16 * q + i) * TS + 4 * g]);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) AT[tw][q] = mfma4(za[m], zd[m], AT[tw][q]);
+                }
+            }
+        }
+        lds_sync();
+        // ---- wave FW: strict(Khat Ahat^T) by column, inverted; wave 1: lower(Qhat Ahat^T)
+        if (w == FW) {
             f32x4 km2[2] = {zero4, zero4};
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
@@ -644,33 +688,39 @@ __device__ __forceinline__ void vla_alpha_body(AlphaLds<D> &s, const VlaArgs &a,
             s.aq[lane] = aq;
         }
         lds_sync();
-        // ---- the state step's operands (tile w): Ktil = Tc Khat, Qtil = Qhat - Aq Ktil
+        // ---- the state step's operands (per tile): Ktil = Tc Khat, Qtil = Qhat - Aq Ktil
         {
             const f32x4 tc = s.top[lane], aqv = s.aq[lane];
-            // B operand at step m: Khat[4g + m][col]
-            f32x4 kb, qb;
+            if (tiles) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                kb[r] = KH[(4 * g + r) * DS + col];
-                qb[r] = QH[(4 * g + r) * DS + col];
-            }
-            f32x4 k0 = mfma4(tc[0], kb[0], zero4), k1 = mfma4(tc[1], kb[1], zero4);
-            k0 = mfma4(tc[2], kb[2], k0);
-            k1 = mfma4(tc[3], kb[3], k1);
-            const f32x4 kt = k0 + k1;  // lane (g, i): Ktil[4g + r][col], the B operand of Aq Ktil
-            f32x4 q0 = qb, q1 = zero4;
-            q0 = mfma4(-aqv[0], kt[0], q0);
-            q1 = mfma4(-aqv[1], kt[1], q1);
-            q0 = mfma4(-aqv[2], kt[2], q0);
-            q1 = mfma4(-aqv[3], kt[3], q1);
-            const f32x4 qt = q0 + q1;
+                for (int tw = 0; tw < TPW; ++tw) {
+                    const int col = colof(tw);
+                    // B operand at step m: Khat[4g + m][col]
+                    f32x4 kb, qb;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                R.kt[(4 * g + r) * D + col] = kt[r];
-                R.qt[(4 * g + r) * D + col] = qt[r];
+                    for (int r = 0; r < 4; ++r) {
+                        kb[r] = KH[(4 * g + r) * DS + col];
+                        qb[r] = QH[(4 * g + r) * DS + col];
+                    }
+                    f32x4 k0 = mfma4(tc[0], kb[0], zero4), k1 = mfma4(tc[1], kb[1], zero4);
+                    k0 = mfma4(tc[2], kb[2], k0);
+                    k1 = mfma4(tc[3], kb[3], k1);
+                    const f32x4 kt = k0 + k1;  // lane (g, i): Ktil[4g + r][col], the B operand of Aq Ktil
+                    f32x4 q0 = qb, q1 = zero4;
+                    q0 = mfma4(-aqv[0], kt[0], q0);
+                    q1 = mfma4(-aqv[1], kt[1], q1);
+                    q0 = mfma4(-aqv[2], kt[2], q0);
+                    q1 = mfma4(-aqv[3], kt[3], q1);
+                    const f32x4 qt = q0 + q1;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        R.kt[(4 * g + r) * D + col] = kt[r];
+                        R.qt[(4 * g + r) * D + col] = qt[r];
+                    }
+                }
             }
             if (w == 0) R.top[lane] = tc;
-            if (w == NW - 1) {
+            if (w == (TPW > 1 ? FW : NW - 1)) {
                 // (Aq Tc)^T = Tc^T Aq^T: A operand Tc^T (lane (g, i) step m:
                 // Tc[4g + m][i]), B operand Aq^T (step m: Aq[i][4g + m], the
                 // A-order aq); the product lands in Aq Tc's A-operand order
@@ -688,21 +738,28 @@ __device__ __forceinline__ void vla_alpha_body(AlphaLds<D> &s, const VlaArgs &a,
         lds_sync();  // chunk tiles free for the next chunk
     }
 
-    if (a.A_out && seg1 == T) {
+    if (a.A_out && seg1 == T && tiles) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
-            *reinterpret_cast<float4 *>(a.A_out + sb + static_cast<int64_t>(col) * D + 16 * q + 4 * g) =
-                make_float4(AT[q][0], AT[q][1], AT[q][2], AT[q][3]);
+        for (int tw = 0; tw < TPW; ++tw) {
+            const int col = colof(tw);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                *reinterpret_cast<float4 *>(a.A_out + sb + static_cast<int64_t>(col) * D + 16 * q + 4 * g) =
+                    make_float4(AT[tw][q][0], AT[tw][q][1], AT[tw][q][2], AT[tw][q][3]);
+        }
     }
 }
 
+// Two waves per SIMD: with D = 96's four-wave workgroups, two workgroups per
+// compute unit (the other sizes need no more than 256 registers anyway).
 template <typename IO, int D>
-__global__ __launch_bounds__(64 * (D / 16)) void vla_alpha_kernel(VlaArgs a, const float *__restrict__ Aseg,
-                                                                   VlaChunk<D> *__restrict__ rec, int nseg,
-                                                                   unsigned int *status) {
+__global__ __launch_bounds__(64 * alpha_waves<D>()) __attribute__((amdgpu_waves_per_eu(2))) void vla_alpha_kernel(VlaArgs a, const float *__restrict__ Aseg,
+                                                                          VlaChunk<D> *__restrict__ rec, int nseg,
+                                                                          unsigned int *status) {
     __shared__ AlphaLds<D> s;
     vla_alpha_body<IO, D>(s, a, Aseg, rec, nseg, status);
 }
+
 // ================================ state ================================
 // Carry waves of the state kernel: D/16, one 16 x 16 tile of S^T each; with
 // two carries (d = 32) a third wave forms the output on a free SIMD, and with
@@ -869,7 +926,7 @@ hipError_t launch_d(const VlaArgs &a, hipStream_t stream) {
         vla_gram_kernel<IO, D><<<heads * (nseg - 1), 64 * (D / 16), 0, stream>>>(a, G, nseg, status);
         vla_inverse_kernel<D><<<heads * (nseg - 1), 256, 0, stream>>>(a, G, Aseg, nseg);
     }
-    vla_alpha_kernel<IO, D><<<heads * nseg, 64 * (D / 16), 0, stream>>>(a, Aseg, rec, nseg, status);
+    vla_alpha_kernel<IO, D><<<heads * nseg, 64 * alpha_waves<D>(), 0, stream>>>(a, Aseg, rec, nseg, status);
     vla_state_kernel<IO, D><<<heads * (D / 16), 64 * state_waves<D>(), 0, stream>>>(a, rec);
     return hipGetLastError();
 }
