@@ -312,6 +312,11 @@ __global__ __launch_bounds__(kMlpThreads) void loglin_lambda_kernel(int64_t M, i
     __shared__ f32x4v w1t[kLogLinMaxHidden][NLP / 4];  // w1t[j][l] = W1[l][j]
     __shared__ f32x4v w2s[kLogLinMaxHidden][NLP / 4];  // w2s[j][l] = W2[j][l]
     __shared__ float bs[NLP];
+    // The workgroup's rows (inputs, then outputs) pass through LDS, so that
+    // global loads and stores run over consecutive addresses.  Thread t owns
+    // the nL words of row t: for odd nL the lanes' accesses to one level hit
+    // distinct banks, for even nL a few share one.
+    __shared__ float io[kMlpThreads * NLP];
     float *w1f = reinterpret_cast<float *>(w1t), *w2f = reinterpret_cast<float *>(w2s);
     for (int e = threadIdx.x; e < nh * NLP; e += kMlpThreads) {
         const int jj = e / NLP, l = e % NLP;
@@ -319,13 +324,17 @@ __global__ __launch_bounds__(kMlpThreads) void loglin_lambda_kernel(int64_t M, i
         w2f[e] = l < nL ? W2[jj * nL + l] : 0.f;
     }
     if (threadIdx.x < NLP) bs[threadIdx.x] = threadIdx.x < nL ? bias[threadIdx.x] : 0.f;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kMlpThreads;
+    const int nrows = static_cast<int>(min(static_cast<int64_t>(kMlpThreads), M - r0));
+    const int ne = nrows * nL;
+    for (int e = threadIdx.x; e < ne; e += kMlpThreads) io[e] = IO::ld(d, r0 * nL + e);
     __syncthreads();
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * kMlpThreads + threadIdx.x;
-    if (r >= M) return;
+    const int t = threadIdx.x;
+    const bool live = t < nrows;
     float x[NLP], o[NLP];
 #pragma unroll
     for (int l = 0; l < NLP; ++l) {
-        x[l] = l < nL ? IO::ld(d, r * nL + l) : 0.f;
+        x[l] = (l < nL && live) ? io[t * nL + l] : 0.f;
         o[l] = bs[l];
     }
     // h = d W1 one hidden unit at a time, folded straight into h W2
@@ -346,10 +355,15 @@ __global__ __launch_bounds__(kMlpThreads) void loglin_lambda_kernel(int64_t M, i
             for (int e = 0; e < 4; ++e) o[4 * q + e] = fmaf(hj, w[e], o[4 * q + e]);
         }
     }
-    // softplus(x) = max(x, 0) + log1p(exp(-|x|))
+    // softplus(x) = max(x, 0) + log1p(exp(-|x|)), through LDS to the output
+    __syncthreads();  // every row's inputs read before io is overwritten
+    if (live) {
 #pragma unroll
-    for (int l = 0; l < NLP; ++l)
-        if (l < nL) lam[r * nL + l] = fmaxf(o[l], 0.f) + log1pf(expf(-fabsf(o[l])));
+        for (int l = 0; l < NLP; ++l)
+            if (l < nL) io[t * nL + l] = fmaxf(o[l], 0.f) + log1pf(expf(-fabsf(o[l])));
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < ne; e += kMlpThreads) lam[r0 * nL + e] = io[e];
 }
 
 template <typename IO>
