@@ -74,6 +74,8 @@ def _lib(prec: str = "f64") -> ctypes.CDLL:
             lib.oracle_delta_forward_side.restype = ctypes.c_int
             lib.oracle_vla_forward.argtypes = [L, L, L, L] + [dp] * 13 + [ctypes.c_int]
             lib.oracle_vla_forward.restype = ctypes.c_int
+            lib.oracle_vla_forward_ratio.argtypes = [L, L, L, L] + [dp] * 11 + [ctypes.c_int]
+            lib.oracle_vla_forward_ratio.restype = ctypes.c_int
             lib.oracle_delta_backward.argtypes = [ctypes.c_int, L, L, L, L, L] + [dp] * 18 + [ctypes.c_int]
             lib.oracle_delta_backward.restype = ctypes.c_int
             lib.oracle_loglinear_forward.argtypes = [ctypes.c_int, L, L, L, L, L, L, L] + [dp] * 11 + [ctypes.c_int]
@@ -301,6 +303,32 @@ def vla_forward(q, k, v, p, A_in=None, S_in=None, diagnostics=False, nthreads=0,
     if diagnostics:
         return out, A_out, S_out, diag
     return out, A_out, S_out
+
+
+def vla_forward_ratio(q, k, v, p, A_in=None, S_in=None, n_in=None, nthreads=0, precision="f64"):
+    """VLA forward scan with the output read as a ratio of two recurrences:
+    the state S and a d-vector n that follows the same write rule with the
+    value 1, y = (S q-hat) / (n . q-hat).
+
+    q, k, v, p: [B,T,H,d]; A_in, S_in: [B,H,d,d] or None (identity, zero);
+    n_in: [B,H,d] or None (zero).  Returns (out, A_out, S_out, n_out).
+    """
+    q = _in(q)
+    B, T, H, d = q.shape
+    k, v, p = (_in(x, (B, T, H, d)) for x in (k, v, p))
+    A_in = _in(A_in, (B, H, d, d))
+    S_in = _in(S_in, (B, H, d, d))
+    n_in = _in(n_in, (B, H, d))
+    out = np.zeros((B, T, H, d), np.float64)
+    A_out = np.zeros((B, H, d, d), np.float64)
+    S_out = np.zeros((B, H, d, d), np.float64)
+    n_out = np.zeros((B, H, d), np.float64)
+    rc = _lib(precision).oracle_vla_forward_ratio(
+        B, T, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(p), _ptr(A_in), _ptr(S_in), _ptr(n_in), _ptr(out),
+        _ptr(A_out), _ptr(S_out), _ptr(n_out), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_vla_forward_ratio failed")
+    return out, A_out, S_out, n_out
 
 
 def real_bytes(precision="f64") -> int:

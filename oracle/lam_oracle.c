@@ -526,6 +526,122 @@ static void vla_chain(long b, long h, long T, long H, long d, const double *q,
 }
 
 /*
+ * VLA with the output read as a ratio of two recurrences, one (b, h) chain
+ * ([VLA] section 2.3: the output is a ratio of recurrences as in standard
+ * linear attention).  In linear attention the numerator and the denominator
+ * accumulate the same way, the denominator over a value of 1; here the
+ * denominator is a d-vector n that follows rule 3 with the value 1
+ * (reading X7), and the read divides:
+ *   rules 1-2  as vla_chain
+ *   rule 3     S <- S + (v - S k-hat) alpha-hat^T,
+ *              n <- n + (1 - n . k-hat) alpha-hat
+ *   read       y = (S q-hat) / (n . q-hat)
+ * The steps are written out again here rather than shared with vla_chain.
+ */
+static void vla_ratio_chain(long b, long h, long T, long H, long d, const double *q,
+                            const double *k, const double *v, const double *p,
+                            const double *A_in, const double *S_in, const double *n_in,
+                            double *out, double *A_out, double *S_out, double *n_out,
+                            real *A, real *S, real *n, real *kh, real *qh, real *pp,
+                            real *z, real *a, real *r) {
+    const size_t s0 = st(b, h, H, d, d), n0 = st(b, h, H, d, 1);
+    for (long i = 0; i < d; ++i) {
+        for (long j = 0; j < d; ++j) {
+            A[i * d + j] = A_in ? (real)A_in[s0 + i * d + j] : (real)(i == j);
+            S[i * d + j] = S_in ? (real)S_in[s0 + i * d + j] : (real)0;
+        }
+        n[i] = n_in ? (real)n_in[n0 + i] : (real)0;
+    }
+    for (long t = 0; t < T; ++t) {
+        const size_t o = tok(b, t, h, T, H, d);
+        real nk = 0, nq = 0;
+        for (long j = 0; j < d; ++j) {
+            kh[j] = elu_plus_one((real)k[o + j]);
+            qh[j] = elu_plus_one((real)q[o + j]);
+            nk += kh[j] * kh[j];
+            nq += qh[j] * qh[j];
+        }
+        nk = (real)sqrt((double)nk);
+        nq = (real)sqrt((double)nq);
+        for (long j = 0; j < d; ++j) {
+            kh[j] /= nk;
+            qh[j] /= nq;
+            pp[j] = (real)p[o + j];
+        }
+        /* rule 1 */
+        real den = 1;
+        for (long i = 0; i < d; ++i) {
+            real acc = 0;
+            for (long j = 0; j < d; ++j) acc += A[i * d + j] * pp[j];
+            z[i] = acc;
+        }
+        for (long i = 0; i < d; ++i) den += pp[i] * z[i];
+        for (long i = 0; i < d; ++i)
+            for (long j = 0; j < d; ++j) A[i * d + j] -= z[i] * z[j] / den;
+        /* rule 2 */
+        real na = 0;
+        for (long i = 0; i < d; ++i) {
+            real acc = 0;
+            for (long j = 0; j < d; ++j) acc += A[i * d + j] * kh[j];
+            a[i] = acc;
+            na += acc * acc;
+        }
+        na = (real)sqrt((double)na);
+        for (long i = 0; i < d; ++i) a[i] /= na;
+        /* rule 3, for the values and for the constant 1 */
+        for (long i = 0; i < d; ++i) {
+            real acc = 0;
+            for (long j = 0; j < d; ++j) acc += S[i * d + j] * kh[j];
+            r[i] = (real)v[o + i] - acc;
+        }
+        for (long i = 0; i < d; ++i)
+            for (long j = 0; j < d; ++j) S[i * d + j] += r[i] * a[j];
+        real rn = 1;
+        for (long j = 0; j < d; ++j) rn -= n[j] * kh[j];
+        for (long j = 0; j < d; ++j) n[j] += rn * a[j];
+        /* read: the ratio */
+        real dq = 0;
+        for (long j = 0; j < d; ++j) dq += n[j] * qh[j];
+        for (long i = 0; i < d; ++i) {
+            real acc = 0;
+            for (long j = 0; j < d; ++j) acc += S[i * d + j] * qh[j];
+            out[o + i] = (double)(acc / dq);
+        }
+    }
+    if (A_out) for (long i = 0; i < d * d; ++i) A_out[s0 + i] = (double)A[i];
+    if (S_out) for (long i = 0; i < d * d; ++i) S_out[s0 + i] = (double)S[i];
+    if (n_out) for (long i = 0; i < d; ++i) n_out[n0 + i] = (double)n[i];
+}
+
+/*
+ * oracle_vla_forward_ratio: VLA with the ratio read over a [B,T] block.
+ * Layouts as oracle_vla_forward, plus the denominator state n_in / n_out
+ * [B,H,d] (NULL n_in = zero, NULL n_out = not written).
+ * Returns 0, or -1 on a bad argument or allocation failure.
+ */
+int oracle_vla_forward_ratio(long B, long T, long H, long d, const double *q,
+                             const double *k, const double *v, const double *p,
+                             const double *A_in, const double *S_in, const double *n_in,
+                             double *out, double *A_out, double *S_out, double *n_out,
+                             int nthreads) {
+    if (B < 0 || T < 0 || H < 0 || d <= 0) return -1;
+    if (!q || !k || !v || !p || !out) return -1;
+    const long chains = B * H;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads()) \
+    reduction(| : failed)
+    for (long c = 0; c < chains; ++c) {
+        real *buf = (real *)malloc(sizeof(real) * (size_t)(2 * d * d + 7 * d));
+        if (!buf) { failed = 1; continue; }
+        real *A = buf, *S = buf + d * d, *w = buf + 2 * d * d;
+        vla_ratio_chain(c / H, c % H, T, H, d, q, k, v, p, A_in, S_in, n_in, out, A_out, S_out,
+                        n_out, A, S, w, w + d, w + 2 * d, w + 3 * d, w + 4 * d, w + 5 * d, w + 6 * d);
+        free(buf);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
  * oracle_vla_forward: VLA over a [B,T] block, dk = dv = d.
  * Layouts: q, k, v, p, out [B,T,H,d]; A_in/A_out/S_in/S_out [B,H,d,d]
  * (NULL A_in = identity, NULL S_in = zero, NULL outs = not written).

@@ -80,5 +80,5 @@ def test_oracle_pins_under_asan_ubsan():
                ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1",
                OMP_NUM_THREADS="4")
     r = _run([sys.executable, "-m", "pytest", "-q", "-s", "-p", "no:cacheprovider", "tests/test_oracle_pins.py",
-              "tests/test_golden.py"], env=env)
+              "tests/test_golden.py", "tests/test_oracle_vla_ratio.py"], env=env)
     assert " passed" in r.stdout and "failed" not in r.stdout, r.stdout[-2000:]
