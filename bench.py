@@ -40,9 +40,12 @@ FP32_PEAK_TFS = 157.3
 def algorithmic_bytes(w, decode=False) -> int:
     """Every input read once, out and the final state written once (no
     initial state), in the storage dtype.  A decode step also reads the
-    state it updates."""
+    state it updates (VLA's decode step, with the ratio read: A, S and the
+    denominator n, each read and written)."""
     es = 2 if w.dtype == "bf16" else 4
     n_th = w.B * w.T * w.H
+    if decode and w.variant == "vla":
+        return n_th * 5 * w.dk * es + 2 * w.B * w.H * (2 * w.dk * w.dk + w.dk) * 4
     if decode:
         return algorithmic_bytes(w) + w.B * w.H * w.dv * w.dk * 4
     if w.variant == "vla":
@@ -143,6 +146,7 @@ KERNEL_SOURCES = {  # schedule -> kernel source per variant family
     ("recurrent", "kda"): "delta_recurrent.hip",
     ("recurrent", "vla"): "vla_recurrent.hip",
     ("step", "delta"): "delta_step.hip",
+    ("step", "vla"): "vla_recurrent.hip",
     ("backward", "delta"): "delta_backward.hip",
     ("route", "delta"): "route.hip",
     ("loglinear", "delta"): "loglin_recurrent.hip",
@@ -212,7 +216,10 @@ def cpu_baseline(w, x, batch_rows: int, min_seconds: float):
     reps, dt = 0, 0.0
     while reps == 0 or dt < min_seconds:
         t0 = time.perf_counter()
-        if w.variant == "vla":
+        if w.variant == "vla" and "n_in" in sl:  # decode with the ratio read, from the same states
+            oracle.vla_forward_ratio(sl["q"], sl["k"], sl["v"], sl["p"], A_in=sl["A_in"], S_in=sl["S_in"],
+                                     n_in=sl["n_in"], nthreads=th)
+        elif w.variant == "vla":
             oracle.vla_forward(sl["q"], sl["k"], sl["v"], sl["p"], nthreads=th)
         else:
             oracle.delta_forward(w.variant, sl["q"], sl["k"], sl["v"], sl["beta"], alpha=sl.get("alpha"),
@@ -342,6 +349,10 @@ def main():
         copies = [{n: t[:, 0].contiguous() for n, t in g.items()} for g in copies]
         s0 = np.random.default_rng(w.seed).standard_normal((w.B, w.H, w.dv, w.dk)) * 0.1
         x["state_in"] = s0.astype(np.float32).astype(np.float64)
+        if w.variant == "vla":  # fresh penalty, a loaded memory and denominator
+            x["A_in"] = np.broadcast_to(np.eye(w.dk), (w.B, w.H, w.dk, w.dk)).copy()
+            x["S_in"] = x.pop("state_in")
+            x["n_in"] = np.full((w.B, w.H, w.dk), 0.8 / np.sqrt(w.dk))
     outs = []
     for g in copies:
         if kind == "backward":
@@ -368,6 +379,10 @@ def main():
             g["W2"] = torch.from_numpy((jr.standard_normal((nh, nL)) * 0.3).astype(np.float32)).to(dev)
             g["b"] = torch.full((nL,), 0.54, dtype=torch.float32, device=dev)
             outs.append(torch.empty((w.B, w.T, w.H, nL), dtype=torch.float32, device=dev))
+        elif decode and w.variant == "vla":
+            f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+            outs.append((torch.empty((w.B, w.H, w.dv), dtype=g["q"].dtype, device=dev),
+                         f32(x["A_in"]), f32(x["S_in"]), f32(x["n_in"])))
         elif decode:
             outs.append((torch.empty((w.B, w.H, w.dv), dtype=g["q"].dtype, device=dev),
                          torch.from_numpy(x["state_in"].astype(np.float32)).to(dev)))
@@ -407,6 +422,8 @@ def main():
                                   erase_b=g.get("erase_b"), write_w=g.get("write_w"), out=o[0], state_out=o[1])
         elif kind == "lambda":
             lam.loglinear_lambda(g["d"], g["W1"], g["W2"], g["b"], out=o)
+        elif decode and w.variant == "vla":
+            lam.vla_step_ratio(g["q"], g["k"], g["v"], g["p"], o[1], o[2], o[3], out=o[0])
         elif decode:
             lam.step(w.variant, g["q"], g["k"], g["v"], g["beta"], alpha=g.get("alpha"),
                      erase_b=g.get("erase_b"), write_w=g.get("write_w"), state=o[1], out=o[0])
@@ -545,7 +562,8 @@ def main():
     line = {
         "metric": "gated delta-rule fwd tokens/s, B8 T4096 H8 d128; % of HBM/MFMA roofline"
         if name == I.METRIC_WORKLOAD else (job_metric[kind] if job else
-                                           (f"{w.variant} decode tokens/s (one token per stream per call), {name}"
+                                           (f"{w.variant} decode tokens/s (one token per stream per call"
+                                            f"{', ratio read' if w.variant == 'vla' else ''}), {name}"
                                             if decode else f"{w.variant} fwd tokens/s, {name}")),
         "value": value,
         "unit": "tokens/s",

@@ -101,6 +101,10 @@ def library() -> ctypes.CDLL:
             lib.lam_step.restype = ci
             lib.lam_vla_step.argtypes = [ci, i64, i64, i64] + [vp] * 7 + [vp]
             lib.lam_vla_step.restype = ci
+            lib.lam_vla_forward_ratio.argtypes = [ci, i64, i64, i64, i64] + [vp] * 11 + [vp]
+            lib.lam_vla_forward_ratio.restype = ci
+            lib.lam_vla_step_ratio.argtypes = [ci, i64, i64, i64] + [vp] * 8 + [vp]
+            lib.lam_vla_step_ratio.restype = ci
             lib.lam_status_string.argtypes = [ci]
             lib.lam_status_string.restype = ctypes.c_char_p
             lib.lam_abi_version.restype = ci
@@ -489,6 +493,46 @@ def vla_forward(q, k, v, p, A_in=None, S_in=None, *, algo="auto", out=None, A_ou
     return out, A_out, S_out
 
 
+def vla_forward_ratio(q, k, v, p, A_in=None, S_in=None, n_in=None, *, out=None, A_out=None, S_out=None,
+                      n_out=None, stream=None):
+    """VLA forward scan with the output read as a ratio of two recurrences:
+    the denominator n [B,H,d] follows the write rule with the value 1 and
+    y = (S qhat) / (n . qhat) (token-recurrent kernel).
+
+    q, k, v, p: [B,T,H,d] (float32 or bfloat16); A_in, S_in: fp32 [B,H,d,d]
+    or None (identity, zero); n_in: fp32 [B,H,d] or None (zero).  Returns
+    (out, A_out, S_out, n_out).
+    """
+    import torch
+
+    B, T, H, d = q.shape
+    dt, dev = q.dtype, q.device
+    for n, t in (("q", q), ("k", k), ("v", v), ("p", p)):
+        _check(t, n, (B, T, H, d), dt, dev)
+    for n, t in (("A_in", A_in), ("S_in", S_in)):
+        _check(t, n, (B, H, d, d), torch.float32, dev)
+    _check(n_in, "n_in", (B, H, d), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, d), dtype=dt, device=dev)
+    _check(out, "out", (B, T, H, d), dt, dev)
+    if A_out is None:
+        A_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    if S_out is None:
+        S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    if n_out is None:
+        n_out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    for n, t in (("A_out", A_out), ("S_out", S_out)):
+        _check(t, n, (B, H, d, d), torch.float32, dev)
+    _check(n_out, "n_out", (B, H, d), torch.float32, dev)
+    rc = library().lam_vla_forward_ratio(_dtype_code(q), B, T, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(p),
+                                         _ptr(A_in), _ptr(S_in), _ptr(n_in), _ptr(out), _ptr(A_out),
+                                         _ptr(S_out), _ptr(n_out), _stream(stream))
+    if rc != 0:
+        raise LamError(rc, "lam_vla_forward_ratio")
+    _after_call(None, "lam_vla_forward_ratio")
+    return out, A_out, S_out, n_out
+
+
 def step(variant, q, k, v, beta, alpha=None, erase_b=None, write_w=None, *, state, out=None,
          stream=None):
     """One-token decode step for N streams, the memory updated in place.
@@ -554,4 +598,30 @@ def vla_step(q, k, v, p, A, S, *, out=None, stream=None):
     if rc != 0:
         raise LamError(rc, "lam_vla_step")
     _after_call(None, "lam_vla_step")
+    return out
+
+
+def vla_step_ratio(q, k, v, p, A, S, n, *, out=None, stream=None):
+    """One-token VLA step with the ratio read for N streams: q, k, v, p
+    [N,H,d]; A, S fp32 [N,H,d,d] and the denominator n fp32 [N,H,d] updated in
+    place.  Returns out [N,H,d]."""
+    import torch
+
+    N, H, d = q.shape
+    dt, dev = q.dtype, q.device
+    for nm, t in (("q", q), ("k", k), ("v", v), ("p", p)):
+        _check(t, nm, (N, H, d), dt, dev)
+    if A is None or S is None or n is None:
+        raise ValueError("A, S and n: required (updated in place)")
+    _check(A, "A", (N, H, d, d), torch.float32, dev)
+    _check(S, "S", (N, H, d, d), torch.float32, dev)
+    _check(n, "n", (N, H, d), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, d), dtype=dt, device=dev)
+    _check(out, "out", (N, H, d), dt, dev)
+    rc = library().lam_vla_step_ratio(_dtype_code(q), N, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(p), _ptr(A),
+                                      _ptr(S), _ptr(n), _ptr(out), _stream(stream))
+    if rc != 0:
+        raise LamError(rc, "lam_vla_step_ratio")
+    _after_call(None, "lam_vla_step_ratio")
     return out

@@ -492,6 +492,67 @@ lam_status lam_vla_step(int dtype, int64_t N, int64_t H, int64_t d, const void *
                            LAM_ALGO_RECURRENT, stream);
 }
 
+lam_status lam_vla_forward_ratio(int dtype, int64_t B, int64_t T, int64_t H, int64_t d, const void *q,
+                                 const void *k, const void *v, const void *p, const float *A_in,
+                                 const float *S_in, const float *n_in, void *out, float *A_out, float *S_out,
+                                 float *n_out, hipStream_t stream) {
+    lam_status st = check_vla_shape(dtype, B, T, H, d, LAM_ALGO_RECURRENT);
+    if (st != LAM_OK) return st;
+    if (B == 0 || H == 0) return LAM_OK;
+    int64_t n, nst;
+    elems(B, T, H, d, n);
+    elems(B, 1, H, d * d, nst);
+    const int64_t nnb = B * H * d * 4;  // bytes of n
+    if (T > 0 && (!q || !k || !v || !p || !out)) return LAM_ERR_INVALID_ARG;
+    const int64_t es = dtype == LAM_BF16 ? 2 : 4;
+    const int64_t ob = n * es;
+    const void *all[] = {q, k, v, p, A_in, S_in, n_in, A_out, S_out, n_out};
+    const int64_t all_b[] = {ob, ob, ob, ob, nst * 4, nst * 4, nnb, nst * 4, nst * 4, nnb};
+    for (int i = 0; i < 10; ++i)
+        if (overlaps(out, ob, all[i], all_b[i])) return LAM_ERR_INVALID_ARG;
+    const float *ins[3] = {A_in, S_in, n_in};
+    const int64_t in_b[3] = {nst * 4, nst * 4, nnb};
+    float *outs[3] = {A_out, S_out, n_out};
+    const int64_t out_b[3] = {nst * 4, nst * 4, nnb};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 3; ++i)  // an output may be its own input's buffer, nothing else
+            if (outs[o] && ins[i] && !(o == i && outs[o] == ins[i]) && overlaps(outs[o], out_b[o], ins[i], in_b[i]))
+                return LAM_ERR_INVALID_ARG;
+        for (int o2 = o + 1; o2 < 3; ++o2)
+            if (outs[o] && outs[o2] && overlaps(outs[o], out_b[o], outs[o2], out_b[o2])) return LAM_ERR_INVALID_ARG;
+    }
+    if (T == 0 && !A_out && !S_out && !n_out) return LAM_OK;
+    lam::VlaArgs a{};
+    a.dtype = dtype;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.d = static_cast<int>(d);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.p = p;
+    a.A_in = A_in;
+    a.S_in = S_in;
+    a.out = out;
+    a.A_out = A_out;
+    a.S_out = S_out;
+    a.ratio = true;
+    a.n_in = n_in;
+    a.n_out = n_out;
+    return from_hip(lam::launch_vla_recurrent(a, stream));
+}
+
+lam_status lam_vla_step_ratio(int dtype, int64_t N, int64_t H, int64_t d, const void *q, const void *k,
+                              const void *v, const void *p, float *A, float *S, float *n, void *out,
+                              hipStream_t stream) {
+    lam_status st = check_vla_shape(dtype, N, 1, H, d, LAM_ALGO_RECURRENT);
+    if (st != LAM_OK) return st;
+    if (N == 0 || H == 0) return LAM_OK;
+    if (!A || !S || !n) return LAM_ERR_INVALID_ARG;
+    return lam_vla_forward_ratio(dtype, N, 1, H, d, q, k, v, p, A, S, n, out, A, S, n, stream);
+}
+
 lam_status lam_vla_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, int64_t d, int algo,
                                   size_t *bytes) {
     if (!bytes) return LAM_ERR_INVALID_ARG;

@@ -40,6 +40,10 @@ struct VlaArgs {
     void *out;
     float *A_out, *S_out;
     void *ws;
+    // ratio read (token-recurrent kernel only): the denominator state [B,H,d]
+    bool ratio;
+    const float *n_in;
+    float *n_out;
 };
 
 // Size of the status block at the start of every workspace; the derived

@@ -16,6 +16,15 @@
 // exchange of z and alphahat through LDS finish the token.  Feature maps and
 // norms of a whole tile of keys and queries are computed up front with wave
 // reductions.
+//
+// Ratio read (RATIO): section 2.3 reads the output as a ratio of
+// recurrences, as in standard linear attention, where the denominator
+// accumulates like the numerator over a value of 1.  The denominator here is
+// a d-vector n that follows the write rule with the value 1,
+//   n <- n + (1 - n.khat) alphahat,   y = (S qhat) / (n.qhat),
+// and by the same algebra as y, n'.qhat = n.qhat + (1 - n.khat)(alphahat.qhat).
+// Every row group keeps its own copy of n (the columns of its lanes), so
+// n.khat and n.qhat are lane-group sums like the rows of S khat and S qhat.
 #include "device_common.h"
 #include "lam_internal.h"
 
@@ -37,7 +46,7 @@ struct VlaShape {
 
 __device__ __forceinline__ float elu_plus_one(float x) { return x > 0.f ? x + 1.f : expf(x); }
 
-template <typename IO, int D>
+template <typename IO, int D, bool RATIO>
 __global__ __launch_bounds__(VlaShape<D>::NT) void vla_recurrent_kernel(VlaArgs a) {
     using Sh = VlaShape<D>;
     constexpr int NW = Sh::NW, NT = Sh::NT, TPR = Sh::TPR, NRG = Sh::NRG, RPT = Sh::RPT,
@@ -62,6 +71,10 @@ __global__ __launch_bounds__(VlaShape<D>::NT) void vla_recurrent_kernel(VlaArgs 
             A[r][m] = a.A_in ? a.A_in[sb + i * D + j] : (i == j ? 1.f : 0.f);
             S[r][m] = a.S_in ? a.S_in[sb + i * D + j] : 0.f;
         }
+    const int64_t nb = (static_cast<int64_t>(b) * H + h) * D;
+    float nrow[CPT];
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) nrow[m] = (RATIO && a.n_in) ? a.n_in[nb + lr + TPR * m] : 0.f;
 
     constexpr int SLOTS = (TT * D + NT - 1) / NT;
     float rq[SLOTS], rk[SLOTS], rp[SLOTS], rv[SLOTS];
@@ -125,6 +138,7 @@ __global__ __launch_bounds__(VlaShape<D>::NT) void vla_recurrent_kernel(VlaArgs 
 
         for (int t = 0; t < nt; ++t) {
             float zp[RPT], wk[RPT], skr[RPT], sqr[RPT];
+            float nk = 0.f, nq = 0.f;  // n.khat, n.qhat (ratio read)
 #pragma unroll
             for (int r = 0; r < RPT; ++r) zp[r] = wk[r] = skr[r] = sqr[r] = 0.f;
 #pragma unroll
@@ -138,6 +152,10 @@ __global__ __launch_bounds__(VlaShape<D>::NT) void vla_recurrent_kernel(VlaArgs 
                     skr[r] = fmaf(S[r][m], kj, skr[r]);
                     sqr[r] = fmaf(S[r][m], qj, sqr[r]);
                 }
+                if constexpr (RATIO) {
+                    nk = fmaf(nrow[m], kj, nk);
+                    nq = fmaf(nrow[m], qj, nq);
+                }
             }
 #pragma unroll
             for (int r = 0; r < RPT; ++r) {
@@ -145,6 +163,10 @@ __global__ __launch_bounds__(VlaShape<D>::NT) void vla_recurrent_kernel(VlaArgs 
                 wk[r] = group_sum<TPR>(wk[r]);
                 skr[r] = group_sum<TPR>(skr[r]);
                 sqr[r] = group_sum<TPR>(sqr[r]);
+            }
+            if constexpr (RATIO) {
+                nk = group_sum<TPR>(nk);
+                nq = group_sum<TPR>(nq);
             }
             // row sums p.z and khat.z (one lane per row contributes)
             float pz = 0.f, kz = 0.f;
@@ -205,13 +227,15 @@ __global__ __launch_bounds__(VlaShape<D>::NT) void vla_recurrent_kernel(VlaArgs 
             }
             const float inv = 1.f / sqrtf(aa);
             const float ahq = aq * inv;
+            const float rn = 1.f - nk;                                // the denominator's residual
+            const float ry = RATIO ? 1.f / fmaf(rn, ahq, nq) : 1.f;  // 1 / (n'.qhat)
             float rr[RPT];
 #pragma unroll
             for (int r = 0; r < RPT; ++r) {
                 const int i = rg + NRG * r;
                 rr[r] = sv[t][i] - skr[r];
                 if (lr == 0) {
-                    sy[t][i] = fmaf(rr[r], ahq, sqr[r]);
+                    sy[t][i] = RATIO ? fmaf(rr[r], ahq, sqr[r]) * ry : fmaf(rr[r], ahq, sqr[r]);
                     sa[i] = av[r] * inv;
                 }
             }
@@ -231,6 +255,7 @@ __global__ __launch_bounds__(VlaShape<D>::NT) void vla_recurrent_kernel(VlaArgs 
                 const float aj = sa[lr + TPR * m];
 #pragma unroll
                 for (int r = 0; r < RPT; ++r) S[r][m] = fmaf(rr[r], aj, S[r][m]);
+                if constexpr (RATIO) nrow[m] = fmaf(rn, aj, nrow[m]);
             }
             __syncthreads();  // sz / sa / red slots free for the next token
         }
@@ -250,12 +275,20 @@ __global__ __launch_bounds__(VlaShape<D>::NT) void vla_recurrent_kernel(VlaArgs 
             if (a.A_out) a.A_out[sb + i * D + j] = A[r][m];
             if (a.S_out) a.S_out[sb + i * D + j] = S[r][m];
         }
+    if constexpr (RATIO) __syncthreads();  // every row group has read n_in (n_out may be the same buffer)
+    if (RATIO && a.n_out && rg == 0) {
+#pragma unroll
+        for (int m = 0; m < CPT; ++m) a.n_out[nb + lr + TPR * m] = nrow[m];
+    }
 }
 
 template <typename IO, int D>
 hipError_t launch_d(const VlaArgs &a, hipStream_t stream) {
     const unsigned blocks = static_cast<unsigned>(a.B * a.H);
-    vla_recurrent_kernel<IO, D><<<dim3(blocks), dim3(VlaShape<D>::NT), 0, stream>>>(a);
+    if (a.ratio)
+        vla_recurrent_kernel<IO, D, true><<<dim3(blocks), dim3(VlaShape<D>::NT), 0, stream>>>(a);
+    else
+        vla_recurrent_kernel<IO, D, false><<<dim3(blocks), dim3(VlaShape<D>::NT), 0, stream>>>(a);
     return hipGetLastError();
 }
 

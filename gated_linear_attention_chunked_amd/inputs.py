@@ -79,6 +79,8 @@ DECODE_WORKLOADS = {
     w.name: w
     for w in (
         Workload("gdn_step_bf16_N256_H8_d128", "gdn", "bf16", 256, 1, 8, 128, 128, seed=9, gate_mu=2.0),
+        # VLA decode with the ratio read: A, S and the denominator n carried per stream
+        Workload("vla_ratio_step_f32_N256_H8_d96", "vla", "f32", 256, 1, 8, 96, 96, seed=10),
     )
 }
 

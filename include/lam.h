@@ -269,6 +269,29 @@ lam_status lam_vla_forward(int dtype, int64_t B, int64_t T, int64_t H, int64_t d
                            float *S_out, void *workspace, size_t workspace_bytes, int algo,
                            hipStream_t stream);
 
+/*
+ * VLA forward scan with the output read as a ratio of two recurrences
+ * ("Technical summary: Variational Linear Attention (VLA)", section 2.3: the
+ * output is a ratio of recurrences as in standard linear attention, where
+ * numerator and denominator accumulate alike, the denominator over a value
+ * of 1).  The denominator is a d-vector n per (b, h) that follows the write
+ * rule with the value 1:
+ *   n <- n + (1 - n . khat) alphahat,   y = (S qhat) / (n . qhat),
+ * with S, A, khat, qhat and alphahat exactly as lam_vla_forward.  y is not
+ * guarded against n . qhat near zero (a zero n_in makes the first token's
+ * denominator alphahat . qhat).  Token-recurrent kernel; no workspace.
+ *   q, k, v, p, A_in, S_in, out, A_out, S_out   as lam_vla_forward
+ *   n_in         [B,H,d] fp32 or NULL (zero)
+ *   n_out        [B,H,d] fp32 or NULL (not written); may equal n_in
+ * An output may be its own input's buffer (A_out = A_in, S_out = S_in,
+ * n_out = n_in) and must not otherwise overlap an input, another output or
+ * `out`.  Errors as lam_vla_forward.
+ */
+lam_status lam_vla_forward_ratio(int dtype, int64_t B, int64_t T, int64_t H, int64_t d,
+                                 const void *q, const void *k, const void *v, const void *p,
+                                 const float *A_in, const float *S_in, const float *n_in, void *out,
+                                 float *A_out, float *S_out, float *n_out, hipStream_t stream);
+
 /* Bytes of workspace lam_vla_forward needs (0: none); as above. */
 lam_status lam_vla_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, int64_t d,
                                   int algo, size_t *bytes);
@@ -343,6 +366,16 @@ lam_status lam_step(int variant, int dtype, int64_t N, int64_t H, int64_t dk, in
 lam_status lam_vla_step(int dtype, int64_t N, int64_t H, int64_t d, const void *q, const void *k,
                         const void *v, const void *p, float *A, float *S, void *out,
                         hipStream_t stream);
+
+/*
+ * lam_vla_step with the ratio read: one token for N concurrent streams, A,
+ * S [N,H,d,d] and the denominator n [N,H,d] fp32 updated in place (all
+ * required).  Equivalent to lam_vla_forward_ratio with T = 1 and in-place
+ * states.
+ */
+lam_status lam_vla_step_ratio(int dtype, int64_t N, int64_t H, int64_t d, const void *q, const void *k,
+                              const void *v, const void *p, float *A, float *S, float *n, void *out,
+                              hipStream_t stream);
 
 /*
  * lam_forward for callers that cannot allocate device memory (code under HIP

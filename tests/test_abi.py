@@ -131,6 +131,36 @@ def test_vla_rejects_bad_arguments(lib):
     assert _vla(lib, B=0, q=None, k=None, v=None, p=None, out=None) == OK
 
 
+def _vla_ratio(lib, dtype=0, B=2, T=8, H=2, d=32, q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000,
+               p=FAKE + 0x30000000, Ain=None, Sin=None, nin=None, out=FAKE + 0x40000000, Aout=None, Sout=None,
+               nout=None):
+    return lib.lam_vla_forward_ratio(dtype, B, T, H, d, q, k, v, p, Ain, Sin, nin, out, Aout, Sout, nout, None)
+
+
+def test_vla_ratio_rejects_bad_arguments(lib):
+    """The ratio read's entry points: the same shape checks as the plain VLA
+    scan, plus the denominator state's buffers (none of these reaches HIP)."""
+    assert _vla_ratio(lib, dtype=5) == INVALID
+    assert _vla_ratio(lib, B=-1) == INVALID
+    assert _vla_ratio(lib, d=40) == UNSUPPORTED
+    assert _vla_ratio(lib, d=0) == INVALID
+    for name in ("q", "k", "v", "p", "out"):
+        assert _vla_ratio(lib, **{name: None}) == INVALID, name
+    assert _vla_ratio(lib, out=FAKE + 4) == INVALID                              # out over q
+    assert _vla_ratio(lib, nout=FAKE + 0x40000000 + 64) == INVALID               # n_out inside out
+    S = FAKE + 0x60000000
+    assert _vla_ratio(lib, Sin=S, nout=S + 64) == INVALID                        # n_out over S_in
+    assert _vla_ratio(lib, nin=S, Aout=S) == INVALID                             # A_out over n_in
+    X = FAKE + 0x70000000
+    assert _vla_ratio(lib, Aout=X, nout=X + 64) == INVALID                       # two outputs overlap
+    assert _vla_ratio(lib, B=0, q=None, k=None, v=None, p=None, out=None) == OK
+    A, S2, n, o = FAKE + 0x80000000, FAKE + 0x90000000, FAKE + 0xA0000000, FAKE + 0xB0000000
+    assert lib.lam_vla_step_ratio(0, 2, 2, 32, FAKE, FAKE + 0x10000000, FAKE + 0x20000000, FAKE + 0x30000000,
+                                  A, S2, None, o, None) == INVALID              # n is updated in place
+    assert lib.lam_vla_step_ratio(0, 2, 2, 40, FAKE, FAKE, FAKE, FAKE, A, S2, n, o, None) == UNSUPPORTED
+    assert lib.lam_vla_step_ratio(3, 2, 2, 32, FAKE, FAKE, FAKE, FAKE, A, S2, n, o, None) == INVALID
+
+
 def test_binding_fails_loudly_without_gpu_tensors():
     import torch
 

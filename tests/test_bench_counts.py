@@ -77,3 +77,17 @@ def test_loglinear_levels_and_occupancy():
     assert [bench.loglinear_levels(T) for T in (1, 2, 3, 4, 5, 4096, 4097)] == [1, 2, 3, 3, 4, 13, 14]
     # positions 0..7: popcounts 0,1,1,2,1,2,2,3 -> 12, plus one level 0 each -> 20
     assert bench.loglinear_occupancy(8) == 20
+
+
+def test_decode_counts():
+    """Decode steps read and write the state they update.  Gated DeltaNet
+    N256 H8 d128 bf16: 1028 B per stream-head (q, k, v, out, alpha, beta) +
+    the fp32 state read and written (2 x 65,536 B).  VLA with the ratio read,
+    N256 H8 d96 fp32: q, k, v, p, out 5 x 96 x 4 = 1920 B, A and S read and
+    written 4 x 96 x 96 x 4 = 147,456 B, the denominator read and written
+    2 x 96 x 4 = 768 B, per stream-head."""
+    g = I.DECODE_WORKLOADS["gdn_step_bf16_N256_H8_d128"]
+    assert bench.algorithmic_bytes(g, True) == 2048 * 1028 + 2 * 2048 * 65_536
+    v = I.DECODE_WORKLOADS["vla_ratio_step_f32_N256_H8_d96"]
+    assert bench.algorithmic_bytes(v, True) == 2048 * (1920 + 147_456 + 768)
+    assert bench.algorithmic_flops(v) == 2048 * 12 * 96 * 96
