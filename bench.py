@@ -152,7 +152,7 @@ KERNEL_SOURCES = {  # schedule -> kernel source per variant family
     ("loglinear", "delta"): "loglin_recurrent.hip",
     ("lambda", "delta"): "loglin_recurrent.hip",
 }
-SHARED_HEADERS = ("chunk_common.h", "device_common.h", "lam_internal.h")
+SHARED_HEADERS = ("chunk_common.h", "chunk_f32.h", "device_common.h", "lam_internal.h")
 
 
 def kernel_source_hash(ran: str, variant: str):

@@ -1,0 +1,299 @@
+// chunk_f32.h -- the fp32 chunked scan shared by VLA and by the fp32 form of
+// the delta-rule family (DeltaNet, Gated DeltaNet, Gated DeltaNet-2).
+//
+// Both rules, cut into chunks of VC = 16 tokens (rows = tokens, S the memory
+// at the chunk start), take one state step of the same shape once the
+// state-independent parts of a chunk are formed:
+//   U = Tc V - Ktil S^T,   Y = Qtil S^T + (Aq Tc) V,   S^T <- gC S^T + Ahat^T U.
+// VLA ("Technical summary: Variational Linear Attention (VLA)", section 2.3):
+//   Tc = (I + strict(Khat Ahat^T))^{-1}, Ktil = Tc Khat, Aq = lower(Qhat Ahat^T),
+//   Qtil = Qhat - Aq Ktil, Ahat the gates, gC = 1.
+// The delta rule ("Mechanisms, trade-offs and cross-layer routing of
+// linear-attention architectures", "Technical details"), in the residual
+// form with gamma_t the running decay and Gamma_ts = gamma_t / gamma_s:
+//   Tc = (I + strict(E K^T * Gamma) diag(beta))^{-1}, Ktil = Tc diag(gamma) E,
+//   Aq = lower(Q K^T * Gamma) diag(beta), Qtil = diag(gamma) Q - Aq Ktil,
+//   Ahat = diag(beta gamma_C / gamma) K, gC = gamma_C,
+// so U is the chunk's residuals (Z - decayed prediction), V the targets z.
+// A derivation kernel per rule writes these operands to a per-chunk record;
+// the state kernel below runs the step.
+#pragma once
+
+#include "device_common.h"
+#include "lam_internal.h"
+
+namespace lam {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int VC = 16;    // chunk length
+constexpr int VLTS = 20;  // column stride (floats) of a 16x16 matrix stored by column
+
+// fp32 16x16x4 product.  Operand layout (lane = 16 g + i): A supplies row i,
+// column g; B supplies row g, column i; the accumulator holds rows 4g..4g+3 of
+// column i.  Contractions over 16 run as four steps with k = 4g + m at step
+// m, so each lane's operands for the four steps are four consecutive floats.
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 lds4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+template <int I>
+struct icst {
+    static constexpr int value = I;
+};
+// Workgroup barrier that orders LDS only.  Threads of these kernels share
+// data only through LDS, and a plain __syncthreads() would also wait for
+// every global load in flight (the next chunks' prefetch) at each barrier.
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// f(icst<0>) ... f(icst<N - 1>)
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &f) {
+    if constexpr (I < N) {
+        f(icst<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+// f(icst<0>) ... f(icst<14>)
+template <int I = 0, typename F>
+__device__ __forceinline__ void static_for15(F &f) {
+    if constexpr (I < 15) {
+        f(icst<I>{});
+        static_for15<I + 1>(f);
+    }
+}
+
+// Value of lane N of this lane's quad (DPP quad_perm [N, N, N, N]).
+template <int N>
+__device__ __forceinline__ float quad_lane(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), N * 0x55, 0xf, 0xf, false));
+}
+
+// (I + L)^{-1} for strictly lower L given by columns, written in A-operand
+// order (element (row, col) at out[(col / 4) * 16 + row][col % 4]).  One wave:
+// lane = (col = lane / 4, row quad q = lane % 4), forward substitution in
+// fp32; X[j][col] comes from the quad by DPP, and the columns of L, which do
+// not depend on X, are read two steps ahead.
+__device__ __forceinline__ void unit_lower_inverse(const float *lt, f32x4 *out, int lane) {
+    const int col = lane >> 2, q = lane & 3;
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == col) ? 1.f : 0.f;
+    f32x4 lw[3];
+    lw[0] = lds4(lt + 4 * q);
+    lw[1] = lds4(lt + VLTS + 4 * q);
+    auto step = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j + 2 < 15) lw[(j + 2) % 3] = lds4(lt + (j + 2) * VLTS + 4 * q);
+        const f32x4 lj = lw[j % 3];                  // L[4q + r][j]
+        const float xj = quad_lane<j / 4>(x[j % 4]);  // X[j][col]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = fmaf(-lj[r], xj, x[r]);
+    };
+    static_for15(step);
+    float *o = reinterpret_cast<float *>(out);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3)] = x[r];
+}
+
+
+
+// Per-chunk record the derivation writes for the state kernel (DK = the key
+// dimension; rows past the end of the sequence are zero).
+template <int DK>
+struct ChunkRec {
+    float kt[VC * DK];        // Ktil, rows t
+    float qt[VC * DK];        // Qtil, rows t
+    f32x4 aht[DK / 16][64];   // Ahat^T tiles, A-operand order: lane (g, i) of tile j holds Ahat[4g + m][16j + i]
+    f32x4 top[64];            // Tc, A-operand order
+    f32x4 aqt[64];            // Aq Tc, A-operand order
+    f32x4 gc;                 // gC (the chunk's decay of the state) in every slot; unused without decay
+};
+
+// What the state kernel reads and writes besides the records.
+struct ScanArgs {
+    int64_t B, T, H;
+    const void *v, *w;       // targets [B,T,H,DV]; write gates (z = w * v) or NULL
+    void *out;               // y [B,T,H,DV]
+    const float *S_in;       // [B,H,DV,DK] fp32 or NULL (zero)
+    float *S_out;            // [B,H,DV,DK] fp32 or NULL
+    void *side;              // per-token routing signal [B,T,H,DV] or NULL
+    int side_kind;           // kSideResidual (U) or kSideValue (z)
+};
+
+// Carry waves of the state kernel: DK/16, one 16 x 16 tile of S^T each; with
+// two carries (DK = 32) a third wave forms the output on a free SIMD, and
+// with more carries wave 3 forms it (waves take SIMDs in turn, so at DK = 96
+// wave 3 is the one carry that has its SIMD to itself).
+template <int DK>
+__host__ __device__ constexpr int state_waves() { return DK / 16 <= 2 ? DK / 16 + 1 : DK / 16; }
+template <int DK>
+__host__ __device__ constexpr int state_y_wave() { return DK / 16 <= 2 ? DK / 16 : 3; }
+// The wave that forms Tc V: the output wave with two carries, else wave 2
+// (with up to four carries it has its SIMD to itself).
+template <int DK>
+__host__ __device__ constexpr int state_v_wave() { return DK / 16 <= 2 ? DK / 16 : 2; }
+
+// One workgroup per (b, h, 16 value rows of S).  Carry wave j < DK/16 keeps
+// the 16 x 16 tile of S^T at key rows 16j .. 16j + 15 and the workgroup's
+// value columns; the products over the key dimension are summed across the
+// waves through LDS (fixed order, so every wave forms the same sums).
+// DECAY: the records carry gC; GATES2: the targets are z = w * v.
+template <typename IO, int DK, int DV, bool DECAY, bool GATES2>
+__global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(ScanArgs a,
+                                                                             const ChunkRec<DK> *__restrict__ rec) {
+    constexpr int NW = DK / 16;
+    constexpr int YW = state_y_wave<DK>();  // the wave that forms the output
+    constexpr int VW = state_v_wave<DK>();  // the wave that forms Tc V
+    __shared__ f32x4 part[2][2][NW][64];  // [chunk parity][Ktil S^T, Qtil S^T][wave][lane]
+    __shared__ f32x4 tv[2][64];           // [chunk parity] Tc V
+    const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
+    int head, vt;
+    xcd_group_map(blockIdx.x, static_cast<int>(a.B * a.H), DV / 16, head, vt);
+    const int b = head / H, h = head % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, i = lane & 15;
+    const int vcol = 16 * vt + i;
+    const int64_t sb = static_cast<int64_t>(head) * DV * DK;
+    const int nch = (T + VC - 1) / VC;
+    auto tok = [&](int t) { return ((static_cast<int64_t>(b) * T + t) * H + h) * DV; };  // value rows
+
+    // ST lane (g, i): S^T[16w + 4g + r][vcol] = S[vcol][16w + 4g + r]
+    f32x4 ST = {0.f, 0.f, 0.f, 0.f};
+    if (a.S_in && w < NW) {
+        const float4 x = *reinterpret_cast<const float4 *>(a.S_in + sb + static_cast<int64_t>(vcol) * DK + 16 * w + 4 * g);
+        ST = f32x4{x.x, x.y, x.z, x.w};
+    }
+    const ChunkRec<DK> *R0 = rec + static_cast<int64_t>(head) * nch;
+    const bool is_carry = w < NW, is_y = w == YW;
+    struct Ops {
+        f32x4 kt, qt, aht, top, aqt;
+        float v[4], w[GATES2 ? 4 : 1], gc;
+    };
+    // Every wave issues the same loads whatever its role (an output-only wave
+    // reads the last carry's operands and ignores them): with role-dependent
+    // loads the compiler's load-counter waits would drain the whole ring.
+    const int wc = min(w, NW - 1);
+    auto load = [&](int c, Ops &o) {  // past the end: the last chunk again (never used)
+        const int cc = min(c, nch - 1);
+        const ChunkRec<DK> &R = R0[cc];
+        o.kt = *reinterpret_cast<const f32x4 *>(&R.kt[i * DK + 16 * wc + 4 * g]);
+        o.qt = *reinterpret_cast<const f32x4 *>(&R.qt[i * DK + 16 * wc + 4 * g]);
+        o.aht = R.aht[wc][lane];
+        o.aqt = R.aqt[lane];
+        o.top = R.top[lane];
+        const int t0 = cc * VC, n = min(VC, T - t0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = min(4 * g + r, n - 1);
+            o.v[r] = IO::ld(a.v, tok(t0 + t) + vcol);
+            if constexpr (GATES2) o.w[r] = IO::ld(a.w, tok(t0 + t) + vcol);
+        }
+        o.gc = DECAY ? R.gc[0] : 1.f;
+    };
+    // one chunk's step from its operand set
+    auto step = [&](const Ops &cur, int c) {
+        const int p = c & 1, t0 = c * VC, n = min(VC, T - t0);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        if (is_carry) {
+            // partial Ktil S^T and Qtil S^T over this wave's key rows (two
+            // accumulators per product keep the dependent chains short)
+            f32x4 pk0 = mfma4(cur.kt[0], ST[0], zero), pk1 = mfma4(cur.kt[1], ST[1], zero);
+            f32x4 pq0 = mfma4(cur.qt[0], ST[0], zero), pq1 = mfma4(cur.qt[1], ST[1], zero);
+            pk0 = mfma4(cur.kt[2], ST[2], pk0);
+            pk1 = mfma4(cur.kt[3], ST[3], pk1);
+            pq0 = mfma4(cur.qt[2], ST[2], pq0);
+            pq1 = mfma4(cur.qt[3], ST[3], pq1);
+            part[p][0][w][lane] = pk0 + pk1;
+            part[p][1][w][lane] = pq0 + pq1;
+        }
+        // V's rows (zero past the end), the B operand of Tc V and (Aq Tc) V
+        f32x4 vb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float z = GATES2 ? cur.v[r] * cur.w[r] : cur.v[r];
+            vb[r] = 4 * g + r < n ? z : 0.f;
+        }
+        if (w == VW) {
+            f32x4 a0 = mfma4(cur.top[0], vb[0], zero), a1 = mfma4(cur.top[1], vb[1], zero);
+            a0 = mfma4(cur.top[2], vb[2], a0);
+            a1 = mfma4(cur.top[3], vb[3], a1);
+            tv[p][lane] = a0 + a1;
+        }
+        f32x4 y0 = zero;
+        if (is_y) {
+            f32x4 y1 = mfma4(cur.aqt[1], vb[1], zero);
+            y0 = mfma4(cur.aqt[0], vb[0], zero);
+            y1 = mfma4(cur.aqt[3], vb[3], y1);
+            y0 = mfma4(cur.aqt[2], vb[2], y0);
+            y0 += y1;
+        }
+        lds_sync();
+        if (is_carry) {
+            // U = Tc V - Ktil S^T (rows past the end: zero), summed in a fixed
+            // order so every wave forms the same U; then S^T += Ahat^T U
+            f32x4 z = part[p][0][0][lane];
+#pragma unroll
+            for (int j = 1; j < NW; ++j) z += part[p][0][j][lane];
+            const f32x4 u = tv[p][lane] - z;
+            f32x4 d0 = mfma4(cur.aht[0], u[0], zero), d1 = mfma4(cur.aht[1], u[1], zero);
+            d0 = mfma4(cur.aht[2], u[2], d0);
+            d1 = mfma4(cur.aht[3], u[3], d1);
+            if constexpr (DECAY) ST = ST * cur.gc + (d0 + d1);
+            else ST += d0 + d1;
+            if (a.side_kind == kSideResidual && w == 0) {  // the chunk's residuals U
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g + r < n) IO::st(a.side, tok(t0 + 4 * g + r) + vcol, u[r]);
+            }
+        }
+        if (is_y) {  // Y = Qtil S^T + (Aq Tc) V
+            f32x4 y = part[p][1][0][lane];
+#pragma unroll
+            for (int j = 1; j < NW; ++j) y += part[p][1][j][lane];
+            y += y0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r < n) IO::st(a.out, tok(t0 + 4 * g + r) + vcol, y[r]);
+            if (a.side_kind == kSideValue) {  // the write values z
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g + r < n) IO::st(a.side, tok(t0 + 4 * g + r) + vcol, vb[r]);
+            }
+        }
+    };
+    // A ring of NS operand sets: the loads run NS chunks ahead (the records
+    // come from L2 or HBM, a step takes a few hundred cycles); every trip
+    // refills each set it consumes (past the end: the last chunk again,
+    // never used), so the loads in flight always form the same queue.
+    constexpr int NS = 4;
+    Ops o[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) load(j, o[j]);
+    int c = 0;
+    for (; c + NS <= nch; c += NS) {
+        auto trip = [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            step(o[j], c + j);
+            load(c + j + NS, o[j]);
+        };
+        static_for<NS>(trip);
+    }
+    auto tail = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if (c + j < nch) step(o[j], c + j);
+    };
+    static_for<NS>(tail);
+    if (a.S_out && is_carry)
+        *reinterpret_cast<float4 *>(a.S_out + sb + static_cast<int64_t>(vcol) * DK + 16 * w + 4 * g) =
+            make_float4(ST[0], ST[1], ST[2], ST[3]);
+}
+
+
+}  // namespace
+}  // namespace lam

@@ -40,89 +40,14 @@
 //            (Aq Tc) V do not depend on the state, so the only products on
 //            the chunk-to-chunk chain are Ktil S^T, Qtil S^T and the update.
 // The last segment's alpha workgroup writes A_out; the state workgroups
-// write S_out.
-#include "device_common.h"
-#include "lam_internal.h"
+// write S_out.  The state kernel and the chunk record are in chunk_f32.h,
+// shared with the fp32 form of the delta-rule family.
+#include "chunk_f32.h"
 
 namespace lam {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int VC = 16;    // chunk length
-constexpr int VLTS = 20;  // column stride (floats) of a 16x16 matrix stored by column
-
-// fp32 16x16x4 product.  Operand layout (lane = 16 g + i): A supplies row i,
-// column g; B supplies row g, column i; the accumulator holds rows 4g..4g+3 of
-// column i.  Contractions over 16 run as four steps with k = 4g + m at step
-// m, so each lane's operands for the four steps are four consecutive floats.
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 lds4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
-template <int I>
-struct icst {
-    static constexpr int value = I;
-};
-// Workgroup barrier that orders LDS only.  Threads of these kernels share
-// data only through LDS, and a plain __syncthreads() would also wait for
-// every global load in flight (the next chunks' prefetch) at each barrier.
-__device__ __forceinline__ void lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-// f(icst<0>) ... f(icst<N - 1>)
-template <int N, int I = 0, typename F>
-__device__ __forceinline__ void static_for(F &f) {
-    if constexpr (I < N) {
-        f(icst<I>{});
-        static_for<N, I + 1>(f);
-    }
-}
-// f(icst<0>) ... f(icst<14>)
-template <int I = 0, typename F>
-__device__ __forceinline__ void static_for15(F &f) {
-    if constexpr (I < 15) {
-        f(icst<I>{});
-        static_for15<I + 1>(f);
-    }
-}
 __device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
-
-// Value of lane N of this lane's quad (DPP quad_perm [N, N, N, N]).
-template <int N>
-__device__ __forceinline__ float quad_lane(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), N * 0x55, 0xf, 0xf, false));
-}
-
-// (I + L)^{-1} for strictly lower L given by columns, written in A-operand
-// order (element (row, col) at out[(col / 4) * 16 + row][col % 4]).  One wave:
-// lane = (col = lane / 4, row quad q = lane % 4), forward substitution in
-// fp32; X[j][col] comes from the quad by DPP, and the columns of L, which do
-// not depend on X, are read two steps ahead.
-__device__ __forceinline__ void unit_lower_inverse(const float *lt, f32x4 *out, int lane) {
-    const int col = lane >> 2, q = lane & 3;
-    float x[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == col) ? 1.f : 0.f;
-    f32x4 lw[3];
-    lw[0] = lds4(lt + 4 * q);
-    lw[1] = lds4(lt + VLTS + 4 * q);
-    auto step = [&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        if constexpr (j + 2 < 15) lw[(j + 2) % 3] = lds4(lt + (j + 2) * VLTS + 4 * q);
-        const f32x4 lj = lw[j % 3];                  // L[4q + r][j]
-        const float xj = quad_lane<j / 4>(x[j % 4]);  // X[j][col]
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = fmaf(-lj[r], xj, x[r]);
-    };
-    static_for15(step);
-    float *o = reinterpret_cast<float *>(out);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[((col >> 2) * 16 + 4 * q + r) * 4 + (col & 3)] = x[r];
-}
-
 
 constexpr int NT64 = 64;  // lanes per wave
 
@@ -130,16 +55,6 @@ constexpr int NT64 = 64;  // lanes per wave
 // first costs one d x d inversion; longer segments lengthen the chain inside
 // each alpha workgroup.
 __host__ __device__ constexpr int seg_len(int D) { return D <= 32 ? 128 : 256; }
-
-// Per-chunk record the alpha kernel writes for the state kernel.
-template <int D>
-struct VlaChunk {
-    float kt[VC * D];        // Ktil = Tc Khat, rows t (zero past the end of the sequence)
-    float qt[VC * D];        // Qtil = Qhat - Aq Ktil, rows t (zero past the end)
-    f32x4 aht[D / 16][64];   // alphahat^T tiles, A-operand order: lane (g, i) of tile j holds ahat[4g + m][16j + i]
-    f32x4 top[64];           // Tc = (I + strict(Khat Ahat^T))^{-1}, A-operand order
-    f32x4 aqt[64];           // Aq Tc with Aq = lower(Qhat Ahat^T), A-operand order
-};
 
 // Workspace layout of one call (after the status block): G and the segment-
 // start inverses, one D x D fp32 matrix per (b, h, segment), then the chunk
@@ -158,7 +73,7 @@ VlaLayout vla_layout(int64_t B, int64_t T, int64_t H) {
     L.g_off = kStatusBytes;
     L.a_off = up(L.g_off + mat);
     L.rec_off = up(L.a_off + mat);
-    L.bytes = L.rec_off + static_cast<size_t>(B * H * L.nch) * sizeof(VlaChunk<D>);
+    L.bytes = L.rec_off + static_cast<size_t>(B * H * L.nch) * sizeof(ChunkRec<D>);
     return L;
 }
 
@@ -372,7 +287,7 @@ __host__ __device__ constexpr int alpha_waves() { return D / 16 / alpha_tpw<D>()
 // w TPW .. w TPW + TPW - 1 of A^T as fp32 accumulator tiles.
 template <typename IO, int D>
 __device__ __forceinline__ void vla_alpha_body(AlphaLds<D> &s, const VlaArgs &a, const float *__restrict__ Aseg,
-                                               VlaChunk<D> *__restrict__ rec, int nseg, unsigned int *status) {
+                                               ChunkRec<D> *__restrict__ rec, int nseg, unsigned int *status) {
     constexpr int NW = D / 16, NQ = D / 16;
     constexpr int TPW = alpha_tpw<D>(), NTW = NW / TPW, NWV = alpha_waves<D>(), NT = 64 * NWV;
     constexpr int FW = TPW > 1 ? NTW : 0;  // the wave that runs the recurrence for F and forms Tc
@@ -490,7 +405,7 @@ __device__ __forceinline__ void vla_alpha_body(AlphaLds<D> &s, const VlaArgs &a,
         const int n = min(VC, seg1 - c0), n1 = max(0, min(VC, seg1 - c0 - VC));  // rows of this chunk, of the next
         const int cb = ((c0 - seg0) / VC) & 1, nb = cb ^ 1;
         const float *P = s.p[cb], *KH = s.kh[cb], *QH = s.qh[cb];
-        VlaChunk<D> &R = rec[static_cast<int64_t>(head) * nch + c0 / VC];
+        ChunkRec<D> &R = rec[static_cast<int64_t>(head) * nch + c0 / VC];
         // ---- stage chunk c + 1 into the other buffer, refill the registers
         stage(nb, n1);
         fetch(c0 + 2 * VC);
@@ -754,164 +669,13 @@ __device__ __forceinline__ void vla_alpha_body(AlphaLds<D> &s, const VlaArgs &a,
 // compute unit (the other sizes need no more than 256 registers anyway).
 template <typename IO, int D>
 __global__ __launch_bounds__(64 * alpha_waves<D>()) __attribute__((amdgpu_waves_per_eu(2))) void vla_alpha_kernel(VlaArgs a, const float *__restrict__ Aseg,
-                                                                          VlaChunk<D> *__restrict__ rec, int nseg,
+                                                                          ChunkRec<D> *__restrict__ rec, int nseg,
                                                                           unsigned int *status) {
     __shared__ AlphaLds<D> s;
     vla_alpha_body<IO, D>(s, a, Aseg, rec, nseg, status);
 }
 
 // ================================ state ================================
-// Carry waves of the state kernel: D/16, one 16 x 16 tile of S^T each; with
-// two carries (d = 32) a third wave forms the output on a free SIMD, and with
-// more carries wave 3 forms it (waves take SIMDs in turn, so at d = 96 wave 3
-// is the one carry that has its SIMD to itself).
-template <int D>
-__host__ __device__ constexpr int state_waves() { return D / 16 <= 2 ? D / 16 + 1 : D / 16; }
-template <int D>
-__host__ __device__ constexpr int state_y_wave() { return D / 16 <= 2 ? D / 16 : 3; }
-// The wave that forms Tc V: the output wave with two carries, else wave 2
-// (with up to four carries it has its SIMD to itself).
-template <int D>
-__host__ __device__ constexpr int state_v_wave() { return D / 16 <= 2 ? D / 16 : 2; }
-
-// One workgroup per (b, h, 16 value rows of S).  Carry wave j < D/16 keeps
-// the 16 x 16 tile of S^T at key rows 16j .. 16j + 15 and the workgroup's
-// value columns; the products over the key dimension are summed across the
-// waves through LDS (fixed order, so every wave forms the same sums).
-template <typename IO, int D>
-__global__ __launch_bounds__(64 * state_waves<D>()) void vla_state_kernel(VlaArgs a, const VlaChunk<D> *__restrict__ rec) {
-    constexpr int NW = D / 16;
-    constexpr int YW = state_y_wave<D>();  // the wave that forms the output
-    constexpr int VW = state_v_wave<D>();  // the wave that forms Tc V
-    __shared__ f32x4 part[2][2][NW][64];  // [chunk parity][Ktil S^T, Qtil S^T][wave][lane]
-    __shared__ f32x4 tv[2][64];           // [chunk parity] Tc V
-    const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
-    int head, vt;
-    xcd_group_map(blockIdx.x, static_cast<int>(a.B * a.H), NW, head, vt);
-    const int b = head / H, h = head % H;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4, i = lane & 15;
-    const int vcol = 16 * vt + i;
-    const int64_t sb = static_cast<int64_t>(head) * D * D;
-    const int nch = (T + VC - 1) / VC;
-    auto tok = [&](int t) { return ((static_cast<int64_t>(b) * T + t) * H + h) * D; };
-
-    // ST lane (g, i): S^T[16w + 4g + r][vcol] = S[vcol][16w + 4g + r]
-    f32x4 ST = {0.f, 0.f, 0.f, 0.f};
-    if (a.S_in && w < NW) {
-        const float4 x = *reinterpret_cast<const float4 *>(a.S_in + sb + static_cast<int64_t>(vcol) * D + 16 * w + 4 * g);
-        ST = f32x4{x.x, x.y, x.z, x.w};
-    }
-    const VlaChunk<D> *R0 = rec + static_cast<int64_t>(head) * nch;
-    const bool is_carry = w < NW, is_y = w == YW;
-    struct Ops {
-        f32x4 kt, qt, aht, top, aqt;
-        float v[4];
-    };
-    // Every wave issues the same loads whatever its role (an output-only wave
-    // reads the last carry's operands and ignores them): with role-dependent
-    // loads the compiler's load-counter waits would drain the whole ring.
-    const int wc = min(w, NW - 1);
-    auto load = [&](int c, Ops &o) {  // past the end: the last chunk again (never used)
-        const int cc = min(c, nch - 1);
-        const VlaChunk<D> &R = R0[cc];
-        o.kt = *reinterpret_cast<const f32x4 *>(&R.kt[i * D + 16 * wc + 4 * g]);
-        o.qt = *reinterpret_cast<const f32x4 *>(&R.qt[i * D + 16 * wc + 4 * g]);
-        o.aht = R.aht[wc][lane];
-        o.aqt = R.aqt[lane];
-        o.top = R.top[lane];
-        const int t0 = cc * VC, n = min(VC, T - t0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = min(4 * g + r, n - 1);
-            o.v[r] = IO::ld(a.v, tok(t0 + t) + vcol);
-        }
-    };
-    // one chunk's step from its operand set
-    auto step = [&](const Ops &cur, int c) {
-        const int p = c & 1, t0 = c * VC, n = min(VC, T - t0);
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        if (is_carry) {
-            // partial Ktil S^T and Qtil S^T over this wave's key rows (two
-            // accumulators per product keep the dependent chains short)
-            f32x4 pk0 = mfma4(cur.kt[0], ST[0], zero), pk1 = mfma4(cur.kt[1], ST[1], zero);
-            f32x4 pq0 = mfma4(cur.qt[0], ST[0], zero), pq1 = mfma4(cur.qt[1], ST[1], zero);
-            pk0 = mfma4(cur.kt[2], ST[2], pk0);
-            pk1 = mfma4(cur.kt[3], ST[3], pk1);
-            pq0 = mfma4(cur.qt[2], ST[2], pq0);
-            pq1 = mfma4(cur.qt[3], ST[3], pq1);
-            part[p][0][w][lane] = pk0 + pk1;
-            part[p][1][w][lane] = pq0 + pq1;
-        }
-        // V's rows (zero past the end), the B operand of Tc V and (Aq Tc) V
-        f32x4 vb;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vb[r] = 4 * g + r < n ? cur.v[r] : 0.f;
-        if (w == VW) {
-            f32x4 a0 = mfma4(cur.top[0], vb[0], zero), a1 = mfma4(cur.top[1], vb[1], zero);
-            a0 = mfma4(cur.top[2], vb[2], a0);
-            a1 = mfma4(cur.top[3], vb[3], a1);
-            tv[p][lane] = a0 + a1;
-        }
-        f32x4 y0 = zero;
-        if (is_y) {
-            f32x4 y1 = mfma4(cur.aqt[1], vb[1], zero);
-            y0 = mfma4(cur.aqt[0], vb[0], zero);
-            y1 = mfma4(cur.aqt[3], vb[3], y1);
-            y0 = mfma4(cur.aqt[2], vb[2], y0);
-            y0 += y1;
-        }
-        lds_sync();
-        if (is_carry) {
-            // U = Tc V - Ktil S^T (rows past the end: zero), summed in a fixed
-            // order so every wave forms the same U; then S^T += Ahat^T U
-            f32x4 z = part[p][0][0][lane];
-#pragma unroll
-            for (int j = 1; j < NW; ++j) z += part[p][0][j][lane];
-            const f32x4 u = tv[p][lane] - z;
-            f32x4 d0 = mfma4(cur.aht[0], u[0], zero), d1 = mfma4(cur.aht[1], u[1], zero);
-            d0 = mfma4(cur.aht[2], u[2], d0);
-            d1 = mfma4(cur.aht[3], u[3], d1);
-            ST += d0 + d1;
-        }
-        if (is_y) {  // Y = Qtil S^T + (Aq Tc) V
-            f32x4 y = part[p][1][0][lane];
-#pragma unroll
-            for (int j = 1; j < NW; ++j) y += part[p][1][j][lane];
-            y += y0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (4 * g + r < n) IO::st(a.out, tok(t0 + 4 * g + r) + vcol, y[r]);
-        }
-    };
-    // A ring of NS operand sets: the loads run NS chunks ahead (the records
-    // come from L2 or HBM, a step takes a few hundred cycles); every trip
-    // refills each set it consumes (past the end: the last chunk again,
-    // never used), so the loads in flight always form the same queue.
-    constexpr int NS = 4;
-    Ops o[NS];
-#pragma unroll
-    for (int j = 0; j < NS; ++j) load(j, o[j]);
-    int c = 0;
-    for (; c + NS <= nch; c += NS) {
-        auto trip = [&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            step(o[j], c + j);
-            load(c + j + NS, o[j]);
-        };
-        static_for<NS>(trip);
-    }
-    auto tail = [&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        if (c + j < nch) step(o[j], c + j);
-    };
-    static_for<NS>(tail);
-    if (a.S_out && is_carry)
-        *reinterpret_cast<float4 *>(a.S_out + sb + static_cast<int64_t>(vcol) * D + 16 * w + 4 * g) =
-            make_float4(ST[0], ST[1], ST[2], ST[3]);
-}
-
 template <typename IO, int D>
 hipError_t launch_d(const VlaArgs &a, hipStream_t stream) {
     const VlaLayout L = vla_layout<D>(a.B, a.T, a.H);
@@ -919,7 +683,7 @@ hipError_t launch_d(const VlaArgs &a, hipStream_t stream) {
     unsigned int *status = reinterpret_cast<unsigned int *>(ws);
     float *G = reinterpret_cast<float *>(ws + L.g_off);
     float *Aseg = reinterpret_cast<float *>(ws + L.a_off);
-    VlaChunk<D> *rec = reinterpret_cast<VlaChunk<D> *>(ws + L.rec_off);
+    ChunkRec<D> *rec = reinterpret_cast<ChunkRec<D> *>(ws + L.rec_off);
     const int nseg = static_cast<int>(L.nseg);
     const unsigned heads = static_cast<unsigned>(a.B * a.H);
     if (nseg > 1) {
@@ -927,7 +691,16 @@ hipError_t launch_d(const VlaArgs &a, hipStream_t stream) {
         vla_inverse_kernel<D><<<heads * (nseg - 1), 256, 0, stream>>>(a, G, Aseg, nseg);
     }
     vla_alpha_kernel<IO, D><<<heads * nseg, 64 * alpha_waves<D>(), 0, stream>>>(a, Aseg, rec, nseg, status);
-    vla_state_kernel<IO, D><<<heads * (D / 16), 64 * state_waves<D>(), 0, stream>>>(a, rec);
+    ScanArgs sa{};
+    sa.B = a.B;
+    sa.T = a.T;
+    sa.H = a.H;
+    sa.v = a.v;
+    sa.out = a.out;
+    sa.S_in = a.S_in;
+    sa.S_out = a.S_out;
+    sa.side_kind = kSideNone;
+    chunk_state_kernel<IO, D, D, false, false><<<heads * (D / 16), 64 * state_waves<D>(), 0, stream>>>(sa, rec);
     return hipGetLastError();
 }
 
