@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "lam")
 LIB = os.path.join(PKG, "liblam.so")
-SOURCES = ["lam_api.cpp", "delta_recurrent.hip", "vla_recurrent.hip", "delta_chunked.hip", "kda_chunked.hip", "vla_chunked.hip", "lam_noalloc.hip", "delta_step.hip", "delta_backward.hip", "route.hip", "loglin_recurrent.hip"]
+SOURCES = ["lam_api.cpp", "delta_recurrent.hip", "vla_recurrent.hip", "delta_chunked.hip", "delta_chunked_f32.hip", "kda_chunked.hip", "vla_chunked.hip", "lam_noalloc.hip", "delta_step.hip", "delta_backward.hip", "route.hip", "loglin_recurrent.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

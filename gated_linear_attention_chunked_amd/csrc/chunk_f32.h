@@ -117,6 +117,7 @@ struct ChunkRec {
 // What the state kernel reads and writes besides the records.
 struct ScanArgs {
     int64_t B, T, H;
+    int dv;                  // value width DV (a multiple of 16)
     const void *v, *w;       // targets [B,T,H,DV]; write gates (z = w * v) or NULL
     void *out;               // y [B,T,H,DV]
     const float *S_in;       // [B,H,DV,DK] fp32 or NULL (zero)
@@ -143,7 +144,7 @@ __host__ __device__ constexpr int state_v_wave() { return DK / 16 <= 2 ? DK / 16
 // value columns; the products over the key dimension are summed across the
 // waves through LDS (fixed order, so every wave forms the same sums).
 // DECAY: the records carry gC; GATES2: the targets are z = w * v.
-template <typename IO, int DK, int DV, bool DECAY, bool GATES2>
+template <typename IO, int DK, bool DECAY, bool GATES2>
 __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(ScanArgs a,
                                                                              const ChunkRec<DK> *__restrict__ rec) {
     constexpr int NW = DK / 16;
@@ -153,6 +154,7 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
     __shared__ f32x4 tv[2][64];           // [chunk parity] Tc V
     const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
     int head, vt;
+    const int DV = a.dv;
     xcd_group_map(blockIdx.x, static_cast<int>(a.B * a.H), DV / 16, head, vt);
     const int b = head / H, h = head % H;
     const int tid = threadIdx.x, lane = tid & 63;

@@ -834,13 +834,22 @@ hipError_t launch_var(const DeltaArgs &a, hipStream_t stream) {
 
 }  // namespace
 
+namespace {
+// the bf16 schedule of this file; every other DeltaNet / Gated DeltaNet /
+// Gated DeltaNet-2 shape takes the fp32 chunked form (delta_chunked_f32.hip)
+bool bf16_schedule(const DeltaArgs &a) {
+    return a.dtype == kBF16 && (a.dk == 64 || a.dk == 128) && a.dv % BV == 0;
+}
+}  // namespace
+
 bool delta_chunked_supported(const DeltaArgs &a) {
     if (a.variant == kKimiDelta) return kda_chunked_supported(a);
-    return a.dtype == kBF16 && (a.dk == 64 || a.dk == 128) && a.dv % BV == 0;
+    return bf16_schedule(a) || delta_f32_chunked_supported(a);
 }
 
 bool delta_chunked_workspace(const DeltaArgs &a, size_t *bytes) {
     if (a.variant == kKimiDelta) return kda_chunked_workspace(a, bytes);
+    if (!bf16_schedule(a)) return delta_f32_chunked_workspace(a, bytes);
     const int64_t tasks = a.B * a.H * ((a.T + C - 1) / C);
     if (tasks > 0x7fffffff) return false;
     *bytes = kStatusBytes + static_cast<size_t>(tasks) * sizeof(DerBlock);
@@ -849,6 +858,7 @@ bool delta_chunked_workspace(const DeltaArgs &a, size_t *bytes) {
 
 hipError_t launch_delta_chunked(const DeltaArgs &a, hipStream_t stream) {
     if (!delta_chunked_supported(a)) return hipErrorNotSupported;
+    if (a.variant != kKimiDelta && !bf16_schedule(a)) return launch_delta_f32_chunked(a, stream);
     switch (a.variant) {
         case kDeltaNet: return launch_var<kDeltaNet>(a, stream);
         case kGatedDeltaNet: return launch_var<kGatedDeltaNet>(a, stream);

@@ -65,6 +65,14 @@ bool delta_chunked_workspace(const DeltaArgs &a, size_t *bytes);
 // Enqueues the chunked kernels; a.ws holds at least
 // delta_chunked_workspace(a) bytes.
 hipError_t launch_delta_chunked(const DeltaArgs &a, hipStream_t stream);
+// The fp32 chunked form of DeltaNet, Gated DeltaNet and Gated DeltaNet-2
+// (16-token chunks on fp32 matrix cores, any storage dtype, dk in {32, 64,
+// 96, 128}, dv a multiple of 16): the chunked schedule for the shapes the
+// bf16 one does not take.  Workspace: the status block, then one chunk record
+// per (b, h, 16-token chunk).
+bool delta_f32_chunked_supported(const DeltaArgs &a);
+bool delta_f32_chunked_workspace(const DeltaArgs &a, size_t *bytes);
+hipError_t launch_delta_f32_chunked(const DeltaArgs &a, hipStream_t stream);
 // VLA chunked schedule (fp32 matrix cores, any dtype of the token streams).
 bool vla_chunked_supported(const VlaArgs &a);
 bool vla_chunked_workspace(const VlaArgs &a, size_t *bytes);

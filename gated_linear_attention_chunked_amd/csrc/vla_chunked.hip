@@ -695,12 +695,13 @@ hipError_t launch_d(const VlaArgs &a, hipStream_t stream) {
     sa.B = a.B;
     sa.T = a.T;
     sa.H = a.H;
+    sa.dv = D;
     sa.v = a.v;
     sa.out = a.out;
     sa.S_in = a.S_in;
     sa.S_out = a.S_out;
     sa.side_kind = kSideNone;
-    chunk_state_kernel<IO, D, D, false, false><<<heads * (D / 16), 64 * state_waves<D>(), 0, stream>>>(sa, rec);
+    chunk_state_kernel<IO, D, false, false><<<heads * (D / 16), 64 * state_waves<D>(), 0, stream>>>(sa, rec);
     return hipGetLastError();
 }
 

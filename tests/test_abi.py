@@ -185,13 +185,16 @@ def test_workspace_size_query(lib):
     # Kimi Delta: 14,848 B per 16-token sub-chunk at dk = 128, counted in pairs
     assert _ws_size(lib, 2, 1, 2, 32768, 8, 128, 128) == (OK, 256 + 2 * 8 * 2048 * 14848)
     assert _ws_size(lib, 2, 1, 1, 17, 1, 128, 128) == (OK, 256 + 2 * 14848)
+    # fp32 chunked form (any storage at dk 32 / 96, fp32 at every size): one
+    # record per (b, h, 16-token chunk), 26,640 B at dk = 128, 8,208 B at dk = 32
+    assert _ws_size(lib, 1, 0, 8, 4096, 8, 128, 128) == (OK, 256 + 8 * 8 * 256 * 26640)
+    assert _ws_size(lib, 0, 1, 1, 17, 2, 32, 64) == (OK, 256 + 2 * 2 * 8208)
     # schedules with no workspace
-    assert _ws_size(lib, 1, 0, 8, 4096, 8, 128, 128) == (OK, 0)              # fp32 storage: recurrent
     assert _ws_size(lib, 1, 1, 8, 4096, 8, 128, 128, algo=1) == (OK, 0)      # recurrent asked for
     assert _ws_size(lib, 1, 1, 8, 0, 8, 128, 128) == (OK, 0)                 # T = 0: state copy
     assert _ws_size(lib, 1, 1, 0, 100, 8, 128, 128) == (OK, 0)               # empty batch
     # the statuses lam_forward would return
-    assert _ws_size(lib, 1, 0, 8, 64, 8, 128, 128, algo=2)[0] == UNSUPPORTED  # fp32 chunked
+    assert _ws_size(lib, 2, 0, 8, 64, 8, 128, 128, algo=2)[0] == UNSUPPORTED  # Kimi Delta fp32 chunked
     assert _ws_size(lib, 9)[0] == INVALID
     assert _ws_size(lib, dk=48)[0] == UNSUPPORTED
     assert _ws_size(lib, B=-1)[0] == INVALID

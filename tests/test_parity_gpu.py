@@ -423,10 +423,10 @@ def test_chunked_rejects_unsupported():
     with pytest.raises(lam.LamError) as e:
         lam.forward("kda", g["q"], g["k"], g["v"], g["beta"], alpha=g["alpha"], algo="chunked")
     assert e.value.status == 2
-    w = _w("gdn", "f32", 1, 70, 1, 128, 128, seed=1)
+    w = _w("kda", "f32", 1, 70, 1, 128, 128, seed=1)
     g = I.to_device(I.make_inputs(w), "f32", "cuda")
     with pytest.raises(lam.LamError):
-        lam.forward("gdn", g["q"], g["k"], g["v"], g["beta"], alpha=g["alpha"], algo="chunked")
+        lam.forward("kda", g["q"], g["k"], g["v"], g["beta"], alpha=g["alpha"], algo="chunked")
     torch.cuda.synchronize()
 
 
