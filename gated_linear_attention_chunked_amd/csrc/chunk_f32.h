@@ -126,28 +126,32 @@ struct ScanArgs {
     int side_kind;           // kSideResidual (U) or kSideValue (z)
 };
 
-// Carry waves of the state kernel: DK/16, one 16 x 16 tile of S^T each; with
-// two carries (DK = 32) a third wave forms the output on a free SIMD, and
-// with more carries wave 3 forms it (waves take SIMDs in turn, so at DK = 96
-// wave 3 is the one carry that has its SIMD to itself).
+// Key tiles of S^T per carry wave of the state kernel: one at DK = 32, two
+// from DK = 64 on, so a workgroup has at most four carries (one per SIMD) and,
+// at about 240 registers a lane, two workgroups share a CU.
 template <int DK>
-__host__ __device__ constexpr int state_waves() { return DK / 16 <= 2 ? DK / 16 + 1 : DK / 16; }
+__host__ __device__ constexpr int state_tpw() { return DK >= 64 ? 2 : 1; }
 template <int DK>
-__host__ __device__ constexpr int state_y_wave() { return DK / 16 <= 2 ? DK / 16 : 3; }
-// The wave that forms Tc V: the output wave with two carries, else wave 2
-// (with up to four carries it has its SIMD to itself).
+__host__ __device__ constexpr int state_carries() { return DK / 16 / state_tpw<DK>(); }
+// With fewer than four carries one more wave forms the output and Tc V on the
+// free SIMD; with four, carry 3 forms the output and carry 2 Tc V.
 template <int DK>
-__host__ __device__ constexpr int state_v_wave() { return DK / 16 <= 2 ? DK / 16 : 2; }
+__host__ __device__ constexpr int state_waves() { return state_carries<DK>() < 4 ? state_carries<DK>() + 1 : 4; }
+template <int DK>
+__host__ __device__ constexpr int state_y_wave() { return state_carries<DK>() < 4 ? state_carries<DK>() : 3; }
+template <int DK>
+__host__ __device__ constexpr int state_v_wave() { return state_carries<DK>() < 4 ? state_carries<DK>() : 2; }
 
-// One workgroup per (b, h, 16 value rows of S).  Carry wave j < DK/16 keeps
-// the 16 x 16 tile of S^T at key rows 16j .. 16j + 15 and the workgroup's
+// One workgroup per (b, h, 16 value rows of S).  Carry wave w keeps the TPW
+// 16 x 16 tiles of S^T at key rows 16 (TPW w + j) .. + 15 and the workgroup's
 // value columns; the products over the key dimension are summed across the
 // waves through LDS (fixed order, so every wave forms the same sums).
 // DECAY: the records carry gC; GATES2: the targets are z = w * v.
 template <typename IO, int DK, bool DECAY, bool GATES2>
 __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(ScanArgs a,
                                                                              const ChunkRec<DK> *__restrict__ rec) {
-    constexpr int NW = DK / 16;
+    constexpr int TPW = state_tpw<DK>();
+    constexpr int NW = state_carries<DK>();
     constexpr int YW = state_y_wave<DK>();  // the wave that forms the output
     constexpr int VW = state_v_wave<DK>();  // the wave that forms Tc V
     __shared__ f32x4 part[2][2][NW][64];  // [chunk parity][Ktil S^T, Qtil S^T][wave][lane]
@@ -163,18 +167,31 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
     const int vcol = 16 * vt + i;
     const int64_t sb = static_cast<int64_t>(head) * DV * DK;
     const int nch = (T + VC - 1) / VC;
-    auto tok = [&](int t) { return ((static_cast<int64_t>(b) * T + t) * H + h) * DV; };  // value rows
+    // Token rows of the value-shaped tensors: a wave-uniform element offset of
+    // (b, t0, h, column 16 vt) plus a 32-bit lane offset (row 4g + r of the
+    // chunk, column i); H * DV is at most 2^24, so the lane offsets fit.
+    const int HD = H * DV;
+    const int64_t cbase = (static_cast<int64_t>(b) * T * H + h) * DV + 16 * vt;
+    auto chunk_base = [&](int t0) { return cbase + static_cast<int64_t>(t0) * HD; };
+    int roff[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) roff[r] = (4 * g + r) * HD + i;
 
-    // ST lane (g, i): S^T[16w + 4g + r][vcol] = S[vcol][16w + 4g + r]
-    f32x4 ST = {0.f, 0.f, 0.f, 0.f};
-    if (a.S_in && w < NW) {
-        const float4 x = *reinterpret_cast<const float4 *>(a.S_in + sb + static_cast<int64_t>(vcol) * DK + 16 * w + 4 * g);
-        ST = f32x4{x.x, x.y, x.z, x.w};
+    // ST[j] lane (g, i): S^T[kr + 4g + r][vcol] = S[vcol][kr + 4g + r], kr = 16 (TPW w + j)
+    f32x4 ST[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        ST[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (a.S_in && w < NW) {
+            const float4 x = *reinterpret_cast<const float4 *>(a.S_in + sb + static_cast<int64_t>(vcol) * DK +
+                                                               16 * (TPW * w + j) + 4 * g);
+            ST[j] = f32x4{x.x, x.y, x.z, x.w};
+        }
     }
     const ChunkRec<DK> *R0 = rec + static_cast<int64_t>(head) * nch;
     const bool is_carry = w < NW, is_y = w == YW;
     struct Ops {
-        f32x4 kt, qt, aht, top, aqt;
+        f32x4 kt[TPW], qt[TPW], aht[TPW], top, aqt;
         float v[4], w[GATES2 ? 4 : 1], gc;
     };
     // Every wave issues the same loads whatever its role (an output-only wave
@@ -184,33 +201,57 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
     auto load = [&](int c, Ops &o) {  // past the end: the last chunk again (never used)
         const int cc = min(c, nch - 1);
         const ChunkRec<DK> &R = R0[cc];
-        o.kt = *reinterpret_cast<const f32x4 *>(&R.kt[i * DK + 16 * wc + 4 * g]);
-        o.qt = *reinterpret_cast<const f32x4 *>(&R.qt[i * DK + 16 * wc + 4 * g]);
-        o.aht = R.aht[wc][lane];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int kr = 16 * (TPW * wc + j);
+            o.kt[j] = *reinterpret_cast<const f32x4 *>(&R.kt[i * DK + kr + 4 * g]);
+            o.qt[j] = *reinterpret_cast<const f32x4 *>(&R.qt[i * DK + kr + 4 * g]);
+            o.aht[j] = R.aht[TPW * wc + j][lane];
+        }
         o.aqt = R.aqt[lane];
         o.top = R.top[lane];
         const int t0 = cc * VC, n = min(VC, T - t0);
+        const int64_t cb = chunk_base(t0);
+        const int last = (n - 1) * HD + i;  // rows past the end read the chunk's last row
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = min(4 * g + r, n - 1);
-            o.v[r] = IO::ld(a.v, tok(t0 + t) + vcol);
-            if constexpr (GATES2) o.w[r] = IO::ld(a.w, tok(t0 + t) + vcol);
+            const int off = 4 * g + r < n ? roff[r] : last;
+            o.v[r] = IO::ld(a.v, cb + off);
+            if constexpr (GATES2) o.w[r] = IO::ld(a.w, cb + off);
         }
         o.gc = DECAY ? R.gc[0] : 1.f;
     };
     // one chunk's step from its operand set
+    // rows 4g + r < n of a chunk's output (branch-free for whole chunks)
+    auto store_rows = [&](void *dst, int64_t cb, int n, const f32x4 &x) {
+        if (n == VC) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) IO::st(dst, cb + roff[r], x[r]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r < n) IO::st(dst, cb + roff[r], x[r]);
+        }
+    };
     auto step = [&](const Ops &cur, int c) {
         const int p = c & 1, t0 = c * VC, n = min(VC, T - t0);
+        const int64_t cb = chunk_base(t0);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         if (is_carry) {
             // partial Ktil S^T and Qtil S^T over this wave's key rows (two
             // accumulators per product keep the dependent chains short)
-            f32x4 pk0 = mfma4(cur.kt[0], ST[0], zero), pk1 = mfma4(cur.kt[1], ST[1], zero);
-            f32x4 pq0 = mfma4(cur.qt[0], ST[0], zero), pq1 = mfma4(cur.qt[1], ST[1], zero);
-            pk0 = mfma4(cur.kt[2], ST[2], pk0);
-            pk1 = mfma4(cur.kt[3], ST[3], pk1);
-            pq0 = mfma4(cur.qt[2], ST[2], pq0);
-            pq1 = mfma4(cur.qt[3], ST[3], pq1);
+            f32x4 pk0 = zero, pk1 = zero, pq0 = zero, pq1 = zero;
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                pk0 = mfma4(cur.kt[j][0], ST[j][0], pk0);
+                pk1 = mfma4(cur.kt[j][1], ST[j][1], pk1);
+                pq0 = mfma4(cur.qt[j][0], ST[j][0], pq0);
+                pq1 = mfma4(cur.qt[j][1], ST[j][1], pq1);
+                pk0 = mfma4(cur.kt[j][2], ST[j][2], pk0);
+                pk1 = mfma4(cur.kt[j][3], ST[j][3], pk1);
+                pq0 = mfma4(cur.qt[j][2], ST[j][2], pq0);
+                pq1 = mfma4(cur.qt[j][3], ST[j][3], pq1);
+            }
             part[p][0][w][lane] = pk0 + pk1;
             part[p][1][w][lane] = pq0 + pq1;
         }
@@ -243,37 +284,32 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
 #pragma unroll
             for (int j = 1; j < NW; ++j) z += part[p][0][j][lane];
             const f32x4 u = tv[p][lane] - z;
-            f32x4 d0 = mfma4(cur.aht[0], u[0], zero), d1 = mfma4(cur.aht[1], u[1], zero);
-            d0 = mfma4(cur.aht[2], u[2], d0);
-            d1 = mfma4(cur.aht[3], u[3], d1);
-            if constexpr (DECAY) ST = ST * cur.gc + (d0 + d1);
-            else ST += d0 + d1;
-            if (a.side_kind == kSideResidual && w == 0) {  // the chunk's residuals U
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (4 * g + r < n) IO::st(a.side, tok(t0 + 4 * g + r) + vcol, u[r]);
+            for (int j = 0; j < TPW; ++j) {
+                f32x4 d0 = mfma4(cur.aht[j][0], u[0], zero), d1 = mfma4(cur.aht[j][1], u[1], zero);
+                d0 = mfma4(cur.aht[j][2], u[2], d0);
+                d1 = mfma4(cur.aht[j][3], u[3], d1);
+                if constexpr (DECAY) ST[j] = ST[j] * cur.gc + (d0 + d1);
+                else ST[j] += d0 + d1;
             }
+            if (a.side_kind == kSideResidual && w == 0) store_rows(a.side, cb, n, u);  // the residuals U
         }
         if (is_y) {  // Y = Qtil S^T + (Aq Tc) V
             f32x4 y = part[p][1][0][lane];
 #pragma unroll
             for (int j = 1; j < NW; ++j) y += part[p][1][j][lane];
             y += y0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (4 * g + r < n) IO::st(a.out, tok(t0 + 4 * g + r) + vcol, y[r]);
-            if (a.side_kind == kSideValue) {  // the write values z
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (4 * g + r < n) IO::st(a.side, tok(t0 + 4 * g + r) + vcol, vb[r]);
-            }
+            store_rows(a.out, cb, n, y);
+            if (a.side_kind == kSideValue) store_rows(a.side, cb, n, vb);  // the write values z
         }
     };
     // A ring of NS operand sets: the loads run NS chunks ahead (the records
-    // come from L2 or HBM, a step takes a few hundred cycles); every trip
+    // come from L2 or HBM, a step takes about a microsecond); every trip
     // refills each set it consumes (past the end: the last chunk again,
-    // never used), so the loads in flight always form the same queue.
-    constexpr int NS = 4;
+    // never used), so the loads in flight always form the same queue.  Three
+    // sets keep the kernel under 256 registers a lane, so two four-wave
+    // workgroups share a CU.
+    constexpr int NS = 3;
     Ops o[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) load(j, o[j]);
@@ -291,9 +327,12 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
         if (c + j < nch) step(o[j], c + j);
     };
     static_for<NS>(tail);
-    if (a.S_out && is_carry)
-        *reinterpret_cast<float4 *>(a.S_out + sb + static_cast<int64_t>(vcol) * DK + 16 * w + 4 * g) =
-            make_float4(ST[0], ST[1], ST[2], ST[3]);
+    if (a.S_out && is_carry) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+            *reinterpret_cast<float4 *>(a.S_out + sb + static_cast<int64_t>(vcol) * DK + 16 * (TPW * w + j) + 4 * g) =
+                make_float4(ST[j][0], ST[j][1], ST[j][2], ST[j][3]);
+    }
 }
 
 

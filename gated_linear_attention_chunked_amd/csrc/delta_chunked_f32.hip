@@ -26,10 +26,11 @@
 namespace lam {
 namespace {
 
-template <int DK>
+template <int DK, bool GATES2>
 struct DeriveF32Lds {
     static constexpr int RS = DK + 4;  // row stride of the token-row tiles
-    alignas(16) float k[VC * RS], q[VC * RS], e[VC * RS];
+    alignas(16) float k[VC * RS], q[VC * RS];
+    alignas(16) float e[GATES2 ? VC * RS : 4];  // erase-gated keys b * k (Gated DeltaNet-2)
     alignas(16) float lt[VC * VLTS];  // N diag(beta), strictly lower, by column
     alignas(16) float am[VC][VC + 1]; // Aq, row-major
     alignas(16) f32x4 top[64];        // Tc, A-operand order
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(64) void delta_f32_derive_kernel(DeltaArgs a, Chunk
                                                               unsigned int *status) {
     constexpr bool kDecay = VARIANT != kDeltaNet;
     constexpr bool kGates2 = VARIANT == kGatedDeltaNet2;
-    using L = DeriveF32Lds<DK>;
+    using L = DeriveF32Lds<DK, kGates2>;
     constexpr int RS = L::RS;
     __shared__ L s;
     const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
@@ -68,18 +69,17 @@ __global__ __launch_bounds__(64) void delta_f32_derive_kernel(DeltaArgs a, Chunk
 
     // ---- token rows (past the end: zero) and gates (past the end: no decay, beta 0)
     const int64_t tk = (static_cast<int64_t>(b) * T + t0) * H + h;  // token index of row 0
-    // (loads read clamped rows inside the sequence; padding rows are zeroed after)
-    for (int e = lane; e < VC * DK; e += 64) {
-        const int t = e / DK, j = e % DK;
+    // Four elements a lane per load, every load issued before the first wait;
+    // loads read clamped rows inside the sequence, padding rows are zeroed.
+    constexpr int Q4 = DK / 4, NL = VC * Q4 / 64;  // 4-element groups per row, per lane
+    float4 kr[NL], qr[NL], br[kGates2 ? NL : 1];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+        const int e = lane + 64 * u, t = e / Q4, j = 4 * (e % Q4);
         const int64_t gi = (tk + static_cast<int64_t>(min(t, n - 1)) * H) * DK + j;
-        const bool ok = t < n;
-        const float kv = IO::ld(a.k, gi), qv = IO::ld(a.q, gi);
-        s.k[t * RS + j] = ok ? kv : 0.f;
-        s.q[t * RS + j] = ok ? qv : 0.f;
-        if constexpr (kGates2) {
-            const float bv = IO::ld(a.erase_b, gi);
-            s.e[t * RS + j] = ok ? kv * bv : 0.f;
-        }
+        kr[u] = IO::ld4(a.k, gi);
+        qr[u] = IO::ld4(a.q, gi);
+        if constexpr (kGates2) br[u] = IO::ld4(a.erase_b, gi);
     }
     if (lane < VC) {
         const bool ok = lane < n;
@@ -98,6 +98,22 @@ __global__ __launch_bounds__(64) void delta_f32_derive_kernel(DeltaArgs a, Chunk
         s.bt[lane] = bv;
         s.sc[lane] = bv * exp2f(gC - gl);
         if (lane == 0) rec[blockIdx.x].gc = f32x4{exp2f(gC), exp2f(gC), exp2f(gC), exp2f(gC)};
+    }
+    // (selected component by component: a select of whole vectors becomes a
+    // select of their addresses in private memory)
+    auto keep = [](bool ok, float4 x) {
+        return make_float4(ok ? x.x : 0.f, ok ? x.y : 0.f, ok ? x.z : 0.f, ok ? x.w : 0.f);
+    };
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+        const int e = lane + 64 * u, t = e / Q4, j = 4 * (e % Q4);
+        const bool ok = t < n;
+        *reinterpret_cast<float4 *>(&s.k[t * RS + j]) = keep(ok, kr[u]);
+        *reinterpret_cast<float4 *>(&s.q[t * RS + j]) = keep(ok, qr[u]);
+        if constexpr (kGates2) {
+            const float4 ke = make_float4(kr[u].x * br[u].x, kr[u].y * br[u].y, kr[u].z * br[u].z, kr[u].w * br[u].w);
+            *reinterpret_cast<float4 *>(&s.e[t * RS + j]) = keep(ok, ke);
+        }
     }
     __syncthreads();
 

@@ -28,6 +28,10 @@ struct IoF32 {
     static __device__ __forceinline__ void st(void *p, int64_t i, float x) {
         static_cast<float *>(p)[i] = x;
     }
+    // elements i .. i + 3 (i a multiple of 4 in a 16-byte aligned tensor)
+    static __device__ __forceinline__ float4 ld4(const void *p, int64_t i) {
+        return *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+    }
 };
 struct IoBF16 {
     using T = uint16_t;
@@ -36,6 +40,12 @@ struct IoBF16 {
     }
     static __device__ __forceinline__ void st(void *p, int64_t i, float x) {
         static_cast<uint16_t *>(p)[i] = f32_to_bf16_bits(x);
+    }
+    // elements i .. i + 3 (i a multiple of 4 in an 8-byte aligned tensor)
+    static __device__ __forceinline__ float4 ld4(const void *p, int64_t i) {
+        const uint2 x = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + i);
+        return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                           __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
     }
 };
 

@@ -57,7 +57,13 @@ extern "C" lam_status lam_forward_noalloc(int variant, int dtype, int64_t B, int
     size_t need = 0;
     lam_status st = lam_forward_workspace_size(variant, dtype, B, T, H, dk, dv, algo, &need);
     if (st != LAM_OK) return st;
-    if (need > kScratchBytes) return LAM_ERR_SCRATCH_LIMIT;
+    if (need > kScratchBytes) {
+        // auto: the recurrent schedule needs no workspace; an explicit
+        // chunked request that does not fit is refused
+        if (algo != LAM_ALGO_AUTO) return LAM_ERR_SCRATCH_LIMIT;
+        algo = LAM_ALGO_RECURRENT;
+        need = 0;
+    }
     void *ws = nullptr;
     if (need > 0) {
         if (scratch_ptr(&ws) != hipSuccess) return LAM_ERR_HIP;

@@ -380,16 +380,19 @@ lam_status lam_vla_step_ratio(int dtype, int64_t N, int64_t H, int64_t d, const 
 /*
  * lam_forward for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation).  The
- * same arguments, schedules, kernels and results as lam_forward, with the
- * workspace replaced by a fixed device array inside the library of
- * LAM_NOALLOC_SCRATCH_BYTES (32 MiB; it covers the chunked delta schedules at
- * B8 T4096 H8 d128, 24.1 MB), held on each GPU the library runs on until the
- * process ends.  A call whose lam_forward_workspace_size exceeds it returns
- * LAM_ERR_SCRATCH_LIMIT before any HIP call.  Nothing is allocated or freed;
- * the first call on a device looks up that device's array address (the
- * stream must belong to the current device).  Every call on one GPU shares
- * that GPU's array: calls that may overlap on one GPU (other streams, other
- * threads) race and must be ordered by the caller.
+ * same arguments, kernels and results as lam_forward, with the workspace
+ * replaced by a fixed device array inside the library of
+ * LAM_NOALLOC_SCRATCH_BYTES (32 MiB: the bf16 chunked schedule of Gated
+ * DeltaNet at B8 T4096 H8 d128 needs 24.1 MB; the fp32 chunk records need
+ * 26,640 B per (b, h, 16 tokens) at dk = 128), held on each GPU the library
+ * runs on until the process ends.  With LAM_ALGO_AUTO, a call whose chunked
+ * workspace exceeds the array runs the recurrent schedule (no workspace)
+ * instead; with LAM_ALGO_CHUNKED such a call returns LAM_ERR_SCRATCH_LIMIT
+ * before any HIP call.  Nothing is allocated or freed; the first call on a
+ * device looks up that device's array address (the stream must belong to the
+ * current device).  Every call on one GPU shares that GPU's array: calls that
+ * may overlap on one GPU (other streams, other threads) race and must be
+ * ordered by the caller.
  */
 #define LAM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 lam_status lam_forward_noalloc(int variant, int dtype, int64_t B, int64_t T, int64_t H,

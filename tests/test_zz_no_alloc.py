@@ -16,14 +16,15 @@ SCRATCH_LIMIT = 4
 SCRATCH_BYTES = 32 << 20
 
 
-def _call_noalloc(lib, w, g, out, st_out):
+def _call_noalloc(lib, w, g, out, st_out, algo=0):
     import torch
 
     var = {"deltanet": 0, "gdn": 1, "kda": 2, "gdn2": 3}[w.variant]
+    dt = {"f32": 0, "bf16": 1}[w.dtype]
     p = lambda t: None if t is None else t.data_ptr()
-    return lib.lam_forward_noalloc(var, 1, w.B, w.T, w.H, w.dk, w.dv, p(g["q"]), p(g["k"]), p(g["v"]),
+    return lib.lam_forward_noalloc(var, dt, w.B, w.T, w.H, w.dk, w.dv, p(g["q"]), p(g["k"]), p(g["v"]),
                                    p(g.get("alpha")), p(g.get("erase_b")), p(g.get("write_w")),
-                                   p(g["beta"]), None, p(out), p(st_out), 0,
+                                   p(g["beta"]), None, p(out), p(st_out), algo,
                                    torch.cuda.current_stream().cuda_stream)
 
 
@@ -60,5 +61,34 @@ def test_noalloc_refuses_calls_beyond_its_scratch():
     assert lam.workspace_size("kda", "bf16", 2, 4096, 8, 128, 128) > SCRATCH_BYTES
     fake = torch.empty(16, dtype=torch.bfloat16, device="cuda")  # never touched: refused first
     g = {k_: fake for k_ in ("q", "k", "v", "alpha", "beta")}
-    assert _call_noalloc(lib, w, g, fake, None) == SCRATCH_LIMIT
+    assert _call_noalloc(lib, w, g, fake, None, algo=2) == SCRATCH_LIMIT
     assert b"scratch" in lib.lam_status_string(SCRATCH_LIMIT)
+
+
+def test_noalloc_auto_beyond_its_scratch_runs_recurrent():
+    """With algo auto, a call whose fp32 chunk records outgrow the array runs
+    the recurrent schedule: bit for bit lam_forward's recurrent result, and the
+    oracle's at the fp32 gate on sampled chains; a smaller call after it takes
+    the chunked schedule through the array again."""
+    import torch
+
+    import gated_linear_attention_chunked_amd as lam
+
+    lib = lam.library()
+    big = I.Workload("gdn_f32_B2_T4096_H4_d128", "gdn", "f32", 2, 4096, 4, 128, 128, seed=8802)
+    small = I.Workload("gdn_f32_B1_T99_H2_d64", "gdn", "f32", 1, 99, 2, 64, 64, seed=8803)
+    assert lam.workspace_size("gdn", "f32", 2, 4096, 4, 128, 128) > SCRATCH_BYTES
+    assert 0 < lam.workspace_size("gdn", "f32", 1, 99, 2, 64, 64) <= SCRATCH_BYTES
+    for w, algo, chains in ((big, "recurrent", [(0, 1), (1, 3)]), (small, "chunked", None)):
+        x = I.make_inputs(w)
+        g = I.to_device(x, "f32", "cuda")
+        out = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
+        st = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
+        assert _call_noalloc(lib, w, g, out, st) == 0
+        torch.cuda.synchronize()
+        got = (out.cpu().numpy().astype(np.float64), st.cpu().numpy().astype(np.float64))
+        ref_fwd = U.run_gpu(w, x, algo=algo)
+        assert np.array_equal(got[0], ref_fwd[0]) and np.array_equal(got[1], ref_fwd[1]), w.name
+        if chains is not None:
+            got = U.pick_chains(got, chains)
+        U.check(w, got, U.run_oracle(w, x, chains=chains), label=w.name + " noalloc auto")
