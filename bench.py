@@ -79,6 +79,8 @@ JOBS = {
     "route_bf16_B8_T4096_N1024_D1024": ("route", "gdn_bf16_B8_T4096_H8_d128", {"D": 1024}),
     "gdn_loglinear_bf16_B8_T4096_H8_d128": ("loglinear", "gdn_bf16_B8_T4096_H8_d128", {}),
     "loglinear_lambda_bf16_B8_T4096_H8_L13": ("lambda", "gdn_bf16_B8_T4096_H8_d128", {"nh": 26}),
+    # the throughput workload's forward with fp32 storage (the fp32 chunked form)
+    "gdn_f32_B8_T4096_H8_d128": ("forward", "gdn_bf16_B8_T4096_H8_d128", {"dtype": "f32"}),
 }
 
 
@@ -140,6 +142,7 @@ def job_counts(kind: str, w, extra=None):
 
 KERNEL_SOURCES = {  # schedule -> kernel source per variant family
     ("chunked", "delta"): "delta_chunked.hip",
+    ("chunked", "delta_f32"): "delta_chunked_f32.hip",
     ("chunked", "kda"): "kda_chunked.hip",
     ("chunked", "vla"): "vla_chunked.hip",
     ("recurrent", "delta"): "delta_recurrent.hip",
@@ -148,6 +151,7 @@ KERNEL_SOURCES = {  # schedule -> kernel source per variant family
     ("step", "delta"): "delta_step.hip",
     ("step", "vla"): "vla_recurrent.hip",
     ("backward", "delta"): "delta_backward.hip",
+    ("backward_chunked", "delta"): "delta_chunked_f32.hip",
     ("route", "delta"): "route.hip",
     ("loglinear", "delta"): "loglin_recurrent.hip",
     ("lambda", "delta"): "loglin_recurrent.hip",
@@ -155,11 +159,21 @@ KERNEL_SOURCES = {  # schedule -> kernel source per variant family
 SHARED_HEADERS = ("chunk_common.h", "chunk_f32.h", "device_common.h", "lam_internal.h")
 
 
-def kernel_source_hash(ran: str, variant: str):
+def bf16_matrix_schedule(w) -> bool:
+    """The delta-rule chunked schedules that feed bf16 operands to the matrix
+    cores: bf16 storage at dk 64 or 128 (every other delta-rule shape takes
+    the fp32 chunked form)."""
+    return w.dtype == "bf16" and w.dk in (64, 128)
+
+
+def kernel_source_hash(ran: str, w):
     """(source file name, sha256 over that source and the shared headers)."""
     import hashlib
 
+    variant = w.variant
     fam = variant if variant in ("kda", "vla") else "delta"
+    if ran == "chunked" and fam == "delta" and not bf16_matrix_schedule(w):
+        fam = "delta_f32"
     name = KERNEL_SOURCES.get((ran, fam)) or KERNEL_SOURCES[(ran, "delta")]
     csrc = os.path.join(ROOT, "gated_linear_attention_chunked_amd", "csrc")
     h = hashlib.sha256()
@@ -176,7 +190,7 @@ def measured_traffic(w, ran: str, name=None):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(path))["workloads"][name or w.name]
-        name, sha = kernel_source_hash(ran, w.variant)
+        name, sha = kernel_source_hash(ran, w)
     except (OSError, KeyError, ValueError):
         return None
     if rec.get("schedule") != ran or rec.get("source") != name or rec.get("sha256") != sha:
@@ -340,6 +354,8 @@ def main():
         sys.exit(2)
     kind, extra = (job[0], job[2]) if job else ("decode" if decode else "forward", {})
     w = I.DECODE_WORKLOADS[name] if decode else I.WORKLOADS[job[1] if job else name]
+    if extra.get("dtype"):  # a forward workload's shapes with another storage dtype
+        w = w.replace(name=name, dtype=extra["dtype"])
     x = I.make_inputs(w)
     dev = torch.device("cuda:0")
     copies = [I.to_device(x, w.dtype, dev) for _ in range(max(1, args.copies))]
@@ -397,7 +413,7 @@ def main():
     # one caller-owned workspace for every step: the steps run in order on
     # one stream, so each may reuse it
     if kind == "backward":
-        nws = lam.backward_workspace_size(w.variant, w.dtype, w.B, w.T, w.H, w.dk, w.dv)
+        nws = lam.backward_workspace_size(w.variant, w.dtype, w.B, w.T, w.H, w.dk, w.dv, algo=args.algo)
     elif decode or kind in ("route", "loglinear", "lambda"):
         nws = 0
     elif w.variant == "vla":
@@ -410,7 +426,7 @@ def main():
         g, o = copies[i % len(copies)], outs[i % len(outs)]
         if kind == "backward":
             lam.backward(w.variant, g["q"], g["k"], g["v"], g["beta"], g["dout"], alpha=g.get("alpha"),
-                         erase_b=g.get("erase_b"), write_w=g.get("write_w"), workspace=wsp)
+                         erase_b=g.get("erase_b"), write_w=g.get("write_w"), algo=args.algo, workspace=wsp)
         elif kind == "side":
             lam.forward(w.variant, g["q"], g["k"], g["v"], g["beta"], alpha=g.get("alpha"), erase_b=g.get("erase_b"),
                         write_w=g.get("write_w"), algo=args.algo, out=o[0], state_out=o[1], workspace=wsp,
@@ -476,7 +492,11 @@ def main():
 
     tokens = w.B * w.T
     value = tokens * args.steps / wall
-    if kind in ("backward", "route", "loglinear", "lambda"):
+    if kind == "backward":
+        # the chunked adjoint (fp32 matrix cores) for every variant but Kimi Delta, unless told otherwise
+        chunked_bwd = w.variant != "kda" and w.T > 0 and args.algo != "recurrent"
+        ran = "backward_chunked" if chunked_bwd else "backward"
+    elif kind in ("route", "loglinear", "lambda"):
         ran = kind
     elif decode:
         ran = "step"
@@ -486,12 +506,18 @@ def main():
     else:
         ran = args.algo if args.algo != "auto" else lam.select_algo(w.variant, w.dtype, w.T, w.dk, w.dv)
     # arithmetic type: the recurrent schedules and fp32 storage compute in
-    # fp32; the delta-rule chunked schedule on bf16 storage feeds bf16
-    # operands to the matrix cores (fp32 accumulate, fp32 state); the VLA
-    # chunked schedule uses fp32 matrix-core products for every dtype
-    arith_dtype = "bf16" if (ran in ("chunked", "route") and w.dtype == "bf16" and w.variant != "vla") else "f32"
+    # fp32; the delta-rule chunked schedules on bf16 storage at dk 64 / 128
+    # feed bf16 operands to the matrix cores (fp32 accumulate, fp32 state);
+    # the VLA chunked schedule and the fp32 chunked delta form (every other
+    # shape) use fp32 matrix-core products
+    if ran == "route":
+        arith_dtype = "bf16" if w.dtype == "bf16" else "f32"
+    elif ran == "chunked" and w.variant != "vla" and bf16_matrix_schedule(w):
+        arith_dtype = "bf16"
+    else:
+        arith_dtype = "f32"
     mean_launch_s = mean_launch_ms / 1e3
-    if job:
+    if job and kind != "forward":
         abytes, aflops = job_counts(kind, w, extra)
     else:
         abytes = algorithmic_bytes(w, decode)
@@ -500,7 +526,7 @@ def main():
     # the binding roofline: HBM bytes, or the algorithmic flops on the unit
     # the schedule computes them with (matrix cores for the chunked schedules,
     # the fp32 vector ALU for the recurrent ones), whichever takes longer
-    if ran in ("chunked", "route"):
+    if ran in ("chunked", "route", "backward_chunked"):
         cpeak, cbound = (MFMA_BF16_PEAK_TFS if arith_dtype == "bf16" else FP32_PEAK_TFS), "mfma"
     elif ran == "step":
         cpeak, cbound = FP32_PEAK_TFS, "alu"
@@ -543,7 +569,7 @@ def main():
         del src, dst
 
     cpu = None
-    if not args.no_cpu_baseline and job:
+    if not args.no_cpu_baseline and job and kind != "forward":
         rows = min(w.B, args.cpu_rows or 1)
         cpu = cpu_baseline_job(kind, w, x, extra, rows, args.cpu_seconds)
     elif not args.no_cpu_baseline:
@@ -561,7 +587,7 @@ def main():
     }
     line = {
         "metric": "gated delta-rule fwd tokens/s, B8 T4096 H8 d128; % of HBM/MFMA roofline"
-        if name == I.METRIC_WORKLOAD else (job_metric[kind] if job else
+        if name == I.METRIC_WORKLOAD else (job_metric[kind] if kind in job_metric else
                                            (f"{w.variant} decode tokens/s (one token per stream per call"
                                             f"{', ratio read' if w.variant == 'vla' else ''}), {name}"
                                             if decode else f"{w.variant} fwd tokens/s, {name}")),

@@ -93,9 +93,9 @@ def library() -> ctypes.CDLL:
             lib.lam_loglinear_levels.restype = i64
             lib.lam_loglinear_lambda.argtypes = [ci, i64, i64, i64] + [vp] * 5 + [vp]
             lib.lam_loglinear_lambda.restype = ci
-            lib.lam_backward.argtypes = [ci, ci, i64, i64, i64, i64, i64] + [vp] * 18 + [vp, sz, vp]
+            lib.lam_backward.argtypes = [ci, ci, i64, i64, i64, i64, i64] + [vp] * 18 + [ci, vp, sz, vp]
             lib.lam_backward.restype = ci
-            lib.lam_backward_workspace_size.argtypes = [ci, ci, i64, i64, i64, i64, i64, ctypes.POINTER(sz)]
+            lib.lam_backward_workspace_size.argtypes = [ci, ci, i64, i64, i64, i64, i64, ci, ctypes.POINTER(sz)]
             lib.lam_backward_workspace_size.restype = ci
             lib.lam_step.argtypes = [ci, ci, i64, i64, i64, i64] + [vp] * 9 + [vp]
             lib.lam_step.restype = ci
@@ -132,11 +132,11 @@ def workspace_size(variant, dtype, B, T, H, dk, dv, algo="auto") -> int:
     return int(n.value)
 
 
-def backward_workspace_size(variant, dtype, B, T, H, dk, dv) -> int:
+def backward_workspace_size(variant, dtype, B, T, H, dk, dv, algo="auto") -> int:
     """Bytes of workspace ``backward`` needs for these arguments."""
     n = ctypes.c_size_t(0)
     rc = library().lam_backward_workspace_size(VARIANTS[variant], DTYPES[dtype], B, T, H, dk, dv,
-                                               ctypes.byref(n))
+                                               ALGOS[algo], ctypes.byref(n))
     if rc != 0:
         raise LamError(rc, "lam_backward_workspace_size")
     return int(n.value)
@@ -394,12 +394,13 @@ def route(h, s, P, *, stream=None):
 
 
 def backward(variant, q, k, v, beta, dout, alpha=None, erase_b=None, write_w=None, state_in=None,
-             dstate_out=None, *, with_dstate_in=True, stream=None, workspace=None):
+             dstate_out=None, *, with_dstate_in=True, algo="auto", stream=None, workspace=None):
     """Gradients of sum(dout * out) + sum(dstate_out * state_out) for
     ``forward(variant, q, k, v, beta, alpha, erase_b, write_w, state_in)``.
 
     Inputs as ``forward``; dout [B,T,H,dv] in their dtype; dstate_out fp32
-    [B,H,dv,dk] or None.  Returns a dict of fp32 tensors: dq, dk, dv, dbeta,
+    [B,H,dv,dk] or None; algo "auto" / "recurrent" / "chunked" as
+    ``forward``.  Returns a dict of fp32 tensors: dq, dk, dv, dbeta,
     dstate_in (None unless ``with_dstate_in``), and dalpha ("gdn", "gdn2",
     "kda"), derase_b and dwrite_w ("gdn2").
     """
@@ -440,13 +441,13 @@ def backward(variant, q, k, v, beta, dout, alpha=None, erase_b=None, write_w=Non
         g["derase_b"] = torch.empty((B, T, H, dk), **f32)
         g["dwrite_w"] = torch.empty((B, T, H, dv), **f32)
     ws = _workspace(backward_workspace_size(variant, {torch.float32: "f32", torch.bfloat16: "bf16"}[dt],
-                                            B, T, H, dk, dv), workspace, dev, stream)
+                                            B, T, H, dk, dv, algo), workspace, dev, stream)
     rc = library().lam_backward(var, _dtype_code(q), B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(alpha), _ptr(erase_b), _ptr(write_w), _ptr(beta), _ptr(state_in),
                                 _ptr(dout), _ptr(dstate_out), _ptr(g["dq"]), _ptr(g["dk"]),
                                 _ptr(g["dv"]), _ptr(g.get("dalpha")), _ptr(g.get("derase_b")),
                                 _ptr(g.get("dwrite_w")), _ptr(g["dbeta"]), _ptr(g["dstate_in"]),
-                                _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+                                ALGOS[algo], _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     if rc != 0:
         raise LamError(rc, "lam_backward")
     _after_call(ws, "lam_backward")

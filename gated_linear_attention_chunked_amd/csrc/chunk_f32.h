@@ -124,6 +124,9 @@ struct ScanArgs {
     float *S_out;            // [B,H,DV,DK] fp32 or NULL
     void *side;              // per-token routing signal [B,T,H,DV] or NULL
     int side_kind;           // kSideResidual (U) or kSideValue (z)
+    // the backward pass's forward recompute (KEEP) also writes:
+    float *s_chunks;         // S^T at every chunk start, [B*H][chunks][DK][DV] fp32
+    float *u_f32;            // the residuals U, [B,T,H,DV] fp32
 };
 
 // Key tiles of S^T per carry wave of the state kernel: one at DK = 32, two
@@ -146,8 +149,10 @@ __host__ __device__ constexpr int state_v_wave() { return state_carries<DK>() < 
 // 16 x 16 tiles of S^T at key rows 16 (TPW w + j) .. + 15 and the workgroup's
 // value columns; the products over the key dimension are summed across the
 // waves through LDS (fixed order, so every wave forms the same sums).
-// DECAY: the records carry gC; GATES2: the targets are z = w * v.
-template <typename IO, int DK, bool DECAY, bool GATES2>
+// DECAY: the records carry gC; GATES2: the targets are z = w * v; KEEP:
+// also the state at every chunk start and U in fp32 (the backward pass's
+// forward recompute).
+template <typename IO, int DK, bool DECAY, bool GATES2, bool KEEP = false>
 __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(ScanArgs a,
                                                                              const ChunkRec<DK> *__restrict__ rec) {
     constexpr int TPW = state_tpw<DK>();
@@ -221,7 +226,6 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
         }
         o.gc = DECAY ? R.gc[0] : 1.f;
     };
-    // one chunk's step from its operand set
     // rows 4g + r < n of a chunk's output (branch-free for whole chunks)
     auto store_rows = [&](void *dst, int64_t cb, int n, const f32x4 &x) {
         if (n == VC) {
@@ -233,10 +237,18 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
                 if (4 * g + r < n) IO::st(dst, cb + roff[r], x[r]);
         }
     };
+    // one chunk's step from its operand set
     auto step = [&](const Ops &cur, int c) {
         const int p = c & 1, t0 = c * VC, n = min(VC, T - t0);
         const int64_t cb = chunk_base(t0);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        if (KEEP && is_carry) {  // the state at this chunk's start, S^T rows
+            float *dst = a.s_chunks + (static_cast<int64_t>(head) * nch + c) * DK * DV + vcol;
+#pragma unroll
+            for (int j = 0; j < TPW; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[static_cast<int64_t>(16 * (TPW * w + j) + 4 * g + r) * DV] = ST[j][r];
+        }
         if (is_carry) {
             // partial Ktil S^T and Qtil S^T over this wave's key rows (two
             // accumulators per product keep the dependent chains short)
@@ -293,13 +305,18 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
                 else ST[j] += d0 + d1;
             }
             if (a.side_kind == kSideResidual && w == 0) store_rows(a.side, cb, n, u);  // the residuals U
+            if (KEEP && w == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g + r < n) a.u_f32[cb + roff[r]] = u[r];
+            }
         }
         if (is_y) {  // Y = Qtil S^T + (Aq Tc) V
             f32x4 y = part[p][1][0][lane];
 #pragma unroll
             for (int j = 1; j < NW; ++j) y += part[p][1][j][lane];
             y += y0;
-            store_rows(a.out, cb, n, y);
+            if (a.out) store_rows(a.out, cb, n, y);
             if (a.side_kind == kSideValue) store_rows(a.side, cb, n, vb);  // the write values z
         }
     };
@@ -335,6 +352,209 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
     }
 }
 
+
+
+// ------------------------------------------------------------ adjoint scan
+// Reverse mode of the state step above.  With G = dL/dS^T at a chunk's end
+// (G' below) and dY the output cotangents of the chunk, the adjoint of
+//   U = Tc Z - Ktil S^T,  Y = diag(gamma) Q S^T + Aq U,  S'^T = gC S^T + Ahat^T U
+// is, per chunk in reverse,
+//   dX   = dU-adjoint of the solve = (Aq Tc)^T dY + Ahat' G',  Ahat' = Tc^T Ahat,
+//   G    = gC G' + (diag(gamma) Q)^T dY - (diag(gamma) E)^T dX,
+// and dX is the gradient of the chunk's targets Z.  It has the state step's
+// shape: one product over the key dimension (Ahat' G') summed across the
+// waves, a state-independent term ((Aq Tc)^T dY) formed beside it, and a
+// rank-16 update of the carried tiles.  Ahat' and the transposed operands
+// come from the same derivation, in this record.
+template <int DK>
+struct AdjRec {
+    float ap[VC * DK];          // Ahat' = Tc^T Ahat, rows t
+    f32x4 gqt[DK / 16][64];     // (diag(gamma) Q)^T tiles: lane (g, i) of tile j holds gamma_{4g+m} Q[4g + m][16j + i]
+    f32x4 get[DK / 16][64];     // (diag(gamma) E)^T tiles, the same order
+    f32x4 aqtt[64];             // (Aq Tc)^T, A-operand order
+    f32x4 gc;                   // gC in every slot; unused without decay
+};
+
+struct AdjArgs {
+    int64_t B, T, H;
+    int dv;                      // value width DV (a multiple of 16)
+    const void *dy;              // output cotangents [B,T,H,DV], storage dtype
+    const void *v, *w;           // targets and write gates (Gated DeltaNet-2), else NULL
+    const float *dS_in;          // cotangent of the final state [B,H,DV,DK] or NULL (zero)
+    float *dS_out;               // cotangent of the initial state [B,H,DV,DK] or NULL
+    float *ds_chunks;            // G' at every chunk end (the same layout as S^T rows per chunk)
+    float *dx;                   // dX [B,T,H,DV] fp32
+    float *dv_out, *dw_out;      // gradients of v and (Gated DeltaNet-2) w, [B,T,H,DV] fp32
+};
+
+// One workgroup per (b, h, 16 value columns), chunks in reverse; roles as
+// in chunk_state_kernel (carry waves hold TPW tiles of G^T, the wave VW
+// forms the state-independent term).
+template <typename IO, int DK, bool DECAY, bool GATES2>
+__global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_adjoint_kernel(AdjArgs a,
+                                                                               const AdjRec<DK> *__restrict__ rec) {
+    constexpr int TPW = state_tpw<DK>();
+    constexpr int NW = state_carries<DK>();
+    constexpr int VW = state_v_wave<DK>();
+    __shared__ f32x4 part[2][NW][64];  // [step parity][wave][lane]: Ahat' G' partials
+    __shared__ f32x4 tv[2][64];        // [step parity] (Aq Tc)^T dY
+    const int T = static_cast<int>(a.T), H = static_cast<int>(a.H);
+    int head, vt;
+    const int DV = a.dv;
+    xcd_group_map(blockIdx.x, static_cast<int>(a.B * a.H), DV / 16, head, vt);
+    const int b = head / H, h = head % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, i = lane & 15;
+    const int vcol = 16 * vt + i;
+    const int64_t sb = static_cast<int64_t>(head) * DV * DK;
+    const int nch = (T + VC - 1) / VC;
+    const int HD = H * DV;
+    const int64_t cbase = (static_cast<int64_t>(b) * T * H + h) * DV + 16 * vt;
+    auto chunk_base = [&](int t0) { return cbase + static_cast<int64_t>(t0) * HD; };
+    int roff[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) roff[r] = (4 * g + r) * HD + i;
+
+    // GT[j] lane (g, i): G^T[kr + 4g + r][vcol], kr = 16 (TPW w + j)
+    f32x4 GT[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        GT[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (a.dS_in && w < NW) {
+            const float4 x = *reinterpret_cast<const float4 *>(a.dS_in + sb + static_cast<int64_t>(vcol) * DK +
+                                                               16 * (TPW * w + j) + 4 * g);
+            GT[j] = f32x4{x.x, x.y, x.z, x.w};
+        }
+    }
+    const AdjRec<DK> *R0 = rec + static_cast<int64_t>(head) * nch;
+    const bool is_carry = w < NW;
+    struct Ops {
+        f32x4 ap[TPW], gq[TPW], ge[TPW], aq;
+        float y[4], v[GATES2 ? 4 : 1], w[GATES2 ? 4 : 1], gc;
+    };
+    const int wc = min(w, NW - 1);
+    // step s works on chunk nch - 1 - s; past the end: chunk 0 again (never used)
+    auto load = [&](int st, Ops &o) {
+        const int cc = max(nch - 1 - st, 0);
+        const AdjRec<DK> &R = R0[cc];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int kr = 16 * (TPW * wc + j);
+            o.ap[j] = *reinterpret_cast<const f32x4 *>(&R.ap[i * DK + kr + 4 * g]);
+            o.gq[j] = R.gqt[TPW * wc + j][lane];
+            o.ge[j] = R.get[TPW * wc + j][lane];
+        }
+        o.aq = R.aqtt[lane];
+        const int t0 = cc * VC, n = min(VC, T - t0);
+        const int64_t cb = chunk_base(t0);
+        const int last = (n - 1) * HD + i;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int off = 4 * g + r < n ? roff[r] : last;
+            o.y[r] = IO::ld(a.dy, cb + off);
+            if constexpr (GATES2) {
+                o.v[r] = IO::ld(a.v, cb + off);
+                o.w[r] = IO::ld(a.w, cb + off);
+            }
+        }
+        o.gc = DECAY ? R.gc[0] : 1.f;
+    };
+    auto step = [&](const Ops &cur, int st) {
+        const int c = nch - 1 - st, p = st & 1, t0 = c * VC, n = min(VC, T - t0);
+        const int64_t cb = chunk_base(t0);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        if (is_carry) {
+            // G' (the cotangent of the state after this chunk), kept for the
+            // gradient kernel
+            float *dst = a.ds_chunks + (static_cast<int64_t>(head) * nch + c) * DK * DV + vcol;
+#pragma unroll
+            for (int j = 0; j < TPW; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[static_cast<int64_t>(16 * (TPW * w + j) + 4 * g + r) * DV] = GT[j][r];
+            // partial Ahat' G' over this wave's key rows
+            f32x4 pk0 = zero, pk1 = zero;
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                pk0 = mfma4(cur.ap[j][0], GT[j][0], pk0);
+                pk1 = mfma4(cur.ap[j][1], GT[j][1], pk1);
+                pk0 = mfma4(cur.ap[j][2], GT[j][2], pk0);
+                pk1 = mfma4(cur.ap[j][3], GT[j][3], pk1);
+            }
+            part[p][w][lane] = pk0 + pk1;
+        }
+        // dY's rows (zero past the end): the B operand of (Aq Tc)^T dY and of the update
+        f32x4 yb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yb[r] = 4 * g + r < n ? cur.y[r] : 0.f;
+        if (w == VW) {
+            f32x4 a0 = mfma4(cur.aq[0], yb[0], zero), a1 = mfma4(cur.aq[1], yb[1], zero);
+            a0 = mfma4(cur.aq[2], yb[2], a0);
+            a1 = mfma4(cur.aq[3], yb[3], a1);
+            tv[p][lane] = a0 + a1;
+        }
+        lds_sync();
+        if (is_carry) {
+            // dX = (Aq Tc)^T dY + Ahat' G' (summed in a fixed order), then
+            // G^T <- gC G^T + (gamma Q)^T dY - (gamma E)^T dX
+            f32x4 z = part[p][0][lane];
+#pragma unroll
+            for (int j = 1; j < NW; ++j) z += part[p][j][lane];
+            const f32x4 dx = tv[p][lane] + z;
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                f32x4 d0 = mfma4(cur.gq[j][0], yb[0], zero), d1 = mfma4(cur.gq[j][1], yb[1], zero);
+                d0 = mfma4(cur.gq[j][2], yb[2], d0);
+                d1 = mfma4(cur.gq[j][3], yb[3], d1);
+                d0 = mfma4(cur.ge[j][0], -dx[0], d0);
+                d1 = mfma4(cur.ge[j][1], -dx[1], d1);
+                d0 = mfma4(cur.ge[j][2], -dx[2], d0);
+                d1 = mfma4(cur.ge[j][3], -dx[3], d1);
+                if constexpr (DECAY) GT[j] = GT[j] * cur.gc + (d0 + d1);
+                else GT[j] += d0 + d1;
+            }
+            if (w == 0) {  // dX, and the gradients of the targets z = w * v (z = v)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (4 * g + r < n) {
+                        const int64_t o = cb + roff[r];
+                        a.dx[o] = dx[r];
+                        if constexpr (GATES2) {
+                            a.dv_out[o] = cur.w[r] * dx[r];
+                            a.dw_out[o] = cur.v[r] * dx[r];
+                        } else {
+                            a.dv_out[o] = dx[r];
+                        }
+                    }
+                }
+            }
+        }
+    };
+    constexpr int NS = 3;
+    Ops o[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) load(j, o[j]);
+    int st = 0;
+    for (; st + NS <= nch; st += NS) {
+        auto trip = [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            step(o[j], st + j);
+            load(st + j + NS, o[j]);
+        };
+        static_for<NS>(trip);
+    }
+    auto tail = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if (st + j < nch) step(o[j], st + j);
+    };
+    static_for<NS>(tail);
+    if (a.dS_out && is_carry) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+            *reinterpret_cast<float4 *>(a.dS_out + sb + static_cast<int64_t>(vcol) * DK + 16 * (TPW * w + j) + 4 * g) =
+                make_float4(GT[j][0], GT[j][1], GT[j][2], GT[j][3]);
+    }
+}
 
 }  // namespace
 }  // namespace lam

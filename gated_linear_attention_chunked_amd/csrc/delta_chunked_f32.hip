@@ -50,9 +50,11 @@ __device__ __forceinline__ float prefix16(float x, int i) {
 
 // One wave per (b, h, chunk of 16 tokens): the chunk record for the state
 // kernel.  Lane (g, i): g = lane / 16, i = lane % 16.
-template <typename IO, int VARIANT, int DK>
+// BWD: also the adjoint scan's record (Tc^T Ahat, the transposed decayed
+// queries and erase keys, (Aq Tc)^T) for the backward pass.
+template <typename IO, int VARIANT, int DK, bool BWD>
 __global__ __launch_bounds__(64) void delta_f32_derive_kernel(DeltaArgs a, ChunkRec<DK> *__restrict__ rec,
-                                                              unsigned int *status) {
+                                                              AdjRec<DK> *__restrict__ arec, unsigned int *status) {
     constexpr bool kDecay = VARIANT != kDeltaNet;
     constexpr bool kGates2 = VARIANT == kGatedDeltaNet2;
     using L = DeriveF32Lds<DK, kGates2>;
@@ -97,7 +99,10 @@ __global__ __launch_bounds__(64) void delta_f32_derive_kernel(DeltaArgs a, Chunk
         s.gm[lane] = exp2f(gl);
         s.bt[lane] = bv;
         s.sc[lane] = bv * exp2f(gC - gl);
-        if (lane == 0) rec[blockIdx.x].gc = f32x4{exp2f(gC), exp2f(gC), exp2f(gC), exp2f(gC)};
+        if (lane == 0) {
+            rec[blockIdx.x].gc = f32x4{exp2f(gC), exp2f(gC), exp2f(gC), exp2f(gC)};
+            if constexpr (BWD) arec[blockIdx.x].gc = f32x4{exp2f(gC), exp2f(gC), exp2f(gC), exp2f(gC)};
+        }
     }
     // (selected component by component: a select of whole vectors becomes a
     // select of their addresses in private memory)
@@ -164,14 +169,22 @@ __global__ __launch_bounds__(64) void delta_f32_derive_kernel(DeltaArgs a, Chunk
         gmv[m] = s.gm[4 * g + m];
         scv[m] = s.sc[4 * g + m];
     }
+    // Tc as a B operand (lane (g, i) step m: Tc[4g + m][i]), i.e. Tc^T as an A operand
+    f32x4 tcb;
+    {
+        const float *tf = reinterpret_cast<const float *>(s.top);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) tcb[m] = tf[((i >> 2) * 16 + 4 * g + m) * 4 + (i & 3)];
+    }
 #pragma unroll
     for (int j = 0; j < DK / 16; ++j) {
         const int col = 16 * j + i;
         // Ktil = Tc (diag(gamma) E): B operand at step m = gamma_{4g+m} E[4g + m][col]
-        f32x4 k0 = zero4, k1 = zero4;
+        f32x4 k0 = zero4, k1 = zero4, ge;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const float bm = gmv[m] * E[(4 * g + m) * RS + col];
+            ge[m] = bm;
             if (m & 1) k1 = mfma4(tc[m], bm, k1);
             else k0 = mfma4(tc[m], bm, k0);
         }
@@ -180,6 +193,10 @@ __global__ __launch_bounds__(64) void delta_f32_derive_kernel(DeltaArgs a, Chunk
         f32x4 q0, q1 = zero4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) q0[r] = gmv[r] * s.q[(4 * g + r) * RS + col];
+        if constexpr (BWD) {  // (gamma Q)^T and (gamma E)^T tiles: the same values in A-operand order
+            arec[blockIdx.x].gqt[j][lane] = q0;
+            arec[blockIdx.x].get[j][lane] = ge;
+        }
         q0 = mfma4(-aqa[0], kt[0], q0);
         q1 = mfma4(-aqa[1], kt[1], q1);
         q0 = mfma4(-aqa[2], kt[2], q0);
@@ -195,20 +212,38 @@ __global__ __launch_bounds__(64) void delta_f32_derive_kernel(DeltaArgs a, Chunk
             R.qt[(4 * g + r) * DK + col] = qt[r];
         }
         R.aht[j][lane] = ah;
+        if constexpr (BWD) {  // Ahat' = Tc^T Ahat: A operand Tc^T, B operand Ahat (step m: Ahat[4g + m][col])
+            f32x4 p0 = zero4, p1 = zero4;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (m & 1) p1 = mfma4(tcb[m], ah[m], p1);
+                else p0 = mfma4(tcb[m], ah[m], p0);
+            }
+            const f32x4 ap = p0 + p1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) arec[blockIdx.x].ap[(4 * g + r) * DK + col] = ap[r];
+        }
     }
     R.top[lane] = tc;
     // Aq Tc in A-operand order, as (Aq Tc)^T = Tc^T Aq^T: A operand Tc^T
     // (lane (g, i) step m: Tc[4g + m][i]), B operand Aq^T (step m: Aq[i][4g + m])
     {
-        const float *tf = reinterpret_cast<const float *>(s.top);
         f32x4 a0 = zero4, a1 = zero4;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const float tcm = tf[((i >> 2) * 16 + 4 * g + m) * 4 + (i & 3)];
-            if (m & 1) a1 = mfma4(tcm, aqa[m], a1);
-            else a0 = mfma4(tcm, aqa[m], a0);
+            if (m & 1) a1 = mfma4(tcb[m], aqa[m], a1);
+            else a0 = mfma4(tcb[m], aqa[m], a0);
         }
         R.aqt[lane] = a0 + a1;
+    }
+    if constexpr (BWD) {  // (Aq Tc)^T in A-operand order = Aq Tc in accumulator order: A Aq, B Tc
+        f32x4 a0 = zero4, a1 = zero4;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            if (m & 1) a1 = mfma4(aqa[m], tcb[m], a1);
+            else a0 = mfma4(aqa[m], tcb[m], a0);
+        }
+        arec[blockIdx.x].aqtt[lane] = a0 + a1;
     }
 }
 
@@ -219,7 +254,8 @@ hipError_t launch_kd(const DeltaArgs &a, hipStream_t stream) {
     const int64_t nch = (a.T + VC - 1) / VC;
     unsigned int *status = static_cast<unsigned int *>(a.ws);
     ChunkRec<DK> *rec = reinterpret_cast<ChunkRec<DK> *>(static_cast<char *>(a.ws) + kStatusBytes);
-    delta_f32_derive_kernel<IO, VARIANT, DK><<<static_cast<unsigned>(a.B * a.H * nch), 64, 0, stream>>>(a, rec, status);
+    delta_f32_derive_kernel<IO, VARIANT, DK, false>
+        <<<static_cast<unsigned>(a.B * a.H * nch), 64, 0, stream>>>(a, rec, nullptr, status);
     ScanArgs sa{};
     sa.B = a.B;
     sa.T = a.T;
@@ -258,6 +294,345 @@ hipError_t launch_io(const DeltaArgs &a, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
+// ------------------------------------------------------------ backward
+// The gradients of one chunk from the chunk-start state S0, the cotangent
+// G' of the state after the chunk, the residuals U and dX (from the forward
+// recompute and the adjoint scan): in the residual form above, with
+// Nm = strict(E K^T * Gamma), Am = lower(Q K^T * Gamma), Kc = diag(sc) K,
+// sc = beta gamma_C / gamma,
+//   dQ  = diag(gamma) dY S0 + dQK K,         dQK = (dY U^T * lower) diag(beta) * Gamma
+//   dE  = -diag(gamma) dX S0 + dEK K,        dEK = -(dX U^T * strict) diag(beta) * Gamma
+//   dK  = dEK^T E + dQK^T Q + diag(sc) U G' (+ dE, or b * dE when E = b * K)
+//   dbeta_s = sum_t (dA_ts Am_ts + dL_ts Nm_ts) + dsc_s gamma_C / gamma_s,   dsc = rowsum(U G' * K)
+//   d log gamma_t = rowsum(gw) - colsum(gw) + dg_t gamma_t - dsc_t sc_t
+//                   (+ <G', S0> gamma_C + sum_s dsc_s sc_s at the last token),
+//   gw = (dNm * E K^T + dAm * Q K^T) * Gamma,  dg = rowsum(Q * dY S0) - rowsum(E * dX S0),
+// and d alpha_j = sum_{t >= j} d log gamma_t / alpha_j.  The three products
+// over the value dimension and the 16 x 16 Gram blocks run on the matrix
+// cores; the rest is per-element.
+template <int DK, bool G2>
+struct GradLds {
+    static constexpr int RS = DK + 4;
+    alignas(16) float q[VC * RS], k[VC * RS];
+    alignas(16) float e[G2 ? VC * RS : 4];
+    alignas(16) float p1[VC * RS], p2[VC * RS], pk[VC * RS];  // dY S0, dX S0, U G' (rows t)
+    float ek[VC][VC + 1], qk[VC][VC + 1], dyu[VC][VC + 1], dxu[VC][VC + 1];
+    float dek[VC][VC + 1], dqk[VC][VC + 1], gw[VC][VC + 1], bc[VC][VC + 1];
+    float l2[VC], gm[VC], bt[VC], sc[VC];
+    float dgc[4];
+};
+
+struct BwdWs {
+    const float *s_chunks, *ds_chunks, *u, *dx;
+};
+
+template <typename IO, int VARIANT, int DK>
+__global__ __launch_bounds__(256) void delta_f32_grad_kernel(DeltaBwdArgs ga, BwdWs wp) {
+    constexpr bool kDecay = VARIANT != kDeltaNet;
+    constexpr bool kGates2 = VARIANT == kGatedDeltaNet2;
+    using L = GradLds<DK, kGates2>;
+    constexpr int RS = L::RS;
+    __shared__ L s;
+    const DeltaArgs &a = ga.f;
+    const int T = static_cast<int>(a.T), H = static_cast<int>(a.H), DV = a.dv;
+    const int nch = (T + VC - 1) / VC;
+    const int head = blockIdx.x / nch, c = blockIdx.x % nch;
+    const int b = head / H, h = head % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, i = lane & 15;
+    const int t0 = c * VC, n = min(VC, T - t0);
+    const int64_t tk = (static_cast<int64_t>(b) * T + t0) * H + h;  // token index of row 0
+    const float *E = kGates2 ? s.e : s.k;
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    auto keep = [](bool ok, float4 x) {
+        return make_float4(ok ? x.x : 0.f, ok ? x.y : 0.f, ok ? x.z : 0.f, ok ? x.w : 0.f);
+    };
+
+    // ---- the chunk's q, k (and b * k) rows, zero past the end; gates
+    constexpr int Q4 = DK / 4;
+    for (int e = tid; e < VC * Q4; e += 256) {
+        const int t = e / Q4, j = 4 * (e % Q4);
+        const int64_t gi = (tk + static_cast<int64_t>(min(t, n - 1)) * H) * DK + j;
+        const bool ok = t < n;
+        const float4 kv = IO::ld4(a.k, gi), qv = IO::ld4(a.q, gi);
+        *reinterpret_cast<float4 *>(&s.k[t * RS + j]) = keep(ok, kv);
+        *reinterpret_cast<float4 *>(&s.q[t * RS + j]) = keep(ok, qv);
+        if constexpr (kGates2) {
+            const float4 bv = IO::ld4(a.erase_b, gi);
+            *reinterpret_cast<float4 *>(&s.e[t * RS + j]) =
+                keep(ok, make_float4(kv.x * bv.x, kv.y * bv.y, kv.z * bv.z, kv.w * bv.w));
+        }
+    }
+    if (tid < VC) {  // the same decay logarithms and scales as the derivation
+        const bool ok = tid < n;
+        const int64_t ti = tk + static_cast<int64_t>(min(tid, n - 1)) * H;
+        float la = 0.f;
+        if constexpr (kDecay) {
+            const float av = IO::ld(a.alpha, ti);
+            la = ok ? log2_decay(av) : 0.f;
+        }
+        const float gl = prefix16(la, tid);
+        const float gC = __shfl(gl, VC - 1, 16);
+        const float bl = IO::ld(a.beta, ti);
+        const float bv = ok ? bl : 0.f;
+        s.l2[tid] = gl;
+        s.gm[tid] = exp2f(gl);
+        s.bt[tid] = bv;
+        s.sc[tid] = bv * exp2f(gC - gl);
+    }
+    __syncthreads();
+
+    // ---- products over the value dimension: lane (g, i) reads row i (token
+    // t0 + i, zero past the end), values 16 vt + 4g .. + 3
+    const float *S0 = wp.s_chunks + (static_cast<int64_t>(head) * nch + c) * DK * DV;   // S0^T rows
+    const float *G1 = wp.ds_chunks + (static_cast<int64_t>(head) * nch + c) * DK * DV;  // G'^T rows
+    const bool rok = i < n;
+    const int64_t rowi = (tk + static_cast<int64_t>(min(i, n - 1)) * H) * DV + 4 * g;
+    auto row_f32 = [&](const float *base, int vt) {
+        const float4 x = keep(rok, *reinterpret_cast<const float4 *>(base + rowi + 16 * vt));
+        return f32x4{x.x, x.y, x.z, x.w};
+    };
+    auto row_dy = [&](int vt) {
+        const float4 x = keep(rok, IO::ld4(ga.dout, rowi + 16 * vt));
+        return f32x4{x.x, x.y, x.z, x.w};
+    };
+    float dgc = 0.f;
+    for (int kt = w; kt < DK / 16; kt += 4) {
+        f32x4 a1 = zero4, a2 = zero4, a3 = zero4;
+        for (int vt = 0; vt < DV / 16; ++vt) {
+            const f32x4 yr = row_dy(vt), xr = row_f32(wp.dx, vt), ur = row_f32(wp.u, vt);
+            const int64_t so = static_cast<int64_t>(16 * kt + i) * DV + 16 * vt + 4 * g;
+            const float4 sv4 = *reinterpret_cast<const float4 *>(S0 + so);
+            const float4 gv4 = *reinterpret_cast<const float4 *>(G1 + so);
+            const f32x4 sv = {sv4.x, sv4.y, sv4.z, sv4.w}, gv = {gv4.x, gv4.y, gv4.z, gv4.w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                a1 = mfma4(yr[m], sv[m], a1);
+                a2 = mfma4(xr[m], sv[m], a2);
+                a3 = mfma4(ur[m], gv[m], a3);
+                dgc = fmaf(sv[m], gv[m], dgc);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int o = (4 * g + r) * RS + 16 * kt + i;
+            s.p1[o] = a1[r];
+            s.p2[o] = a2[r];
+            s.pk[o] = a3[r];
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dgc += __shfl_xor(dgc, off);
+    if (lane == 0) s.dgc[w] = dgc;
+    // ---- the 16 x 16 blocks: dY U^T (wave 0), dX U^T (wave 1), E K^T (wave 2), Q K^T (wave 3)
+    {
+        f32x4 acc0 = zero4, acc1 = zero4;
+        if (w < 2) {
+            for (int vt = 0; vt < DV / 16; ++vt) {
+                const f32x4 ar = w == 0 ? row_dy(vt) : row_f32(wp.dx, vt), ur = row_f32(wp.u, vt);
+                acc0 = mfma4(ar[0], ur[0], acc0);
+                acc1 = mfma4(ar[1], ur[1], acc1);
+                acc0 = mfma4(ar[2], ur[2], acc0);
+                acc1 = mfma4(ar[3], ur[3], acc1);
+            }
+        } else {
+            const float *X = w == 2 ? E : s.q;
+#pragma unroll
+            for (int q4 = 0; q4 < DK / 16; ++q4) {
+                const f32x4 xr = lds4(&X[i * RS + 16 * q4 + 4 * g]);
+                const f32x4 kr = lds4(&s.k[i * RS + 16 * q4 + 4 * g]);
+                acc0 = mfma4(xr[0], kr[0], acc0);
+                acc1 = mfma4(xr[1], kr[1], acc1);
+                acc0 = mfma4(xr[2], kr[2], acc0);
+                acc1 = mfma4(xr[3], kr[3], acc1);
+            }
+        }
+        const f32x4 acc = acc0 + acc1;
+        float(*dst)[VC + 1] = w == 0 ? s.dyu : w == 1 ? s.dxu : w == 2 ? s.ek : s.qk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[4 * g + r][i] = acc[r];
+    }
+    __syncthreads();
+
+    // ---- per (t, s): the adjoints through Aq and the solve
+    {
+        const int t = tid >> 4, u = tid & 15;
+        const bool tri = u <= t, str = u < t;
+        const float G = tri ? (kDecay ? exp2f(s.l2[t] - s.l2[u]) : 1.f) : 0.f;
+        const float ek = s.ek[t][u], qk = s.qk[t][u];
+        const float nm = str ? ek * G : 0.f, am = tri ? qk * G : 0.f;
+        const float dA = tri ? s.dyu[t][u] : 0.f, dL = str ? -s.dxu[t][u] : 0.f;
+        s.bc[t][u] = dA * am + dL * nm;
+        const float dAm = dA * s.bt[u], dNm = dL * s.bt[u];
+        s.dek[t][u] = dNm * G;
+        s.dqk[t][u] = dAm * G;
+        s.gw[t][u] = (dNm * ek + dAm * qk) * G;
+    }
+    __syncthreads();
+
+    // ---- per token: dbeta and the decay's adjoint (wave 0, lanes 0 .. 15)
+    if (tid < VC) {
+        const int t = tid;
+        float dg = 0.f, dsc = 0.f;
+        for (int j = 0; j < DK; ++j) {
+            dg = fmaf(s.q[t * RS + j], s.p1[t * RS + j], dg);
+            dg = fmaf(-E[t * RS + j], s.p2[t * RS + j], dg);
+            dsc = fmaf(s.pk[t * RS + j], s.k[t * RS + j], dsc);
+        }
+        float dbe = 0.f, gwr = 0.f, gwc = 0.f;
+        for (int u = 0; u < VC; ++u) {
+            dbe += s.bc[u][t];
+            gwr += s.gw[t][u];
+            gwc += s.gw[u][t];
+        }
+        const float gC = s.gm[VC - 1];
+        dbe = fmaf(dsc, exp2f(s.l2[VC - 1] - s.l2[t]), dbe);
+        const int64_t ti = tk + static_cast<int64_t>(min(t, n - 1)) * H;
+        if (t < n) ga.dbeta[ti] = dbe;
+        if constexpr (kDecay) {
+            float scs = dsc * s.sc[t];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) scs += __shfl_xor(scs, off, 16);
+            float dlg = gwr - gwc + dg * s.gm[t] - dsc * s.sc[t];
+            if (t == n - 1) dlg += (s.dgc[0] + s.dgc[1] + s.dgc[2] + s.dgc[3]) * gC + scs;
+            if (t >= n) dlg = 0.f;
+            // d log alpha_j = sum_{t >= j} d log gamma_t (suffix sum over the chunk)
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                const float y = __shfl_down(dlg, off, 16);
+                dlg += t + off < 16 ? y : 0.f;
+            }
+            if (t < n) ga.dalpha[ti] = dlg / IO::ld(a.alpha, ti);
+        }
+    }
+
+    // ---- per (t, key): dQ, dE, dK on the matrix cores (16 x 16 by 16 x 16 per key tile)
+    for (int kt = w; kt < DK / 16; kt += 4) {
+        const int col = 16 * kt + i;
+        f32x4 aq = zero4, ae = zero4, ak0 = zero4, ak1 = zero4;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int u = 4 * g + m;
+            aq = mfma4(s.dqk[i][u], s.k[u * RS + col], aq);   // dQK K
+            ae = mfma4(s.dek[i][u], s.k[u * RS + col], ae);   // dEK K
+            ak0 = mfma4(s.dek[u][i], E[u * RS + col], ak0);   // dEK^T E
+            ak1 = mfma4(s.dqk[u][i], s.q[u * RS + col], ak1); // dQK^T Q
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * g + r;
+            if (t < n) {
+                const int o = t * RS + col;
+                const float dq = fmaf(s.gm[t], s.p1[o], aq[r]);
+                const float dE = fmaf(-s.gm[t], s.p2[o], ae[r]);
+                float dk = fmaf(s.sc[t], s.pk[o], ak0[r] + ak1[r]);
+                const int64_t gi = (tk + static_cast<int64_t>(t) * H) * DK + col;
+                if constexpr (kGates2) {
+                    ga.derase_b[gi] = s.k[o] * dE;
+                    dk = fmaf(IO::ld(a.erase_b, gi), dE, dk);
+                } else {
+                    dk += dE;
+                }
+                ga.dq[gi] = dq;
+                ga.dk[gi] = dk;
+            }
+        }
+    }
+}
+
+template <int DK>
+struct BwdLayout {
+    size_t rec_off, arec_off, s_off, ds_off, u_off, dx_off, bytes;
+};
+template <int DK>
+bool bwd_layout(const DeltaArgs &a, BwdLayout<DK> *L) {
+    const int64_t nch = (a.T + VC - 1) / VC, tasks = a.B * a.H * nch;
+    if (tasks > 0x7fffffff || a.B * a.H * (a.dv / 16) > 0x7fffffff) return false;
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    const size_t st = static_cast<size_t>(tasks) * DK * a.dv * sizeof(float);
+    const size_t rows = static_cast<size_t>(a.B * a.T * a.H) * a.dv * sizeof(float);
+    L->rec_off = kStatusBytes;
+    L->arec_off = up(L->rec_off + static_cast<size_t>(tasks) * sizeof(ChunkRec<DK>));
+    L->s_off = up(L->arec_off + static_cast<size_t>(tasks) * sizeof(AdjRec<DK>));
+    L->ds_off = up(L->s_off + st);
+    L->u_off = up(L->ds_off + st);
+    L->dx_off = up(L->u_off + rows);
+    L->bytes = L->dx_off + rows;
+    return true;
+}
+
+template <typename IO, int VARIANT, int DK>
+hipError_t launch_bwd_kd(const DeltaBwdArgs &g, hipStream_t stream) {
+    constexpr bool kDecay = VARIANT != kDeltaNet;
+    constexpr bool kGates2 = VARIANT == kGatedDeltaNet2;
+    const DeltaArgs &a = g.f;
+    BwdLayout<DK> L;
+    if (!bwd_layout<DK>(a, &L)) return hipErrorInvalidValue;
+    char *ws = static_cast<char *>(a.ws);
+    const int64_t nch = (a.T + VC - 1) / VC, tasks = a.B * a.H * nch;
+    unsigned int *status = reinterpret_cast<unsigned int *>(ws);
+    ChunkRec<DK> *rec = reinterpret_cast<ChunkRec<DK> *>(ws + L.rec_off);
+    AdjRec<DK> *arec = reinterpret_cast<AdjRec<DK> *>(ws + L.arec_off);
+    float *s_chunks = reinterpret_cast<float *>(ws + L.s_off);
+    float *ds_chunks = reinterpret_cast<float *>(ws + L.ds_off);
+    float *u = reinterpret_cast<float *>(ws + L.u_off);
+    float *dx = reinterpret_cast<float *>(ws + L.dx_off);
+    const unsigned scan_grid = static_cast<unsigned>(a.B * a.H * (a.dv / 16));
+    delta_f32_derive_kernel<IO, VARIANT, DK, true><<<static_cast<unsigned>(tasks), 64, 0, stream>>>(a, rec, arec, status);
+    ScanArgs sa{};  // the forward again, keeping each chunk's start state and U
+    sa.B = a.B;
+    sa.T = a.T;
+    sa.H = a.H;
+    sa.dv = a.dv;
+    sa.v = a.v;
+    sa.w = kGates2 ? a.write_w : nullptr;
+    sa.S_in = a.state_in;
+    sa.side_kind = kSideNone;
+    sa.s_chunks = s_chunks;
+    sa.u_f32 = u;
+    chunk_state_kernel<IO, DK, kDecay, kGates2, true><<<scan_grid, 64 * state_waves<DK>(), 0, stream>>>(sa, rec);
+    AdjArgs aa{};
+    aa.B = a.B;
+    aa.T = a.T;
+    aa.H = a.H;
+    aa.dv = a.dv;
+    aa.dy = g.dout;
+    aa.v = kGates2 ? a.v : nullptr;
+    aa.w = kGates2 ? a.write_w : nullptr;
+    aa.dS_in = g.dstate_out;
+    aa.dS_out = g.dstate_in;
+    aa.ds_chunks = ds_chunks;
+    aa.dx = dx;
+    aa.dv_out = g.dv;
+    aa.dw_out = kGates2 ? g.dwrite_w : nullptr;
+    chunk_adjoint_kernel<IO, DK, kDecay, kGates2><<<scan_grid, 64 * state_waves<DK>(), 0, stream>>>(aa, arec);
+    delta_f32_grad_kernel<IO, VARIANT, DK>
+        <<<static_cast<unsigned>(tasks), 256, 0, stream>>>(g, BwdWs{s_chunks, ds_chunks, u, dx});
+    return hipGetLastError();
+}
+
+template <typename IO, int VARIANT>
+hipError_t launch_bwd_v(const DeltaBwdArgs &g, hipStream_t stream) {
+    switch (g.f.dk) {
+        case 32: return launch_bwd_kd<IO, VARIANT, 32>(g, stream);
+        case 64: return launch_bwd_kd<IO, VARIANT, 64>(g, stream);
+        case 96: return launch_bwd_kd<IO, VARIANT, 96>(g, stream);
+        case 128: return launch_bwd_kd<IO, VARIANT, 128>(g, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename IO>
+hipError_t launch_bwd_io(const DeltaBwdArgs &g, hipStream_t stream) {
+    switch (g.f.variant) {
+        case kDeltaNet: return launch_bwd_v<IO, kDeltaNet>(g, stream);
+        case kGatedDeltaNet: return launch_bwd_v<IO, kGatedDeltaNet>(g, stream);
+        case kGatedDeltaNet2: return launch_bwd_v<IO, kGatedDeltaNet2>(g, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int DK>
 size_t rec_bytes() { return sizeof(ChunkRec<DK>); }
 
@@ -281,6 +656,23 @@ bool delta_f32_chunked_workspace(const DeltaArgs &a, size_t *bytes) {
     if (tasks > 0x7fffffff || a.B * a.H * (a.dv / 16) > 0x7fffffff) return false;
     *bytes = kStatusBytes + static_cast<size_t>(tasks) * per;
     return true;
+}
+
+bool delta_f32_backward_workspace(const DeltaArgs &a, size_t *bytes) {
+    if (!delta_f32_chunked_supported(a)) return false;
+    bool ok = false;
+    switch (a.dk) {
+        case 32: { BwdLayout<32> L; ok = bwd_layout<32>(a, &L); *bytes = L.bytes; break; }
+        case 64: { BwdLayout<64> L; ok = bwd_layout<64>(a, &L); *bytes = L.bytes; break; }
+        case 96: { BwdLayout<96> L; ok = bwd_layout<96>(a, &L); *bytes = L.bytes; break; }
+        case 128: { BwdLayout<128> L; ok = bwd_layout<128>(a, &L); *bytes = L.bytes; break; }
+    }
+    return ok;
+}
+
+hipError_t launch_delta_f32_backward(const DeltaBwdArgs &g, hipStream_t stream) {
+    if (!delta_f32_chunked_supported(g.f) || g.f.T <= 0) return hipErrorNotSupported;
+    return g.f.dtype == kBF16 ? launch_bwd_io<IoBF16>(g, stream) : launch_bwd_io<IoF32>(g, stream);
 }
 
 hipError_t launch_delta_f32_chunked(const DeltaArgs &a, hipStream_t stream) {

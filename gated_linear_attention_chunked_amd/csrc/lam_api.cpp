@@ -143,7 +143,7 @@ const char *lam_status_string(int s) {
     return "unknown status";
 }
 
-int lam_abi_version(void) { return 200; }
+int lam_abi_version(void) { return 201; }
 
 int lam_select_algo(int variant, int dtype, int64_t T, int64_t dk, int64_t dv) {
     if (variant < LAM_DELTANET || variant > LAM_GATED_DELTANET2) return -1;
@@ -359,15 +359,29 @@ lam_status lam_route(int dtype, int64_t M, int64_t D, int64_t N, const void *s, 
     return from_hip(lam::launch_route(dtype, M, D, N, s, P, h, stream));
 }
 
+namespace {
+// The backward schedule of a validated call: chunked (fp32 matrix cores) or
+// token-recurrent, and its workspace.
+lam_status plan_backward(const lam::DeltaArgs &a, int algo, bool *chunked, size_t *bytes) {
+    *chunked = false;
+    *bytes = 0;
+    if (a.B == 0 || a.H == 0) return LAM_OK;
+    const bool chunked_ok = lam::delta_f32_chunked_supported(a);
+    if (algo == LAM_ALGO_CHUNKED && !chunked_ok) return LAM_ERR_UNSUPPORTED;
+    *chunked = chunked_ok && a.T > 0 && algo != LAM_ALGO_RECURRENT;
+    const bool ok = *chunked ? lam::delta_f32_backward_workspace(a, bytes) : lam::delta_backward_workspace(a, bytes);
+    return ok ? LAM_OK : LAM_ERR_UNSUPPORTED;
+}
+}  // namespace
+
 lam_status lam_backward_workspace_size(int variant, int dtype, int64_t B, int64_t T, int64_t H,
-                                       int64_t dk, int64_t dv, size_t *bytes) {
+                                       int64_t dk, int64_t dv, int algo, size_t *bytes) {
     if (!bytes) return LAM_ERR_INVALID_ARG;
     *bytes = 0;
-    lam_status st = check_delta_shape(variant, dtype, B, T, H, dk, dv, LAM_ALGO_RECURRENT);
+    lam_status st = check_delta_shape(variant, dtype, B, T, H, dk, dv, algo);
     if (st != LAM_OK) return st;
-    if (B == 0 || H == 0) return LAM_OK;
-    lam::DeltaArgs a = shape_args(variant, dtype, B, T, H, dk, dv);
-    return lam::delta_backward_workspace(a, bytes) ? LAM_OK : LAM_ERR_UNSUPPORTED;
+    bool chunked;
+    return plan_backward(shape_args(variant, dtype, B, T, H, dk, dv), algo, &chunked, bytes);
 }
 
 lam_status lam_backward(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
@@ -375,12 +389,14 @@ lam_status lam_backward(int variant, int dtype, int64_t B, int64_t T, int64_t H,
                         const void *alpha, const void *erase_b, const void *write_w,
                         const void *beta, const float *state_in, const void *dout,
                         const float *dstate_out, float *dq, float *dk_, float *dv_, float *dalpha,
-                        float *derase_b, float *dwrite_w, float *dbeta, float *dstate_in,
+                        float *derase_b, float *dwrite_w, float *dbeta, float *dstate_in, int algo,
                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
     size_t need = 0;
-    lam_status st = lam_backward_workspace_size(variant, dtype, B, T, H, dk, dv, &need);
+    lam_status st = lam_backward_workspace_size(variant, dtype, B, T, H, dk, dv, algo, &need);
     if (st != LAM_OK) return st;
     if (B == 0 || H == 0) return LAM_OK;
+    bool chunked;
+    plan_backward(shape_args(variant, dtype, B, T, H, dk, dv), algo, &chunked, &need);
     int64_t nk, nv, ns, nst;
     elems(B, T, H, dk, nk);
     elems(B, T, H, dv, nv);
@@ -434,6 +450,7 @@ lam_status lam_backward(int variant, int dtype, int64_t B, int64_t T, int64_t H,
     g.dbeta = dbeta;
     g.dstate_in = dstate_in;
     g.ckpt = reinterpret_cast<float *>(static_cast<char *>(workspace) + lam::kStatusBytes);
+    if (chunked) return from_hip(lam::launch_delta_f32_backward(g, stream));
     return from_hip(lam::launch_delta_backward(g, stream));
 }
 

@@ -93,6 +93,14 @@ struct DeltaBwdArgs {
 };
 bool delta_backward_workspace(const DeltaArgs &a, size_t *bytes);
 hipError_t launch_delta_backward(const DeltaBwdArgs &g, hipStream_t stream);
+// The chunked backward of DeltaNet, Gated DeltaNet and Gated DeltaNet-2 on
+// fp32 matrix cores (shapes as delta_f32_chunked_supported, T > 0): the
+// derivation with the adjoint records, the forward again keeping each
+// chunk's start state and residuals, the adjoint scan in reverse, and the
+// chunk-parallel gradients.  Workspace: the status block, the records, the
+// per-chunk states and state cotangents, U and dX.
+bool delta_f32_backward_workspace(const DeltaArgs &a, size_t *bytes);
+hipError_t launch_delta_f32_backward(const DeltaBwdArgs &g, hipStream_t stream);
 
 // Log-linear (Fenwick-tree) readout: f as the plain scan (state_in /
 // state_out are level states [B,H,nL,dv,dk]), nL levels, t0 = absolute

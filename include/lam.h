@@ -315,25 +315,41 @@ lam_status lam_vla_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, in
  *                   [B,T,H,dv] (required for Gated DeltaNet-2); dstate_in
  *                   [B,H,dv,dk] or NULL.  No gradient buffer may overlap
  *                   another argument.
- *   workspace       lam_backward_workspace_size bytes: the forward state
- *                   every 16 tokens, B*H*ceil(T/16)*dv*dk*4 B, plus the
- *                   status block.
+ *   algo            lam_algo.  LAM_ALGO_CHUNKED (DeltaNet, Gated DeltaNet,
+ *                   Gated DeltaNet-2; what LAM_ALGO_AUTO picks for them when
+ *                   T > 0): the adjoint in 16-token chunks on fp32 matrix
+ *                   cores -- the chunk records, the forward again keeping
+ *                   each chunk's start state and residuals, the state
+ *                   cotangent scanned in reverse, then every chunk's
+ *                   gradients in parallel; bitwise reproducible.
+ *                   LAM_ALGO_RECURRENT (and Kimi Delta): token-recurrent,
+ *                   forward checkpoints every 16 tokens; dq, dk, dbeta,
+ *                   dalpha and derase_b sum over the memory's dv rows with
+ *                   atomics across workgroups, so those five are not
+ *                   bitwise reproducible run to run (dv, dwrite_w and
+ *                   dstate_in are).  LAM_ALGO_CHUNKED for Kimi Delta
+ *                   returns LAM_ERR_UNSUPPORTED.
+ *   workspace       lam_backward_workspace_size bytes for the same algo.
+ *                   Chunked: per (b, h, 16-token chunk) the two records
+ *                   (52 KB at dk = 128) and the chunk's start state and
+ *                   state cotangent (2 * dv * dk * 4 B), plus U and dX
+ *                   (2 * B*T*H*dv * 4 B): 3.2 GB at B8 T4096 H8 d128.
+ *                   Recurrent: the forward state every 16 tokens,
+ *                   B*H*ceil(T/16)*dv*dk*4 B.  Both plus the status block.
  * T = 0 writes dstate_in = dstate_out (zero if NULL).
- * dq, dk, dbeta, dalpha and derase_b sum over the memory's dv rows, which
- * several workgroups add into with atomics: those five are not bitwise
- * reproducible run to run; dv, dwrite_w and dstate_in are.
  */
 lam_status lam_backward(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
                         int64_t dv, const void *q, const void *k, const void *v,
                         const void *alpha, const void *erase_b, const void *write_w,
                         const void *beta, const float *state_in, const void *dout,
                         const float *dstate_out, float *dq, float *dk_, float *dv_, float *dalpha,
-                        float *derase_b, float *dwrite_w, float *dbeta, float *dstate_in,
+                        float *derase_b, float *dwrite_w, float *dbeta, float *dstate_in, int algo,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace lam_backward needs (> 0 for any non-empty call). */
+/* Bytes of workspace lam_backward needs with this algo (> 0 for any
+ * non-empty call). */
 lam_status lam_backward_workspace_size(int variant, int dtype, int64_t B, int64_t T, int64_t H,
-                                       int64_t dk, int64_t dv, size_t *bytes);
+                                       int64_t dk, int64_t dv, int algo, size_t *bytes);
 
 /*
  * One-token decode step for N concurrent streams: the rule above applied to

@@ -55,7 +55,7 @@ def test_status_strings_and_version(lib):
     for s in range(5):
         assert lib.lam_status_string(s)
     assert lib.lam_status_string(99) == b"unknown status"
-    assert lib.lam_abi_version() == 200
+    assert lib.lam_abi_version() == 201
 
 
 def _fwd(lib, variant=1, dtype=1, B=2, T=8, H=2, dk=64, dv=64, q=FAKE, k=FAKE + 0x10000000,
@@ -240,7 +240,7 @@ def test_step_rejects_bad_arguments(lib):
     assert lib.lam_vla_step(0, 2, 2, 40, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
 
 
-def _bwd(lib, variant=1, dtype=1, B=2, T=8, H=2, dk=64, dv=64, ws=None, ws_bytes=0, **kw):
+def _bwd(lib, variant=1, dtype=1, B=2, T=8, H=2, dk=64, dv=64, ws=None, ws_bytes=0, algo=1, **kw):
     p = dict(q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, alpha=FAKE + 0x30000000,
              eb=FAKE + 0x40000000, ww=FAKE + 0x50000000, beta=FAKE + 0x60000000, sin=None,
              dout=FAKE + 0x70000000, dsout=None, gq=FAKE + 0x100000000, gk=FAKE + 0x110000000,
@@ -249,18 +249,32 @@ def _bwd(lib, variant=1, dtype=1, B=2, T=8, H=2, dk=64, dv=64, ws=None, ws_bytes
     p.update(kw)
     return lib.lam_backward(variant, dtype, B, T, H, dk, dv, p["q"], p["k"], p["v"], p["alpha"], p["eb"],
                             p["ww"], p["beta"], p["sin"], p["dout"], p["dsout"], p["gq"], p["gk"], p["gv"],
-                            p["dalpha"], p["deb"], p["dww"], p["dbeta"], p["dsin"], ws, ws_bytes, None)
+                            p["dalpha"], p["deb"], p["dww"], p["dbeta"], p["dsin"], algo, ws, ws_bytes, None)
 
 
 def test_backward_rejects_bad_arguments(lib):
     n = ctypes.c_size_t(0)
-    assert lib.lam_backward_workspace_size(1, 1, 2, 8, 2, 64, 64, ctypes.byref(n)) == OK
+    assert lib.lam_backward_workspace_size(1, 1, 2, 8, 2, 64, 64, 1, ctypes.byref(n)) == OK
     need = n.value
-    # the forward state every 16 tokens plus the 256-byte status block
+    # recurrent: the forward state every 16 tokens plus the 256-byte status block
     assert need == 256 + 2 * 2 * 1 * 64 * 64 * 4
-    assert lib.lam_backward_workspace_size(1, 1, 2, 0, 2, 64, 64, ctypes.byref(n)) == OK and n.value == 256
-    assert lib.lam_backward_workspace_size(1, 1, 2, 8, 2, 48, 64, ctypes.byref(n)) == UNSUPPORTED
-    assert lib.lam_backward_workspace_size(9, 1, 2, 8, 2, 64, 64, ctypes.byref(n)) == INVALID
+    assert lib.lam_backward_workspace_size(1, 1, 2, 0, 2, 64, 64, 1, ctypes.byref(n)) == OK and n.value == 256
+    assert lib.lam_backward_workspace_size(1, 1, 2, 0, 2, 64, 64, 0, ctypes.byref(n)) == OK and n.value == 256
+    # chunked (what auto picks): per (b, h, 16-token chunk) a 14,352-byte forward
+    # record and a 13,328-byte adjoint record at dk = 64, the chunk's start
+    # state and state cotangent (64 x 64 fp32 each), then U and dX (B*T*H*dv
+    # fp32 each); every region starts on a 256-byte boundary
+    up = lambda x: (x + 255) // 256 * 256
+    chunked = up(up(256 + 4 * 14352) + 4 * 13328) + 2 * 4 * 64 * 64 * 4 + 2 * 2 * 8 * 2 * 64 * 4
+    for algo in (0, 2):
+        assert lib.lam_backward_workspace_size(1, 1, 2, 8, 2, 64, 64, algo, ctypes.byref(n)) == OK
+        assert n.value == chunked, (algo, n.value, chunked)
+    assert lib.lam_backward_workspace_size(2, 1, 2, 8, 2, 64, 64, 2, ctypes.byref(n)) == UNSUPPORTED  # Kimi Delta
+    assert lib.lam_backward_workspace_size(2, 1, 2, 8, 2, 64, 64, 0, ctypes.byref(n)) == OK           # recurrent
+    assert lib.lam_backward_workspace_size(1, 1, 2, 8, 2, 64, 64, 3, ctypes.byref(n)) == INVALID      # algo
+    assert lib.lam_backward_workspace_size(1, 1, 2, 8, 2, 48, 64, 1, ctypes.byref(n)) == UNSUPPORTED
+    assert lib.lam_backward_workspace_size(9, 1, 2, 8, 2, 64, 64, 1, ctypes.byref(n)) == INVALID
+    assert _bwd(lib, algo=0, ws=FAKE + 0x200000000, ws_bytes=chunked - 1) == INVALID   # too small for chunked
     WS = FAKE + 0x200000000
     assert _bwd(lib) == INVALID                                       # no workspace
     assert _bwd(lib, ws=WS, ws_bytes=need - 1) == INVALID             # too small
