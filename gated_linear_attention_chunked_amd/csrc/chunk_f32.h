@@ -325,8 +325,8 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
     // refills each set it consumes (past the end: the last chunk again,
     // never used), so the loads in flight always form the same queue.  Three
     // sets keep the kernel under 256 registers a lane, so two four-wave
-    // workgroups share a CU.
-    constexpr int NS = 3;
+    // workgroups share a CU (two with KEEP's extra stores).
+    constexpr int NS = KEEP ? 2 : 3;
     Ops o[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) load(j, o[j]);

@@ -397,58 +397,90 @@ __global__ __launch_bounds__(256) void delta_f32_grad_kernel(DeltaBwdArgs ga, Bw
         const float4 x = keep(rok, IO::ld4(ga.dout, rowi + 16 * vt));
         return f32x4{x.x, x.y, x.z, x.w};
     };
-    float dgc = 0.f;
-    for (int kt = w; kt < DK / 16; kt += 4) {
-        f32x4 a1 = zero4, a2 = zero4, a3 = zero4;
-        for (int vt = 0; vt < DV / 16; ++vt) {
-            const f32x4 yr = row_dy(vt), xr = row_f32(wp.dx, vt), ur = row_f32(wp.u, vt);
-            const int64_t so = static_cast<int64_t>(16 * kt + i) * DV + 16 * vt + 4 * g;
-            const float4 sv4 = *reinterpret_cast<const float4 *>(S0 + so);
-            const float4 gv4 = *reinterpret_cast<const float4 *>(G1 + so);
-            const f32x4 sv = {sv4.x, sv4.y, sv4.z, sv4.w}, gv = {gv4.x, gv4.y, gv4.z, gv4.w};
+    // One pass over the value tiles, two at a time (every load of a pair in
+    // flight before the first product): this wave's key tiles kt = w + 4 jt
+    // take dY S0, dX S0 and U G'; waves 0 and 1 also take dY U^T and dX U^T
+    // from the same rows.
+    constexpr int KT = DK / 16, MT = (KT + 3) / 4;
+    f32x4 a1[MT], a2[MT], a3[MT];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                a1 = mfma4(yr[m], sv[m], a1);
-                a2 = mfma4(xr[m], sv[m], a2);
-                a3 = mfma4(ur[m], gv[m], a3);
-                dgc = fmaf(sv[m], gv[m], dgc);
+    for (int jt = 0; jt < MT; ++jt) a1[jt] = a2[jt] = a3[jt] = zero4;
+    f32x4 cc0 = zero4, cc1 = zero4;
+    float dgc = 0.f;
+    for (int vt = 0; vt < DV / 16; vt += 2) {  // DV / 16 is even
+        f32x4 yr[2], xr[2], ur[2], sv[2][MT], gv[2][MT];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            yr[u] = row_dy(vt + u);
+            xr[u] = row_f32(wp.dx, vt + u);
+            ur[u] = row_f32(wp.u, vt + u);
+#pragma unroll
+            for (int jt = 0; jt < MT; ++jt) {
+                const int kt = w + 4 * jt;
+                if (kt < KT) {
+                    const int64_t so = static_cast<int64_t>(16 * kt + i) * DV + 16 * (vt + u) + 4 * g;
+                    const float4 s4 = *reinterpret_cast<const float4 *>(S0 + so);
+                    const float4 g4 = *reinterpret_cast<const float4 *>(G1 + so);
+                    sv[u][jt] = f32x4{s4.x, s4.y, s4.z, s4.w};
+                    gv[u][jt] = f32x4{g4.x, g4.y, g4.z, g4.w};
+                }
             }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int o = (4 * g + r) * RS + 16 * kt + i;
-            s.p1[o] = a1[r];
-            s.p2[o] = a2[r];
-            s.pk[o] = a3[r];
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int jt = 0; jt < MT; ++jt) {
+                if (w + 4 * jt < KT) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        a1[jt] = mfma4(yr[u][m], sv[u][jt][m], a1[jt]);
+                        a2[jt] = mfma4(xr[u][m], sv[u][jt][m], a2[jt]);
+                        a3[jt] = mfma4(ur[u][m], gv[u][jt][m], a3[jt]);
+                        dgc = fmaf(sv[u][jt][m], gv[u][jt][m], dgc);
+                    }
+                }
+            }
+            if (w < 2) {
+                const f32x4 ar = w == 0 ? yr[u] : xr[u];
+                cc0 = mfma4(ar[0], ur[u][0], cc0);
+                cc1 = mfma4(ar[1], ur[u][1], cc1);
+                cc0 = mfma4(ar[2], ur[u][2], cc0);
+                cc1 = mfma4(ar[3], ur[u][3], cc1);
+            }
+        }
+    }
+#pragma unroll
+    for (int jt = 0; jt < MT; ++jt) {
+        const int kt = w + 4 * jt;
+        if (kt < KT) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int o = (4 * g + r) * RS + 16 * kt + i;
+                s.p1[o] = a1[jt][r];
+                s.p2[o] = a2[jt][r];
+                s.pk[o] = a3[jt][r];
+            }
         }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dgc += __shfl_xor(dgc, off);
     if (lane == 0) s.dgc[w] = dgc;
-    // ---- the 16 x 16 blocks: dY U^T (wave 0), dX U^T (wave 1), E K^T (wave 2), Q K^T (wave 3)
+    // ---- the 16 x 16 blocks: dY U^T (wave 0) and dX U^T (wave 1) from the
+    // pass above, E K^T (wave 2) and Q K^T (wave 3) from LDS
     {
-        f32x4 acc0 = zero4, acc1 = zero4;
-        if (w < 2) {
-            for (int vt = 0; vt < DV / 16; ++vt) {
-                const f32x4 ar = w == 0 ? row_dy(vt) : row_f32(wp.dx, vt), ur = row_f32(wp.u, vt);
-                acc0 = mfma4(ar[0], ur[0], acc0);
-                acc1 = mfma4(ar[1], ur[1], acc1);
-                acc0 = mfma4(ar[2], ur[2], acc0);
-                acc1 = mfma4(ar[3], ur[3], acc1);
-            }
-        } else {
+        if (w >= 2) {
             const float *X = w == 2 ? E : s.q;
 #pragma unroll
             for (int q4 = 0; q4 < DK / 16; ++q4) {
                 const f32x4 xr = lds4(&X[i * RS + 16 * q4 + 4 * g]);
                 const f32x4 kr = lds4(&s.k[i * RS + 16 * q4 + 4 * g]);
-                acc0 = mfma4(xr[0], kr[0], acc0);
-                acc1 = mfma4(xr[1], kr[1], acc1);
-                acc0 = mfma4(xr[2], kr[2], acc0);
-                acc1 = mfma4(xr[3], kr[3], acc1);
+                cc0 = mfma4(xr[0], kr[0], cc0);
+                cc1 = mfma4(xr[1], kr[1], cc1);
+                cc0 = mfma4(xr[2], kr[2], cc0);
+                cc1 = mfma4(xr[3], kr[3], cc1);
             }
         }
-        const f32x4 acc = acc0 + acc1;
+        const f32x4 acc = cc0 + cc1;
         float(*dst)[VC + 1] = w == 0 ? s.dyu : w == 1 ? s.dxu : w == 2 ? s.ek : s.qk;
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[4 * g + r][i] = acc[r];
@@ -480,30 +512,33 @@ __global__ __launch_bounds__(256) void delta_f32_grad_kernel(DeltaBwdArgs ga, Bw
             dg = fmaf(-E[t * RS + j], s.p2[t * RS + j], dg);
             dsc = fmaf(s.pk[t * RS + j], s.k[t * RS + j], dsc);
         }
-        float dbe = 0.f, gwr = 0.f, gwc = 0.f;
-        for (int u = 0; u < VC; ++u) {
-            dbe += s.bc[u][t];
-            gwr += s.gw[t][u];
-            gwc += s.gw[u][t];
-        }
+        float dbe = 0.f;
+        for (int u = 0; u < VC; ++u) dbe += s.bc[u][t];
         const float gC = s.gm[VC - 1];
         dbe = fmaf(dsc, exp2f(s.l2[VC - 1] - s.l2[t]), dbe);
         const int64_t ti = tk + static_cast<int64_t>(min(t, n - 1)) * H;
         if (t < n) ga.dbeta[ti] = dbe;
         if constexpr (kDecay) {
-            float scs = dsc * s.sc[t];
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) scs += __shfl_xor(scs, off, 16);
-            float dlg = gwr - gwc + dg * s.gm[t] - dsc * s.sc[t];
-            if (t == n - 1) dlg += (s.dgc[0] + s.dgc[1] + s.dgc[2] + s.dgc[3]) * gC + scs;
-            if (t >= n) dlg = 0.f;
-            // d log alpha_j = sum_{t >= j} d log gamma_t (suffix sum over the chunk)
+            // d log alpha_j = sum_{t >= j} d log gamma_t, summed in the form
+            // without cancellation: the Gamma terms with both indices >= j
+            // cancel (only gw_ab, a >= j > b, remain), and so do the sc terms
+            // of tokens >= j against the last token's sum:
+            //   sum_{a >= j, b < j} gw_ab + sum_{t >= j} dg_t gamma_t
+            //   + <G', S0> gamma_C + sum_{s < j} dsc_s sc_s
+            float dlog = 0.f;
+            for (int aa = t; aa < VC; ++aa)
+                for (int bb = 0; bb < t; ++bb) dlog += s.gw[aa][bb];
+            float dgs = dg * s.gm[t];  // suffix sum over t' >= t
+            float scp = dsc * s.sc[t];  // prefix sum over t' <= t, made exclusive below
+            const float own = scp;
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) {
-                const float y = __shfl_down(dlg, off, 16);
-                dlg += t + off < 16 ? y : 0.f;
+                const float y = __shfl_down(dgs, off, 16), z = __shfl_up(scp, off, 16);
+                dgs += t + off < 16 ? y : 0.f;
+                scp += t >= off ? z : 0.f;
             }
-            if (t < n) ga.dalpha[ti] = dlg / IO::ld(a.alpha, ti);
+            dlog += dgs + (s.dgc[0] + s.dgc[1] + s.dgc[2] + s.dgc[3]) * gC + (scp - own);
+            if (t < n) ga.dalpha[ti] = dlog / IO::ld(a.alpha, ti);
         }
     }
 
