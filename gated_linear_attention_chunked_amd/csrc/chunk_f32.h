@@ -194,9 +194,11 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
         }
     }
     const ChunkRec<DK> *R0 = rec + static_cast<int64_t>(head) * nch;
-    const bool is_carry = w < NW, is_y = w == YW;
+    // KEEP forms no output: no Qtil or Aq Tc operands, no Y products
+    const bool is_carry = w < NW, is_y = !KEEP && w == YW;
+    constexpr int QN = KEEP ? 1 : TPW;
     struct Ops {
-        f32x4 kt[TPW], qt[TPW], aht[TPW], top, aqt;
+        f32x4 kt[TPW], qt[QN], aht[TPW], top, aqt;
         float v[4], w[GATES2 ? 4 : 1], gc;
     };
     // Every wave issues the same loads whatever its role (an output-only wave
@@ -210,10 +212,10 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
         for (int j = 0; j < TPW; ++j) {
             const int kr = 16 * (TPW * wc + j);
             o.kt[j] = *reinterpret_cast<const f32x4 *>(&R.kt[i * DK + kr + 4 * g]);
-            o.qt[j] = *reinterpret_cast<const f32x4 *>(&R.qt[i * DK + kr + 4 * g]);
+            if constexpr (!KEEP) o.qt[j] = *reinterpret_cast<const f32x4 *>(&R.qt[i * DK + kr + 4 * g]);
             o.aht[j] = R.aht[TPW * wc + j][lane];
         }
-        o.aqt = R.aqt[lane];
+        if constexpr (!KEEP) o.aqt = R.aqt[lane];
         o.top = R.top[lane];
         const int t0 = cc * VC, n = min(VC, T - t0);
         const int64_t cb = chunk_base(t0);
@@ -257,15 +259,19 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
             for (int j = 0; j < TPW; ++j) {
                 pk0 = mfma4(cur.kt[j][0], ST[j][0], pk0);
                 pk1 = mfma4(cur.kt[j][1], ST[j][1], pk1);
-                pq0 = mfma4(cur.qt[j][0], ST[j][0], pq0);
-                pq1 = mfma4(cur.qt[j][1], ST[j][1], pq1);
+                if constexpr (!KEEP) {
+                    pq0 = mfma4(cur.qt[j][0], ST[j][0], pq0);
+                    pq1 = mfma4(cur.qt[j][1], ST[j][1], pq1);
+                }
                 pk0 = mfma4(cur.kt[j][2], ST[j][2], pk0);
                 pk1 = mfma4(cur.kt[j][3], ST[j][3], pk1);
-                pq0 = mfma4(cur.qt[j][2], ST[j][2], pq0);
-                pq1 = mfma4(cur.qt[j][3], ST[j][3], pq1);
+                if constexpr (!KEEP) {
+                    pq0 = mfma4(cur.qt[j][2], ST[j][2], pq0);
+                    pq1 = mfma4(cur.qt[j][3], ST[j][3], pq1);
+                }
             }
             part[p][0][w][lane] = pk0 + pk1;
-            part[p][1][w][lane] = pq0 + pq1;
+            if constexpr (!KEEP) part[p][1][w][lane] = pq0 + pq1;
         }
         // V's rows (zero past the end), the B operand of Tc V and (Aq Tc) V
         f32x4 vb;
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
             tv[p][lane] = a0 + a1;
         }
         f32x4 y0 = zero;
-        if (is_y) {
+        if (!KEEP && is_y) {
             f32x4 y1 = mfma4(cur.aqt[1], vb[1], zero);
             y0 = mfma4(cur.aqt[0], vb[0], zero);
             y1 = mfma4(cur.aqt[3], vb[3], y1);
@@ -311,7 +317,7 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
                     if (4 * g + r < n) a.u_f32[cb + roff[r]] = u[r];
             }
         }
-        if (is_y) {  // Y = Qtil S^T + (Aq Tc) V
+        if (!KEEP && is_y) {  // Y = Qtil S^T + (Aq Tc) V
             f32x4 y = part[p][1][0][lane];
 #pragma unroll
             for (int j = 1; j < NW; ++j) y += part[p][1][j][lane];
@@ -530,7 +536,7 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_adjoint_kernel(A
             }
         }
     };
-    constexpr int NS = 3;
+    constexpr int NS = KEEP ? 2 : 3;
     Ops o[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) load(j, o[j]);

@@ -189,18 +189,20 @@ __global__ __launch_bounds__(64) void delta_f32_derive_kernel(DeltaArgs a, Chunk
             else k0 = mfma4(tc[m], bm, k0);
         }
         const f32x4 kt = k0 + k1;  // lane (g, i): Ktil[4g + r][col], the B operand of Aq Ktil
-        // Qtil = diag(gamma) Q - Aq Ktil
+        // Qtil = diag(gamma) Q - Aq Ktil (not for the backward: its forward
+        // recompute forms no output)
         f32x4 q0, q1 = zero4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) q0[r] = gmv[r] * s.q[(4 * g + r) * RS + col];
         if constexpr (BWD) {  // (gamma Q)^T and (gamma E)^T tiles: the same values in A-operand order
             arec[blockIdx.x].gqt[j][lane] = q0;
             arec[blockIdx.x].get[j][lane] = ge;
+        } else {
+            q0 = mfma4(-aqa[0], kt[0], q0);
+            q1 = mfma4(-aqa[1], kt[1], q1);
+            q0 = mfma4(-aqa[2], kt[2], q0);
+            q1 = mfma4(-aqa[3], kt[3], q1);
         }
-        q0 = mfma4(-aqa[0], kt[0], q0);
-        q1 = mfma4(-aqa[1], kt[1], q1);
-        q0 = mfma4(-aqa[2], kt[2], q0);
-        q1 = mfma4(-aqa[3], kt[3], q1);
         const f32x4 qt = q0 + q1;
         // Ahat^T tile j, A-operand order: lane (g, i) step m holds Ahat[4g + m][col]
         f32x4 ah;
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(64) void delta_f32_derive_kernel(DeltaArgs a, Chunk
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             R.kt[(4 * g + r) * DK + col] = kt[r];
-            R.qt[(4 * g + r) * DK + col] = qt[r];
+            if constexpr (!BWD) R.qt[(4 * g + r) * DK + col] = qt[r];
         }
         R.aht[j][lane] = ah;
         if constexpr (BWD) {  // Ahat' = Tc^T Ahat: A operand Tc^T, B operand Ahat (step m: Ahat[4g + m][col])
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(64) void delta_f32_derive_kernel(DeltaArgs a, Chunk
     R.top[lane] = tc;
     // Aq Tc in A-operand order, as (Aq Tc)^T = Tc^T Aq^T: A operand Tc^T
     // (lane (g, i) step m: Tc[4g + m][i]), B operand Aq^T (step m: Aq[i][4g + m])
-    {
+    if constexpr (!BWD) {
         f32x4 a0 = zero4, a1 = zero4;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
