@@ -536,7 +536,7 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_adjoint_kernel(A
             }
         }
     };
-    constexpr int NS = KEEP ? 2 : 3;
+    constexpr int NS = 3;
     Ops o[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) load(j, o[j]);
