@@ -125,7 +125,7 @@ struct ScanArgs {
     void *side;              // per-token routing signal [B,T,H,DV] or NULL
     int side_kind;           // kSideResidual (U) or kSideValue (z)
     // the backward pass's forward recompute (KEEP) also writes:
-    float *s_chunks;         // S^T at every chunk start, [B*H][chunks][DK][DV] fp32
+    float *s_chunks;         // S^T at the start of every even chunk, [B*H][pairs][DK][DV] fp32
     float *u_f32;            // the residuals U, [B,T,H,DV] fp32
 };
 
@@ -244,8 +244,8 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
         const int p = c & 1, t0 = c * VC, n = min(VC, T - t0);
         const int64_t cb = chunk_base(t0);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        if (KEEP && is_carry) {  // the state at this chunk's start, S^T rows
-            float *dst = a.s_chunks + (static_cast<int64_t>(head) * nch + c) * DK * DV + vcol;
+        if (KEEP && is_carry && (c & 1) == 0) {  // the state at this pair of chunks' start, S^T rows
+            float *dst = a.s_chunks + (static_cast<int64_t>(head) * ((nch + 1) / 2) + (c >> 1)) * DK * DV + vcol;
 #pragma unroll
             for (int j = 0; j < TPW; ++j)
 #pragma unroll
@@ -388,7 +388,8 @@ struct AdjArgs {
     const void *v, *w;           // targets and write gates (Gated DeltaNet-2), else NULL
     const float *dS_in;          // cotangent of the final state [B,H,DV,DK] or NULL (zero)
     float *dS_out;               // cotangent of the initial state [B,H,DV,DK] or NULL
-    float *ds_chunks;            // G' at every chunk end (the same layout as S^T rows per chunk)
+    float *ds_chunks;            // G' at the end of every pair of chunks (odd chunks, and the
+                                 // last chunk), the layout of s_chunks
     float *dx;                   // dX [B,T,H,DV] fp32
     float *dv_out, *dw_out;      // gradients of v and (Gated DeltaNet-2) w, [B,T,H,DV] fp32
 };
@@ -471,13 +472,15 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_adjoint_kernel(A
         const int64_t cb = chunk_base(t0);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         if (is_carry) {
-            // G' (the cotangent of the state after this chunk), kept for the
-            // gradient kernel
-            float *dst = a.ds_chunks + (static_cast<int64_t>(head) * nch + c) * DK * DV + vcol;
+            // G' (the cotangent of the state after this chunk) at the end of
+            // each pair of chunks, kept for the gradient kernel
+            if ((c & 1) || c == nch - 1) {
+                float *dst = a.ds_chunks + (static_cast<int64_t>(head) * ((nch + 1) / 2) + (c >> 1)) * DK * DV + vcol;
 #pragma unroll
-            for (int j = 0; j < TPW; ++j)
+                for (int j = 0; j < TPW; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dst[static_cast<int64_t>(16 * (TPW * w + j) + 4 * g + r) * DV] = GT[j][r];
+                    for (int r = 0; r < 4; ++r) dst[static_cast<int64_t>(16 * (TPW * w + j) + 4 * g + r) * DV] = GT[j][r];
+            }
             // partial Ahat' G' over this wave's key rows
             f32x4 pk0 = zero, pk1 = zero;
 #pragma unroll

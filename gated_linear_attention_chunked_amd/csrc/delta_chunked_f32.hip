@@ -325,11 +325,12 @@ struct GradLds {
 };
 
 struct BwdWs {
-    const float *s_chunks, *ds_chunks, *u, *dx;
+    const float *s_chunks, *ds_chunks, *u, *dx;  // states per pair of chunks; U and dX per token
+    const void *rec, *arec;                      // the chunk records and adjoint records
 };
 
 template <typename IO, int VARIANT, int DK>
-__global__ __launch_bounds__(256) void delta_f32_grad_kernel(DeltaBwdArgs ga, BwdWs wp) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void delta_f32_grad_kernel(DeltaBwdArgs ga, BwdWs wp) {
     constexpr bool kDecay = VARIANT != kDeltaNet;
     constexpr bool kGates2 = VARIANT == kGatedDeltaNet2;
     using L = GradLds<DK, kGates2>;
@@ -387,8 +388,39 @@ __global__ __launch_bounds__(256) void delta_f32_grad_kernel(DeltaBwdArgs ga, Bw
 
     // ---- products over the value dimension: lane (g, i) reads row i (token
     // t0 + i, zero past the end), values 16 vt + 4g .. + 3
-    const float *S0 = wp.s_chunks + (static_cast<int64_t>(head) * nch + c) * DK * DV;   // S0^T rows
-    const float *G1 = wp.ds_chunks + (static_cast<int64_t>(head) * nch + c) * DK * DV;  // G'^T rows
+    // The states are kept per pair of chunks: S at the start of the even
+    // chunk, G' at the end of the odd one (or of the last chunk).  An odd
+    // chunk forms its S0 = gC_prev S + U_prev^T Ahat_prev from its
+    // predecessor; an even chunk with a successor forms its
+    // G' = gC_next G'_next + dY_next^T (gamma Q)_next - dX_next^T (gamma E)_next.
+    // Both come out in the order the products below read them (lane (g, i):
+    // value 4g + m of the tile, key i).
+    constexpr int KT = DK / 16, MT = (KT + 3) / 4;
+    const int np = (nch + 1) / 2;
+    const bool odd = c & 1, from_next = !odd && c + 1 < nch;
+    const float *S0 = wp.s_chunks + (static_cast<int64_t>(head) * np + (c >> 1)) * DK * DV;   // S^T rows
+    const float *G1 = wp.ds_chunks + (static_cast<int64_t>(head) * np + (c >> 1)) * DK * DV;  // G'^T rows
+    // B operands of the update, per key tile (odd: Ahat_prev; even: (gamma
+    // Q)_next and (gamma E)_next), and its decay
+    f32x4 b1[MT], b2[MT];
+    float g_nb = 1.f;
+    if (odd) {
+        const ChunkRec<DK> &Rp = static_cast<const ChunkRec<DK> *>(wp.rec)[static_cast<int64_t>(head) * nch + c - 1];
+        g_nb = Rp.gc[0];
+#pragma unroll
+        for (int jt = 0; jt < MT; ++jt)
+            if (w + 4 * jt < KT) b1[jt] = Rp.aht[w + 4 * jt][lane];
+    } else if (from_next) {
+        const AdjRec<DK> &An = static_cast<const AdjRec<DK> *>(wp.arec)[static_cast<int64_t>(head) * nch + c + 1];
+        g_nb = An.gc[0];
+#pragma unroll
+        for (int jt = 0; jt < MT; ++jt)
+            if (w + 4 * jt < KT) {
+                b1[jt] = An.gqt[w + 4 * jt][lane];
+                b2[jt] = An.get[w + 4 * jt][lane];
+            }
+    }
+    const int n_next = min(VC, T - t0 - VC);  // rows of the next chunk (when there is one)
     const bool rok = i < n;
     const int64_t rowi = (tk + static_cast<int64_t>(min(i, n - 1)) * H) * DV + 4 * g;
     auto row_f32 = [&](const float *base, int vt) {
@@ -403,7 +435,6 @@ __global__ __launch_bounds__(256) void delta_f32_grad_kernel(DeltaBwdArgs ga, Bw
     // flight before the first product): this wave's key tiles kt = w + 4 jt
     // take dY S0, dX S0 and U G'; waves 0 and 1 also take dY U^T and dX U^T
     // from the same rows.
-    constexpr int KT = DK / 16, MT = (KT + 3) / 4;
     f32x4 a1[MT], a2[MT], a3[MT];
 #pragma unroll
     for (int jt = 0; jt < MT; ++jt) a1[jt] = a2[jt] = a3[jt] = zero4;
@@ -411,6 +442,9 @@ __global__ __launch_bounds__(256) void delta_f32_grad_kernel(DeltaBwdArgs ga, Bw
     float dgc = 0.f;
     for (int vt = 0; vt < DV / 16; vt += 2) {  // DV / 16 is even
         f32x4 yr[2], xr[2], ur[2], sv[2][MT], gv[2][MT];
+        // A operands of the update (odd: U_prev; even: dY_next, dX_next): lane
+        // (g, i) step m holds token 4g + m, value 16 vt + i
+        f32x4 a_1[2], a_2[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             yr[u] = row_dy(vt + u);
@@ -427,6 +461,43 @@ __global__ __launch_bounds__(256) void delta_f32_grad_kernel(DeltaBwdArgs ga, Bw
                     gv[u][jt] = f32x4{g4.x, g4.y, g4.z, g4.w};
                 }
             }
+            if (odd) {  // the previous chunk is whole
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    a_1[u][m] = wp.u[(tk + static_cast<int64_t>(4 * g + m - VC) * H) * DV + 16 * (vt + u) + i];
+            } else if (from_next) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int r = 4 * g + m;
+                    const int64_t o = (tk + static_cast<int64_t>(VC + min(r, n_next - 1)) * H) * DV + 16 * (vt + u) + i;
+                    const float yv = IO::ld(ga.dout, o), xv = wp.dx[o];
+                    a_1[u][m] = r < n_next ? yv : 0.f;
+                    a_2[u][m] = r < n_next ? -xv : 0.f;
+                }
+            }
+        }
+        if (odd || from_next) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int jt = 0; jt < MT; ++jt) {
+                    if (w + 4 * jt < KT) {
+                        if (odd) {
+                            f32x4 acc = sv[u][jt] * g_nb;
+#pragma unroll
+                            for (int m = 0; m < 4; ++m) acc = mfma4(a_1[u][m], b1[jt][m], acc);
+                            sv[u][jt] = acc;
+                        } else {
+                            f32x4 acc = gv[u][jt] * g_nb;
+#pragma unroll
+                            for (int m = 0; m < 4; ++m) {
+                                acc = mfma4(a_1[u][m], b1[jt][m], acc);
+                                acc = mfma4(a_2[u][m], b2[jt][m], acc);
+                            }
+                            gv[u][jt] = acc;
+                        }
+                    }
+                }
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -587,7 +658,7 @@ bool bwd_layout(const DeltaArgs &a, BwdLayout<DK> *L) {
     const int64_t nch = (a.T + VC - 1) / VC, tasks = a.B * a.H * nch;
     if (tasks > 0x7fffffff || a.B * a.H * (a.dv / 16) > 0x7fffffff) return false;
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-    const size_t st = static_cast<size_t>(tasks) * DK * a.dv * sizeof(float);
+    const size_t st = static_cast<size_t>(a.B * a.H * ((nch + 1) / 2)) * DK * a.dv * sizeof(float);  // per pair of chunks
     const size_t rows = static_cast<size_t>(a.B * a.T * a.H) * a.dv * sizeof(float);
     L->rec_off = kStatusBytes;
     L->arec_off = up(L->rec_off + static_cast<size_t>(tasks) * sizeof(ChunkRec<DK>));
@@ -645,7 +716,7 @@ hipError_t launch_bwd_kd(const DeltaBwdArgs &g, hipStream_t stream) {
     aa.dw_out = kGates2 ? g.dwrite_w : nullptr;
     chunk_adjoint_kernel<IO, DK, kDecay, kGates2><<<scan_grid, 64 * state_waves<DK>(), 0, stream>>>(aa, arec);
     delta_f32_grad_kernel<IO, VARIANT, DK>
-        <<<static_cast<unsigned>(tasks), 256, 0, stream>>>(g, BwdWs{s_chunks, ds_chunks, u, dx});
+        <<<static_cast<unsigned>(tasks), 256, 0, stream>>>(g, BwdWs{s_chunks, ds_chunks, u, dx, rec, arec});
     return hipGetLastError();
 }
 

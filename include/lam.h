@@ -331,9 +331,9 @@ lam_status lam_vla_workspace_size(int dtype, int64_t B, int64_t T, int64_t H, in
  *                   returns LAM_ERR_UNSUPPORTED.
  *   workspace       lam_backward_workspace_size bytes for the same algo.
  *                   Chunked: per (b, h, 16-token chunk) the two records
- *                   (52 KB at dk = 128) and the chunk's start state and
- *                   state cotangent (2 * dv * dk * 4 B), plus U and dX
- *                   (2 * B*T*H*dv * 4 B): 3.2 GB at B8 T4096 H8 d128.
+ *                   (52 KB at dk = 128), per (b, h, pair of chunks) a state
+ *                   and a state cotangent (2 * dv * dk * 4 B), plus U and dX
+ *                   (2 * B*T*H*dv * 4 B): 2.2 GB at B8 T4096 H8 d128.
  *                   Recurrent: the forward state every 16 tokens,
  *                   B*H*ceil(T/16)*dv*dk*4 B.  Both plus the status block.
  * T = 0 writes dstate_in = dstate_out (zero if NULL).
