@@ -361,14 +361,15 @@ __global__ __launch_bounds__(64 * state_waves<DK>()) void chunk_state_kernel(Sca
 
 
 // ------------------------------------------------------------ adjoint scan
-// Reverse mode of the state step above.  With G = dL/dS^T at a chunk's end
-// (G' below) and dY the output cotangents of the chunk, the adjoint of
+// Reverse mode of the state step above (the delta-rule form, Ktil =
+// Tc diag(gamma) E).  With G' = dL/dS^T at a chunk's end, G the same at its
+// start and dY the chunk's output cotangents, the adjoint of
 //   U = Tc Z - Ktil S^T,  Y = diag(gamma) Q S^T + Aq U,  S'^T = gC S^T + Ahat^T U
 // is, per chunk in reverse,
-//   dX   = dU-adjoint of the solve = (Aq Tc)^T dY + Ahat' G',  Ahat' = Tc^T Ahat,
-//   G    = gC G' + (diag(gamma) Q)^T dY - (diag(gamma) E)^T dX,
+//   dX = Tc^T (Aq^T dY + Ahat G'^T) = (Aq Tc)^T dY + Ahat' G'^T,  Ahat' = Tc^T Ahat,
+//   G  = gC G' + (diag(gamma) Q)^T dY - (diag(gamma) E)^T dX,
 // and dX is the gradient of the chunk's targets Z.  It has the state step's
-// shape: one product over the key dimension (Ahat' G') summed across the
+// shape: one product over the key dimension (Ahat' G'^T) summed across the
 // waves, a state-independent term ((Aq Tc)^T dY) formed beside it, and a
 // rank-16 update of the carried tiles.  Ahat' and the transposed operands
 // come from the same derivation, in this record.

@@ -21,6 +21,12 @@
 // Every exponent is a difference g_t - g_s with s <= t (or g_C - g_t), so no
 // factor exceeds one.  Nothing here crosses chunks, so the derivation runs
 // for every chunk at once; the state kernel then walks the chunks.
+//
+// The backward pass of the same rule (the gradients of sum <dY, Y> +
+// <dS_T, S_T>) is here too: the derivation with the adjoint records, the
+// forward again keeping the states it needs, the adjoint scan of
+// chunk_f32.h in reverse, and a chunk-parallel kernel for the gradients
+// (below, "backward").
 #include "chunk_f32.h"
 
 namespace lam {
