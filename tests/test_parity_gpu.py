@@ -138,13 +138,14 @@ def test_chunked_long_sequences(variant, T, dk):
     U.check(w, got, ref, label=w.name)
 
 
-@pytest.mark.parametrize("variant", ["gdn", "gdn2", "kda"])
-def test_chunked_workspaces_streams_and_threads(variant):
+@pytest.mark.parametrize("variant,dtype", [("gdn", "bf16"), ("gdn2", "bf16"), ("kda", "bf16"),
+                                           ("gdn", "f32"), ("gdn2", "f32"), ("deltanet", "f32")])
+def test_chunked_workspaces_streams_and_threads(variant, dtype):
     """The caller owns the workspace.  Calls queued on two streams with a
     workspace each, a small call reusing a large call's workspace on one
     stream, and calls from two host threads on one stream (each with a
     workspace from torch's allocator) must all give the results of isolated
-    calls, bit for bit."""
+    calls, bit for bit (fp32 storage: the fp32 chunked form)."""
     import threading
 
     import torch
@@ -152,10 +153,10 @@ def test_chunked_workspaces_streams_and_threads(variant):
     import gated_linear_attention_chunked_amd as lam
 
     shapes = [(2, 900, 4, 128, 128), (3, 130, 2, 64, 64)]
-    ws = [_w(variant, "bf16", *sh, seed=5100 + i) for i, sh in enumerate(shapes)]
+    ws = [_w(variant, dtype, *sh, seed=5100 + i) for i, sh in enumerate(shapes)]
     xs = [I.make_inputs(w) for w in ws]
     alone = [U.run_gpu(w, x, algo="chunked") for w, x in zip(ws, xs)]
-    gs = [I.to_device(x, "bf16", "cuda") for x in xs]
+    gs = [I.to_device(x, dtype, "cuda") for x in xs]
 
     def call(g, **kw):
         return lam.forward(variant, g["q"], g["k"], g["v"], g["beta"], alpha=g.get("alpha"),
@@ -166,7 +167,7 @@ def test_chunked_workspaces_streams_and_threads(variant):
         assert np.array_equal(out.float().cpu().numpy().astype(np.float64), ref[0])
         assert np.array_equal(st.cpu().numpy().astype(np.float64), ref[1])
 
-    need = [lam.workspace_size(variant, "bf16", *sh, algo="chunked") for sh in shapes]
+    need = [lam.workspace_size(variant, dtype, *sh, algo="chunked") for sh in shapes]
     assert need[0] > need[1] > 0
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     wss = [torch.empty(n, dtype=torch.uint8, device="cuda") for n in need]
