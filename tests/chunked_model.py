@@ -214,7 +214,7 @@ def kda_paired(q, k, v, beta, alpha, state_in=None):
 
 
 def delta_chunked_backward(variant, q, k, v, beta, dout, alpha=None, erase_b=None, write_w=None,
-                           state_in=None, dstate_out=None, C=64):
+                           state_in=None, dstate_out=None, C=64, dlog_direct=False):
     """Adjoint of the chunked form above for DeltaNet, Gated DeltaNet and
     Gated DeltaNet-2, in the residual form the GPU evaluates: per chunk, with
     N = strict(E K^T * Gam), A = lower(Q K^T * Gam) diag(beta) and
@@ -317,8 +317,58 @@ def delta_chunked_backward(variant, q, k, v, beta, dout, alpha=None, erase_b=Non
                 out["dk"][b, c0:c1, h] = dK
                 out["dbeta"][b, c0:c1, h] = dbe
                 if variant != "deltanet":
-                    dlog = np.cumsum(dlg[::-1])[::-1]          # d log(alpha_j) = sum_{t >= j} dlg_t
+                    if dlog_direct:
+                        # the same sums with the cancelling terms left out: the
+                        # Gamma terms with both indices >= j and the sc terms of
+                        # tokens >= j against the last token's sum
+                        dg_g = (dg * g)[::-1].cumsum()[::-1]
+                        sc_pre = np.concatenate([[0.0], np.cumsum(dsc * sc)[:-1]])
+                        dlog = np.array([gw[j:, :j].sum() for j in range(n)]) + dg_g + dgC * g[-1] + sc_pre
+                    else:
+                        dlog = np.cumsum(dlg[::-1])[::-1]      # d log(alpha_j) = sum_{t >= j} dlg_t
                     out["dalpha"][b, c0:c1, h] = dlog / alpha[b, c0:c1, h]
                 dS = dSn
             out["dstate_in"][b, h] = dS
     return out
+
+
+def delta_record_adjoint(variant, q, k, v, beta, dout, alpha=None, erase_b=None, write_w=None,
+                         state_in=None, dstate_out=None, C=16):
+    """The reverse scan in the record form the GPU's adjoint kernel runs: per
+    chunk, with Tc = (I + N diag(beta))^{-1}, Aq = lower(Q K^T * Gam) diag(beta),
+    Ahat = diag(beta gamma_C / gamma) K and Ahat' = Tc^T Ahat,
+        dX  = (Aq Tc)^T dY + Ahat' G'^T,
+        G^T = gamma_C G'^T + (diag(gamma) Q)^T dY - (diag(gamma) E)^T dX.
+    Returns (dX [B, T, H, dv], dstate_in [B, H, dv, dk]); dX is the gradient of
+    the targets z (v, or w * v for Gated DeltaNet-2)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    g2 = variant == "gdn2"
+    dX = np.zeros((B, T, H, dv))
+    dS_in = np.zeros((B, H, dv, dk))
+    for b in range(B):
+        for h in range(H):
+            recs = []
+            for c0 in range(0, T, C):
+                c1 = min(T, c0 + C)
+                n = c1 - c0
+                Q, K = q[b, c0:c1, h], k[b, c0:c1, h]
+                be = beta[b, c0:c1, h]
+                tril = np.tril(np.ones((n, n)))
+                stril = np.tril(np.ones((n, n)), -1)
+                lg = np.zeros(n) if variant == "deltanet" else np.cumsum(np.log(alpha[b, c0:c1, h]))
+                Gam = np.where(tril > 0, np.exp(np.where(tril > 0, lg[:, None] - lg[None, :], 0.0)), 0.0)
+                g = np.exp(lg)
+                E = erase_b[b, c0:c1, h] * K if g2 else K
+                Tc = np.linalg.inv(np.eye(n) + (stril * (E @ K.T) * Gam) * be[None, :])
+                Aq = (tril * (Q @ K.T) * Gam) * be[None, :]
+                Ah = (be * np.exp(lg[-1] - lg))[:, None] * K
+                recs.append((c0, c1, Tc.T @ Ah, Aq @ Tc, g[:, None] * Q, g[:, None] * E, g[-1]))
+            G = np.zeros((dv, dk)) if dstate_out is None else dstate_out[b, h].copy()
+            for (c0, c1, Ap, AqTc, gQ, gE, gC) in reversed(recs):
+                dY = dout[b, c0:c1, h]
+                x = AqTc.T @ dY + Ap @ G.T
+                dX[b, c0:c1, h] = x
+                G = (gC * G.T + gQ.T @ dY - gE.T @ x).T
+            dS_in[b, h] = G
+    return dX, dS_in

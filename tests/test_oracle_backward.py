@@ -132,3 +132,49 @@ def test_chunked_adjoint_equals_token_adjoint(variant, C):
     for n, g in ref.items():
         scale = max(np.max(np.abs(g)), 1e-30)
         assert np.max(np.abs(got[n] - g)) <= 1e-10 * scale, (n, np.max(np.abs(got[n] - g)) / scale)
+
+
+@pytest.mark.parametrize("variant", ["deltanet", "gdn", "gdn2"])
+@pytest.mark.parametrize("C", [1, 16])
+def test_record_form_adjoint_scan(variant, C):
+    """The reverse scan in the record form the adjoint kernel runs (Ahat' =
+    Tc^T Ahat, (Aq Tc)^T, the decayed query and erase-key operands) gives the
+    oracle's dW0 and, through dX, its dv (and dw for Gated DeltaNet-2)."""
+    from tests import chunked_model
+
+    r = np.random.default_rng(23)
+    x, dout, dstate = _inputs(29, variant, B=1, T=45, H=2, dk=8, dv=6)
+    if "alpha" in x:
+        x["alpha"] = r.uniform(0.6, 1.0, x["alpha"].shape)
+    ref = _grads(variant, x, dout, dstate)
+    dX, dS = chunked_model.delta_record_adjoint(variant, x["q"], x["k"], x["v"], x["beta"], dout,
+                                                alpha=x.get("alpha"), erase_b=x.get("erase_b"),
+                                                write_w=x.get("write_w"), state_in=x["state_in"],
+                                                dstate_out=dstate, C=C)
+    tol = lambda g: 1e-10 * max(np.max(np.abs(g)), 1e-30)
+    assert np.max(np.abs(dS - ref["dstate_in"])) <= tol(ref["dstate_in"])
+    if variant == "gdn2":
+        assert np.max(np.abs(x["write_w"] * dX - ref["dv"])) <= tol(ref["dv"])
+        assert np.max(np.abs(x["v"] * dX - ref["dwrite_w"])) <= tol(ref["dwrite_w"])
+    else:
+        assert np.max(np.abs(dX - ref["dv"])) <= tol(ref["dv"])
+
+
+@pytest.mark.parametrize("variant", ["gdn", "gdn2"])
+@pytest.mark.parametrize("C", [4, 16])
+def test_direct_decay_gradient_form(variant, C):
+    """d alpha summed without the cancelling terms (the form the chunked
+    gradient kernel uses) equals the oracle's, also under strong decays."""
+    from tests import chunked_model
+
+    for lo, hi in ((0.85, 1.0), (0.001, 0.01)):
+        r = np.random.default_rng(31)
+        x, dout, dstate = _inputs(37, variant, B=1, T=40, H=2, dk=8, dv=6)
+        x["alpha"] = r.uniform(lo, hi, x["alpha"].shape)
+        ref = _grads(variant, x, dout, dstate)
+        got = chunked_model.delta_chunked_backward(variant, x["q"], x["k"], x["v"], x["beta"], dout,
+                                                   alpha=x["alpha"], erase_b=x.get("erase_b"),
+                                                   write_w=x.get("write_w"), state_in=x["state_in"],
+                                                   dstate_out=dstate, C=C, dlog_direct=True)
+        g = ref["dalpha"]
+        assert np.max(np.abs(got["dalpha"] - g)) <= 1e-9 * np.max(np.abs(g)), (lo, hi)
