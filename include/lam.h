@@ -52,7 +52,9 @@
  *   dk = 128: 6,144 B per (b, h, 64-token chunk) for DeltaNet, Gated
  *   DeltaNet and Gated DeltaNet-2 (25.2 MB at B8 T4096 H8), and 14,848 B per
  *   (b, h, 16-token sub-chunk, counted in whole pairs) for Kimi Delta
- *   (487 MB at B2 T32768 H8), plus the 256-byte status block.
+ *   (487 MB at B2 T32768 H8); the fp32 chunked form (fp32 storage, and
+ *   bf16 at dk 32 / 96): 26,640 B per (b, h, 16-token chunk) at dk = 128,
+ *   8,208 B at dk = 32; plus the 256-byte status block.
  *   Status block: the first 256 bytes of a workspace.  Word 0 (uint32)
  *   receives LAM_DEVICE_* bits from the call's kernels: the call's first
  *   kernel sets it to 0, and a later kernel ORs in LAM_DEVICE_WAIT_TIMEOUT if
@@ -171,9 +173,10 @@ typedef enum { LAM_SIDE_NONE = 0, LAM_SIDE_RESIDUAL = 1, LAM_SIDE_VALUE = 2 } la
  *   side_out     [B,T,H,dv] in dtype, required unless LAM_SIDE_NONE; may not
  *                overlap any other argument or the workspace
  * Same workspace (lam_forward_workspace_size), schedules and errors as
- * lam_forward.  On the chunked schedule the residual is rounded to bf16 where
- * the scan rounds it for its own products (the value emitted is the one the
- * memory update uses); the token-recurrent schedule computes it in fp32.
+ * lam_forward.  On the bf16 chunked schedules the residual is rounded to bf16
+ * where the scan rounds it for its own products (the value emitted is the one
+ * the memory update uses); the fp32 chunked form and the token-recurrent
+ * schedule compute it in fp32.
  */
 lam_status lam_forward_side(int variant, int dtype, int64_t B, int64_t T, int64_t H, int64_t dk,
                             int64_t dv, const void *q, const void *k, const void *v,
@@ -420,8 +423,10 @@ lam_status lam_forward_noalloc(int variant, int dtype, int64_t B, int64_t T, int
 /*
  * The schedule LAM_ALGO_AUTO runs for these arguments: LAM_ALGO_RECURRENT or
  * LAM_ALGO_CHUNKED (the chunked one computes its contractions with bf16
- * operands and fp32 accumulation when dtype is LAM_BF16, in fp32 otherwise).
- * Returns -1 for arguments lam_forward would reject.
+ * operands and fp32 accumulation when dtype is LAM_BF16 and dk is 64 or 128,
+ * in fp32 on 16-token chunks otherwise; Kimi Delta's chunked schedule takes
+ * bf16 at dk 64 / 128 only).  Returns -1 for arguments lam_forward would
+ * reject.
  */
 int lam_select_algo(int variant, int dtype, int64_t T, int64_t dk, int64_t dv);
 
