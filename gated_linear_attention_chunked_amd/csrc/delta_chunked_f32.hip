@@ -323,10 +323,10 @@ struct GradLds {
     static constexpr int RS = DK + 4;
     alignas(16) float q[VC * RS], k[VC * RS];
     alignas(16) float e[G2 ? VC * RS : 4];
-    alignas(16) float p1[VC * RS], p2[VC * RS], pk[VC * RS];  // dY S0, dX S0, U G' (rows t)
     float ek[VC][VC + 1], qk[VC][VC + 1], dyu[VC][VC + 1], dxu[VC][VC + 1];
     float dek[VC][VC + 1], dqk[VC][VC + 1], gw[VC][VC + 1], bc[VC][VC + 1];
     float l2[VC], gm[VC], bt[VC], sc[VC];
+    float pdg[4][VC], pdsc[4][VC];  // per wave: its key tiles' part of dg_t and dsc_t
     float dgc[4];
 };
 
@@ -437,107 +437,135 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         const float4 x = keep(rok, IO::ld4(ga.dout, rowi + 16 * vt));
         return f32x4{x.x, x.y, x.z, x.w};
     };
-    // One pass over the value tiles, two at a time (every load of a pair in
-    // flight before the first product): this wave's key tiles kt = w + 4 jt
-    // take dY S0, dX S0 and U G'; waves 0 and 1 also take dY U^T and dX U^T
-    // from the same rows.
+    // One pass over the value tiles, software-pipelined: the loads of the
+    // next tile are in flight while this tile's products run.  This wave's
+    // key tiles kt = w + 4 jt take dY S0, dX S0 and U G'; waves 0 and 1 also
+    // take dY U^T and dX U^T from the same rows.  KIND: 0 an odd chunk (S0
+    // rebuilt from its predecessor), 1 an even chunk with a successor (G'
+    // rebuilt), 2 the last chunk when it is even (both as stored).
     f32x4 a1[MT], a2[MT], a3[MT];
 #pragma unroll
     for (int jt = 0; jt < MT; ++jt) a1[jt] = a2[jt] = a3[jt] = zero4;
     f32x4 cc0 = zero4, cc1 = zero4;
     float dgc = 0.f;
-    for (int vt = 0; vt < DV / 16; vt += 2) {  // DV / 16 is even
-        f32x4 yr[2], xr[2], ur[2], sv[2][MT], gv[2][MT];
-        // A operands of the update (odd: U_prev; even: dY_next, dX_next): lane
-        // (g, i) step m holds token 4g + m, value 16 vt + i
-        f32x4 a_1[2], a_2[2];
+    struct Tile {
+        f32x4 yr, xr, ur, sv[MT], gv[MT];
+        f32x4 a_1, a_2;  // A operands of the rebuild: lane (g, i) step m holds token 4g + m, value 16 vt + i
+    };
+    auto load_tile = [&](auto kind, int vt, Tile &o) {
+        constexpr int K = decltype(kind)::value;
+        o.yr = row_dy(vt);
+        o.xr = row_f32(wp.dx, vt);
+        o.ur = row_f32(wp.u, vt);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            yr[u] = row_dy(vt + u);
-            xr[u] = row_f32(wp.dx, vt + u);
-            ur[u] = row_f32(wp.u, vt + u);
-#pragma unroll
-            for (int jt = 0; jt < MT; ++jt) {
-                const int kt = w + 4 * jt;
-                if (kt < KT) {
-                    const int64_t so = static_cast<int64_t>(16 * kt + i) * DV + 16 * (vt + u) + 4 * g;
-                    const float4 s4 = *reinterpret_cast<const float4 *>(S0 + so);
-                    const float4 g4 = *reinterpret_cast<const float4 *>(G1 + so);
-                    sv[u][jt] = f32x4{s4.x, s4.y, s4.z, s4.w};
-                    gv[u][jt] = f32x4{g4.x, g4.y, g4.z, g4.w};
-                }
-            }
-            if (odd) {  // the previous chunk is whole
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    a_1[u][m] = wp.u[(tk + static_cast<int64_t>(4 * g + m - VC) * H) * DV + 16 * (vt + u) + i];
-            } else if (from_next) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int r = 4 * g + m;
-                    const int64_t o = (tk + static_cast<int64_t>(VC + min(r, n_next - 1)) * H) * DV + 16 * (vt + u) + i;
-                    const float yv = IO::ld(ga.dout, o), xv = wp.dx[o];
-                    a_1[u][m] = r < n_next ? yv : 0.f;
-                    a_2[u][m] = r < n_next ? -xv : 0.f;
-                }
+        for (int jt = 0; jt < MT; ++jt) {
+            const int kt = w + 4 * jt;
+            if (kt < KT) {
+                const int64_t so = static_cast<int64_t>(16 * kt + i) * DV + 16 * vt + 4 * g;
+                const float4 s4 = *reinterpret_cast<const float4 *>(S0 + so);
+                const float4 g4 = *reinterpret_cast<const float4 *>(G1 + so);
+                o.sv[jt] = f32x4{s4.x, s4.y, s4.z, s4.w};
+                o.gv[jt] = f32x4{g4.x, g4.y, g4.z, g4.w};
             }
         }
-        if (odd || from_next) {
+        if constexpr (K == 0) {  // the previous chunk is whole
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int m = 0; m < 4; ++m)
+                o.a_1[m] = wp.u[(tk + static_cast<int64_t>(4 * g + m - VC) * H) * DV + 16 * vt + i];
+        } else if constexpr (K == 1) {
 #pragma unroll
-                for (int jt = 0; jt < MT; ++jt) {
-                    if (w + 4 * jt < KT) {
-                        if (odd) {
-                            f32x4 acc = sv[u][jt] * g_nb;
-#pragma unroll
-                            for (int m = 0; m < 4; ++m) acc = mfma4(a_1[u][m], b1[jt][m], acc);
-                            sv[u][jt] = acc;
-                        } else {
-                            f32x4 acc = gv[u][jt] * g_nb;
-#pragma unroll
-                            for (int m = 0; m < 4; ++m) {
-                                acc = mfma4(a_1[u][m], b1[jt][m], acc);
-                                acc = mfma4(a_2[u][m], b2[jt][m], acc);
-                            }
-                            gv[u][jt] = acc;
-                        }
-                    }
-                }
+            for (int m = 0; m < 4; ++m) {
+                const int r = 4 * g + m;
+                const int64_t off = (tk + static_cast<int64_t>(VC + min(r, n_next - 1)) * H) * DV + 16 * vt + i;
+                const float yv = IO::ld(ga.dout, off), xv = wp.dx[off];
+                o.a_1[m] = r < n_next ? yv : 0.f;
+                o.a_2[m] = r < n_next ? -xv : 0.f;
+            }
         }
+    };
+    auto use_tile = [&](auto kind, Tile &o) {
+        constexpr int K = decltype(kind)::value;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int jt = 0; jt < MT; ++jt) {
+            if (w + 4 * jt < KT) {
+                if constexpr (K == 0) {
+                    f32x4 acc = o.sv[jt] * g_nb;
 #pragma unroll
-            for (int jt = 0; jt < MT; ++jt) {
-                if (w + 4 * jt < KT) {
+                    for (int m = 0; m < 4; ++m) acc = mfma4(o.a_1[m], b1[jt][m], acc);
+                    o.sv[jt] = acc;
+                } else if constexpr (K == 1) {
+                    f32x4 acc = o.gv[jt] * g_nb;
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        a1[jt] = mfma4(yr[u][m], sv[u][jt][m], a1[jt]);
-                        a2[jt] = mfma4(xr[u][m], sv[u][jt][m], a2[jt]);
-                        a3[jt] = mfma4(ur[u][m], gv[u][jt][m], a3[jt]);
-                        dgc = fmaf(sv[u][jt][m], gv[u][jt][m], dgc);
+                        acc = mfma4(o.a_1[m], b1[jt][m], acc);
+                        acc = mfma4(o.a_2[m], b2[jt][m], acc);
                     }
+                    o.gv[jt] = acc;
                 }
             }
-            if (w < 2) {
-                const f32x4 ar = w == 0 ? yr[u] : xr[u];
-                cc0 = mfma4(ar[0], ur[u][0], cc0);
-                cc1 = mfma4(ar[1], ur[u][1], cc1);
-                cc0 = mfma4(ar[2], ur[u][2], cc0);
-                cc1 = mfma4(ar[3], ur[u][3], cc1);
+        }
+#pragma unroll
+        for (int jt = 0; jt < MT; ++jt) {
+            if (w + 4 * jt < KT) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    a1[jt] = mfma4(o.yr[m], o.sv[jt][m], a1[jt]);
+                    a2[jt] = mfma4(o.xr[m], o.sv[jt][m], a2[jt]);
+                    a3[jt] = mfma4(o.ur[m], o.gv[jt][m], a3[jt]);
+                    dgc = fmaf(o.sv[jt][m], o.gv[jt][m], dgc);
+                }
             }
         }
-    }
+        if (w < 2) {
+            const f32x4 ar = w == 0 ? o.yr : o.xr;
+            cc0 = mfma4(ar[0], o.ur[0], cc0);
+            cc1 = mfma4(ar[1], o.ur[1], cc1);
+            cc0 = mfma4(ar[2], o.ur[2], cc0);
+            cc1 = mfma4(ar[3], o.ur[3], cc1);
+        }
+    };
+    auto run = [&](auto kind) {
+        const int nt = DV / 16;  // even
+        Tile ta, tb;
+        load_tile(kind, 0, ta);
+        for (int vt = 0; vt < nt; vt += 2) {
+            load_tile(kind, vt + 1, tb);
+            use_tile(kind, ta);
+            load_tile(kind, min(vt + 2, nt - 1), ta);  // past the end: the last tile again (never used)
+            use_tile(kind, tb);
+        }
+    };
+    if (odd) run(icst<0>{});
+    else if (from_next) run(icst<1>{});
+    else run(icst<2>{});
+    // this wave's part of the per-token sums over the key dimension,
+    // dg_t = <Q_t, (dY S0)_t> - <E_t, (dX S0)_t> and dsc_t = <(U G')_t, K_t>
+    // (zero for a wave without key tiles)
+    {
+        float pg[4] = {0.f, 0.f, 0.f, 0.f}, ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int jt = 0; jt < MT; ++jt) {
-        const int kt = w + 4 * jt;
-        if (kt < KT) {
+        for (int jt = 0; jt < MT; ++jt) {
+            const int kt = w + 4 * jt;
+            if (kt < KT) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int o = (4 * g + r) * RS + 16 * kt + i;
+                    pg[r] = fmaf(s.q[o], a1[jt][r], pg[r]);
+                    pg[r] = fmaf(-E[o], a2[jt][r], pg[r]);
+                    ps[r] = fmaf(a3[jt][r], s.k[o], ps[r]);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pg[r] = group_sum<16>(pg[r]);
+            ps[r] = group_sum<16>(ps[r]);
+        }
+        if (i == 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int o = (4 * g + r) * RS + 16 * kt + i;
-                s.p1[o] = a1[jt][r];
-                s.p2[o] = a2[jt][r];
-                s.pk[o] = a3[jt][r];
+                s.pdg[w][4 * g + r] = pg[r];
+                s.pdsc[w][4 * g + r] = ps[r];
             }
         }
     }
@@ -585,12 +613,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // ---- per token: dbeta and the decay's adjoint (wave 0, lanes 0 .. 15)
     if (tid < VC) {
         const int t = tid;
-        float dg = 0.f, dsc = 0.f;
-        for (int j = 0; j < DK; ++j) {
-            dg = fmaf(s.q[t * RS + j], s.p1[t * RS + j], dg);
-            dg = fmaf(-E[t * RS + j], s.p2[t * RS + j], dg);
-            dsc = fmaf(s.pk[t * RS + j], s.k[t * RS + j], dsc);
-        }
+        const float dg = (s.pdg[0][t] + s.pdg[1][t]) + (s.pdg[2][t] + s.pdg[3][t]);
+        const float dsc = (s.pdsc[0][t] + s.pdsc[1][t]) + (s.pdsc[2][t] + s.pdsc[3][t]);
         float dbe = 0.f;
         for (int u = 0; u < VC; ++u) dbe += s.bc[u][t];
         const float gC = s.gm[VC - 1];
@@ -622,7 +646,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
 
     // ---- per (t, key): dQ, dE, dK on the matrix cores (16 x 16 by 16 x 16 per key tile)
-    for (int kt = w; kt < DK / 16; kt += 4) {
+    // (the same lanes hold the same key tile's dY S0, dX S0 and U G' rows
+    // from the pass over the value tiles, so those stay in registers)
+#pragma unroll
+    for (int jt = 0; jt < MT; ++jt) {
+        const int kt = w + 4 * jt;
+        if (kt >= KT) continue;
         const int col = 16 * kt + i;
         f32x4 aq = zero4, ae = zero4, ak0 = zero4, ak1 = zero4;
 #pragma unroll
@@ -638,9 +667,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             const int t = 4 * g + r;
             if (t < n) {
                 const int o = t * RS + col;
-                const float dq = fmaf(s.gm[t], s.p1[o], aq[r]);
-                const float dE = fmaf(-s.gm[t], s.p2[o], ae[r]);
-                float dk = fmaf(s.sc[t], s.pk[o], ak0[r] + ak1[r]);
+                const float dq = fmaf(s.gm[t], a1[jt][r], aq[r]);
+                const float dE = fmaf(-s.gm[t], a2[jt][r], ae[r]);
+                float dk = fmaf(s.sc[t], a3[jt][r], ak0[r] + ak1[r]);
                 const int64_t gi = (tk + static_cast<int64_t>(t) * H) * DK + col;
                 if constexpr (kGates2) {
                     ga.derase_b[gi] = s.k[o] * dE;
