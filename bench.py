@@ -326,9 +326,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the scan shards over (batch, head) chains with no communication; see the "
-              "design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the scan shards over (batch, head) chains with no communication between them)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -28,7 +28,7 @@
  * check).  Inputs and outputs are always double arrays; a float build rounds
  * each input once on load.
  *
- * Readings taken where the pages are silent (each listed in the design notes):
+ * Readings taken where the pages are silent:
  *   - the read happens after the update: y_t = W_t q_t (and S_t q-hat_t);
  *   - Gated DeltaNet's residual is taken against the decayed memory,
  *     r = v - (alpha W_{t-1}) k;
@@ -814,5 +814,5 @@ int oracle_loglinear_forward(int variant, long B, long T, long H, long dk, long 
     return failed ? -1 : 0;
 }
 
-/* Size of `real` in this build (8 for the fp64 oracle, 4 for the spread check). */
+/* Size of `real` as compiled (8 for the fp64 oracle, 4 for the spread check). */
 int oracle_real_bytes(void) { return (int)sizeof(real); }
