@@ -147,6 +147,26 @@ def test_full_grid_every_gradient():
     _check(_run(w, x, dout, dstate, s0), _ref(w, x, dout, dstate, s0), w.name)
 
 
+@pytest.mark.parametrize("name", ["gdn_bf16_B8_T4096_H8_d128", "gdn2_bf16_B8_T4096_H8_d128"])
+def test_full_size_sampled(name):
+    """The forward's throughput shape (the backward bench line's launch),
+    full grid; three (b, h) chains checked against the oracle one by one (the
+    gradients of a chain depend on that chain alone)."""
+    w = I.WORKLOADS[name]
+    x = I.make_inputs(w)
+    dout, dstate = I.make_cotangents(w, 11)
+    got = _run(w, x, dout, dstate, None)
+    for b, h in [(0, 0), (3, 5), (7, 7)]:
+        sl = lambda a: None if a is None else a[b:b + 1, :, h:h + 1]
+        xs = {k: sl(v) for k, v in x.items()}
+        ref = _ref(w, xs, sl(dout), dstate[b:b + 1, h:h + 1], None)
+        mine = {}
+        for n, v in got.items():
+            if v is not None:
+                mine[n] = v[b:b + 1, h:h + 1] if n == "dstate_in" else v[b:b + 1, :, h:h + 1]
+        _check(mine, ref, f"{name} chain ({b},{h})")
+
+
 def test_kda_chunked_is_unsupported():
     import gated_linear_attention_chunked_amd as lam
 

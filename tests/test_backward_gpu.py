@@ -1,5 +1,8 @@
-"""GPU parity of the backward pass (lam_backward through the C ABI) against
-the oracle's fp64 adjoint on the same seeded inputs and cotangents.
+"""GPU parity of the token-recurrent backward pass (lam_backward through the
+C ABI with algo "recurrent", the only form for Kimi Delta) against the
+oracle's fp64 adjoint on the same seeded inputs and cotangents.  The chunked
+backward, the default for the other three variants, has its own tests in
+test_backward_chunked_gpu.py.
 
 The kernel computes in fp32 from the stored inputs (bf16 storage included),
 recomputing the forward states from fp32 checkpoints, so every gradient is
@@ -26,7 +29,7 @@ def _w(variant, dtype, B, T, H, dk, dv, seed, gate_mu=-1.0):
                       dk, dv, seed=seed, gate_mu=gate_mu)
 
 
-def _gpu(w, x, dout, dstate, state_in, with_dstate_in=True):
+def _gpu(w, x, dout, dstate, state_in, with_dstate_in=True, algo="recurrent"):
     import torch
 
     import gated_linear_attention_chunked_amd as lam
@@ -36,7 +39,7 @@ def _gpu(w, x, dout, dstate, state_in, with_dstate_in=True):
     f32 = lambda a: None if a is None else torch.from_numpy(a.astype(np.float32)).cuda()
     r = lam.backward(w.variant, g["q"], g["k"], g["v"], g["beta"], dy, alpha=g.get("alpha"),
                      erase_b=g.get("erase_b"), write_w=g.get("write_w"), state_in=f32(state_in),
-                     dstate_out=f32(dstate), with_dstate_in=with_dstate_in)
+                     dstate_out=f32(dstate), with_dstate_in=with_dstate_in, algo=algo)
     torch.cuda.synchronize()
     return {k: (None if v is None else v.cpu().numpy().astype(np.float64)) for k, v in r.items()}
 
@@ -130,11 +133,11 @@ def test_backward_empty_sequence_passes_the_state_adjoint():
     dst = torch.randn(2, 3, 64, 64, device="cuda")
     e = lambda *s: torch.empty(*s, device="cuda", dtype=torch.bfloat16)
     r = lam.backward("gdn", e(2, 0, 3, 64), e(2, 0, 3, 64), e(2, 0, 3, 64), e(2, 0, 3), e(2, 0, 3, 64),
-                     alpha=e(2, 0, 3), dstate_out=dst)
+                     alpha=e(2, 0, 3), dstate_out=dst, algo="recurrent")
     torch.cuda.synchronize()
     assert torch.equal(r["dstate_in"], dst)
     r = lam.backward("gdn", e(2, 0, 3, 64), e(2, 0, 3, 64), e(2, 0, 3, 64), e(2, 0, 3), e(2, 0, 3, 64),
-                     alpha=e(2, 0, 3))
+                     alpha=e(2, 0, 3), algo="recurrent")
     torch.cuda.synchronize()
     assert torch.count_nonzero(r["dstate_in"]).item() == 0
 
