@@ -167,8 +167,11 @@ def bf16_matrix_schedule(w) -> bool:
 
 
 def kernel_source_hash(ran: str, w):
-    """(source file name, sha256 over that source and the shared headers)."""
+    """(source file name, sha256 over that source, the shared headers and
+    the source's own compiler flags, if it has any)."""
     import hashlib
+
+    from gated_linear_attention_chunked_amd.build import SOURCE_FLAGS
 
     variant = w.variant
     fam = variant if variant in ("kda", "vla") else "delta"
@@ -179,6 +182,8 @@ def kernel_source_hash(ran: str, w):
     h = hashlib.sha256()
     for f in (name,) + SHARED_HEADERS:
         h.update(open(os.path.join(csrc, f), "rb").read())
+    if SOURCE_FLAGS.get(name):
+        h.update(" ".join(SOURCE_FLAGS[name]).encode())
     return name, h.hexdigest()
 
 
