@@ -336,7 +336,7 @@ struct BwdWs {
 };
 
 template <typename IO, int VARIANT, int DK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void delta_f32_grad_kernel(DeltaBwdArgs ga, BwdWs wp) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void delta_f32_grad_kernel(DeltaBwdArgs ga, BwdWs wp) {
     constexpr bool kDecay = VARIANT != kDeltaNet;
     constexpr bool kGates2 = VARIANT == kGatedDeltaNet2;
     using L = GradLds<DK, kGates2>;
@@ -437,12 +437,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         const float4 x = keep(rok, IO::ld4(ga.dout, rowi + 16 * vt));
         return f32x4{x.x, x.y, x.z, x.w};
     };
-    // One pass over the value tiles, software-pipelined: the loads of the
-    // next tile are in flight while this tile's products run.  This wave's
-    // key tiles kt = w + 4 jt take dY S0, dX S0 and U G'; waves 0 and 1 also
-    // take dY U^T and dX U^T from the same rows.  KIND: 0 an odd chunk (S0
-    // rebuilt from its predecessor), 1 an even chunk with a successor (G'
-    // rebuilt), 2 the last chunk when it is even (both as stored).
+    // One pass over the value tiles, a tile's loads then its products: at
+    // about 112 registers a lane four workgroups share a compute unit, and
+    // their waves cover each other's load latency (holding the next tile's
+    // loads in flight instead needs about 180 registers and halves that).
+    // This wave's key tiles kt = w + 4 jt take dY S0, dX S0 and U G'; waves
+    // 0 and 1 also take dY U^T and dX U^T from the same rows.  KIND: 0 an odd
+    // chunk (S0 rebuilt from its predecessor), 1 an even chunk with a
+    // successor (G' rebuilt), 2 the last chunk when it is even (both as
+    // stored).
     f32x4 a1[MT], a2[MT], a3[MT];
 #pragma unroll
     for (int jt = 0; jt < MT; ++jt) a1[jt] = a2[jt] = a3[jt] = zero4;
@@ -525,14 +528,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         }
     };
     auto run = [&](auto kind) {
-        const int nt = DV / 16;  // even
-        Tile ta, tb;
-        load_tile(kind, 0, ta);
-        for (int vt = 0; vt < nt; vt += 2) {
-            load_tile(kind, vt + 1, tb);
+        const int nt = DV / 16;
+        for (int vt = 0; vt < nt; ++vt) {
+            Tile ta;
+            load_tile(kind, vt, ta);
             use_tile(kind, ta);
-            load_tile(kind, min(vt + 2, nt - 1), ta);  // past the end: the last tile again (never used)
-            use_tile(kind, tb);
         }
     };
     if (odd) run(icst<0>{});
