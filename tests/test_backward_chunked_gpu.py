@@ -36,7 +36,7 @@ def _w(variant, dtype, B, T, H, dk, dv, seed, gate_mu=-1.0):
                       dk, dv, seed=seed, gate_mu=gate_mu)
 
 
-def _run(w, x, dout, dstate, s0, algo="chunked"):
+def _run(w, x, dout, dstate, s0, algo="chunked", with_dstate_in=True):
     import torch
 
     import gated_linear_attention_chunked_amd as lam
@@ -46,7 +46,7 @@ def _run(w, x, dout, dstate, s0, algo="chunked"):
     f32 = lambda a: None if a is None else torch.from_numpy(a.astype(np.float32)).cuda()
     r = lam.backward(w.variant, g["q"], g["k"], g["v"], g["beta"], dy, alpha=g.get("alpha"),
                      erase_b=g.get("erase_b"), write_w=g.get("write_w"), state_in=f32(s0),
-                     dstate_out=f32(dstate), algo=algo)
+                     dstate_out=f32(dstate), algo=algo, with_dstate_in=with_dstate_in)
     torch.cuda.synchronize()
     return {k: (None if v is None else v.cpu().numpy().astype(np.float64)) for k, v in r.items()}
 
@@ -100,11 +100,15 @@ def test_lengths(variant, T):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_without_state(variant):
-    """No initial state and no final-state cotangent (both taken as zero)."""
+@pytest.mark.parametrize("with_dstate_in", [True, False])
+def test_without_state(variant, with_dstate_in):
+    """No initial state and no final-state cotangent (both taken as zero);
+    the initial state's cotangent asked for or not."""
     w = _w(variant, "f32", 2, 70, 2, 128, 128, seed=9920)
     x, dout, dstate, s0 = _case(w, with_state=False)
-    _check(_run(w, x, dout, dstate, s0), _ref(w, x, dout, dstate, s0), w.name)
+    got = _run(w, x, dout, dstate, s0, with_dstate_in=with_dstate_in)
+    assert (got["dstate_in"] is None) == (not with_dstate_in)
+    _check(got, _ref(w, x, dout, dstate, s0), w.name)
 
 
 @pytest.mark.parametrize("variant,gate_mu", [("gdn", -4.0), ("gdn2", -4.0), ("deltanet", 0.0), ("gdn", 6.0)])
