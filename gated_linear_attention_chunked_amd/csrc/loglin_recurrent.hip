@@ -22,8 +22,11 @@
 // in tiles of TT.  Per token and occupied level: decay, prediction (one
 // lane-group sum), erase; then the write into level 0; then one read, the
 // levels folded column by column with their lambdas before a single
-// lane-group sum.  Which levels hold anything is a uniform bit mask, so
-// empty levels (on average about half) cost one scalar branch.
+// lane-group sum.  Which levels hold anything is a uniform bit mask: for
+// Kimi Delta and Gated DeltaNet-2 an empty level (on average about half)
+// costs one scalar branch; DeltaNet and Gated DeltaNet run every level's
+// transition without branches (an empty level stays zero), which lets the
+// levels' independent chains interleave.
 #include "device_common.h"
 #include "lam_internal.h"
 
@@ -48,6 +51,7 @@ __global__ __launch_bounds__(kLThreads) void loglin_recurrent_kernel(LogLinArgs 
     constexpr bool kChanDecay = VARIANT == kKimiDelta;
     constexpr bool kScalarDecay = VARIANT == kGatedDeltaNet || VARIANT == kGatedDeltaNet2;
     constexpr bool kGates2 = VARIANT == kGatedDeltaNet2;
+    constexpr bool kAllLevels = !kChanDecay && !kGates2;
     const DeltaArgs &a = g.f;
 
     const int T = static_cast<int>(a.T), H = static_cast<int>(a.H), dv = a.dv, nL = g.nL;
@@ -202,12 +206,15 @@ __global__ __launch_bounds__(kLThreads) void loglin_recurrent_kernel(LogLinArgs 
             const float be = sbeta[t];
             float z = sv[t][rl];
             if constexpr (kGates2) z *= swrite[t][rl];
-            // ---- transition of every occupied level: decay, then erase with its own prediction
+            // ---- transition of every occupied level: decay, then erase with its own prediction.
+            // An empty level holds zeros and stays zero under the transition, so where the
+            // registers allow (scalar or no decay, no erase gate) every level takes it
+            // without a branch: the levels' independent chains then interleave.
             float pr[LMAX];
 #pragma unroll
             for (int l = 0; l < LMAX; ++l) {
                 pr[l] = 0.f;
-                if ((occ >> l) & 1u) {
+                if (kAllLevels || ((occ >> l) & 1u)) {
 #pragma unroll
                     for (int m = 0; m < CPT; ++m) {
                         S[l][m] *= dd[m];
@@ -217,10 +224,10 @@ __global__ __launch_bounds__(kLThreads) void loglin_recurrent_kernel(LogLinArgs 
             }
 #pragma unroll
             for (int l = 0; l < LMAX; ++l)
-                if ((occ >> l) & 1u) pr[l] = group_sum<TPR>(pr[l]);
+                if (kAllLevels || ((occ >> l) & 1u)) pr[l] = group_sum<TPR>(pr[l]);
 #pragma unroll
             for (int l = 0; l < LMAX; ++l) {
-                if ((occ >> l) & 1u) {
+                if (kAllLevels || ((occ >> l) & 1u)) {
                     const float bp = be * pr[l];
 #pragma unroll
                     for (int m = 0; m < CPT; ++m) S[l][m] = fmaf(-bp, kk[m], S[l][m]);
